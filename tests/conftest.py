@@ -1,0 +1,24 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: long-running CPU test")
+
+
+@pytest.fixture(scope="session")
+def gpu_lib():
+    """The HIP binding; skips cleanly only when no GPU is present."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_select_amd as msa
+    msa.load()  # raises if the library is missing: the GPU path never falls back
+    return msa

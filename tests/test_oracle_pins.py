@@ -1,0 +1,355 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each test checks the oracle against something other than its own code:
+a library routine (torch's bf16 cast, torch's CPU attention and autograd),
+a closed form, a hand-derived golden fixture, an invariant of the method,
+brute force on tiny inputs, or finite differences.  No GPU is needed.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from planted import load_planted
+
+RNG = np.random.default_rng(1234)
+
+
+def f32(t):
+    return t.float().numpy()
+
+
+# ---------------------------------------------------------------- bf16 rounding
+def test_round_to_bf16_matches_torch_cast():
+    x = RNG.standard_normal(200000).astype(np.float32) * np.float32(3.0)
+    # exact ties: bit pattern with the low 16 bits equal to 0x8000
+    ties = (RNG.integers(0, 2**15, 1000).astype(np.uint32) << 17 | 0x8000).view(np.float32)
+    ties = ties[np.isfinite(ties)]
+    x = np.concatenate([x, ties, np.array([0.0, -0.0, 1e-40, -3e38], dtype=np.float32)])
+    want = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    got = O.round_to_bf16(x)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+# ---------------------------------------------------------------- gemma RMSNorm
+def test_rmsnorm_closed_forms():
+    x = (RNG.standard_normal((64, 128)) * 2.5).astype(np.float32)
+    eps = 1e-6
+    w0 = np.zeros(128, np.float32)
+    y = O.gemma_rmsnorm(x, w0, eps).astype(np.float64)
+    ms = (x.astype(np.float64) ** 2).mean(axis=1)
+    # mean(y^2) = mean(x^2) / (mean(x^2) + eps)
+    np.testing.assert_allclose((y ** 2).mean(axis=1), ms / (ms + eps), rtol=2e-6)
+    # (1 + w) with w = -1 kills the output; w = 1 doubles it exactly
+    assert np.all(O.gemma_rmsnorm(x, -np.ones(128, np.float32), eps) == 0)
+    assert np.array_equal(O.gemma_rmsnorm(x, np.ones(128, np.float32), eps), 2 * O.gemma_rmsnorm(x, w0, eps))
+    # the weight scales channel d by (1 + w_d)
+    w = (RNG.standard_normal(128) * 0.1).astype(np.float32)
+    np.testing.assert_allclose(O.gemma_rmsnorm(x, w, eps), O.gemma_rmsnorm(x, w0, eps) * (1 + w), rtol=1e-6)
+
+
+# ---------------------------------------------------------------- RoPE
+def test_rope_identity_at_position_zero_and_passthrough():
+    y = RNG.standard_normal((5, 128)).astype(np.float32)
+    out = O.rope_rotate_half(y, np.zeros(5, np.int64), 1e7, 64)
+    assert np.array_equal(out, y)
+    out = O.rope_rotate_half(y, np.arange(5) * 977, 1e7, 64)
+    assert np.array_equal(out[:, 64:], y[:, 64:])
+
+
+def test_rope_unit_vectors_give_rotation_angles():
+    """e_i and e_{i+32} map to (cos t, sin t) and (-sin t, cos t) on dims (i, i+32),
+    with t = p * base**(-i/32) -- the rotary definition with 64 rotated dims."""
+    base = 1e7
+    for p in [1, 3, 1000, 32767]:
+        for i in [0, 1, 7, 16, 31]:
+            e = np.zeros((1, 128), np.float32)
+            e[0, i] = 1
+            out = O.rope_rotate_half(e, np.array([p]), base, 64)[0].astype(np.float64)
+            t = p * base ** (-i / 32.0)
+            assert abs(out[i] - math.cos(t)) < 1e-7 and abs(out[i + 32] - math.sin(t)) < 1e-7
+            nz = np.delete(np.arange(128), [i, i + 32])
+            assert np.all(out[nz] == 0)
+            e = np.zeros((1, 128), np.float32)
+            e[0, i + 32] = 1
+            out = O.rope_rotate_half(e, np.array([p]), base, 64)[0].astype(np.float64)
+            assert abs(out[i] + math.sin(t)) < 1e-7 and abs(out[i + 32] - math.cos(t)) < 1e-7
+
+
+def test_rope_matches_complex_multiplication():
+    y = RNG.standard_normal((50, 128)).astype(np.float32)
+    pos = RNG.integers(0, 32768, 50)
+    out = O.rope_rotate_half(y, pos, 5e6, 64).astype(np.float64)
+    z = y[:, :32].astype(np.float64) + 1j * y[:, 32:64].astype(np.float64)
+    freqs = np.array([5e6 ** (-i / 32.0) for i in range(32)])
+    zr = z * np.exp(1j * pos[:, None] * freqs[None, :])
+    np.testing.assert_allclose(out[:, :32], zr.real, atol=3e-6)
+    np.testing.assert_allclose(out[:, 32:64], zr.imag, atol=3e-6)
+
+
+def test_rope_logits_depend_on_relative_position_only():
+    q = RNG.standard_normal((20, 128)).astype(np.float32)
+    k = RNG.standard_normal((20, 128)).astype(np.float32)
+    pq = RNG.integers(0, 4000, 20)
+    pk = RNG.integers(0, 4000, 20)
+    for shift in [1, 517, 9000]:
+        a = (O.rope_rotate_half(q, pq, 1e7, 64).astype(np.float64) * O.rope_rotate_half(k, pk, 1e7, 64)).sum(1)
+        b = (O.rope_rotate_half(q, pq + shift, 1e7, 64).astype(np.float64) *
+             O.rope_rotate_half(k, pk + shift, 1e7, 64)).sum(1)
+        np.testing.assert_allclose(a, b, atol=5e-5 * np.abs(a).max())
+
+
+# ---------------------------------------------------------------- block scores (brute force)
+def test_block_max_scores_brute_force():
+    L, D, B = 45, 16, 8
+    qf = O.round_to_bf16(RNG.standard_normal((L, D)).astype(np.float32))
+    kf = O.round_to_bf16(RNG.standard_normal((L, D)).astype(np.float32))
+    got = O.block_max_scores(qf, kf, B)
+    for i in range(L):
+        for c in range((L + B - 1) // B):
+            vals = [math.fsum(float(qf[i, d]) * float(kf[j, d]) for d in range(D))
+                    for j in range(c * B, min(c * B + B, L)) if j <= i]
+            want = np.float32(max(vals)) if vals else -np.inf
+            assert got[i, c] == want, (i, c)
+
+
+# ---------------------------------------------------------------- planted selection (golden)
+def test_planted_selection_golden():
+    P = load_planted()
+    res = O.index_select(f32(P["idx_q"]), f32(P["idx_k"]), f32(P["w_q"]), f32(P["w_k"]),
+                         P["cu_seqlens"], block=P["block"], topk=P["topk"])
+    for t, ids, why in P["expected"]:
+        assert list(res.blk_idx[t, 0]) == ids, (t, why)
+    # the planted gaps are wide: no expected row is a near tie except the exact 3/9 tie
+    assert res.gap[P["expected"][3][0], 0] > 1e-2
+
+
+# ---------------------------------------------------------------- selection invariants
+def test_selection_invariants_random():
+    p = synth.make_custom_pack([2600, 700, 2300], num_q_heads=2, num_kv_heads=2, seed=5)
+    cu = p.cu_seqlens.numpy()
+    res = O.index_select(f32(p.idx_q), f32(p.idx_k), f32(p.w_q), f32(p.w_k), cu)
+    seq, pos = O.sequence_layout(cu)
+    for h in range(2):
+        scores = {}
+        for s in range(3):
+            a, b = int(cu[s]), int(cu[s + 1])
+            qf = O.indexer_features(f32(p.idx_q)[a:b, h], f32(p.w_q), pos[a:b], 1e-6, 1e7, 64)
+            kf = O.indexer_features(f32(p.idx_k)[a:b, h], f32(p.w_k), pos[a:b], 1e-6, 1e7, 64)
+            scores[s] = O.block_max_scores(qf, kf, 128)
+        for t in range(0, int(cu[-1]), 7):
+            b = int(pos[t]) // 128
+            ids = [int(c) for c in res.blk_idx[t, h] if c >= 0]
+            assert b in ids
+            assert len(ids) == min(16, b + 1)
+            assert all(0 <= c <= b for c in ids) and ids == sorted(set(ids))
+            if b >= 16:
+                sc = scores[int(seq[t])][int(pos[t]) - 0]
+                sel = [c for c in ids if c != b]
+                uns = [c for c in range(b) if c not in ids]
+                assert min(sc[sel]) >= max(sc[uns])
+
+
+def test_bf16_feature_rounding_matters_only_near_ties():
+    """Skipping the bf16 rounding of the features moves only rows whose 16th/17th
+    scores sit within the bf16 rounding noise of the scores (a few 1e-3 relative):
+    the rounding is a real part of the definition, and its effect is bounded."""
+    p = synth.make_custom_pack([4096], seed=3)
+    args = (f32(p.idx_q), f32(p.idx_k), f32(p.w_q), f32(p.w_k), p.cu_seqlens.numpy())
+    a = O.index_select(*args)
+    b = O.index_select(*args, round_bf16=False)
+    diff = (a.blk_idx != b.blk_idx).any(axis=2)
+    assert diff.sum() > 0
+    assert np.all(a.gap[diff] < 1e-2)
+    assert diff.sum() < 0.05 * np.isfinite(a.gap).sum()
+
+
+# ---------------------------------------------------------------- attention helpers (torch references)
+def _torch_dense(q, k, v, do, mask, scale):
+    """Dense fp64 attention per kv group with a boolean mask [T, T]; torch autograd grads."""
+    T, Hq, D = q.shape
+    Hk = k.shape[1]
+    G = Hq // Hk
+    qt = torch.tensor(q, dtype=torch.float64, requires_grad=True)
+    kt = torch.tensor(k, dtype=torch.float64, requires_grad=True)
+    vt = torch.tensor(v, dtype=torch.float64, requires_grad=True)
+    Q = qt.permute(1, 0, 2).unsqueeze(0)                                # [1, Hq, T, D]
+    K = kt.permute(1, 0, 2).repeat_interleave(G, dim=0).unsqueeze(0)
+    V = vt.permute(1, 0, 2).repeat_interleave(G, dim=0).unsqueeze(0)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        Q, K, V, attn_mask=torch.tensor(mask)[None, None] if mask.ndim == 2 else torch.tensor(mask)[None],
+        scale=scale)
+    o = out[0].permute(1, 0, 2)
+    (o * torch.tensor(do, dtype=torch.float64)).sum().backward()
+    return o.detach().numpy(), qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+def _pack_np(lengths, hq, hk, seed):
+    p = synth.make_custom_pack(lengths, num_q_heads=hq, num_kv_heads=hk, seed=seed)
+    return p, f32(p.q), f32(p.k), f32(p.v), f32(p.do), p.cu_seqlens.numpy()
+
+
+# ---------------------------------------------------------------- P1: dense equality up to 2048
+def test_dense_equality_up_to_2048_tokens():
+    """16 blocks x 128 = 2048 keys: at or below that length the method is full causal attention."""
+    p, q, k, v, do, cu = _pack_np([1024, 640, 384], 4, 2, 11)
+    sel = O.index_select(f32(p.idx_q), f32(p.idx_k), f32(p.w_q), f32(p.w_k), cu)
+    seq, pos = O.sequence_layout(cu)
+    for t in range(0, int(cu[-1]), 13):
+        b = int(pos[t]) // 128
+        assert list(sel.blk_idx[t, 0, :b + 1]) == list(range(b + 1))
+    scale = 1 / math.sqrt(128)
+    Ofw, LSE = O.attention_forward(q, k, v, sel.blk_idx, cu, scale)
+    dQ, dK, dV = O.attention_backward(q, k, v, do, sel.blk_idx, cu, scale)
+    for s in range(3):
+        a, b = int(cu[s]), int(cu[s + 1])
+        G = 2
+        Q = torch.tensor(q[a:b], dtype=torch.float64).permute(1, 0, 2)[None]
+        K = torch.tensor(k[a:b], dtype=torch.float64).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+        V = torch.tensor(v[a:b], dtype=torch.float64).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+        out, lse = torch.ops.aten._scaled_dot_product_flash_attention_for_cpu(Q, K, V, 0.0, True, scale=scale)
+        np.testing.assert_allclose(Ofw[a:b], out[0].permute(1, 0, 2).numpy(), atol=1e-12)
+        np.testing.assert_allclose(LSE[a:b], lse[0].permute(1, 0).numpy(), atol=1e-12)
+        mask = np.tril(np.ones((b - a, b - a), dtype=bool))
+        o_t, dq_t, dk_t, dv_t = _torch_dense(q[a:b], k[a:b], v[a:b], do[a:b], mask, scale)
+        np.testing.assert_allclose(dQ[a:b], dq_t, atol=1e-10)
+        np.testing.assert_allclose(dK[a:b], dk_t, atol=1e-10)
+        np.testing.assert_allclose(dV[a:b], dv_t, atol=1e-10)
+
+
+# ---------------------------------------------------------------- P2: masked dense attention
+def test_sparse_equals_masked_dense_attention():
+    p, q, k, v, do, cu = _pack_np([2400, 300], 4, 2, 21)
+    sel = O.index_select(f32(p.idx_q), f32(p.idx_k), f32(p.w_q), f32(p.w_k), cu)
+    T = int(cu[-1])
+    seq, pos = O.sequence_layout(cu)
+    scale = 1 / math.sqrt(128)
+    Ofw, _ = O.attention_forward(q, k, v, sel.blk_idx, cu, scale)
+    dQ, dK, dV = O.attention_backward(q, k, v, do, sel.blk_idx, cu, scale)
+    # per kv head masks: mask[h, i, j] = same sequence, j <= i, block(j) listed for (i, h)
+    Hk = 2
+    G = 2
+    mask = np.zeros((Hk, T, T), dtype=bool)
+    for h in range(Hk):
+        for i in range(T):
+            s = seq[i]
+            for c in sel.blk_idx[i, h]:
+                if c < 0:
+                    continue
+                lo = int(cu[s]) + int(c) * 128
+                hi = min(lo + 128, i + 1)
+                mask[h, i, lo:hi] = True
+    assert mask.sum() < np.tril(np.ones((T, T), bool)).sum() * Hk * 0.95  # really sparse
+    full_mask = np.repeat(mask, G, axis=0)
+    o_t, dq_t, dk_t, dv_t = _torch_dense(q, k, v, do, full_mask, scale)
+    np.testing.assert_allclose(Ofw, o_t, atol=1e-11)
+    np.testing.assert_allclose(dQ, dq_t, atol=1e-10)
+    np.testing.assert_allclose(dK, dk_t, atol=1e-10)
+    np.testing.assert_allclose(dV, dv_t, atol=1e-10)
+
+
+# ---------------------------------------------------------------- P3: finite differences
+def test_backward_finite_differences():
+    rng = np.random.default_rng(7)
+    lengths, Hq, Hk, D, B, K = [37, 26], 2, 1, 16, 8, 3
+    T = sum(lengths)
+    cu = np.array([0, 37, 63])
+    q = rng.standard_normal((T, Hq, D))
+    k = rng.standard_normal((T, Hk, D))
+    v = rng.standard_normal((T, Hk, D))
+    do = rng.standard_normal((T, Hq, D))
+    # a sparse selection: own block plus up to two random earlier blocks
+    seq, pos = O.sequence_layout(cu)
+    blk = np.full((T, Hk, K), -1, np.int32)
+    for i in range(T):
+        b = pos[i] // B
+        earlier = rng.permutation(b)[:K - 1] if b > 0 else []
+        ids = sorted([b] + [int(c) for c in earlier])
+        blk[i, 0, :len(ids)] = ids
+    scale = 0.37
+
+    def loss(q_, k_, v_):
+        o, _ = O.attention_forward(q_, k_, v_, blk, cu, scale, block=B)
+        return float((o * do).sum())
+
+    dQ, dK, dV = O.attention_backward(q, k, v, do, blk, cu, scale, block=B)
+    h = 1e-6
+    for name, x, g in [("q", q, dQ), ("k", k, dK), ("v", v, dV)]:
+        for _ in range(3):
+            u = rng.standard_normal(x.shape)
+            xp, xm = x + h * u, x - h * u
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            an = float((g * u).sum())
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+# ---------------------------------------------------------------- P7: GQA closed form
+def test_gqa_identical_heads_closed_form():
+    rng = np.random.default_rng(8)
+    cu = np.array([0, 300])
+    T, D, G = 300, 128, 16
+    q1 = rng.standard_normal((T, 1, D))
+    do1 = rng.standard_normal((T, 1, D))
+    k = rng.standard_normal((T, 1, D))
+    v = rng.standard_normal((T, 1, D))
+    seq, pos = O.sequence_layout(cu)
+    blk = np.full((T, 1, 16), -1, np.int32)
+    for i in range(T):
+        b = pos[i] // 128
+        blk[i, 0, :b + 1] = np.arange(b + 1)
+    s = 1 / math.sqrt(128)
+    o1, l1 = O.attention_forward(q1, k, v, blk, cu, s)
+    dq1, dk1, dv1 = O.attention_backward(q1, k, v, do1, blk, cu, s)
+    qG = np.repeat(q1, G, axis=1)
+    doG = np.repeat(do1, G, axis=1)
+    oG, lG = O.attention_forward(qG, k, v, blk, cu, s)
+    dqG, dkG, dvG = O.attention_backward(qG, k, v, doG, blk, cu, s)
+    np.testing.assert_allclose(oG, np.repeat(o1, G, axis=1), atol=1e-12)
+    np.testing.assert_allclose(lG, np.repeat(l1, G, axis=1), atol=1e-12)
+    np.testing.assert_allclose(dqG, np.repeat(dq1, G, axis=1), atol=1e-11)
+    np.testing.assert_allclose(dkG, G * dk1, atol=1e-9)
+    np.testing.assert_allclose(dvG, G * dv1, atol=1e-9)
+
+
+# ---------------------------------------------------------------- P8: q = 0 closed form
+def test_zero_query_uniform_attention_closed_form():
+    rng = np.random.default_rng(9)
+    lengths = [400, 170]
+    cu = np.array([0, 400, 570])
+    T, Hq, Hk, D, B, K = 570, 2, 1, 32, 32, 4
+    q = np.zeros((T, Hq, D))
+    k = rng.standard_normal((T, Hk, D))
+    v = rng.standard_normal((T, Hk, D))
+    do = rng.standard_normal((T, Hq, D))
+    seq, pos = O.sequence_layout(cu)
+    blk = np.full((T, Hk, K), -1, np.int32)
+    for i in range(T):
+        b = pos[i] // B
+        ids = sorted(set([b] + [int(c) for c in rng.integers(0, b + 1, K - 1)]))
+        blk[i, 0, :len(ids)] = ids
+    o, lse = O.attention_forward(q, k, v, blk, cu, 0.2, block=B)
+    dq, dk, dv = O.attention_backward(q, k, v, do, blk, cu, 0.2, block=B)
+    dv_want = np.zeros_like(dv)
+    for i in range(T):
+        s = seq[i]
+        keys = []
+        for c in blk[i, 0]:
+            if c >= 0:
+                keys += [int(cu[s]) + j for j in range(c * B, min(c * B + B, pos[i] + 1))]
+        n = len(keys)
+        vm = v[keys, 0].mean(axis=0)
+        for g in range(Hq):
+            np.testing.assert_allclose(o[i, g], vm, atol=1e-12)
+            assert abs(lse[i, g] - math.log(n)) < 1e-12
+            # dS_j = (dP_j - mean dP) / n ; dq = scale * sum_j dS_j k_j
+            dP = v[keys, 0] @ do[i, g]
+            dS = (dP - dP.mean()) / n
+            np.testing.assert_allclose(dq[i, g], 0.2 * (dS @ k[keys, 0]), atol=1e-12)
+            dv_want[keys, 0] += do[i, g] / n
+    assert np.all(dk == 0)
+    np.testing.assert_allclose(dv, dv_want, atol=1e-12)
