@@ -1,0 +1,246 @@
+"""Python binding of the MSA HIP library (include/msa.h), argument marshalling only.
+
+Every step of the path runs in the HIP kernels of ``libmsa.so``; this module
+turns torch tensors into device pointers, element strides and the current HIP
+stream, sizes and hands over the workspace, and raises on a non-zero status.
+There is no CPU fallback: without the built library every call raises.
+
+Entry points carry the C names:
+
+* ``msa_index_select`` -- frozen lightning-indexer block selection;
+* ``msa_attn_fwd``     -- block-sparse GQA attention forward (O, LSE);
+* ``msa_attn_bwd``     -- its backward (dQ, dK, dV);
+* ``msa_workspace_size``, ``msa_status_string``, ``msa_check_cu_seqlens``.
+
+``MSAAttention`` wraps forward and backward as a ``torch.autograd.Function``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmsa.so")
+
+MSA_OK = 0
+MSA_ERR_INVALID_ARG = -1
+MSA_ERR_UNSUPPORTED = -2
+MSA_ERR_WORKSPACE = -3
+MSA_ERR_HIP = -4
+MSA_OP_SELECT = 1
+MSA_OP_FWD = 2
+MSA_OP_BWD = 3
+
+# Every symbol include/msa.h declares.
+EXPORTED = ("msa_workspace_size", "msa_index_select", "msa_attn_fwd", "msa_attn_bwd",
+            "msa_status_string", "msa_check_cu_seqlens", "msa_version")
+
+
+class MsaDims(ctypes.Structure):
+    _fields_ = [("total_tokens", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("max_seqlen", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("topk_blocks", ctypes.c_int32)]
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libmsa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    lib.msa_workspace_size.argtypes = [ctypes.POINTER(MsaDims), _I32, ctypes.POINTER(_SZ)]
+    lib.msa_workspace_size.restype = _I32
+    lib.msa_index_select.argtypes = [ctypes.POINTER(MsaDims), _P, _I64, _I64, _P, _I64, _I64, _P, _P,
+                                     _F, _F, _I32, _P, _P, _P, _SZ, _P]
+    lib.msa_index_select.restype = _I32
+    lib.msa_attn_fwd.argtypes = [ctypes.POINTER(MsaDims), _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64,
+                                 _P, _P, _F, _P, _I64, _I64, _P, _P, _SZ, _P]
+    lib.msa_attn_fwd.restype = _I32
+    lib.msa_attn_bwd.argtypes = [ctypes.POINTER(MsaDims),
+                                 _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64,
+                                 _P, _P, _I64, _I64, _P, _P, _F,
+                                 _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _SZ, _P]
+    lib.msa_attn_bwd.restype = _I32
+    lib.msa_status_string.argtypes = [_I32]
+    lib.msa_status_string.restype = ctypes.c_char_p
+    lib.msa_check_cu_seqlens.argtypes = [ctypes.POINTER(MsaDims), _P, _P]
+    lib.msa_check_cu_seqlens.restype = _I32
+    lib.msa_version.argtypes = []
+    lib.msa_version.restype = _I32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().msa_status_string(int(status)).decode()
+
+
+msa_status_string = status_string
+
+
+def make_dims(total_tokens: int, num_seqs: int, max_seqlen: int, num_q_heads: int, num_kv_heads: int,
+              head_dim: int = 128, block_size: int = 128, topk_blocks: int = 16) -> MsaDims:
+    return MsaDims(int(total_tokens), int(num_seqs), int(max_seqlen), int(num_q_heads), int(num_kv_heads),
+                   int(head_dim), int(block_size), int(topk_blocks))
+
+
+def msa_workspace_size(dims: MsaDims, op: int) -> int:
+    n = _SZ(0)
+    st = load().msa_workspace_size(ctypes.byref(dims), int(op), ctypes.byref(n))
+    if st != MSA_OK:
+        raise MsaError(st, "msa_workspace_size")
+    return int(n.value)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _bf16_view(t: torch.Tensor, name: str) -> Tuple[int, int]:
+    if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1 or not t.is_cuda:
+        raise ValueError(f"{name}: expected a CUDA bf16 [T, H, 128] tensor with a contiguous last dim")
+    return t.stride(0), t.stride(1)
+
+
+def _workspace(dims: MsaDims, op: int, device, workspace: Optional[torch.Tensor]) -> Tuple[Optional[torch.Tensor], int]:
+    need = msa_workspace_size(dims, op)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel()
+
+
+def _dims_for(cu_seqlens: torch.Tensor, max_seqlen: int, q_heads: int, kv_heads: int, T: int) -> MsaDims:
+    return make_dims(T, cu_seqlens.numel() - 1, max_seqlen, q_heads, kv_heads)
+
+
+def _check(st: int, where: str):
+    if st != MSA_OK:
+        raise MsaError(st, where)
+
+
+def msa_index_select(idx_q: torch.Tensor, idx_k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
+                     cu_seqlens: torch.Tensor, max_seqlen: int, *, eps: float = 1e-6, rope_base: float = 1e7,
+                     rope_dims: int = 64, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block ids [T, Hk, 16] (int32, ascending, -1 padded) chosen by the frozen indexer."""
+    lib = load()
+    T, Hk, _ = idx_q.shape
+    sq = _bf16_view(idx_q, "idx_q")
+    sk = _bf16_view(idx_k, "idx_k")
+    if idx_k.shape[1] == 1 and Hk > 1:
+        sk = (sk[0], 0)
+    dims = _dims_for(cu_seqlens, max_seqlen, 16 * Hk, Hk, T)
+    if out is None:
+        out = torch.empty(T, Hk, 16, dtype=torch.int32, device=idx_q.device)
+    ws, nbytes = _workspace(dims, MSA_OP_SELECT, idx_q.device, workspace)
+    st = lib.msa_index_select(ctypes.byref(dims), _ptr(idx_q), sq[0], sq[1], _ptr(idx_k), sk[0], sk[1],
+                              _ptr(w_q.contiguous()), _ptr(w_k.contiguous()), float(eps), float(rope_base),
+                              int(rope_dims), _ptr(cu_seqlens), _ptr(out), _ptr(ws), nbytes, _stream(idx_q))
+    _check(st, "msa_index_select")
+    return out
+
+
+def msa_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, blk_idx: torch.Tensor,
+                 cu_seqlens: torch.Tensor, max_seqlen: int, softmax_scale: Optional[float] = None, *,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Block-sparse GQA attention forward: returns O [T, Hq, 128] bf16 and LSE [T, Hq] fp32."""
+    lib = load()
+    T, Hq, D = q.shape
+    Hk = k.shape[1]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    sq, sk, sv = _bf16_view(q, "q"), _bf16_view(k, "k"), _bf16_view(v, "v")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty(T, Hq, dtype=torch.float32, device=q.device)
+    so = _bf16_view(out, "out")
+    dims = _dims_for(cu_seqlens, max_seqlen, Hq, Hk, T)
+    ws, nbytes = _workspace(dims, MSA_OP_FWD, q.device, workspace)
+    st = lib.msa_attn_fwd(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0], sv[1],
+                          _ptr(blk_idx), _ptr(cu_seqlens), scale, _ptr(out), so[0], so[1], _ptr(lse),
+                          _ptr(ws), nbytes, _stream(q))
+    _check(st, "msa_attn_fwd")
+    return out, lse
+
+
+def msa_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                 do: torch.Tensor, blk_idx: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+                 softmax_scale: Optional[float] = None, *, dq: Optional[torch.Tensor] = None,
+                 dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Backward of msa_attn_fwd: returns dQ, dK, dV (bf16, shaped like q, k, v)."""
+    lib = load()
+    T, Hq, D = q.shape
+    Hk = k.shape[1]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if dq is None:
+        dq = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if dk is None:
+        dk = torch.empty_like(k, memory_format=torch.contiguous_format)
+    if dv is None:
+        dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    views = [_bf16_view(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do"),
+                                           (dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    dims = _dims_for(cu_seqlens, max_seqlen, Hq, Hk, T)
+    ws, nbytes = _workspace(dims, MSA_OP_BWD, q.device, workspace)
+    (sq, sk, sv, so, sdo, sdq, sdk, sdv) = views
+    st = lib.msa_attn_bwd(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0], sv[1],
+                          _ptr(o), so[0], so[1], _ptr(lse), _ptr(do), sdo[0], sdo[1], _ptr(blk_idx),
+                          _ptr(cu_seqlens), scale, _ptr(dq), sdq[0], sdq[1], _ptr(dk), sdk[0], sdk[1],
+                          _ptr(dv), sdv[0], sdv[1], _ptr(ws), nbytes, _stream(q))
+    _check(st, "msa_attn_bwd")
+    return dq, dk, dv
+
+
+def msa_check_cu_seqlens(cu_seqlens: torch.Tensor, total_tokens: int, max_seqlen: int,
+                         num_q_heads: int = 16, num_kv_heads: int = 1) -> int:
+    """Debug check of the cu_seqlens contract (synchronizes the stream); returns the status."""
+    dims = make_dims(total_tokens, cu_seqlens.numel() - 1, max_seqlen, num_q_heads, num_kv_heads)
+    return int(load().msa_check_cu_seqlens(ctypes.byref(dims), _ptr(cu_seqlens), _stream(cu_seqlens)))
+
+
+class MSAAttention(torch.autograd.Function):
+    """Block-sparse attention with autograd: apply(q, k, v, blk_idx, cu_seqlens, max_seqlen, scale)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, blk_idx, cu_seqlens, max_seqlen, softmax_scale=None):
+        o, lse = msa_attn_fwd(q, k, v, blk_idx, cu_seqlens, max_seqlen, softmax_scale)
+        ctx.save_for_backward(q, k, v, o, lse, blk_idx, cu_seqlens)
+        ctx.max_seqlen = max_seqlen
+        ctx.scale = softmax_scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse, blk_idx, cu = ctx.saved_tensors
+        dq, dk, dv = msa_attn_bwd(q, k, v, o, lse, do.contiguous(), blk_idx, cu, ctx.max_seqlen, ctx.scale)
+        return dq, dk, dv, None, None, None, None

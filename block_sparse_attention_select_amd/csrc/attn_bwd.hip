@@ -1,0 +1,425 @@
+// Block-sparse GQA attention backward on gfx950.
+//
+// What is computed (radixark/miles PR #4581, kernel-tuning commit: gradients
+// of the block-sparse kernel, dK/dV of a KV head summed over its query heads;
+// the follow-up commit stores dV with V's own strides): with
+// P = exp(scale q.k - LSE), dP = dO . v, Delta = rowsum(dO * O) and
+// dS = P (dP - Delta):
+//     dq   = scale * sum_j dS_j k_j                      (token-major pass)
+//     dk_j = scale * sum dS q,  dv_j = sum P dO           (key-block-major pass)
+// the key-block sums running over every (query, head) of the group that
+// selected the block.
+//
+// Kernels:
+//   bwd_prep_kernel     Delta, plus per-token transposed copies of q and dO
+//                       ([d][16 heads]) used as MFMA operands by dK/dV;
+//   attn_bwd_dq_kernel  one wavefront per (token, KV head), the forward's
+//                       transposed-score layout (lane = head row);
+//   attn_bwd_dkdv_kernel one workgroup per (block, chunk of queries): the
+//                       selecting queries of the chunk are listed in token
+//                       order, then each wavefront accumulates 32 keys x 128
+//                       dims of dK and dV in registers, two tokens (32 rows)
+//                       per MFMA step; the chunk's sums go to a workspace
+//                       slice;
+//   dkdv_reduce_kernel  sums the slices of a block in chunk order (fixed
+//                       order, no atomics: bitwise deterministic) and writes
+//                       bf16 dK/dV with their own strides.
+#include "msa_internal.h"
+
+namespace msa {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Delta and transposed q / dO.  One wavefront per (token, KV head).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_prep_kernel(
+    const u16* __restrict__ o, int64_t o_st, int64_t o_sh,
+    const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
+    const u16* __restrict__ q, int64_t q_st, int64_t q_sh, int T, int Hk,
+    float* __restrict__ delta, u16* __restrict__ qT, u16* __restrict__ doT) {
+  __shared__ u16 tq[4][kHeadDim][kGroup + 2];
+  __shared__ u16 tdo[4][kHeadDim][kGroup + 2];
+  const int wl = threadIdx.x >> 6;
+  const int wave_raw = blockIdx.x * 4 + wl;
+  const int lane = threadIdx.x & 63;
+  // Every wavefront reaches the barrier below; surplus ones redo the last
+  // (token, head) without storing.
+  const bool active = wave_raw < T * Hk;
+  const int wave = active ? wave_raw : T * Hk - 1;
+  const int t = wave / Hk;
+  const int h = wave - t * Hk;
+  const int head = lane >> 2;   // 0..15
+  const int quarter = lane & 3; // 32 dims each
+  const int hq = h * kGroup + head;
+  const u16* orow = o + (int64_t)t * o_st + (int64_t)hq * o_sh + 32 * quarter;
+  const u16* drow = dO + (int64_t)t * do_st + (int64_t)hq * do_sh + 32 * quarter;
+  const u16* qrow = q + (int64_t)t * q_st + (int64_t)hq * q_sh + 32 * quarter;
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4 ov = *reinterpret_cast<const uint4*>(orow + 8 * j);
+    const uint4 dv = *reinterpret_cast<const uint4*>(drow + 8 * j);
+    const uint4 qv = *reinterpret_cast<const uint4*>(qrow + 8 * j);
+    const u16* op = reinterpret_cast<const u16*>(&ov);
+    const u16* dp = reinterpret_cast<const u16*>(&dv);
+    const u16* qp = reinterpret_cast<const u16*>(&qv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc += bf2f(op[e]) * bf2f(dp[e]);
+      tdo[wl][32 * quarter + 8 * j + e][head] = dp[e];
+      tq[wl][32 * quarter + 8 * j + e][head] = qp[e];
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  if (active && quarter == 0) delta[(int64_t)t * (Hk * kGroup) + hq] = acc;
+  __syncthreads();
+  if (!active) return;
+  // each lane writes two d rows of 16 heads (2 x 32 bytes) of each tensor
+  const int64_t base = ((int64_t)t * Hk + h) * (kHeadDim * kGroup);
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int d = 2 * lane + rr;
+    uint32_t wq[8], wd[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      wq[e] = (uint32_t)tq[wl][d][2 * e] | ((uint32_t)tq[wl][d][2 * e + 1] << 16);
+      wd[e] = (uint32_t)tdo[wl][d][2 * e] | ((uint32_t)tdo[wl][d][2 * e + 1] << 16);
+    }
+    uint4* qdst = reinterpret_cast<uint4*>(qT + base + d * kGroup);
+    uint4* ddst = reinterpret_cast<uint4*>(doT + base + d * kGroup);
+    qdst[0] = make_uint4(wq[0], wq[1], wq[2], wq[3]);
+    qdst[1] = make_uint4(wq[4], wq[5], wq[6], wq[7]);
+    ddst[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    ddst[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ.  One wavefront per (token, KV head); lane = head row (li), as in the
+// forward.  dQ^T = K^T dS^T with K^T from the per-block transposed copy.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
+    const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
+    const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
+    const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
+    const u16* __restrict__ kt, const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
+    const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ blk_idx, const int32_t* __restrict__ cu, const int32_t* __restrict__ blkbase,
+    int S, int T, int Hk, float scale_log2, float scale, u16* __restrict__ dq, int64_t dq_st, int64_t dq_sh) {
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int li = lane & 15;
+  if (wave >= T * Hk) return;
+  const int t = wave / Hk;
+  const int h = wave - t * Hk;
+  const int s = find_seq(cu, S, t);
+  const int seq0 = cu[s];
+  const int pos = t - seq0;
+  const int b = pos / kBlock;
+  const int gb0 = blkbase[s];
+  const int my_blk = lane < kTopk ? blk_idx[(int64_t)wave * kTopk + lane] : -1;
+  const int hq = h * kGroup + li;
+
+  const u16* qrow = q + (int64_t)t * q_st + (int64_t)hq * q_sh;
+  const u16* drow = dO + (int64_t)t * do_st + (int64_t)hq * do_sh;
+  bf16x8 qb[4], db[4];
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds) {
+    qb[ds] = load_bf16x8(qrow + 32 * ds + 8 * g);
+    db[ds] = load_bf16x8(drow + 32 * ds + 8 * g);
+  }
+  const float l2 = lse[(int64_t)t * (Hk * kGroup) + hq];
+  const bool live = l2 > -INFINITY;
+  const float lse2 = live ? l2 * kLog2e : 0.f;
+  const float dl = delta[(int64_t)t * (Hk * kGroup) + hq];
+
+  f32x4 dqacc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) dqacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int i = 0; i < kTopk; ++i) {
+    const int c = __shfl(my_blk, i);
+    if (c < 0 || c > b) continue;
+    const int kstart = seq0 + kBlock * c;
+    const bool diag = (c == b);
+    f32x4 sacc[8], pacc[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int kl = 32 * (kk >> 1) + 8 * (li >> 2) + 4 * (kk & 1) + (li & 3);
+      const int kg = min(kstart + kl, T - 1);
+      const u16* krow = k + (int64_t)kg * k_st + (int64_t)h * k_sh;
+      const u16* vrow = v + (int64_t)kg * v_st + (int64_t)h * v_sh;
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      f32x4 bb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) {
+        a = mfma16x16x32(load_bf16x8(krow + 32 * ds + 8 * g), qb[ds], a);
+        bb = mfma16x16x32(load_bf16x8(vrow + 32 * ds + 8 * g), db[ds], bb);
+      }
+      sacc[kk] = a;
+      pacc[kk] = bb;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kl = 32 * (kk >> 1) + 8 * g + 4 * (kk & 1) + r;
+        float p = exp2f(sacc[kk][r] * scale_log2 - lse2);
+        if (!live || (diag && kBlock * c + kl > pos)) p = 0.f;
+        sacc[kk][r] = p * (pacc[kk][r] - dl);
+      }
+    bf16x8 dsf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) dsf[ks] = pack_bf16x8(sacc[2 * ks], sacc[2 * ks + 1]);
+    const u16* ktb = kt + ((int64_t)(gb0 + c) * Hk + h) * (kHeadDim * kBlock);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        dqacc[dt] = mfma16x16x32(load_bf16x8(ktb + (16 * dt + li) * kBlock + 32 * ks + 8 * g), dsf[ks], dqacc[dt]);
+  }
+  u16* out = dq + (int64_t)t * dq_st + (int64_t)hq * dq_sh;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<uint2*>(out + 16 * dt + 4 * g) = pack_bf16x4(dqacc[dt] * scale);
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV per (work item, KV head).
+// ---------------------------------------------------------------------------
+constexpr int kMaxChunk = 4096;
+
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
+    const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
+    const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
+    const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
+    const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
+    const u16* __restrict__ qT, const u16* __restrict__ doT,
+    const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ blk_idx, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ blkbase, const int32_t* __restrict__ blk_seq,
+    const int32_t* __restrict__ itembase, const int32_t* __restrict__ totals,
+    int Hk, int chunk, int items_cap, float scale_log2,
+    int32_t* __restrict__ item_count, float* __restrict__ part_dk, float* __restrict__ part_dv) {
+  __shared__ int sel[kMaxChunk];
+  __shared__ int wcount[4];
+  const int item = blockIdx.x;
+  const int h = blockIdx.y;
+  if (item >= totals[1]) return;
+  const int nblk = totals[0];
+  const int gb = upper_index(itembase, nblk, item);
+  const int s = blk_seq[gb];
+  const int c = gb - blkbase[s];
+  const int kidx = item - itembase[gb];
+  const int seq0 = cu[s];
+  const int L = cu[s + 1] - seq0;
+  const int p_begin = kBlock * c + kidx * chunk;
+  const int p_end = min(p_begin + chunk, L);
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int li = lane & 15;
+  const int Hq = Hk * kGroup;
+
+  // 1. list the queries of this chunk that selected block c, in token order
+  int nsel = 0;
+  for (int p0 = p_begin; p0 < p_end; p0 += 256) {
+    const int p = p0 + threadIdx.x;
+    bool hit = false;
+    if (p < p_end) {
+      const int4* ids = reinterpret_cast<const int4*>(blk_idx + ((int64_t)(seq0 + p) * Hk + h) * kTopk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int4 x = ids[j];
+        hit |= (x.x == c) | (x.y == c) | (x.z == c) | (x.w == c);
+      }
+    }
+    const uint64_t m = __ballot(hit);
+    const int before = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) wcount[wave] = __popcll(m);
+    __syncthreads();
+    int off = nsel;
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      off += w < wave ? wcount[w] : 0;
+      tot += wcount[w];
+    }
+    if (hit) sel[off + before] = seq0 + p;
+    nsel += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) item_count[(int64_t)h * items_cap + item] = nsel;
+  if (nsel == 0) return;
+
+  // 2. this wavefront's 32 keys of K and V as B operands (keys past the
+  //    sequence end are zero and always masked by causality)
+  const int kbase = kBlock * c + 32 * wave;
+  bf16x8 kf[2][4], vf[2][4];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int kp = kbase + 16 * kk + li;
+    const bool ok = kp < L;
+    const u16* krow = k + (int64_t)(seq0 + kp) * k_st + (int64_t)h * k_sh;
+    const u16* vrow = v + (int64_t)(seq0 + kp) * v_st + (int64_t)h * v_sh;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      kf[kk][ds] = ok ? load_bf16x8(krow + 32 * ds + 8 * g) : zero_bf16x8();
+      vf[kk][ds] = ok ? load_bf16x8(vrow + 32 * ds + 8 * g) : zero_bf16x8();
+    }
+  }
+  f32x4 dk[2][8], dv[2][8];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      dk[kk][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dv[kk][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  // 3. two selecting tokens (32 query rows) per step
+  for (int n = 0; n < nsel; n += 2) {
+    const int toks[2] = {sel[n], n + 1 < nsel ? sel[n + 1] : -1};
+    f32x4 pv[2][2], dsv[2][2];
+#pragma unroll
+    for (int tk = 0; tk < 2; ++tk) {
+      const int t = toks[tk];
+      if (t < 0) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          pv[tk][kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dsv[tk][kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        continue;
+      }
+      const int pos_t = t - seq0;
+      const u16* qrow = q + (int64_t)t * q_st + (int64_t)(h * kGroup + li) * q_sh;
+      const u16* drow = dO + (int64_t)t * do_st + (int64_t)(h * kGroup + li) * do_sh;
+      bf16x8 qa[4], da[4];
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) {
+        qa[ds] = load_bf16x8(qrow + 32 * ds + 8 * g);
+        da[ds] = load_bf16x8(drow + 32 * ds + 8 * g);
+      }
+      const float4 l4 = *reinterpret_cast<const float4*>(lse + (int64_t)t * Hq + h * kGroup + 4 * g);
+      const float4 d4 = *reinterpret_cast<const float4*>(delta + (int64_t)t * Hq + h * kGroup + 4 * g);
+      const float lr[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dr[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        f32x4 sa = {0.f, 0.f, 0.f, 0.f};
+        f32x4 pa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds) {
+          sa = mfma16x16x32(qa[ds], kf[kk][ds], sa);
+          pa = mfma16x16x32(da[ds], vf[kk][ds], pa);
+        }
+        const int kp = kbase + 16 * kk + li;
+        f32x4 pr, dsr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool live = lr[r] > -INFINITY && kp <= pos_t;
+          const float p = live ? exp2f(sa[r] * scale_log2 - lr[r] * kLog2e) : 0.f;
+          pr[r] = p;
+          dsr[r] = p * (pa[r] - dr[r]);
+        }
+        pv[tk][kk] = pr;
+        dsv[tk][kk] = dsr;
+      }
+    }
+    bf16x8 pA[2], sA[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      pA[kk] = pack_bf16x8(pv[0][kk], pv[1][kk]);
+      sA[kk] = pack_bf16x8(dsv[0][kk], dsv[1][kk]);
+    }
+    const int64_t ta = ((int64_t)toks[0] * Hk + h) * (kHeadDim * kGroup);
+    const int64_t tb = toks[1] >= 0 ? ((int64_t)toks[1] * Hk + h) * (kHeadDim * kGroup) : ta;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d = 16 * dt + li;
+      bf16x8 bdo = load_bf16x4x2(doT + ta + d * kGroup + 4 * g, doT + tb + d * kGroup + 4 * g);
+      bf16x8 bq = load_bf16x4x2(qT + ta + d * kGroup + 4 * g, qT + tb + d * kGroup + 4 * g);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        dv[kk][dt] = mfma16x16x32(pA[kk], bdo, dv[kk][dt]);
+        dk[kk][dt] = mfma16x16x32(sA[kk], bq, dk[kk][dt]);
+      }
+    }
+  }
+
+  // 4. this chunk's slice: part[h][item][key][d], key = 32w + 16kk + 4g + r, d = 16dt + li
+  const int64_t slice = ((int64_t)h * items_cap + item) * (kBlock * kHeadDim);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = 32 * wave + 16 * kk + 4 * g + r;
+        const int64_t off = slice + (int64_t)key * kHeadDim + 16 * dt + li;
+        part_dk[off] = dk[kk][dt][r];
+        part_dv[off] = dv[kk][dt][r];
+      }
+}
+
+// ---------------------------------------------------------------------------
+// Ordered reduction of the per-chunk slices of one (block, KV head).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(
+    const float* __restrict__ part_dk, const float* __restrict__ part_dv, const int32_t* __restrict__ item_count,
+    const int32_t* __restrict__ itembase, const int32_t* __restrict__ blk_seq, const int32_t* __restrict__ blkbase,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ totals, int Hk, int items_cap, float scale,
+    u16* __restrict__ dk, int64_t dk_st, int64_t dk_sh, u16* __restrict__ dv, int64_t dv_st, int64_t dv_sh) {
+  const int gb = blockIdx.x;
+  const int h = blockIdx.y;
+  if (gb >= totals[0]) return;
+  const int s = blk_seq[gb];
+  const int c = gb - blkbase[s];
+  const int seq0 = cu[s];
+  const int L = cu[s + 1] - seq0;
+  const int i0 = itembase[gb];
+  const int i1 = min(itembase[gb + 1], items_cap);
+  for (int e = threadIdx.x * 4; e < kBlock * kHeadDim; e += 256 * 4) {
+    const int key = e / kHeadDim;
+    const int d = e - key * kHeadDim;
+    const int kp = kBlock * c + key;
+    if (kp >= L) continue;
+    f32x4 adk = {0.f, 0.f, 0.f, 0.f};
+    f32x4 adv = {0.f, 0.f, 0.f, 0.f};
+    for (int it = i0; it < i1; ++it) {
+      if (item_count[(int64_t)h * items_cap + it] == 0) continue;
+      const int64_t off = ((int64_t)h * items_cap + it) * (kBlock * kHeadDim) + e;
+      const float4 a = *reinterpret_cast<const float4*>(part_dk + off);
+      const float4 b = *reinterpret_cast<const float4*>(part_dv + off);
+      adk += f32x4{a.x, a.y, a.z, a.w};
+      adv += f32x4{b.x, b.y, b.z, b.w};
+    }
+    *reinterpret_cast<uint2*>(dk + (int64_t)(seq0 + kp) * dk_st + (int64_t)h * dk_sh + d) = pack_bf16x4(adk * scale);
+    *reinterpret_cast<uint2*>(dv + (int64_t)(seq0 + kp) * dv_st + (int64_t)h * dv_sh + d) = pack_bf16x4(adv);
+  }
+}
+
+}  // namespace
+
+void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStream_t st) {
+  const int T = (int)z.T, Hk = (int)z.Hk, S = (int)z.S;
+  const unsigned wgs_tok = (unsigned)((z.T * z.Hk + 3) / 4);
+  launch_block_transpose(z, a.k, a.k_st, a.k_sh, a.cu, p, a.kt, st);
+  bwd_prep_kernel<<<wgs_tok, 256, 0, st>>>(a.o, a.o_st, a.o_sh, a.dO, a.do_st, a.do_sh, a.q, a.q_st, a.q_sh, T, Hk,
+                                           a.delta, a.qT, a.doT);
+  attn_bwd_dq_kernel<<<wgs_tok, 256, 0, st>>>(a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.kt,
+                                              a.dO, a.do_st, a.do_sh, a.lse, a.delta, a.blk_idx, a.cu, p.blkbase, S,
+                                              T, Hk, a.scale * kLog2e, a.scale, a.dq, a.dq_st, a.dq_sh);
+  attn_bwd_dkdv_kernel<<<dim3((unsigned)z.items_cap, (unsigned)Hk), 256, 0, st>>>(
+      a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.dO, a.do_st, a.do_sh, a.qT, a.doT, a.lse,
+      a.delta, a.blk_idx, a.cu, p.blkbase, p.blk_seq, p.itembase, p.totals, Hk, (int)z.chunk, (int)z.items_cap,
+      a.scale * kLog2e, a.item_count, a.part_dk, a.part_dv);
+  dkdv_reduce_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)Hk), 256, 0, st>>>(
+      a.part_dk, a.part_dv, a.item_count, p.itembase, p.blk_seq, p.blkbase, a.cu, p.totals, Hk, (int)z.items_cap,
+      a.scale, a.dk, a.dk_st, a.dk_sh, a.dv, a.dv_st, a.dv_sh);
+}
+
+}  // namespace msa

@@ -1,0 +1,317 @@
+// C ABI of the MSA library: argument validation, workspace carving and the
+// launch sequence of each operation on the caller's stream.  No host sync
+// (except the explicit debug check), no allocation, no state.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/msa.h"
+#include "msa_internal.h"
+
+using msa::Sizes;
+using msa::PlanBufs;
+using msa::u16;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kPartialBudget = int64_t(1) << 30;  // bytes of dK/dV chunk slices before chunks grow
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_dims(const msa_dims* d) {
+  if (!d) return MSA_ERR_INVALID_ARG;
+  if (d->total_tokens < 0 || d->num_seqs < 0 || d->max_seqlen < 0 || d->num_q_heads <= 0 ||
+      d->num_kv_heads <= 0)
+    return MSA_ERR_INVALID_ARG;
+  if (d->total_tokens > 0 && (d->num_seqs < 1 || d->max_seqlen < 1)) return MSA_ERR_INVALID_ARG;
+  if (d->max_seqlen > d->total_tokens && d->total_tokens > 0) return MSA_ERR_INVALID_ARG;
+  if (d->head_dim != msa::kHeadDim || d->block_size != msa::kBlock || d->topk_blocks != msa::kTopk)
+    return MSA_ERR_UNSUPPORTED;
+  if (d->num_q_heads != msa::kGroup * d->num_kv_heads) return MSA_ERR_UNSUPPORTED;
+  if (d->max_seqlen > MSA_MAX_SEQLEN) return MSA_ERR_UNSUPPORTED;
+  if (d->num_kv_heads > 65535) return MSA_ERR_UNSUPPORTED;
+  // 32-bit element counts inside the kernels
+  if ((int64_t)d->total_tokens * d->num_q_heads * msa::kHeadDim >= (int64_t(1) << 31)) return MSA_ERR_UNSUPPORTED;
+  return MSA_OK;
+}
+
+Sizes sizes_of(const msa_dims* d) {
+  Sizes z;
+  z.T = d->total_tokens;
+  z.S = d->num_seqs;
+  z.Hq = d->num_q_heads;
+  z.Hk = d->num_kv_heads;
+  z.max_seqlen = d->max_seqlen;
+  z.nbmax = (z.max_seqlen + msa::kBlock - 1) / msa::kBlock;
+  // sum_s ceil(L_s / 128) <= (T + 127 S) / 128, and <= T (one token per block at least)
+  int64_t cap = (z.T + (msa::kBlock - 1) * z.S) / msa::kBlock;
+  if (cap > z.T) cap = z.T;
+  if (cap < 1) cap = 1;
+  z.nblk_cap = cap;
+  // dK/dV work items: block c of a length-L sequence has ceil((L - 128c)/chunk)
+  // items; summed over a pack this is <= nblk + (T * max_seqlen / 256 + T) / chunk.
+  int64_t chunk = 512;
+  for (;;) {
+    const int64_t items = z.nblk_cap + (z.T * z.max_seqlen / 256 + z.T) / chunk + 2;
+    const int64_t bytes = items * z.Hk * msa::kBlock * msa::kHeadDim * 4 * 2;
+    if (bytes <= kPartialBudget || chunk >= 4096) {
+      z.chunk = chunk;
+      z.items_cap = items;
+      break;
+    }
+    chunk *= 2;
+  }
+  return z;
+}
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? (T*)(base + off) : nullptr;
+    off = align_up(off + count * sizeof(T));
+    return p;
+  }
+};
+
+PlanBufs carve_plan(Carver& c, const Sizes& z) {
+  PlanBufs p;
+  p.blkbase = c.take<int32_t>(z.S + 1);
+  p.blk_seq = c.take<int32_t>(z.nblk_cap);
+  p.itembase = c.take<int32_t>(z.nblk_cap + 1);
+  p.totals = c.take<int32_t>(4);
+  return p;
+}
+
+struct SelectWs {
+  PlanBufs plan;
+  u16* qfeat;
+  u16* kfeat;
+  float* scores;
+};
+SelectWs carve_select(Carver& c, const Sizes& z) {
+  SelectWs w;
+  w.plan = carve_plan(c, z);
+  w.qfeat = c.take<u16>(z.T * z.Hk * msa::kHeadDim);
+  w.kfeat = c.take<u16>(z.T * z.Hk * msa::kHeadDim);
+  w.scores = c.take<float>(z.T * z.Hk * z.nbmax);
+  return w;
+}
+
+struct FwdWs {
+  PlanBufs plan;
+  u16* vt;
+};
+FwdWs carve_fwd(Carver& c, const Sizes& z) {
+  FwdWs w;
+  w.plan = carve_plan(c, z);
+  w.vt = c.take<u16>(z.nblk_cap * z.Hk * msa::kHeadDim * msa::kBlock);
+  return w;
+}
+
+struct BwdWs {
+  PlanBufs plan;
+  u16* kt;
+  float* delta;
+  u16* qT;
+  u16* doT;
+  int32_t* item_count;
+  float* part_dk;
+  float* part_dv;
+};
+BwdWs carve_bwd(Carver& c, const Sizes& z) {
+  BwdWs w;
+  w.plan = carve_plan(c, z);
+  w.kt = c.take<u16>(z.nblk_cap * z.Hk * msa::kHeadDim * msa::kBlock);
+  w.delta = c.take<float>(z.T * z.Hq);
+  w.qT = c.take<u16>(z.T * z.Hk * msa::kHeadDim * msa::kGroup);
+  w.doT = c.take<u16>(z.T * z.Hk * msa::kHeadDim * msa::kGroup);
+  w.item_count = c.take<int32_t>(z.Hk * z.items_cap);
+  w.part_dk = c.take<float>(z.Hk * z.items_cap * msa::kBlock * msa::kHeadDim);
+  w.part_dv = c.take<float>(z.Hk * z.items_cap * msa::kBlock * msa::kHeadDim);
+  return w;
+}
+
+size_t ws_bytes_for(const Sizes& z, int op) {
+  Carver c(nullptr);
+  switch (op) {
+    case MSA_OP_SELECT: carve_select(c, z); break;
+    case MSA_OP_FWD: carve_fwd(c, z); break;
+    case MSA_OP_BWD: carve_bwd(c, z); break;
+    default: return 0;
+  }
+  return c.off;
+}
+
+// A bf16 [T, H, 128] tensor view: 16-byte aligned base, non-negative strides
+// that are multiples of 8 elements.  Inputs may broadcast (zero stride);
+// outputs may not.
+bool ok_view(const void* p, int64_t st_t, int64_t st_h, bool is_output) {
+  if (!p || !aligned(p, 16)) return false;
+  if (st_t < 0 || st_h < 0) return false;
+  if (st_t % 8 != 0 || st_h % 8 != 0) return false;
+  if (is_output && (st_t == 0 || st_h == 0)) return false;
+  return true;
+}
+bool in_view(const void* p, int64_t st_t, int64_t st_h) { return ok_view(p, st_t, st_h, false); }
+bool out_view(const void* p, int64_t st_t, int64_t st_h) { return ok_view(p, st_t, st_h, true); }
+
+int check_ws(void* ws, size_t bytes, size_t need) {
+  if (need == 0) return MSA_OK;
+  if (!ws || !aligned(ws, kAlign) || bytes < need) return MSA_ERR_WORKSPACE;
+  return MSA_OK;
+}
+
+int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int msa_version(void) { return 100; }
+
+const char* msa_status_string(int status) {
+  switch (status) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG: null pointer, negative size, or bad stride/alignment";
+    case MSA_ERR_UNSUPPORTED:
+      return "MSA_ERR_UNSUPPORTED: needs head_dim=128, block_size=128, topk_blocks=16, num_q_heads=16*num_kv_heads, "
+             "max_seqlen<=131072";
+    case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE: workspace null, not 256-byte aligned, or too small";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown MSA status";
+  }
+}
+
+int msa_workspace_size(const msa_dims* dims, int op, size_t* bytes) {
+  if (!bytes) return MSA_ERR_INVALID_ARG;
+  int st = check_dims(dims);
+  if (st != MSA_OK) return st;
+  if (op != MSA_OP_SELECT && op != MSA_OP_FWD && op != MSA_OP_BWD) return MSA_ERR_INVALID_ARG;
+  *bytes = dims->total_tokens == 0 ? 0 : ws_bytes_for(sizes_of(dims), op);
+  return MSA_OK;
+}
+
+int msa_index_select(const msa_dims* dims, const void* idx_q, int64_t sq_t, int64_t sq_h, const void* idx_k,
+                     int64_t sk_t, int64_t sk_h, const void* w_q, const void* w_k, float eps, float rope_base,
+                     int32_t rope_dims, const int32_t* cu_seqlens, int32_t* blk_idx, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MSA_OK) return st;
+  if (rope_dims != 64) return MSA_ERR_UNSUPPORTED;
+  if (!(eps >= 0.f) || !(rope_base > 1.f) || rope_base != rope_base) return MSA_ERR_INVALID_ARG;
+  if (dims->total_tokens == 0) return MSA_OK;
+  if (!in_view(idx_q, sq_t, sq_h) || !in_view(idx_k, sk_t, sk_h)) return MSA_ERR_INVALID_ARG;
+  if (!w_q || !w_k || !aligned(w_q, 2) || !aligned(w_k, 2)) return MSA_ERR_INVALID_ARG;
+  if (!cu_seqlens || !aligned(cu_seqlens, 4) || !blk_idx || !aligned(blk_idx, 16)) return MSA_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(dims);
+  st = check_ws(workspace, workspace_bytes, ws_bytes_for(z, MSA_OP_SELECT));
+  if (st != MSA_OK) return st;
+  Carver c(workspace);
+  SelectWs w = carve_select(c, z);
+  msa::launch_plan(cu_seqlens, z, w.plan, stream);
+  msa::launch_select(z, (const u16*)idx_q, sq_t, sq_h, (const u16*)idx_k, sk_t, sk_h, (const u16*)w_q,
+                     (const u16*)w_k, eps, rope_base, cu_seqlens, w.plan, w.qfeat, w.kfeat, w.scores, blk_idx,
+                     stream);
+  return launch_status();
+}
+
+int msa_attn_fwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh, const void* k, int64_t k_st,
+                 int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh, const int32_t* blk_idx,
+                 const int32_t* cu_seqlens, float softmax_scale, void* o, int64_t o_st, int64_t o_sh, float* lse,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MSA_OK) return st;
+  if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return MSA_ERR_INVALID_ARG;
+  if (dims->total_tokens == 0) return MSA_OK;
+  if (!in_view(q, q_st, q_sh) || !in_view(k, k_st, k_sh) || !in_view(v, v_st, v_sh) || !out_view(o, o_st, o_sh))
+    return MSA_ERR_INVALID_ARG;
+  if (!blk_idx || !aligned(blk_idx, 16) || !cu_seqlens || !aligned(cu_seqlens, 4) || !lse || !aligned(lse, 16))
+    return MSA_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(dims);
+  st = check_ws(workspace, workspace_bytes, ws_bytes_for(z, MSA_OP_FWD));
+  if (st != MSA_OK) return st;
+  Carver c(workspace);
+  FwdWs w = carve_fwd(c, z);
+  msa::launch_plan(cu_seqlens, z, w.plan, stream);
+  msa::launch_block_transpose(z, (const u16*)v, v_st, v_sh, cu_seqlens, w.plan, w.vt, stream);
+  msa::launch_attn_fwd(z, (const u16*)q, q_st, q_sh, (const u16*)k, k_st, k_sh, w.vt, blk_idx, cu_seqlens, w.plan,
+                       softmax_scale, (u16*)o, o_st, o_sh, lse, stream);
+  return launch_status();
+}
+
+int msa_attn_bwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh, const void* k, int64_t k_st,
+                 int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh, const void* o, int64_t o_st, int64_t o_sh,
+                 const float* lse, const void* do_, int64_t do_st, int64_t do_sh, const int32_t* blk_idx,
+                 const int32_t* cu_seqlens, float softmax_scale, void* dq, int64_t dq_st, int64_t dq_sh, void* dk,
+                 int64_t dk_st, int64_t dk_sh, void* dv, int64_t dv_st, int64_t dv_sh, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MSA_OK) return st;
+  if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return MSA_ERR_INVALID_ARG;
+  if (dims->total_tokens == 0) return MSA_OK;
+  if (!in_view(q, q_st, q_sh) || !in_view(k, k_st, k_sh) || !in_view(v, v_st, v_sh) || !in_view(o, o_st, o_sh) ||
+      !in_view(do_, do_st, do_sh) || !out_view(dq, dq_st, dq_sh) || !out_view(dk, dk_st, dk_sh) ||
+      !out_view(dv, dv_st, dv_sh))
+    return MSA_ERR_INVALID_ARG;
+  if (!blk_idx || !aligned(blk_idx, 16) || !cu_seqlens || !aligned(cu_seqlens, 4) || !lse || !aligned(lse, 16))
+    return MSA_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(dims);
+  st = check_ws(workspace, workspace_bytes, ws_bytes_for(z, MSA_OP_BWD));
+  if (st != MSA_OK) return st;
+  Carver c(workspace);
+  BwdWs w = carve_bwd(c, z);
+  msa::BwdArgs a;
+  a.q = (const u16*)q; a.q_st = q_st; a.q_sh = q_sh;
+  a.k = (const u16*)k; a.k_st = k_st; a.k_sh = k_sh;
+  a.v = (const u16*)v; a.v_st = v_st; a.v_sh = v_sh;
+  a.o = (const u16*)o; a.o_st = o_st; a.o_sh = o_sh;
+  a.lse = lse;
+  a.dO = (const u16*)do_; a.do_st = do_st; a.do_sh = do_sh;
+  a.blk_idx = blk_idx;
+  a.cu = cu_seqlens;
+  a.scale = softmax_scale;
+  a.dq = (u16*)dq; a.dq_st = dq_st; a.dq_sh = dq_sh;
+  a.dk = (u16*)dk; a.dk_st = dk_st; a.dk_sh = dk_sh;
+  a.dv = (u16*)dv; a.dv_st = dv_st; a.dv_sh = dv_sh;
+  a.kt = w.kt;
+  a.delta = w.delta;
+  a.qT = w.qT;
+  a.doT = w.doT;
+  a.item_count = w.item_count;
+  a.part_dk = w.part_dk;
+  a.part_dv = w.part_dv;
+  msa::launch_plan(cu_seqlens, z, w.plan, stream);
+  msa::launch_attn_bwd(z, a, w.plan, stream);
+  return launch_status();
+}
+
+int msa_check_cu_seqlens(const msa_dims* dims, const int32_t* cu_seqlens, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MSA_OK) return st;
+  if (!cu_seqlens) return MSA_ERR_INVALID_ARG;
+  const int S = dims->num_seqs;
+  std::vector<int32_t> h((size_t)S + 1);
+  if (hipMemcpyAsync(h.data(), cu_seqlens, sizeof(int32_t) * h.size(), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return MSA_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MSA_ERR_HIP;
+  if (h[0] != 0 || h[S] != dims->total_tokens) return MSA_ERR_INVALID_ARG;
+  for (int s = 0; s < S; ++s) {
+    const int64_t len = (int64_t)h[s + 1] - h[s];
+    if (len < 0 || len > dims->max_seqlen) return MSA_ERR_INVALID_ARG;
+  }
+  return MSA_OK;
+}
+
+}  // extern "C"

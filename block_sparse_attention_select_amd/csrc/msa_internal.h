@@ -1,0 +1,143 @@
+// Internal declarations of the MSA HIP library: device helpers shared by the
+// kernels, the workspace layout and the host-side launchers.  gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msa {
+
+constexpr int kHeadDim = 128;   // D
+constexpr int kBlock = 128;     // keys per block
+constexpr int kTopk = 16;       // selected blocks per query
+constexpr int kGroup = 16;      // query heads per KV head
+constexpr int kMaxBlocks = 1024;  // blocks per sequence this build handles (131072 tokens)
+
+typedef uint16_t u16;
+
+// ----------------------------------------------------------------------------
+// Workspace layout (all offsets 256-byte aligned).  Computed identically by
+// msa_workspace_size and by each operation.
+// ----------------------------------------------------------------------------
+struct Sizes {
+  int64_t T, S, Hq, Hk, max_seqlen;
+  int64_t nbmax;      // ceil(max_seqlen / 128): blocks of the longest sequence
+  int64_t nblk_cap;   // bound on the total number of blocks of the pack
+  int64_t chunk;      // tokens per dK/dV work item
+  int64_t items_cap;  // bound on the number of dK/dV work items per KV head
+};
+
+struct PlanBufs {
+  int32_t* blkbase;   // [S+1]       first global block of each sequence
+  int32_t* blk_seq;   // [nblk_cap]  sequence of each global block
+  int32_t* itembase;  // [nblk_cap+1] first dK/dV work item of each global block
+  int32_t* totals;    // [4]         {number of blocks, number of work items}
+};
+
+// ----------------------------------------------------------------------------
+// Device helpers
+// ----------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(u16 h) { return __uint_as_float(((uint32_t)h) << 16); }
+__device__ __forceinline__ u16 f2bf(float f) { return __builtin_bit_cast(u16, (__bf16)f); }
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const u16* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
+
+// Two 4-element halves (8 bytes each) joined into one MFMA operand.
+__device__ __forceinline__ bf16x8 load_bf16x4x2(const u16* lo, const u16* hi) {
+  uint2 a = *reinterpret_cast<const uint2*>(lo);
+  uint2 b = *reinterpret_cast<const uint2*>(hi);
+  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(f32x4 lo, f32x4 hi) {
+  bf16x8 r;
+  r[0] = (__bf16)lo[0]; r[1] = (__bf16)lo[1]; r[2] = (__bf16)lo[2]; r[3] = (__bf16)lo[3];
+  r[4] = (__bf16)hi[0]; r[5] = (__bf16)hi[1]; r[6] = (__bf16)hi[2]; r[7] = (__bf16)hi[3];
+  return r;
+}
+
+__device__ __forceinline__ uint2 pack_bf16x4(f32x4 v) {
+  uint32_t a = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  uint32_t b = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  return make_uint2(a, b);
+}
+
+// Largest s in [0, S) with cu[s] <= t (the sequence holding token t).
+__device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int S, int t) {
+  int lo = 0, hi = S;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Largest i in [0, n) with a[i] <= x, for non-decreasing a.
+__device__ __forceinline__ int upper_index(const int32_t* __restrict__ a, int n, int x) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (a[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ----------------------------------------------------------------------------
+// Launchers (host functions, each defined next to its kernels).
+// ----------------------------------------------------------------------------
+void launch_plan(const int32_t* cu, const Sizes& z, const PlanBufs& p, hipStream_t st);
+
+void launch_select(const Sizes& z, const u16* idx_q, int64_t sq_t, int64_t sq_h,
+                   const u16* idx_k, int64_t sk_t, int64_t sk_h, const u16* w_q, const u16* w_k,
+                   float eps, float rope_base, const int32_t* cu, const PlanBufs& p,
+                   u16* qfeat, u16* kfeat, float* scores, int32_t* blk_idx, hipStream_t st);
+
+void launch_block_transpose(const Sizes& z, const u16* x, int64_t st_t, int64_t st_h,
+                            const int32_t* cu, const PlanBufs& p, u16* xt, hipStream_t st);
+
+void launch_attn_fwd(const Sizes& z, const u16* q, int64_t q_st, int64_t q_sh,
+                     const u16* k, int64_t k_st, int64_t k_sh, const u16* vt,
+                     const int32_t* blk_idx, const int32_t* cu, const PlanBufs& p, float scale,
+                     u16* o, int64_t o_st, int64_t o_sh, float* lse, hipStream_t st);
+
+struct BwdArgs {
+  const u16* q; int64_t q_st, q_sh;
+  const u16* k; int64_t k_st, k_sh;
+  const u16* v; int64_t v_st, v_sh;
+  const u16* o; int64_t o_st, o_sh;
+  const float* lse;
+  const u16* dO; int64_t do_st, do_sh;
+  const int32_t* blk_idx;
+  const int32_t* cu;
+  float scale;
+  u16* dq; int64_t dq_st, dq_sh;
+  u16* dk; int64_t dk_st, dk_sh;
+  u16* dv; int64_t dv_st, dv_sh;
+  // workspace
+  u16* kt;          // [nblk_cap][Hk][128 d][128 keys] K transposed per block
+  float* delta;     // [T][Hq]
+  u16* qT;          // [T][Hk][128 d][16 heads]
+  u16* doT;         // [T][Hk][128 d][16 heads]
+  int32_t* item_count;  // [Hk][items_cap]
+  float* part_dk;   // [Hk][items_cap][128][128]
+  float* part_dv;
+};
+
+void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStream_t st);
+
+}  // namespace msa

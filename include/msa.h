@@ -1,0 +1,185 @@
+/*
+ * msa.h -- C ABI of the MSA block-sparse attention hot path on AMD Instinct
+ * MI355X (gfx950): the frozen lightning-indexer block selection and the GQA
+ * block-sparse flash attention forward and backward over the selected blocks.
+ *
+ * What the operations compute is stated on these pages:
+ *   [M31] miles docs, "MiniMax-M3.1-Flash", section 1 Model Introduction and
+ *         section 5 Recipe Configuration (5.1 THD packing, 5.4 frozen indexer);
+ *   [PR]  radixark/miles PR #4581, kernel-tuning commit message and PR body
+ *         (per-block max-logit select, block-sparse attention fwd/bwd, dV
+ *         stored with V's own strides, no host sync between select and attention);
+ *   [MB]  NVIDIA Megatron-Bridge, "MiniMax-M3", Architecture Notes and Known
+ *         Limitations (gemma RMSNorm x*(1+w), partial RoPE, 16 x 128 keys).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors are THD-packed: token-major, then head, then the 128-wide head dim,
+ * which must be contiguous (stride 1).  Token and head strides are given in
+ * elements; they and every tensor pointer must keep 16-byte alignment (strides
+ * multiples of 8 bf16 elements).  All tensor pointers, cu_seqlens and the
+ * workspace are DEVICE pointers; msa_dims is read on the host.  bf16 means
+ * 16-bit brain-float storage.
+ *
+ * cu_seqlens holds num_seqs+1 int32 offsets: cu[0] = 0, non-decreasing,
+ * cu[num_seqs] = total_tokens, every length <= max_seqlen.  The library never
+ * reads it back to the host (no host sync); it trusts this contract, which
+ * msa_check_cu_seqlens can verify in debug builds of a caller.
+ * Positions and 128-token blocks restart with every sequence ([M31] 5.1).
+ *
+ * Heads: query head g reads KV head g / (num_q_heads / num_kv_heads); index
+ * head h selects the blocks of KV head h ([M31] section 1).  This build
+ * supports head_dim = 128, block_size = 128, topk_blocks = 16 and exactly 16
+ * query heads per KV head (one TP4 shard of MiniMax-M3 is 16 q / 1 kv).
+ *
+ * Ownership and execution: the caller allocates every input, output and the
+ * workspace (size from msa_workspace_size).  The library allocates nothing,
+ * keeps no pointer after a call returns and holds no state between calls.
+ * Work is enqueued on `stream` and runs asynchronously; outputs are
+ * overwritten, never accumulated.  Identical inputs give bitwise identical
+ * outputs.  Calls sharing one workspace must be ordered on one stream.
+ *
+ * Errors: every entry point returns MSA_OK (0) or a negative status.  On an
+ * argument error nothing is launched.  MSA_ERR_HIP reports a launch failure
+ * (hipGetLastError) after work may already have been enqueued.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_OK 0
+#define MSA_ERR_INVALID_ARG (-1) /* null pointer, negative size, bad stride or alignment    */
+#define MSA_ERR_UNSUPPORTED (-2) /* valid but outside this build: D/block/topk/group/limits   */
+#define MSA_ERR_WORKSPACE (-3)   /* workspace null, misaligned (256 B) or smaller than needed */
+#define MSA_ERR_HIP (-4)         /* the HIP runtime reported an error                         */
+
+#define MSA_OP_SELECT 1
+#define MSA_OP_FWD 2
+#define MSA_OP_BWD 3
+
+/* Longest sequence this build accepts (1024 blocks of 128 tokens). */
+#define MSA_MAX_SEQLEN 131072
+
+typedef struct msa_dims {
+  int32_t total_tokens; /* T = cu_seqlens[num_seqs]; 0 makes every call a no-op          */
+  int32_t num_seqs;     /* S >= 1 when T > 0                                             */
+  int32_t max_seqlen;   /* host-side bound on every sequence length, sizes the grids     */
+  int32_t num_q_heads;  /* Hq = 16 * Hk                                                  */
+  int32_t num_kv_heads; /* Hk = number of index heads                                    */
+  int32_t head_dim;     /* must be 128                                                   */
+  int32_t block_size;   /* must be 128                                                   */
+  int32_t topk_blocks;  /* must be 16                                                    */
+} msa_dims;
+
+/*
+ * Workspace bytes that operation `op` (MSA_OP_*) needs for `dims`, written to
+ * *bytes.  The pointer passed to the operation must be 256-byte aligned.
+ */
+int msa_workspace_size(const msa_dims* dims, int op, size_t* bytes);
+
+/*
+ * Frozen lightning-indexer block selection ([M31] section 1; [PR] per-block
+ * max-logit scores, rules and top-k; [MB] Architecture Notes for the norm).
+ *
+ * For token t at sequence-local position p (block b = p / 128) and index
+ * head h:
+ *   q~ = bf16( RoPE_p( RMSNorm(idx_q[t,h]) * (1 + w_q) ) ),
+ *   k~_j likewise from idx_k[j,h] and w_k,
+ * where RMSNorm(x) = x / sqrt(mean(x^2) + eps) over the 128 dims, and RoPE_p
+ * rotates pairs (i, i+32), i < 32, of dims [0, 64) by p * rope_base^(-2i/64)
+ * (rotate-half) leaving dims [64, 128) unchanged; norm and RoPE run in fp32
+ * with fp64 angles.  Block c <= b scores max_{j in c, j <= t} q~ . k~_j
+ * (fp32 accumulation).  Selection: blocks 0..b when b < 16, else block b
+ * plus the 15 best of 0..b-1 (higher score first, lower id on equal scores).
+ *
+ *   idx_q   [T, Hk, 128] bf16, strides (sq_t, sq_h)
+ *   idx_k   [T, Hk, 128] bf16, strides (sk_t, sk_h); sk_h = 0 shares one key head
+ *   w_q,w_k [128] bf16 gemma weights (applied as 1 + w)
+ *   eps (1e-6), rope_base (1e7), rope_dims (must be 64)
+ *   blk_idx [T, Hk, 16] int32 output, contiguous: sequence-local block ids in
+ *           ascending order, padded with -1 when b < 15.
+ */
+int msa_index_select(const msa_dims* dims,
+                     const void* idx_q, int64_t sq_t, int64_t sq_h,
+                     const void* idx_k, int64_t sk_t, int64_t sk_h,
+                     const void* w_q, const void* w_k,
+                     float eps, float rope_base, int32_t rope_dims,
+                     const int32_t* cu_seqlens, int32_t* blk_idx,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Block-sparse GQA attention forward ([M31] section 1: each query attends to
+ * its selected blocks; [PR] QSA block-sparse kernel).
+ *
+ * For token t, query head g, KV head h = g / 16: the key set J is every key
+ * j <= t of the blocks listed in blk_idx[t,h] (ids outside 0..b and -1 are
+ * ignored; ids must be distinct).  O[t,g] = sum_j softmax_j(scale * q.k_j) v_j
+ * with fp32 softmax and accumulation; LSE[t,g] = natural log of the softmax
+ * denominator (the max-shifted sum), saved for the backward.  A row whose key
+ * set is empty gets O = 0 and LSE = -inf.
+ *
+ *   q [T,Hq,128], k,v [T,Hk,128], o [T,Hq,128] bf16 with their own strides;
+ *   blk_idx [T,Hk,16] int32 contiguous; lse [T,Hq] fp32 contiguous output.
+ */
+int msa_attn_fwd(const msa_dims* dims,
+                 const void* q, int64_t q_st, int64_t q_sh,
+                 const void* k, int64_t k_st, int64_t k_sh,
+                 const void* v, int64_t v_st, int64_t v_sh,
+                 const int32_t* blk_idx, const int32_t* cu_seqlens, float softmax_scale,
+                 void* o, int64_t o_st, int64_t o_sh, float* lse,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Block-sparse GQA attention backward ([PR]: gradients of the block-sparse
+ * kernel; dK/dV of a KV head are the sum over its query heads, reduced here
+ * in a fixed order without atomics; dV is written with V's own strides).
+ *
+ * Gradients of sum(O * dO) over the same key sets as the forward, from the
+ * forward's O and LSE:  P = exp(scale q.k - LSE), dP = dO.v,
+ * Delta = rowsum(dO * O), dS = P (dP - Delta); dq = scale sum_j dS k_j;
+ * dk_j = scale sum dS q and dv_j = sum P dO over every (query, head) of the
+ * group that attends to key j.  The indexer is frozen ([M31] 5.4): there is
+ * no gradient for the select inputs.
+ *
+ *   q, k, v, o, do_ as in the forward (each with its own strides), lse [T,Hq]
+ *   fp32 from the forward; outputs dq [T,Hq,128], dk, dv [T,Hk,128] bf16
+ *   with their own strides (dv need not share dk's layout).
+ */
+int msa_attn_bwd(const msa_dims* dims,
+                 const void* q, int64_t q_st, int64_t q_sh,
+                 const void* k, int64_t k_st, int64_t k_sh,
+                 const void* v, int64_t v_st, int64_t v_sh,
+                 const void* o, int64_t o_st, int64_t o_sh,
+                 const float* lse,
+                 const void* do_, int64_t do_st, int64_t do_sh,
+                 const int32_t* blk_idx, const int32_t* cu_seqlens, float softmax_scale,
+                 void* dq, int64_t dq_st, int64_t dq_sh,
+                 void* dk, int64_t dk_st, int64_t dk_sh,
+                 void* dv, int64_t dv_st, int64_t dv_sh,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static, human-readable text for a status code. */
+const char* msa_status_string(int status);
+
+/*
+ * Debug check of the cu_seqlens contract.  Unlike every other entry point it
+ * copies cu_seqlens to the host and synchronizes `stream`.  Returns MSA_OK,
+ * MSA_ERR_INVALID_ARG when the offsets break the contract, or MSA_ERR_HIP.
+ */
+int msa_check_cu_seqlens(const msa_dims* dims, const int32_t* cu_seqlens, hipStream_t stream);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int msa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */

@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects bad arguments before it
+launches anything.  No GPU is needed (and none is touched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import block_sparse_attention_select_amd as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+# The argument checks below pass made-up device addresses that must never be
+# dereferenced; keep them off machines with a GPU.
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="uses fake device pointers; CPU-only host checks")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = msa.load()
+    names = declared_functions()
+    assert set(names) == set(msa.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", msa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (msa_\w+)", out))
+    assert set(names) <= exported
+    assert lib.msa_version() >= 100
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4):
+        s = msa.status_string(st)
+        assert s.startswith("MSA_")
+    assert "unknown" in msa.status_string(7)
+
+
+def dims(**kw):
+    base = dict(total_tokens=16384, num_seqs=3, max_seqlen=7122, num_q_heads=16, num_kv_heads=1)
+    base.update(kw)
+    return msa.make_dims(**base)
+
+
+def test_workspace_sizes_are_positive_and_monotone():
+    small = {op: msa.msa_workspace_size(dims(total_tokens=1024, num_seqs=1, max_seqlen=1024), op)
+             for op in (msa.MSA_OP_SELECT, msa.MSA_OP_FWD, msa.MSA_OP_BWD)}
+    big = {op: msa.msa_workspace_size(dims(), op) for op in (msa.MSA_OP_SELECT, msa.MSA_OP_FWD, msa.MSA_OP_BWD)}
+    for op in small:
+        assert 0 < small[op] < big[op]
+        assert big[op] % 256 == 0
+    assert msa.msa_workspace_size(dims(total_tokens=0, num_seqs=0, max_seqlen=0), msa.MSA_OP_BWD) == 0
+    # the unsharded 32k layer stays within a few GiB of scratch
+    assert msa.msa_workspace_size(dims(total_tokens=32768, num_seqs=1, max_seqlen=32768, num_q_heads=64,
+                                       num_kv_heads=4), msa.MSA_OP_BWD) < 3 << 30
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), msa.MSA_ERR_UNSUPPORTED),
+    (dict(block_size=64), msa.MSA_ERR_UNSUPPORTED),
+    (dict(topk_blocks=8), msa.MSA_ERR_UNSUPPORTED),
+    (dict(num_q_heads=8), msa.MSA_ERR_UNSUPPORTED),
+    (dict(num_q_heads=32, num_kv_heads=1), msa.MSA_ERR_UNSUPPORTED),
+    (dict(max_seqlen=200000, total_tokens=300000), msa.MSA_ERR_UNSUPPORTED),
+    (dict(total_tokens=-1), msa.MSA_ERR_INVALID_ARG),
+    (dict(num_seqs=0), msa.MSA_ERR_INVALID_ARG),
+    (dict(max_seqlen=0), msa.MSA_ERR_INVALID_ARG),
+    (dict(max_seqlen=20000), msa.MSA_ERR_INVALID_ARG),
+])
+def test_workspace_size_rejects_bad_dims(kw, status):
+    n = ctypes.c_size_t(0)
+    d = dims(**kw)
+    assert msa.load().msa_workspace_size(ctypes.byref(d), msa.MSA_OP_FWD, ctypes.byref(n)) == status
+
+
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced
+
+
+def _fwd(lib, d, q=FAKE, q_st=2048, q_sh=128, k=FAKE, v=FAKE, blk=FAKE, cu=FAKE, scale=0.088, o=FAKE,
+         o_st=2048, o_sh=128, lse=FAKE, ws=FAKE, nbytes=1 << 40):
+    return lib.msa_attn_fwd(ctypes.byref(d), q, q_st, q_sh, k, 128, 128, v, 128, 128, blk, cu, scale,
+                            o, o_st, o_sh, lse, ws, nbytes, None)
+
+
+@no_gpu
+def test_fwd_argument_errors_launch_nothing():
+    lib = msa.load()
+    d = dims()
+    assert _fwd(lib, d, q=None) == msa.MSA_ERR_INVALID_ARG
+    assert _fwd(lib, d, q=FAKE + 2) == msa.MSA_ERR_INVALID_ARG       # misaligned
+    assert _fwd(lib, d, q_st=2047) == msa.MSA_ERR_INVALID_ARG         # stride not a multiple of 8
+    assert _fwd(lib, d, o_sh=0) == msa.MSA_ERR_INVALID_ARG            # broadcast output
+    assert _fwd(lib, d, blk=None) == msa.MSA_ERR_INVALID_ARG
+    assert _fwd(lib, d, lse=FAKE + 4) == msa.MSA_ERR_INVALID_ARG
+    assert _fwd(lib, d, scale=0.0) == msa.MSA_ERR_INVALID_ARG
+    assert _fwd(lib, d, scale=float("nan")) == msa.MSA_ERR_INVALID_ARG
+    assert _fwd(lib, d, ws=None) == msa.MSA_ERR_WORKSPACE
+    assert _fwd(lib, d, ws=FAKE + 16) == msa.MSA_ERR_WORKSPACE        # not 256-byte aligned
+    need = msa.msa_workspace_size(d, msa.MSA_OP_FWD)
+    assert _fwd(lib, d, nbytes=need - 1) == msa.MSA_ERR_WORKSPACE
+    # empty pack: a no-op that touches nothing
+    assert _fwd(lib, dims(total_tokens=0, num_seqs=0, max_seqlen=0), q=None, ws=None) == msa.MSA_OK
+
+
+@no_gpu
+def test_select_and_bwd_argument_errors_launch_nothing():
+    lib = msa.load()
+    d = dims()
+    sel = lambda **kw: lib.msa_index_select(
+        ctypes.byref(kw.get("d", d)), kw.get("iq", FAKE), 128, 128, FAKE, 128, kw.get("sk_h", 128), FAKE, FAKE,
+        1e-6, kw.get("base", 1e7), kw.get("rope", 64), FAKE, kw.get("blk", FAKE), kw.get("ws", FAKE),
+        kw.get("n", 1 << 40), None)
+    assert sel(rope=32) == msa.MSA_ERR_UNSUPPORTED
+    assert sel(base=1.0) == msa.MSA_ERR_INVALID_ARG
+    assert sel(iq=None) == msa.MSA_ERR_INVALID_ARG
+    assert sel(blk=FAKE + 4) == msa.MSA_ERR_INVALID_ARG
+    assert sel(n=0) == msa.MSA_ERR_WORKSPACE
+    assert sel(d=dims(total_tokens=0, num_seqs=0, max_seqlen=0), iq=None, ws=None) == msa.MSA_OK
+
+    def bwd(dv_sh=128, ws=FAKE, n=1 << 40, lse=FAKE):
+        return lib.msa_attn_bwd(ctypes.byref(d), FAKE, 2048, 128, FAKE, 128, 128, FAKE, 128, 128, FAKE, 2048, 128,
+                                lse, FAKE, 2048, 128, FAKE, FAKE, 0.088, FAKE, 2048, 128, FAKE, 128, 128,
+                                FAKE, 128, dv_sh, ws, n, None)
+    assert bwd(dv_sh=0) == msa.MSA_ERR_INVALID_ARG
+    assert bwd(lse=None) == msa.MSA_ERR_INVALID_ARG
+    assert bwd(n=msa.msa_workspace_size(d, msa.MSA_OP_BWD) - 256) == msa.MSA_ERR_WORKSPACE
