@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark of the MSA hot path on one MI355X: index-select + block-sparse
+attention forward + backward over one 16384-token THD pack.
+
+A step is one pass of the whole path over one pack already resident in HBM:
+msa_index_select, then msa_attn_fwd on its block ids, then msa_attn_bwd.
+Prints ONE JSON line.  ``value`` is milliseconds per pack (select + fwd +
+bwd; lower is better); the line also carries the split, the counted-FLOP
+throughput of fwd+bwd against the bf16 MFMA peak, the roofline of the
+dominant kernel (HIP-event timed on its launch stream) and the CPU oracle
+timed on a bounded sample of the same pack.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "MSA fwd+bwd ms & select ms per 16k-token THD pack; % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+D = 128
+
+# Algorithmic work per unit, for the roofline of each kernel:
+#   select_scores: 2*D FLOP per causal (query, key) pair per index head;
+#   attn_fwd:      4*D FLOP per (query head, selected causal key)   [S, PV];
+#   attn_bwd_dq:   6*D FLOP per (query head, selected causal key)   [S, dP, dQ];
+#   attn_bwd_dkdv: 8*D FLOP per (query head, selected causal key)   [S, dP, dV, dK].
+FLOP_PER_KEY = {"attn_fwd": 4 * D, "attn_bwd_dq": 6 * D, "attn_bwd_dkdv": 8 * D}
+
+
+def selected_keys(blk: np.ndarray, cu: np.ndarray) -> int:
+    """Sum over (token, kv head) of the causal keys in the listed blocks."""
+    T = blk.shape[0]
+    pos = np.empty(T, np.int64)
+    for s in range(len(cu) - 1):
+        pos[cu[s]:cu[s + 1]] = np.arange(cu[s + 1] - cu[s])
+    b = pos // 128
+    valid = (blk >= 0) & (blk <= b[:, None, None])
+    full = (blk < b[:, None, None]) & valid
+    own = (blk == b[:, None, None])
+    n = full.sum(axis=2) * 128 + own.sum(axis=2) * (pos % 128 + 1)[:, None]
+    return int(n.sum())
+
+
+def causal_pairs(lengths) -> int:
+    return int(sum(L * (L + 1) // 2 for L in lengths))
+
+
+def cpu_baseline(p, stride: int):
+    """The oracle as it stands, on this host: select on the whole pack, fwd+bwd on
+    every `stride`-th token, scaled to the full pack."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    f = lambda t: t.float().numpy()
+    cu = p.cu_seqlens.numpy()
+    t0 = time.perf_counter()
+    res = O.index_select(f(p.idx_q), f(p.idx_k), f(p.w_q), f(p.w_k), cu)
+    t_sel = time.perf_counter() - t0
+    rows = np.arange(0, p.total, stride)
+    q, k, v, do = f(p.q), f(p.k), f(p.v), f(p.do)
+    t0 = time.perf_counter()
+    O.attention_forward(q, k, v, res.blk_idx, cu, p.softmax_scale, rows=rows)
+    O.attention_backward(q, k, v, do, res.blk_idx, cu, p.softmax_scale, rows=rows)
+    t_att = time.perf_counter() - t0
+    est_ms = (t_sel + t_att * p.total / len(rows)) * 1e3
+    return {"value": round(est_ms, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
+            "sample": f"select on all {p.total} tokens ({t_sel:.1f} s); fwd+bwd on every {stride}th token "
+                      f"({len(rows)} rows, {t_att:.1f} s) scaled x{p.total / len(rows):.0f}",
+            "host_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="pack16k", choices=sorted(synth.CONFIGS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-stride", type=int, default=3, help="oracle fwd+bwd sample: every n-th token")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the MSA path shards by KV head with no exchange step, "
+              "so only --gpus 1 is run here", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import block_sparse_attention_select_amd as msa
+    msa.load()
+
+    p = synth.make_pack(args.config, args.seed)
+    dev = torch.device("cuda:0")
+    g = lambda t: t.to(dev)
+    cu = g(p.cu_seqlens)
+    q, k, v, do = g(p.q), g(p.k), g(p.v), g(p.do)
+    iq, ik, wq, wk = g(p.idx_q), g(p.idx_k), g(p.w_q), g(p.w_k)
+    T, Hq, Hk = p.total, p.num_q_heads, p.num_kv_heads
+    dims = msa.make_dims(T, len(p.lengths), p.max_seqlen, Hq, Hk)
+    ws = {op: torch.empty(max(msa.msa_workspace_size(dims, op), 1), dtype=torch.uint8, device=dev)
+          for op in (msa.MSA_OP_SELECT, msa.MSA_OP_FWD, msa.MSA_OP_BWD)}
+    blk = torch.empty(T, Hk, 16, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(T, Hq, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        msa.msa_index_select(iq, ik, wq, wk, cu, p.max_seqlen, out=blk, workspace=ws[msa.MSA_OP_SELECT])
+        if ev is not None:
+            ev[1].record()
+        msa.msa_attn_fwd(q, k, v, blk, cu, p.max_seqlen, out=o, lse=lse, workspace=ws[msa.MSA_OP_FWD])
+        if ev is not None:
+            ev[2].record()
+        msa.msa_attn_bwd(q, k, v, o, lse, do, blk, cu, p.max_seqlen, dq=dq, dk=dk, dv=dv,
+                         workspace=ws[msa.MSA_OP_BWD])
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    sel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    fwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    # per-kernel durations: HIP event pairs recorded by the library on the launch stream
+    msa.msa_timing_collect()
+    msa.msa_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = msa.msa_timing_collect()
+    msa.msa_timing_enable(False)
+    kernels = {name: round(ms / n, 4) for name, (n, ms) in kt.items()}
+
+    # counted work
+    blk_np = blk.cpu().numpy()
+    cu_np = p.cu_seqlens.numpy()
+    nkeys = selected_keys(blk_np, cu_np)              # (token, kv head, key) triples
+    per_qhead = nkeys * (Hq // Hk)                    # (token, q head, key)
+    fwd_flop = 4 * D * per_qhead
+    fb_flop = 14 * D * per_qhead
+    sel_flop = 2 * D * causal_pairs(p.lengths) * Hk
+    sel_bytes = 2 * T * Hk * D * 2 + T * Hk * 16 * 4
+    fb_ms = fwd_ms + bwd_ms
+    fb_tflops = fb_flop / (fb_ms * 1e-3) / 1e12
+
+    dom = max(kt.items(), key=lambda kv: kv[1][1])[0]
+    dom_ms = kt[dom][1] / kt[dom][0]
+    if dom in FLOP_PER_KEY:
+        dom_flop = FLOP_PER_KEY[dom] * per_qhead
+    elif dom == "select_scores":
+        dom_flop = sel_flop
+    else:
+        dom_flop = None
+    roofline = None
+    if dom_flop is not None:
+        ach = dom_flop / (dom_ms * 1e-3) / 1e12
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "avg_launch_ms": round(dom_ms, 4), "algorithmic_flop_per_launch": int(dom_flop)}
+
+    line = {
+        "metric": METRIC,
+        "value": round(wall_ms, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: {p.total}-token THD pack, seed {args.seed}, lengths {p.lengths}, "
+                               f"{Hq} q / {Hk} kv / {Hk} index heads, D 128, block 128, top-16",
+                   "seq_lens": p.lengths, "num_q_heads": Hq, "num_kv_heads": Hk, "head_dim": D,
+                   "block_size": 128, "topk_blocks": 16, "parallelism": "none (1 GPU)"},
+        "select_ms": round(sel_ms, 4),
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "fwd_bwd_ms": round(fb_ms, 4),
+        "fwd_bwd_counted_gflop": round(fb_flop / 1e9, 1),
+        "fwd_bwd_tflops": round(fb_tflops, 2),
+        "fwd_bwd_mfma_frac": round(fb_tflops / PEAK_BF16_TFLOPS, 4),
+        "fwd_tflops": round(fwd_flop / (fwd_ms * 1e-3) / 1e12, 2),
+        "select_gflop": round(sel_flop / 1e9, 2),
+        "select_algorithmic_mb": round(sel_bytes / 1e6, 2),
+        "select_hbm_gbs": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1),
+        "select_hbm_frac": round(sel_bytes / (sel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "select_binding_frac": round(max(sel_bytes / (PEAK_HBM_GBS * 1e9), sel_flop / (PEAK_BF16_TFLOPS * 1e12))
+                                     / (sel_ms * 1e-3), 4),
+        "kernels_avg_ms": kernels,
+        "roofline": roofline,
+        "context_gb300_ms": {"fwd_bwd": 6.7, "select": 0.62, "note": "pages' GB300 figures on unpublished 16k packs"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(p, args.cpu_stride)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -37,7 +37,8 @@ MSA_OP_BWD = 3
 
 # Every symbol include/msa.h declares.
 EXPORTED = ("msa_workspace_size", "msa_index_select", "msa_attn_fwd", "msa_attn_bwd",
-            "msa_status_string", "msa_check_cu_seqlens", "msa_version")
+            "msa_status_string", "msa_check_cu_seqlens", "msa_timing_enable", "msa_timing_collect",
+            "msa_version")
 
 
 class MsaDims(ctypes.Structure):
@@ -45,6 +46,10 @@ class MsaDims(ctypes.Structure):
                 ("max_seqlen", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("topk_blocks", ctypes.c_int32)]
+
+
+class MsaKernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_float)]
 
 
 class MsaError(RuntimeError):
@@ -89,6 +94,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.msa_status_string.restype = ctypes.c_char_p
     lib.msa_check_cu_seqlens.argtypes = [ctypes.POINTER(MsaDims), _P, _P]
     lib.msa_check_cu_seqlens.restype = _I32
+    lib.msa_timing_enable.argtypes = [_I32]
+    lib.msa_timing_enable.restype = _I32
+    lib.msa_timing_collect.argtypes = [ctypes.POINTER(MsaKernelTime), _I32, ctypes.POINTER(_I32)]
+    lib.msa_timing_collect.restype = _I32
     lib.msa_version.argtypes = []
     lib.msa_version.restype = _I32
     _lib = lib
@@ -226,6 +235,20 @@ def msa_check_cu_seqlens(cu_seqlens: torch.Tensor, total_tokens: int, max_seqlen
     """Debug check of the cu_seqlens contract (synchronizes the stream); returns the status."""
     dims = make_dims(total_tokens, cu_seqlens.numel() - 1, max_seqlen, num_q_heads, num_kv_heads)
     return int(load().msa_check_cu_seqlens(ctypes.byref(dims), _ptr(cu_seqlens), _stream(cu_seqlens)))
+
+
+def msa_timing_enable(enable: bool = True) -> None:
+    """Bracket every kernel launch with HIP events on its stream (see msa_timing_collect)."""
+    _check(load().msa_timing_enable(1 if enable else 0), "msa_timing_enable")
+
+
+def msa_timing_collect() -> dict:
+    """{kernel name: (launches, total ms)} since the previous collect; waits for the events."""
+    cap = 64
+    arr = (MsaKernelTime * cap)()
+    n = _I32(0)
+    _check(load().msa_timing_collect(arr, cap, ctypes.byref(n)), "msa_timing_collect")
+    return {arr[i].name.decode(): (int(arr[i].launches), float(arr[i].total_ms)) for i in range(n.value)}
 
 
 class MSAAttention(torch.autograd.Function):

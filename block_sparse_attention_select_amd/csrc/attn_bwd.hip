@@ -408,18 +408,30 @@ void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStr
   const int T = (int)z.T, Hk = (int)z.Hk, S = (int)z.S;
   const unsigned wgs_tok = (unsigned)((z.T * z.Hk + 3) / 4);
   launch_block_transpose(z, a.k, a.k_st, a.k_sh, a.cu, p, a.kt, st);
-  bwd_prep_kernel<<<wgs_tok, 256, 0, st>>>(a.o, a.o_st, a.o_sh, a.dO, a.do_st, a.do_sh, a.q, a.q_st, a.q_sh, T, Hk,
-                                           a.delta, a.qT, a.doT);
-  attn_bwd_dq_kernel<<<wgs_tok, 256, 0, st>>>(a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.kt,
-                                              a.dO, a.do_st, a.do_sh, a.lse, a.delta, a.blk_idx, a.cu, p.blkbase, S,
-                                              T, Hk, a.scale * kLog2e, a.scale, a.dq, a.dq_st, a.dq_sh);
-  attn_bwd_dkdv_kernel<<<dim3((unsigned)z.items_cap, (unsigned)Hk), 256, 0, st>>>(
-      a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.dO, a.do_st, a.do_sh, a.qT, a.doT, a.lse,
-      a.delta, a.blk_idx, a.cu, p.blkbase, p.blk_seq, p.itembase, p.totals, Hk, (int)z.chunk, (int)z.items_cap,
-      a.scale * kLog2e, a.item_count, a.part_dk, a.part_dv);
-  dkdv_reduce_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)Hk), 256, 0, st>>>(
-      a.part_dk, a.part_dv, a.item_count, p.itembase, p.blk_seq, p.blkbase, a.cu, p.totals, Hk, (int)z.items_cap,
-      a.scale, a.dk, a.dk_st, a.dk_sh, a.dv, a.dv_st, a.dv_sh);
+  {
+    KernelTimer timer("bwd_prep", st);
+    bwd_prep_kernel<<<wgs_tok, 256, 0, st>>>(a.o, a.o_st, a.o_sh, a.dO, a.do_st, a.do_sh, a.q, a.q_st, a.q_sh, T, Hk,
+                                             a.delta, a.qT, a.doT);
+  }
+  {
+    KernelTimer timer("attn_bwd_dq", st);
+    attn_bwd_dq_kernel<<<wgs_tok, 256, 0, st>>>(a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.kt,
+                                                a.dO, a.do_st, a.do_sh, a.lse, a.delta, a.blk_idx, a.cu, p.blkbase, S,
+                                                T, Hk, a.scale * kLog2e, a.scale, a.dq, a.dq_st, a.dq_sh);
+  }
+  {
+    KernelTimer timer("attn_bwd_dkdv", st);
+    attn_bwd_dkdv_kernel<<<dim3((unsigned)z.items_cap, (unsigned)Hk), 256, 0, st>>>(
+        a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.dO, a.do_st, a.do_sh, a.qT, a.doT, a.lse,
+        a.delta, a.blk_idx, a.cu, p.blkbase, p.blk_seq, p.itembase, p.totals, Hk, (int)z.chunk, (int)z.items_cap,
+        a.scale * kLog2e, a.item_count, a.part_dk, a.part_dv);
+  }
+  {
+    KernelTimer timer("dkdv_reduce", st);
+    dkdv_reduce_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)Hk), 256, 0, st>>>(
+        a.part_dk, a.part_dv, a.item_count, p.itembase, p.blk_seq, p.blkbase, a.cu, p.totals, Hk, (int)z.items_cap,
+        a.scale, a.dk, a.dk_st, a.dk_sh, a.dv, a.dv_st, a.dv_sh);
+  }
 }
 
 }  // namespace msa

@@ -167,8 +167,11 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
 
 void launch_block_transpose(const Sizes& z, const u16* x, int64_t st_t, int64_t st_h,
                             const int32_t* cu, const PlanBufs& p, u16* xt, hipStream_t st) {
-  block_transpose_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk), 256, 0, st>>>(
-      x, st_t, st_h, cu, p.blkbase, p.blk_seq, p.totals, (int)z.Hk, xt);
+  {
+    KernelTimer timer("block_transpose", st);
+    block_transpose_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk), 256, 0, st>>>(
+        x, st_t, st_h, cu, p.blkbase, p.blk_seq, p.totals, (int)z.Hk, xt);
+  }
 }
 
 void launch_attn_fwd(const Sizes& z, const u16* q, int64_t q_st, int64_t q_sh,
@@ -176,9 +179,12 @@ void launch_attn_fwd(const Sizes& z, const u16* q, int64_t q_st, int64_t q_sh,
                      const int32_t* blk_idx, const int32_t* cu, const PlanBufs& p, float scale,
                      u16* o, int64_t o_st, int64_t o_sh, float* lse, hipStream_t st) {
   const int64_t waves = z.T * z.Hk;
-  attn_fwd_kernel<<<dim3((unsigned)((waves + 3) / 4)), 256, 0, st>>>(
-      q, q_st, q_sh, k, k_st, k_sh, vt, blk_idx, cu, p.blkbase, (int)z.S, (int)z.T, (int)z.Hk,
-      scale * kLog2e, o, o_st, o_sh, lse);
+  {
+    KernelTimer timer("attn_fwd", st);
+    attn_fwd_kernel<<<dim3((unsigned)((waves + 3) / 4)), 256, 0, st>>>(
+        q, q_st, q_sh, k, k_st, k_sh, vt, blk_idx, cu, p.blkbase, (int)z.S, (int)z.T, (int)z.Hk,
+        scale * kLog2e, o, o_st, o_sh, lse);
+  }
 }
 
 }  // namespace msa

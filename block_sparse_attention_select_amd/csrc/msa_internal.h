@@ -98,6 +98,23 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ----------------------------------------------------------------------------
+// Optional per-kernel timing: while msa_timing_enable(1) is in force, a
+// KernelTimer records a HIP event pair around the launch it scopes.
+// ----------------------------------------------------------------------------
+class KernelTimer {
+ public:
+  KernelTimer(const char* name, hipStream_t st);
+  ~KernelTimer();
+  KernelTimer(const KernelTimer&) = delete;
+  KernelTimer& operator=(const KernelTimer&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t st_;
+  hipEvent_t start_ = nullptr;
+};
+
+// ----------------------------------------------------------------------------
 // Launchers (host functions, each defined next to its kernels).
 // ----------------------------------------------------------------------------
 void launch_plan(const int32_t* cu, const Sizes& z, const PlanBufs& p, hipStream_t st);

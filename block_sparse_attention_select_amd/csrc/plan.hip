@@ -69,7 +69,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 }  // namespace
 
 void launch_plan(const int32_t* cu, const Sizes& z, const PlanBufs& p, hipStream_t st) {
-  plan_kernel<<<1, kPlanThreads, 0, st>>>(cu, (int)z.S, (int)z.chunk, p.blkbase, p.blk_seq, p.itembase, p.totals);
+  {
+    KernelTimer timer("plan", st);
+    plan_kernel<<<1, kPlanThreads, 0, st>>>(cu, (int)z.S, (int)z.chunk, p.blkbase, p.blk_seq, p.itembase, p.totals);
+  }
 }
 
 }  // namespace msa

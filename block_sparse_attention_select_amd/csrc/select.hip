@@ -252,14 +252,23 @@ void launch_select(const Sizes& z, const u16* idx_q, int64_t sq_t, int64_t sq_h,
                    u16* qfeat, u16* kfeat, float* scores, int32_t* blk_idx, hipStream_t st) {
   const int T = (int)z.T, Hk = (int)z.Hk, S = (int)z.S;
   const int64_t waves_pro = z.T * z.Hk * 2;
-  select_prologue_kernel<<<dim3((unsigned)((waves_pro + 3) / 4)), 256, 0, st>>>(
-      idx_q, sq_t, sq_h, idx_k, sk_t, sk_h, w_q, w_k, eps, rope_base, cu, S, T, Hk, qfeat, kfeat);
+  {
+    KernelTimer timer("select_prologue", st);
+    select_prologue_kernel<<<dim3((unsigned)((waves_pro + 3) / 4)), 256, 0, st>>>(
+        idx_q, sq_t, sq_h, idx_k, sk_t, sk_h, w_q, w_k, eps, rope_base, cu, S, T, Hk, qfeat, kfeat);
+  }
   const unsigned kchunks = (unsigned)((z.nbmax + kKeyChunk - 1) / kKeyChunk);
-  select_scores_kernel<<<dim3((unsigned)z.nblk_cap, kchunks, (unsigned)Hk), 256, 0, st>>>(
-      qfeat, kfeat, cu, p.blkbase, p.blk_seq, p.totals, Hk, (int)z.nbmax, scores);
+  {
+    KernelTimer timer("select_scores", st);
+    select_scores_kernel<<<dim3((unsigned)z.nblk_cap, kchunks, (unsigned)Hk), 256, 0, st>>>(
+        qfeat, kfeat, cu, p.blkbase, p.blk_seq, p.totals, Hk, (int)z.nbmax, scores);
+  }
   const int64_t waves_top = z.T * z.Hk;
-  select_topk_kernel<<<dim3((unsigned)((waves_top + 3) / 4)), 256, 0, st>>>(scores, cu, S, T, Hk, (int)z.nbmax,
-                                                                           blk_idx);
+  {
+    KernelTimer timer("select_topk", st);
+    select_topk_kernel<<<dim3((unsigned)((waves_top + 3) / 4)), 256, 0, st>>>(scores, cu, S, T, Hk, (int)z.nbmax,
+                                                                             blk_idx);
+  }
 }
 
 }  // namespace msa

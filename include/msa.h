@@ -175,6 +175,25 @@ const char* msa_status_string(int status);
  */
 int msa_check_cu_seqlens(const msa_dims* dims, const int32_t* cu_seqlens, hipStream_t stream);
 
+/*
+ * Kernel timing, for benchmarks and profiling.  When enabled, every kernel the
+ * library launches is bracketed by a pair of HIP events recorded on the launch
+ * stream.  msa_timing_collect waits for the recorded events, then writes up to
+ * `capacity` per-kernel totals (launch count and summed milliseconds, kernels
+ * in first-launch order; `name` points to static storage) and the number
+ * written to *count, and forgets what it reported.  Timing adds two event
+ * records per launch; leave it off outside measurement.  Process-wide state,
+ * guarded by a mutex.
+ */
+typedef struct msa_kernel_time {
+  const char* name;
+  int32_t launches;
+  float total_ms;
+} msa_kernel_time;
+
+int msa_timing_enable(int enable);
+int msa_timing_collect(msa_kernel_time* out, int32_t capacity, int32_t* count);
+
 /* Library version, major * 10000 + minor * 100 + patch. */
 int msa_version(void);
 
