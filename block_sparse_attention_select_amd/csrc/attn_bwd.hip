@@ -15,15 +15,12 @@
 //                       ([d][16 heads]) used as MFMA operands by dK/dV;
 //   attn_bwd_dq_kernel  one wavefront per (token, KV head), the forward's
 //                       transposed-score layout (lane = head row);
-//   attn_bwd_dkdv_kernel one workgroup per (block, chunk of queries): the
-//                       selecting queries of the chunk are listed in token
-//                       order, then each wavefront accumulates 32 keys x 128
-//                       dims of dK and dV in registers, two tokens (32 rows)
-//                       per MFMA step; the chunk's sums go to a workspace
-//                       slice;
-//   dkdv_reduce_kernel  sums the slices of a block in chunk order (fixed
-//                       order, no atomics: bitwise deterministic) and writes
-//                       bf16 dK/dV with their own strides.
+//   attn_bwd_dkdv_kernel (attn_bwd_dkdv.hip) key-block-major dK/dV per chunk
+//                       of selecting queries;
+//   dkdv_reduce_kernel  sums the per-chunk slices of a block in chunk order
+//                       (fixed order, no atomics: bitwise deterministic) and
+//                       writes bf16 dK/dV with their own strides; blocks with a
+//                       single chunk were finished by the dK/dV kernel.
 #include "msa_internal.h"
 
 namespace msa {
@@ -167,8 +164,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kl = 32 * (kk >> 1) + 8 * g + 4 * (kk & 1) + r;
-        float p = exp2f(sacc[kk][r] * scale_log2 - lse2);
-        if (!live || (diag && kBlock * c + kl > pos)) p = 0.f;
+        const float e = fast_exp2(sacc[kk][r] * scale_log2 - lse2);
+        const float p = (!live || (diag && kBlock * c + kl > pos)) ? 0.f : e;
         sacc[kk][r] = p * (pacc[kk][r] - dl);
       }
     bf16x8 dsf[4];
@@ -179,190 +176,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        dqacc[dt] = mfma16x16x32(load_bf16x8(ktb + (16 * dt + li) * kBlock + 32 * ks + 8 * g), dsf[ks], dqacc[dt]);
+        dqacc[dt] = mfma16x16x32(load_bf16x8(ktb + ((dt * 4 + ks) * 64 + lane) * 8), dsf[ks], dqacc[dt]);
   }
   u16* out = dq + (int64_t)t * dq_st + (int64_t)hq * dq_sh;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<uint2*>(out + 16 * dt + 4 * g) = pack_bf16x4(dqacc[dt] * scale);
-}
-
-// ---------------------------------------------------------------------------
-// dK / dV per (work item, KV head).
-// ---------------------------------------------------------------------------
-constexpr int kMaxChunk = 4096;
-
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
-    const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
-    const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
-    const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
-    const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
-    const u16* __restrict__ qT, const u16* __restrict__ doT,
-    const float* __restrict__ lse, const float* __restrict__ delta,
-    const int32_t* __restrict__ blk_idx, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ blkbase, const int32_t* __restrict__ blk_seq,
-    const int32_t* __restrict__ itembase, const int32_t* __restrict__ totals,
-    int Hk, int chunk, int items_cap, float scale_log2,
-    int32_t* __restrict__ item_count, float* __restrict__ part_dk, float* __restrict__ part_dv) {
-  __shared__ int sel[kMaxChunk];
-  __shared__ int wcount[4];
-  const int item = blockIdx.x;
-  const int h = blockIdx.y;
-  if (item >= totals[1]) return;
-  const int nblk = totals[0];
-  const int gb = upper_index(itembase, nblk, item);
-  const int s = blk_seq[gb];
-  const int c = gb - blkbase[s];
-  const int kidx = item - itembase[gb];
-  const int seq0 = cu[s];
-  const int L = cu[s + 1] - seq0;
-  const int p_begin = kBlock * c + kidx * chunk;
-  const int p_end = min(p_begin + chunk, L);
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 4;
-  const int li = lane & 15;
-  const int Hq = Hk * kGroup;
-
-  // 1. list the queries of this chunk that selected block c, in token order
-  int nsel = 0;
-  for (int p0 = p_begin; p0 < p_end; p0 += 256) {
-    const int p = p0 + threadIdx.x;
-    bool hit = false;
-    if (p < p_end) {
-      const int4* ids = reinterpret_cast<const int4*>(blk_idx + ((int64_t)(seq0 + p) * Hk + h) * kTopk);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int4 x = ids[j];
-        hit |= (x.x == c) | (x.y == c) | (x.z == c) | (x.w == c);
-      }
-    }
-    const uint64_t m = __ballot(hit);
-    const int before = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) wcount[wave] = __popcll(m);
-    __syncthreads();
-    int off = nsel;
-    int tot = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      off += w < wave ? wcount[w] : 0;
-      tot += wcount[w];
-    }
-    if (hit) sel[off + before] = seq0 + p;
-    nsel += tot;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) item_count[(int64_t)h * items_cap + item] = nsel;
-  if (nsel == 0) return;
-
-  // 2. this wavefront's 32 keys of K and V as B operands (keys past the
-  //    sequence end are zero and always masked by causality)
-  const int kbase = kBlock * c + 32 * wave;
-  bf16x8 kf[2][4], vf[2][4];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int kp = kbase + 16 * kk + li;
-    const bool ok = kp < L;
-    const u16* krow = k + (int64_t)(seq0 + kp) * k_st + (int64_t)h * k_sh;
-    const u16* vrow = v + (int64_t)(seq0 + kp) * v_st + (int64_t)h * v_sh;
-#pragma unroll
-    for (int ds = 0; ds < 4; ++ds) {
-      kf[kk][ds] = ok ? load_bf16x8(krow + 32 * ds + 8 * g) : zero_bf16x8();
-      vf[kk][ds] = ok ? load_bf16x8(vrow + 32 * ds + 8 * g) : zero_bf16x8();
-    }
-  }
-  f32x4 dk[2][8], dv[2][8];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      dk[kk][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dv[kk][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-  // 3. two selecting tokens (32 query rows) per step
-  for (int n = 0; n < nsel; n += 2) {
-    const int toks[2] = {sel[n], n + 1 < nsel ? sel[n + 1] : -1};
-    f32x4 pv[2][2], dsv[2][2];
-#pragma unroll
-    for (int tk = 0; tk < 2; ++tk) {
-      const int t = toks[tk];
-      if (t < 0) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          pv[tk][kk] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dsv[tk][kk] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        continue;
-      }
-      const int pos_t = t - seq0;
-      const u16* qrow = q + (int64_t)t * q_st + (int64_t)(h * kGroup + li) * q_sh;
-      const u16* drow = dO + (int64_t)t * do_st + (int64_t)(h * kGroup + li) * do_sh;
-      bf16x8 qa[4], da[4];
-#pragma unroll
-      for (int ds = 0; ds < 4; ++ds) {
-        qa[ds] = load_bf16x8(qrow + 32 * ds + 8 * g);
-        da[ds] = load_bf16x8(drow + 32 * ds + 8 * g);
-      }
-      const float4 l4 = *reinterpret_cast<const float4*>(lse + (int64_t)t * Hq + h * kGroup + 4 * g);
-      const float4 d4 = *reinterpret_cast<const float4*>(delta + (int64_t)t * Hq + h * kGroup + 4 * g);
-      const float lr[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dr[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        f32x4 sa = {0.f, 0.f, 0.f, 0.f};
-        f32x4 pa = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ds = 0; ds < 4; ++ds) {
-          sa = mfma16x16x32(qa[ds], kf[kk][ds], sa);
-          pa = mfma16x16x32(da[ds], vf[kk][ds], pa);
-        }
-        const int kp = kbase + 16 * kk + li;
-        f32x4 pr, dsr;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool live = lr[r] > -INFINITY && kp <= pos_t;
-          const float p = live ? exp2f(sa[r] * scale_log2 - lr[r] * kLog2e) : 0.f;
-          pr[r] = p;
-          dsr[r] = p * (pa[r] - dr[r]);
-        }
-        pv[tk][kk] = pr;
-        dsv[tk][kk] = dsr;
-      }
-    }
-    bf16x8 pA[2], sA[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      pA[kk] = pack_bf16x8(pv[0][kk], pv[1][kk]);
-      sA[kk] = pack_bf16x8(dsv[0][kk], dsv[1][kk]);
-    }
-    const int64_t ta = ((int64_t)toks[0] * Hk + h) * (kHeadDim * kGroup);
-    const int64_t tb = toks[1] >= 0 ? ((int64_t)toks[1] * Hk + h) * (kHeadDim * kGroup) : ta;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int d = 16 * dt + li;
-      bf16x8 bdo = load_bf16x4x2(doT + ta + d * kGroup + 4 * g, doT + tb + d * kGroup + 4 * g);
-      bf16x8 bq = load_bf16x4x2(qT + ta + d * kGroup + 4 * g, qT + tb + d * kGroup + 4 * g);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        dv[kk][dt] = mfma16x16x32(pA[kk], bdo, dv[kk][dt]);
-        dk[kk][dt] = mfma16x16x32(sA[kk], bq, dk[kk][dt]);
-      }
-    }
-  }
-
-  // 4. this chunk's slice: part[h][item][key][d], key = 32w + 16kk + 4g + r, d = 16dt + li
-  const int64_t slice = ((int64_t)h * items_cap + item) * (kBlock * kHeadDim);
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = 32 * wave + 16 * kk + 4 * g + r;
-        const int64_t off = slice + (int64_t)key * kHeadDim + 16 * dt + li;
-        part_dk[off] = dk[kk][dt][r];
-        part_dv[off] = dv[kk][dt][r];
-      }
 }
 
 // ---------------------------------------------------------------------------
@@ -382,6 +200,7 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
   const int L = cu[s + 1] - seq0;
   const int i0 = itembase[gb];
   const int i1 = min(itembase[gb + 1], items_cap);
+  if (i1 - i0 == 1) return;  // a block with one work item was written by the dK/dV kernel itself
   for (int e = threadIdx.x * 4; e < kBlock * kHeadDim; e += 256 * 4) {
     const int key = e / kHeadDim;
     const int d = e - key * kHeadDim;
@@ -419,13 +238,7 @@ void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStr
                                                 a.dO, a.do_st, a.do_sh, a.lse, a.delta, a.blk_idx, a.cu, p.blkbase, S,
                                                 T, Hk, a.scale * kLog2e, a.scale, a.dq, a.dq_st, a.dq_sh);
   }
-  {
-    KernelTimer timer("attn_bwd_dkdv", st);
-    attn_bwd_dkdv_kernel<<<dim3((unsigned)z.items_cap, (unsigned)Hk), 256, 0, st>>>(
-        a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.dO, a.do_st, a.do_sh, a.qT, a.doT, a.lse,
-        a.delta, a.blk_idx, a.cu, p.blkbase, p.blk_seq, p.itembase, p.totals, Hk, (int)z.chunk, (int)z.items_cap,
-        a.scale * kLog2e, a.item_count, a.part_dk, a.part_dv);
-  }
+  launch_attn_bwd_dkdv(z, a, p, st);
   {
     KernelTimer timer("dkdv_reduce", st);
     dkdv_reduce_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)Hk), 256, 0, st>>>(

@@ -1,0 +1,293 @@
+// dK / dV of the block-sparse GQA attention, key-block-major, on gfx950.
+//
+// What is computed (radixark/miles PR #4581, kernel-tuning commit: the dK/dV
+// kernel of a KV head sums over that head's query heads, each partial written
+// to its own slice and the slices summed -- here in a fixed order):
+//     dv_j = sum P dO,   dk_j = scale * sum dS q
+// over every (query, head) of the group whose selected blocks include j's
+// block, with P = exp(scale q.k - LSE) and dS = P (dO.v - Delta).
+//
+// One workgroup per (global block, chunk of query positions, KV head).
+//   1. The chunk's queries that selected the block are listed in token order
+//      (wavefront ballots, so the list and every later sum are deterministic).
+//   2. Each of the 4 wavefronts keeps 32 keys of K and V as MFMA B operands
+//      and the 32 x 128 fp32 dK and dV sums in registers for the whole item.
+//   3. Selecting tokens stream through LDS four at a time (one per
+//      wavefront), double buffered: while the wavefronts compute on one
+//      buffer, each wavefront's next token sits in registers (global loads in
+//      flight) and is written to the other buffer after the compute; one
+//      LDS-only barrier per round.  Per token the stage holds q and dO laid
+//      out so each MFMA A operand is one contiguous 1 KB read, their
+//      [d][head] transposes (B operands of dK and dV, 512 contiguous bytes per
+//      read) and the token's 16 LSE and Delta values.
+//   4. Two tokens (32 query rows) per MFMA step: S = q K^T and dP = dO V^T
+//      (A from LDS, B from registers), then dV += P^T dO and dK += dS^T q
+//      with P and dS taken straight from the score registers.
+//   5. A block whose queries fit one chunk writes bf16 dK/dV itself; other
+//      blocks write fp32 slices that dkdv_reduce_kernel sums in chunk order.
+#include "msa_internal.h"
+
+namespace msa {
+
+namespace {
+
+constexpr int kBatch = 4;  // tokens per staging round, one loaded by each wavefront
+
+struct TokenRegs {  // one token's stage data in flight, 16 KB + 128 B per wavefront
+  u32x4 q0, q1, q2, q3, d0, d1, d2, d3, t0, t1, t2, t3, u0, u1, u2, u3;
+  float st;
+};
+
+__device__ __forceinline__ void fetch_token(TokenRegs& f, int t, int h, int Hk, int lane,
+                                            const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
+                                            const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
+                                            const u16* __restrict__ qT, const u16* __restrict__ doT,
+                                            const float* __restrict__ lse, const float* __restrict__ delta) {
+  const int li = lane & 15;
+  const int g = lane >> 4;
+  const u32x4* qr = reinterpret_cast<const u32x4*>(q + (int64_t)t * q_st + (int64_t)(h * kGroup + li) * q_sh + 8 * g);
+  const u32x4* dr = reinterpret_cast<const u32x4*>(dO + (int64_t)t * do_st + (int64_t)(h * kGroup + li) * do_sh + 8 * g);
+  f.q0 = qr[0]; f.q1 = qr[4]; f.q2 = qr[8]; f.q3 = qr[12];
+  f.d0 = dr[0]; f.d1 = dr[4]; f.d2 = dr[8]; f.d3 = dr[12];
+  const u32x4* qt4 = reinterpret_cast<const u32x4*>(qT + ((int64_t)t * Hk + h) * (kHeadDim * kGroup)) + lane;
+  const u32x4* dt4 = reinterpret_cast<const u32x4*>(doT + ((int64_t)t * Hk + h) * (kHeadDim * kGroup)) + lane;
+  f.t0 = qt4[0]; f.t1 = qt4[64]; f.t2 = qt4[128]; f.t3 = qt4[192];
+  f.u0 = dt4[0]; f.u1 = dt4[64]; f.u2 = dt4[128]; f.u3 = dt4[192];
+  const int64_t row = (int64_t)t * (Hk * kGroup) + h * kGroup;
+  f.st = lane < 16 ? lse[row + lane] : (lane < 32 ? delta[row + lane - 16] : 0.f);
+}
+
+// Stage layout of one token (u32x4 units): [0,256) q, [256,512) dO, each as
+// [ds][lane]; [512,768) q^T and [768,1024) dO^T as [d][16 heads].
+__device__ __forceinline__ void stage_token(const TokenRegs& f, u32x4* slot, float* stats, int lane) {
+  u32x4* p = slot + lane;
+  p[0] = f.q0; p[64] = f.q1; p[128] = f.q2; p[192] = f.q3;
+  p[256] = f.d0; p[320] = f.d1; p[384] = f.d2; p[448] = f.d3;
+  p[512] = f.t0; p[576] = f.t1; p[640] = f.t2; p[704] = f.t3;
+  p[768] = f.u0; p[832] = f.u1; p[896] = f.u2; p[960] = f.u3;
+  if (lane < 32) stats[lane] = f.st;
+}
+
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
+    const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
+    const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
+    const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
+    const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
+    const u16* __restrict__ qT, const u16* __restrict__ doT,
+    const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ blk_idx, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ blkbase, const int32_t* __restrict__ blk_seq,
+    const int32_t* __restrict__ itembase, const int32_t* __restrict__ totals,
+    int Hk, int chunk, int items_cap, float scale_log2, float scale,
+    int32_t* __restrict__ item_count, float* __restrict__ part_dk, float* __restrict__ part_dv,
+    u16* __restrict__ dk_out, int64_t dk_st, int64_t dk_sh, u16* __restrict__ dv_out, int64_t dv_st, int64_t dv_sh) {
+  __shared__ u32x4 stage[2][kBatch][1024];
+  __shared__ __align__(16) float stats[2][kBatch][32];
+  __shared__ int sel[kDkdvChunkMax];
+  __shared__ int wcount[4];
+
+  const int item = blockIdx.x;
+  const int h = blockIdx.y;
+  if (item >= totals[1]) return;
+  const int nblk = totals[0];
+  const int gb = upper_index(itembase, nblk, item);
+  const int s = blk_seq[gb];
+  const int c = gb - blkbase[s];
+  const int kidx = item - itembase[gb];
+  const bool single = itembase[gb + 1] - itembase[gb] == 1;
+  const int seq0 = cu[s];
+  const int L = cu[s + 1] - seq0;
+  const int p_begin = kBlock * c + kidx * chunk;
+  const int p_end = min(p_begin + chunk, L);
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int li = lane & 15;
+
+  // 1. the chunk's queries that selected block c, in token order
+  int nsel = 0;
+  for (int p0 = p_begin; p0 < p_end; p0 += 256) {
+    const int p = p0 + threadIdx.x;
+    bool hit = false;
+    if (p < p_end) {
+      const int4* ids = reinterpret_cast<const int4*>(blk_idx + ((int64_t)(seq0 + p) * Hk + h) * kTopk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int4 x = ids[j];
+        hit |= (x.x == c) | (x.y == c) | (x.z == c) | (x.w == c);
+      }
+    }
+    const uint64_t m = __ballot(hit);
+    const int before = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) wcount[wave] = __popcll(m);
+    __syncthreads();
+    int off = nsel;
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      off += w < wave ? wcount[w] : 0;
+      tot += wcount[w];
+    }
+    if (hit) sel[off + before] = seq0 + p;
+    nsel += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) item_count[(int64_t)h * items_cap + item] = nsel;
+
+  // 2. K and V of this wavefront's 32 keys as B operands (zero past the sequence end)
+  const int kbase = kBlock * c + 32 * wave;
+  bf16x8 kf[2][4], vf[2][4];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int kp = kbase + 16 * kk + li;
+    const bool ok = kp < L;
+    const u16* krow = k + (int64_t)(seq0 + kp) * k_st + (int64_t)h * k_sh + 8 * g;
+    const u16* vrow = v + (int64_t)(seq0 + kp) * v_st + (int64_t)h * v_sh + 8 * g;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      kf[kk][ds] = ok ? load_bf16x8(krow + 32 * ds) : zero_bf16x8();
+      vf[kk][ds] = ok ? load_bf16x8(vrow + 32 * ds) : zero_bf16x8();
+    }
+  }
+  f32x4 dk[2][8], dv[2][8];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      dk[kk][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dv[kk][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  // 3./4. stream the selecting tokens through LDS, two per MFMA step
+  if (nsel > 0) {
+    const int nbatch = (nsel + kBatch - 1) / kBatch;
+    TokenRegs f;
+    // slots past the end repeat the last token (finite operands, masked to zero)
+    fetch_token(f, sel[min(wave, nsel - 1)], h, Hk, lane, q, q_st, q_sh, dO, do_st, do_sh, qT, doT, lse, delta);
+    stage_token(f, stage[0][wave], stats[0][wave], lane);
+    lds_barrier();
+    for (int bi = 0; bi < nbatch; ++bi) {
+      const int cur = bi & 1;
+      const bool more = bi + 1 < nbatch;
+      if (more)
+        fetch_token(f, sel[min((bi + 1) * kBatch + wave, nsel - 1)], h, Hk, lane, q, q_st, q_sh, dO, do_st, do_sh,
+                    qT, doT, lse, delta);
+#pragma unroll
+      for (int pp = 0; pp < kBatch / 2; ++pp) {
+        const int n0 = bi * kBatch + 2 * pp;
+        if (n0 < nsel) {
+          const bool valid[2] = {true, n0 + 1 < nsel};
+          const int pos[2] = {sel[n0] - seq0, valid[1] ? sel[n0 + 1] - seq0 : 0};
+          const u32x4* b[2] = {stage[cur][2 * pp], stage[cur][2 * pp + 1]};
+          const float* st[2] = {stats[cur][2 * pp], stats[cur][2 * pp + 1]};
+
+          // S = q K^T and dP = dO V^T per token, turned at once into bf16 P and dS
+          // halves: lane (key li, group g) keeps rows 4g..4g+3 of each token.
+          f32x4 ph[2][2], sh[2][2];  // [kk][token]
+#pragma unroll
+          for (int tk = 0; tk < 2; ++tk) {
+            f32x4 sacc[2], pacc[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+              sacc[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+              pacc[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int ds = 0; ds < 4; ++ds) {
+              const bf16x8 qa = __builtin_bit_cast(bf16x8, b[tk][ds * 64 + lane]);
+              const bf16x8 da = __builtin_bit_cast(bf16x8, b[tk][256 + ds * 64 + lane]);
+#pragma unroll
+              for (int kk = 0; kk < 2; ++kk) {
+                sacc[kk] = mfma16x16x32(qa, kf[kk][ds], sacc[kk]);
+                pacc[kk] = mfma16x16x32(da, vf[kk][ds], pacc[kk]);
+              }
+            }
+            const float4 l4 = reinterpret_cast<const float4*>(st[tk])[g];
+            const float4 d4 = reinterpret_cast<const float4*>(st[tk] + 16)[g];
+            const float lr[4] = {l4.x, l4.y, l4.z, l4.w};
+            const float dr[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+              const int kp = kbase + 16 * kk + li;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const bool live = valid[tk] && lr[r] > -INFINITY && kp <= pos[tk];
+                const float e = fast_exp2(sacc[kk][r] * scale_log2 - lr[r] * kLog2e);
+                ph[kk][tk][r] = live ? e : 0.f;
+                sh[kk][tk][r] = live ? e * (pacc[kk][r] - dr[r]) : 0.f;
+              }
+            }
+          }
+          bf16x8 pA[2], sA[2];
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            pA[kk] = pack_bf16x8(ph[kk][0], ph[kk][1]);
+            sA[kk] = pack_bf16x8(sh[kk][0], sh[kk][1]);
+          }
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+            const int off = (16 * dt + li) * 4 + g;  // in uint2 units within a [d][16] tile
+            const uint2* qt0 = reinterpret_cast<const uint2*>(b[0] + 512);
+            const uint2* qt1 = reinterpret_cast<const uint2*>(b[1] + 512);
+            const uint2* dt0 = reinterpret_cast<const uint2*>(b[0] + 768);
+            const uint2* dt1 = reinterpret_cast<const uint2*>(b[1] + 768);
+            const uint2 a0 = dt0[off], a1 = dt1[off], c0 = qt0[off], c1 = qt1[off];
+            const bf16x8 bdo = __builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y});
+            const bf16x8 bq = __builtin_bit_cast(bf16x8, u32x4{c0.x, c0.y, c1.x, c1.y});
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+              dv[kk][dt] = mfma16x16x32(pA[kk], bdo, dv[kk][dt]);
+              dk[kk][dt] = mfma16x16x32(sA[kk], bq, dk[kk][dt]);
+            }
+          }
+        }
+      }
+      if (more) stage_token(f, stage[cur ^ 1][wave], stats[cur ^ 1][wave], lane);
+      lds_barrier();
+    }
+  }
+
+  // 5. results: lane holds key 32w + 16kk + 4g + r, dim 16dt + li
+  if (single) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kp = kbase + 16 * kk + 4 * g + r;
+        if (kp >= L) continue;
+        u16* dkr = dk_out + (int64_t)(seq0 + kp) * dk_st + (int64_t)h * dk_sh + li;
+        u16* dvr = dv_out + (int64_t)(seq0 + kp) * dv_st + (int64_t)h * dv_sh + li;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          dkr[16 * dt] = f2bf(dk[kk][dt][r] * scale);
+          dvr[16 * dt] = f2bf(dv[kk][dt][r]);
+        }
+      }
+  } else if (nsel > 0) {
+    const int64_t slice = ((int64_t)h * items_cap + item) * (kBlock * kHeadDim);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = 32 * wave + 16 * kk + 4 * g + r;
+          const int64_t off = slice + (int64_t)key * kHeadDim + 16 * dt + li;
+          part_dk[off] = dk[kk][dt][r];
+          part_dv[off] = dv[kk][dt][r];
+        }
+  }
+}
+
+}  // namespace
+
+void launch_attn_bwd_dkdv(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStream_t st) {
+  KernelTimer timer("attn_bwd_dkdv", st);
+  attn_bwd_dkdv_kernel<<<dim3((unsigned)z.items_cap, (unsigned)z.Hk), 256, 0, st>>>(
+      a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.dO, a.do_st, a.do_sh, a.qT, a.doT, a.lse,
+      a.delta, a.blk_idx, a.cu, p.blkbase, p.blk_seq, p.itembase, p.totals, (int)z.Hk, (int)z.chunk,
+      (int)z.items_cap, a.scale * kLog2e, a.scale, a.item_count, a.part_dk, a.part_dv, a.dk, a.dk_st, a.dk_sh, a.dv,
+      a.dv_st, a.dv_sh);
+}
+
+}  // namespace msa

@@ -19,14 +19,16 @@
 // and tile 2s+1 keys 32s + 8g + {4..7} in lane group g = lane / 16, so the
 // eight P values a lane owns are eight consecutive keys -- the same eight
 // consecutive keys the V^T operand reads.
-#include "msa_internal.h"
+#include "attn_stage.h"
 
 namespace msa {
 
 namespace {
 
-// Per-block transposed copy: xt[gb][h][d][key] (128 x 128 bf16), keys past the
-// end of the sequence zero-filled.
+// Per-block transposed copy in MFMA operand order: for global block gb and
+// KV head h, 32 runs of 64 lanes x 8 bf16, run dt*4 + ks, lane li + 16g holding
+// x[key = 32ks + 8g + 0..7][dim = 16dt + li] (keys past the sequence end are
+// zero).  This is the A operand of O^T = V^T P^T (and of dQ^T = K^T dS^T).
 __global__ __launch_bounds__(256) void block_transpose_kernel(const u16* __restrict__ x, int64_t st_t, int64_t st_h,
                                                               const int32_t* __restrict__ cu,
                                                               const int32_t* __restrict__ blkbase,
@@ -45,121 +47,216 @@ __global__ __launch_bounds__(256) void block_transpose_kernel(const u16* __restr
     const int key = i >> 4;
     const int ch = i & 15;
     const int kp = kBlock * c + key;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (kp < L) v = *reinterpret_cast<const uint4*>(x + (int64_t)(seq0 + kp) * st_t + (int64_t)h * st_h + ch * 8);
-    *reinterpret_cast<uint4*>(&tile[key][ch * 8]) = v;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (kp < L) v = *reinterpret_cast<const u32x4*>(x + (int64_t)(seq0 + kp) * st_t + (int64_t)h * st_h + ch * 8);
+    *reinterpret_cast<u32x4*>(&tile[key][ch * 8]) = v;
   }
   __syncthreads();
   u16* dst = xt + ((int64_t)gb * Hk + h) * (kHeadDim * kBlock);
-  for (int i = threadIdx.x; i < kHeadDim * 16; i += 256) {
-    const int d = i >> 4;
-    const int kc = i & 15;
+  for (int i = threadIdx.x; i < 32 * 64; i += 256) {
+    const int run = i >> 6;
+    const int lane = i & 63;
+    const int d = 16 * (run >> 2) + (lane & 15);
+    const int k0 = 32 * (run & 3) + 8 * (lane >> 4);
     uint32_t w[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = (uint32_t)tile[8 * kc + 2 * e][d] | ((uint32_t)tile[8 * kc + 2 * e + 1][d] << 16);
-    *reinterpret_cast<uint4*>(dst + d * kBlock + 8 * kc) = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)tile[k0 + 2 * e][d] | ((uint32_t)tile[k0 + 2 * e + 1][d] << 16);
+    *reinterpret_cast<u32x4*>(dst + (int64_t)i * 8) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
-__global__ __launch_bounds__(256) void attn_fwd_kernel(
+// ---------------------------------------------------------------------------
+// Forward.  One workgroup of 8 wavefronts per (tile of 16 consecutive tokens,
+// KV head); wavefront w owns tokens 2w and 2w+1 of the tile (their q as MFMA B
+// operands, their O accumulators and softmax state, all in registers).
+//   1. The union of the tile's selected blocks is built in LDS (a bitmap over
+//      the tile's global block range, compacted in ascending order).
+//   2. The workgroup walks that union.  Each block's K (A operand of
+//      S^T = K Q^T) and V^T (A operand of O^T = V^T P^T) are copied into one of
+//      two LDS buffers while the previous block is being used; every wavefront
+//      then updates those of its tokens that selected the block.  K and V are
+//      read from HBM/L2 once per tile instead of once per token.
+// ---------------------------------------------------------------------------
+constexpr int kTileTok = 16;
+constexpr int kFwdWaves = 8;
+constexpr int kUnionWords = 34;  // a tile's blocks span fewer than 34 * 32 global ids
+constexpr int kMaxUnion = kTileTok * kTopk;
+
+__global__ __launch_bounds__(512) void attn_fwd_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
     const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
     const u16* __restrict__ vt, const int32_t* __restrict__ blk_idx,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ blkbase, int S, int T, int Hk,
-    float scale_log2, u16* __restrict__ o, int64_t o_st, int64_t o_sh, float* __restrict__ lse) {
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ blkbase, const int32_t* __restrict__ blk_seq,
+    int S, int T, int Hk, float scale_log2, u16* __restrict__ o, int64_t o_st, int64_t o_sh,
+    float* __restrict__ lse) {
+  __shared__ u32x4 kbuf[2][32][64];
+  __shared__ u32x4 vbuf[2][32][64];
+  __shared__ uint32_t bitmap[kUnionWords];
+  __shared__ int ulist[kMaxUnion];
+  __shared__ int nunion;
+
+  const int h = blockIdx.y;
+  const int t0 = blockIdx.x * kTileTok;
+  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int li = lane & 15;
-  if (wave >= T * Hk) return;
-  const int t = wave / Hk;
-  const int h = wave - t * Hk;
-  const int s = find_seq(cu, S, t);
-  const int seq0 = cu[s];
-  const int pos = t - seq0;
-  const int b = pos / kBlock;
-  const int gb0 = blkbase[s];
-  const int my_blk = lane < kTopk ? blk_idx[(int64_t)wave * kTopk + lane] : -1;
 
-  const u16* qrow = q + (int64_t)t * q_st + (int64_t)(h * kGroup + li) * q_sh;
-  bf16x8 qb[4];
-#pragma unroll
-  for (int ds = 0; ds < 4; ++ds) qb[ds] = load_bf16x8(qrow + 32 * ds + 8 * g);
+  // this lane's (token, slot): token 2*wave + (g & 1), slot li
+  const int tj = 2 * wave + (g & 1);
+  const int t = t0 + tj;
+  const bool tvalid = t < T;
+  int s_t = 0, pos_t = 0, b_t = -1, my_gb = -1;
+  if (tvalid) {
+    s_t = find_seq(cu, S, t);
+    pos_t = t - cu[s_t];
+    b_t = pos_t / kBlock;
+    const int c = blk_idx[((int64_t)t * Hk + h) * kTopk + li];
+    if (c >= 0 && c <= b_t) my_gb = blkbase[s_t] + c;
+  }
+  const int gb_lo = blkbase[find_seq(cu, S, t0)];
 
-  f32x4 oacc[8];
+  // 1. union of the tile's blocks
+  if (threadIdx.x < kUnionWords) bitmap[threadIdx.x] = 0u;
+  __syncthreads();
+  if (g < 2 && my_gb >= 0 && my_gb - gb_lo < kUnionWords * 32)
+    atomicOr(&bitmap[(my_gb - gb_lo) >> 5], 1u << ((my_gb - gb_lo) & 31));
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t bits = lane < kUnionWords ? bitmap[lane] : 0u;
+    const int cnt = __popc(bits);
+    int incl = cnt;
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-
-  for (int i = 0; i < kTopk; ++i) {
-    const int c = __shfl(my_blk, i);
-    if (c < 0 || c > b) continue;
-    const int kstart = seq0 + kBlock * c;
-    const bool diag = (c == b);
-
-    f32x4 st[8];
-#pragma unroll
-    for (int kt = 0; kt < 8; ++kt) {
-      const int kl = 32 * (kt >> 1) + 8 * (li >> 2) + 4 * (kt & 1) + (li & 3);
-      const int kg = min(kstart + kl, T - 1);
-      const u16* krow = k + (int64_t)kg * k_st + (int64_t)h * k_sh;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ds = 0; ds < 4; ++ds) acc = mfma16x16x32(load_bf16x8(krow + 32 * ds + 8 * g), qb[ds], acc);
-      st[kt] = acc;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kl = 32 * (kt >> 1) + 8 * g + 4 * (kt & 1) + r;
-        float z = st[kt][r] * scale_log2;
-        if (diag && kBlock * c + kl > pos) z = -INFINITY;
-        st[kt][r] = z;
-        mx = fmaxf(mx, z);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    float rs = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(st[kt][r] - m_new);
-        st[kt][r] = p;
-        rs += p;
-      }
-    rs += __shfl_xor(rs, 16);
-    rs += __shfl_xor(rs, 32);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) oacc[dt] *= alpha;
+    int pos = incl - cnt;
+    while (bits) {
+      const int bit = __ffs(bits) - 1;
+      ulist[pos++] = gb_lo + 32 * lane + bit;
+      bits &= bits - 1u;
+    }
+    if (lane == 63) nunion = incl;
+  }
+  __syncthreads();
+  const int nu = nunion;
 
-    bf16x8 pf[4];
+  // per-token state (j = 0, 1 for tokens 2w, 2w+1)
+  int tok_t[2], tok_pos[2], tok_b[2], tok_base[2];
+  bool tok_ok[2];
+  bf16x8 qb[2][4];
+  f32x4 oacc[2][8];
+  float m_run[2], l_run[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) pf[ks] = pack_bf16x8(st[2 * ks], st[2 * ks + 1]);
-    const u16* vtb = vt + ((int64_t)(gb0 + c) * Hk + h) * (kHeadDim * kBlock);
+  for (int j = 0; j < 2; ++j) {
+    tok_t[j] = t0 + 2 * wave + j;
+    tok_ok[j] = tok_t[j] < T;
+    tok_pos[j] = __builtin_amdgcn_readlane(pos_t, 16 * j);
+    tok_b[j] = __builtin_amdgcn_readlane(b_t, 16 * j);
+    tok_base[j] = tok_ok[j] ? blkbase[__builtin_amdgcn_readlane(s_t, 16 * j)] : 0;
+    const u16* qrow = q + (int64_t)min(tok_t[j], T - 1) * q_st + (int64_t)(h * kGroup + li) * q_sh;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+    for (int ds = 0; ds < 4; ++ds) qb[j][ds] = tok_ok[j] ? load_bf16x8(qrow + 32 * ds + 8 * g) : zero_bf16x8();
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        oacc[dt] = mfma16x16x32(load_bf16x8(vtb + (16 * dt + li) * kBlock + 32 * ks + 8 * g), pf[ks], oacc[dt]);
+    for (int dt = 0; dt < 8; ++dt) oacc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.f;
   }
 
-  const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-  u16* orow = o + (int64_t)t * o_st + (int64_t)(h * kGroup + li) * o_sh;
+  // 2. walk the union, staging block u+1 while block u is used
+  auto stage = [&](int u, int buf) {
+    const int gb = ulist[u];
+    const int sb = blk_seq[gb];
+    const int kstart = cu[sb] + kBlock * (gb - blkbase[sb]);
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = pack_bf16x4(oacc[dt] * inv);
+    for (int ii = 0; ii < 8; ++ii) {
+      const int id = 8 * wave + ii;  // waves 0-3: K runs, waves 4-7: V^T runs
+      if (wave < 4) {
+        const int key = min(kstart + score_key(id >> 2, li), T - 1);
+        dma16(k + (int64_t)key * k_st + (int64_t)h * k_sh + 32 * (id & 3) + 8 * g, lds_offset(&kbuf[buf][id][0]));
+      } else {
+        const int run = id - 32;
+        dma16(vt + (((int64_t)gb * Hk + h) * 32 + run) * 512 + lane * 8, lds_offset(&vbuf[buf][run][0]));
+      }
+    }
+  };
+  if (nu > 0) stage(0, 0);
+  wait_copies();
+  wait_all_loads();
+  __syncthreads();
+
+  for (int u = 0; u < nu; ++u) {
+    const int buf = u & 1;
+    if (u + 1 < nu) stage(u + 1, buf ^ 1);
+    const int gb = ulist[u];
+    const uint64_t hits = __ballot(my_gb == gb);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (((hits >> (16 * j)) & 0xFFFFull) == 0) continue;
+      const int c = gb - tok_base[j];
+      const bool diag = (c == tok_b[j]);
+      f32x4 st[8];
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds)
+          acc = mfma16x16x32(__builtin_bit_cast(bf16x8, kbuf[buf][kt * 4 + ds][lane]), qb[j][ds], acc);
+        st[kt] = acc;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float z = st[kt][r] * scale_log2;
+          if (diag && kBlock * c + score_key(kt, 4 * g + r) > tok_pos[j]) z = -INFINITY;
+          st[kt][r] = z;
+          mx = fmaxf(mx, z);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[j], mx);
+      const float alpha = fast_exp2(m_run[j] - m_new);
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(st[kt][r] - m_new);
+          st[kt][r] = p;
+          rs += p;
+        }
+      rs += __shfl_xor(rs, 16);
+      rs += __shfl_xor(rs, 32);
+      l_run[j] = l_run[j] * alpha + rs;
+      m_run[j] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) oacc[j][dt] *= alpha;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) pf[ks] = pack_bf16x8(st[2 * ks], st[2 * ks + 1]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          oacc[j][dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, vbuf[buf][dt * 4 + ks][lane]), pf[ks], oacc[j][dt]);
+    }
+    wait_copies();
+    lds_barrier();
   }
-  if (g == 0) {
-    lse[(int64_t)t * (Hk * kGroup) + h * kGroup + li] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (!tok_ok[j]) continue;
+    const float inv = l_run[j] > 0.f ? 1.0f / l_run[j] : 0.f;
+    u16* orow = o + (int64_t)tok_t[j] * o_st + (int64_t)(h * kGroup + li) * o_sh;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = pack_bf16x4(oacc[j][dt] * inv);
+    if (g == 0)
+      lse[(int64_t)tok_t[j] * (Hk * kGroup) + h * kGroup + li] =
+          l_run[j] > 0.f ? (m_run[j] + __log2f(l_run[j])) * kLn2 : -INFINITY;
   }
 }
 
@@ -178,13 +275,11 @@ void launch_attn_fwd(const Sizes& z, const u16* q, int64_t q_st, int64_t q_sh,
                      const u16* k, int64_t k_st, int64_t k_sh, const u16* vt,
                      const int32_t* blk_idx, const int32_t* cu, const PlanBufs& p, float scale,
                      u16* o, int64_t o_st, int64_t o_sh, float* lse, hipStream_t st) {
-  const int64_t waves = z.T * z.Hk;
-  {
-    KernelTimer timer("attn_fwd", st);
-    attn_fwd_kernel<<<dim3((unsigned)((waves + 3) / 4)), 256, 0, st>>>(
-        q, q_st, q_sh, k, k_st, k_sh, vt, blk_idx, cu, p.blkbase, (int)z.S, (int)z.T, (int)z.Hk,
-        scale * kLog2e, o, o_st, o_sh, lse);
-  }
+  KernelTimer timer("attn_fwd", st);
+  const unsigned tiles = (unsigned)((z.T + kTileTok - 1) / kTileTok);
+  attn_fwd_kernel<<<dim3(tiles, (unsigned)z.Hk), 64 * kFwdWaves, 0, st>>>(
+      q, q_st, q_sh, k, k_st, k_sh, vt, blk_idx, cu, p.blkbase, p.blk_seq, (int)z.S, (int)z.T, (int)z.Hk,
+      scale * kLog2e, o, o_st, o_sh, lse);
 }
 
 }  // namespace msa

@@ -1,0 +1,52 @@
+// LDS staging helpers shared by the attention kernels (gfx950).
+//
+// Blocks of K, V and their transposes are copied global -> LDS with
+// global_load_lds_dwordx4: each of the 64 lanes of a wavefront reads 16 bytes
+// from its own global address and the hardware writes them to LDS at
+// M0 + 16 * lane, i.e. one contiguous 1 KB run per instruction.  Choosing each
+// lane's source address therefore lays the data out in LDS exactly as an MFMA
+// operand read wants it: operand (tile, step) of lane l sits at
+// stage[tile * steps + step][l], and every operand read is one conflict-free
+// ds_read_b128 of a contiguous 1 KB run.
+//
+// The copies are issued from inline assembly so that the compiler does not
+// pair them with the conservative "wait for every outstanding load" it would
+// otherwise place before each LDS read; the kernels instead wait explicitly
+// (vmcnt(0)) right before the barrier that publishes a staged block.
+#pragma once
+
+#include "msa_internal.h"
+
+namespace msa {
+
+// LDS byte offset of a __shared__ object (the low half of its flat address).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+// Copies 16 bytes from `src` (this lane) to LDS at lds_base + 16 * lane.
+// `lds_base` must be wavefront-uniform.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
+// Waits until every copy this wavefront issued has landed in LDS.
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Waits for every outstanding global load, visibly to the compiler (which
+// then knows registers loaded earlier need no further wait inside a loop).
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Key of row m of score tile kt (16 keys per tile, 8 tiles per block).  Tiles
+// 2s and 2s+1 together cover keys 32s..32s+31 such that the accumulator rows a
+// lane of group g holds (4g..4g+3 of each tile) are the eight consecutive keys
+// 32s + 8g .. 32s + 8g + 7 -- the k-range that lane supplies in the next
+// contraction over keys.
+__device__ __forceinline__ int score_key(int kt, int m) {
+  return 32 * (kt >> 1) + 8 * (m >> 2) + 4 * (kt & 1) + (m & 3);
+}
+
+}  // namespace msa

@@ -60,7 +60,7 @@ Sizes sizes_of(const msa_dims* d) {
   for (;;) {
     const int64_t items = z.nblk_cap + (z.T * z.max_seqlen / 256 + z.T) / chunk + 2;
     const int64_t bytes = items * z.Hk * msa::kBlock * msa::kHeadDim * 4 * 2;
-    if (bytes <= kPartialBudget || chunk >= 4096) {
+    if (bytes <= kPartialBudget || chunk >= msa::kDkdvChunkMax) {
       z.chunk = chunk;
       z.items_cap = items;
       break;

@@ -39,6 +39,9 @@ struct PlanBufs {
 // Device helpers
 // ----------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+// Native 16-byte vector: unlike HIP's uint4 (a union-based struct) it stays in
+// registers when copied around.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(u16 h) { return __uint_as_float(((uint32_t)h) << 16); }
@@ -93,6 +96,9 @@ __device__ __forceinline__ int upper_index(const int32_t* __restrict__ a, int n,
   }
   return lo;
 }
+
+// 2^x on the transcendental unit (v_exp_f32), branch-free; 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -156,5 +162,18 @@ struct BwdArgs {
 };
 
 void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStream_t st);
+void launch_attn_bwd_dkdv(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStream_t st);
+
+// Largest number of query positions in one dK/dV work item.
+constexpr int kDkdvChunkMax = 2048;
+
+// Barrier for LDS traffic only: waits for this wavefront's LDS operations,
+// then for every wavefront of the workgroup, without draining outstanding
+// global loads (prefetches stay in flight across it).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 }  // namespace msa
