@@ -13,15 +13,15 @@
 // Kernels:
 //   bwd_prep_kernel     Delta, plus per-token transposed copies of q and dO
 //                       ([d][16 heads]) used as MFMA operands by dK/dV;
-//   attn_bwd_dq_kernel  one wavefront per (token, KV head), the forward's
-//                       transposed-score layout (lane = head row);
+//   attn_bwd_dq_kernel  token-major dQ, tiles of 16 tokens walking the union
+//                       of their blocks with K, V and K^T staged in LDS;
 //   attn_bwd_dkdv_kernel (attn_bwd_dkdv.hip) key-block-major dK/dV per chunk
 //                       of selecting queries;
 //   dkdv_reduce_kernel  sums the per-chunk slices of a block in chunk order
 //                       (fixed order, no atomics: bitwise deterministic) and
 //                       writes bf16 dK/dV with their own strides; blocks with a
 //                       single chunk were finished by the dK/dV kernel.
-#include "msa_internal.h"
+#include "attn_stage.h"
 
 namespace msa {
 
@@ -73,114 +73,210 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
   if (active && quarter == 0) delta[(int64_t)t * (Hk * kGroup) + hq] = acc;
   __syncthreads();
   if (!active) return;
-  // each lane writes two d rows of 16 heads (2 x 32 bytes) of each tensor
+  // transposes in MFMA B-operand order: 8-byte entry (dt, lane = li + 16g)
+  // holds heads 4g..4g+3 of dim 16dt + li.
   const int64_t base = ((int64_t)t * Hk + h) * (kHeadDim * kGroup);
+  const int li = lane & 15;
+  const int g = lane >> 4;
 #pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int d = 2 * lane + rr;
-    uint32_t wq[8], wd[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      wq[e] = (uint32_t)tq[wl][d][2 * e] | ((uint32_t)tq[wl][d][2 * e + 1] << 16);
-      wd[e] = (uint32_t)tdo[wl][d][2 * e] | ((uint32_t)tdo[wl][d][2 * e + 1] << 16);
-    }
-    uint4* qdst = reinterpret_cast<uint4*>(qT + base + d * kGroup);
-    uint4* ddst = reinterpret_cast<uint4*>(doT + base + d * kGroup);
-    qdst[0] = make_uint4(wq[0], wq[1], wq[2], wq[3]);
-    qdst[1] = make_uint4(wq[4], wq[5], wq[6], wq[7]);
-    ddst[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-    ddst[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+  for (int dt = 0; dt < 8; ++dt) {
+    const int d = 16 * dt + li;
+    const uint2 wq = make_uint2((uint32_t)tq[wl][d][4 * g] | ((uint32_t)tq[wl][d][4 * g + 1] << 16),
+                                (uint32_t)tq[wl][d][4 * g + 2] | ((uint32_t)tq[wl][d][4 * g + 3] << 16));
+    const uint2 wd = make_uint2((uint32_t)tdo[wl][d][4 * g] | ((uint32_t)tdo[wl][d][4 * g + 1] << 16),
+                                (uint32_t)tdo[wl][d][4 * g + 2] | ((uint32_t)tdo[wl][d][4 * g + 3] << 16));
+    *reinterpret_cast<uint2*>(qT + base + (dt * 64 + lane) * 4) = wq;
+    *reinterpret_cast<uint2*>(doT + base + (dt * 64 + lane) * 4) = wd;
   }
 }
 
 // ---------------------------------------------------------------------------
-// dQ.  One wavefront per (token, KV head); lane = head row (li), as in the
-// forward.  dQ^T = K^T dS^T with K^T from the per-block transposed copy.
+// dQ.  Same tiling as the forward: one 8-wavefront workgroup per (tile of 16
+// consecutive tokens, KV head), wavefront w owning tokens 2w and 2w+1 (their
+// q and dO as MFMA B operands and their dQ^T accumulators in registers).  The
+// workgroup walks the union of the tile's selected blocks in halves of 64
+// keys; each half's K and V (A operands of S^T = K Q^T and dP^T = V dO^T) and
+// K^T (A operand of dQ^T = K^T dS^T) are copied into one of two LDS buffers
+// while the previous half is used.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
+constexpr int kTileTok = 16;
+constexpr int kDqWaves = 8;
+constexpr int kUnionWords = 34;
+constexpr int kMaxUnion = kTileTok * kTopk;
+
+__global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
     const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
     const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
     const u16* __restrict__ kt, const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
     const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ blk_idx, const int32_t* __restrict__ cu, const int32_t* __restrict__ blkbase,
-    int S, int T, int Hk, float scale_log2, float scale, u16* __restrict__ dq, int64_t dq_st, int64_t dq_sh) {
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int32_t* __restrict__ blk_seq, int S, int T, int Hk, float scale_log2, float scale,
+    u16* __restrict__ dq, int64_t dq_st, int64_t dq_sh) {
+  __shared__ u32x4 kbuf[2][16][64];
+  __shared__ u32x4 vbuf[2][16][64];
+  __shared__ u32x4 tbuf[2][16][64];
+  __shared__ uint32_t bitmap[kUnionWords];
+  __shared__ int ulist[kMaxUnion];
+  __shared__ int nunion;
+
+  const int h = blockIdx.y;
+  const int t0 = blockIdx.x * kTileTok;
+  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int li = lane & 15;
-  if (wave >= T * Hk) return;
-  const int t = wave / Hk;
-  const int h = wave - t * Hk;
-  const int s = find_seq(cu, S, t);
-  const int seq0 = cu[s];
-  const int pos = t - seq0;
-  const int b = pos / kBlock;
-  const int gb0 = blkbase[s];
-  const int my_blk = lane < kTopk ? blk_idx[(int64_t)wave * kTopk + lane] : -1;
-  const int hq = h * kGroup + li;
+  const int Hq = Hk * kGroup;
 
-  const u16* qrow = q + (int64_t)t * q_st + (int64_t)hq * q_sh;
-  const u16* drow = dO + (int64_t)t * do_st + (int64_t)hq * do_sh;
-  bf16x8 qb[4], db[4];
-#pragma unroll
-  for (int ds = 0; ds < 4; ++ds) {
-    qb[ds] = load_bf16x8(qrow + 32 * ds + 8 * g);
-    db[ds] = load_bf16x8(drow + 32 * ds + 8 * g);
+  const int tj = 2 * wave + (g & 1);
+  const int t = t0 + tj;
+  const bool tvalid = t < T;
+  int s_t = 0, pos_t = 0, b_t = -1, my_gb = -1;
+  if (tvalid) {
+    s_t = find_seq(cu, S, t);
+    pos_t = t - cu[s_t];
+    b_t = pos_t / kBlock;
+    const int c = blk_idx[((int64_t)t * Hk + h) * kTopk + li];
+    if (c >= 0 && c <= b_t) my_gb = blkbase[s_t] + c;
   }
-  const float l2 = lse[(int64_t)t * (Hk * kGroup) + hq];
-  const bool live = l2 > -INFINITY;
-  const float lse2 = live ? l2 * kLog2e : 0.f;
-  const float dl = delta[(int64_t)t * (Hk * kGroup) + hq];
+  const int gb_lo = blkbase[find_seq(cu, S, t0)];
 
-  f32x4 dqacc[8];
+  if (threadIdx.x < kUnionWords) bitmap[threadIdx.x] = 0u;
+  __syncthreads();
+  if (g < 2 && my_gb >= 0 && my_gb - gb_lo < kUnionWords * 32)
+    atomicOr(&bitmap[(my_gb - gb_lo) >> 5], 1u << ((my_gb - gb_lo) & 31));
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t bits = lane < kUnionWords ? bitmap[lane] : 0u;
+    const int cnt = __popc(bits);
+    int incl = cnt;
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) dqacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int i = 0; i < kTopk; ++i) {
-    const int c = __shfl(my_blk, i);
-    if (c < 0 || c > b) continue;
-    const int kstart = seq0 + kBlock * c;
-    const bool diag = (c == b);
-    f32x4 sacc[8], pacc[8];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int kl = 32 * (kk >> 1) + 8 * (li >> 2) + 4 * (kk & 1) + (li & 3);
-      const int kg = min(kstart + kl, T - 1);
-      const u16* krow = k + (int64_t)kg * k_st + (int64_t)h * k_sh;
-      const u16* vrow = v + (int64_t)kg * v_st + (int64_t)h * v_sh;
-      f32x4 a = {0.f, 0.f, 0.f, 0.f};
-      f32x4 bb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ds = 0; ds < 4; ++ds) {
-        a = mfma16x16x32(load_bf16x8(krow + 32 * ds + 8 * g), qb[ds], a);
-        bb = mfma16x16x32(load_bf16x8(vrow + 32 * ds + 8 * g), db[ds], bb);
-      }
-      sacc[kk] = a;
-      pacc[kk] = bb;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
     }
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kl = 32 * (kk >> 1) + 8 * g + 4 * (kk & 1) + r;
-        const float e = fast_exp2(sacc[kk][r] * scale_log2 - lse2);
-        const float p = (!live || (diag && kBlock * c + kl > pos)) ? 0.f : e;
-        sacc[kk][r] = p * (pacc[kk][r] - dl);
-      }
-    bf16x8 dsf[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) dsf[ks] = pack_bf16x8(sacc[2 * ks], sacc[2 * ks + 1]);
-    const u16* ktb = kt + ((int64_t)(gb0 + c) * Hk + h) * (kHeadDim * kBlock);
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        dqacc[dt] = mfma16x16x32(load_bf16x8(ktb + ((dt * 4 + ks) * 64 + lane) * 8), dsf[ks], dqacc[dt]);
+    int pos = incl - cnt;
+    while (bits) {
+      const int bit = __ffs(bits) - 1;
+      ulist[pos++] = gb_lo + 32 * lane + bit;
+      bits &= bits - 1u;
+    }
+    if (lane == 63) nunion = incl;
   }
-  u16* out = dq + (int64_t)t * dq_st + (int64_t)hq * dq_sh;
+  __syncthreads();
+  const int nsteps = 2 * nunion;  // halves of 64 keys
+
+  int tok_t[2], tok_pos[2], tok_b[2], tok_base[2];
+  bool tok_ok[2];
+  bf16x8 qb[2][4], db[2][4];
+  f32x4 dqacc[2][8];
+  float lse2[2], dl[2];
+  bool live[2];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<uint2*>(out + 16 * dt + 4 * g) = pack_bf16x4(dqacc[dt] * scale);
+  for (int j = 0; j < 2; ++j) {
+    tok_t[j] = t0 + 2 * wave + j;
+    tok_ok[j] = tok_t[j] < T;
+    tok_pos[j] = __builtin_amdgcn_readlane(pos_t, 16 * j);
+    tok_b[j] = __builtin_amdgcn_readlane(b_t, 16 * j);
+    tok_base[j] = tok_ok[j] ? blkbase[__builtin_amdgcn_readlane(s_t, 16 * j)] : 0;
+    const int tc = min(tok_t[j], T - 1);
+    const u16* qrow = q + (int64_t)tc * q_st + (int64_t)(h * kGroup + li) * q_sh;
+    const u16* drow = dO + (int64_t)tc * do_st + (int64_t)(h * kGroup + li) * do_sh;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      qb[j][ds] = tok_ok[j] ? load_bf16x8(qrow + 32 * ds + 8 * g) : zero_bf16x8();
+      db[j][ds] = tok_ok[j] ? load_bf16x8(drow + 32 * ds + 8 * g) : zero_bf16x8();
+    }
+    const float l2 = lse[(int64_t)tc * Hq + h * kGroup + li];
+    live[j] = tok_ok[j] && l2 > -INFINITY;
+    lse2[j] = live[j] ? l2 * kLog2e : 0.f;
+    dl[j] = delta[(int64_t)tc * Hq + h * kGroup + li];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) dqacc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // step w: block ulist[w / 2], keys 64 * (w & 1) .. +63
+  auto stage = [&](int w, int buf) {
+    const int gb = ulist[w >> 1];
+    const int half = w & 1;
+    const int sb = blk_seq[gb];
+    const int kstart = cu[sb] + kBlock * (gb - blkbase[sb]);
+#pragma unroll
+    for (int ii = 0; ii < 6; ++ii) {
+      const int id = 6 * wave + ii;
+      if (id < 32) {  // K (id < 16) or V runs: local tile kt' = r >> 2, step ds = r & 3
+        const int r = id & 15;
+        const int key = min(kstart + score_key(4 * half + (r >> 2), li), T - 1);
+        if (id < 16)
+          dma16(k + (int64_t)key * k_st + (int64_t)h * k_sh + 32 * (r & 3) + 8 * g, lds_offset(&kbuf[buf][r][0]));
+        else
+          dma16(v + (int64_t)key * v_st + (int64_t)h * v_sh + 32 * (r & 3) + 8 * g, lds_offset(&vbuf[buf][r][0]));
+      } else {  // K^T runs dt * 4 + 2 * half + ks' -> local run dt * 2 + ks'
+        const int r = id - 32;
+        const int run = (r >> 1) * 4 + 2 * half + (r & 1);
+        dma16(kt + (((int64_t)gb * Hk + h) * 32 + run) * 512 + lane * 8, lds_offset(&tbuf[buf][r][0]));
+      }
+    }
+  };
+  if (nsteps > 0) stage(0, 0);
+  wait_copies();
+  wait_all_loads();
+  __syncthreads();
+
+  for (int w = 0; w < nsteps; ++w) {
+    const int buf = w & 1;
+    if (w + 1 < nsteps) stage(w + 1, buf ^ 1);
+    const int gb = ulist[w >> 1];
+    const int half = w & 1;
+    const uint64_t hits = __ballot(my_gb == gb);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (((hits >> (16 * j)) & 0xFFFFull) == 0) continue;
+      const int c = gb - tok_base[j];
+      const bool diag = (c == tok_b[j]);
+      const int key0 = kBlock * c + 64 * half;
+      if (diag && key0 > tok_pos[j]) continue;  // the whole half lies after the query
+      f32x4 sacc[4], pacc[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        f32x4 bb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds) {
+          a = mfma16x16x32(__builtin_bit_cast(bf16x8, kbuf[buf][kk * 4 + ds][lane]), qb[j][ds], a);
+          bb = mfma16x16x32(__builtin_bit_cast(bf16x8, vbuf[buf][kk * 4 + ds][lane]), db[j][ds], bb);
+        }
+        sacc[kk] = a;
+        pacc[kk] = bb;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = key0 + score_key(kk, 4 * g + r);
+          const float e = fast_exp2(sacc[kk][r] * scale_log2 - lse2[j]);
+          const bool on = live[j] && !(diag && key > tok_pos[j]);
+          sacc[kk][r] = on ? e * (pacc[kk][r] - dl[j]) : 0.f;
+        }
+      const bf16x8 dsf0 = pack_bf16x8(sacc[0], sacc[1]);
+      const bf16x8 dsf1 = pack_bf16x8(sacc[2], sacc[3]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        dqacc[j][dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, tbuf[buf][dt * 2][lane]), dsf0, dqacc[j][dt]);
+        dqacc[j][dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, tbuf[buf][dt * 2 + 1][lane]), dsf1, dqacc[j][dt]);
+      }
+    }
+    wait_copies();
+    lds_barrier();
+  }
+
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (!tok_ok[j]) continue;
+    u16* out = dq + (int64_t)tok_t[j] * dq_st + (int64_t)(h * kGroup + li) * dq_sh;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<uint2*>(out + 16 * dt + 4 * g) = pack_bf16x4(dqacc[j][dt] * scale);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -188,8 +284,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
     const float* __restrict__ part_dk, const float* __restrict__ part_dv, const int32_t* __restrict__ item_count,
-    const int32_t* __restrict__ itembase, const int32_t* __restrict__ blk_seq, const int32_t* __restrict__ blkbase,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ totals, int Hk, int items_cap, float scale,
+    const int32_t* __restrict__ seqitem, const int32_t* __restrict__ blk_seq, const int32_t* __restrict__ blkbase,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ totals, int Hk, int chunk, int items_cap, float scale,
     u16* __restrict__ dk, int64_t dk_st, int64_t dk_sh, u16* __restrict__ dv, int64_t dv_st, int64_t dv_sh) {
   const int gb = blockIdx.x;
   const int h = blockIdx.y;
@@ -198,9 +294,10 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
   const int c = gb - blkbase[s];
   const int seq0 = cu[s];
   const int L = cu[s + 1] - seq0;
-  const int i0 = itembase[gb];
-  const int i1 = min(itembase[gb + 1], items_cap);
-  if (i1 - i0 == 1) return;  // a block with one work item was written by the dK/dV kernel itself
+  const int nch = (L + chunk - 1) / chunk;
+  const int jmin = (kBlock * c) / chunk;
+  if (jmin == nch - 1) return;  // a block with one work item was written by the dK/dV kernel itself
+  const int item0 = seqitem[s];
   for (int e = threadIdx.x * 4; e < kBlock * kHeadDim; e += 256 * 4) {
     const int key = e / kHeadDim;
     const int d = e - key * kHeadDim;
@@ -208,13 +305,18 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
     if (kp >= L) continue;
     f32x4 adk = {0.f, 0.f, 0.f, 0.f};
     f32x4 adv = {0.f, 0.f, 0.f, 0.f};
-    for (int it = i0; it < i1; ++it) {
+    int base = 0;  // items of the chunks before j
+    for (int j = 0; j < nch; ++j) {
+      const int cnt = (min((j + 1) * chunk, L) - 1) / kBlock + 1;
+      const int it = item0 + base + c;
+      base += cnt;
+      if (j < jmin || it >= items_cap) continue;
       if (item_count[(int64_t)h * items_cap + it] == 0) continue;
       const int64_t off = ((int64_t)h * items_cap + it) * (kBlock * kHeadDim) + e;
-      const float4 a = *reinterpret_cast<const float4*>(part_dk + off);
-      const float4 b = *reinterpret_cast<const float4*>(part_dv + off);
-      adk += f32x4{a.x, a.y, a.z, a.w};
-      adv += f32x4{b.x, b.y, b.z, b.w};
+      const f32x4 pa = *reinterpret_cast<const f32x4*>(part_dk + off);
+      const f32x4 pb = *reinterpret_cast<const f32x4*>(part_dv + off);
+      adk += pa;
+      adv += pb;
     }
     *reinterpret_cast<uint2*>(dk + (int64_t)(seq0 + kp) * dk_st + (int64_t)h * dk_sh + d) = pack_bf16x4(adk * scale);
     *reinterpret_cast<uint2*>(dv + (int64_t)(seq0 + kp) * dv_st + (int64_t)h * dv_sh + d) = pack_bf16x4(adv);
@@ -234,16 +336,16 @@ void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStr
   }
   {
     KernelTimer timer("attn_bwd_dq", st);
-    attn_bwd_dq_kernel<<<wgs_tok, 256, 0, st>>>(a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.kt,
-                                                a.dO, a.do_st, a.do_sh, a.lse, a.delta, a.blk_idx, a.cu, p.blkbase, S,
-                                                T, Hk, a.scale * kLog2e, a.scale, a.dq, a.dq_st, a.dq_sh);
+    attn_bwd_dq_kernel<<<dim3((unsigned)((z.T + kTileTok - 1) / kTileTok), (unsigned)Hk), 64 * kDqWaves, 0, st>>>(
+        a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.kt, a.dO, a.do_st, a.do_sh, a.lse, a.delta,
+        a.blk_idx, a.cu, p.blkbase, p.blk_seq, S, T, Hk, a.scale * kLog2e, a.scale, a.dq, a.dq_st, a.dq_sh);
   }
   launch_attn_bwd_dkdv(z, a, p, st);
   {
     KernelTimer timer("dkdv_reduce", st);
     dkdv_reduce_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)Hk), 256, 0, st>>>(
-        a.part_dk, a.part_dv, a.item_count, p.itembase, p.blk_seq, p.blkbase, a.cu, p.totals, Hk, (int)z.items_cap,
-        a.scale, a.dk, a.dk_st, a.dk_sh, a.dv, a.dv_st, a.dv_sh);
+        a.part_dk, a.part_dv, a.item_count, p.seqitem, p.blk_seq, p.blkbase, a.cu, p.totals, Hk, (int)z.chunk,
+        (int)z.items_cap, a.scale, a.dk, a.dk_st, a.dk_sh, a.dv, a.dv_st, a.dv_sh);
   }
 }
 

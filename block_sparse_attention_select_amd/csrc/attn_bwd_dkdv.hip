@@ -7,25 +7,28 @@
 // over every (query, head) of the group whose selected blocks include j's
 // block, with P = exp(scale q.k - LSE) and dS = P (dO.v - Delta).
 //
-// One workgroup per (global block, chunk of query positions, KV head).
+// One workgroup per (work item, KV head); a work item is one chunk of query
+// positions of a sequence paired with one block those queries may select (the
+// plan orders items by chunk, so concurrent workgroups share their queries in
+// L2).
 //   1. The chunk's queries that selected the block are listed in token order
 //      (wavefront ballots, so the list and every later sum are deterministic).
 //   2. Each of the 4 wavefronts keeps 32 keys of K and V as MFMA B operands
 //      and the 32 x 128 fp32 dK and dV sums in registers for the whole item.
 //   3. Selecting tokens stream through LDS four at a time (one per
-//      wavefront), double buffered: while the wavefronts compute on one
-//      buffer, each wavefront's next token sits in registers (global loads in
-//      flight) and is written to the other buffer after the compute; one
-//      LDS-only barrier per round.  Per token the stage holds q and dO laid
+//      wavefront), double buffered with global_load_lds copies issued while
+//      the previous four are used.  Per token the stage holds q and dO laid
 //      out so each MFMA A operand is one contiguous 1 KB read, their
-//      [d][head] transposes (B operands of dK and dV, 512 contiguous bytes per
-//      read) and the token's 16 LSE and Delta values.
+//      [d][head] transposes (B operands of dK and dV, prepared by
+//      bwd_prep_kernel in operand order: 512 contiguous bytes per read) and the
+//      token's 16 LSE and Delta values.
 //   4. Two tokens (32 query rows) per MFMA step: S = q K^T and dP = dO V^T
 //      (A from LDS, B from registers), then dV += P^T dO and dK += dS^T q
 //      with P and dS taken straight from the score registers.
-//   5. A block whose queries fit one chunk writes bf16 dK/dV itself; other
-//      blocks write fp32 slices that dkdv_reduce_kernel sums in chunk order.
-#include "msa_internal.h"
+//   5. A block whose selecting queries all lie in one chunk writes bf16 dK/dV
+//      itself; other blocks write fp32 slices that dkdv_reduce_kernel sums in
+//      chunk order.
+#include "attn_stage.h"
 
 namespace msa {
 
@@ -33,39 +36,34 @@ namespace {
 
 constexpr int kBatch = 4;  // tokens per staging round, one loaded by each wavefront
 
-struct TokenRegs {  // one token's stage data in flight, 16 KB + 128 B per wavefront
-  u32x4 q0, q1, q2, q3, d0, d1, d2, d3, t0, t1, t2, t3, u0, u1, u2, u3;
-  float st;
-};
-
-__device__ __forceinline__ void fetch_token(TokenRegs& f, int t, int h, int Hk, int lane,
+// Stage layout of one token (u32x4 units): [0,256) q and [256,512) dO as
+// [ds][lane]; [512,768) q^T and [768,1024) dO^T as [dt][lane] pairs of 8-byte
+// entries (straight copies of the prepared transposes); stats: 16 LSE then 16
+// Delta values.  Wavefront w copies token w of a round: 16 runs of 1 KB and
+// one 128-byte run.
+__device__ __forceinline__ void stage_token(int t, int h, int Hk, int lane, uint32_t slot_lds, uint32_t stats_lds,
                                             const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
                                             const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
                                             const u16* __restrict__ qT, const u16* __restrict__ doT,
                                             const float* __restrict__ lse, const float* __restrict__ delta) {
   const int li = lane & 15;
   const int g = lane >> 4;
-  const u32x4* qr = reinterpret_cast<const u32x4*>(q + (int64_t)t * q_st + (int64_t)(h * kGroup + li) * q_sh + 8 * g);
-  const u32x4* dr = reinterpret_cast<const u32x4*>(dO + (int64_t)t * do_st + (int64_t)(h * kGroup + li) * do_sh + 8 * g);
-  f.q0 = qr[0]; f.q1 = qr[4]; f.q2 = qr[8]; f.q3 = qr[12];
-  f.d0 = dr[0]; f.d1 = dr[4]; f.d2 = dr[8]; f.d3 = dr[12];
-  const u32x4* qt4 = reinterpret_cast<const u32x4*>(qT + ((int64_t)t * Hk + h) * (kHeadDim * kGroup)) + lane;
-  const u32x4* dt4 = reinterpret_cast<const u32x4*>(doT + ((int64_t)t * Hk + h) * (kHeadDim * kGroup)) + lane;
-  f.t0 = qt4[0]; f.t1 = qt4[64]; f.t2 = qt4[128]; f.t3 = qt4[192];
-  f.u0 = dt4[0]; f.u1 = dt4[64]; f.u2 = dt4[128]; f.u3 = dt4[192];
-  const int64_t row = (int64_t)t * (Hk * kGroup) + h * kGroup;
-  f.st = lane < 16 ? lse[row + lane] : (lane < 32 ? delta[row + lane - 16] : 0.f);
-}
-
-// Stage layout of one token (u32x4 units): [0,256) q, [256,512) dO, each as
-// [ds][lane]; [512,768) q^T and [768,1024) dO^T as [d][16 heads].
-__device__ __forceinline__ void stage_token(const TokenRegs& f, u32x4* slot, float* stats, int lane) {
-  u32x4* p = slot + lane;
-  p[0] = f.q0; p[64] = f.q1; p[128] = f.q2; p[192] = f.q3;
-  p[256] = f.d0; p[320] = f.d1; p[384] = f.d2; p[448] = f.d3;
-  p[512] = f.t0; p[576] = f.t1; p[640] = f.t2; p[704] = f.t3;
-  p[768] = f.u0; p[832] = f.u1; p[896] = f.u2; p[960] = f.u3;
-  if (lane < 32) stats[lane] = f.st;
+  const u16* qr = q + (int64_t)t * q_st + (int64_t)(h * kGroup + li) * q_sh + 8 * g;
+  const u16* dr = dO + (int64_t)t * do_st + (int64_t)(h * kGroup + li) * do_sh + 8 * g;
+  const u16* qt = qT + ((int64_t)t * Hk + h) * (kHeadDim * kGroup) + 8 * lane;
+  const u16* dt = doT + ((int64_t)t * Hk + h) * (kHeadDim * kGroup) + 8 * lane;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    dma16(qr + 32 * i, slot_lds + i * 1024);
+    dma16(dr + 32 * i, slot_lds + 4096 + i * 1024);
+    dma16(qt + 512 * i, slot_lds + 8192 + i * 1024);
+    dma16(dt + 512 * i, slot_lds + 12288 + i * 1024);
+  }
+  if (lane < 32) {
+    const int64_t row = (int64_t)t * (Hk * kGroup) + h * kGroup;
+    const float* src = lane < 16 ? lse + row + lane : delta + row + lane - 16;
+    dma4(src, stats_lds);
+  }
 }
 
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
@@ -77,8 +75,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ blk_idx, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ blkbase, const int32_t* __restrict__ blk_seq,
-    const int32_t* __restrict__ itembase, const int32_t* __restrict__ totals,
-    int Hk, int chunk, int items_cap, float scale_log2, float scale,
+    const int32_t* __restrict__ seqitem, const int32_t* __restrict__ totals,
+    int S, int Hk, int chunk, int items_cap, float scale_log2, float scale,
     int32_t* __restrict__ item_count, float* __restrict__ part_dk, float* __restrict__ part_dv,
     u16* __restrict__ dk_out, int64_t dk_st, int64_t dk_sh, u16* __restrict__ dv_out, int64_t dv_st, int64_t dv_sh) {
   __shared__ u32x4 stage[2][kBatch][1024];
@@ -89,16 +87,24 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const int item = blockIdx.x;
   const int h = blockIdx.y;
   if (item >= totals[1]) return;
-  const int nblk = totals[0];
-  const int gb = upper_index(itembase, nblk, item);
-  const int s = blk_seq[gb];
-  const int c = gb - blkbase[s];
-  const int kidx = item - itembase[gb];
-  const bool single = itembase[gb + 1] - itembase[gb] == 1;
+  // decode (sequence, query chunk j, block c) from the item index
+  const int s = upper_index(seqitem, S, item);
   const int seq0 = cu[s];
   const int L = cu[s + 1] - seq0;
-  const int p_begin = kBlock * c + kidx * chunk;
-  const int p_end = min(p_begin + chunk, L);
+  const int nch = (L + chunk - 1) / chunk;
+  int r = item - seqitem[s];
+  int j = 0;
+  for (;;) {
+    const int cnt = (min((j + 1) * chunk, L) - 1) / kBlock + 1;
+    if (r < cnt) break;
+    r -= cnt;
+    ++j;
+  }
+  const int c = r;
+  const int jmin = (kBlock * c) / chunk;
+  const bool single = (j == nch - 1) && (j == jmin);
+  const int p_begin = max(j * chunk, kBlock * c);
+  const int p_end = min((j + 1) * chunk, L);
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
@@ -112,8 +118,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     if (p < p_end) {
       const int4* ids = reinterpret_cast<const int4*>(blk_idx + ((int64_t)(seq0 + p) * Hk + h) * kTopk);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int4 x = ids[j];
+      for (int jj = 0; jj < 4; ++jj) {
+        const int4 x = ids[jj];
         hit |= (x.x == c) | (x.y == c) | (x.z == c) | (x.w == c);
       }
     }
@@ -161,17 +167,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   // 3./4. stream the selecting tokens through LDS, two per MFMA step
   if (nsel > 0) {
     const int nbatch = (nsel + kBatch - 1) / kBatch;
-    TokenRegs f;
     // slots past the end repeat the last token (finite operands, masked to zero)
-    fetch_token(f, sel[min(wave, nsel - 1)], h, Hk, lane, q, q_st, q_sh, dO, do_st, do_sh, qT, doT, lse, delta);
-    stage_token(f, stage[0][wave], stats[0][wave], lane);
-    lds_barrier();
+    auto stage_round = [&](int bi, int buf) {
+      stage_token(sel[min(bi * kBatch + wave, nsel - 1)], h, Hk, lane, lds_offset(&stage[buf][wave][0]),
+                  lds_offset(&stats[buf][wave][0]), q, q_st, q_sh, dO, do_st, do_sh, qT, doT, lse, delta);
+    };
+    stage_round(0, 0);
+    wait_copies();
+    wait_all_loads();
+    __syncthreads();
     for (int bi = 0; bi < nbatch; ++bi) {
       const int cur = bi & 1;
-      const bool more = bi + 1 < nbatch;
-      if (more)
-        fetch_token(f, sel[min((bi + 1) * kBatch + wave, nsel - 1)], h, Hk, lane, q, q_st, q_sh, dO, do_st, do_sh,
-                    qT, doT, lse, delta);
+      if (bi + 1 < nbatch) stage_round(bi + 1, cur ^ 1);
 #pragma unroll
       for (int pp = 0; pp < kBatch / 2; ++pp) {
         const int n0 = bi * kBatch + 2 * pp;
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
           }
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) {
-            const int off = (16 * dt + li) * 4 + g;  // in uint2 units within a [d][16] tile
+            const int off = dt * 64 + lane;  // 8-byte entry of a [dt][lane] transpose run
             const uint2* qt0 = reinterpret_cast<const uint2*>(b[0] + 512);
             const uint2* qt1 = reinterpret_cast<const uint2*>(b[1] + 512);
             const uint2* dt0 = reinterpret_cast<const uint2*>(b[0] + 768);
@@ -242,7 +249,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
           }
         }
       }
-      if (more) stage_token(f, stage[cur ^ 1][wave], stats[cur ^ 1][wave], lane);
+      wait_copies();
       lds_barrier();
     }
   }
@@ -285,7 +292,7 @@ void launch_attn_bwd_dkdv(const Sizes& z, const BwdArgs& a, const PlanBufs& p, h
   KernelTimer timer("attn_bwd_dkdv", st);
   attn_bwd_dkdv_kernel<<<dim3((unsigned)z.items_cap, (unsigned)z.Hk), 256, 0, st>>>(
       a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.dO, a.do_st, a.do_sh, a.qT, a.doT, a.lse,
-      a.delta, a.blk_idx, a.cu, p.blkbase, p.blk_seq, p.itembase, p.totals, (int)z.Hk, (int)z.chunk,
+      a.delta, a.blk_idx, a.cu, p.blkbase, p.blk_seq, p.seqitem, p.totals, (int)z.S, (int)z.Hk, (int)z.chunk,
       (int)z.items_cap, a.scale * kLog2e, a.scale, a.item_count, a.part_dk, a.part_dv, a.dk, a.dk_st, a.dk_sh, a.dv,
       a.dv_st, a.dv_sh);
 }

@@ -33,6 +33,14 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// Copies 4 bytes from `src` (this lane) to LDS at lds_base + 4 * lane.
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
 // Waits until every copy this wavefront issued has landed in LDS.
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

@@ -54,11 +54,16 @@ Sizes sizes_of(const msa_dims* d) {
   if (cap > z.T) cap = z.T;
   if (cap < 1) cap = 1;
   z.nblk_cap = cap;
-  // dK/dV work items: block c of a length-L sequence has ceil((L - 128c)/chunk)
-  // items; summed over a pack this is <= nblk + (T * max_seqlen / 256 + T) / chunk.
+  // dK/dV work items: chunk j of a length-L sequence pairs with blocks
+  // 0 .. (min((j+1)*chunk, L) - 1) / 128.  With n = ceil(L / chunk) chunks and
+  // m = chunk / 128, a sequence has at most min(n * ceil(L / 128),
+  // m * n * (n + 1) / 2) items; both sum over a pack to the bounds below.
   int64_t chunk = 512;
   for (;;) {
-    const int64_t items = z.nblk_cap + (z.T * z.max_seqlen / 256 + z.T) / chunk + 2;
+    const int64_t m = chunk / msa::kBlock;
+    const int64_t b1 = z.T * z.max_seqlen / (msa::kBlock * chunk) + z.T / chunk + z.T / msa::kBlock + 2 * z.S + 1;
+    const int64_t b2 = z.T * z.max_seqlen / (2 * msa::kBlock * chunk) + 3 * z.T / (2 * msa::kBlock) + z.S * m + 1;
+    const int64_t items = b1 < b2 ? b1 : b2;
     const int64_t bytes = items * z.Hk * msa::kBlock * msa::kHeadDim * 4 * 2;
     if (bytes <= kPartialBudget || chunk >= msa::kDkdvChunkMax) {
       z.chunk = chunk;
@@ -86,7 +91,7 @@ PlanBufs carve_plan(Carver& c, const Sizes& z) {
   PlanBufs p;
   p.blkbase = c.take<int32_t>(z.S + 1);
   p.blk_seq = c.take<int32_t>(z.nblk_cap);
-  p.itembase = c.take<int32_t>(z.nblk_cap + 1);
+  p.seqitem = c.take<int32_t>(z.S + 1);
   p.totals = c.take<int32_t>(4);
   return p;
 }

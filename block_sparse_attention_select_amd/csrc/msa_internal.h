@@ -24,14 +24,14 @@ struct Sizes {
   int64_t T, S, Hq, Hk, max_seqlen;
   int64_t nbmax;      // ceil(max_seqlen / 128): blocks of the longest sequence
   int64_t nblk_cap;   // bound on the total number of blocks of the pack
-  int64_t chunk;      // tokens per dK/dV work item
+  int64_t chunk;      // query positions per dK/dV work item (a multiple of 128)
   int64_t items_cap;  // bound on the number of dK/dV work items per KV head
 };
 
 struct PlanBufs {
   int32_t* blkbase;   // [S+1]       first global block of each sequence
   int32_t* blk_seq;   // [nblk_cap]  sequence of each global block
-  int32_t* itembase;  // [nblk_cap+1] first dK/dV work item of each global block
+  int32_t* seqitem;   // [S+1]       first dK/dV work item of each sequence
   int32_t* totals;    // [4]         {number of blocks, number of work items}
 };
 
@@ -154,8 +154,8 @@ struct BwdArgs {
   // workspace
   u16* kt;          // [nblk_cap][Hk][128 d][128 keys] K transposed per block
   float* delta;     // [T][Hq]
-  u16* qT;          // [T][Hk][128 d][16 heads]
-  u16* doT;         // [T][Hk][128 d][16 heads]
+  u16* qT;          // [T][Hk][8 dt][64 lanes][4 heads]: q transposed in MFMA operand order
+  u16* doT;         // same for dO
   int32_t* item_count;  // [Hk][items_cap]
   float* part_dk;   // [Hk][items_cap][128][128]
   float* part_dv;

@@ -4,10 +4,14 @@
 // radixark/miles PR #4581, PR body).
 //
 // Blocks are numbered pack-wide: sequence s owns global blocks
-// blkbase[s] .. blkbase[s+1]-1, block c of s being blkbase[s] + c.  A dK/dV
-// work item is one global block paired with one chunk of `chunk` consecutive
-// query positions starting at the block itself (earlier queries cannot select
-// it): block c of a length-L sequence has ceil((L - 128 c) / chunk) items.
+// blkbase[s] .. blkbase[s+1]-1, block c of s being blkbase[s] + c.
+//
+// dK/dV work items are ordered by (sequence, query chunk, block): chunk j of a
+// length-L sequence holds query positions [j*chunk, min((j+1)*chunk, L)) and
+// forms one item with every block c that one of those queries may select,
+// c = 0 .. (min((j+1)*chunk, L) - 1) / 128.  Consecutive items therefore read
+// the same queries, which keeps them in L2 while the workgroups of a chunk run.
+// seqitem[s] is the first item of sequence s.
 #include "msa_internal.h"
 
 namespace msa {
@@ -16,23 +20,31 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 
+__device__ __forceinline__ int chunk_items(int L, int chunk, int j) {
+  return (min((j + 1) * chunk, L) - 1) / kBlock + 1;
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ cu, int S, int chunk,
                                                              int32_t* __restrict__ blkbase,
                                                              int32_t* __restrict__ blk_seq,
-                                                             int32_t* __restrict__ itembase,
+                                                             int32_t* __restrict__ seqitem,
                                                              int32_t* __restrict__ totals) {
   __shared__ int sb[kPlanThreads];
   __shared__ int si[kPlanThreads];
   const int tid = threadIdx.x;
   int carry_b = 0, carry_i = 0;
-  if (tid == 0) blkbase[0] = 0;
+  if (tid == 0) {
+    blkbase[0] = 0;
+    seqitem[0] = 0;
+  }
   for (int base = 0; base < S; base += kPlanThreads) {
     const int s = base + tid;
     int L = 0, nb = 0, ni = 0;
     if (s < S) {
       L = cu[s + 1] - cu[s];
       nb = (L + kBlock - 1) / kBlock;
-      for (int c = 0; c < nb; ++c) ni += (L - kBlock * c + chunk - 1) / chunk;
+      const int nch = (L + chunk - 1) / chunk;
+      for (int j = 0; j < nch; ++j) ni += chunk_items(L, chunk, j);
     }
     sb[tid] = nb;
     si[tid] = ni;
@@ -47,20 +59,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     }
     if (s < S) {
       const int b0 = carry_b + sb[tid] - nb;
-      int it = carry_i + si[tid] - ni;
       blkbase[s + 1] = b0 + nb;
-      for (int c = 0; c < nb; ++c) {
-        blk_seq[b0 + c] = s;
-        itembase[b0 + c] = it;
-        it += (L - kBlock * c + chunk - 1) / chunk;
-      }
+      seqitem[s + 1] = carry_i + si[tid];
+      for (int c = 0; c < nb; ++c) blk_seq[b0 + c] = s;
     }
     carry_b += sb[kPlanThreads - 1];
     carry_i += si[kPlanThreads - 1];
     __syncthreads();
   }
   if (tid == 0) {
-    itembase[carry_b] = carry_i;
     totals[0] = carry_b;
     totals[1] = carry_i;
   }
@@ -71,7 +78,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 void launch_plan(const int32_t* cu, const Sizes& z, const PlanBufs& p, hipStream_t st) {
   {
     KernelTimer timer("plan", st);
-    plan_kernel<<<1, kPlanThreads, 0, st>>>(cu, (int)z.S, (int)z.chunk, p.blkbase, p.blk_seq, p.itembase, p.totals);
+    plan_kernel<<<1, kPlanThreads, 0, st>>>(cu, (int)z.S, (int)z.chunk, p.blkbase, p.blk_seq, p.seqitem, p.totals);
   }
 }
 
