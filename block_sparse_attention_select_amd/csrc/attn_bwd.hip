@@ -249,15 +249,23 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
         sacc[kk] = a;
         pacc[kk] = bb;
       }
+      if (diag || !live[j]) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = key0 + score_key(kk, 4 * g + r);
-          const float e = fast_exp2(sacc[kk][r] * scale_log2 - lse2[j]);
-          const bool on = live[j] && !(diag && key > tok_pos[j]);
-          sacc[kk][r] = on ? e * (pacc[kk][r] - dl[j]) : 0.f;
-        }
+          for (int r = 0; r < 4; ++r) {
+            const int key = key0 + score_key(kk, 4 * g + r);
+            const float e = fast_exp2(fmaf(sacc[kk][r], scale_log2, -lse2[j]));
+            const bool on = live[j] && key <= tok_pos[j];
+            sacc[kk][r] = on ? e * (pacc[kk][r] - dl[j]) : 0.f;
+          }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sacc[kk][r] = fast_exp2(fmaf(sacc[kk][r], scale_log2, -lse2[j])) * (pacc[kk][r] - dl[j]);
+      }
       const bf16x8 dsf0 = pack_bf16x8(sacc[0], sacc[1]);
       const bf16x8 dsf1 = pack_bf16x8(sacc[2], sacc[3]);
 #pragma unroll
@@ -288,7 +296,8 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ totals, int Hk, int chunk, int items_cap, float scale,
     u16* __restrict__ dk, int64_t dk_st, int64_t dk_sh, u16* __restrict__ dv, int64_t dv_st, int64_t dv_sh) {
   const int gb = blockIdx.x;
-  const int h = blockIdx.y;
+  const int slice = blockIdx.y;  // 16 keys of the block
+  const int h = blockIdx.z;
   if (gb >= totals[0]) return;
   const int s = blk_seq[gb];
   const int c = gb - blkbase[s];
@@ -298,7 +307,8 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
   const int jmin = (kBlock * c) / chunk;
   if (jmin == nch - 1) return;  // a block with one work item was written by the dK/dV kernel itself
   const int item0 = seqitem[s];
-  for (int e = threadIdx.x * 4; e < kBlock * kHeadDim; e += 256 * 4) {
+  const int e0 = slice * 16 * kHeadDim;
+  for (int e = e0 + threadIdx.x * 4; e < e0 + 16 * kHeadDim; e += 256 * 4) {
     const int key = e / kHeadDim;
     const int d = e - key * kHeadDim;
     const int kp = kBlock * c + key;
@@ -343,7 +353,7 @@ void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStr
   launch_attn_bwd_dkdv(z, a, p, st);
   {
     KernelTimer timer("dkdv_reduce", st);
-    dkdv_reduce_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)Hk), 256, 0, st>>>(
+    dkdv_reduce_kernel<<<dim3((unsigned)z.nblk_cap, kBlock / 16, (unsigned)Hk), 256, 0, st>>>(
         a.part_dk, a.part_dv, a.item_count, p.seqitem, p.blk_seq, p.blkbase, a.cu, p.totals, Hk, (int)z.chunk,
         (int)z.items_cap, a.scale, a.dk, a.dk_st, a.dk_sh, a.dv, a.dv_st, a.dv_sh);
   }

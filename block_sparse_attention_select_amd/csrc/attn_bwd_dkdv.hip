@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const bool live = valid[tk] && lr[r] > -INFINITY && kp <= pos[tk];
-                const float e = fast_exp2(sacc[kk][r] * scale_log2 - lr[r] * kLog2e);
+                const float e = fast_exp2(fmaf(sacc[kk][r], scale_log2, -lr[r] * kLog2e));
                 ph[kk][tk][r] = live ? e : 0.f;
                 sh[kk][tk][r] = live ? e * (pacc[kk][r] - dr[r]) : 0.f;
               }

@@ -79,6 +79,7 @@ __global__ __launch_bounds__(256) void block_transpose_kernel(const u16* __restr
 // ---------------------------------------------------------------------------
 constexpr int kTileTok = 16;
 constexpr int kFwdWaves = 8;
+constexpr float kRescaleSlack = 8.f;  // log2 units
 constexpr int kUnionWords = 34;  // a tile's blocks span fewer than 34 * 32 global ids
 constexpr int kMaxUnion = kTileTok * kTopk;
 
@@ -205,35 +206,50 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
           acc = mfma16x16x32(__builtin_bit_cast(bf16x8, kbuf[buf][kt * 4 + ds][lane]), qb[j][ds], acc);
         st[kt] = acc;
       }
+      // Online softmax in base 2 on the raw scores: the scale is folded into
+      // the exponent's FMA (scale > 0 keeps the max), masking only on the
+      // query's own block.  The running max moves only when a row's new max
+      // exceeds it by more than kRescaleSlack: until then P stays below
+      // 2^kRescaleSlack, the sums stay consistent with the kept max, and the
+      // accumulator rescale is skipped for the whole wavefront.
       float mx = -INFINITY;
+      if (diag) {
 #pragma unroll
-      for (int kt = 0; kt < 8; ++kt)
+        for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float z = st[kt][r] * scale_log2;
-          if (diag && kBlock * c + score_key(kt, 4 * g + r) > tok_pos[j]) z = -INFINITY;
-          st[kt][r] = z;
-          mx = fmaxf(mx, z);
-        }
+          for (int r = 0; r < 4; ++r) {
+            if (kBlock * c + score_key(kt, 4 * g + r) > tok_pos[j]) st[kt][r] = -INFINITY;
+            mx = fmaxf(mx, st[kt][r]);
+          }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[kt][r]);
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[j], mx);
-      const float alpha = fast_exp2(m_run[j] - m_new);
+      const float m_cand = mx * scale_log2;
+      const bool grow = m_cand > m_run[j] + kRescaleSlack;
+      const float m_use = grow ? m_cand : m_run[j];
+      const float alpha = grow ? fast_exp2(m_run[j] - m_cand) : 1.f;
       float rs = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(st[kt][r] - m_new);
+          const float p = fast_exp2(fmaf(st[kt][r], scale_log2, -m_use));
           st[kt][r] = p;
           rs += p;
         }
       rs += __shfl_xor(rs, 16);
       rs += __shfl_xor(rs, 32);
       l_run[j] = l_run[j] * alpha + rs;
-      m_run[j] = m_new;
+      m_run[j] = m_use;
+      if (__ballot(grow)) {
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) oacc[j][dt] *= alpha;
+        for (int dt = 0; dt < 8; ++dt) oacc[j][dt] *= alpha;
+      }
       bf16x8 pf[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) pf[ks] = pack_bf16x8(st[2 * ks], st[2 * ks + 1]);
