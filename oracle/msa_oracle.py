@@ -298,13 +298,15 @@ def key_set(i: int, blocks: Iterable[int], seq_start: int, pos_i: int, block: in
 
 def attention_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, blk_idx: np.ndarray,
                       cu_seqlens: Sequence[int], scale: float, block: int = 128,
-                      rows: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+                      rows: Optional[Sequence[int]] = None,
+                      heads: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
     """O = softmax(scale * q k^T) v over each query's selected causal keys, and LSE.
 
     ``q`` [T, Hq, D]; ``k``, ``v`` [T, Hk, D]; ``blk_idx`` [T, Hk, K] with
     sequence-local block ids.  Query head g reads KV head g // (Hq/Hk).
     Returns fp64 O [n, Hq, D] and natural-log LSE [n, Hq] for the tokens in
     ``rows`` (default: all).  A query with no key gets O = 0 and LSE = -inf.
+    ``heads`` restricts the work to some KV heads (the other outputs stay 0).
     """
     T, Hq, D = q.shape
     Hk = k.shape[1]
@@ -314,9 +316,10 @@ def attention_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, blk_idx: np.n
     rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
     O = np.zeros((len(rows), Hq, D), dtype=F64)
     LSE = np.full((len(rows), Hq), -np.inf, dtype=F64)
+    heads = range(Hk) if heads is None else heads
     for n, i in enumerate(rows):
         i = int(i)
-        for h in range(Hk):
+        for h in heads:
             J = key_set(i, blk_idx[i, h], int(cu[seq[i]]), int(pos[i]), block)
             if len(J) == 0:
                 continue
@@ -334,7 +337,8 @@ def attention_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, blk_idx: np.n
 
 def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
                        blk_idx: np.ndarray, cu_seqlens: Sequence[int], scale: float,
-                       block: int = 128, rows: Optional[Sequence[int]] = None
+                       block: int = 128, rows: Optional[Sequence[int]] = None,
+                       heads: Optional[Sequence[int]] = None
                        ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Gradients of sum(O * dO) with respect to q, k and v (fp64).
 
@@ -345,7 +349,8 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
 
     ``rows`` restricts the queries: dQ then covers those rows only and dK/dV
     hold only their contributions (useful to check one key block by passing
-    every query that selected it).
+    every query that selected it).  ``heads`` restricts the work to some KV
+    heads.
     """
     T, Hq, D = q.shape
     Hk = k.shape[1]
@@ -356,9 +361,10 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
     dQ = np.zeros((len(rows), Hq, D), dtype=F64)
     dK = np.zeros((T, Hk, D), dtype=F64)
     dV = np.zeros((T, Hk, D), dtype=F64)
+    heads = range(Hk) if heads is None else heads
     for n, i in enumerate(rows):
         i = int(i)
-        for h in range(Hk):
+        for h in heads:
             J = key_set(i, blk_idx[i, h], int(cu[seq[i]]), int(pos[i]), block)
             if len(J) == 0:
                 continue
