@@ -13,6 +13,9 @@ timed on a bounded sample of the same pack.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -58,6 +61,57 @@ def causal_pairs(lengths) -> int:
     return int(sum(L * (L + 1) // 2 for L in lengths))
 
 
+CSRC = os.path.join(ROOT, "block_sparse_attention_select_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    """Hash of every HIP/C++ source of the library: counters taken on other sources are stale."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(config: str) -> str:
+    return os.path.join(PROFILES, f"traffic_{config}.json")
+
+
+def summarize_pmc(dirs, config: str, copy_mib: int) -> dict:
+    """Per-kernel HBM bytes per dispatch from rocprofv3 --pmc CSVs (FETCH_SIZE and
+    WRITE_SIZE, in KiB), each scaled by what the same counter reads for the plain
+    copy of `copy_mib` MiB that --calibrate-copy runs."""
+    acc = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] not in ("FETCH_SIZE", "WRITE_SIZE"):
+                    continue
+                name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("msa::", "")
+                e = acc.setdefault(name, {}).setdefault(r["Counter_Name"], {})
+                e[r["Dispatch_Id"]] = e.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    avg = {k: {c: sum(v.values()) / len(v) for c, v in d.items()} for k, d in acc.items()}
+    # the calibration copy: the library-external kernel that wrote the most
+    copies = [d for k, d in avg.items() if not k.endswith("_kernel") and "FETCH_SIZE" in d and "WRITE_SIZE" in d]
+    if not copies:
+        raise SystemExit("no calibration kernel with FETCH_SIZE and WRITE_SIZE in the PMC runs (use --calibrate-copy)")
+    cp = max(copies, key=lambda d: d["WRITE_SIZE"])
+    nbytes = copy_mib * 2**20
+    f_fetch = nbytes / (cp["FETCH_SIZE"] * 1024)
+    f_write = nbytes / (cp["WRITE_SIZE"] * 1024)
+    out = {"config": config, "source_hash": kernel_source_hash(), "copy_mib": copy_mib,
+           "copy_factor_fetch": round(f_fetch, 4), "copy_factor_write": round(f_write, 4), "kernels": {}}
+    for k, d in avg.items():
+        if k.endswith("_kernel") and "FETCH_SIZE" in d and "WRITE_SIZE" in d:
+            fb = d["FETCH_SIZE"] * 1024 * f_fetch
+            wb = d["WRITE_SIZE"] * 1024 * f_write
+            out["kernels"][k[:-len("_kernel")]] = {"fetch_bytes": int(fb), "write_bytes": int(wb),
+                                                   "hbm_bytes": int(fb + wb)}
+    return out
+
+
 def cpu_baseline(p, stride: int):
     """The oracle as it stands, on this host: select on the whole pack, fwd+bwd on
     every `stride`-th token, scaled to the full pack."""
@@ -94,7 +148,20 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-stride", type=int, default=3, help="oracle fwd+bwd sample: every n-th token")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after timing, copy MIB MiB device-to-device (a PMC calibration kernel)")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="write profiles/traffic_<config>.json from rocprofv3 --pmc output dirs and exit")
+    ap.add_argument("--copy-mib", type=int, default=1024, help="size of the calibration copy in those runs")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        out = summarize_pmc(args.summarize_pmc, args.config, args.copy_mib)
+        os.makedirs(PROFILES, exist_ok=True)
+        with open(traffic_file(args.config), "w") as f:
+            json.dump(out, f, indent=1)
+        print(json.dumps(out))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the MSA path shards by KV head with no exchange step, "
@@ -181,11 +248,18 @@ def main():
         dom_flop = sel_flop
     else:
         dom_flop = None
+    traffic = None
+    tf = traffic_file(args.config)
+    if os.path.exists(tf):
+        rec = json.load(open(tf))
+        if rec.get("source_hash") == kernel_source_hash() and dom in rec.get("kernels", {}):
+            traffic = rec["kernels"][dom]["hbm_bytes"]
     roofline = None
     if dom_flop is not None:
         ach = dom_flop / (dom_ms * 1e-3) / 1e12
         roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                    "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                     "avg_launch_ms": round(dom_ms, 4), "algorithmic_flop_per_launch": int(dom_flop)}
 
     line = {
@@ -223,6 +297,15 @@ def main():
         "roofline": roofline,
         "context_gb300_ms": {"fwd_bwd": 6.7, "select": 0.62, "note": "pages' GB300 figures on unpublished 16k packs"},
     }
+    if args.calibrate_copy > 0:
+        # a plain streaming kernel of known traffic (read n, write n bytes); a
+        # tensor copy would go to the DMA engines and leave no kernel to count
+        src = torch.zeros(args.calibrate_copy * 2**20 // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(p, args.cpu_stride)
     else:
