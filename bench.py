@@ -93,11 +93,12 @@ def summarize_pmc(dirs, config: str, copy_mib: int) -> dict:
                 e = acc.setdefault(name, {}).setdefault(r["Counter_Name"], {})
                 e[r["Dispatch_Id"]] = e.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
     avg = {k: {c: sum(v.values()) / len(v) for c, v in d.items()} for k, d in acc.items()}
-    # the calibration copy: the library-external kernel that wrote the most
+    # the calibration kernel: the library-external kernel that both read and
+    # wrote the most (the streaming pass --calibrate-copy runs)
     copies = [d for k, d in avg.items() if not k.endswith("_kernel") and "FETCH_SIZE" in d and "WRITE_SIZE" in d]
     if not copies:
         raise SystemExit("no calibration kernel with FETCH_SIZE and WRITE_SIZE in the PMC runs (use --calibrate-copy)")
-    cp = max(copies, key=lambda d: d["WRITE_SIZE"])
+    cp = max(copies, key=lambda d: min(d["FETCH_SIZE"], d["WRITE_SIZE"]))
     nbytes = copy_mib * 2**20
     f_fetch = nbytes / (cp["FETCH_SIZE"] * 1024)
     f_write = nbytes / (cp["WRITE_SIZE"] * 1024)
