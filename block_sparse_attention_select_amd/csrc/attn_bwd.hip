@@ -11,8 +11,7 @@
 // selected the block.
 //
 // Kernels:
-//   bwd_prep_kernel     Delta, plus per-token transposed copies of q and dO
-//                       ([d][16 heads]) used as MFMA operands by dK/dV;
+//   bwd_prep_kernel     Delta = rowsum(dO * O);
 //   attn_bwd_dq_kernel  token-major dQ, tiles of 16 tokens walking the union
 //                       of their blocks with K, V and K^T staged in LDS;
 //   attn_bwd_dkdv_kernel (attn_bwd_dkdv.hip) key-block-major dK/dV per chunk
@@ -28,66 +27,35 @@ namespace msa {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Delta and transposed q / dO.  One wavefront per (token, KV head).
+// Delta = rowsum(dO * O) per (token, query head): one wavefront per (token,
+// KV head), four lanes per head row.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_prep_kernel(
     const u16* __restrict__ o, int64_t o_st, int64_t o_sh,
-    const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
-    const u16* __restrict__ q, int64_t q_st, int64_t q_sh, int T, int Hk,
-    float* __restrict__ delta, u16* __restrict__ qT, u16* __restrict__ doT) {
-  __shared__ u16 tq[4][kHeadDim][kGroup + 2];
-  __shared__ u16 tdo[4][kHeadDim][kGroup + 2];
-  const int wl = threadIdx.x >> 6;
-  const int wave_raw = blockIdx.x * 4 + wl;
+    const u16* __restrict__ dO, int64_t do_st, int64_t do_sh, int T, int Hk, float* __restrict__ delta) {
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  // Every wavefront reaches the barrier below; surplus ones redo the last
-  // (token, head) without storing.
-  const bool active = wave_raw < T * Hk;
-  const int wave = active ? wave_raw : T * Hk - 1;
+  if (wave >= T * Hk) return;
   const int t = wave / Hk;
   const int h = wave - t * Hk;
-  const int head = lane >> 2;   // 0..15
-  const int quarter = lane & 3; // 32 dims each
-  const int hq = h * kGroup + head;
+  const int hq = h * kGroup + (lane >> 2);
+  const int quarter = lane & 3;
   const u16* orow = o + (int64_t)t * o_st + (int64_t)hq * o_sh + 32 * quarter;
   const u16* drow = dO + (int64_t)t * do_st + (int64_t)hq * do_sh + 32 * quarter;
-  const u16* qrow = q + (int64_t)t * q_st + (int64_t)hq * q_sh + 32 * quarter;
   float acc = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint4 ov = *reinterpret_cast<const uint4*>(orow + 8 * j);
-    const uint4 dv = *reinterpret_cast<const uint4*>(drow + 8 * j);
-    const uint4 qv = *reinterpret_cast<const uint4*>(qrow + 8 * j);
-    const u16* op = reinterpret_cast<const u16*>(&ov);
-    const u16* dp = reinterpret_cast<const u16*>(&dv);
-    const u16* qp = reinterpret_cast<const u16*>(&qv);
+    const u32x4 ov = *reinterpret_cast<const u32x4*>(orow + 8 * j);
+    const u32x4 dv = *reinterpret_cast<const u32x4*>(drow + 8 * j);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      acc += bf2f(op[e]) * bf2f(dp[e]);
-      tdo[wl][32 * quarter + 8 * j + e][head] = dp[e];
-      tq[wl][32 * quarter + 8 * j + e][head] = qp[e];
+    for (int e = 0; e < 4; ++e) {
+      acc += bf2f((u16)(ov[e] & 0xFFFFu)) * bf2f((u16)(dv[e] & 0xFFFFu));
+      acc += bf2f((u16)(ov[e] >> 16)) * bf2f((u16)(dv[e] >> 16));
     }
   }
   acc += __shfl_xor(acc, 1);
   acc += __shfl_xor(acc, 2);
-  if (active && quarter == 0) delta[(int64_t)t * (Hk * kGroup) + hq] = acc;
-  __syncthreads();
-  if (!active) return;
-  // transposes in MFMA B-operand order: 8-byte entry (dt, lane = li + 16g)
-  // holds heads 4g..4g+3 of dim 16dt + li.
-  const int64_t base = ((int64_t)t * Hk + h) * (kHeadDim * kGroup);
-  const int li = lane & 15;
-  const int g = lane >> 4;
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    const int d = 16 * dt + li;
-    const uint2 wq = make_uint2((uint32_t)tq[wl][d][4 * g] | ((uint32_t)tq[wl][d][4 * g + 1] << 16),
-                                (uint32_t)tq[wl][d][4 * g + 2] | ((uint32_t)tq[wl][d][4 * g + 3] << 16));
-    const uint2 wd = make_uint2((uint32_t)tdo[wl][d][4 * g] | ((uint32_t)tdo[wl][d][4 * g + 1] << 16),
-                                (uint32_t)tdo[wl][d][4 * g + 2] | ((uint32_t)tdo[wl][d][4 * g + 3] << 16));
-    *reinterpret_cast<uint2*>(qT + base + (dt * 64 + lane) * 4) = wq;
-    *reinterpret_cast<uint2*>(doT + base + (dt * 64 + lane) * 4) = wd;
-  }
+  if (quarter == 0) delta[(int64_t)t * (Hk * kGroup) + hq] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -341,8 +309,7 @@ void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStr
   launch_block_transpose(z, a.k, a.k_st, a.k_sh, a.cu, p, a.kt, st);
   {
     KernelTimer timer("bwd_prep", st);
-    bwd_prep_kernel<<<wgs_tok, 256, 0, st>>>(a.o, a.o_st, a.o_sh, a.dO, a.do_st, a.do_sh, a.q, a.q_st, a.q_sh, T, Hk,
-                                             a.delta, a.qT, a.doT);
+    bwd_prep_kernel<<<wgs_tok, 256, 0, st>>>(a.o, a.o_st, a.o_sh, a.dO, a.do_st, a.do_sh, T, Hk, a.delta);
   }
   {
     KernelTimer timer("attn_bwd_dq", st);

@@ -15,16 +15,17 @@
 //      (wavefront ballots, so the list and every later sum are deterministic).
 //   2. Each of the 4 wavefronts keeps 32 keys of K and V as MFMA B operands
 //      and the 32 x 128 fp32 dK and dV sums in registers for the whole item.
-//   3. Selecting tokens stream through LDS four at a time (one per
+//   3. Selecting tokens stream through LDS eight at a time (two per
 //      wavefront), double buffered with global_load_lds copies issued while
-//      the previous four are used.  Per token the stage holds q and dO laid
-//      out so each MFMA A operand is one contiguous 1 KB read, their
-//      [d][head] transposes (B operands of dK and dV, prepared by
-//      bwd_prep_kernel in operand order: 512 contiguous bytes per read) and the
+//      the previous eight are used.  Per token the stage holds q and dO laid
+//      out so each MFMA A operand is one contiguous 1 KB read, plus the
 //      token's 16 LSE and Delta values.
 //   4. Two tokens (32 query rows) per MFMA step: S = q K^T and dP = dO V^T
 //      (A from LDS, B from registers), then dV += P^T dO and dK += dS^T q
-//      with P and dS taken straight from the score registers.
+//      with P and dS taken straight from the score registers.  The B operands
+//      of dV and dK (dO and q with the head rows as the contraction index) are
+//      read from the same stage with ds_read_b64_tr_b16, which transposes 4x4
+//      groups of 16-bit elements across lanes on the fly.
 //   5. A block whose selecting queries all lie in one chunk writes bf16 dK/dV
 //      itself; other blocks write fp32 slices that dkdv_reduce_kernel sums in
 //      chunk order.
@@ -34,30 +35,24 @@ namespace msa {
 
 namespace {
 
-constexpr int kBatch = 4;  // tokens per staging round, one loaded by each wavefront
+constexpr int kBatch = 8;  // tokens per staging round, two loaded by each wavefront
 
 // Stage layout of one token (u32x4 units): [0,256) q and [256,512) dO as
-// [ds][lane]; [512,768) q^T and [768,1024) dO^T as [dt][lane] pairs of 8-byte
-// entries (straight copies of the prepared transposes); stats: 16 LSE then 16
-// Delta values.  Wavefront w copies token w of a round: 16 runs of 1 KB and
-// one 128-byte run.
+// [ds][lane], lane li + 16g of run ds holding row li, dims 32ds + 8g .. +7;
+// stats: 16 LSE then 16 Delta values.  Wavefront w copies tokens 2w and 2w+1
+// of a round: 8 runs of 1 KB and one 128-byte run each.
 __device__ __forceinline__ void stage_token(int t, int h, int Hk, int lane, uint32_t slot_lds, uint32_t stats_lds,
                                             const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
                                             const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
-                                            const u16* __restrict__ qT, const u16* __restrict__ doT,
                                             const float* __restrict__ lse, const float* __restrict__ delta) {
   const int li = lane & 15;
   const int g = lane >> 4;
   const u16* qr = q + (int64_t)t * q_st + (int64_t)(h * kGroup + li) * q_sh + 8 * g;
   const u16* dr = dO + (int64_t)t * do_st + (int64_t)(h * kGroup + li) * do_sh + 8 * g;
-  const u16* qt = qT + ((int64_t)t * Hk + h) * (kHeadDim * kGroup) + 8 * lane;
-  const u16* dt = doT + ((int64_t)t * Hk + h) * (kHeadDim * kGroup) + 8 * lane;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     dma16(qr + 32 * i, slot_lds + i * 1024);
     dma16(dr + 32 * i, slot_lds + 4096 + i * 1024);
-    dma16(qt + 512 * i, slot_lds + 8192 + i * 1024);
-    dma16(dt + 512 * i, slot_lds + 12288 + i * 1024);
   }
   if (lane < 32) {
     const int64_t row = (int64_t)t * (Hk * kGroup) + h * kGroup;
@@ -66,12 +61,28 @@ __device__ __forceinline__ void stage_token(int t, int h, int Hk, int lane, uint
   }
 }
 
+// Byte offset, within a staged [ds][lane] tensor, of the 4 elements lane
+// (s, gg) (s = lane % 16, gg = lane / 16) hands to ds_read_b64_tr_b16 so that
+// the lane receives rows 4gg .. 4gg+3 of dim 16dt + s: source lane s of a
+// 16-lane group points at row 4gg + s/4, dims 16dt + 4(s%4) .. +3.
+__device__ __forceinline__ uint32_t tr_offset(int dt, int lane) {
+  const int s = lane & 15;
+  const int gg = lane >> 4;
+  return (uint32_t)((dt >> 1) * 1024 + (4 * gg + (s >> 2)) * 16 + (2 * (dt & 1) + ((s & 3) >> 1)) * 256 +
+                    8 * (s & 1));
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 read_tr16(uint32_t lds_byte) {
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(uintptr_t)lds_byte);
+  return __builtin_bit_cast(uint2, r);
+}
+
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
     const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
     const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
     const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
-    const u16* __restrict__ qT, const u16* __restrict__ doT,
     const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ blk_idx, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ blkbase, const int32_t* __restrict__ blk_seq,
@@ -79,7 +90,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     int S, int Hk, int chunk, int items_cap, float scale_log2, float scale,
     int32_t* __restrict__ item_count, float* __restrict__ part_dk, float* __restrict__ part_dv,
     u16* __restrict__ dk_out, int64_t dk_st, int64_t dk_sh, u16* __restrict__ dv_out, int64_t dv_st, int64_t dv_sh) {
-  __shared__ u32x4 stage[2][kBatch][1024];
+  __shared__ u32x4 stage[2][kBatch][512];
   __shared__ __align__(16) float stats[2][kBatch][32];
   __shared__ int sel[kDkdvChunkMax];
   __shared__ int wcount[4];
@@ -169,8 +180,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     const int nbatch = (nsel + kBatch - 1) / kBatch;
     // slots past the end repeat the last token (finite operands, masked to zero)
     auto stage_round = [&](int bi, int buf) {
-      stage_token(sel[min(bi * kBatch + wave, nsel - 1)], h, Hk, lane, lds_offset(&stage[buf][wave][0]),
-                  lds_offset(&stats[buf][wave][0]), q, q_st, q_sh, dO, do_st, do_sh, qT, doT, lse, delta);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int slot = 2 * wave + e;
+        stage_token(sel[min(bi * kBatch + slot, nsel - 1)], h, Hk, lane, lds_offset(&stage[buf][slot][0]),
+                    lds_offset(&stats[buf][slot][0]), q, q_st, q_sh, dO, do_st, do_sh, lse, delta);
+      }
     };
     stage_round(0, 0);
     wait_copies();
@@ -233,12 +248,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
           }
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) {
-            const int off = dt * 64 + lane;  // 8-byte entry of a [dt][lane] transpose run
-            const uint2* qt0 = reinterpret_cast<const uint2*>(b[0] + 512);
-            const uint2* qt1 = reinterpret_cast<const uint2*>(b[1] + 512);
-            const uint2* dt0 = reinterpret_cast<const uint2*>(b[0] + 768);
-            const uint2* dt1 = reinterpret_cast<const uint2*>(b[1] + 768);
-            const uint2 a0 = dt0[off], a1 = dt1[off], c0 = qt0[off], c1 = qt1[off];
+            const uint32_t off = tr_offset(dt, lane);
+            const uint2 a0 = read_tr16(lds_offset(b[0] + 256) + off);
+            const uint2 a1 = read_tr16(lds_offset(b[1] + 256) + off);
+            const uint2 c0 = read_tr16(lds_offset(b[0]) + off);
+            const uint2 c1 = read_tr16(lds_offset(b[1]) + off);
             const bf16x8 bdo = __builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y});
             const bf16x8 bq = __builtin_bit_cast(bf16x8, u32x4{c0.x, c0.y, c1.x, c1.y});
 #pragma unroll
@@ -291,7 +305,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 void launch_attn_bwd_dkdv(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStream_t st) {
   KernelTimer timer("attn_bwd_dkdv", st);
   attn_bwd_dkdv_kernel<<<dim3((unsigned)z.items_cap, (unsigned)z.Hk), 256, 0, st>>>(
-      a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.dO, a.do_st, a.do_sh, a.qT, a.doT, a.lse,
+      a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.dO, a.do_st, a.do_sh, a.lse,
       a.delta, a.blk_idx, a.cu, p.blkbase, p.blk_seq, p.seqitem, p.totals, (int)z.S, (int)z.Hk, (int)z.chunk,
       (int)z.items_cap, a.scale * kLog2e, a.scale, a.item_count, a.part_dk, a.part_dv, a.dk, a.dk_st, a.dk_sh, a.dv,
       a.dv_st, a.dv_sh);

@@ -154,8 +154,6 @@ struct BwdArgs {
   // workspace
   u16* kt;          // [nblk_cap][Hk][128 d][128 keys] K transposed per block
   float* delta;     // [T][Hq]
-  u16* qT;          // [T][Hk][8 dt][64 lanes][4 heads]: q transposed in MFMA operand order
-  u16* doT;         // same for dO
   int32_t* item_count;  // [Hk][items_cap]
   float* part_dk;   // [Hk][items_cap][128][128]
   float* part_dv;
