@@ -27,12 +27,14 @@ namespace msa {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Delta = rowsum(dO * O) per (token, query head): one wavefront per (token,
-// KV head), four lanes per head row.
+// Delta = rowsum(dO * O) per (token, query head), and the row's -LSE in base
+// 2 (-inf for a row without keys, so that exp2(s * scale_log2 + nlse) is 0
+// there): one wavefront per (token, KV head), four lanes per head row.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_prep_kernel(
     const u16* __restrict__ o, int64_t o_st, int64_t o_sh,
-    const u16* __restrict__ dO, int64_t do_st, int64_t do_sh, int T, int Hk, float* __restrict__ delta) {
+    const u16* __restrict__ dO, int64_t do_st, int64_t do_sh, const float* __restrict__ lse, int T, int Hk,
+    float* __restrict__ delta, float* __restrict__ nlse) {
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (wave >= T * Hk) return;
@@ -55,7 +57,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
   }
   acc += __shfl_xor(acc, 1);
   acc += __shfl_xor(acc, 2);
-  if (quarter == 0) delta[(int64_t)t * (Hk * kGroup) + hq] = acc;
+  const int64_t row = (int64_t)t * (Hk * kGroup) + hq;
+  if (quarter == 0) delta[row] = acc;
+  if (quarter == 1) {
+    const float l = lse[row];
+    nlse[row] = l > -INFINITY ? -l * kLog2e : -INFINITY;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -309,7 +316,8 @@ void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStr
   launch_block_transpose(z, a.k, a.k_st, a.k_sh, a.cu, p, a.kt, st);
   {
     KernelTimer timer("bwd_prep", st);
-    bwd_prep_kernel<<<wgs_tok, 256, 0, st>>>(a.o, a.o_st, a.o_sh, a.dO, a.do_st, a.do_sh, T, Hk, a.delta);
+    bwd_prep_kernel<<<wgs_tok, 256, 0, st>>>(a.o, a.o_st, a.o_sh, a.dO, a.do_st, a.do_sh, a.lse, T, Hk, a.delta,
+                                                     a.nlse);
   }
   {
     KernelTimer timer("attn_bwd_dq", st);

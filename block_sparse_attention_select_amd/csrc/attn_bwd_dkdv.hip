@@ -39,12 +39,12 @@ constexpr int kBatch = 8;  // tokens per staging round, two loaded by each wavef
 
 // Stage layout of one token (u32x4 units): [0,256) q and [256,512) dO as
 // [ds][lane], lane li + 16g of run ds holding row li, dims 32ds + 8g .. +7;
-// stats: 16 LSE then 16 Delta values.  Wavefront w copies tokens 2w and 2w+1
+// stats: 16 -LSE*log2(e) then 16 Delta values.  Wavefront w copies tokens 2w and 2w+1
 // of a round: 8 runs of 1 KB and one 128-byte run each.
 __device__ __forceinline__ void stage_token(int t, int h, int Hk, int lane, uint32_t slot_lds, uint32_t stats_lds,
                                             const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
                                             const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
-                                            const float* __restrict__ lse, const float* __restrict__ delta) {
+                                            const float* __restrict__ nlse, const float* __restrict__ delta) {
   const int li = lane & 15;
   const int g = lane >> 4;
   const u16* qr = q + (int64_t)t * q_st + (int64_t)(h * kGroup + li) * q_sh + 8 * g;
@@ -56,7 +56,7 @@ __device__ __forceinline__ void stage_token(int t, int h, int Hk, int lane, uint
   }
   if (lane < 32) {
     const int64_t row = (int64_t)t * (Hk * kGroup) + h * kGroup;
-    const float* src = lane < 16 ? lse + row + lane : delta + row + lane - 16;
+    const float* src = lane < 16 ? nlse + row + lane : delta + row + lane - 16;
     dma4(src, stats_lds);
   }
 }
@@ -64,12 +64,12 @@ __device__ __forceinline__ void stage_token(int t, int h, int Hk, int lane, uint
 // Byte offset, within a staged [ds][lane] tensor, of the 4 elements lane
 // (s, gg) (s = lane % 16, gg = lane / 16) hands to ds_read_b64_tr_b16 so that
 // the lane receives rows 4gg .. 4gg+3 of dim 16dt + s: source lane s of a
-// 16-lane group points at row 4gg + s/4, dims 16dt + 4(s%4) .. +3.
-__device__ __forceinline__ uint32_t tr_offset(int dt, int lane) {
+// 16-lane group points at row 4gg + s/4, dims 16dt + 4(s%4) .. +3, i.e. at
+// (dt/2) * 1024 + (dt%2) * 512 + tr_lane_offset(lane).
+__device__ __forceinline__ uint32_t tr_lane_offset(int lane) {
   const int s = lane & 15;
   const int gg = lane >> 4;
-  return (uint32_t)((dt >> 1) * 1024 + (4 * gg + (s >> 2)) * 16 + (2 * (dt & 1) + ((s & 3) >> 1)) * 256 +
-                    8 * (s & 1));
+  return (uint32_t)((4 * gg + (s >> 2)) * 16 + ((s & 3) >> 1) * 256 + 8 * (s & 1));
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
     const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
     const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
-    const float* __restrict__ lse, const float* __restrict__ delta,
+    const float* __restrict__ nlse, const float* __restrict__ delta,
     const int32_t* __restrict__ blk_idx, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ blkbase, const int32_t* __restrict__ blk_seq,
     const int32_t* __restrict__ seqitem, const int32_t* __restrict__ totals,
@@ -177,6 +177,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 
   // 3./4. stream the selecting tokens through LDS, two per MFMA step
   if (nsel > 0) {
+    const uint32_t tro = tr_lane_offset(lane);
     const int nbatch = (nsel + kBatch - 1) / kBatch;
     // slots past the end repeat the last token (finite operands, masked to zero)
     auto stage_round = [&](int bi, int buf) {
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
       for (int e = 0; e < 2; ++e) {
         const int slot = 2 * wave + e;
         stage_token(sel[min(bi * kBatch + slot, nsel - 1)], h, Hk, lane, lds_offset(&stage[buf][slot][0]),
-                    lds_offset(&stats[buf][slot][0]), q, q_st, q_sh, dO, do_st, do_sh, lse, delta);
+                    lds_offset(&stats[buf][slot][0]), q, q_st, q_sh, dO, do_st, do_sh, nlse, delta);
       }
     };
     stage_round(0, 0);
@@ -198,14 +199,17 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
       for (int pp = 0; pp < kBatch / 2; ++pp) {
         const int n0 = bi * kBatch + 2 * pp;
         if (n0 < nsel) {
-          const bool valid[2] = {true, n0 + 1 < nsel};
-          const int pos[2] = {sel[n0] - seq0, valid[1] ? sel[n0 + 1] - seq0 : 0};
+          // a missing second token is treated as a query at position -1 of
+          // this block: every key is after it, so it contributes nothing
+          const int pos[2] = {sel[n0] - seq0, n0 + 1 < nsel ? sel[n0 + 1] - seq0 : -1};
           const u32x4* b[2] = {stage[cur][2 * pp], stage[cur][2 * pp + 1]};
           const float* st[2] = {stats[cur][2 * pp], stats[cur][2 * pp + 1]};
 
-          // S = q K^T and dP = dO V^T per token, turned at once into bf16 P and dS
-          // halves: lane (key li, group g) keeps rows 4g..4g+3 of each token.
-          f32x4 ph[2][2], sh[2][2];  // [kk][token]
+          // S = q K^T and dP = dO V^T per token, turned at once into bf16 P and
+          // dS: lane (key li, group g) keeps rows 4g..4g+3 of each token, packed
+          // two per dword as the A operand of dV and dK (dwords 0-1 token 0,
+          // dwords 2-3 token 1).
+          u32x4 pw[2], sw[2];
 #pragma unroll
           for (int tk = 0; tk < 2; ++tk) {
             f32x4 sacc[2], pacc[2];
@@ -224,35 +228,46 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
                 pacc[kk] = mfma16x16x32(da, vf[kk][ds], pacc[kk]);
               }
             }
-            const float4 l4 = reinterpret_cast<const float4*>(st[tk])[g];
-            const float4 d4 = reinterpret_cast<const float4*>(st[tk] + 16)[g];
-            const float lr[4] = {l4.x, l4.y, l4.z, l4.w};
-            const float dr[4] = {d4.x, d4.y, d4.z, d4.w};
+            const f32x4 nl = reinterpret_cast<const f32x4*>(st[tk])[g];
+            const f32x4 d4 = reinterpret_cast<const f32x4*>(st[tk] + 16)[g];
+            f32x4 e[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) e[kk][r] = fast_exp2(fmaf(sacc[kk][r], scale_log2, nl[r]));
+            if (pos[tk] < kBlock * c + kBlock) {  // the query's own block (or no query): causal mask
+#pragma unroll
+              for (int kk = 0; kk < 2; ++kk) {
+                const bool on = kbase + 16 * kk + li <= pos[tk];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) e[kk][r] = on ? e[kk][r] : 0.f;
+              }
+            }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-              const int kp = kbase + 16 * kk + li;
+              f32x4 d;
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const bool live = valid[tk] && lr[r] > -INFINITY && kp <= pos[tk];
-                const float e = fast_exp2(fmaf(sacc[kk][r], scale_log2, -lr[r] * kLog2e));
-                ph[kk][tk][r] = live ? e : 0.f;
-                sh[kk][tk][r] = live ? e * (pacc[kk][r] - dr[r]) : 0.f;
-              }
+              for (int r = 0; r < 4; ++r) d[r] = e[kk][r] * (pacc[kk][r] - d4[r]);
+              pw[kk][2 * tk] = pack_bf16x2(e[kk][0], e[kk][1]);
+              pw[kk][2 * tk + 1] = pack_bf16x2(e[kk][2], e[kk][3]);
+              sw[kk][2 * tk] = pack_bf16x2(d[0], d[1]);
+              sw[kk][2 * tk + 1] = pack_bf16x2(d[2], d[3]);
             }
           }
           bf16x8 pA[2], sA[2];
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk) {
-            pA[kk] = pack_bf16x8(ph[kk][0], ph[kk][1]);
-            sA[kk] = pack_bf16x8(sh[kk][0], sh[kk][1]);
+            pA[kk] = __builtin_bit_cast(bf16x8, pw[kk]);
+            sA[kk] = __builtin_bit_cast(bf16x8, sw[kk]);
           }
+          const uint32_t q0 = lds_offset(b[0]) + tro, q1 = lds_offset(b[1]) + tro;
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) {
-            const uint32_t off = tr_offset(dt, lane);
-            const uint2 a0 = read_tr16(lds_offset(b[0] + 256) + off);
-            const uint2 a1 = read_tr16(lds_offset(b[1] + 256) + off);
-            const uint2 c0 = read_tr16(lds_offset(b[0]) + off);
-            const uint2 c1 = read_tr16(lds_offset(b[1]) + off);
+            const uint32_t off = (dt >> 1) * 1024 + (dt & 1) * 512;
+            const uint2 a0 = read_tr16(q0 + 4096 + off);
+            const uint2 a1 = read_tr16(q1 + 4096 + off);
+            const uint2 c0 = read_tr16(q0 + off);
+            const uint2 c1 = read_tr16(q1 + off);
             const bf16x8 bdo = __builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y});
             const bf16x8 bq = __builtin_bit_cast(bf16x8, u32x4{c0.x, c0.y, c1.x, c1.y});
 #pragma unroll
@@ -305,7 +320,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 void launch_attn_bwd_dkdv(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStream_t st) {
   KernelTimer timer("attn_bwd_dkdv", st);
   attn_bwd_dkdv_kernel<<<dim3((unsigned)z.items_cap, (unsigned)z.Hk), 256, 0, st>>>(
-      a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.dO, a.do_st, a.do_sh, a.lse,
+      a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.dO, a.do_st, a.do_sh, a.nlse,
       a.delta, a.blk_idx, a.cu, p.blkbase, p.blk_seq, p.seqitem, p.totals, (int)z.S, (int)z.Hk, (int)z.chunk,
       (int)z.items_cap, a.scale * kLog2e, a.scale, a.item_count, a.part_dk, a.part_dv, a.dk, a.dk_st, a.dk_sh, a.dv,
       a.dv_st, a.dv_sh);

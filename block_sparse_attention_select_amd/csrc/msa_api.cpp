@@ -126,6 +126,7 @@ struct BwdWs {
   PlanBufs plan;
   u16* kt;
   float* delta;
+  float* nlse;
   int32_t* item_count;
   float* part_dk;
   float* part_dv;
@@ -135,6 +136,7 @@ BwdWs carve_bwd(Carver& c, const Sizes& z) {
   w.plan = carve_plan(c, z);
   w.kt = c.take<u16>(z.nblk_cap * z.Hk * msa::kHeadDim * msa::kBlock);
   w.delta = c.take<float>(z.T * z.Hq);
+  w.nlse = c.take<float>(z.T * z.Hq);
   w.item_count = c.take<int32_t>(z.Hk * z.items_cap);
   w.part_dk = c.take<float>(z.Hk * z.items_cap * msa::kBlock * msa::kHeadDim);
   w.part_dv = c.take<float>(z.Hk * z.items_cap * msa::kBlock * msa::kHeadDim);
@@ -288,6 +290,7 @@ int msa_attn_bwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh
   a.dv = (u16*)dv; a.dv_st = dv_st; a.dv_sh = dv_sh;
   a.kt = w.kt;
   a.delta = w.delta;
+  a.nlse = w.nlse;
   a.item_count = w.item_count;
   a.part_dk = w.part_dk;
   a.part_dv = w.part_dv;

@@ -71,6 +71,12 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(f32x4 lo, f32x4 hi) {
   return r;
 }
 
+// Two floats to one dword of bf16 (round to nearest even), low half first.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
+}
+
 __device__ __forceinline__ uint2 pack_bf16x4(f32x4 v) {
   uint32_t a = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
   uint32_t b = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
@@ -154,6 +160,7 @@ struct BwdArgs {
   // workspace
   u16* kt;          // [nblk_cap][Hk][128 d][128 keys] K transposed per block
   float* delta;     // [T][Hq]
+  float* nlse;      // [T][Hq] -LSE * log2(e), -inf for rows without keys
   int32_t* item_count;  // [Hk][items_cap]
   float* part_dk;   // [Hk][items_cap][128][128]
   float* part_dv;
