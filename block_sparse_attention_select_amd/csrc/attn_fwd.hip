@@ -66,24 +66,28 @@ __global__ __launch_bounds__(256) void block_transpose_kernel(const u16* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Forward.  One workgroup of 8 wavefronts per (tile of 16 consecutive tokens,
-// KV head); wavefront w owns tokens 2w and 2w+1 of the tile (their q as MFMA B
-// operands, their O accumulators and softmax state, all in registers).
+// Forward.  One workgroup of 16 wavefronts per (tile of 16 consecutive tokens,
+// KV head); wavefront w owns token w of the tile (its q as MFMA B operands, its
+// O accumulators and softmax state, all in registers).  One token per
+// wavefront keeps a wavefront within 128 registers, so four of them share a
+// SIMD and hide each other's MFMA -> softmax -> MFMA dependency chains.
 //   1. The union of the tile's selected blocks is built in LDS (a bitmap over
 //      the tile's global block range, compacted in ascending order).
 //   2. The workgroup walks that union.  Each block's K (A operand of
 //      S^T = K Q^T) and V^T (A operand of O^T = V^T P^T) are copied into one of
 //      two LDS buffers while the previous block is being used; every wavefront
-//      then updates those of its tokens that selected the block.  K and V are
+//      then updates its token if that token selected the block.  K and V are
 //      read from HBM/L2 once per tile instead of once per token.
 // ---------------------------------------------------------------------------
 constexpr int kTileTok = 16;
-constexpr int kFwdWaves = 8;
+constexpr int kTokPerWave = 1;
+constexpr int kFwdWaves = kTileTok / kTokPerWave;
+constexpr int kRunsPerWave = 64 / kFwdWaves;  // K and V^T runs staged per wavefront
 constexpr float kRescaleSlack = 8.f;  // log2 units
 constexpr int kUnionWords = 34;  // a tile's blocks span fewer than 34 * 32 global ids
 constexpr int kMaxUnion = kTileTok * kTopk;
 
-__global__ __launch_bounds__(512) void attn_fwd_kernel(
+__global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
     const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
     const u16* __restrict__ vt, const int32_t* __restrict__ blk_idx,
@@ -103,8 +107,8 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
   const int g = lane >> 4;
   const int li = lane & 15;
 
-  // this lane's (token, slot): token 2*wave + (g & 1), slot li
-  const int tj = 2 * wave + (g & 1);
+  // this lane's (token, slot): token kTokPerWave * wave + g % kTokPerWave, slot li
+  const int tj = kTokPerWave * wave + g % kTokPerWave;
   const int t = t0 + tj;
   const bool tvalid = t < T;
   int s_t = 0, pos_t = 0, b_t = -1, my_gb = -1;
@@ -120,7 +124,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
   // 1. union of the tile's blocks
   if (threadIdx.x < kUnionWords) bitmap[threadIdx.x] = 0u;
   __syncthreads();
-  if (g < 2 && my_gb >= 0 && my_gb - gb_lo < kUnionWords * 32)
+  if (g < kTokPerWave && my_gb >= 0 && my_gb - gb_lo < kUnionWords * 32)
     atomicOr(&bitmap[(my_gb - gb_lo) >> 5], 1u << ((my_gb - gb_lo) & 31));
   __syncthreads();
   if (wave == 0) {
@@ -144,14 +148,14 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
   const int nu = nunion;
 
   // per-token state (j = 0, 1 for tokens 2w, 2w+1)
-  int tok_t[2], tok_pos[2], tok_b[2], tok_base[2];
-  bool tok_ok[2];
-  bf16x8 qb[2][4];
-  f32x4 oacc[2][8];
-  float m_run[2], l_run[2];
+  int tok_t[kTokPerWave], tok_pos[kTokPerWave], tok_b[kTokPerWave], tok_base[kTokPerWave];
+  bool tok_ok[kTokPerWave];
+  bf16x8 qb[kTokPerWave][4];
+  f32x4 oacc[kTokPerWave][8];
+  float m_run[kTokPerWave], l_run[kTokPerWave];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    tok_t[j] = t0 + 2 * wave + j;
+  for (int j = 0; j < kTokPerWave; ++j) {
+    tok_t[j] = t0 + kTokPerWave * wave + j;
     tok_ok[j] = tok_t[j] < T;
     tok_pos[j] = __builtin_amdgcn_readlane(pos_t, 16 * j);
     tok_b[j] = __builtin_amdgcn_readlane(b_t, 16 * j);
@@ -171,9 +175,9 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
     const int sb = blk_seq[gb];
     const int kstart = cu[sb] + kBlock * (gb - blkbase[sb]);
 #pragma unroll
-    for (int ii = 0; ii < 8; ++ii) {
-      const int id = 8 * wave + ii;  // waves 0-3: K runs, waves 4-7: V^T runs
-      if (wave < 4) {
+    for (int ii = 0; ii < kRunsPerWave; ++ii) {
+      const int id = kRunsPerWave * wave + ii;  // runs 0-31: K, 32-63: V^T
+      if (id < 32) {
         const int key = min(kstart + score_key(id >> 2, li), T - 1);
         dma16(k + (int64_t)key * k_st + (int64_t)h * k_sh + 32 * (id & 3) + 8 * g, lds_offset(&kbuf[buf][id][0]));
       } else {
@@ -193,78 +197,84 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
     const int gb = ulist[u];
     const uint64_t hits = __ballot(my_gb == gb);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kTokPerWave; ++j) {
       if (((hits >> (16 * j)) & 0xFFFFull) == 0) continue;
       const int c = gb - tok_base[j];
       const bool diag = (c == tok_b[j]);
-      f32x4 st[8];
+      // Two halves of 64 keys, each a full online-softmax update.  Base 2 on
+      // the raw scores: the scale is folded into the exponent's FMA (scale > 0
+      // keeps the max); masking only on the query's own block, where a half
+      // that starts after the query is skipped.  The running max moves only
+      // when a row's new max exceeds it by more than kRescaleSlack: until then
+      // P stays below 2^kRescaleSlack, the sums stay consistent with the kept
+      // max, and the accumulator rescale is skipped for the whole wavefront.
+      // l_run holds this lane's share of the row sum (its keys 8g..8g+7 of
+      // every 32); the four shares are added at the end.
 #pragma unroll
-      for (int kt = 0; kt < 8; ++kt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int hf = 0; hf < 2; ++hf) {
+        if (diag && kBlock * c + 64 * hf > tok_pos[j]) break;
+        f32x4 st[4];
 #pragma unroll
-        for (int ds = 0; ds < 4; ++ds)
-          acc = mfma16x16x32(__builtin_bit_cast(bf16x8, kbuf[buf][kt * 4 + ds][lane]), qb[j][ds], acc);
-        st[kt] = acc;
-      }
-      // Online softmax in base 2 on the raw scores: the scale is folded into
-      // the exponent's FMA (scale > 0 keeps the max), masking only on the
-      // query's own block.  The running max moves only when a row's new max
-      // exceeds it by more than kRescaleSlack: until then P stays below
-      // 2^kRescaleSlack, the sums stay consistent with the kept max, and the
-      // accumulator rescale is skipped for the whole wavefront.
-      float mx = -INFINITY;
-      if (diag) {
+        for (int kt = 0; kt < 4; ++kt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kt = 0; kt < 8; ++kt)
+          for (int ds = 0; ds < 4; ++ds)
+            acc = mfma16x16x32(__builtin_bit_cast(bf16x8, kbuf[buf][(4 * hf + kt) * 4 + ds][lane]), qb[j][ds], acc);
+          st[kt] = acc;
+        }
+        float mx = -INFINITY;
+        if (diag) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (kBlock * c + score_key(4 * hf + kt, 4 * g + r) > tok_pos[j]) st[kt][r] = -INFINITY;
+              mx = fmaxf(mx, st[kt][r]);
+            }
+        } else {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[kt][r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_cand = mx * scale_log2;
+        const bool grow = m_cand > m_run[j] + kRescaleSlack;
+        const float m_use = grow ? m_cand : m_run[j];
+        const float alpha = grow ? fast_exp2(m_run[j] - m_cand) : 1.f;
+        float rs = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            if (kBlock * c + score_key(kt, 4 * g + r) > tok_pos[j]) st[kt][r] = -INFINITY;
-            mx = fmaxf(mx, st[kt][r]);
+            const float p = fast_exp2(fmaf(st[kt][r], scale_log2, -m_use));
+            st[kt][r] = p;
+            rs += p;
           }
-      } else {
+        l_run[j] = l_run[j] * alpha + rs;
+        m_run[j] = m_use;
+        if (__ballot(grow)) {
 #pragma unroll
-        for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[kt][r]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_cand = mx * scale_log2;
-      const bool grow = m_cand > m_run[j] + kRescaleSlack;
-      const float m_use = grow ? m_cand : m_run[j];
-      const float alpha = grow ? fast_exp2(m_run[j] - m_cand) : 1.f;
-      float rs = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(fmaf(st[kt][r], scale_log2, -m_use));
-          st[kt][r] = p;
-          rs += p;
+          for (int dt = 0; dt < 8; ++dt) oacc[j][dt] *= alpha;
         }
-      rs += __shfl_xor(rs, 16);
-      rs += __shfl_xor(rs, 32);
-      l_run[j] = l_run[j] * alpha + rs;
-      m_run[j] = m_use;
-      if (__ballot(grow)) {
+        const bf16x8 pf0 = pack_bf16x8(st[0], st[1]);
+        const bf16x8 pf1 = pack_bf16x8(st[2], st[3]);
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) oacc[j][dt] *= alpha;
+        for (int dt = 0; dt < 8; ++dt) {
+          oacc[j][dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, vbuf[buf][dt * 4 + 2 * hf][lane]), pf0, oacc[j][dt]);
+          oacc[j][dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, vbuf[buf][dt * 4 + 2 * hf + 1][lane]), pf1, oacc[j][dt]);
+        }
       }
-      bf16x8 pf[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) pf[ks] = pack_bf16x8(st[2 * ks], st[2 * ks + 1]);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          oacc[j][dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, vbuf[buf][dt * 4 + ks][lane]), pf[ks], oacc[j][dt]);
     }
     wait_copies();
     lds_barrier();
   }
 
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < kTokPerWave; ++j) {
+    l_run[j] += __shfl_xor(l_run[j], 16);
+    l_run[j] += __shfl_xor(l_run[j], 32);
     if (!tok_ok[j]) continue;
     const float inv = l_run[j] > 0.f ? 1.0f / l_run[j] : 0.f;
     u16* orow = o + (int64_t)tok_t[j] * o_st + (int64_t)(h * kGroup + li) * o_sh;
