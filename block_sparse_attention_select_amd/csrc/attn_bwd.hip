@@ -66,20 +66,22 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dQ.  Same tiling as the forward: one 8-wavefront workgroup per (tile of 16
-// consecutive tokens, KV head), wavefront w owning tokens 2w and 2w+1 (their
-// q and dO as MFMA B operands and their dQ^T accumulators in registers).  The
+// dQ.  Same tiling as the forward: one 16-wavefront workgroup per (tile of 16
+// consecutive tokens, KV head), wavefront w owning token w (its q and dO as
+// MFMA B operands and its dQ^T accumulators in registers, within 128 registers
+// so that four wavefronts share a SIMD).  The
 // workgroup walks the union of the tile's selected blocks in halves of 64
 // keys; each half's K and V (A operands of S^T = K Q^T and dP^T = V dO^T) and
 // K^T (A operand of dQ^T = K^T dS^T) are copied into one of two LDS buffers
 // while the previous half is used.
 // ---------------------------------------------------------------------------
 constexpr int kTileTok = 16;
-constexpr int kDqWaves = 8;
+constexpr int kTokPerWave = 1;
+constexpr int kDqWaves = kTileTok / kTokPerWave;
 constexpr int kUnionWords = 34;
 constexpr int kMaxUnion = kTileTok * kTopk;
 
-__global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
     const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
     const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
   const int li = lane & 15;
   const int Hq = Hk * kGroup;
 
-  const int tj = 2 * wave + (g & 1);
+  const int tj = kTokPerWave * wave + g % kTokPerWave;
   const int t = t0 + tj;
   const bool tvalid = t < T;
   int s_t = 0, pos_t = 0, b_t = -1, my_gb = -1;
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
 
   if (threadIdx.x < kUnionWords) bitmap[threadIdx.x] = 0u;
   __syncthreads();
-  if (g < 2 && my_gb >= 0 && my_gb - gb_lo < kUnionWords * 32)
+  if (g < kTokPerWave && my_gb >= 0 && my_gb - gb_lo < kUnionWords * 32)
     atomicOr(&bitmap[(my_gb - gb_lo) >> 5], 1u << ((my_gb - gb_lo) & 31));
   __syncthreads();
   if (wave == 0) {
@@ -141,15 +143,15 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
   __syncthreads();
   const int nsteps = 2 * nunion;  // halves of 64 keys
 
-  int tok_t[2], tok_pos[2], tok_b[2], tok_base[2];
-  bool tok_ok[2];
-  bf16x8 qb[2][4], db[2][4];
-  f32x4 dqacc[2][8];
-  float lse2[2], dl[2];
-  bool live[2];
+  int tok_t[kTokPerWave], tok_pos[kTokPerWave], tok_b[kTokPerWave], tok_base[kTokPerWave];
+  bool tok_ok[kTokPerWave];
+  bf16x8 qb[kTokPerWave][4], db[kTokPerWave][4];
+  f32x4 dqacc[kTokPerWave][8];
+  float lse2[kTokPerWave], dl[kTokPerWave];
+  bool live[kTokPerWave];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    tok_t[j] = t0 + 2 * wave + j;
+  for (int j = 0; j < kTokPerWave; ++j) {
+    tok_t[j] = t0 + kTokPerWave * wave + j;
     tok_ok[j] = tok_t[j] < T;
     tok_pos[j] = __builtin_amdgcn_readlane(pos_t, 16 * j);
     tok_b[j] = __builtin_amdgcn_readlane(b_t, 16 * j);
@@ -171,27 +173,21 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
   }
 
   // step w: block ulist[w / 2], keys 64 * (w & 1) .. +63
+  // wavefront r copies run r of K, of V (local tile r / 4, step r % 4) and of
+  // K^T (runs dt * 4 + 2 * half + ks' of the block -> local run dt * 2 + ks')
+  static_assert(kDqWaves == 16, "one K, V and K^T run per wavefront");
+  const u16* k_lane = k + (int64_t)h * k_sh + 32 * (wave & 3) + 8 * g;
+  const u16* v_lane = v + (int64_t)h * v_sh + 32 * (wave & 3) + 8 * g;
+  const int kt_run = (wave >> 1) * 4 + (wave & 1);
   auto stage = [&](int w, int buf) {
     const int gb = ulist[w >> 1];
     const int half = w & 1;
     const int sb = blk_seq[gb];
     const int kstart = cu[sb] + kBlock * (gb - blkbase[sb]);
-#pragma unroll
-    for (int ii = 0; ii < 6; ++ii) {
-      const int id = 6 * wave + ii;
-      if (id < 32) {  // K (id < 16) or V runs: local tile kt' = r >> 2, step ds = r & 3
-        const int r = id & 15;
-        const int key = min(kstart + score_key(4 * half + (r >> 2), li), T - 1);
-        if (id < 16)
-          dma16(k + (int64_t)key * k_st + (int64_t)h * k_sh + 32 * (r & 3) + 8 * g, lds_offset(&kbuf[buf][r][0]));
-        else
-          dma16(v + (int64_t)key * v_st + (int64_t)h * v_sh + 32 * (r & 3) + 8 * g, lds_offset(&vbuf[buf][r][0]));
-      } else {  // K^T runs dt * 4 + 2 * half + ks' -> local run dt * 2 + ks'
-        const int r = id - 32;
-        const int run = (r >> 1) * 4 + 2 * half + (r & 1);
-        dma16(kt + (((int64_t)gb * Hk + h) * 32 + run) * 512 + lane * 8, lds_offset(&tbuf[buf][r][0]));
-      }
-    }
+    const int key = min(kstart + score_key(4 * half + (wave >> 2), li), T - 1);
+    dma16(k_lane + (int64_t)key * k_st, lds_offset(&kbuf[buf][wave][0]));
+    dma16(v_lane + (int64_t)key * v_st, lds_offset(&vbuf[buf][wave][0]));
+    dma16(kt + (((int64_t)gb * Hk + h) * 32 + kt_run + 2 * half) * 512 + lane * 8, lds_offset(&tbuf[buf][wave][0]));
   };
   if (nsteps > 0) stage(0, 0);
   wait_copies();
@@ -205,48 +201,50 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
     const int half = w & 1;
     const uint64_t hits = __ballot(my_gb == gb);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kTokPerWave; ++j) {
       if (((hits >> (16 * j)) & 0xFFFFull) == 0) continue;
       const int c = gb - tok_base[j];
       const bool diag = (c == tok_b[j]);
       const int key0 = kBlock * c + 64 * half;
       if (diag && key0 > tok_pos[j]) continue;  // the whole half lies after the query
-      f32x4 sacc[4], pacc[4];
+      // two quarters of 32 keys: S^T, dP^T, then dS^T as one B operand of dQ^T
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-        f32x4 bb = {0.f, 0.f, 0.f, 0.f};
+      for (int qq = 0; qq < 2; ++qq) {
+        if (diag && key0 + 32 * qq > tok_pos[j]) break;
+        f32x4 sacc[2], pacc[2];
 #pragma unroll
-        for (int ds = 0; ds < 4; ++ds) {
-          a = mfma16x16x32(__builtin_bit_cast(bf16x8, kbuf[buf][kk * 4 + ds][lane]), qb[j][ds], a);
-          bb = mfma16x16x32(__builtin_bit_cast(bf16x8, vbuf[buf][kk * 4 + ds][lane]), db[j][ds], bb);
-        }
-        sacc[kk] = a;
-        pacc[kk] = bb;
-      }
-      if (diag || !live[j]) {
+        for (int kk = 0; kk < 2; ++kk) {
+          f32x4 a = {0.f, 0.f, 0.f, 0.f};
+          f32x4 bb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = key0 + score_key(kk, 4 * g + r);
-            const float e = fast_exp2(fmaf(sacc[kk][r], scale_log2, -lse2[j]));
-            const bool on = live[j] && key <= tok_pos[j];
-            sacc[kk][r] = on ? e * (pacc[kk][r] - dl[j]) : 0.f;
+          for (int ds = 0; ds < 4; ++ds) {
+            a = mfma16x16x32(__builtin_bit_cast(bf16x8, kbuf[buf][(2 * qq + kk) * 4 + ds][lane]), qb[j][ds], a);
+            bb = mfma16x16x32(__builtin_bit_cast(bf16x8, vbuf[buf][(2 * qq + kk) * 4 + ds][lane]), db[j][ds], bb);
           }
-      } else {
+          sacc[kk] = a;
+          pacc[kk] = bb;
+        }
+        if (diag || !live[j]) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+          for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            sacc[kk][r] = fast_exp2(fmaf(sacc[kk][r], scale_log2, -lse2[j])) * (pacc[kk][r] - dl[j]);
-      }
-      const bf16x8 dsf0 = pack_bf16x8(sacc[0], sacc[1]);
-      const bf16x8 dsf1 = pack_bf16x8(sacc[2], sacc[3]);
+            for (int r = 0; r < 4; ++r) {
+              const int key = key0 + score_key(2 * qq + kk, 4 * g + r);
+              const float e = fast_exp2(fmaf(sacc[kk][r], scale_log2, -lse2[j]));
+              const bool on = live[j] && key <= tok_pos[j];
+              sacc[kk][r] = on ? e * (pacc[kk][r] - dl[j]) : 0.f;
+            }
+        } else {
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        dqacc[j][dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, tbuf[buf][dt * 2][lane]), dsf0, dqacc[j][dt]);
-        dqacc[j][dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, tbuf[buf][dt * 2 + 1][lane]), dsf1, dqacc[j][dt]);
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              sacc[kk][r] = fast_exp2(fmaf(sacc[kk][r], scale_log2, -lse2[j])) * (pacc[kk][r] - dl[j]);
+        }
+        const bf16x8 dsf = pack_bf16x8(sacc[0], sacc[1]);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          dqacc[j][dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, tbuf[buf][dt * 2 + qq][lane]), dsf, dqacc[j][dt]);
       }
     }
     wait_copies();
@@ -254,7 +252,7 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_kernel(
   }
 
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < kTokPerWave; ++j) {
     if (!tok_ok[j]) continue;
     u16* out = dq + (int64_t)tok_t[j] * dq_st + (int64_t)(h * kGroup + li) * dq_sh;
 #pragma unroll
