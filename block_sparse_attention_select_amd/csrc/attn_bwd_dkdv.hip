@@ -35,30 +35,33 @@ namespace msa {
 
 namespace {
 
-constexpr int kBatch = 8;  // tokens per staging round, two loaded by each wavefront
+constexpr int kBatch = 4;  // tokens per staging round, kBatch / 4 loaded by each wavefront
 
 // Stage layout of one token (u32x4 units): [0,256) q and [256,512) dO as
 // [ds][lane], lane li + 16g of run ds holding row li, dims 32ds + 8g .. +7;
-// stats: 16 -LSE*log2(e) then 16 Delta values.  Wavefront w copies tokens 2w and 2w+1
-// of a round: 8 runs of 1 KB and one 128-byte run each.
+// stats: 16 -LSE*log2(e) then 16 Delta values.  One wavefront copies a token:
+// 8 runs of 1 KB and one 128-byte run.  Addresses are a wavefront-uniform
+// base (the token's row, scalar registers) plus a per-lane byte offset (head
+// li, dims 8g..).
 __device__ __forceinline__ void stage_token(int t, int h, int Hk, int lane, uint32_t slot_lds, uint32_t stats_lds,
                                             const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
                                             const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
                                             const float* __restrict__ nlse, const float* __restrict__ delta) {
-  const int li = lane & 15;
-  const int g = lane >> 4;
-  const u16* qr = q + (int64_t)t * q_st + (int64_t)(h * kGroup + li) * q_sh + 8 * g;
-  const u16* dr = dO + (int64_t)t * do_st + (int64_t)(h * kGroup + li) * do_sh + 8 * g;
+  t = __builtin_amdgcn_readfirstlane(t);
+  const uint32_t q_off = (uint32_t)(2 * ((lane & 15) * q_sh + 8 * (lane >> 4)));
+  const uint32_t do_off = (uint32_t)(2 * ((lane & 15) * do_sh + 8 * (lane >> 4)));
+  const u16* qr = q + (int64_t)t * q_st + (int64_t)(h * kGroup) * q_sh;
+  const u16* dr = dO + (int64_t)t * do_st + (int64_t)(h * kGroup) * do_sh;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    dma16(qr + 32 * i, slot_lds + i * 1024);
-    dma16(dr + 32 * i, slot_lds + 4096 + i * 1024);
+    dma16s(qr + 32 * i, q_off, slot_lds + i * 1024);
+    dma16s(dr + 32 * i, do_off, slot_lds + 4096 + i * 1024);
   }
-  if (lane < 32) {
-    const int64_t row = (int64_t)t * (Hk * kGroup) + h * kGroup;
-    const float* src = lane < 16 ? nlse + row + lane : delta + row + lane - 16;
-    dma4(src, stats_lds);
-  }
+  const int64_t row = (int64_t)t * (Hk * kGroup) + h * kGroup;
+  if (lane < 16)
+    dma4s(nlse + row, 4 * lane, stats_lds);
+  else if (lane < 32)
+    dma4s(delta + row - 16, 4 * lane, stats_lds);
 }
 
 // Byte offset, within a staged [ds][lane] tensor, of the 4 elements lane
@@ -72,13 +75,22 @@ __device__ __forceinline__ uint32_t tr_lane_offset(int lane) {
   return (uint32_t)((4 * gg + (s >> 2)) * 16 + ((s & 3) >> 1) * 256 + 8 * (s & 1));
 }
 
+// This lane's index, recomputed where it is used: an opaque value the
+// compiler cannot hoist, so lane-derived offsets are rebuilt with a few VALU
+// operations instead of being held in registers (or spilled) across the loop.
+__device__ __forceinline__ int fresh_lane() {
+  int x;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+  return x;
+}
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint2 read_tr16(uint32_t lds_byte) {
   const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(uintptr_t)lds_byte);
   return __builtin_bit_cast(uint2, r);
 }
 
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
     const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
     const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
@@ -116,7 +128,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const bool single = (j == nch - 1) && (j == jmin);
   const int p_begin = max(j * chunk, kBlock * c);
   const int p_end = min((j + 1) * chunk, L);
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int li = lane & 15;
@@ -177,14 +189,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 
   // 3./4. stream the selecting tokens through LDS, two per MFMA step
   if (nsel > 0) {
-    const uint32_t tro = tr_lane_offset(lane);
+
     const int nbatch = (nsel + kBatch - 1) / kBatch;
     // slots past the end repeat the last token (finite operands, masked to zero)
     auto stage_round = [&](int bi, int buf) {
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int slot = 2 * wave + e;
-        stage_token(sel[min(bi * kBatch + slot, nsel - 1)], h, Hk, lane, lds_offset(&stage[buf][slot][0]),
+      for (int e = 0; e < kBatch / 4; ++e) {
+        const int slot = (kBatch / 4) * wave + e;
+        stage_token(sel[min(bi * kBatch + slot, nsel - 1)], h, Hk, fresh_lane(), lds_offset(&stage[buf][slot][0]),
                     lds_offset(&stats[buf][slot][0]), q, q_st, q_sh, dO, do_st, do_sh, nlse, delta);
       }
     };
@@ -195,7 +207,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     for (int bi = 0; bi < nbatch; ++bi) {
       const int cur = bi & 1;
       if (bi + 1 < nbatch) stage_round(bi + 1, cur ^ 1);
-#pragma unroll
+#pragma unroll 1
       for (int pp = 0; pp < kBatch / 2; ++pp) {
         const int n0 = bi * kBatch + 2 * pp;
         if (n0 < nsel) {
@@ -210,6 +222,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
           // two per dword as the A operand of dV and dK (dwords 0-1 token 0,
           // dwords 2-3 token 1).
           u32x4 pw[2], sw[2];
+          const int ln = fresh_lane();
 #pragma unroll
           for (int tk = 0; tk < 2; ++tk) {
             f32x4 sacc[2], pacc[2];
@@ -220,16 +233,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
             }
 #pragma unroll
             for (int ds = 0; ds < 4; ++ds) {
-              const bf16x8 qa = __builtin_bit_cast(bf16x8, b[tk][ds * 64 + lane]);
-              const bf16x8 da = __builtin_bit_cast(bf16x8, b[tk][256 + ds * 64 + lane]);
+              const bf16x8 qa = __builtin_bit_cast(bf16x8, b[tk][ds * 64 + ln]);
+              const bf16x8 da = __builtin_bit_cast(bf16x8, b[tk][256 + ds * 64 + ln]);
 #pragma unroll
               for (int kk = 0; kk < 2; ++kk) {
                 sacc[kk] = mfma16x16x32(qa, kf[kk][ds], sacc[kk]);
                 pacc[kk] = mfma16x16x32(da, vf[kk][ds], pacc[kk]);
               }
             }
-            const f32x4 nl = reinterpret_cast<const f32x4*>(st[tk])[g];
-            const f32x4 d4 = reinterpret_cast<const f32x4*>(st[tk] + 16)[g];
+            const f32x4 nl = reinterpret_cast<const f32x4*>(st[tk])[ln >> 4];
+            const f32x4 d4 = reinterpret_cast<const f32x4*>(st[tk] + 16)[ln >> 4];
             f32x4 e[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
@@ -260,6 +273,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
             pA[kk] = __builtin_bit_cast(bf16x8, pw[kk]);
             sA[kk] = __builtin_bit_cast(bf16x8, sw[kk]);
           }
+          const uint32_t tro = tr_lane_offset(ln);
           const uint32_t q0 = lds_offset(b[0]) + tro, q1 = lds_offset(b[1]) + tro;
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) {

@@ -33,6 +33,23 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// As dma16, reading from the wavefront-uniform address `sbase` plus this
+// lane's unsigned byte offset `voff` (the base stays in scalar registers).
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
+// As dma16s, 4 bytes per lane (LDS at lds_base + 4 * lane).
+__device__ __forceinline__ void dma4s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
 // Copies 4 bytes from `src` (this lane) to LDS at lds_base + 4 * lane.
 __device__ __forceinline__ void dma4(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
