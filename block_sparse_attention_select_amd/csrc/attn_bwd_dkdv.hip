@@ -75,15 +75,6 @@ __device__ __forceinline__ uint32_t tr_lane_offset(int lane) {
   return (uint32_t)((4 * gg + (s >> 2)) * 16 + ((s & 3) >> 1) * 256 + 8 * (s & 1));
 }
 
-// This lane's index, recomputed where it is used: an opaque value the
-// compiler cannot hoist, so lane-derived offsets are rebuilt with a few VALU
-// operations instead of being held in registers (or spilled) across the loop.
-__device__ __forceinline__ int fresh_lane() {
-  int x;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
-  return x;
-}
-
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint2 read_tr16(uint32_t lds_byte) {
   const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(uintptr_t)lds_byte);

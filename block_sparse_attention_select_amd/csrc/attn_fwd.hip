@@ -102,7 +102,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
 
   const int h = blockIdx.y;
   const int t0 = blockIdx.x * kTileTok;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int li = lane & 15;
@@ -169,21 +169,32 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
     l_run[j] = 0.f;
   }
 
-  // 2. walk the union, staging block u+1 while block u is used
+  // 2. walk the union, staging block u+1 while block u is used.  Waves 0-7
+  // copy K runs 4w .. 4w+3 (keys score_key(w, .), dims 32 ii ..), waves 8-15
+  // V^T runs 4(w-8) .. +3; each copy is a scalar base plus a lane offset.
+  static_assert(kFwdWaves == 16 && kRunsPerWave == 4, "staging assumes 16 wavefronts");
   auto stage = [&](int u, int buf) {
-    const int gb = ulist[u];
-    const int sb = blk_seq[gb];
-    const int kstart = cu[sb] + kBlock * (gb - blkbase[sb]);
+    const int gb = __builtin_amdgcn_readfirstlane(ulist[u]);
+    const int ln = fresh_lane();
+    if (wave < 8) {
+      const int sb = blk_seq[gb];
+      const int kstart = cu[sb] + kBlock * (gb - blkbase[sb]);
+      if (kstart + kBlock <= T) {
+        const u16* base = k + (int64_t)kstart * k_st + (int64_t)h * k_sh;
+        const uint32_t off = (uint32_t)(2 * (score_key(wave, ln & 15) * k_st + 8 * (ln >> 4)));
 #pragma unroll
-    for (int ii = 0; ii < kRunsPerWave; ++ii) {
-      const int id = kRunsPerWave * wave + ii;  // runs 0-31: K, 32-63: V^T
-      if (id < 32) {
-        const int key = min(kstart + score_key(id >> 2, li), T - 1);
-        dma16(k + (int64_t)key * k_st + (int64_t)h * k_sh + 32 * (id & 3) + 8 * g, lds_offset(&kbuf[buf][id][0]));
-      } else {
-        const int run = id - 32;
-        dma16(vt + (((int64_t)gb * Hk + h) * 32 + run) * 512 + lane * 8, lds_offset(&vbuf[buf][run][0]));
+        for (int ii = 0; ii < 4; ++ii) dma16s(base + 32 * ii, off, lds_offset(&kbuf[buf][4 * wave + ii][0]));
+      } else {  // the pack's last block: keys past the end repeat the last token
+        const int key = min(kstart + score_key(wave, ln & 15), T - 1);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          dma16(k + (int64_t)key * k_st + (int64_t)h * k_sh + 32 * ii + 8 * (ln >> 4),
+                lds_offset(&kbuf[buf][4 * wave + ii][0]));
       }
+    } else {
+      const u16* base = vt + (((int64_t)gb * Hk + h) * 32 + 4 * (wave - 8)) * 512;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) dma16s(base + 512 * ii, 16 * ln, lds_offset(&vbuf[buf][4 * (wave - 8) + ii][0]));
     }
   };
   if (nu > 0) stage(0, 0);
@@ -213,14 +224,26 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         if (diag && kBlock * c + 64 * hf > tok_pos[j]) break;
+        // S^T for the half's four key tiles: the four accumulation chains are
+        // interleaved (consecutive MFMAs independent) and the K operand reads
+        // run eight ahead of the MFMAs that consume them
         f32x4 st[4];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int kt = 0; kt < 4; ++kt) st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        {
+          bf16x8 ka[16];
 #pragma unroll
-          for (int ds = 0; ds < 4; ++ds)
-            acc = mfma16x16x32(__builtin_bit_cast(bf16x8, kbuf[buf][(4 * hf + kt) * 4 + ds][lane]), qb[j][ds], acc);
-          st[kt] = acc;
+          for (int i = 0; i < 16; ++i)
+            ka[i] = __builtin_bit_cast(bf16x8, kbuf[buf][(4 * hf + (i & 3)) * 4 + (i >> 2)][lane]);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) st[i & 3] = mfma16x16x32(ka[i], qb[j][i >> 2], st[i & 3]);
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
         float mx = -INFINITY;
         if (diag) {
@@ -260,10 +283,22 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
         }
         const bf16x8 pf0 = pack_bf16x8(st[0], st[1]);
         const bf16x8 pf1 = pack_bf16x8(st[2], st[3]);
+        // O^T += V^T P^T: eight independent accumulators per sweep, V operand
+        // reads eight ahead
+        {
+          bf16x8 va[16];
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          oacc[j][dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, vbuf[buf][dt * 4 + 2 * hf][lane]), pf0, oacc[j][dt]);
-          oacc[j][dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, vbuf[buf][dt * 4 + 2 * hf + 1][lane]), pf1, oacc[j][dt]);
+          for (int i = 0; i < 16; ++i)
+            va[i] = __builtin_bit_cast(bf16x8, vbuf[buf][(i & 7) * 4 + 2 * hf + (i >> 3)][lane]);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[j][i & 7] = mfma16x16x32(va[i], i < 8 ? pf0 : pf1, oacc[j][i & 7]);
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
       }
     }

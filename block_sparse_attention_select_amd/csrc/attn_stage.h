@@ -65,6 +65,15 @@ __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)
 // then knows registers loaded earlier need no further wait inside a loop).
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// This lane's index, recomputed where it is used: an opaque value the
+// compiler cannot hoist, so lane-derived offsets are rebuilt with a few VALU
+// operations instead of being held in registers (or spilled) across a loop.
+__device__ __forceinline__ int fresh_lane() {
+  int x;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+  return x;
+}
+
 // Key of row m of score tile kt (16 keys per tile, 8 tiles per block).  Tiles
 // 2s and 2s+1 together cover keys 32s..32s+31 such that the accumulator rows a
 // lane of group g holds (4g..4g+3 of each tile) are the eight consecutive keys

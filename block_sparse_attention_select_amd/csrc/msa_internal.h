@@ -106,6 +106,44 @@ __device__ __forceinline__ int upper_index(const int32_t* __restrict__ a, int n,
 // 2^x on the transcendental unit (v_exp_f32), branch-free; 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lane exchanges across the four row groups of an MFMA accumulator column
+// (lanes li, li+16, li+32, li+48).  v_permlane32_swap / v_permlane16_swap on
+// two copies of x leave lane i holding x from lanes i and i^32 (resp. i^16) in
+// the two results.  The second copy goes through an empty asm so the compiler
+// cannot treat the two operands as one value and fold the cross-lane swap away.
+__device__ __forceinline__ void swap32(float x, float& a, float& b) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x), v = u;
+  asm volatile("" : "+v"(v));
+  const auto r = __builtin_amdgcn_permlane32_swap(u, v, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];  // (bit_cast of a vector element reads element 0)
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ void swap16(float x, float& a, float& b) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x), v = u;
+  asm volatile("" : "+v"(v));
+  const auto r = __builtin_amdgcn_permlane16_swap(u, v, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];  // (bit_cast of a vector element reads element 0)
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+
+// Maximum over the four row groups, in lane-swap VALU ops instead of LDS permutes.
+__device__ __forceinline__ float max_over_groups(float x) {
+  float a, b;
+  swap32(x, a, b);
+  swap16(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+
+// Sum over the four row groups.
+__device__ __forceinline__ float sum_over_groups(float x) {
+  float a, b;
+  swap32(x, a, b);
+  swap16(a + b, a, b);
+  return a + b;
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
