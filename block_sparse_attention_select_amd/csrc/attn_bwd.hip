@@ -99,7 +99,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
 
   const int h = blockIdx.y;
   const int t0 = blockIdx.x * kTileTok;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int li = lane & 15;
@@ -176,18 +176,26 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
   // wavefront r copies run r of K, of V (local tile r / 4, step r % 4) and of
   // K^T (runs dt * 4 + 2 * half + ks' of the block -> local run dt * 2 + ks')
   static_assert(kDqWaves == 16, "one K, V and K^T run per wavefront");
-  const u16* k_lane = k + (int64_t)h * k_sh + 32 * (wave & 3) + 8 * g;
-  const u16* v_lane = v + (int64_t)h * v_sh + 32 * (wave & 3) + 8 * g;
   const int kt_run = (wave >> 1) * 4 + (wave & 1);
   auto stage = [&](int w, int buf) {
-    const int gb = ulist[w >> 1];
+    const int gb = __builtin_amdgcn_readfirstlane(ulist[w >> 1]);
     const int half = w & 1;
     const int sb = blk_seq[gb];
     const int kstart = cu[sb] + kBlock * (gb - blkbase[sb]);
-    const int key = min(kstart + score_key(4 * half + (wave >> 2), li), T - 1);
-    dma16(k_lane + (int64_t)key * k_st, lds_offset(&kbuf[buf][wave][0]));
-    dma16(v_lane + (int64_t)key * v_st, lds_offset(&vbuf[buf][wave][0]));
-    dma16(kt + (((int64_t)gb * Hk + h) * 32 + kt_run + 2 * half) * 512 + lane * 8, lds_offset(&tbuf[buf][wave][0]));
+    const int ln = fresh_lane();
+    const int kl = score_key(4 * half + (wave >> 2), ln & 15);
+    if (kstart + kBlock <= T) {
+      const uint32_t koff = (uint32_t)(2 * (kl * k_st + 8 * (ln >> 4)));
+      const uint32_t voff = (uint32_t)(2 * (kl * v_st + 8 * (ln >> 4)));
+      dma16s(k + (int64_t)kstart * k_st + (int64_t)h * k_sh + 32 * (wave & 3), koff, lds_offset(&kbuf[buf][wave][0]));
+      dma16s(v + (int64_t)kstart * v_st + (int64_t)h * v_sh + 32 * (wave & 3), voff, lds_offset(&vbuf[buf][wave][0]));
+    } else {  // the pack's last block: keys past the end repeat the last token
+      const int key = min(kstart + kl, T - 1);
+      const int d0 = 32 * (wave & 3) + 8 * (ln >> 4);
+      dma16(k + (int64_t)key * k_st + (int64_t)h * k_sh + d0, lds_offset(&kbuf[buf][wave][0]));
+      dma16(v + (int64_t)key * v_st + (int64_t)h * v_sh + d0, lds_offset(&vbuf[buf][wave][0]));
+    }
+    dma16s(kt + (((int64_t)gb * Hk + h) * 32 + kt_run + 2 * half) * 512, 16 * ln, lds_offset(&tbuf[buf][wave][0]));
   };
   if (nsteps > 0) stage(0, 0);
   wait_copies();
@@ -211,18 +219,36 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
         if (diag && key0 + 32 * qq > tok_pos[j]) break;
+        // S^T and dP^T: four independent accumulation chains interleaved,
+        // K / V operand reads eight ahead of the MFMAs that use them
         f32x4 sacc[2], pacc[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          f32x4 a = {0.f, 0.f, 0.f, 0.f};
-          f32x4 bb = {0.f, 0.f, 0.f, 0.f};
+          sacc[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+          pacc[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        {
+          bf16x8 op[16];  // i = ds * 4 + kk * 2 + (0: K, 1: V)
 #pragma unroll
-          for (int ds = 0; ds < 4; ++ds) {
-            a = mfma16x16x32(__builtin_bit_cast(bf16x8, kbuf[buf][(2 * qq + kk) * 4 + ds][lane]), qb[j][ds], a);
-            bb = mfma16x16x32(__builtin_bit_cast(bf16x8, vbuf[buf][(2 * qq + kk) * 4 + ds][lane]), db[j][ds], bb);
+          for (int i = 0; i < 16; ++i) {
+            const int run = (2 * qq + ((i >> 1) & 1)) * 4 + (i >> 2);
+            op[i] = __builtin_bit_cast(bf16x8, (i & 1) ? vbuf[buf][run][lane] : kbuf[buf][run][lane]);
           }
-          sacc[kk] = a;
-          pacc[kk] = bb;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kk = (i >> 1) & 1, ds = i >> 2;
+            if (i & 1)
+              pacc[kk] = mfma16x16x32(op[i], db[j][ds], pacc[kk]);
+            else
+              sacc[kk] = mfma16x16x32(op[i], qb[j][ds], sacc[kk]);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
         if (diag || !live[j]) {
 #pragma unroll
@@ -242,9 +268,20 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
               sacc[kk][r] = fast_exp2(fmaf(sacc[kk][r], scale_log2, -lse2[j])) * (pacc[kk][r] - dl[j]);
         }
         const bf16x8 dsf = pack_bf16x8(sacc[0], sacc[1]);
+        {
+          bf16x8 ta[8];
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          dqacc[j][dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, tbuf[buf][dt * 2 + qq][lane]), dsf, dqacc[j][dt]);
+          for (int dt = 0; dt < 8; ++dt) ta[dt] = __builtin_bit_cast(bf16x8, tbuf[buf][dt * 2 + qq][lane]);
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) dqacc[j][dt] = mfma16x16x32(ta[dt], dsf, dqacc[j][dt]);
+          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+        }
       }
     }
     wait_copies();

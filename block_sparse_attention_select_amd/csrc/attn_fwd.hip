@@ -260,8 +260,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[kt][r]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_over_groups(mx);
         const float m_cand = mx * scale_log2;
         const bool grow = m_cand > m_run[j] + kRescaleSlack;
         const float m_use = grow ? m_cand : m_run[j];
@@ -308,8 +307,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
 
 #pragma unroll
   for (int j = 0; j < kTokPerWave; ++j) {
-    l_run[j] += __shfl_xor(l_run[j], 16);
-    l_run[j] += __shfl_xor(l_run[j], 32);
+    l_run[j] = sum_over_groups(l_run[j]);
     if (!tok_ok[j]) continue;
     const float inv = l_run[j] > 0.f ? 1.0f / l_run[j] : 0.f;
     u16* orow = o + (int64_t)tok_t[j] * o_st + (int64_t)(h * kGroup + li) * o_sh;
