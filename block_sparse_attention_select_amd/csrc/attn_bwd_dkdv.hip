@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int32_t* __restrict__ blk_idx, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ blkbase, const int32_t* __restrict__ blk_seq,
     const int32_t* __restrict__ seqitem, const int32_t* __restrict__ totals,
-    int S, int Hk, int chunk, int items_cap, float scale_log2, float scale,
+    int S, int Hk, int chunk, int items_cap, const int32_t* __restrict__ item_order, float scale_log2, float scale,
     int32_t* __restrict__ item_count, float* __restrict__ part_dk, float* __restrict__ part_dv,
     u16* __restrict__ dk_out, int64_t dk_st, int64_t dk_sh, u16* __restrict__ dv_out, int64_t dv_st, int64_t dv_sh) {
   __shared__ u32x4 stage[2][kBatch][512];
@@ -98,9 +98,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ int sel[kDkdvChunkMax];
   __shared__ int wcount[4];
 
-  const int item = blockIdx.x;
   const int h = blockIdx.y;
-  if (item >= totals[1]) return;
+  if ((int)blockIdx.x >= totals[1]) return;
+  const int item = item_order[(int64_t)h * items_cap + blockIdx.x];
   // decode (sequence, query chunk j, block c) from the item index
   const int s = upper_index(seqitem, S, item);
   const int seq0 = cu[s];
@@ -320,14 +320,133 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// ---------------------------------------------------------------------------
+// Launch order.  Items differ a lot in work (a chunk's own and nearby blocks
+// are selected by most of its queries, far blocks by few), and in index order
+// the heavy ones of the last sequence would run last.  The items are instead
+// launched by decreasing number of selecting queries (longest job first), which
+// only changes when each item runs, not what it computes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void dkdv_load_clear_kernel(int32_t* __restrict__ load, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) load[i] = 0;
+}
+
+// One workgroup per (256 consecutive tokens, KV head), a thread per token.
+// The items those tokens can touch form one contiguous index range (items are
+// ordered by sequence, chunk, block), so the counts are gathered in an LDS
+// histogram over that range and added to the global counts once per item.
+constexpr int kLoadSpan = 4096;
+__device__ __forceinline__ int item_base(const int32_t* seqitem, int s, int j, int chunk) {
+  return seqitem[s] + (chunk / kBlock) * (j * (j + 1) / 2);
+}
+__global__ __launch_bounds__(256) void dkdv_load_count_kernel(
+    const int32_t* __restrict__ blk_idx, const int32_t* __restrict__ cu, const int32_t* __restrict__ seqitem,
+    int S, int T, int Hk, int chunk, int items_cap, int32_t* __restrict__ load) {
+  __shared__ int hist[kLoadSpan];
+  const int h = blockIdx.y;
+  const int t0 = blockIdx.x * 256;
+  const int tB = min(t0 + 255, T - 1);
+  const int sA = find_seq(cu, S, t0), sB = find_seq(cu, S, tB);
+  const int jA = (t0 - cu[sA]) / chunk, jB = (tB - cu[sB]) / chunk;
+  const int LB = cu[sB + 1] - cu[sB];
+  const int lo = item_base(seqitem, sA, jA, chunk);
+  const int hi = item_base(seqitem, sB, jB, chunk) + (min((jB + 1) * chunk, LB) - 1) / kBlock + 1;
+  const bool in_lds = hi - lo <= kLoadSpan;
+  int32_t* gl = load + (int64_t)h * items_cap;
+  if (in_lds)
+    for (int i = threadIdx.x; i < hi - lo; i += 256) hist[i] = 0;
+  __syncthreads();
+  const int t = t0 + threadIdx.x;
+  if (t < T) {
+    const int s = find_seq(cu, S, t);
+    const int p = t - cu[s];
+    const int j = p / chunk;
+    const int base = item_base(seqitem, s, j, chunk);
+    const int4* ids = reinterpret_cast<const int4*>(blk_idx + ((int64_t)t * Hk + h) * kTopk);
+#pragma unroll
+    for (int q4 = 0; q4 < kTopk / 4; ++q4) {
+      const int4 x = ids[q4];
+      const int cs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = cs[e];
+        if (c < 0 || c > p / kBlock) continue;
+        if (in_lds)
+          atomicAdd(&hist[base + c - lo], 1);
+        else
+          atomicAdd(&gl[base + c], 1);
+      }
+    }
+  }
+  __syncthreads();
+  if (in_lds)
+    for (int i = threadIdx.x; i < hi - lo; i += 256)
+      if (hist[i] != 0) atomicAdd(&gl[lo + i], hist[i]);
+}
+
+// per KV head: counting sort of the items by decreasing load
+constexpr int kLoadBins = kDkdvChunkMax + 1;
+__global__ __launch_bounds__(1024) void dkdv_order_kernel(const int32_t* __restrict__ load,
+                                                          const int32_t* __restrict__ totals, int items_cap,
+                                                          int32_t* __restrict__ order) {
+  __shared__ int bins[kLoadBins];
+  __shared__ int wsum[16];
+  const int h = blockIdx.x;
+  const int n = totals[1];
+  const int32_t* ld = load + (int64_t)h * items_cap;
+  int32_t* od = order + (int64_t)h * items_cap;
+  for (int b = threadIdx.x; b < kLoadBins; b += 1024) bins[b] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += 1024) atomicAdd(&bins[kLoadBins - 1 - min(ld[i], kLoadBins - 1)], 1);
+  __syncthreads();
+  // exclusive scan of the bins (heaviest first), three bins per thread
+  const int b0 = 3 * threadIdx.x;
+  int v[3], run = 0;
+#pragma unroll
+  for (int e = 0; e < 3; ++e) {
+    v[e] = b0 + e < kLoadBins ? bins[b0 + e] : 0;
+    run += v[e];
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  int pos = base + incl - run;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 3; ++e) {
+    if (b0 + e < kLoadBins) bins[b0 + e] = pos;
+    pos += v[e];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += 1024) od[atomicAdd(&bins[kLoadBins - 1 - min(ld[i], kLoadBins - 1)], 1)] = i;
+}
+
 }  // namespace
 
 void launch_attn_bwd_dkdv(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStream_t st) {
+  {
+    KernelTimer timer("dkdv_order", st);
+    const int n = (int)(z.Hk * z.items_cap);
+    dkdv_load_clear_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(a.item_load, n);
+    if (z.T > 0)
+      dkdv_load_count_kernel<<<dim3((unsigned)((z.T + 255) / 256), (unsigned)z.Hk), 256, 0, st>>>(
+          a.blk_idx, a.cu, p.seqitem, (int)z.S, (int)z.T, (int)z.Hk, (int)z.chunk, (int)z.items_cap, a.item_load);
+    dkdv_order_kernel<<<(unsigned)z.Hk, 1024, 0, st>>>(a.item_load, p.totals, (int)z.items_cap, a.item_order);
+  }
   KernelTimer timer("attn_bwd_dkdv", st);
   attn_bwd_dkdv_kernel<<<dim3((unsigned)z.items_cap, (unsigned)z.Hk), 256, 0, st>>>(
       a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.dO, a.do_st, a.do_sh, a.nlse,
       a.delta, a.blk_idx, a.cu, p.blkbase, p.blk_seq, p.seqitem, p.totals, (int)z.S, (int)z.Hk, (int)z.chunk,
-      (int)z.items_cap, a.scale * kLog2e, a.scale, a.item_count, a.part_dk, a.part_dv, a.dk, a.dk_st, a.dk_sh, a.dv,
+      (int)z.items_cap, a.item_order, a.scale * kLog2e, a.scale, a.item_count, a.part_dk, a.part_dv, a.dk, a.dk_st, a.dk_sh, a.dv,
       a.dv_st, a.dv_sh);
 }
 

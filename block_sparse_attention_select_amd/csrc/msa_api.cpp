@@ -128,6 +128,8 @@ struct BwdWs {
   float* delta;
   float* nlse;
   int32_t* item_count;
+  int32_t* item_load;
+  int32_t* item_order;
   float* part_dk;
   float* part_dv;
 };
@@ -138,6 +140,8 @@ BwdWs carve_bwd(Carver& c, const Sizes& z) {
   w.delta = c.take<float>(z.T * z.Hq);
   w.nlse = c.take<float>(z.T * z.Hq);
   w.item_count = c.take<int32_t>(z.Hk * z.items_cap);
+  w.item_load = c.take<int32_t>(z.Hk * z.items_cap);
+  w.item_order = c.take<int32_t>(z.Hk * z.items_cap);
   w.part_dk = c.take<float>(z.Hk * z.items_cap * msa::kBlock * msa::kHeadDim);
   w.part_dv = c.take<float>(z.Hk * z.items_cap * msa::kBlock * msa::kHeadDim);
   return w;
@@ -292,6 +296,8 @@ int msa_attn_bwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh
   a.delta = w.delta;
   a.nlse = w.nlse;
   a.item_count = w.item_count;
+  a.item_load = w.item_load;
+  a.item_order = w.item_order;
   a.part_dk = w.part_dk;
   a.part_dv = w.part_dv;
   msa::launch_plan(cu_seqlens, z, w.plan, stream);

@@ -200,6 +200,8 @@ struct BwdArgs {
   float* delta;     // [T][Hq]
   float* nlse;      // [T][Hq] -LSE * log2(e), -inf for rows without keys
   int32_t* item_count;  // [Hk][items_cap]
+  int32_t* item_load;   // [Hk][items_cap] selecting queries per item (launch order only)
+  int32_t* item_order;  // [Hk][items_cap] items by decreasing load
   float* part_dk;   // [Hk][items_cap][128][128]
   float* part_dv;
 };
