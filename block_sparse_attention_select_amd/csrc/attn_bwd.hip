@@ -11,9 +11,10 @@
 // selected the block.
 //
 // Kernels:
-//   bwd_prep_kernel     Delta = rowsum(dO * O);
 //   attn_bwd_dq_kernel  token-major dQ, tiles of 16 tokens walking the union
-//                       of their blocks with K, V and K^T staged in LDS;
+//                       of their blocks with K, V and K^T staged in LDS; it
+//                       also forms Delta = rowsum(dO * O) and -LSE * log2(e)
+//                       for the dK/dV pass;
 //   attn_bwd_dkdv_kernel (attn_bwd_dkdv.hip) key-block-major dK/dV per chunk
 //                       of selecting queries;
 //   dkdv_reduce_kernel  sums the per-chunk slices of a block in chunk order
@@ -25,45 +26,6 @@
 namespace msa {
 
 namespace {
-
-// ---------------------------------------------------------------------------
-// Delta = rowsum(dO * O) per (token, query head), and the row's -LSE in base
-// 2 (-inf for a row without keys, so that exp2(s * scale_log2 + nlse) is 0
-// there): one wavefront per (token, KV head), four lanes per head row.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_prep_kernel(
-    const u16* __restrict__ o, int64_t o_st, int64_t o_sh,
-    const u16* __restrict__ dO, int64_t do_st, int64_t do_sh, const float* __restrict__ lse, int T, int Hk,
-    float* __restrict__ delta, float* __restrict__ nlse) {
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (wave >= T * Hk) return;
-  const int t = wave / Hk;
-  const int h = wave - t * Hk;
-  const int hq = h * kGroup + (lane >> 2);
-  const int quarter = lane & 3;
-  const u16* orow = o + (int64_t)t * o_st + (int64_t)hq * o_sh + 32 * quarter;
-  const u16* drow = dO + (int64_t)t * do_st + (int64_t)hq * do_sh + 32 * quarter;
-  float acc = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const u32x4 ov = *reinterpret_cast<const u32x4*>(orow + 8 * j);
-    const u32x4 dv = *reinterpret_cast<const u32x4*>(drow + 8 * j);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc += bf2f((u16)(ov[e] & 0xFFFFu)) * bf2f((u16)(dv[e] & 0xFFFFu));
-      acc += bf2f((u16)(ov[e] >> 16)) * bf2f((u16)(dv[e] >> 16));
-    }
-  }
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  const int64_t row = (int64_t)t * (Hk * kGroup) + hq;
-  if (quarter == 0) delta[row] = acc;
-  if (quarter == 1) {
-    const float l = lse[row];
-    nlse[row] = l > -INFINITY ? -l * kLog2e : -INFINITY;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // dQ.  Same tiling as the forward: one 16-wavefront workgroup per (tile of 16
@@ -85,11 +47,12 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
     const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
     const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
-    const u16* __restrict__ kt, const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
-    const float* __restrict__ lse, const float* __restrict__ delta,
+    const u16* __restrict__ kt, const u16* __restrict__ o, int64_t o_st, int64_t o_sh,
+    const u16* __restrict__ dO, int64_t do_st, int64_t do_sh, const float* __restrict__ lse,
     const int32_t* __restrict__ blk_idx, const int32_t* __restrict__ cu, const int32_t* __restrict__ blkbase,
     const int32_t* __restrict__ blk_seq, int S, int T, int Hk, float scale_log2, float scale,
-    u16* __restrict__ dq, int64_t dq_st, int64_t dq_sh) {
+    u16* __restrict__ dq, int64_t dq_st, int64_t dq_sh, float* __restrict__ delta, float* __restrict__ nlse,
+    int32_t* __restrict__ clear, int nclear) {
   __shared__ u32x4 kbuf[2][16][64];
   __shared__ u32x4 vbuf[2][16][64];
   __shared__ u32x4 tbuf[2][16][64];
@@ -99,6 +62,10 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
 
   const int h = blockIdx.y;
   const int t0 = blockIdx.x * kTileTok;
+  // zero the dK/dV item-load counters for the pass that follows
+  for (int i = (blockIdx.y * gridDim.x + blockIdx.x) * 64 * kDqWaves + threadIdx.x; i < nclear;
+       i += gridDim.x * gridDim.y * 64 * kDqWaves)
+    clear[i] = 0;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
@@ -164,10 +131,26 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
       qb[j][ds] = tok_ok[j] ? load_bf16x8(qrow + 32 * ds + 8 * g) : zero_bf16x8();
       db[j][ds] = tok_ok[j] ? load_bf16x8(drow + 32 * ds + 8 * g) : zero_bf16x8();
     }
-    const float l2 = lse[(int64_t)tc * Hq + h * kGroup + li];
+    const int64_t row = (int64_t)tc * Hq + h * kGroup + li;
+    const float l2 = lse[row];
     live[j] = tok_ok[j] && l2 > -INFINITY;
     lse2[j] = live[j] ? l2 * kLog2e : 0.f;
-    dl[j] = delta[(int64_t)tc * Hq + h * kGroup + li];
+    // Delta = rowsum(dO * O) of head li: this lane's 32 dims (those of its dO
+    // operand), then the four row groups
+    const u16* orow = o + (int64_t)tc * o_st + (int64_t)(h * kGroup + li) * o_sh;
+    float dsum = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      const bf16x8 ov = tok_ok[j] ? load_bf16x8(orow + 32 * ds + 8 * g) : zero_bf16x8();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum += (float)db[j][ds][e] * (float)ov[e];
+    }
+    dl[j] = sum_over_groups(dsum);
+    // Delta and -LSE in base 2 (-inf for a row without keys) for the dK/dV pass
+    if (tok_ok[j] && g == 0) {
+      delta[row] = dl[j];
+      nlse[row] = l2 > -INFINITY ? -l2 * kLog2e : -INFINITY;
+    }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) dqacc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -347,18 +330,13 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
 
 void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStream_t st) {
   const int T = (int)z.T, Hk = (int)z.Hk, S = (int)z.S;
-  const unsigned wgs_tok = (unsigned)((z.T * z.Hk + 3) / 4);
   launch_block_transpose(z, a.k, a.k_st, a.k_sh, a.cu, p, a.kt, st);
-  {
-    KernelTimer timer("bwd_prep", st);
-    bwd_prep_kernel<<<wgs_tok, 256, 0, st>>>(a.o, a.o_st, a.o_sh, a.dO, a.do_st, a.do_sh, a.lse, T, Hk, a.delta,
-                                                     a.nlse);
-  }
   {
     KernelTimer timer("attn_bwd_dq", st);
     attn_bwd_dq_kernel<<<dim3((unsigned)((z.T + kTileTok - 1) / kTileTok), (unsigned)Hk), 64 * kDqWaves, 0, st>>>(
-        a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.kt, a.dO, a.do_st, a.do_sh, a.lse, a.delta,
-        a.blk_idx, a.cu, p.blkbase, p.blk_seq, S, T, Hk, a.scale * kLog2e, a.scale, a.dq, a.dq_st, a.dq_sh);
+        a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.kt, a.o, a.o_st, a.o_sh, a.dO, a.do_st,
+        a.do_sh, a.lse, a.blk_idx, a.cu, p.blkbase, p.blk_seq, S, T, Hk, a.scale * kLog2e, a.scale, a.dq, a.dq_st,
+        a.dq_sh, a.delta, a.nlse, a.item_load, (int)(z.Hk * z.items_cap));
   }
   launch_attn_bwd_dkdv(z, a, p, st);
   {

@@ -325,13 +325,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // are selected by most of its queries, far blocks by few), and in index order
 // the heavy ones of the last sequence would run last.  The items are instead
 // launched by decreasing number of selecting queries (longest job first), which
-// only changes when each item runs, not what it computes.
+// only changes when each item runs, not what it computes.  The counters are
+// zeroed by the dQ pass that precedes this one.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void dkdv_load_clear_kernel(int32_t* __restrict__ load, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) load[i] = 0;
-}
-
 // One workgroup per (256 consecutive tokens, KV head), a thread per token.
 // The items those tokens can touch form one contiguous index range (items are
 // ordered by sequence, chunk, block), so the counts are gathered in an LDS
@@ -435,8 +431,6 @@ __global__ __launch_bounds__(1024) void dkdv_order_kernel(const int32_t* __restr
 void launch_attn_bwd_dkdv(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStream_t st) {
   {
     KernelTimer timer("dkdv_order", st);
-    const int n = (int)(z.Hk * z.items_cap);
-    dkdv_load_clear_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(a.item_load, n);
     if (z.T > 0)
       dkdv_load_count_kernel<<<dim3((unsigned)((z.T + 255) / 256), (unsigned)z.Hk), 256, 0, st>>>(
           a.blk_idx, a.cu, p.seqitem, (int)z.S, (int)z.T, (int)z.Hk, (int)z.chunk, (int)z.items_cap, a.item_load);
