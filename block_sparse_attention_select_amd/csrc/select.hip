@@ -12,18 +12,20 @@
 //
 // Kernels: select_prologue (features), select_scores (MFMA + per-row block
 // maximum), select_topk (wavefront arg-max rounds).
-#include "msa_internal.h"
+#include "attn_stage.h"
 
 namespace msa {
 
 namespace {
 
 // ---------------------------------------------------------------------------
-// 1. Features.  One wavefront per (token, head, q-or-k).  Lane l < 32 holds
-// the RoPE pair (l, l + 32); lane l >= 32 holds dims 32 + l and 64 + l.
-// The arithmetic order (square, sum, scale by 1/128, add eps, sqrt, divide,
-// multiply by x, multiply by (1 + w); rotation as two products and one sum)
-// is kept free of fused multiply-adds so every step rounds once in fp32.
+// 1. Features.  One wavefront per token: the RoPE angles of its position are
+// computed once (fp64, rounded to fp32) and applied to the q and k features of
+// every head.  Lane l < 32 holds the RoPE pair (l, l + 32); lane l >= 32 holds
+// dims 32 + l and 64 + l.  The arithmetic order (square, sum, scale by 1/128,
+// add eps, sqrt, divide, multiply by x, multiply by (1 + w); rotation as two
+// products and one sum) is kept free of fused multiply-adds so every step
+// rounds once in fp32.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void select_prologue_kernel(
     const u16* __restrict__ idx_q, int64_t sq_t, int64_t sq_h,
@@ -32,61 +34,67 @@ __global__ __launch_bounds__(256) void select_prologue_kernel(
     const int32_t* __restrict__ cu, int S, int T, int Hk,
     u16* __restrict__ qfeat, u16* __restrict__ kfeat) {
 #pragma clang fp contract(off)
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (wave >= T * Hk * 2) return;
-  const int which = wave & 1;
-  const int th = wave >> 1;
-  const int t = th / Hk;
-  const int h = th - t * Hk;
+  if (t >= T) return;
   const int s = find_seq(cu, S, t);
   const int pos = t - cu[s];
-  const u16* x = which ? idx_k + (int64_t)t * sk_t + (int64_t)h * sk_h
-                       : idx_q + (int64_t)t * sq_t + (int64_t)h * sq_h;
-  const u16* w = which ? w_k : w_q;
-  u16* out = (which ? kfeat : qfeat) + ((int64_t)t * Hk + h) * kHeadDim;
-
   const int d0 = lane < 32 ? lane : 32 + lane;
   const int d1 = d0 + 32;
-  const float x0 = bf2f(x[d0]);
-  const float x1 = bf2f(x[d1]);
-  float ss = x0 * x0 + x1 * x1;
-  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
-  const float ms = ss * (1.0f / 128.0f);
-  const float r = 1.0f / sqrtf(ms + eps);
-  float y0 = (x0 * r) * (1.0f + bf2f(w[d0]));
-  float y1 = (x1 * r) * (1.0f + bf2f(w[d1]));
+  float c = 1.f, sf = 0.f;
   if (lane < 32) {
     const double inv_freq = pow((double)rope_base, -(double)(2 * lane) / 64.0);
     const double theta = (double)pos * inv_freq;
     double sn, cs;
     sincos(theta, &sn, &cs);
-    const float c = (float)cs;
-    const float sf = (float)sn;
-    const float o0 = (y0 * c) - (y1 * sf);
-    const float o1 = (y1 * c) + (y0 * sf);
-    y0 = o0;
-    y1 = o1;
+    c = (float)cs;
+    sf = (float)sn;
   }
-  out[d0] = f2bf(y0);
-  out[d1] = f2bf(y1);
+  for (int h = 0; h < Hk; ++h) {
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const u16* x = which ? idx_k + (int64_t)t * sk_t + (int64_t)h * sk_h
+                           : idx_q + (int64_t)t * sq_t + (int64_t)h * sq_h;
+      const u16* w = which ? w_k : w_q;
+      u16* out = (which ? kfeat : qfeat) + ((int64_t)t * Hk + h) * kHeadDim;
+      const float x0 = bf2f(x[d0]);
+      const float x1 = bf2f(x[d1]);
+      float ss = x0 * x0 + x1 * x1;
+      for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+      const float ms = ss * (1.0f / 128.0f);
+      const float r = 1.0f / sqrtf(ms + eps);
+      float y0 = (x0 * r) * (1.0f + bf2f(w[d0]));
+      float y1 = (x1 * r) * (1.0f + bf2f(w[d1]));
+      if (lane < 32) {
+        const float o0 = (y0 * c) - (y1 * sf);
+        const float o1 = (y1 * c) + (y0 * sf);
+        y0 = o0;
+        y1 = o1;
+      }
+      out[d0] = f2bf(y0);
+      out[d1] = f2bf(y1);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
 // 2. Block scores.  One workgroup (4 wavefronts) per (query block, chunk of
-// kKeyChunk key blocks, head).  Wavefront w owns query rows 32w..32w+31 of
-// the query block; its bf16 features stay in registers as MFMA A operands.
-// Each key block (128 x 128 bf16) is staged in LDS with a 16-byte row pad so
-// the B-operand reads of 16 consecutive keys hit distinct banks.
+// kKeyChunk key blocks, head).  Wavefront w owns query rows 32w..32w+31 of the
+// query block; their bf16 features stay in registers as MFMA B operands of
+// S^T = K Q^T, so a lane's accumulators are keys of one query and the block
+// maximum is a per-lane maximum plus one exchange across the four row groups.
+// Key blocks are copied into LDS in A-operand order with global_load_lds, the
+// next one while the current one is used; each K operand read feeds the
+// MFMAs of both 16-query tiles of the wavefront.
 // ---------------------------------------------------------------------------
 constexpr int kKeyChunk = 8;
-constexpr int kRowPad = 17;  // uint4 per staged key row (16 data + 1 pad)
 
 __global__ __launch_bounds__(256) void select_scores_kernel(
     const u16* __restrict__ qfeat, const u16* __restrict__ kfeat, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ blkbase, const int32_t* __restrict__ blk_seq,
     const int32_t* __restrict__ totals, int Hk, int nbmax, float* __restrict__ scores) {
-  __shared__ uint4 ktile[kBlock * kRowPad];
+  // run kt * 4 + ds, lane li + 16 g: key 16 kt + li, dims 32 ds + 8 g .. +7
+  __shared__ u32x4 kst[2][32][64];
   const int gb = blockIdx.x;
   const int kc = blockIdx.y;
   const int h = blockIdx.z;
@@ -98,84 +106,84 @@ __global__ __launch_bounds__(256) void select_scores_kernel(
   const int c1 = min(min(c0 + kKeyChunk, qb + 1), nbmax);  // nbmax bound holds when lengths <= max_seqlen
   const int seq0 = cu[s];
   const int L = cu[s + 1] - seq0;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int li = lane & 15;
 
-  bf16x8 qa[2][4];
+  bf16x8 qf[2][4];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     const int qp = kBlock * qb + 32 * wave + 16 * rt + li;
     const u16* src = qfeat + ((int64_t)(seq0 + qp) * Hk + h) * kHeadDim;
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds) qa[rt][ds] = qp < L ? load_bf16x8(src + 32 * ds + 8 * g) : zero_bf16x8();
+    for (int ds = 0; ds < 4; ++ds) qf[rt][ds] = qp < L ? load_bf16x8(src + 32 * ds + 8 * g) : zero_bf16x8();
   }
 
-  for (int c = c0; c < c1; ++c) {
-    __syncthreads();
-    for (int i = threadIdx.x; i < kBlock * 16; i += 256) {
-      const int key = i >> 4;
-      const int ch = i & 15;
-      const int kp = kBlock * c + key;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (kp < L) v = *reinterpret_cast<const uint4*>(kfeat + ((int64_t)(seq0 + kp) * Hk + h) * kHeadDim + ch * 8);
-      ktile[key * kRowPad + ch] = v;
+  // wavefront w copies runs 8w .. 8w+7 (key tiles 2w, 2w+1); keys past the
+  // sequence end repeat its last key (they are masked as later than every query)
+  auto stage = [&](int c, int buf) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int kt = 2 * wave + e;
+      const int kp = min(kBlock * c + 16 * kt + li, L - 1);
+      const u16* src = kfeat + ((int64_t)(seq0 + kp) * Hk + h) * kHeadDim + 8 * g;
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) dma16(src + 32 * ds, lds_offset(&kst[buf][4 * kt + ds][0]));
     }
-    __syncthreads();
+  };
+  stage(c0, 0);
+  wait_copies();
+  wait_all_loads();
+  __syncthreads();
 
-    float rmax[2][4];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) rmax[rt][r] = -INFINITY;
-
+  for (int c = c0; c < c1; ++c) {
+    const int buf = (c - c0) & 1;
+    if (c + 1 < c1) stage(c + 1, buf ^ 1);
+    const bool diag = c == qb;
+    float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
-      bf16x8 kb[4];
+      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) kb[ds] = __builtin_bit_cast(bf16x8, ktile[(16 * kt + li) * kRowPad + 4 * ds + g]);
-      const int kp = kBlock * c + 16 * kt + li;
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ds = 0; ds < 4; ++ds) acc = mfma16x16x32(qa[rt][ds], kb[ds], acc);
+      for (int ds = 0; ds < 4; ++ds) {
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, kst[buf][4 * kt + ds][lane]);
+        a0 = mfma16x16x32(ka, qf[0][ds], a0);
+        a1 = mfma16x16x32(ka, qf[1][ds], a1);
+      }
+      if (diag) {  // key 16kt + 4g + r against query 32w + 16rt + li of the same block
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int qp = kBlock * qb + 32 * wave + 16 * rt + 4 * g + r;
-          const float v = kp <= qp ? acc[r] : -INFINITY;
-          rmax[rt][r] = fmaxf(rmax[rt][r], v);
+          const int key = 16 * kt + 4 * g + r;
+          if (key > 32 * wave + li) a0[r] = -INFINITY;
+          if (key > 32 * wave + 16 + li) a1[r] = -INFINITY;
         }
       }
+      m0 = fmaxf(m0, fmaxf(fmaxf(a0[0], a0[1]), fmaxf(a0[2], a0[3])));
+      m1 = fmaxf(m1, fmaxf(fmaxf(a1[0], a1[1]), fmaxf(a1[2], a1[3])));
     }
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = rmax[rt][r];
-        v = fmaxf(v, __shfl_xor(v, 1));
-        v = fmaxf(v, __shfl_xor(v, 2));
-        v = fmaxf(v, __shfl_xor(v, 4));
-        v = fmaxf(v, __shfl_xor(v, 8));
-        rmax[rt][r] = v;
-      }
-    if (li == 0) {
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int qp = kBlock * qb + 32 * wave + 16 * rt + 4 * g + r;
-          if (qp < L) scores[((int64_t)(seq0 + qp) * Hk + h) * nbmax + c] = rmax[rt][r];
-        }
+    m0 = max_over_groups(m0);
+    m1 = max_over_groups(m1);
+    if (g == 0) {
+      const int qp = kBlock * qb + 32 * wave + li;
+      if (qp < L) scores[((int64_t)(seq0 + qp) * Hk + h) * nbmax + c] = m0;
+      if (qp + 16 < L) scores[((int64_t)(seq0 + qp + 16) * Hk + h) * nbmax + c] = m1;
     }
+    wait_copies();
+    lds_barrier();
   }
 }
 
 // ---------------------------------------------------------------------------
-// 3. Top-k.  One wavefront per (token, head): 15 rounds of a wavefront-wide
-// arg-max over the block scores (score descending, id ascending), then the
-// 16 ids are ranked to ascending order.
+// 3. Top-k.  One wavefront per (token, head).  The candidates are blocks
+// 0 .. b-1 (b = own block); order: score descending, id ascending.
+//   * b <= 64: lane c holds candidate c; its rank is the number of candidates
+//     ordered before it, counted against each candidate in turn (broadcast
+//     from its lane).  The 15 of rank < 15 are written in id order (ballot
+//     prefix), then the own block.
+//   * b > 64: 15 rounds of a wavefront-wide arg-max over the candidates, each
+//     lane scanning its up to 16 (only as far as b reaches), then the 16 ids
+//     are ranked to ascending order.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
   return av > bv || (av == bv && ai < bi);
@@ -190,25 +198,38 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restric
   const int t = wave / Hk;
   const int s = find_seq(cu, S, t);
   const int pos = t - cu[s];
-  const int b = pos / kBlock;
+  const int b = __builtin_amdgcn_readfirstlane(pos / kBlock);
   int32_t* out = blk_idx + (int64_t)wave * kTopk;
   if (b < kTopk) {
     if (lane < kTopk) out[lane] = lane <= b ? lane : -1;
     return;
   }
   const float* row = scores + (int64_t)wave * nbmax;
-  constexpr int kPer = kMaxBlocks / 64;
-  float v[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int c = lane + 64 * j;
+  auto load = [&](int c) {
     float x = -INFINITY;
     if (c < b && c < nbmax) {
       x = row[c];
       if (x != x) x = -INFINITY;  // NaN ranks last
     }
-    v[j] = x;
+    return x;
+  };
+  if (b <= 64) {
+    const float v = load(lane);
+    int rank = 0;
+    for (int j = 0; j < b; ++j) {
+      const float vj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
+      rank += better(vj, j, v, lane) ? 1 : 0;
+    }
+    const bool chosen = lane < b && rank < kTopk - 1;
+    const uint64_t m = __ballot(chosen);
+    if (chosen) out[__popcll(m & ((1ull << lane) - 1ull))] = lane;
+    if (lane == 0) out[kTopk - 1] = b;
+    return;
   }
+  constexpr int kPer = kMaxBlocks / 64;
+  float v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) v[j] = 64 * j < b ? load(lane + 64 * j) : -INFINITY;
   unsigned taken = 0;
   int mine = -1;
   for (int k = 0; k < kTopk - 1; ++k) {
@@ -216,6 +237,7 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restric
     int bi = 0x7fffffff;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
+      if (64 * j >= b) break;
       const int c = lane + 64 * j;
       if (c < b && !((taken >> j) & 1u) && better(v[j], c, bv, bi)) {
         bv = v[j];
@@ -251,10 +273,9 @@ void launch_select(const Sizes& z, const u16* idx_q, int64_t sq_t, int64_t sq_h,
                    float eps, float rope_base, const int32_t* cu, const PlanBufs& p,
                    u16* qfeat, u16* kfeat, float* scores, int32_t* blk_idx, hipStream_t st) {
   const int T = (int)z.T, Hk = (int)z.Hk, S = (int)z.S;
-  const int64_t waves_pro = z.T * z.Hk * 2;
   {
     KernelTimer timer("select_prologue", st);
-    select_prologue_kernel<<<dim3((unsigned)((waves_pro + 3) / 4)), 256, 0, st>>>(
+    select_prologue_kernel<<<dim3((unsigned)((z.T + 3) / 4)), 256, 0, st>>>(
         idx_q, sq_t, sq_h, idx_k, sk_t, sk_h, w_q, w_k, eps, rope_base, cu, S, T, Hk, qfeat, kfeat);
   }
   const unsigned kchunks = (unsigned)((z.nbmax + kKeyChunk - 1) / kKeyChunk);
