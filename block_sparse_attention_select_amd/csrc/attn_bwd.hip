@@ -58,6 +58,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
   __shared__ u32x4 tbuf[2][16][64];
   __shared__ uint32_t bitmap[kUnionWords];
   __shared__ int ulist[kMaxUnion];
+  __shared__ int ukey0[kMaxUnion];  // first token of each union block
   __shared__ int nunion;
 
   const int h = blockIdx.y;
@@ -102,7 +103,10 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     int pos = incl - cnt;
     while (bits) {
       const int bit = __ffs(bits) - 1;
-      ulist[pos++] = gb_lo + 32 * lane + bit;
+      const int gbu = gb_lo + 32 * lane + bit;
+      const int sb = blk_seq[gbu];
+      ulist[pos] = gbu;
+      ukey0[pos++] = cu[sb] + kBlock * (gbu - blkbase[sb]);
       bits &= bits - 1u;
     }
     if (lane == 63) nunion = incl;
@@ -163,8 +167,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
   auto stage = [&](int w, int buf) {
     const int gb = __builtin_amdgcn_readfirstlane(ulist[w >> 1]);
     const int half = w & 1;
-    const int sb = blk_seq[gb];
-    const int kstart = cu[sb] + kBlock * (gb - blkbase[sb]);
+    const int kstart = __builtin_amdgcn_readfirstlane(ukey0[w >> 1]);
     const int ln = fresh_lane();
     const int kl = score_key(4 * half + (wave >> 2), ln & 15);
     if (kstart + kBlock <= T) {

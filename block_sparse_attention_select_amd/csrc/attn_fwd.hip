@@ -98,6 +98,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
   __shared__ u32x4 vbuf[2][32][64];
   __shared__ uint32_t bitmap[kUnionWords];
   __shared__ int ulist[kMaxUnion];
+  __shared__ int ukey0[kMaxUnion];  // first token of each union block
   __shared__ int nunion;
 
   const int h = blockIdx.y;
@@ -139,7 +140,10 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
     int pos = incl - cnt;
     while (bits) {
       const int bit = __ffs(bits) - 1;
-      ulist[pos++] = gb_lo + 32 * lane + bit;
+      const int gbu = gb_lo + 32 * lane + bit;
+      const int sb = blk_seq[gbu];
+      ulist[pos] = gbu;
+      ukey0[pos++] = cu[sb] + kBlock * (gbu - blkbase[sb]);
       bits &= bits - 1u;
     }
     if (lane == 63) nunion = incl;
@@ -177,8 +181,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
     const int gb = __builtin_amdgcn_readfirstlane(ulist[u]);
     const int ln = fresh_lane();
     if (wave < 8) {
-      const int sb = blk_seq[gb];
-      const int kstart = cu[sb] + kBlock * (gb - blkbase[sb]);
+      const int kstart = __builtin_amdgcn_readfirstlane(ukey0[u]);
       if (kstart + kBlock <= T) {
         const u16* base = k + (int64_t)kstart * k_st + (int64_t)h * k_sh;
         const uint32_t off = (uint32_t)(2 * (score_key(wave, ln & 15) * k_st + 8 * (ln >> 4)));
