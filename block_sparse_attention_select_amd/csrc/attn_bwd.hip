@@ -32,10 +32,10 @@ namespace {
 // consecutive tokens, KV head), wavefront w owning token w (its q and dO as
 // MFMA B operands and its dQ^T accumulators in registers, within 128 registers
 // so that four wavefronts share a SIMD).  The
-// workgroup walks the union of the tile's selected blocks in halves of 64
-// keys; each half's K and V (A operands of S^T = K Q^T and dP^T = V dO^T) and
-// K^T (A operand of dQ^T = K^T dS^T) are copied into one of two LDS buffers
-// while the previous half is used.
+// workgroup walks the union of the tile's selected blocks; each block's K and
+// V (A operands of S^T = K Q^T and dP^T = V dO^T) are copied into one of two
+// LDS buffers while the previous block is used, and the K^T operands of
+// dQ^T = K^T dS^T are read transposed from the same K copy.
 // ---------------------------------------------------------------------------
 constexpr int kTileTok = 16;
 constexpr int kTokPerWave = 1;
@@ -47,15 +47,14 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
     const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
     const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
-    const u16* __restrict__ kt, const u16* __restrict__ o, int64_t o_st, int64_t o_sh,
+    const u16* __restrict__ o, int64_t o_st, int64_t o_sh,
     const u16* __restrict__ dO, int64_t do_st, int64_t do_sh, const float* __restrict__ lse,
     const int32_t* __restrict__ blk_idx, const int32_t* __restrict__ cu, const int32_t* __restrict__ blkbase,
     const int32_t* __restrict__ blk_seq, int S, int T, int Hk, float scale_log2, float scale,
     u16* __restrict__ dq, int64_t dq_st, int64_t dq_sh, float* __restrict__ delta, float* __restrict__ nlse,
     int32_t* __restrict__ clear, int nclear) {
-  __shared__ u32x4 kbuf[2][16][64];
-  __shared__ u32x4 vbuf[2][16][64];
-  __shared__ u32x4 tbuf[2][16][64];
+  __shared__ u32x4 kbuf[2][32][64];
+  __shared__ u32x4 vbuf[2][32][64];
   __shared__ uint32_t bitmap[kUnionWords];
   __shared__ int ulist[kMaxUnion];
   __shared__ int ukey0[kMaxUnion];  // first token of each union block
@@ -112,7 +111,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     if (lane == 63) nunion = incl;
   }
   __syncthreads();
-  const int nsteps = 2 * nunion;  // halves of 64 keys
+  const int nsteps = nunion;
 
   int tok_t[kTokPerWave], tok_pos[kTokPerWave], tok_b[kTokPerWave], tok_base[kTokPerWave];
   bool tok_ok[kTokPerWave];
@@ -159,51 +158,51 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     for (int dt = 0; dt < 8; ++dt) dqacc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // step w: block ulist[w / 2], keys 64 * (w & 1) .. +63
-  // wavefront r copies run r of K, of V (local tile r / 4, step r % 4) and of
-  // K^T (runs dt * 4 + 2 * half + ks' of the block -> local run dt * 2 + ks')
-  static_assert(kDqWaves == 16, "one K, V and K^T run per wavefront");
-  const int kt_run = (wave >> 1) * 4 + (wave & 1);
-  auto stage = [&](int w, int buf) {
-    const int gb = __builtin_amdgcn_readfirstlane(ulist[w >> 1]);
-    const int half = w & 1;
-    const int kstart = __builtin_amdgcn_readfirstlane(ukey0[w >> 1]);
+  // step u: union block u.  Wavefronts 0-7 copy the four K runs of key tile w
+  // (run 4w + ds: keys score_key(w, .), dims 32 ds ..), wavefronts 8-15 the
+  // same runs of V; each copy is a scalar base plus a lane offset.
+  static_assert(kDqWaves == 16, "four K or V runs per wavefront");
+  auto stage = [&](int u, int buf) {
+    const int kstart = __builtin_amdgcn_readfirstlane(ukey0[u]);
     const int ln = fresh_lane();
-    const int kl = score_key(4 * half + (wave >> 2), ln & 15);
+    const int tile = wave & 7;
+    const bool is_k = wave < 8;
+    const u16* x = is_k ? k : v;
+    const int64_t x_st = is_k ? k_st : v_st, x_sh = is_k ? k_sh : v_sh;
+    u32x4* dst = is_k ? &kbuf[buf][4 * tile][0] : &vbuf[buf][4 * tile][0];
+    const int kl = score_key(tile, ln & 15);
     if (kstart + kBlock <= T) {
-      const uint32_t koff = (uint32_t)(2 * (kl * k_st + 8 * (ln >> 4)));
-      const uint32_t voff = (uint32_t)(2 * (kl * v_st + 8 * (ln >> 4)));
-      dma16s(k + (int64_t)kstart * k_st + (int64_t)h * k_sh + 32 * (wave & 3), koff, lds_offset(&kbuf[buf][wave][0]));
-      dma16s(v + (int64_t)kstart * v_st + (int64_t)h * v_sh + 32 * (wave & 3), voff, lds_offset(&vbuf[buf][wave][0]));
+      const u16* base = x + (int64_t)kstart * x_st + (int64_t)h * x_sh;
+      const uint32_t off = (uint32_t)(2 * (kl * x_st + 8 * (ln >> 4)));
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) dma16s(base + 32 * ds, off, lds_offset(dst + 64 * ds));
     } else {  // the pack's last block: keys past the end repeat the last token
       const int key = min(kstart + kl, T - 1);
-      const int d0 = 32 * (wave & 3) + 8 * (ln >> 4);
-      dma16(k + (int64_t)key * k_st + (int64_t)h * k_sh + d0, lds_offset(&kbuf[buf][wave][0]));
-      dma16(v + (int64_t)key * v_st + (int64_t)h * v_sh + d0, lds_offset(&vbuf[buf][wave][0]));
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds)
+        dma16(x + (int64_t)key * x_st + (int64_t)h * x_sh + 32 * ds + 8 * (ln >> 4), lds_offset(dst + 64 * ds));
     }
-    dma16s(kt + (((int64_t)gb * Hk + h) * 32 + kt_run + 2 * half) * 512, 16 * ln, lds_offset(&tbuf[buf][wave][0]));
   };
   if (nsteps > 0) stage(0, 0);
   wait_copies();
   wait_all_loads();
   __syncthreads();
 
-  for (int w = 0; w < nsteps; ++w) {
-    const int buf = w & 1;
-    if (w + 1 < nsteps) stage(w + 1, buf ^ 1);
-    const int gb = ulist[w >> 1];
-    const int half = w & 1;
+  for (int u = 0; u < nsteps; ++u) {
+    const int buf = u & 1;
+    if (u + 1 < nsteps) stage(u + 1, buf ^ 1);
+    const int gb = ulist[u];
     const uint64_t hits = __ballot(my_gb == gb);
 #pragma unroll
     for (int j = 0; j < kTokPerWave; ++j) {
       if (((hits >> (16 * j)) & 0xFFFFull) == 0) continue;
       const int c = gb - tok_base[j];
       const bool diag = (c == tok_b[j]);
-      const int key0 = kBlock * c + 64 * half;
-      if (diag && key0 > tok_pos[j]) continue;  // the whole half lies after the query
-      // two quarters of 32 keys: S^T, dP^T, then dS^T as one B operand of dQ^T
+      const int key0 = kBlock * c;
+      // four quarters of 32 keys: S^T, dP^T, then dS^T as one B operand of
+      // dQ^T; on the own block the quarters after the query are skipped
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq) {
+      for (int qq = 0; qq < 4; ++qq) {
         if (diag && key0 + 32 * qq > tok_pos[j]) break;
         // S^T and dP^T: four independent accumulation chains interleaved,
         // K / V operand reads eight ahead of the MFMAs that use them
@@ -255,16 +254,23 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
         }
         const bf16x8 dsf = pack_bf16x8(sacc[0], sacc[1]);
         {
+          // K^T operands read transposed from the K stage: keys 8g .. 8g+7 of
+          // the quarter (tiles 2qq, 2qq+1, rows 4g .. 4g+3) at dim 16dt + li
+          const uint32_t kq = lds_offset(&kbuf[buf][8 * qq][0]) + tr_lane_offset(fresh_lane());
           bf16x8 ta[8];
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt) ta[dt] = __builtin_bit_cast(bf16x8, tbuf[buf][dt * 2 + qq][lane]);
+          for (int dt = 0; dt < 8; ++dt) {
+            const uint32_t off = kq + (dt >> 1) * 1024 + (dt & 1) * 512;
+            const uint2 lo = read_tr16(off), hi = read_tr16(off + 4096);
+            ta[dt] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+          }
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) dqacc[j][dt] = mfma16x16x32(ta[dt], dsf, dqacc[j][dt]);
-          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
           }
           __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
         }
@@ -333,11 +339,10 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
 
 void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStream_t st) {
   const int T = (int)z.T, Hk = (int)z.Hk, S = (int)z.S;
-  launch_block_transpose(z, a.k, a.k_st, a.k_sh, a.cu, p, a.kt, st);
   {
     KernelTimer timer("attn_bwd_dq", st);
     attn_bwd_dq_kernel<<<dim3((unsigned)((z.T + kTileTok - 1) / kTileTok), (unsigned)Hk), 64 * kDqWaves, 0, st>>>(
-        a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.kt, a.o, a.o_st, a.o_sh, a.dO, a.do_st,
+        a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.o, a.o_st, a.o_sh, a.dO, a.do_st,
         a.do_sh, a.lse, a.blk_idx, a.cu, p.blkbase, p.blk_seq, S, T, Hk, a.scale * kLog2e, a.scale, a.dq, a.dq_st,
         a.dq_sh, a.delta, a.nlse, a.item_load, (int)(z.Hk * z.items_cap));
   }

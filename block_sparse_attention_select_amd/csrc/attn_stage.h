@@ -74,6 +74,26 @@ __device__ __forceinline__ int fresh_lane() {
   return x;
 }
 
+// Transposed operand reads.  ds_read_b64_tr_b16 hands output lane i of each
+// 16-lane group element e = source lane (4e + i/4)'s element i%4, where every
+// source lane points at 4 consecutive bf16.  Byte offset, within a staged
+// [ds][lane] tensor, of the 4 elements lane
+// (s, gg) (s = lane % 16, gg = lane / 16) hands to ds_read_b64_tr_b16 so that
+// the lane receives rows 4gg .. 4gg+3 of dim 16dt + s: source lane s of a
+// 16-lane group points at row 4gg + s/4, dims 16dt + 4(s%4) .. +3, i.e. at
+// (dt/2) * 1024 + (dt%2) * 512 + tr_lane_offset(lane).
+__device__ __forceinline__ uint32_t tr_lane_offset(int lane) {
+  const int s = lane & 15;
+  const int gg = lane >> 4;
+  return (uint32_t)((4 * gg + (s >> 2)) * 16 + ((s & 3) >> 1) * 256 + 8 * (s & 1));
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 read_tr16(uint32_t lds_byte) {
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(uintptr_t)lds_byte);
+  return __builtin_bit_cast(uint2, r);
+}
+
 // Key of row m of score tile kt (16 keys per tile, 8 tiles per block).  Tiles
 // 2s and 2s+1 together cover keys 32s..32s+31 such that the accumulator rows a
 // lane of group g holds (4g..4g+3 of each tile) are the eight consecutive keys

@@ -124,7 +124,6 @@ FwdWs carve_fwd(Carver& c, const Sizes& z) {
 
 struct BwdWs {
   PlanBufs plan;
-  u16* kt;
   float* delta;
   float* nlse;
   int32_t* item_count;
@@ -136,7 +135,6 @@ struct BwdWs {
 BwdWs carve_bwd(Carver& c, const Sizes& z) {
   BwdWs w;
   w.plan = carve_plan(c, z);
-  w.kt = c.take<u16>(z.nblk_cap * z.Hk * msa::kHeadDim * msa::kBlock);
   w.delta = c.take<float>(z.T * z.Hq);
   w.nlse = c.take<float>(z.T * z.Hq);
   w.item_count = c.take<int32_t>(z.Hk * z.items_cap);
@@ -292,7 +290,6 @@ int msa_attn_bwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh
   a.dq = (u16*)dq; a.dq_st = dq_st; a.dq_sh = dq_sh;
   a.dk = (u16*)dk; a.dk_st = dk_st; a.dk_sh = dk_sh;
   a.dv = (u16*)dv; a.dv_st = dv_st; a.dv_sh = dv_sh;
-  a.kt = w.kt;
   a.delta = w.delta;
   a.nlse = w.nlse;
   a.item_count = w.item_count;

@@ -196,7 +196,6 @@ struct BwdArgs {
   u16* dk; int64_t dk_st, dk_sh;
   u16* dv; int64_t dv_st, dv_sh;
   // workspace
-  u16* kt;          // [nblk_cap][Hk][128 d][128 keys] K transposed per block
   float* delta;     // [T][Hq]
   float* nlse;      // [T][Hq] -LSE * log2(e), -inf for rows without keys
   int32_t* item_count;  // [Hk][items_cap]
