@@ -37,6 +37,9 @@ design notes of the repository):
   own block plus the 15 best of blocks 0..b-1, higher score first and the
   lower block id first on equal scores; ids are returned ascending, padded
   with -1;
+* the optional forced initial block (the "init" of the pages' init/local/
+  causal rules) keeps block 0 as well, leaving 14 slots for the best of
+  blocks 1..b-1;
 * attention keys for query i are the keys j <= i of its selected blocks in
   its own sequence; softmax scale 1/sqrt(128); query head g uses KV head
   g // (Hq / Hk).
@@ -199,24 +202,31 @@ def block_max_scores(qf: np.ndarray, kf: np.ndarray, block: int,
     return out
 
 
-def select_row(scores: np.ndarray, own: int, topk: int) -> Tuple[List[int], float]:
+def select_row(scores: np.ndarray, own: int, topk: int, force_init: bool = False) -> Tuple[List[int], float]:
     """Selection for one query whose own block is ``own``.
 
     Returns the ascending block ids and the relative gap between the last
-    selected and the first unselected non-own score (inf when every causal
-    block fits, i.e. own + 1 <= topk).
+    selected and the first unselected score among the blocks chosen by score
+    (inf when every causal block fits, i.e. own + 1 <= topk).
+
+    ``force_init`` is the "init" rule of the pages' init/local/causal rules
+    ([PR] commit message), read as: block 0 is always kept, like the own block,
+    and the remaining topk - 2 slots go to the best of blocks 1 .. own-1.
     """
     if own + 1 <= topk:
         return list(range(own + 1)), float("inf")
-    cand = np.arange(own)
-    sc = scores[:own].astype(F32)
+    first = 1 if force_init else 0
+    forced = [0, own] if force_init else [own]
+    n_pick = topk - len(forced)
+    cand = np.arange(first, own)
+    sc = scores[first:own].astype(F32)
     order = np.lexsort((cand, -sc.astype(F64)))       # score descending, id ascending
-    keep = [int(c) for c in cand[order[:topk - 1]]]
-    s_last = F64(sc[order[topk - 2]])
-    s_next = F64(sc[order[topk - 1]])
+    keep = [int(c) for c in cand[order[:n_pick]]]
+    s_last = F64(sc[order[n_pick - 1]])
+    s_next = F64(sc[order[n_pick]])
     den = max(abs(s_last), abs(s_next))
     gap = abs(s_last - s_next) / den if den > 0 else 0.0
-    return sorted(keep + [own]), float(gap)
+    return sorted(keep + forced), float(gap)
 
 
 @dataclass
@@ -232,13 +242,15 @@ class SelectResult:
 def index_select(idx_q: np.ndarray, idx_k: np.ndarray, w_q: np.ndarray, w_k: np.ndarray,
                  cu_seqlens: Sequence[int], block: int = 128, topk: int = 16,
                  eps: float = 1e-6, rope_base: float = 1e7, rope_dims: int = 64,
-                 rows: Optional[np.ndarray] = None, round_bf16: bool = True) -> SelectResult:
+                 rows: Optional[np.ndarray] = None, round_bf16: bool = True,
+                 force_init: bool = False) -> SelectResult:
     """Frozen lightning-indexer block selection ([M31] section 1, [PR]).
 
     ``idx_q``: [T, Hk, D]; ``idx_k``: [T, Hk, D] or [T, 1, D] (one key head
     shared by every index head).  Index head h selects the blocks for KV head
     h.  ``rows`` restricts the output to a subset of tokens (sampled checks);
-    the returned arrays then follow ``rows``.
+    the returned arrays then follow ``rows``.  ``force_init`` keeps block 0 in
+    every selection (see ``select_row``).
     """
     idx_q = np.asarray(idx_q, dtype=F32)
     idx_k = np.asarray(idx_k, dtype=F32)
@@ -267,7 +279,7 @@ def index_select(idx_q: np.ndarray, idx_k: np.ndarray, w_q: np.ndarray, w_k: np.
             sc = block_max_scores(qbuf, kf, block, rows=mine - a)
             for n, t in enumerate(mine):
                 own = int(pos[t]) // block
-                ids, g = select_row(sc[n], own, topk)
+                ids, g = select_row(sc[n], own, topk, force_init)
                 slot = row_slot[int(t)]
                 blk[slot, h, :len(ids)] = ids
                 gap[slot, h] = g

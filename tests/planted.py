@@ -33,11 +33,14 @@ def load_planted():
             assert p < seq["length"]
             idx_k[int(cu[s]) + p, 0, 64] = x
     w = torch.zeros(D, dtype=torch.float32)
-    expected = []
-    for e in spec["expected"]:
-        t = int(cu[e["seq"]]) + e["pos"]
-        ids = list(e["ids"]) + [-1] * (spec["topk"] - len(e["ids"]))
-        expected.append((t, ids, e["why"]))
+    def cases(key):
+        out = []
+        for e in spec[key]:
+            t = int(cu[e["seq"]]) + e["pos"]
+            ids = list(e["ids"]) + [-1] * (spec["topk"] - len(e["ids"]))
+            out.append((t, ids, e["why"]))
+        return out
     return dict(idx_q=idx_q.to(torch.bfloat16), idx_k=idx_k.to(torch.bfloat16),
                 w_q=w.to(torch.bfloat16), w_k=w.to(torch.bfloat16), cu_seqlens=cu,
-                lengths=lengths, block=B, topk=spec["topk"], expected=expected)
+                lengths=lengths, block=B, topk=spec["topk"], expected=cases("expected"),
+                expected_force_init=cases("expected_force_init"))

@@ -127,6 +127,53 @@ def test_planted_selection_golden():
     assert res.gap[P["expected"][3][0], 0] > 1e-2
 
 
+def test_planted_selection_force_init_golden():
+    """The forced initial block, on hand-derived planted cases."""
+    P = load_planted()
+    res = O.index_select(f32(P["idx_q"]), f32(P["idx_k"]), f32(P["w_q"]), f32(P["w_k"]),
+                         P["cu_seqlens"], block=P["block"], topk=P["topk"], force_init=True)
+    for t, ids, why in P["expected_force_init"]:
+        assert list(res.blk_idx[t, 0]) == ids, (t, why)
+
+
+def test_force_init_brute_force():
+    """The forced initial block against an independent brute force: every
+    (block 0, own block, 14-subset of 1..b-1) candidate set is ranked by the
+    scores it keeps; the best set (highest sorted scores, lower ids on ties)
+    must be the oracle's.  Tiny rows only (b = 16, 17)."""
+    import itertools
+    rng = np.random.default_rng(7)
+    for trial in range(6):
+        own = 16 + trial % 2
+        sc = rng.integers(-3, 4, own).astype(np.float32)  # small integers: plenty of ties
+        ids, _ = O.select_row(sc, own, 16, force_init=True)
+        best = None
+        for sub in itertools.combinations(range(1, own), 14):
+            key = sorted(((-float(sc[c]), c) for c in sub))
+            if best is None or key < best[0]:
+                best = (key, sub)
+        assert ids == sorted([0, own] + list(best[1])), (trial, ids)
+
+
+def test_force_init_relation_to_plain_selection():
+    """With block 0 among the plain choice the rule changes nothing; otherwise
+    it replaces the weakest block chosen by score with block 0."""
+    rng = np.random.default_rng(8)
+    for trial in range(200):
+        own = int(rng.integers(16, 80))
+        sc = rng.standard_normal(own).astype(np.float32)
+        if trial % 3 == 0:
+            sc[0] = -10.0  # block 0 certainly not chosen by score
+        plain, _ = O.select_row(sc, own, 16)
+        forced, _ = O.select_row(sc, own, 16, force_init=True)
+        if 0 in plain:
+            assert forced == plain
+        else:
+            chosen = [c for c in plain if c != own]
+            weakest = min(chosen, key=lambda c: (sc[c], -c))
+            assert forced == sorted([c for c in plain if c != weakest] + [0])
+
+
 # ---------------------------------------------------------------- selection invariants
 def test_selection_invariants_random():
     p = synth.make_custom_pack([2600, 700, 2300], num_q_heads=2, num_kv_heads=2, seed=5)
