@@ -219,6 +219,20 @@ def main():
     fwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
 
+    # the forced-initial-block selection variant on the same pack (not part of the step)
+    blk_init = torch.empty_like(blk)
+    ei = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(2):
+        msa.msa_index_select(iq, ik, wq, wk, cu, p.max_seqlen, force_init=True, out=blk_init,
+                             workspace=ws[msa.MSA_OP_SELECT])
+    ei[0].record()
+    for _ in range(args.steps):
+        msa.msa_index_select(iq, ik, wq, wk, cu, p.max_seqlen, force_init=True, out=blk_init,
+                             workspace=ws[msa.MSA_OP_SELECT])
+    ei[1].record()
+    torch.cuda.synchronize()
+    sel_init_ms = ei[0].elapsed_time(ei[1]) / args.steps
+
     # per-kernel durations: HIP event pairs recorded by the library on the launch stream
     msa.msa_timing_collect()
     msa.msa_timing_enable(True)
@@ -281,6 +295,7 @@ def main():
                    "seq_lens": p.lengths, "num_q_heads": Hq, "num_kv_heads": Hk, "head_dim": D,
                    "block_size": 128, "topk_blocks": 16, "parallelism": "none (1 GPU)"},
         "select_ms": round(sel_ms, 4),
+        "select_force_init_ms": round(sel_init_ms, 4),
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
         "fwd_bwd_ms": round(fb_ms, 4),

@@ -31,12 +31,13 @@ MSA_ERR_INVALID_ARG = -1
 MSA_ERR_UNSUPPORTED = -2
 MSA_ERR_WORKSPACE = -3
 MSA_ERR_HIP = -4
+MSA_SELECT_FORCE_INIT = 1
 MSA_OP_SELECT = 1
 MSA_OP_FWD = 2
 MSA_OP_BWD = 3
 
 # Every symbol include/msa.h declares.
-EXPORTED = ("msa_workspace_size", "msa_index_select", "msa_attn_fwd", "msa_attn_bwd",
+EXPORTED = ("msa_workspace_size", "msa_index_select", "msa_index_select_ex", "msa_attn_fwd", "msa_attn_bwd",
             "msa_status_string", "msa_check_cu_seqlens", "msa_timing_enable", "msa_timing_collect",
             "msa_version")
 
@@ -82,6 +83,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.msa_index_select.argtypes = [ctypes.POINTER(MsaDims), _P, _I64, _I64, _P, _I64, _I64, _P, _P,
                                      _F, _F, _I32, _P, _P, _P, _SZ, _P]
     lib.msa_index_select.restype = _I32
+    lib.msa_index_select_ex.argtypes = [ctypes.POINTER(MsaDims), _P, _I64, _I64, _P, _I64, _I64, _P, _P,
+                                        _F, _F, _I32, ctypes.c_uint32, _P, _P, _P, _SZ, _P]
+    lib.msa_index_select_ex.restype = _I32
     lib.msa_attn_fwd.argtypes = [ctypes.POINTER(MsaDims), _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64,
                                  _P, _P, _F, _P, _I64, _I64, _P, _P, _SZ, _P]
     lib.msa_attn_fwd.restype = _I32
@@ -157,9 +161,10 @@ def _check(st: int, where: str):
 
 def msa_index_select(idx_q: torch.Tensor, idx_k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
                      cu_seqlens: torch.Tensor, max_seqlen: int, *, eps: float = 1e-6, rope_base: float = 1e7,
-                     rope_dims: int = 64, out: Optional[torch.Tensor] = None,
+                     rope_dims: int = 64, force_init: bool = False, out: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Block ids [T, Hk, 16] (int32, ascending, -1 padded) chosen by the frozen indexer."""
+    """Block ids [T, Hk, 16] (int32, ascending, -1 padded) chosen by the frozen indexer.
+    ``force_init`` keeps block 0 in every selection (msa_index_select_ex, MSA_SELECT_FORCE_INIT)."""
     lib = load()
     T, Hk, _ = idx_q.shape
     sq = _bf16_view(idx_q, "idx_q")
@@ -170,10 +175,17 @@ def msa_index_select(idx_q: torch.Tensor, idx_k: torch.Tensor, w_q: torch.Tensor
     if out is None:
         out = torch.empty(T, Hk, 16, dtype=torch.int32, device=idx_q.device)
     ws, nbytes = _workspace(dims, MSA_OP_SELECT, idx_q.device, workspace)
-    st = lib.msa_index_select(ctypes.byref(dims), _ptr(idx_q), sq[0], sq[1], _ptr(idx_k), sk[0], sk[1],
-                              _ptr(w_q.contiguous()), _ptr(w_k.contiguous()), float(eps), float(rope_base),
-                              int(rope_dims), _ptr(cu_seqlens), _ptr(out), _ptr(ws), nbytes, _stream(idx_q))
-    _check(st, "msa_index_select")
+    if force_init:
+        st = lib.msa_index_select_ex(ctypes.byref(dims), _ptr(idx_q), sq[0], sq[1], _ptr(idx_k), sk[0], sk[1],
+                                     _ptr(w_q.contiguous()), _ptr(w_k.contiguous()), float(eps), float(rope_base),
+                                     int(rope_dims), MSA_SELECT_FORCE_INIT, _ptr(cu_seqlens), _ptr(out), _ptr(ws),
+                                     nbytes, _stream(idx_q))
+        _check(st, "msa_index_select_ex")
+    else:
+        st = lib.msa_index_select(ctypes.byref(dims), _ptr(idx_q), sq[0], sq[1], _ptr(idx_k), sk[0], sk[1],
+                                  _ptr(w_q.contiguous()), _ptr(w_k.contiguous()), float(eps), float(rope_base),
+                                  int(rope_dims), _ptr(cu_seqlens), _ptr(out), _ptr(ws), nbytes, _stream(idx_q))
+        _check(st, "msa_index_select")
     return out
 
 

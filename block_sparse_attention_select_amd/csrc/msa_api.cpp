@@ -212,8 +212,17 @@ int msa_index_select(const msa_dims* dims, const void* idx_q, int64_t sq_t, int6
                      int64_t sk_t, int64_t sk_h, const void* w_q, const void* w_k, float eps, float rope_base,
                      int32_t rope_dims, const int32_t* cu_seqlens, int32_t* blk_idx, void* workspace,
                      size_t workspace_bytes, hipStream_t stream) {
+  return msa_index_select_ex(dims, idx_q, sq_t, sq_h, idx_k, sk_t, sk_h, w_q, w_k, eps, rope_base, rope_dims, 0u,
+                             cu_seqlens, blk_idx, workspace, workspace_bytes, stream);
+}
+
+int msa_index_select_ex(const msa_dims* dims, const void* idx_q, int64_t sq_t, int64_t sq_h, const void* idx_k,
+                        int64_t sk_t, int64_t sk_h, const void* w_q, const void* w_k, float eps, float rope_base,
+                        int32_t rope_dims, uint32_t flags, const int32_t* cu_seqlens, int32_t* blk_idx,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = check_dims(dims);
   if (st != MSA_OK) return st;
+  if (flags & ~MSA_SELECT_FORCE_INIT) return MSA_ERR_INVALID_ARG;
   if (rope_dims != 64) return MSA_ERR_UNSUPPORTED;
   if (!(eps >= 0.f) || !(rope_base > 1.f) || rope_base != rope_base) return MSA_ERR_INVALID_ARG;
   if (dims->total_tokens == 0) return MSA_OK;
@@ -227,8 +236,8 @@ int msa_index_select(const msa_dims* dims, const void* idx_q, int64_t sq_t, int6
   SelectWs w = carve_select(c, z);
   msa::launch_plan(cu_seqlens, z, w.plan, stream);
   msa::launch_select(z, (const u16*)idx_q, sq_t, sq_h, (const u16*)idx_k, sk_t, sk_h, (const u16*)w_q,
-                     (const u16*)w_k, eps, rope_base, cu_seqlens, w.plan, w.qfeat, w.kfeat, w.scores, blk_idx,
-                     stream);
+                     (const u16*)w_k, eps, rope_base, cu_seqlens, w.plan, (flags & MSA_SELECT_FORCE_INIT) != 0,
+                     w.qfeat, w.kfeat, w.scores, blk_idx, stream);
   return launch_status();
 }
 

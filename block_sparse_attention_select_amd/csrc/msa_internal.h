@@ -172,7 +172,7 @@ void launch_plan(const int32_t* cu, const Sizes& z, const PlanBufs& p, hipStream
 void launch_select(const Sizes& z, const u16* idx_q, int64_t sq_t, int64_t sq_h,
                    const u16* idx_k, int64_t sk_t, int64_t sk_h, const u16* w_q, const u16* w_k,
                    float eps, float rope_base, const int32_t* cu, const PlanBufs& p,
-                   u16* qfeat, u16* kfeat, float* scores, int32_t* blk_idx, hipStream_t st);
+                   bool force_init, u16* qfeat, u16* kfeat, float* scores, int32_t* blk_idx, hipStream_t st);
 
 void launch_block_transpose(const Sizes& z, const u16* x, int64_t st_t, int64_t st_h,
                             const int32_t* cu, const PlanBufs& p, u16* xt, hipStream_t st);

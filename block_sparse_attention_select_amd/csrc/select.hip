@@ -176,7 +176,8 @@ __global__ __launch_bounds__(256) void select_scores_kernel(
 
 // ---------------------------------------------------------------------------
 // 3. Top-k.  One wavefront per (token, head).  The candidates are blocks
-// 0 .. b-1 (b = own block); order: score descending, id ascending.
+// 0 .. b-1 (b = own block), or 1 .. b-1 when block 0 is forced in (then 14
+// are chosen instead of 15); order: score descending, id ascending.
 //   * b <= 64: lane c holds candidate c; its rank is the number of candidates
 //     ordered before it, counted against each candidate in turn (broadcast
 //     from its lane).  The 15 of rank < 15 are written in id order (ballot
@@ -191,7 +192,8 @@ __device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
 
 __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restrict__ scores,
                                                           const int32_t* __restrict__ cu, int S, int T,
-                                                          int Hk, int nbmax, int32_t* __restrict__ blk_idx) {
+                                                          int Hk, int nbmax, int force_init,
+                                                          int32_t* __restrict__ blk_idx) {
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (wave >= T * Hk) return;
@@ -204,6 +206,8 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restric
     if (lane < kTopk) out[lane] = lane <= b ? lane : -1;
     return;
   }
+  const int first = force_init ? 1 : 0;   // first candidate block
+  const int npick = kTopk - 1 - first;     // blocks chosen by score
   const float* row = scores + (int64_t)wave * nbmax;
   auto load = [&](int c) {
     float x = -INFINITY;
@@ -216,23 +220,26 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restric
   if (b <= 64) {
     const float v = load(lane);
     int rank = 0;
-    for (int j = 0; j < b; ++j) {
+    for (int j = first; j < b; ++j) {
       const float vj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
       rank += better(vj, j, v, lane) ? 1 : 0;
     }
-    const bool chosen = lane < b && rank < kTopk - 1;
+    const bool chosen = lane >= first && lane < b && rank < npick;
     const uint64_t m = __ballot(chosen);
-    if (chosen) out[__popcll(m & ((1ull << lane) - 1ull))] = lane;
-    if (lane == 0) out[kTopk - 1] = b;
+    if (chosen) out[first + __popcll(m & ((1ull << lane) - 1ull))] = lane;
+    if (lane == 0) {
+      if (first) out[0] = 0;
+      out[kTopk - 1] = b;
+    }
     return;
   }
   constexpr int kPer = kMaxBlocks / 64;
   float v[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) v[j] = 64 * j < b ? load(lane + 64 * j) : -INFINITY;
-  unsigned taken = 0;
+  unsigned taken = (first && lane == 0) ? 1u : 0u;  // a forced block 0 is not a candidate
   int mine = -1;
-  for (int k = 0; k < kTopk - 1; ++k) {
+  for (int k = 0; k < npick; ++k) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
@@ -256,6 +263,7 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restric
     if (lane == (bi & 63)) taken |= 1u << (bi >> 6);
     if (lane == k) mine = bi;
   }
+  if (first && lane == npick) mine = 0;
   if (lane == kTopk - 1) mine = b;
   int rank = 0;
 #pragma unroll
@@ -271,7 +279,7 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restric
 void launch_select(const Sizes& z, const u16* idx_q, int64_t sq_t, int64_t sq_h,
                    const u16* idx_k, int64_t sk_t, int64_t sk_h, const u16* w_q, const u16* w_k,
                    float eps, float rope_base, const int32_t* cu, const PlanBufs& p,
-                   u16* qfeat, u16* kfeat, float* scores, int32_t* blk_idx, hipStream_t st) {
+                   bool force_init, u16* qfeat, u16* kfeat, float* scores, int32_t* blk_idx, hipStream_t st) {
   const int T = (int)z.T, Hk = (int)z.Hk, S = (int)z.S;
   {
     KernelTimer timer("select_prologue", st);
@@ -288,7 +296,7 @@ void launch_select(const Sizes& z, const u16* idx_q, int64_t sq_t, int64_t sq_h,
   {
     KernelTimer timer("select_topk", st);
     select_topk_kernel<<<dim3((unsigned)((waves_top + 3) / 4)), 256, 0, st>>>(scores, cu, S, T, Hk, (int)z.nbmax,
-                                                                             blk_idx);
+                                                                             force_init ? 1 : 0, blk_idx);
   }
 }
 

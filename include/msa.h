@@ -60,6 +60,9 @@ extern "C" {
 #define MSA_ERR_WORKSPACE (-3)   /* workspace null, misaligned (256 B) or smaller than needed */
 #define MSA_ERR_HIP (-4)         /* the HIP runtime reported an error                         */
 
+/* Selection flags of msa_index_select_ex. */
+#define MSA_SELECT_FORCE_INIT 1u /* keep block 0 in every selection (the "init" rule) */
+
 #define MSA_OP_SELECT 1
 #define MSA_OP_FWD 2
 #define MSA_OP_BWD 3
@@ -113,6 +116,23 @@ int msa_index_select(const msa_dims* dims,
                      float eps, float rope_base, int32_t rope_dims,
                      const int32_t* cu_seqlens, int32_t* blk_idx,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * msa_index_select with selection flags ([PR] kernel-tuning commit message:
+ * the indexer applies init/local/causal rules before top-k).  flags = 0 is
+ * msa_index_select.  MSA_SELECT_FORCE_INIT reads "init" as a forced initial
+ * block: when b >= 16, block 0 is kept like block b and the other 14 slots go
+ * to the best of blocks 1..b-1 (same order); b < 16 is unchanged (all of
+ * 0..b).  Unknown flag bits return MSA_ERR_INVALID_ARG.  Same workspace as
+ * msa_index_select (MSA_OP_SELECT).
+ */
+int msa_index_select_ex(const msa_dims* dims,
+                        const void* idx_q, int64_t sq_t, int64_t sq_h,
+                        const void* idx_k, int64_t sk_t, int64_t sk_h,
+                        const void* w_q, const void* w_k,
+                        float eps, float rope_base, int32_t rope_dims, uint32_t flags,
+                        const int32_t* cu_seqlens, int32_t* blk_idx,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Block-sparse GQA attention forward ([M31] section 1: each query attends to

@@ -125,6 +125,13 @@ def test_select_and_bwd_argument_errors_launch_nothing():
     assert sel(n=0) == msa.MSA_ERR_WORKSPACE
     assert sel(d=dims(total_tokens=0, num_seqs=0, max_seqlen=0), iq=None, ws=None) == msa.MSA_OK
 
+    sel_ex = lambda flags, **kw: lib.msa_index_select_ex(
+        ctypes.byref(d), FAKE, 128, 128, FAKE, 128, 128, FAKE, FAKE, 1e-6, 1e7, 64, flags, FAKE, FAKE, FAKE,
+        kw.get("n", 1 << 40), None)
+    assert sel_ex(2) == msa.MSA_ERR_INVALID_ARG            # unknown flag bit
+    assert sel_ex(0x80000000) == msa.MSA_ERR_INVALID_ARG
+    assert sel_ex(msa.MSA_SELECT_FORCE_INIT, n=0) == msa.MSA_ERR_WORKSPACE
+
     def bwd(dv_sh=128, ws=FAKE, n=1 << 40, lse=FAKE):
         return lib.msa_attn_bwd(ctypes.byref(d), FAKE, 2048, 128, FAKE, 128, 128, FAKE, 128, 128, FAKE, 2048, 128,
                                 lse, FAKE, 2048, 128, FAKE, FAKE, 0.088, FAKE, 2048, 128, FAKE, 128, 128,

@@ -1,0 +1,81 @@
+"""GPU parity of the selection variants against the oracle.
+
+The forced initial block (msa_index_select_ex with MSA_SELECT_FORCE_INIT; the
+"init" of the pages' init/local/causal rules, radixark/miles PR #4581 commit
+message, read as block 0 always kept): hand-derived planted cases, seeded
+packs on both top-k paths (up to 64 candidate blocks, and more), and attention
+forward + backward on the forced selection.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from planted import load_planted
+
+pytestmark = pytest.mark.gpu
+
+TIE = 1e-3
+
+
+def f32(t):
+    return t.float().cpu().numpy()
+
+
+def dev(t):
+    return t.to("cuda")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def test_force_init_planted_golden(gpu_lib):
+    P = load_planted()
+    cu = torch.from_numpy(P["cu_seqlens"])
+    args = (dev(P["idx_q"]), dev(P["idx_k"]), dev(P["w_q"]), dev(P["w_k"]), dev(cu), max(P["lengths"]))
+    forced = gpu_lib.msa_index_select(*args, force_init=True).cpu().numpy()
+    for t, ids, why in P["expected_force_init"]:
+        assert list(forced[t, 0]) == ids, (t, why)
+    plain = gpu_lib.msa_index_select(*args).cpu().numpy()
+    for t, ids, why in P["expected"]:
+        assert list(plain[t, 0]) == ids, (t, why)
+
+
+@pytest.mark.parametrize("lengths,hk,seed", [([2600, 700, 2300], 1, 51), ([3000, 1100], 2, 52), ([9000], 1, 53)])
+def test_force_init_parity(gpu_lib, lengths, hk, seed):
+    """[9000] has up to 70 candidate blocks: the arg-max-rounds path of top-k."""
+    p = synth.make_custom_pack(lengths, num_q_heads=16 * hk, num_kv_heads=hk, seed=seed)
+    res = O.index_select(f32(p.idx_q), f32(p.idx_k), f32(p.w_q), f32(p.w_k), p.cu_seqlens.numpy(), force_init=True)
+    g = gpu_lib.msa_index_select(dev(p.idx_q), dev(p.idx_k), dev(p.w_q), dev(p.w_k), dev(p.cu_seqlens),
+                                 p.max_seqlen, force_init=True).cpu().numpy()
+    diff = (g != res.blk_idx).any(axis=2)
+    tie = res.gap < TIE
+    say(f"[force_init {lengths} hk={hk}] rows={diff.size} near-tie={int(tie.sum())} "
+        f"mismatch-outside={int((diff & ~tie).sum())}")
+    assert (diff & ~tie).sum() == 0
+    # block 0 is in every row
+    assert (g[:, :, 0] == 0).all()
+
+
+def test_force_init_attention(gpu_lib):
+    """Forward and backward on the forced selection (oracle ids) against the oracle."""
+    msa = gpu_lib
+    p = synth.make_custom_pack([2700, 900], seed=54)
+    cu = p.cu_seqlens.numpy()
+    res = O.index_select(f32(p.idx_q), f32(p.idx_k), f32(p.w_q), f32(p.w_k), cu, force_init=True)
+    blk = dev(torch.from_numpy(res.blk_idx))
+    q, k, v, do = dev(p.q), dev(p.k), dev(p.v), dev(p.do)
+    o, lse = msa.msa_attn_fwd(q, k, v, blk, dev(p.cu_seqlens), p.max_seqlen)
+    dq, dk, dv = msa.msa_attn_bwd(q, k, v, o, lse, do, blk, dev(p.cu_seqlens), p.max_seqlen)
+    torch.cuda.synchronize()
+    s = 1 / math.sqrt(128)
+    Ow, Lw = O.attention_forward(f32(p.q), f32(p.k), f32(p.v), res.blk_idx, cu, s)
+    dQw, dKw, dVw = O.attention_backward(f32(p.q), f32(p.k), f32(p.v), f32(p.do), res.blk_idx, cu, s)
+    rel = lambda a, b: float(np.linalg.norm(np.asarray(a, np.float64) - b) / max(np.linalg.norm(b), 1e-30))
+    assert np.abs(f32(o) - Ow).max() <= 2e-2
+    assert np.abs(lse.cpu().numpy() - Lw).max() <= 1e-3
+    assert rel(f32(dq), dQw) <= 1e-2 and rel(f32(dk), dKw) <= 1e-2 and rel(f32(dv), dVw) <= 1e-2
