@@ -12,6 +12,8 @@ from .msa_oracle import (  # noqa: F401
     index_select,
     indexer_features,
     key_set,
+    qk_norm_rope_backward,
+    qk_norm_rope_forward,
     rope_cos_sin,
     rope_rotate_half,
     round_to_bf16,

@@ -404,3 +404,50 @@ def selectors_of_block(blk_idx: np.ndarray, cu_seqlens: Sequence[int], seq_id: i
     a, b = int(cu[seq_id]), int(cu[seq_id + 1])
     hit = (blk_idx[a:b, head, :] == block_id).any(axis=1)
     return a + np.nonzero(hit)[0]
+
+
+# ---------------------------------------------------------------------------
+# Attention-side q/k norm and partial RoPE  ([M31] section 1: "per-head gemma
+# q/k norm, RoPE on the first 64 dims (base 1e7)"; [MB] Architecture Notes:
+# per-head QK RMSNorm, gemma-style x * (1 + w), partial RoPE on 64 of 128
+# channels).  The step applied to the attention's own q and k before the
+# block-sparse kernel, forward and backward.
+# ---------------------------------------------------------------------------
+
+def qk_norm_rope_forward(x: np.ndarray, w: np.ndarray, pos: np.ndarray, eps: float = 1e-6,
+                         base: float = 1e7, rope_dims: int = 64) -> np.ndarray:
+    """q^ (or k^) = bf16(RoPE_p(RMSNorm(x) * (1 + w))) per head: the same
+    arithmetic as the indexer features, on the attention's [N, H, 128] q or k
+    with one [128] weight shared by the heads.  Returns fp32 holding bf16."""
+    return indexer_features(x, w, pos, eps, base, rope_dims, round_bf16=True)
+
+
+def qk_norm_rope_backward(x: np.ndarray, w: np.ndarray, pos: np.ndarray, dz: np.ndarray,
+                          eps: float = 1e-6, base: float = 1e7,
+                          rope_dims: int = 64) -> Tuple[np.ndarray, np.ndarray]:
+    """Vector-Jacobian product of z = RoPE_p(y), y = x * r * (1 + w),
+    r = 1 / sqrt(mean(x^2) + eps), in fp64 (with the same fp32 cos/sin as the
+    forward).  ``x``, ``dz``: [N, H, D]; returns (dx [N, H, D], dw [D]).
+
+    Written from the definition: RoPE is a rotation, so dy = RoPE_p^T(dz)
+    (rotation by -angle); with g = dy * (1 + w), dx_k = r g_k - x_k r^3
+    sum_j(g_j x_j) / D; and dw_j = sum over rows of dy_j x_j r.
+    """
+    x = np.asarray(x, dtype=F64)
+    dz = np.asarray(dz, dtype=F64)
+    w = np.asarray(w, dtype=F64)
+    D = x.shape[-1]
+    half = rope_dims // 2
+    c, s = rope_cos_sin(pos, base, rope_dims)
+    shape = (x.shape[0],) + (1,) * (x.ndim - 2) + (half,)
+    c = c.astype(F64).reshape(shape)
+    s = s.astype(F64).reshape(shape)
+    dy = dz.copy()
+    dy[..., :half] = c * dz[..., :half] + s * dz[..., half:rope_dims]
+    dy[..., half:rope_dims] = -s * dz[..., :half] + c * dz[..., half:rope_dims]
+    r = 1.0 / np.sqrt((x * x).mean(axis=-1) + eps)
+    g = dy * (1.0 + w)
+    dot = (g * x).sum(axis=-1)
+    dx = r[..., None] * g - x * (r ** 3 * dot / D)[..., None]
+    dw = (dy * x * r[..., None]).reshape(-1, D).sum(axis=0)
+    return dx, dw

@@ -400,3 +400,64 @@ def test_zero_query_uniform_attention_closed_form():
             dv_want[keys, 0] += do[i, g] / n
     assert np.all(dk == 0)
     np.testing.assert_allclose(dv, dv_want, atol=1e-12)
+
+
+# ---------------------------------------------------------------- attention-side q/k norm + RoPE (f2)
+def _qk_loss(x, w, pos, dz):
+    """sum(dz * z) with z the unrounded fp32 forward (norm then RoPE)."""
+    z = O.indexer_features(x, w, pos, 1e-6, 1e7, 64, round_bf16=False)
+    return float((np.asarray(z, np.float64) * dz).sum())
+
+
+def test_qk_norm_rope_backward_finite_differences():
+    rng = np.random.default_rng(11)
+    N, H, D = 3, 2, 128
+    x = rng.standard_normal((N, H, D)).astype(np.float32)
+    w = (0.3 * rng.standard_normal(D)).astype(np.float32)
+    pos = np.array([0, 5, 1234])
+    dz = rng.standard_normal((N, H, D))
+    dx, dw = O.qk_norm_rope_backward(x, w, pos, dz)
+    h = 1e-2
+    for (n, hh, d) in [(0, 0, 3), (1, 1, 40), (2, 0, 70), (2, 1, 127), (1, 0, 31), (0, 1, 32)]:
+        xp, xm = x.copy(), x.copy()
+        xp[n, hh, d] += h
+        xm[n, hh, d] -= h
+        fd = (_qk_loss(xp, w, pos, dz) - _qk_loss(xm, w, pos, dz)) / (2 * h)
+        assert abs(fd - dx[n, hh, d]) <= 2e-3 * max(1.0, abs(dx[n, hh, d])), (n, hh, d, fd, dx[n, hh, d])
+    for d in [0, 17, 33, 64, 100]:
+        wp, wm = w.copy(), w.copy()
+        wp[d] += h
+        wm[d] -= h
+        fd = (_qk_loss(x, wp, pos, dz) - _qk_loss(x, wm, pos, dz)) / (2 * h)
+        assert abs(fd - dw[d]) <= 2e-3 * max(1.0, abs(dw[d])), (d, fd, dw[d])
+
+
+def test_qk_norm_rope_backward_closed_forms():
+    rng = np.random.default_rng(12)
+    N, H, D = 4, 3, 128
+    x = rng.standard_normal((N, H, D)).astype(np.float32)
+    dz = rng.standard_normal((N, H, D))
+    pos = np.array([0, 1, 77, 4000])
+    # eps = 0: RMSNorm is scale-invariant, so the gradient is orthogonal to x
+    w = (0.2 * rng.standard_normal(D)).astype(np.float32)
+    dx, _ = O.qk_norm_rope_backward(x, w, pos, dz, eps=0.0)
+    assert np.abs((dx * x).sum(axis=-1)).max() < 1e-9 * np.abs(dx).max() * D
+    # w = -1: y = 0 for every x, so dx = 0, while dw_j = sum dy_j x_j r
+    dx, dw = O.qk_norm_rope_backward(x, -np.ones(D, np.float32), pos, dz)
+    assert np.abs(dx).max() == 0.0
+    assert np.abs(dw).max() > 0
+    # position 0: RoPE is the identity, so with w = 0 the backward is RMSNorm's alone,
+    # r (dz - x r^2 mean(dz x)), for every head
+    dx0, dw0 = O.qk_norm_rope_backward(x[:1], np.zeros(D, np.float32), pos[:1], dz[:1])
+    xx = x[0].astype(np.float64)
+    r = 1 / np.sqrt((xx * xx).mean(axis=-1) + 1e-6)
+    want = r[:, None] * dz[0] - xx * (r ** 3 * (dz[0] * xx).mean(axis=-1))[:, None]
+    assert np.allclose(dx0[0], want, rtol=1e-12, atol=1e-12)
+    assert np.allclose(dw0, (dz[0] * xx * r[:, None]).sum(axis=0), rtol=1e-12, atol=1e-12)
+    # rotation: dims >= 64 pass through RoPE, so with x fixed and dz nonzero only
+    # there, the result does not depend on the position
+    dzh = dz.copy()
+    dzh[..., :64] = 0
+    a, _ = O.qk_norm_rope_backward(x, w, np.array([0, 0, 0, 0]), dzh)
+    b, _ = O.qk_norm_rope_backward(x, w, pos, dzh)
+    assert np.allclose(a, b, rtol=0, atol=0)
