@@ -233,6 +233,28 @@ def main():
     torch.cuda.synchronize()
     sel_init_ms = ei[0].elapsed_time(ei[1]) / args.steps
 
+    # attention-side q/k norm + partial RoPE, forward and backward, on this pack (not part of the step)
+    gw = torch.Generator().manual_seed(args.seed + 77)
+    wq_a = (0.1 * torch.randn(128, generator=gw)).bfloat16().to(dev)
+    wk_a = (0.1 * torch.randn(128, generator=gw)).bfloat16().to(dev)
+    qh, kh = torch.empty_like(q), torch.empty_like(k)
+    ws_qk = torch.empty(max(msa.msa_workspace_size(dims, msa.MSA_OP_QKNORM_BWD), 1), dtype=torch.uint8, device=dev)
+    qk_fwd = lambda: msa.msa_qk_norm_rope_fwd(q, k, wq_a, wk_a, cu, p.max_seqlen, q_out=qh, k_out=kh)
+    qk_bwd = lambda: msa.msa_qk_norm_rope_bwd(q, k, wq_a, wk_a, cu, p.max_seqlen, dq, dk, workspace=ws_qk)
+    qk_ms = {}
+    for name, fn in (("fwd", qk_fwd), ("bwd", qk_bwd)):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        qk_ms[name] = e0.elapsed_time(e1) / args.steps
+    qk_elems = q.numel() + k.numel()
+    qk_bytes = {"fwd": 2 * qk_elems * 2, "bwd": 3 * qk_elems * 2}  # bf16 in + out (bwd: x and dz in, dx out)
+
     # per-kernel durations: HIP event pairs recorded by the library on the launch stream
     msa.msa_timing_collect()
     msa.msa_timing_enable(True)
@@ -296,6 +318,10 @@ def main():
                    "block_size": 128, "topk_blocks": 16, "parallelism": "none (1 GPU)"},
         "select_ms": round(sel_ms, 4),
         "select_force_init_ms": round(sel_init_ms, 4),
+        "qk_norm_rope_fwd_ms": round(qk_ms["fwd"], 4),
+        "qk_norm_rope_bwd_ms": round(qk_ms["bwd"], 4),
+        "qk_norm_rope_fwd_hbm_frac": round(qk_bytes["fwd"] / (qk_ms["fwd"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "qk_norm_rope_bwd_hbm_frac": round(qk_bytes["bwd"] / (qk_ms["bwd"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
         "fwd_bwd_ms": round(fb_ms, 4),

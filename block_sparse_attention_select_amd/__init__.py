@@ -32,12 +32,14 @@ MSA_ERR_UNSUPPORTED = -2
 MSA_ERR_WORKSPACE = -3
 MSA_ERR_HIP = -4
 MSA_SELECT_FORCE_INIT = 1
+MSA_OP_QKNORM_BWD = 4
 MSA_OP_SELECT = 1
 MSA_OP_FWD = 2
 MSA_OP_BWD = 3
 
 # Every symbol include/msa.h declares.
 EXPORTED = ("msa_workspace_size", "msa_index_select", "msa_index_select_ex", "msa_attn_fwd", "msa_attn_bwd",
+            "msa_qk_norm_rope_fwd", "msa_qk_norm_rope_bwd",
             "msa_status_string", "msa_check_cu_seqlens", "msa_timing_enable", "msa_timing_collect",
             "msa_version")
 
@@ -94,6 +96,13 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                  _P, _P, _I64, _I64, _P, _P, _F,
                                  _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _SZ, _P]
     lib.msa_attn_bwd.restype = _I32
+    lib.msa_qk_norm_rope_fwd.argtypes = [ctypes.POINTER(MsaDims), _P, _I64, _I64, _P, _I64, _I64, _P, _P,
+                                         _F, _F, _I32, _P, _P, _I64, _I64, _P, _I64, _I64, _P]
+    lib.msa_qk_norm_rope_fwd.restype = _I32
+    lib.msa_qk_norm_rope_bwd.argtypes = [ctypes.POINTER(MsaDims), _P, _I64, _I64, _P, _I64, _I64, _P, _P,
+                                         _F, _F, _I32, _P, _P, _I64, _I64, _P, _I64, _I64,
+                                         _P, _I64, _I64, _P, _I64, _I64, _P, _P, _P, _SZ, _P]
+    lib.msa_qk_norm_rope_bwd.restype = _I32
     lib.msa_status_string.argtypes = [_I32]
     lib.msa_status_string.restype = ctypes.c_char_p
     lib.msa_check_cu_seqlens.argtypes = [ctypes.POINTER(MsaDims), _P, _P]
@@ -240,6 +249,54 @@ def msa_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Ten
                           _ptr(dv), sdv[0], sdv[1], _ptr(ws), nbytes, _stream(q))
     _check(st, "msa_attn_bwd")
     return dq, dk, dv
+
+
+def msa_qk_norm_rope_fwd(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
+                         cu_seqlens: torch.Tensor, max_seqlen: int, *, eps: float = 1e-6, rope_base: float = 1e7,
+                         rope_dims: int = 64, q_out: Optional[torch.Tensor] = None,
+                         k_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention-side per-head gemma norm + partial RoPE of q [T, Hq, 128] and k [T, Hk, 128]."""
+    lib = load()
+    T, Hq, _ = q.shape
+    Hk = k.shape[1]
+    if q_out is None:
+        q_out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if k_out is None:
+        k_out = torch.empty(k.shape, dtype=k.dtype, device=k.device)
+    sq, sk, sqo, sko = (_bf16_view(t, n) for t, n in ((q, "q"), (k, "k"), (q_out, "q_out"), (k_out, "k_out")))
+    dims = _dims_for(cu_seqlens, max_seqlen, Hq, Hk, T)
+    st = lib.msa_qk_norm_rope_fwd(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1],
+                                  _ptr(w_q.contiguous()), _ptr(w_k.contiguous()), float(eps), float(rope_base),
+                                  int(rope_dims), _ptr(cu_seqlens), _ptr(q_out), sqo[0], sqo[1], _ptr(k_out),
+                                  sko[0], sko[1], _stream(q))
+    _check(st, "msa_qk_norm_rope_fwd")
+    return q_out, k_out
+
+
+def msa_qk_norm_rope_bwd(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
+                         cu_seqlens: torch.Tensor, max_seqlen: int, dq_hat: torch.Tensor, dk_hat: torch.Tensor, *,
+                         eps: float = 1e-6, rope_base: float = 1e7, rope_dims: int = 64,
+                         workspace: Optional[torch.Tensor] = None):
+    """Backward of msa_qk_norm_rope_fwd: returns dq, dk (bf16) and dw_q, dw_k (fp32 [128])."""
+    lib = load()
+    T, Hq, _ = q.shape
+    Hk = k.shape[1]
+    dq = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    dk = torch.empty(k.shape, dtype=k.dtype, device=k.device)
+    dw_q = torch.empty(128, dtype=torch.float32, device=q.device)
+    dw_k = torch.empty(128, dtype=torch.float32, device=q.device)
+    views = [_bf16_view(t, n) for t, n in ((q, "q"), (k, "k"), (dq_hat, "dq_hat"), (dk_hat, "dk_hat"),
+                                           (dq, "dq"), (dk, "dk"))]
+    sq, sk, sdqh, sdkh, sdq, sdk = views
+    dims = _dims_for(cu_seqlens, max_seqlen, Hq, Hk, T)
+    ws, nbytes = _workspace(dims, MSA_OP_QKNORM_BWD, q.device, workspace)
+    st = lib.msa_qk_norm_rope_bwd(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1],
+                                  _ptr(w_q.contiguous()), _ptr(w_k.contiguous()), float(eps), float(rope_base),
+                                  int(rope_dims), _ptr(cu_seqlens), _ptr(dq_hat), sdqh[0], sdqh[1], _ptr(dk_hat),
+                                  sdkh[0], sdkh[1], _ptr(dq), sdq[0], sdq[1], _ptr(dk), sdk[0], sdk[1], _ptr(dw_q),
+                                  _ptr(dw_k), _ptr(ws), nbytes, _stream(q))
+    _check(st, "msa_qk_norm_rope_bwd")
+    return dq, dk, dw_q, dw_k
 
 
 def msa_check_cu_seqlens(cu_seqlens: torch.Tensor, total_tokens: int, max_seqlen: int,

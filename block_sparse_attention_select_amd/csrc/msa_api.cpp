@@ -151,6 +151,7 @@ size_t ws_bytes_for(const Sizes& z, int op) {
     case MSA_OP_SELECT: carve_select(c, z); break;
     case MSA_OP_FWD: carve_fwd(c, z); break;
     case MSA_OP_BWD: carve_bwd(c, z); break;
+    case MSA_OP_QKNORM_BWD: c.take<float>((int64_t)(msa::kQkBwdMaxRows + msa::kQkBwdMaxRows / 16 + 1) * 256); break;
     default: return 0;
   }
   return c.off;
@@ -203,7 +204,8 @@ int msa_workspace_size(const msa_dims* dims, int op, size_t* bytes) {
   if (!bytes) return MSA_ERR_INVALID_ARG;
   int st = check_dims(dims);
   if (st != MSA_OK) return st;
-  if (op != MSA_OP_SELECT && op != MSA_OP_FWD && op != MSA_OP_BWD) return MSA_ERR_INVALID_ARG;
+  if (op != MSA_OP_SELECT && op != MSA_OP_FWD && op != MSA_OP_BWD && op != MSA_OP_QKNORM_BWD)
+    return MSA_ERR_INVALID_ARG;
   *bytes = dims->total_tokens == 0 ? 0 : ws_bytes_for(sizes_of(dims), op);
   return MSA_OK;
 }
@@ -308,6 +310,74 @@ int msa_attn_bwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh
   a.part_dv = w.part_dv;
   msa::launch_plan(cu_seqlens, z, w.plan, stream);
   msa::launch_attn_bwd(z, a, w.plan, stream);
+  return launch_status();
+}
+
+int msa_qk_norm_rope_fwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh, const void* k,
+                         int64_t k_st, int64_t k_sh, const void* w_q, const void* w_k, float eps, float rope_base,
+                         int32_t rope_dims, const int32_t* cu_seqlens, void* q_out, int64_t qo_st, int64_t qo_sh,
+                         void* k_out, int64_t ko_st, int64_t ko_sh, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MSA_OK) return st;
+  if (rope_dims != 64) return MSA_ERR_UNSUPPORTED;
+  if (!(eps >= 0.f) || !(rope_base > 1.f) || rope_base != rope_base) return MSA_ERR_INVALID_ARG;
+  if (dims->total_tokens == 0) return MSA_OK;
+  if (!in_view(q, q_st, q_sh) || !in_view(k, k_st, k_sh) || !out_view(q_out, qo_st, qo_sh) ||
+      !out_view(k_out, ko_st, ko_sh))
+    return MSA_ERR_INVALID_ARG;
+  if (!w_q || !w_k || !aligned(w_q, 2) || !aligned(w_k, 2) || !cu_seqlens || !aligned(cu_seqlens, 4))
+    return MSA_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(dims);
+  msa::QkNormArgs a{};
+  a.q = (const u16*)q; a.q_st = q_st; a.q_sh = q_sh;
+  a.k = (const u16*)k; a.k_st = k_st; a.k_sh = k_sh;
+  a.w_q = (const u16*)w_q; a.w_k = (const u16*)w_k;
+  a.eps = eps; a.rope_base = rope_base;
+  a.cu = cu_seqlens;
+  a.qo = (u16*)q_out; a.qo_st = qo_st; a.qo_sh = qo_sh;
+  a.ko = (u16*)k_out; a.ko_st = ko_st; a.ko_sh = ko_sh;
+  msa::launch_qk_norm_fwd(z, a, stream);
+  return launch_status();
+}
+
+int msa_qk_norm_rope_bwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh, const void* k,
+                         int64_t k_st, int64_t k_sh, const void* w_q, const void* w_k, float eps, float rope_base,
+                         int32_t rope_dims, const int32_t* cu_seqlens, const void* dq_hat, int64_t dqh_st,
+                         int64_t dqh_sh, const void* dk_hat, int64_t dkh_st, int64_t dkh_sh, void* dq, int64_t dq_st,
+                         int64_t dq_sh, void* dk, int64_t dk_st, int64_t dk_sh, float* dw_q, float* dw_k,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MSA_OK) return st;
+  if (rope_dims != 64) return MSA_ERR_UNSUPPORTED;
+  if (!(eps >= 0.f) || !(rope_base > 1.f) || rope_base != rope_base) return MSA_ERR_INVALID_ARG;
+  if (!dw_q || !dw_k || !aligned(dw_q, 4) || !aligned(dw_k, 4)) return MSA_ERR_INVALID_ARG;
+  if (dims->total_tokens == 0) {  // no rows: the weight gradients are zero
+    msa::QkNormArgs a{};
+    a.dw_q = dw_q;
+    a.dw_k = dw_k;
+    msa::launch_qk_norm_bwd(sizes_of(dims), a, nullptr, stream);
+    return launch_status();
+  }
+  if (!in_view(q, q_st, q_sh) || !in_view(k, k_st, k_sh) || !in_view(dq_hat, dqh_st, dqh_sh) ||
+      !in_view(dk_hat, dkh_st, dkh_sh) || !out_view(dq, dq_st, dq_sh) || !out_view(dk, dk_st, dk_sh))
+    return MSA_ERR_INVALID_ARG;
+  if (!w_q || !w_k || !aligned(w_q, 2) || !aligned(w_k, 2) || !cu_seqlens || !aligned(cu_seqlens, 4))
+    return MSA_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(dims);
+  st = check_ws(workspace, workspace_bytes, ws_bytes_for(z, MSA_OP_QKNORM_BWD));
+  if (st != MSA_OK) return st;
+  msa::QkNormArgs a{};
+  a.q = (const u16*)q; a.q_st = q_st; a.q_sh = q_sh;
+  a.k = (const u16*)k; a.k_st = k_st; a.k_sh = k_sh;
+  a.w_q = (const u16*)w_q; a.w_k = (const u16*)w_k;
+  a.eps = eps; a.rope_base = rope_base;
+  a.cu = cu_seqlens;
+  a.dqh = (const u16*)dq_hat; a.dqh_st = dqh_st; a.dqh_sh = dqh_sh;
+  a.dkh = (const u16*)dk_hat; a.dkh_st = dkh_st; a.dkh_sh = dkh_sh;
+  a.qo = (u16*)dq; a.qo_st = dq_st; a.qo_sh = dq_sh;
+  a.ko = (u16*)dk; a.ko_st = dk_st; a.ko_sh = dk_sh;
+  a.dw_q = dw_q; a.dw_k = dw_k;
+  msa::launch_qk_norm_bwd(z, a, (float*)workspace, stream);
   return launch_status();
 }
 

@@ -182,6 +182,28 @@ void launch_attn_fwd(const Sizes& z, const u16* q, int64_t q_st, int64_t q_sh,
                      const int32_t* blk_idx, const int32_t* cu, const PlanBufs& p, float scale,
                      u16* o, int64_t o_st, int64_t o_sh, float* lse, hipStream_t st);
 
+// Attention-side q/k norm + RoPE.  Forward: q, k in, qo, ko out.  Backward:
+// q, k (the forward's inputs) and dqh, dkh (gradients of its outputs) in,
+// dx written to qo, ko; weight gradients to dw_q, dw_k.
+struct QkNormArgs {
+  const u16* q; int64_t q_st, q_sh;
+  const u16* k; int64_t k_st, k_sh;
+  const u16* w_q;
+  const u16* w_k;
+  float eps, rope_base;
+  const int32_t* cu;
+  const u16* dqh; int64_t dqh_st, dqh_sh;
+  const u16* dkh; int64_t dkh_st, dkh_sh;
+  u16* qo; int64_t qo_st, qo_sh;
+  u16* ko; int64_t ko_st, ko_sh;
+  float* dw_q;
+  float* dw_k;
+};
+constexpr int kQkBwdMaxRows = 1024;  // workgroups of the backward (weight-gradient partial rows)
+int qk_norm_bwd_rows(int64_t T);
+void launch_qk_norm_fwd(const Sizes& z, const QkNormArgs& a, hipStream_t st);
+void launch_qk_norm_bwd(const Sizes& z, const QkNormArgs& a, float* partial, hipStream_t st);
+
 struct BwdArgs {
   const u16* q; int64_t q_st, q_sh;
   const u16* k; int64_t k_st, k_sh;

@@ -66,6 +66,7 @@ extern "C" {
 #define MSA_OP_SELECT 1
 #define MSA_OP_FWD 2
 #define MSA_OP_BWD 3
+#define MSA_OP_QKNORM_BWD 4
 
 /* Longest sequence this build accepts (1024 blocks of 128 tokens). */
 #define MSA_MAX_SEQLEN 131072
@@ -133,6 +134,55 @@ int msa_index_select_ex(const msa_dims* dims,
                         float eps, float rope_base, int32_t rope_dims, uint32_t flags,
                         const int32_t* cu_seqlens, int32_t* blk_idx,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Attention-side q/k norm and partial RoPE, forward ([M31] section 1: per-head
+ * gemma q/k norm, RoPE on the first 64 dims, base 1e7; [MB] Architecture
+ * Notes: per-head QK RMSNorm x * (1 + w), partial RoPE).  The step that
+ * produces the q and k the attention entry points take.
+ *
+ * For every head of q (weights w_q) and of k (weights w_k), at token t's
+ * sequence-local position p:
+ *   out = bf16( RoPE_p( x / sqrt(mean(x^2) + eps) * (1 + w) ) )
+ * with the same arithmetic as the indexer features of msa_index_select (fp32,
+ * fp64 angles rounded to fp32, one rounding to bf16).
+ *
+ *   q [T, Hq, 128], k [T, Hk, 128] bf16 inputs, their own strides;
+ *   w_q, w_k [128] bf16; q_out [T, Hq, 128], k_out [T, Hk, 128] bf16 outputs
+ *   with their own strides (they may not alias the inputs).
+ * No workspace.
+ */
+int msa_qk_norm_rope_fwd(const msa_dims* dims,
+                         const void* q, int64_t q_st, int64_t q_sh,
+                         const void* k, int64_t k_st, int64_t k_sh,
+                         const void* w_q, const void* w_k,
+                         float eps, float rope_base, int32_t rope_dims,
+                         const int32_t* cu_seqlens,
+                         void* q_out, int64_t qo_st, int64_t qo_sh,
+                         void* k_out, int64_t ko_st, int64_t ko_sh, hipStream_t stream);
+
+/*
+ * Backward of msa_qk_norm_rope_fwd: given the forward's inputs q, k and the
+ * gradients dq_hat, dk_hat of its outputs (e.g. msa_attn_bwd's dq, dk),
+ *   dy = RoPE_p^T(dz), g = dy * (1 + w),
+ *   dx = r g - x r^3 sum(g x) / 128,  r = 1 / sqrt(mean(x^2) + eps)
+ * written as bf16 dq, dk (own strides), and the weight gradients
+ *   dw[j] = sum over tokens and heads of dy_j x_j r
+ * as fp32 dw_q[128], dw_k[128] (overwritten, summed in a fixed order).
+ * Workspace: msa_workspace_size(..., MSA_OP_QKNORM_BWD).
+ */
+int msa_qk_norm_rope_bwd(const msa_dims* dims,
+                         const void* q, int64_t q_st, int64_t q_sh,
+                         const void* k, int64_t k_st, int64_t k_sh,
+                         const void* w_q, const void* w_k,
+                         float eps, float rope_base, int32_t rope_dims,
+                         const int32_t* cu_seqlens,
+                         const void* dq_hat, int64_t dqh_st, int64_t dqh_sh,
+                         const void* dk_hat, int64_t dkh_st, int64_t dkh_sh,
+                         void* dq, int64_t dq_st, int64_t dq_sh,
+                         void* dk, int64_t dk_st, int64_t dk_sh,
+                         float* dw_q, float* dw_k,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Block-sparse GQA attention forward ([M31] section 1: each query attends to

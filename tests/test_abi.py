@@ -111,6 +111,23 @@ def test_fwd_argument_errors_launch_nothing():
 
 
 @no_gpu
+def test_qk_norm_argument_errors_launch_nothing():
+    lib = msa.load()
+    d = dims()
+    fwd = lambda **kw: lib.msa_qk_norm_rope_fwd(
+        ctypes.byref(d), kw.get("q", FAKE), 2048, 128, FAKE, 128, 128, FAKE, FAKE, 1e-6, 1e7, kw.get("rope", 64),
+        FAKE, FAKE, 2048, kw.get("qo_sh", 128), FAKE, 128, 128, None)
+    assert fwd(rope=32) == msa.MSA_ERR_UNSUPPORTED
+    assert fwd(q=None) == msa.MSA_ERR_INVALID_ARG
+    assert fwd(qo_sh=0) == msa.MSA_ERR_INVALID_ARG      # broadcast output
+    bwd = lambda **kw: lib.msa_qk_norm_rope_bwd(
+        ctypes.byref(d), FAKE, 2048, 128, FAKE, 128, 128, FAKE, FAKE, 1e-6, 1e7, 64, FAKE, FAKE, 2048, 128,
+        FAKE, 128, 128, FAKE, 2048, 128, FAKE, 128, 128, kw.get("dw", FAKE), FAKE, FAKE, kw.get("n", 1 << 40), None)
+    assert bwd(dw=None) == msa.MSA_ERR_INVALID_ARG
+    assert bwd(n=msa.msa_workspace_size(d, msa.MSA_OP_QKNORM_BWD) - 256) == msa.MSA_ERR_WORKSPACE
+
+
+@no_gpu
 def test_select_and_bwd_argument_errors_launch_nothing():
     lib = msa.load()
     d = dims()
