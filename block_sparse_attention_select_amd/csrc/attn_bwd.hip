@@ -37,7 +37,7 @@ namespace {
 // LDS buffers while the previous block is used, and the K^T operands of
 // dQ^T = K^T dS^T are read transposed from the same K copy.
 // ---------------------------------------------------------------------------
-constexpr int kTileTok = 16;
+constexpr int kTileTok = kAttnTile;
 constexpr int kTokPerWave = 1;
 constexpr int kDqWaves = kTileTok / kTokPerWave;
 constexpr int kUnionWords = 34;
@@ -50,7 +50,8 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     const u16* __restrict__ o, int64_t o_st, int64_t o_sh,
     const u16* __restrict__ dO, int64_t do_st, int64_t do_sh, const float* __restrict__ lse,
     const int32_t* __restrict__ blk_idx, const int32_t* __restrict__ cu, const int32_t* __restrict__ blkbase,
-    const int32_t* __restrict__ blk_seq, int S, int T, int Hk, float scale_log2, float scale,
+    const int32_t* __restrict__ blk_seq, const int32_t* __restrict__ tile_order, int S, int T, int Hk,
+    float scale_log2, float scale,
     u16* __restrict__ dq, int64_t dq_st, int64_t dq_sh, float* __restrict__ delta, float* __restrict__ nlse,
     int32_t* __restrict__ clear, int nclear) {
   __shared__ u32x4 kbuf[2][32][64];
@@ -60,12 +61,11 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
   __shared__ int ukey0[kMaxUnion];  // first token of each union block
   __shared__ int nunion;
 
-  const int h = blockIdx.y;
-  const int t0 = blockIdx.x * kTileTok;
+  // workgroup b runs KV head b % Hk of the tile in launch slot b / Hk
+  const int h = blockIdx.x % Hk;
+  const int t0 = tile_order[blockIdx.x / Hk] * kTileTok;
   // zero the dK/dV item-load counters for the pass that follows
-  for (int i = (blockIdx.y * gridDim.x + blockIdx.x) * 64 * kDqWaves + threadIdx.x; i < nclear;
-       i += gridDim.x * gridDim.y * 64 * kDqWaves)
-    clear[i] = 0;
+  for (int i = blockIdx.x * 64 * kDqWaves + threadIdx.x; i < nclear; i += gridDim.x * 64 * kDqWaves) clear[i] = 0;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
@@ -341,9 +341,10 @@ void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStr
   const int T = (int)z.T, Hk = (int)z.Hk, S = (int)z.S;
   {
     KernelTimer timer("attn_bwd_dq", st);
-    attn_bwd_dq_kernel<<<dim3((unsigned)((z.T + kTileTok - 1) / kTileTok), (unsigned)Hk), 64 * kDqWaves, 0, st>>>(
+    attn_bwd_dq_kernel<<<(unsigned)(z.ntiles * Hk), 64 * kDqWaves, 0, st>>>(
         a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.o, a.o_st, a.o_sh, a.dO, a.do_st,
-        a.do_sh, a.lse, a.blk_idx, a.cu, p.blkbase, p.blk_seq, S, T, Hk, a.scale * kLog2e, a.scale, a.dq, a.dq_st,
+        a.do_sh, a.lse, a.blk_idx, a.cu, p.blkbase, p.blk_seq, p.tile_order, S, T, Hk, a.scale * kLog2e, a.scale,
+        a.dq, a.dq_st,
         a.dq_sh, a.delta, a.nlse, a.item_load, (int)(z.Hk * z.items_cap));
   }
   launch_attn_bwd_dkdv(z, a, p, st);

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void block_transpose_kernel(const u16* __restr
 //      then updates its token if that token selected the block.  K and V are
 //      read from HBM/L2 once per tile instead of once per token.
 // ---------------------------------------------------------------------------
-constexpr int kTileTok = 16;
+constexpr int kTileTok = kAttnTile;
 constexpr int kTokPerWave = 1;
 constexpr int kFwdWaves = kTileTok / kTokPerWave;
 constexpr int kRunsPerWave = 64 / kFwdWaves;  // K and V^T runs staged per wavefront
@@ -92,8 +92,8 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
     const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
     const u16* __restrict__ vt, const int32_t* __restrict__ blk_idx,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ blkbase, const int32_t* __restrict__ blk_seq,
-    int S, int T, int Hk, float scale_log2, u16* __restrict__ o, int64_t o_st, int64_t o_sh,
-    float* __restrict__ lse) {
+    const int32_t* __restrict__ tile_order, int S, int T, int Hk, float scale_log2, u16* __restrict__ o,
+    int64_t o_st, int64_t o_sh, float* __restrict__ lse) {
   __shared__ u32x4 kbuf[2][32][64];
   __shared__ u32x4 vbuf[2][32][64];
   __shared__ uint32_t bitmap[kUnionWords];
@@ -101,8 +101,9 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
   __shared__ int ukey0[kMaxUnion];  // first token of each union block
   __shared__ int nunion;
 
-  const int h = blockIdx.y;
-  const int t0 = blockIdx.x * kTileTok;
+  // workgroup b runs KV head b % Hk of the tile in launch slot b / Hk
+  const int h = blockIdx.x % Hk;
+  const int t0 = tile_order[blockIdx.x / Hk] * kTileTok;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
@@ -338,10 +339,9 @@ void launch_attn_fwd(const Sizes& z, const u16* q, int64_t q_st, int64_t q_sh,
                      const int32_t* blk_idx, const int32_t* cu, const PlanBufs& p, float scale,
                      u16* o, int64_t o_st, int64_t o_sh, float* lse, hipStream_t st) {
   KernelTimer timer("attn_fwd", st);
-  const unsigned tiles = (unsigned)((z.T + kTileTok - 1) / kTileTok);
-  attn_fwd_kernel<<<dim3(tiles, (unsigned)z.Hk), 64 * kFwdWaves, 0, st>>>(
-      q, q_st, q_sh, k, k_st, k_sh, vt, blk_idx, cu, p.blkbase, p.blk_seq, (int)z.S, (int)z.T, (int)z.Hk,
-      scale * kLog2e, o, o_st, o_sh, lse);
+  attn_fwd_kernel<<<(unsigned)(z.ntiles * z.Hk), 64 * kFwdWaves, 0, st>>>(
+      q, q_st, q_sh, k, k_st, k_sh, vt, blk_idx, cu, p.blkbase, p.blk_seq, p.tile_order, (int)z.S, (int)z.T,
+      (int)z.Hk, scale * kLog2e, o, o_st, o_sh, lse);
 }
 
 }  // namespace msa

@@ -54,6 +54,7 @@ Sizes sizes_of(const msa_dims* d) {
   if (cap > z.T) cap = z.T;
   if (cap < 1) cap = 1;
   z.nblk_cap = cap;
+  z.ntiles = (z.T + msa::kAttnTile - 1) / msa::kAttnTile;
   // dK/dV work items: chunk j of a length-L sequence pairs with blocks
   // 0 .. (min((j+1)*chunk, L) - 1) / 128.  With n = ceil(L / chunk) chunks and
   // m = chunk / 128, a sequence has at most min(n * ceil(L / 128),
@@ -93,6 +94,7 @@ PlanBufs carve_plan(Carver& c, const Sizes& z) {
   p.blk_seq = c.take<int32_t>(z.nblk_cap);
   p.seqitem = c.take<int32_t>(z.S + 1);
   p.totals = c.take<int32_t>(4);
+  p.tile_order = c.take<int32_t>(z.ntiles);
   return p;
 }
 

@@ -26,6 +26,7 @@ struct Sizes {
   int64_t nblk_cap;   // bound on the total number of blocks of the pack
   int64_t chunk;      // query positions per dK/dV work item (a multiple of 128)
   int64_t items_cap;  // bound on the number of dK/dV work items per KV head
+  int64_t ntiles;     // ceil(T / kAttnTile)
 };
 
 struct PlanBufs {
@@ -33,7 +34,11 @@ struct PlanBufs {
   int32_t* blk_seq;   // [nblk_cap]  sequence of each global block
   int32_t* seqitem;   // [S+1]       first dK/dV work item of each sequence
   int32_t* totals;    // [4]         {number of blocks, number of work items}
+  int32_t* tile_order;  // [ntiles]  token tiles in launch order (longest expected work first)
 };
+
+// Tokens per workgroup tile of the token-major attention passes (forward, dQ).
+constexpr int kAttnTile = 16;
 
 // ----------------------------------------------------------------------------
 // Device helpers

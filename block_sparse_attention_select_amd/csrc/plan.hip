@@ -12,6 +12,14 @@
 // c = 0 .. (min((j+1)*chunk, L) - 1) / 128.  Consecutive items therefore read
 // the same queries, which keeps them in L2 while the workgroups of a chunk run.
 // seqitem[s] is the first item of sequence s.
+//
+// Token tiles (kAttnTile consecutive tokens of the pack) are put in launch
+// order by decreasing position of their first token within its sequence: a
+// later query has more causal blocks to choose from, so its tile's union of
+// selected blocks, and with it the tile's work, is larger.  Launching the
+// long tiles first (longest-processing-time order) keeps the last wave of
+// workgroups short.  Tiles of equal key may come in any order; the order only
+// decides which workgroup runs when, never what any of them computes.
 #include "msa_internal.h"
 
 namespace msa {
@@ -19,18 +27,28 @@ namespace msa {
 namespace {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kOrderBins = 1024;  // position keys: one per 128-token block (131072 tokens)
 
 __device__ __forceinline__ int chunk_items(int L, int chunk, int j) {
   return (min((j + 1) * chunk, L) - 1) / kBlock + 1;
 }
 
+// Order key of tile i: block of its first token within that token's sequence.
+__device__ __forceinline__ int tile_key(const int32_t* __restrict__ cu, int S, int i) {
+  const int t0 = i * kAttnTile;
+  const int s = find_seq(cu, S, t0);
+  return min((t0 - cu[s]) / kBlock, kOrderBins - 1);
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ cu, int S, int chunk,
-                                                             int32_t* __restrict__ blkbase,
+                                                             int ntiles, int32_t* __restrict__ blkbase,
                                                              int32_t* __restrict__ blk_seq,
                                                              int32_t* __restrict__ seqitem,
-                                                             int32_t* __restrict__ totals) {
+                                                             int32_t* __restrict__ totals,
+                                                             int32_t* __restrict__ tile_order) {
   __shared__ int sb[kPlanThreads];
   __shared__ int si[kPlanThreads];
+  __shared__ int hist[kOrderBins];
   const int tid = threadIdx.x;
   int carry_b = 0, carry_i = 0;
   if (tid == 0) {
@@ -71,6 +89,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     totals[0] = carry_b;
     totals[1] = carry_i;
   }
+
+  // tile launch order: counting sort on the position key, largest key first
+  static_assert(kOrderBins == kPlanThreads, "one scan slot per key");
+  hist[tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < ntiles; i += kPlanThreads) atomicAdd(&hist[tile_key(cu, S, i)], 1);
+  __syncthreads();
+  const int key = kOrderBins - 1 - tid;  // slot tid scans the keys from the top down
+  const int cnt = hist[key];
+  sb[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
+    int a = tid >= off ? sb[tid - off] : 0;
+    __syncthreads();
+    sb[tid] += a;
+    __syncthreads();
+  }
+  hist[key] = sb[tid] - cnt;  // first launch slot of the key
+  __syncthreads();
+  for (int i = tid; i < ntiles; i += kPlanThreads) tile_order[atomicAdd(&hist[tile_key(cu, S, i)], 1)] = i;
 }
 
 }  // namespace
@@ -78,7 +116,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 void launch_plan(const int32_t* cu, const Sizes& z, const PlanBufs& p, hipStream_t st) {
   {
     KernelTimer timer("plan", st);
-    plan_kernel<<<1, kPlanThreads, 0, st>>>(cu, (int)z.S, (int)z.chunk, p.blkbase, p.blk_seq, p.seqitem, p.totals);
+    plan_kernel<<<1, kPlanThreads, 0, st>>>(cu, (int)z.S, (int)z.chunk, (int)z.ntiles, p.blkbase, p.blk_seq,
+                                            p.seqitem, p.totals, p.tile_order);
   }
 }
 
