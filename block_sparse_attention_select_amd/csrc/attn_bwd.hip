@@ -170,7 +170,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     const u16* x = is_k ? k : v;
     const int64_t x_st = is_k ? k_st : v_st, x_sh = is_k ? k_sh : v_sh;
     u32x4* dst = is_k ? &kbuf[buf][4 * tile][0] : &vbuf[buf][4 * tile][0];
-    const int kl = score_key(tile, ln & 15);
+    const int kl = score_key(tile, swz_slot(ln) & 15);  // runs stored swizzled
     if (kstart + kBlock <= T) {
       const u16* base = x + (int64_t)kstart * x_st + (int64_t)h * x_sh;
       const uint32_t off = (uint32_t)(2 * (kl * x_st + 8 * (ln >> 4)));
@@ -213,11 +213,12 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
           pacc[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         {
+          const int swz = swz_slot(lane);
           bf16x8 op[16];  // i = ds * 4 + kk * 2 + (0: K, 1: V)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int run = (2 * qq + ((i >> 1) & 1)) * 4 + (i >> 2);
-            op[i] = __builtin_bit_cast(bf16x8, (i & 1) ? vbuf[buf][run][lane] : kbuf[buf][run][lane]);
+            op[i] = __builtin_bit_cast(bf16x8, (i & 1) ? vbuf[buf][run][swz] : kbuf[buf][run][swz]);
           }
 #pragma unroll
           for (int i = 0; i < 16; ++i) {

@@ -38,18 +38,19 @@ namespace {
 constexpr int kBatch = 4;  // tokens per staging round, kBatch / 4 loaded by each wavefront
 
 // Stage layout of one token (u32x4 units): [0,256) q and [256,512) dO as
-// [ds][lane], lane li + 16g of run ds holding row li, dims 32ds + 8g .. +7;
-// stats: 16 -LSE*log2(e) then 16 Delta values.  One wavefront copies a token:
-// 8 runs of 1 KB and one 128-byte run.  Addresses are a wavefront-uniform
-// base (the token's row, scalar registers) plus a per-lane byte offset (head
-// li, dims 8g..).
+// [ds][slot], operand lane li + 16g of run ds (row li, dims 32ds + 8g .. +7)
+// at slot swz_slot(li + 16g); stats: 16 -LSE*log2(e) then 16 Delta values.
+// One wavefront copies a token: 8 runs of 1 KB and one 128-byte run.
+// Addresses are a wavefront-uniform base (the token's row, scalar registers)
+// plus a per-lane byte offset (head, dims 8g..).
 __device__ __forceinline__ void stage_token(int t, int h, int Hk, int lane, uint32_t slot_lds, uint32_t stats_lds,
                                             const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
                                             const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
                                             const float* __restrict__ nlse, const float* __restrict__ delta) {
   t = __builtin_amdgcn_readfirstlane(t);
-  const uint32_t q_off = (uint32_t)(2 * ((lane & 15) * q_sh + 8 * (lane >> 4)));
-  const uint32_t do_off = (uint32_t)(2 * ((lane & 15) * do_sh + 8 * (lane >> 4)));
+  const int hr = swz_slot(lane) & 15;  // head of this lane's slot (runs stored swizzled)
+  const uint32_t q_off = (uint32_t)(2 * (hr * q_sh + 8 * (lane >> 4)));
+  const uint32_t do_off = (uint32_t)(2 * (hr * do_sh + 8 * (lane >> 4)));
   const u16* qr = q + (int64_t)t * q_st + (int64_t)(h * kGroup) * q_sh;
   const u16* dr = dO + (int64_t)t * do_st + (int64_t)(h * kGroup) * do_sh;
 #pragma unroll
@@ -207,8 +208,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
 #pragma unroll
             for (int ds = 0; ds < 4; ++ds) {
-              const bf16x8 qa = __builtin_bit_cast(bf16x8, b[tk][ds * 64 + ln]);
-              const bf16x8 da = __builtin_bit_cast(bf16x8, b[tk][256 + ds * 64 + ln]);
+              const bf16x8 qa = __builtin_bit_cast(bf16x8, b[tk][ds * 64 + swz_slot(ln)]);
+              const bf16x8 da = __builtin_bit_cast(bf16x8, b[tk][256 + ds * 64 + swz_slot(ln)]);
 #pragma unroll
               for (int kk = 0; kk < 2; ++kk) {
                 sacc[kk] = mfma16x16x32(qa, kf[kk][ds], sacc[kk]);

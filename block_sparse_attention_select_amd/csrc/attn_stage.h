@@ -82,10 +82,26 @@ __device__ __forceinline__ int fresh_lane() {
 // the lane receives rows 4gg .. 4gg+3 of dim 16dt + s: source lane s of a
 // 16-lane group points at row 4gg + s/4, dims 16dt + 4(s%4) .. +3, i.e. at
 // (dt/2) * 1024 + (dt%2) * 512 + tr_lane_offset(lane).
+//
+// Runs that are read transposed are stored swizzled: operand lane l's 16 bytes
+// sit at slot swz_slot(l) of the 1 KB run, i.e. the rows of lane groups 1 and 3
+// are stored with row index xor 12.  LDS has 64 four-byte banks, so slots that
+// agree mod 16 share banks.  A transposed 8-byte read is served half a
+// wavefront per pass; unswizzled, the two 8-dim halves of its 16-dim columns
+// lie 256 bytes apart, on the same banks, and every such read takes two
+// passes.  A plain 16-byte read is served in passes of 16 lanes: within each
+// half wavefront, the lane quads (l / 4) of even bit parity form one pass and
+// those of odd parity the other.  Measured on gfx950, the xor-12 swizzle keeps
+// the slots of every pass of both kinds distinct mod 16 (xor 8 would fix the
+// transposed reads but break the plain ones).
+__device__ __forceinline__ int swz_slot(int l) { return l ^ (((l >> 4) & 1) * 12); }
+
 __device__ __forceinline__ uint32_t tr_lane_offset(int lane) {
   const int s = lane & 15;
   const int gg = lane >> 4;
-  return (uint32_t)((4 * gg + (s >> 2)) * 16 + ((s & 3) >> 1) * 256 + 8 * (s & 1));
+  const int half = (s >> 1) & 1;  // dims 8..15 of the column: the next lane group of the run
+  const int row = (4 * gg + (s >> 2)) ^ (12 * half);
+  return (uint32_t)((16 * half + row) * 16 + 8 * (s & 1));
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
