@@ -42,7 +42,13 @@ design notes of the repository):
   blocks 1..b-1;
 * attention keys for query i are the keys j <= i of its selected blocks in
   its own sequence; softmax scale 1/sqrt(128); query head g uses KV head
-  g // (Hq / Hk).
+  g // (Hq / Hk);
+* the narrow-block variant ([PR] kernel-tuning commit message: the same
+  block-sparse kernel with 4-token blocks, head dim 256, 12 query heads per
+  KV head) is the same attention with ``block=4``; the pages give neither its
+  block count per query nor how its blocks are chosen, so its block lists
+  are inputs (512 per query in the benchmark: the wide variant's 2048-key
+  budget), and its softmax scale is 1/sqrt(256).
 
 Precision.  The norm and RoPE run in fp32 with angles, cos and sin taken in
 fp64 and rounded to fp32, because the bf16 rounding of the features is a

@@ -11,4 +11,5 @@ from .packs import (  # noqa: F401
     pack_lengths,
     make_pack,
     make_custom_pack,
+    random_block_lists,
 )

@@ -52,6 +52,13 @@ CONFIGS = {
                           description="32768-token THD pack, lengths U[2048, 16384]"),
     "layer32k": PackConfig("layer32k", 32768, 32768, 32768, num_q_heads=64, num_kv_heads=4,
                            description="unsharded layer: one 32768-token sequence, 64 q / 4 kv / 4 index heads"),
+    # Narrow-block variant (qwen3.8-next on the pages: 12 q / 1 kv head, head
+    # dim 256, 4-token blocks, 16k-token packs).  The pages give no block count
+    # per query; 512 blocks keep the 2048-key budget of the wide variant.
+    "qsa16k": PackConfig("qsa16k", 16384, 1024, 8192, num_q_heads=12, num_kv_heads=1, head_dim=256,
+                         block_size=4, topk_blocks=512,
+                         description="16384-token THD pack, lengths U[1024, 8192], 12 q / 1 kv heads, "
+                                     "D 256, 4-token blocks, 512 selected per query"),
 }
 
 
@@ -145,3 +152,29 @@ def make_pack(config: str, seed: int = 0) -> Pack:
     p = make_custom_pack(lengths, c.num_q_heads, c.num_kv_heads, seed, c.head_dim,
                          c.block_size, c.topk_blocks, name=config)
     return p
+
+
+def random_block_lists(cu_seqlens, num_kv_heads: int, block: int, topk: int, seed: int) -> np.ndarray:
+    """Seeded block selections ``[T, Hk, topk]`` int32 for attention inputs.
+
+    Query ``t`` at sequence-local position ``p`` owns block ``b = p // block``.
+    With ``b + 1 <= topk`` it lists every block ``0..b``; otherwise its own
+    block and ``topk - 1`` distinct blocks drawn uniformly from ``0..b-1``.
+    Ids are sequence-local, ascending, ``-1`` padded.  The draws come from
+    ``numpy.random.default_rng([seed, 7])``, one permutation per (token, head).
+    """
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T = int(cu[-1])
+    rng = np.random.default_rng([seed, 7])
+    out = np.full((T, num_kv_heads, topk), -1, dtype=np.int32)
+    for s in range(len(cu) - 1):
+        for p in range(int(cu[s + 1] - cu[s])):
+            t = int(cu[s]) + p
+            b = p // block
+            for h in range(num_kv_heads):
+                if b + 1 <= topk:
+                    out[t, h, :b + 1] = np.arange(b + 1)
+                else:
+                    ids = np.sort(np.concatenate([rng.permutation(b)[:topk - 1], [b]]))
+                    out[t, h, :] = ids
+    return out

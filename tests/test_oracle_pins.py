@@ -298,6 +298,62 @@ def test_sparse_equals_masked_dense_attention():
     np.testing.assert_allclose(dV, dv_t, atol=1e-10)
 
 
+# ---------------------------------------------------------------- narrow-block variant (4-token blocks)
+def _narrow_pack(lengths, topk, seed):
+    p = synth.make_custom_pack(lengths, num_q_heads=12, num_kv_heads=1, seed=seed, head_dim=256,
+                               block_size=4, topk_blocks=topk)
+    cu = p.cu_seqlens.numpy()
+    blk = synth.random_block_lists(cu, 1, 4, topk, seed)
+    return p, f32(p.q), f32(p.k), f32(p.v), f32(p.do), cu, blk
+
+
+def test_narrow_dense_equality():
+    """4-token blocks, 64 per query: sequences of at most 256 tokens see every causal key (12 q / 1 kv, D 256)."""
+    p, q, k, v, do, cu, blk = _narrow_pack([200, 56], 64, 41)
+    scale = 1 / math.sqrt(256)
+    Ofw, LSE = O.attention_forward(q, k, v, blk, cu, scale, block=4)
+    dQ, dK, dV = O.attention_backward(q, k, v, do, blk, cu, scale, block=4)
+    for s in range(2):
+        a, b = int(cu[s]), int(cu[s + 1])
+        Q = torch.tensor(q[a:b], dtype=torch.float64).permute(1, 0, 2)[None]
+        K = torch.tensor(k[a:b], dtype=torch.float64).permute(1, 0, 2).repeat_interleave(12, 0)[None]
+        V = torch.tensor(v[a:b], dtype=torch.float64).permute(1, 0, 2).repeat_interleave(12, 0)[None]
+        out, lse = torch.ops.aten._scaled_dot_product_flash_attention_for_cpu(Q, K, V, 0.0, True, scale=scale)
+        np.testing.assert_allclose(Ofw[a:b], out[0].permute(1, 0, 2).numpy(), atol=1e-12)
+        np.testing.assert_allclose(LSE[a:b], lse[0].permute(1, 0).numpy(), atol=1e-12)
+        mask = np.tril(np.ones((b - a, b - a), dtype=bool))
+        o_t, dq_t, dk_t, dv_t = _torch_dense(q[a:b], k[a:b], v[a:b], do[a:b], mask, scale)
+        np.testing.assert_allclose(dQ[a:b], dq_t, atol=1e-10)
+        np.testing.assert_allclose(dK[a:b], dk_t, atol=1e-10)
+        np.testing.assert_allclose(dV[a:b], dv_t, atol=1e-10)
+
+
+def test_narrow_sparse_equals_masked_dense():
+    """4-token blocks, 16 per query out of up to 75: the key set is the listed blocks' causal keys."""
+    p, q, k, v, do, cu, blk = _narrow_pack([300, 90], 16, 42)
+    T = int(cu[-1])
+    seq, pos = O.sequence_layout(cu)
+    scale = 1 / math.sqrt(256)
+    Ofw, _ = O.attention_forward(q, k, v, blk, cu, scale, block=4)
+    dQ, dK, dV = O.attention_backward(q, k, v, do, blk, cu, scale, block=4)
+    # mask[i, j]: same sequence, j <= i, and block (j - start) // 4 listed for i
+    listed = np.zeros((T, 80), dtype=bool)
+    for i in range(T):
+        ids = blk[i, 0][blk[i, 0] >= 0]
+        listed[i, ids] = True
+    j = np.arange(T)
+    same = seq[:, None] == seq[None, :]
+    causal = j[None, :] <= j[:, None]
+    jb = np.clip(pos[None, :] // 4, 0, 79)
+    mask = same & causal & np.take_along_axis(listed, np.broadcast_to(jb, (T, T)), axis=1)
+    assert mask.sum() < 0.5 * (same & causal).sum()
+    o_t, dq_t, dk_t, dv_t = _torch_dense(q, k, v, do, np.repeat(mask[None], 12, axis=0), scale)
+    np.testing.assert_allclose(Ofw, o_t, atol=1e-11)
+    np.testing.assert_allclose(dQ, dq_t, atol=1e-10)
+    np.testing.assert_allclose(dK, dk_t, atol=1e-10)
+    np.testing.assert_allclose(dV, dv_t, atol=1e-10)
+
+
 # ---------------------------------------------------------------- P3: finite differences
 def test_backward_finite_differences():
     rng = np.random.default_rng(7)
