@@ -36,10 +36,12 @@ MSA_OP_QKNORM_BWD = 4
 MSA_OP_SELECT = 1
 MSA_OP_FWD = 2
 MSA_OP_BWD = 3
+MSA_OP_QSA_FWD = 5
+MSA_OP_QSA_BWD = 6
 
 # Every symbol include/msa.h declares.
 EXPORTED = ("msa_workspace_size", "msa_index_select", "msa_index_select_ex", "msa_attn_fwd", "msa_attn_bwd",
-            "msa_qk_norm_rope_fwd", "msa_qk_norm_rope_bwd",
+            "msa_qk_norm_rope_fwd", "msa_qk_norm_rope_bwd", "msa_qsa_attn_fwd", "msa_qsa_attn_bwd",
             "msa_status_string", "msa_check_cu_seqlens", "msa_timing_enable", "msa_timing_collect",
             "msa_version")
 
@@ -96,6 +98,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                  _P, _P, _I64, _I64, _P, _P, _F,
                                  _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _SZ, _P]
     lib.msa_attn_bwd.restype = _I32
+    lib.msa_qsa_attn_fwd.argtypes = lib.msa_attn_fwd.argtypes
+    lib.msa_qsa_attn_fwd.restype = _I32
+    lib.msa_qsa_attn_bwd.argtypes = lib.msa_attn_bwd.argtypes
+    lib.msa_qsa_attn_bwd.restype = _I32
     lib.msa_qk_norm_rope_fwd.argtypes = [ctypes.POINTER(MsaDims), _P, _I64, _I64, _P, _I64, _I64, _P, _P,
                                          _F, _F, _I32, _P, _P, _I64, _I64, _P, _I64, _I64, _P]
     lib.msa_qk_norm_rope_fwd.restype = _I32
@@ -148,7 +154,7 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 def _bf16_view(t: torch.Tensor, name: str) -> Tuple[int, int]:
     if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1 or not t.is_cuda:
-        raise ValueError(f"{name}: expected a CUDA bf16 [T, H, 128] tensor with a contiguous last dim")
+        raise ValueError(f"{name}: expected a CUDA bf16 [T, H, D] tensor with a contiguous last dim")
     return t.stride(0), t.stride(1)
 
 
@@ -248,6 +254,66 @@ def msa_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Ten
                           _ptr(cu_seqlens), scale, _ptr(dq), sdq[0], sdq[1], _ptr(dk), sdk[0], sdk[1],
                           _ptr(dv), sdv[0], sdv[1], _ptr(ws), nbytes, _stream(q))
     _check(st, "msa_attn_bwd")
+    return dq, dk, dv
+
+
+def _qsa_dims(cu_seqlens: torch.Tensor, max_seqlen: int, Hq: int, Hk: int, T: int, topk: int) -> MsaDims:
+    return make_dims(T, cu_seqlens.numel() - 1, max_seqlen, Hq, Hk, head_dim=256, block_size=4, topk_blocks=topk)
+
+
+def msa_qsa_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, blk_idx: torch.Tensor,
+                     cu_seqlens: torch.Tensor, max_seqlen: int, softmax_scale: Optional[float] = None, *,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Narrow-block (4-token blocks, D 256, 12 q heads per KV head) forward: O [T, Hq, 256], LSE [T, Hq].
+    ``blk_idx`` [T, Hk, K] int32 lists sequence-local block ids per query (K <= 1024)."""
+    lib = load()
+    T, Hq, D = q.shape
+    Hk = k.shape[1]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    sq, sk, sv = _bf16_view(q, "q"), _bf16_view(k, "k"), _bf16_view(v, "v")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty(T, Hq, dtype=torch.float32, device=q.device)
+    so = _bf16_view(out, "out")
+    blk_idx = blk_idx.contiguous()
+    dims = _qsa_dims(cu_seqlens, max_seqlen, Hq, Hk, T, blk_idx.shape[2])
+    ws, nbytes = _workspace(dims, MSA_OP_QSA_FWD, q.device, workspace)
+    st = lib.msa_qsa_attn_fwd(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0],
+                              sv[1], _ptr(blk_idx), _ptr(cu_seqlens), scale, _ptr(out), so[0], so[1], _ptr(lse),
+                              _ptr(ws), nbytes, _stream(q))
+    _check(st, "msa_qsa_attn_fwd")
+    return out, lse
+
+
+def msa_qsa_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                     do: torch.Tensor, blk_idx: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+                     softmax_scale: Optional[float] = None, *, dq: Optional[torch.Tensor] = None,
+                     dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Backward of msa_qsa_attn_fwd: returns dQ, dK, dV (bf16, shaped like q, k, v)."""
+    lib = load()
+    T, Hq, D = q.shape
+    Hk = k.shape[1]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if dq is None:
+        dq = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if dk is None:
+        dk = torch.empty_like(k, memory_format=torch.contiguous_format)
+    if dv is None:
+        dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    views = [_bf16_view(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do"),
+                                           (dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    blk_idx = blk_idx.contiguous()
+    dims = _qsa_dims(cu_seqlens, max_seqlen, Hq, Hk, T, blk_idx.shape[2])
+    ws, nbytes = _workspace(dims, MSA_OP_QSA_BWD, q.device, workspace)
+    (sq, sk, sv, so, sdo, sdq, sdk, sdv) = views
+    st = lib.msa_qsa_attn_bwd(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0],
+                              sv[1], _ptr(o), so[0], so[1], _ptr(lse), _ptr(do), sdo[0], sdo[1], _ptr(blk_idx),
+                              _ptr(cu_seqlens), scale, _ptr(dq), sdq[0], sdq[1], _ptr(dk), sdk[0], sdk[1],
+                              _ptr(dv), sdv[0], sdv[1], _ptr(ws), nbytes, _stream(q))
+    _check(st, "msa_qsa_attn_bwd")
     return dq, dk, dv
 
 

@@ -13,7 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmsa.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["plan.hip", "select.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dkdv.hip", "qk_norm.hip", "msa_api.cpp",
+SOURCES = ["plan.hip", "select.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dkdv.hip", "qk_norm.hip", "qsa_attn.hip",
+           "msa_api.cpp",
            "timing.cpp"]
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU forms.

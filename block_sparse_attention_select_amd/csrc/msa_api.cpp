@@ -41,6 +41,65 @@ int check_dims(const msa_dims* d) {
   return MSA_OK;
 }
 
+// Narrow-block variant: head_dim 256, block 4, 12 q heads per KV head,
+// 1..1024 listed blocks per query, sequences up to 32768 tokens.
+int check_qsa_dims(const msa_dims* d) {
+  if (!d) return MSA_ERR_INVALID_ARG;
+  if (d->total_tokens < 0 || d->num_seqs < 0 || d->max_seqlen < 0 || d->num_q_heads <= 0 ||
+      d->num_kv_heads <= 0 || d->topk_blocks <= 0)
+    return MSA_ERR_INVALID_ARG;
+  if (d->total_tokens > 0 && (d->num_seqs < 1 || d->max_seqlen < 1)) return MSA_ERR_INVALID_ARG;
+  if (d->max_seqlen > d->total_tokens && d->total_tokens > 0) return MSA_ERR_INVALID_ARG;
+  if (d->head_dim != msa::kQsaHeadDim || d->block_size != msa::kQsaBlock || d->topk_blocks > msa::kQsaMaxTopk)
+    return MSA_ERR_UNSUPPORTED;
+  if (d->num_q_heads != msa::kQsaGroup * d->num_kv_heads) return MSA_ERR_UNSUPPORTED;
+  if (d->max_seqlen > MSA_QSA_MAX_SEQLEN) return MSA_ERR_UNSUPPORTED;
+  if (d->num_kv_heads > 65535) return MSA_ERR_UNSUPPORTED;
+  if ((int64_t)d->total_tokens * d->num_q_heads * msa::kQsaHeadDim >= (int64_t(1) << 31)) return MSA_ERR_UNSUPPORTED;
+  return MSA_OK;
+}
+
+// Grid and workspace bounds of a pack whose blocks (dK/dV work items, key
+// numbering) are `unit` tokens wide, with `dhead` dims per head.
+void size_blocks(Sizes& z, int64_t unit, int64_t dhead) {
+  // sum_s ceil(L_s / unit) <= (T + (unit - 1) S) / unit, and <= T
+  int64_t cap = (z.T + (unit - 1) * z.S) / unit;
+  if (cap > z.T) cap = z.T;
+  if (cap < 1) cap = 1;
+  z.nblk_cap = cap;
+  z.ntiles = (z.T + msa::kAttnTile - 1) / msa::kAttnTile;
+  // dK/dV work items: chunk j of a length-L sequence pairs with blocks
+  // 0 .. (min((j+1)*chunk, L) - 1) / unit.  With n = ceil(L / chunk) chunks and
+  // m = chunk / unit, a sequence has at most min(n * ceil(L / unit),
+  // m * n * (n + 1) / 2) items; both sum over a pack to the bounds below.
+  int64_t chunk = 512;
+  for (;;) {
+    const int64_t m = chunk / unit;
+    const int64_t b1 = z.T * z.max_seqlen / (unit * chunk) + z.T / chunk + z.T / unit + 2 * z.S + 1;
+    const int64_t b2 = z.T * z.max_seqlen / (2 * unit * chunk) + 3 * z.T / (2 * unit) + z.S * m + 1;
+    const int64_t items = b1 < b2 ? b1 : b2;
+    const int64_t bytes = items * z.Hk * unit * dhead * 4 * 2;
+    if (bytes <= kPartialBudget || chunk >= msa::kDkdvChunkMax) {
+      z.chunk = chunk;
+      z.items_cap = items;
+      break;
+    }
+    chunk *= 2;
+  }
+}
+
+Sizes sizes_of_qsa(const msa_dims* d) {
+  Sizes z;
+  z.T = d->total_tokens;
+  z.S = d->num_seqs;
+  z.Hq = d->num_q_heads;
+  z.Hk = d->num_kv_heads;
+  z.max_seqlen = d->max_seqlen;
+  z.nbmax = (z.max_seqlen + msa::kQsaKeyTile - 1) / msa::kQsaKeyTile;
+  size_blocks(z, msa::kQsaKeyTile, msa::kQsaHeadDim);
+  return z;
+}
+
 Sizes sizes_of(const msa_dims* d) {
   Sizes z;
   z.T = d->total_tokens;
@@ -49,30 +108,7 @@ Sizes sizes_of(const msa_dims* d) {
   z.Hk = d->num_kv_heads;
   z.max_seqlen = d->max_seqlen;
   z.nbmax = (z.max_seqlen + msa::kBlock - 1) / msa::kBlock;
-  // sum_s ceil(L_s / 128) <= (T + 127 S) / 128, and <= T (one token per block at least)
-  int64_t cap = (z.T + (msa::kBlock - 1) * z.S) / msa::kBlock;
-  if (cap > z.T) cap = z.T;
-  if (cap < 1) cap = 1;
-  z.nblk_cap = cap;
-  z.ntiles = (z.T + msa::kAttnTile - 1) / msa::kAttnTile;
-  // dK/dV work items: chunk j of a length-L sequence pairs with blocks
-  // 0 .. (min((j+1)*chunk, L) - 1) / 128.  With n = ceil(L / chunk) chunks and
-  // m = chunk / 128, a sequence has at most min(n * ceil(L / 128),
-  // m * n * (n + 1) / 2) items; both sum over a pack to the bounds below.
-  int64_t chunk = 512;
-  for (;;) {
-    const int64_t m = chunk / msa::kBlock;
-    const int64_t b1 = z.T * z.max_seqlen / (msa::kBlock * chunk) + z.T / chunk + z.T / msa::kBlock + 2 * z.S + 1;
-    const int64_t b2 = z.T * z.max_seqlen / (2 * msa::kBlock * chunk) + 3 * z.T / (2 * msa::kBlock) + z.S * m + 1;
-    const int64_t items = b1 < b2 ? b1 : b2;
-    const int64_t bytes = items * z.Hk * msa::kBlock * msa::kHeadDim * 4 * 2;
-    if (bytes <= kPartialBudget || chunk >= msa::kDkdvChunkMax) {
-      z.chunk = chunk;
-      z.items_cap = items;
-      break;
-    }
-    chunk *= 2;
-  }
+  size_blocks(z, msa::kBlock, msa::kHeadDim);
   return z;
 }
 
@@ -147,6 +183,40 @@ BwdWs carve_bwd(Carver& c, const Sizes& z) {
   return w;
 }
 
+struct QsaFwdWs {
+  PlanBufs plan;
+  uint32_t* bits;
+  u16* vt;
+};
+QsaFwdWs carve_qsa_fwd(Carver& c, const Sizes& z) {
+  QsaFwdWs w;
+  w.plan = carve_plan(c, z);
+  w.bits = c.take<uint32_t>(z.T * z.Hk * msa::kQsaWords);
+  w.vt = c.take<u16>(z.nblk_cap * z.Hk * msa::kQsaKeyTile * msa::kQsaHeadDim);
+  return w;
+}
+
+struct QsaBwdWs {
+  PlanBufs plan;
+  uint32_t* bits;
+  float* delta;
+  float* nlse;
+  int32_t* item_count;
+  float* part_dk;
+  float* part_dv;
+};
+QsaBwdWs carve_qsa_bwd(Carver& c, const Sizes& z) {
+  QsaBwdWs w;
+  w.plan = carve_plan(c, z);
+  w.bits = c.take<uint32_t>(z.T * z.Hk * msa::kQsaWords);
+  w.delta = c.take<float>(z.T * z.Hk * 16);
+  w.nlse = c.take<float>(z.T * z.Hk * 16);
+  w.item_count = c.take<int32_t>(z.Hk * z.items_cap);
+  w.part_dk = c.take<float>(z.Hk * z.items_cap * msa::kQsaKeyTile * msa::kQsaHeadDim);
+  w.part_dv = c.take<float>(z.Hk * z.items_cap * msa::kQsaKeyTile * msa::kQsaHeadDim);
+  return w;
+}
+
 size_t ws_bytes_for(const Sizes& z, int op) {
   Carver c(nullptr);
   switch (op) {
@@ -154,6 +224,8 @@ size_t ws_bytes_for(const Sizes& z, int op) {
     case MSA_OP_FWD: carve_fwd(c, z); break;
     case MSA_OP_BWD: carve_bwd(c, z); break;
     case MSA_OP_QKNORM_BWD: c.take<float>((int64_t)(msa::kQkBwdMaxRows + msa::kQkBwdMaxRows / 16 + 1) * 256); break;
+    case MSA_OP_QSA_FWD: carve_qsa_fwd(c, z); break;
+    case MSA_OP_QSA_BWD: carve_qsa_bwd(c, z); break;
     default: return 0;
   }
   return c.off;
@@ -195,7 +267,8 @@ const char* msa_status_string(int status) {
     case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG: null pointer, negative size, or bad stride/alignment";
     case MSA_ERR_UNSUPPORTED:
       return "MSA_ERR_UNSUPPORTED: needs head_dim=128, block_size=128, topk_blocks=16, num_q_heads=16*num_kv_heads, "
-             "max_seqlen<=131072";
+             "max_seqlen<=131072 (msa_qsa_*: head_dim=256, block_size=4, topk_blocks<=1024, "
+             "num_q_heads=12*num_kv_heads, max_seqlen<=32768)";
     case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE: workspace null, not 256-byte aligned, or too small";
     case MSA_ERR_HIP: return "MSA_ERR_HIP: the HIP runtime reported an error";
     default: return "unknown MSA status";
@@ -204,6 +277,12 @@ const char* msa_status_string(int status) {
 
 int msa_workspace_size(const msa_dims* dims, int op, size_t* bytes) {
   if (!bytes) return MSA_ERR_INVALID_ARG;
+  if (op == MSA_OP_QSA_FWD || op == MSA_OP_QSA_BWD) {
+    int st = check_qsa_dims(dims);
+    if (st != MSA_OK) return st;
+    *bytes = dims->total_tokens == 0 ? 0 : ws_bytes_for(sizes_of_qsa(dims), op);
+    return MSA_OK;
+  }
   int st = check_dims(dims);
   if (st != MSA_OK) return st;
   if (op != MSA_OP_SELECT && op != MSA_OP_FWD && op != MSA_OP_BWD && op != MSA_OP_QKNORM_BWD)
@@ -312,6 +391,86 @@ int msa_attn_bwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh
   a.part_dv = w.part_dv;
   msa::launch_plan(cu_seqlens, z, w.plan, stream);
   msa::launch_attn_bwd(z, a, w.plan, stream);
+  return launch_status();
+}
+
+int msa_qsa_attn_fwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh, const void* k, int64_t k_st,
+                     int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh, const int32_t* blk_idx,
+                     const int32_t* cu_seqlens, float softmax_scale, void* o, int64_t o_st, int64_t o_sh, float* lse,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_qsa_dims(dims);
+  if (st != MSA_OK) return st;
+  if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return MSA_ERR_INVALID_ARG;
+  if (dims->total_tokens == 0) return MSA_OK;
+  if (!in_view(q, q_st, q_sh) || !in_view(k, k_st, k_sh) || !in_view(v, v_st, v_sh) || !out_view(o, o_st, o_sh))
+    return MSA_ERR_INVALID_ARG;
+  if (!blk_idx || !aligned(blk_idx, 4) || !cu_seqlens || !aligned(cu_seqlens, 4) || !lse || !aligned(lse, 16))
+    return MSA_ERR_INVALID_ARG;
+  const Sizes z = sizes_of_qsa(dims);
+  st = check_ws(workspace, workspace_bytes, ws_bytes_for(z, MSA_OP_QSA_FWD));
+  if (st != MSA_OK) return st;
+  Carver c(workspace);
+  QsaFwdWs w = carve_qsa_fwd(c, z);
+  msa::QsaArgs a = {};
+  a.q = (const u16*)q; a.q_st = q_st; a.q_sh = q_sh;
+  a.k = (const u16*)k; a.k_st = k_st; a.k_sh = k_sh;
+  a.v = (const u16*)v; a.v_st = v_st; a.v_sh = v_sh;
+  a.blk_idx = blk_idx;
+  a.topk = dims->topk_blocks;
+  a.cu = cu_seqlens;
+  a.scale = softmax_scale;
+  a.out_o = (u16*)o; a.oo_st = o_st; a.oo_sh = o_sh;
+  a.out_lse = lse;
+  a.bits = w.bits;
+  a.vt = w.vt;
+  msa::launch_plan(cu_seqlens, z, w.plan, stream, msa::kQsaKeyTile);
+  msa::launch_qsa_fwd(z, a, w.plan, stream);
+  return launch_status();
+}
+
+int msa_qsa_attn_bwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh, const void* k, int64_t k_st,
+                     int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh, const void* o, int64_t o_st,
+                     int64_t o_sh, const float* lse, const void* do_, int64_t do_st, int64_t do_sh,
+                     const int32_t* blk_idx, const int32_t* cu_seqlens, float softmax_scale, void* dq, int64_t dq_st,
+                     int64_t dq_sh, void* dk, int64_t dk_st, int64_t dk_sh, void* dv, int64_t dv_st, int64_t dv_sh,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_qsa_dims(dims);
+  if (st != MSA_OK) return st;
+  if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return MSA_ERR_INVALID_ARG;
+  if (dims->total_tokens == 0) return MSA_OK;
+  if (!in_view(q, q_st, q_sh) || !in_view(k, k_st, k_sh) || !in_view(v, v_st, v_sh) || !in_view(o, o_st, o_sh) ||
+      !in_view(do_, do_st, do_sh) || !out_view(dq, dq_st, dq_sh) || !out_view(dk, dk_st, dk_sh) ||
+      !out_view(dv, dv_st, dv_sh))
+    return MSA_ERR_INVALID_ARG;
+  if (!blk_idx || !aligned(blk_idx, 4) || !cu_seqlens || !aligned(cu_seqlens, 4) || !lse || !aligned(lse, 16))
+    return MSA_ERR_INVALID_ARG;
+  const Sizes z = sizes_of_qsa(dims);
+  st = check_ws(workspace, workspace_bytes, ws_bytes_for(z, MSA_OP_QSA_BWD));
+  if (st != MSA_OK) return st;
+  Carver c(workspace);
+  QsaBwdWs w = carve_qsa_bwd(c, z);
+  msa::QsaArgs a = {};
+  a.q = (const u16*)q; a.q_st = q_st; a.q_sh = q_sh;
+  a.k = (const u16*)k; a.k_st = k_st; a.k_sh = k_sh;
+  a.v = (const u16*)v; a.v_st = v_st; a.v_sh = v_sh;
+  a.o = (const u16*)o; a.o_st = o_st; a.o_sh = o_sh;
+  a.lse = lse;
+  a.dO = (const u16*)do_; a.do_st = do_st; a.do_sh = do_sh;
+  a.blk_idx = blk_idx;
+  a.topk = dims->topk_blocks;
+  a.cu = cu_seqlens;
+  a.scale = softmax_scale;
+  a.dq = (u16*)dq; a.dq_st = dq_st; a.dq_sh = dq_sh;
+  a.dk = (u16*)dk; a.dk_st = dk_st; a.dk_sh = dk_sh;
+  a.dv = (u16*)dv; a.dv_st = dv_st; a.dv_sh = dv_sh;
+  a.bits = w.bits;
+  a.delta = w.delta;
+  a.nlse = w.nlse;
+  a.item_count = w.item_count;
+  a.part_dk = w.part_dk;
+  a.part_dv = w.part_dv;
+  msa::launch_plan(cu_seqlens, z, w.plan, stream, msa::kQsaKeyTile);
+  msa::launch_qsa_bwd(z, a, w.plan, stream);
   return launch_status();
 }
 

@@ -172,7 +172,9 @@ class KernelTimer {
 // ----------------------------------------------------------------------------
 // Launchers (host functions, each defined next to its kernels).
 // ----------------------------------------------------------------------------
-void launch_plan(const int32_t* cu, const Sizes& z, const PlanBufs& p, hipStream_t st);
+// Plan of a pack (see plan.hip).  `unit` is the key-block width the plan
+// numbers: kBlock for the wide variant, kQsaKeyTile for the narrow one.
+void launch_plan(const int32_t* cu, const Sizes& z, const PlanBufs& p, hipStream_t st, int unit = 128);
 
 void launch_select(const Sizes& z, const u16* idx_q, int64_t sq_t, int64_t sq_h,
                    const u16* idx_k, int64_t sk_t, int64_t sk_h, const u16* w_q, const u16* w_k,
@@ -237,6 +239,48 @@ void launch_attn_bwd_dkdv(const Sizes& z, const BwdArgs& a, const PlanBufs& p, h
 
 // Largest number of query positions in one dK/dV work item.
 constexpr int kDkdvChunkMax = 2048;
+
+// ----------------------------------------------------------------------------
+// Narrow-block variant: 4-token blocks, head dim 256, 12 query heads per KV
+// head (qsa_attn.hip).  Key tiles of 64 keys (16 blocks) are its unit of
+// staging; Sizes::nblk_cap then counts key tiles and the plan's blkbase /
+// blk_seq number key tiles.
+// ----------------------------------------------------------------------------
+constexpr int kQsaHeadDim = 256;
+constexpr int kQsaBlock = 4;
+constexpr int kQsaGroup = 12;
+constexpr int kQsaKeyTile = 64;
+constexpr int kQsaMaxSeqlen = 32768;
+constexpr int kQsaMaxTopk = 1024;
+constexpr int kQsaWords = kQsaMaxSeqlen / kQsaBlock / 32;  // bitmap words per (token, KV head)
+
+struct QsaArgs {
+  const u16* q; int64_t q_st, q_sh;
+  const u16* k; int64_t k_st, k_sh;
+  const u16* v; int64_t v_st, v_sh;
+  const u16* o; int64_t o_st, o_sh;
+  const float* lse;
+  const u16* dO; int64_t do_st, do_sh;
+  const int32_t* blk_idx;
+  int topk;
+  const int32_t* cu;
+  float scale;
+  u16* out_o; int64_t oo_st, oo_sh;   // forward output
+  float* out_lse;
+  u16* dq; int64_t dq_st, dq_sh;
+  u16* dk; int64_t dk_st, dk_sh;
+  u16* dv; int64_t dv_st, dv_sh;
+  // workspace
+  uint32_t* bits;     // [T][Hk][kQsaWords] selected-block bitmaps
+  u16* vt;            // [key tiles][Hk][32 runs][64 lanes][8] V^T in MFMA operand order (forward)
+  float* delta;       // [T][Hk][16] (heads past 12 zero)
+  float* nlse;        // [T][Hk][16] -LSE * log2(e) (-inf for heads past 12 and empty rows)
+  int32_t* item_count;  // [Hk][items_cap]
+  float* part_dk;     // [Hk][items_cap][64][256]
+  float* part_dv;
+};
+void launch_qsa_fwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStream_t st);
+void launch_qsa_bwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStream_t st);
 
 // Barrier for LDS traffic only: waits for this wavefront's LDS operations,
 // then for every wavefront of the workgroup, without draining outstanding

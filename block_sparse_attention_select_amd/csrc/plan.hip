@@ -4,7 +4,10 @@
 // radixark/miles PR #4581, PR body).
 //
 // Blocks are numbered pack-wide: sequence s owns global blocks
-// blkbase[s] .. blkbase[s+1]-1, block c of s being blkbase[s] + c.
+// blkbase[s] .. blkbase[s+1]-1, block c of s being blkbase[s] + c.  The
+// block width is a template parameter: 128-token blocks for the wide
+// variant, 64-key tiles for the narrow one (whose 4-token blocks are grouped
+// sixteen to a tile); "block" below means that unit.
 //
 // dK/dV work items are ordered by (sequence, query chunk, block): chunk j of a
 // length-L sequence holds query positions [j*chunk, min((j+1)*chunk, L)) and
@@ -29,8 +32,9 @@ namespace {
 constexpr int kPlanThreads = 1024;
 constexpr int kOrderBins = 1024;  // position keys: one per 128-token block (131072 tokens)
 
+template <int kUnit>
 __device__ __forceinline__ int chunk_items(int L, int chunk, int j) {
-  return (min((j + 1) * chunk, L) - 1) / kBlock + 1;
+  return (min((j + 1) * chunk, L) - 1) / kUnit + 1;
 }
 
 // Order key of tile i: block of its first token within that token's sequence.
@@ -40,6 +44,7 @@ __device__ __forceinline__ int tile_key(const int32_t* __restrict__ cu, int S, i
   return min((t0 - cu[s]) / kBlock, kOrderBins - 1);
 }
 
+template <int kUnit>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ cu, int S, int chunk,
                                                              int ntiles, int32_t* __restrict__ blkbase,
                                                              int32_t* __restrict__ blk_seq,
@@ -60,9 +65,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     int L = 0, nb = 0, ni = 0;
     if (s < S) {
       L = cu[s + 1] - cu[s];
-      nb = (L + kBlock - 1) / kBlock;
+      nb = (L + kUnit - 1) / kUnit;
       const int nch = (L + chunk - 1) / chunk;
-      for (int j = 0; j < nch; ++j) ni += chunk_items(L, chunk, j);
+      for (int j = 0; j < nch; ++j) ni += chunk_items<kUnit>(L, chunk, j);
     }
     sb[tid] = nb;
     si[tid] = ni;
@@ -113,12 +118,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 
 }  // namespace
 
-void launch_plan(const int32_t* cu, const Sizes& z, const PlanBufs& p, hipStream_t st) {
-  {
-    KernelTimer timer("plan", st);
-    plan_kernel<<<1, kPlanThreads, 0, st>>>(cu, (int)z.S, (int)z.chunk, (int)z.ntiles, p.blkbase, p.blk_seq,
-                                            p.seqitem, p.totals, p.tile_order);
-  }
+void launch_plan(const int32_t* cu, const Sizes& z, const PlanBufs& p, hipStream_t st, int unit) {
+  KernelTimer timer("plan", st);
+  if (unit == kQsaKeyTile)
+    plan_kernel<kQsaKeyTile><<<1, kPlanThreads, 0, st>>>(cu, (int)z.S, (int)z.chunk, (int)z.ntiles, p.blkbase,
+                                                        p.blk_seq, p.seqitem, p.totals, p.tile_order);
+  else
+    plan_kernel<kBlock><<<1, kPlanThreads, 0, st>>>(cu, (int)z.S, (int)z.chunk, (int)z.ntiles, p.blkbase,
+                                                   p.blk_seq, p.seqitem, p.totals, p.tile_order);
 }
 
 }  // namespace msa

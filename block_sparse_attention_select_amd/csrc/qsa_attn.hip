@@ -1,0 +1,861 @@
+// Narrow-block variant of the block-sparse GQA attention on gfx950: the same
+// attention as the wide kernels (attn_fwd.hip, attn_bwd*.hip) for the pages'
+// second workload, 4-token blocks with head dim 256 and 12 query heads per KV
+// head (radixark/miles PR #4581, kernel-tuning commit message: launch configs
+// per block width, narrow = qwen3.8-next's 4-token blocks; 12 q / 1 kv head,
+// D 256, 16k-token packs).
+//
+// What is computed is the wide variant's definition with 4-token blocks: for
+// token t, query head g and KV head h = g / 12, the keys are every key j <= t
+// of the blocks listed in blk_idx[t, h, :] (sequence-local 4-token block ids,
+// any order, -1 padding; ids past t's own block are ignored, duplicates count
+// once); O = softmax(scale q.k) v with the natural-log LSE; the backward gives
+// dq, dk, dv of sum(O * dO).
+//
+// Tiling.  A query lists hundreds of 4-token blocks, far too small to stage
+// one at a time, so keys are staged in tiles of 64 (16 blocks): the kernels
+// walk key tiles and mask, per query, the blocks it did not list.  Selections
+// arrive as a per-(token, KV head) bitmap over the sequence's blocks
+// (qsa_bitmap_kernel), 16 bits per key tile.
+//   forward   one 8-wavefront workgroup per (8 consecutive tokens, KV head),
+//             wavefront w owning token w (q as MFMA B operands, O^T in
+//             registers); the workgroup walks the union of its tokens' key
+//             tiles with K and V^T staged in LDS, double buffered;
+//   dQ        the same walk with K and V staged; K^T operands are read
+//             transposed from the K stage; it also forms Delta = rowsum(dO*O)
+//             and -LSE * log2(e) per head for the dK/dV pass;
+//   dK/dV     key-tile major: one workgroup per (sequence, query chunk, key
+//             tile), four wavefronts of 16 keys with K and V in registers,
+//             streaming the chunk's selecting tokens through LDS two at a time;
+//             chunk slices are summed in chunk order by qsa_reduce_kernel
+//             (fixed order, no atomics).
+// Query heads are padded from 12 to the MFMA's 16 with zero q (forward, dQ) or
+// with statistics that zero P (dK/dV); padded outputs are never stored.
+#include "attn_stage.h"
+
+namespace msa {
+
+namespace {
+
+constexpr int kD = kQsaHeadDim;   // 256
+constexpr int kG = kQsaGroup;     // 12
+constexpr int kKT = kQsaKeyTile;  // 64
+constexpr int kWords = kQsaWords; // 256
+constexpr int kTok = 8;           // tokens (wavefronts) per forward / dQ workgroup
+constexpr int kUnionWords = 32;   // a tile's key tiles span fewer than 1024 global ids
+constexpr int kUnionMax = kUnionWords * 32;
+constexpr float kRescaleSlack = 8.f;  // log2 units
+
+// 16-bit mask of the blocks of key tile c (sequence-local) in a bitmap row.
+__device__ __forceinline__ uint32_t tile_mask(const uint32_t* row, int c) {
+  return (row[c >> 1] >> (16 * (c & 1))) & 0xFFFFu;
+}
+
+// ---------------------------------------------------------------------------
+// Selection bitmaps: one wavefront per (token, KV head); bit b of the row is
+// set when block b is listed and b <= the token's own block.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void qsa_bitmap_kernel(const int32_t* __restrict__ blk_idx, int topk,
+                                                         const int32_t* __restrict__ cu, int S, int T, int Hk,
+                                                         uint32_t* __restrict__ bits) {
+  __shared__ uint32_t row[4][kWords];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  const int h = blockIdx.y;
+  for (int i = lane; i < kWords; i += 64) row[wave][i] = 0u;
+  __syncthreads();
+  if (t < T) {
+    const int s = find_seq(cu, S, t);
+    const int b = (t - cu[s]) / kQsaBlock;
+    const int32_t* ids = blk_idx + ((int64_t)t * Hk + h) * topk;
+    for (int e = lane; e < topk; e += 64) {
+      const int c = ids[e];
+      if (c >= 0 && c <= b) atomicOr(&row[wave][c >> 5], 1u << (c & 31));
+    }
+  }
+  __syncthreads();
+  if (t < T) {
+    const u32x4 x = {row[wave][4 * lane], row[wave][4 * lane + 1], row[wave][4 * lane + 2], row[wave][4 * lane + 3]};
+    *reinterpret_cast<u32x4*>(bits + ((int64_t)t * Hk + h) * kWords + 4 * lane) = x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// V^T of every (key tile, KV head) in the forward's operand order: run
+// 2 dt + kc, lane li + 16 g holds V[key 32 kc + 8 g + e][dim 16 dt + li],
+// e = 0..7 (zero past the sequence end).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void qsa_vt_kernel(const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
+                                                     const int32_t* __restrict__ cu,
+                                                     const int32_t* __restrict__ ktbase,
+                                                     const int32_t* __restrict__ kt_seq,
+                                                     const int32_t* __restrict__ totals, int Hk,
+                                                     u16* __restrict__ vt) {
+  __shared__ __align__(16) u16 tile[kKT][kD + 8];
+  const int gk = blockIdx.x, h = blockIdx.y;
+  if (gk >= totals[0]) return;
+  const int s = kt_seq[gk];
+  const int c = gk - ktbase[s];
+  const int seq0 = cu[s], L = cu[s + 1] - seq0;
+  for (int i = threadIdx.x; i < kKT * kD / 8; i += 256) {
+    const int key = i / (kD / 8), d8 = (i % (kD / 8)) * 8;
+    const int kp = kKT * c + key;
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    if (kp < L) x = *reinterpret_cast<const uint4*>(v + (int64_t)(seq0 + kp) * v_st + (int64_t)h * v_sh + d8);
+    *reinterpret_cast<uint4*>(&tile[key][d8]) = x;
+  }
+  __syncthreads();
+  u16* dst = vt + ((int64_t)gk * Hk + h) * (32 * 64 * 8);
+  for (int i = threadIdx.x; i < 32 * 64; i += 256) {
+    const int run = i >> 6, ln = i & 63;
+    const int d = 16 * (run >> 1) + (ln & 15);
+    const int k0 = 32 * (run & 1) + 8 * (ln >> 4);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)tile[k0 + 2 * e][d] | ((uint32_t)tile[k0 + 2 * e + 1][d] << 16);
+    *reinterpret_cast<u32x4*>(dst + (int64_t)i * 8) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared prologue of the token-major passes: the tile's 8 tokens' bitmap rows
+// into LDS and the ascending union of the global key tiles they touch.
+// ---------------------------------------------------------------------------
+struct TileUnion {
+  uint32_t bmap[kTok][kWords];
+  uint32_t ubits[kUnionWords];
+  int ulist[kUnionMax];
+  int ukey0[kUnionMax];  // first token of each union key tile
+  int nunion;
+};
+
+__device__ __forceinline__ void build_union(TileUnion& tu, const uint32_t* __restrict__ bits,
+                                            const int32_t* __restrict__ cu, const int32_t* __restrict__ ktbase,
+                                            const int32_t* __restrict__ kt_seq, int S, int Hk, int h, int t0,
+                                            int wave, int lane, bool tok_ok, int t, int pos_t, int ktb_t) {
+  const int gk_lo = ktbase[find_seq(cu, S, t0)];
+  if (threadIdx.x < kUnionWords) tu.ubits[threadIdx.x] = 0u;
+  __syncthreads();
+  const uint32_t* brow = bits + ((int64_t)(tok_ok ? t : 0) * Hk + h) * kWords;
+  const int nw = tok_ok ? (pos_t / kQsaBlock) / 32 + 1 : 0;
+  for (int w = lane; w < kWords; w += 64) {
+    const uint32_t x = w < nw ? brow[w] : 0u;
+    tu.bmap[wave][w] = x;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      if ((x >> (16 * hh)) & 0xFFFFu) {
+        const int rel = ktb_t + 2 * w + hh - gk_lo;
+        atomicOr(&tu.ubits[rel >> 5], 1u << (rel & 31));
+      }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t x = lane < kUnionWords ? tu.ubits[lane] : 0u;
+    const int cnt = __popc(x);
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    int pos = incl - cnt;
+    while (x) {
+      const int bit = __ffs(x) - 1;
+      const int gk = gk_lo + 32 * lane + bit;
+      const int sb = kt_seq[gk];
+      tu.ulist[pos] = gk;
+      tu.ukey0[pos++] = cu[sb] + kKT * (gk - ktbase[sb]);
+      x &= x - 1u;
+    }
+    if (lane == 63) tu.nunion = incl;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Forward.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64 * kTok) void qsa_fwd_kernel(
+    const u16* __restrict__ q, int64_t q_st, int64_t q_sh, const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
+    const u16* __restrict__ vt, const uint32_t* __restrict__ bits, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ ktbase, const int32_t* __restrict__ kt_seq, const int32_t* __restrict__ tile_order,
+    int S, int T, int Hk, float scale_log2, u16* __restrict__ o, int64_t o_st, int64_t o_sh,
+    float* __restrict__ lse) {
+  // K runs kt * 8 + ds: keys score_key(kt, .) of the tile, dims 32 ds ..;
+  // V^T runs 2 dt + kc as laid out by qsa_vt_kernel
+  __shared__ u32x4 kbuf[2][32][64];
+  __shared__ u32x4 vbuf[2][32][64];
+  __shared__ TileUnion tu;
+
+  // workgroup b: KV head b % Hk, second or first half of the 16-token tile in
+  // launch slot b / (2 Hk)
+  const int h = blockIdx.x % Hk;
+  const int t0 = tile_order[blockIdx.x / (2 * Hk)] * kAttnTile + kTok * ((blockIdx.x / Hk) & 1);
+  if (t0 >= T) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int li = lane & 15;
+  const int t = t0 + wave;
+  const bool tok_ok = t < T;
+  int s_t = 0, pos_t = 0;
+  if (tok_ok) {
+    s_t = find_seq(cu, S, t);
+    pos_t = t - cu[s_t];
+  }
+  s_t = __builtin_amdgcn_readfirstlane(s_t);
+  pos_t = __builtin_amdgcn_readfirstlane(pos_t);
+  const int ktb_t = tok_ok ? ktbase[s_t] : 0;
+  const int own_c = pos_t / kKT;
+
+  build_union(tu, bits, cu, ktbase, kt_seq, S, Hk, h, t0, wave, lane, tok_ok, t, pos_t, ktb_t);
+  const int nu = tu.nunion;
+
+  // q of this token as B operands (heads past 12 zero), O^T accumulators
+  bf16x8 qb[8];
+  {
+    const bool hv = tok_ok && li < kG;
+    const u16* qrow = q + (int64_t)(tok_ok ? t : 0) * q_st + (int64_t)(h * kG + min(li, kG - 1)) * q_sh + 8 * g;
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) qb[ds] = hv ? load_bf16x8(qrow + 32 * ds) : zero_bf16x8();
+  }
+  f32x4 oacc[16];
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // staging of union step u: wavefront w copies K runs 4w .. 4w+3 (key tile
+  // w / 2, dims 128 (w % 2) + 32 ii ..) and V^T runs 4w .. 4w+3
+  auto stage = [&](int u, int buf) {
+    const int gk = __builtin_amdgcn_readfirstlane(tu.ulist[u]);
+    const int kstart = __builtin_amdgcn_readfirstlane(tu.ukey0[u]);
+    const int ln = fresh_lane();
+    const int key = score_key(wave >> 1, ln & 15);
+    const int d0 = 128 * (wave & 1) + 8 * (ln >> 4);
+    if (kstart + kKT <= T) {
+      const u16* base = k + (int64_t)kstart * k_st + (int64_t)h * k_sh + 128 * (wave & 1);
+      const uint32_t off = (uint32_t)(2 * (key * k_st + 8 * (ln >> 4)));
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) dma16s(base + 32 * ii, off, lds_offset(&kbuf[buf][4 * wave + ii][0]));
+    } else {  // the pack's last key tile: keys past the end repeat the last token
+      const int kk = min(kstart + key, T - 1);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        dma16(k + (int64_t)kk * k_st + (int64_t)h * k_sh + d0 + 32 * ii, lds_offset(&kbuf[buf][4 * wave + ii][0]));
+    }
+    const u16* vbase = vt + (((int64_t)gk * Hk + h) * 32 + 4 * wave) * 512;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) dma16s(vbase + 512 * ii, 16 * ln, lds_offset(&vbuf[buf][4 * wave + ii][0]));
+  };
+  if (nu > 0) stage(0, 0);
+  wait_copies();
+  wait_all_loads();
+  __syncthreads();
+
+  for (int u = 0; u < nu; ++u) {
+    const int buf = u & 1;
+    if (u + 1 < nu) stage(u + 1, buf ^ 1);
+    const int c = tu.ulist[u] - ktb_t;  // key tile of this token's sequence (when in range)
+    const uint32_t m16 = (tok_ok && c >= 0 && c <= own_c) ? tile_mask(tu.bmap[wave], c) : 0u;
+    if (m16 != 0u) {
+      const bool own = (c == own_c);
+      const int plim = pos_t - kKT * c;  // causal: tile keys at index <= plim
+      // S^T for the tile's four 16-key tiles: four chains interleaved, K
+      // operand reads eight ahead of the MFMAs
+      f32x4 st[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      {
+        bf16x8 ka[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) ka[i] = __builtin_bit_cast(bf16x8, kbuf[buf][(i & 3) * 8 + (i >> 2)][lane]);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) st[i & 3] = mfma16x16x32(ka[i], qb[i >> 2], st[i & 3]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 24; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      }
+      // mask: accumulator row r of tile kt in lane group g is tile key
+      // score_key(kt, 4g + r) = 32 (kt/2) + 8g + 4 (kt%2) + r, all four in
+      // block 8 (kt/2) + 2g + kt%2
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const bool listed = (m16 >> (8 * (kt >> 1) + 2 * g + (kt & 1))) & 1u;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kl = 32 * (kt >> 1) + 8 * g + 4 * (kt & 1) + r;
+          const bool keep = listed && (!own || kl <= plim);
+          st[kt][r] = keep ? st[kt][r] : -INFINITY;
+          mx = fmaxf(mx, st[kt][r]);
+        }
+      }
+      // online softmax in base 2 (scale folded into the exponent's FMA); the
+      // running max moves only when it grows by more than kRescaleSlack
+      mx = max_over_groups(mx);
+      const float m_cand = mx * scale_log2;
+      const bool grow = m_cand > m_run + kRescaleSlack;
+      const float m_use = grow ? m_cand : m_run;
+      const float alpha = grow ? fast_exp2(m_run - m_cand) : 1.f;
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(fmaf(st[kt][r], scale_log2, -m_use));
+          st[kt][r] = p;
+          rs += p;
+        }
+      l_run = l_run * alpha + rs;
+      m_run = m_use;
+      if (__ballot(grow)) {
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt) oacc[dt] *= alpha;
+      }
+      const bf16x8 pf0 = pack_bf16x8(st[0], st[1]);
+      const bf16x8 pf1 = pack_bf16x8(st[2], st[3]);
+      // O^T += V^T P^T over the tile's two 32-key halves
+      {
+        bf16x8 va[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) va[i] = __builtin_bit_cast(bf16x8, vbuf[buf][(i & 15) * 2 + (i >> 4)][lane]);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) oacc[i & 15] = mfma16x16x32(va[i], i < 16 ? pf0 : pf1, oacc[i & 15]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 24; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      }
+    }
+    wait_copies();
+    lds_barrier();
+  }
+
+  // l_run holds this lane's share of the row sum (its keys 8g.. of every 32)
+  l_run = sum_over_groups(l_run);
+  if (tok_ok && li < kG) {
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+    u16* orow = o + (int64_t)t * o_st + (int64_t)(h * kG + li) * o_sh;
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = pack_bf16x4(oacc[dt] * inv);
+    if (g == 0)
+      lse[(int64_t)t * (Hk * kG) + h * kG + li] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and Delta, -LSE log2 e for the dK/dV pass).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64 * kTok) void qsa_dq_kernel(
+    const u16* __restrict__ q, int64_t q_st, int64_t q_sh, const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
+    const u16* __restrict__ v, int64_t v_st, int64_t v_sh, const u16* __restrict__ o, int64_t o_st, int64_t o_sh,
+    const u16* __restrict__ dO, int64_t do_st, int64_t do_sh, const float* __restrict__ lse,
+    const uint32_t* __restrict__ bits, const int32_t* __restrict__ cu, const int32_t* __restrict__ ktbase,
+    const int32_t* __restrict__ kt_seq, const int32_t* __restrict__ tile_order, int S, int T, int Hk,
+    float scale_log2, float scale, u16* __restrict__ dq, int64_t dq_st, int64_t dq_sh, float* __restrict__ delta,
+    float* __restrict__ nlse) {
+  // K and V runs kt * 8 + ds (keys score_key(kt, .), dims 32 ds ..), stored
+  // swizzled (swz_slot) for the transposed K^T reads
+  __shared__ u32x4 kbuf[2][32][64];
+  __shared__ u32x4 vbuf[2][32][64];
+  __shared__ TileUnion tu;
+
+  const int h = blockIdx.x % Hk;
+  const int t0 = tile_order[blockIdx.x / (2 * Hk)] * kAttnTile + kTok * ((blockIdx.x / Hk) & 1);
+  if (t0 >= T) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int li = lane & 15;
+  const int t = t0 + wave;
+  const bool tok_ok = t < T;
+  int s_t = 0, pos_t = 0;
+  if (tok_ok) {
+    s_t = find_seq(cu, S, t);
+    pos_t = t - cu[s_t];
+  }
+  s_t = __builtin_amdgcn_readfirstlane(s_t);
+  pos_t = __builtin_amdgcn_readfirstlane(pos_t);
+  const int ktb_t = tok_ok ? ktbase[s_t] : 0;
+  const int own_c = pos_t / kKT;
+
+  build_union(tu, bits, cu, ktbase, kt_seq, S, Hk, h, t0, wave, lane, tok_ok, t, pos_t, ktb_t);
+  const int nu = tu.nunion;
+
+  // q and dO as B operands; Delta = rowsum(dO * O) and the LSE of this lane's head
+  const bool hv = tok_ok && li < kG;
+  const int hq = h * kG + min(li, kG - 1);
+  const int trow = tok_ok ? t : 0;
+  bf16x8 qb[8], db[8];
+  float dl, lse2;
+  {
+    const u16* qrow = q + (int64_t)trow * q_st + (int64_t)hq * q_sh + 8 * g;
+    const u16* drow = dO + (int64_t)trow * do_st + (int64_t)hq * do_sh + 8 * g;
+    const u16* orow = o + (int64_t)trow * o_st + (int64_t)hq * o_sh + 8 * g;
+    float part = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) {
+      qb[ds] = hv ? load_bf16x8(qrow + 32 * ds) : zero_bf16x8();
+      db[ds] = hv ? load_bf16x8(drow + 32 * ds) : zero_bf16x8();
+      const bf16x8 ob = hv ? load_bf16x8(orow + 32 * ds) : zero_bf16x8();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf((float)db[ds][e], (float)ob[e], part);
+    }
+    dl = sum_over_groups(part);
+    const float l = hv ? lse[(int64_t)t * (Hk * kG) + hq] : -INFINITY;
+    lse2 = l * kLog2e;  // -inf for empty rows and padded heads: P = 0 there
+    if (tok_ok && g == 0) {
+      delta[((int64_t)t * Hk + h) * 16 + li] = hv ? dl : 0.f;
+      nlse[((int64_t)t * Hk + h) * 16 + li] = lse2 > -INFINITY ? -lse2 : -INFINITY;
+    }
+  }
+  const bool live = lse2 > -INFINITY;
+  f32x4 dqacc[16];
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) dqacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // staging of union step u: wavefront w copies K runs 4w .. 4w+3 and the same
+  // V runs (key tile w / 2, dims 128 (w % 2) + 32 ii ..)
+  auto stage = [&](int u, int buf) {
+    const int kstart = __builtin_amdgcn_readfirstlane(tu.ukey0[u]);
+    const int ln = fresh_lane();
+    const int key = score_key(wave >> 1, swz_slot(ln) & 15);  // runs stored swizzled
+    const int d0 = 128 * (wave & 1) + 8 * (ln >> 4);
+    if (kstart + kKT <= T) {
+      const u16* kb = k + (int64_t)kstart * k_st + (int64_t)h * k_sh + 128 * (wave & 1);
+      const u16* vb = v + (int64_t)kstart * v_st + (int64_t)h * v_sh + 128 * (wave & 1);
+      const uint32_t koff = (uint32_t)(2 * (key * k_st + 8 * (ln >> 4)));
+      const uint32_t voff = (uint32_t)(2 * (key * v_st + 8 * (ln >> 4)));
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        dma16s(kb + 32 * ii, koff, lds_offset(&kbuf[buf][4 * wave + ii][0]));
+        dma16s(vb + 32 * ii, voff, lds_offset(&vbuf[buf][4 * wave + ii][0]));
+      }
+    } else {
+      const int kk = min(kstart + key, T - 1);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        dma16(k + (int64_t)kk * k_st + (int64_t)h * k_sh + d0 + 32 * ii, lds_offset(&kbuf[buf][4 * wave + ii][0]));
+        dma16(v + (int64_t)kk * v_st + (int64_t)h * v_sh + d0 + 32 * ii, lds_offset(&vbuf[buf][4 * wave + ii][0]));
+      }
+    }
+  };
+  if (nu > 0) stage(0, 0);
+  wait_copies();
+  wait_all_loads();
+  __syncthreads();
+
+  for (int u = 0; u < nu; ++u) {
+    const int buf = u & 1;
+    if (u + 1 < nu) stage(u + 1, buf ^ 1);
+    const int c = tu.ulist[u] - ktb_t;
+    const uint32_t m16 = (tok_ok && c >= 0 && c <= own_c) ? tile_mask(tu.bmap[wave], c) : 0u;
+    if (m16 != 0u) {
+      const bool own = (c == own_c);
+      const int plim = pos_t - kKT * c;
+      // two halves of 32 keys (key tiles 2kc, 2kc+1): S^T and dP^T, then
+      // dS^T as the B operand of dQ^T = K^T dS^T
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        if (own && 32 * kc > plim) break;
+        f32x4 sacc[2], pacc[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          sacc[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+          pacc[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        {
+          const int swz = swz_slot(lane);
+          bf16x8 op[32];  // i = ds * 4 + kk * 2 + (0: K, 1: V)
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            const int run = (2 * kc + ((i >> 1) & 1)) * 8 + (i >> 2);
+            op[i] = __builtin_bit_cast(bf16x8, (i & 1) ? vbuf[buf][run][swz] : kbuf[buf][run][swz]);
+          }
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            const int kk = (i >> 1) & 1, ds = i >> 2;
+            if (i & 1)
+              pacc[kk] = mfma16x16x32(op[i], db[ds], pacc[kk]);
+            else
+              sacc[kk] = mfma16x16x32(op[i], qb[ds], sacc[kk]);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+          for (int i = 0; i < 24; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        }
+        // dS^T = P^T (dP^T - Delta) on listed causal keys; row r of tile
+        // 2kc + kk in lane group g is tile key 32 kc + 8g + 4kk + r, block
+        // 8 kc + 2g + kk
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const bool listed = live && ((m16 >> (8 * kc + 2 * g + kk)) & 1u);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int kl = 32 * kc + 8 * g + 4 * kk + r;
+            const bool on = listed && (!own || kl <= plim);
+            const float e = fast_exp2(fmaf(sacc[kk][r], scale_log2, -lse2));
+            sacc[kk][r] = on ? e * (pacc[kk][r] - dl) : 0.f;
+          }
+        }
+        const bf16x8 dsf = pack_bf16x8(sacc[0], sacc[1]);
+        {
+          // K^T operands read transposed from the K stage: keys 8g .. 8g+7 of
+          // the half (tiles 2kc, 2kc+1, rows 4g .. 4g+3) at dim 16 dt + li
+          const uint32_t kq = lds_offset(&kbuf[buf][16 * kc][0]) + tr_lane_offset(fresh_lane());
+          bf16x8 ta[16];
+#pragma unroll
+          for (int dt = 0; dt < 16; ++dt) {
+            const uint32_t off = kq + (dt >> 1) * 1024 + (dt & 1) * 512;
+            const uint2 lo = read_tr16(off), hi = read_tr16(off + 8192);
+            ta[dt] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+          }
+#pragma unroll
+          for (int dt = 0; dt < 16; ++dt) dqacc[dt] = mfma16x16x32(ta[dt], dsf, dqacc[dt]);
+          __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+          for (int i = 0; i < 10; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+        }
+      }
+    }
+    wait_copies();
+    lds_barrier();
+  }
+
+  if (tok_ok && li < kG) {
+    u16* out = dq + (int64_t)t * dq_st + (int64_t)(h * kG + li) * dq_sh;
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) *reinterpret_cast<uint2*>(out + 16 * dt + 4 * g) = pack_bf16x4(dqacc[dt] * scale);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV.
+// ---------------------------------------------------------------------------
+constexpr int kPair = 2;  // tokens per staging round (one MFMA step)
+
+// Stage layout of one token (u32x4 units): [0, 512) q and [512, 1024) dO as
+// [ds][slot], operand lane li + 16g of run ds (head li, dims 32 ds + 8g ..) at
+// slot swz_slot(li + 16g); heads past 12 repeat head 11 (finite operands whose
+// P the statistics zero).  Stats: 16 -LSE log2 e, then 16 Delta.
+__device__ __forceinline__ void stage_token(int t, int h, int Hk, int lane, uint32_t slot_lds, uint32_t stats_lds,
+                                            const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
+                                            const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
+                                            const float* __restrict__ nlse, const float* __restrict__ delta) {
+  t = __builtin_amdgcn_readfirstlane(t);
+  const int hr = min(swz_slot(lane) & 15, kG - 1);
+  const uint32_t q_off = (uint32_t)(2 * (hr * q_sh + 8 * (lane >> 4)));
+  const uint32_t do_off = (uint32_t)(2 * (hr * do_sh + 8 * (lane >> 4)));
+  const u16* qr = q + (int64_t)t * q_st + (int64_t)(h * kG) * q_sh;
+  const u16* dr = dO + (int64_t)t * do_st + (int64_t)(h * kG) * do_sh;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    dma16s(qr + 32 * i, q_off, slot_lds + i * 1024);
+    dma16s(dr + 32 * i, do_off, slot_lds + 8192 + i * 1024);
+  }
+  const int64_t row = ((int64_t)t * Hk + h) * 16;
+  if (lane < 16)
+    dma4s(nlse + row, 4 * lane, stats_lds);
+  else if (lane < 32)
+    dma4s(delta + row - 16, 4 * lane, stats_lds);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void qsa_dkdv_kernel(
+    const u16* __restrict__ q, int64_t q_st, int64_t q_sh, const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
+    const u16* __restrict__ v, int64_t v_st, int64_t v_sh, const u16* __restrict__ dO, int64_t do_st,
+    int64_t do_sh, const float* __restrict__ nlse, const float* __restrict__ delta,
+    const uint32_t* __restrict__ bits, const int32_t* __restrict__ cu, const int32_t* __restrict__ seqitem,
+    const int32_t* __restrict__ totals, int S, int Hk, int chunk, int items_cap, float scale_log2, float scale,
+    int32_t* __restrict__ item_count, float* __restrict__ part_dk, float* __restrict__ part_dv,
+    u16* __restrict__ dk_out, int64_t dk_st, int64_t dk_sh, u16* __restrict__ dv_out, int64_t dv_st,
+    int64_t dv_sh) {
+  __shared__ u32x4 stage[2][kPair][1024];
+  __shared__ __align__(16) float stats[2][kPair][32];
+  __shared__ int sel[kDkdvChunkMax];  // (position - p_begin) | (block mask << 16)
+  __shared__ int wcount[4];
+
+  const int h = blockIdx.y;
+  const int item = blockIdx.x;
+  if (item >= totals[1]) return;
+  // decode (sequence, query chunk j, key tile c)
+  const int s = upper_index(seqitem, S, item);
+  const int seq0 = cu[s];
+  const int L = cu[s + 1] - seq0;
+  const int nch = (L + chunk - 1) / chunk;
+  int r = item - seqitem[s];
+  int j = 0;
+  for (;;) {
+    const int cnt = (min((j + 1) * chunk, L) - 1) / kKT + 1;
+    if (r < cnt) break;
+    r -= cnt;
+    ++j;
+  }
+  const int c = r;
+  const int jmin = (kKT * c) / chunk;
+  const bool single = (j == nch - 1) && (j == jmin);
+  const int p_begin = max(j * chunk, kKT * c);
+  const int p_end = min((j + 1) * chunk, L);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int li = lane & 15;
+
+  // 1. the chunk's queries that listed a block of key tile c, in token order
+  int nsel = 0;
+  for (int p0 = p_begin; p0 < p_end; p0 += 256) {
+    const int p = p0 + threadIdx.x;
+    uint32_t m = 0u;
+    if (p < p_end) m = tile_mask(bits + ((int64_t)(seq0 + p) * Hk + h) * kWords, c);
+    const uint64_t bal = __ballot(m != 0u);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wcount[wave] = __popcll(bal);
+    __syncthreads();
+    int off = nsel;
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      off += w < wave ? wcount[w] : 0;
+      tot += wcount[w];
+    }
+    if (m != 0u) sel[off + before] = (p - p_begin) | (int)(m << 16);
+    nsel += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) item_count[(int64_t)h * items_cap + item] = nsel;
+
+  // 2. K and V of this wavefront's 16 keys as B operands (zero past the end)
+  const int kbase = kKT * c + 16 * wave;
+  bf16x8 kf[8], vf[8];
+  {
+    const int kp = kbase + li;
+    const bool ok = kp < L;
+    const u16* krow = k + (int64_t)(seq0 + min(kp, L - 1)) * k_st + (int64_t)h * k_sh + 8 * g;
+    const u16* vrow = v + (int64_t)(seq0 + min(kp, L - 1)) * v_st + (int64_t)h * v_sh + 8 * g;
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) {
+      kf[ds] = ok ? load_bf16x8(krow + 32 * ds) : zero_bf16x8();
+      vf[ds] = ok ? load_bf16x8(vrow + 32 * ds) : zero_bf16x8();
+    }
+  }
+  f32x4 dk[16], dv[16];
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) {
+    dk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // 3. stream the selecting tokens through LDS, two per MFMA step; wavefronts
+  // 0 and 1 copy the two tokens of a round
+  if (nsel > 0) {
+    const int nround = (nsel + kPair - 1) / kPair;
+    auto stage_round = [&](int bi, int buf) {
+      if (wave < kPair) {
+        const int n = min(bi * kPair + wave, nsel - 1);  // past the end: repeat the last token (masked)
+        stage_token(seq0 + p_begin + (sel[n] & 0xFFFF), h, Hk, fresh_lane(), lds_offset(&stage[buf][wave][0]),
+                    lds_offset(&stats[buf][wave][0]), q, q_st, q_sh, dO, do_st, do_sh, nlse, delta);
+      }
+    };
+    stage_round(0, 0);
+    wait_copies();
+    wait_all_loads();
+    __syncthreads();
+#pragma unroll 1
+    for (int bi = 0; bi < nround; ++bi) {
+      const int cur = bi & 1;
+      if (bi + 1 < nround) stage_round(bi + 1, cur ^ 1);
+      const int n0 = bi * kPair;
+      // a missing second token is masked out entirely
+      int pos[2];
+      uint32_t msk[2];
+#pragma unroll
+      for (int tk = 0; tk < 2; ++tk) {
+        const bool ok = n0 + tk < nsel;
+        const int e = sel[min(n0 + tk, nsel - 1)];
+        pos[tk] = p_begin + (e & 0xFFFF);
+        msk[tk] = ok ? ((uint32_t)e >> 16) : 0u;
+      }
+      // S = q K^T and dP = dO V^T per token, turned into bf16 P and dS: lane
+      // (key li, group g) keeps heads 4g .. 4g+3 of each token, two per dword,
+      // as the A operand of dV and dK (dwords 0-1 token 0, dwords 2-3 token 1)
+      u32x4 pw, sw;
+      const int ln = fresh_lane();
+      const int sl = swz_slot(ln);
+      // the lane's key: kbase + li, in block (16 wave + li) / 4 of the tile
+      const int kp = kbase + li;
+#pragma unroll
+      for (int tk = 0; tk < 2; ++tk) {
+        const u32x4* b = stage[cur][tk];
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, pacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < 8; ++ds) {
+          const bf16x8 qa = __builtin_bit_cast(bf16x8, b[ds * 64 + sl]);
+          const bf16x8 da = __builtin_bit_cast(bf16x8, b[512 + ds * 64 + sl]);
+          sacc = mfma16x16x32(qa, kf[ds], sacc);
+          pacc = mfma16x16x32(da, vf[ds], pacc);
+        }
+        const f32x4 nl = reinterpret_cast<const f32x4*>(stats[cur][tk])[ln >> 4];
+        const f32x4 d4 = reinterpret_cast<const f32x4*>(stats[cur][tk] + 16)[ln >> 4];
+        const bool on = ((msk[tk] >> (4 * wave + (li >> 2))) & 1u) && kp <= pos[tk];
+        f32x4 e, d;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          e[rr] = on ? fast_exp2(fmaf(sacc[rr], scale_log2, nl[rr])) : 0.f;
+          d[rr] = e[rr] * (pacc[rr] - d4[rr]);
+        }
+        pw[2 * tk] = pack_bf16x2(e[0], e[1]);
+        pw[2 * tk + 1] = pack_bf16x2(e[2], e[3]);
+        sw[2 * tk] = pack_bf16x2(d[0], d[1]);
+        sw[2 * tk + 1] = pack_bf16x2(d[2], d[3]);
+      }
+      const bf16x8 pA = __builtin_bit_cast(bf16x8, pw);
+      const bf16x8 sA = __builtin_bit_cast(bf16x8, sw);
+      const uint32_t tro = tr_lane_offset(ln);
+      const uint32_t q0 = lds_offset(stage[cur][0]) + tro, q1 = lds_offset(stage[cur][1]) + tro;
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) {
+        const uint32_t off = (dt >> 1) * 1024 + (dt & 1) * 512;
+        const uint2 a0 = read_tr16(q0 + 8192 + off);
+        const uint2 a1 = read_tr16(q1 + 8192 + off);
+        const uint2 c0 = read_tr16(q0 + off);
+        const uint2 c1 = read_tr16(q1 + off);
+        const bf16x8 bdo = __builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y});
+        const bf16x8 bq = __builtin_bit_cast(bf16x8, u32x4{c0.x, c0.y, c1.x, c1.y});
+        dv[dt] = mfma16x16x32(pA, bdo, dv[dt]);
+        dk[dt] = mfma16x16x32(sA, bq, dk[dt]);
+      }
+      wait_copies();
+      lds_barrier();
+    }
+  }
+
+  // 4. results: lane holds key kbase + 4g + r, dim 16 dt + li
+  if (single) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int kp = kbase + 4 * g + rr;
+      if (kp >= L) continue;
+      u16* dkr = dk_out + (int64_t)(seq0 + kp) * dk_st + (int64_t)h * dk_sh + li;
+      u16* dvr = dv_out + (int64_t)(seq0 + kp) * dv_st + (int64_t)h * dv_sh + li;
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) {
+        dkr[16 * dt] = f2bf(dk[dt][rr] * scale);
+        dvr[16 * dt] = f2bf(dv[dt][rr]);
+      }
+    }
+  } else if (nsel > 0) {
+    const int64_t slice = ((int64_t)h * items_cap + item) * (kKT * kD);
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int key = 16 * wave + 4 * g + rr;
+        const int64_t off = slice + (int64_t)key * kD + 16 * dt + li;
+        part_dk[off] = dk[dt][rr];
+        part_dv[off] = dv[dt][rr];
+      }
+  }
+}
+
+// Ordered sum of the chunk slices of one (key tile, 16 keys, KV head).
+__global__ __launch_bounds__(256) void qsa_reduce_kernel(
+    const float* __restrict__ part_dk, const float* __restrict__ part_dv, const int32_t* __restrict__ item_count,
+    const int32_t* __restrict__ seqitem, const int32_t* __restrict__ kt_seq, const int32_t* __restrict__ ktbase,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ totals, int chunk, int items_cap, float scale,
+    u16* __restrict__ dk, int64_t dk_st, int64_t dk_sh, u16* __restrict__ dv, int64_t dv_st, int64_t dv_sh) {
+  const int gk = blockIdx.x;
+  const int slice = blockIdx.y;
+  const int h = blockIdx.z;
+  if (gk >= totals[0]) return;
+  const int s = kt_seq[gk];
+  const int c = gk - ktbase[s];
+  const int seq0 = cu[s];
+  const int L = cu[s + 1] - seq0;
+  const int nch = (L + chunk - 1) / chunk;
+  const int jmin = (kKT * c) / chunk;
+  if (jmin == nch - 1) return;  // a key tile with one work item was written by the dK/dV kernel
+  const int item0 = seqitem[s];
+  const int e0 = slice * 16 * kD;
+  for (int e = e0 + threadIdx.x * 4; e < e0 + 16 * kD; e += 256 * 4) {
+    const int key = e / kD;
+    const int d = e - key * kD;
+    const int kp = kKT * c + key;
+    if (kp >= L) continue;
+    f32x4 adk = {0.f, 0.f, 0.f, 0.f};
+    f32x4 adv = {0.f, 0.f, 0.f, 0.f};
+    int base = 0;
+    for (int j = 0; j < nch; ++j) {
+      const int cnt = (min((j + 1) * chunk, L) - 1) / kKT + 1;
+      const int it = item0 + base + c;
+      base += cnt;
+      if (j < jmin || it >= items_cap) continue;
+      if (item_count[(int64_t)h * items_cap + it] == 0) continue;
+      const int64_t off = ((int64_t)h * items_cap + it) * (kKT * kD) + e;
+      adk += *reinterpret_cast<const f32x4*>(part_dk + off);
+      adv += *reinterpret_cast<const f32x4*>(part_dv + off);
+    }
+    *reinterpret_cast<uint2*>(dk + (int64_t)(seq0 + kp) * dk_st + (int64_t)h * dk_sh + d) = pack_bf16x4(adk * scale);
+    *reinterpret_cast<uint2*>(dv + (int64_t)(seq0 + kp) * dv_st + (int64_t)h * dv_sh + d) = pack_bf16x4(adv);
+  }
+}
+
+void launch_bitmaps(const Sizes& z, const QsaArgs& a, hipStream_t st) {
+  KernelTimer timer("qsa_bitmap", st);
+  qsa_bitmap_kernel<<<dim3((unsigned)((z.T + 3) / 4), (unsigned)z.Hk), 256, 0, st>>>(
+      a.blk_idx, a.topk, a.cu, (int)z.S, (int)z.T, (int)z.Hk, a.bits);
+}
+
+}  // namespace
+
+void launch_qsa_fwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStream_t st) {
+  launch_bitmaps(z, a, st);
+  {
+    KernelTimer timer("qsa_vt", st);
+    qsa_vt_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk), 256, 0, st>>>(
+        a.v, a.v_st, a.v_sh, a.cu, p.blkbase, p.blk_seq, p.totals, (int)z.Hk, a.vt);
+  }
+  KernelTimer timer("qsa_fwd", st);
+  qsa_fwd_kernel<<<(unsigned)(2 * z.ntiles * z.Hk), 64 * kTok, 0, st>>>(
+      a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.vt, a.bits, a.cu, p.blkbase, p.blk_seq, p.tile_order, (int)z.S,
+      (int)z.T, (int)z.Hk, a.scale * kLog2e, a.out_o, a.oo_st, a.oo_sh, a.out_lse);
+}
+
+void launch_qsa_bwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStream_t st) {
+  launch_bitmaps(z, a, st);
+  {
+    KernelTimer timer("qsa_dq", st);
+    qsa_dq_kernel<<<(unsigned)(2 * z.ntiles * z.Hk), 64 * kTok, 0, st>>>(
+        a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.o, a.o_st, a.o_sh, a.dO, a.do_st, a.do_sh,
+        a.lse, a.bits, a.cu, p.blkbase, p.blk_seq, p.tile_order, (int)z.S, (int)z.T, (int)z.Hk, a.scale * kLog2e,
+        a.scale, a.dq, a.dq_st, a.dq_sh, a.delta, a.nlse);
+  }
+  {
+    KernelTimer timer("qsa_dkdv", st);
+    qsa_dkdv_kernel<<<dim3((unsigned)z.items_cap, (unsigned)z.Hk), 256, 0, st>>>(
+        a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.dO, a.do_st, a.do_sh, a.nlse, a.delta,
+        a.bits, a.cu, p.seqitem, p.totals, (int)z.S, (int)z.Hk, (int)z.chunk, (int)z.items_cap, a.scale * kLog2e,
+        a.scale, a.item_count, a.part_dk, a.part_dv, a.dk, a.dk_st, a.dk_sh, a.dv, a.dv_st, a.dv_sh);
+  }
+  {
+    KernelTimer timer("qsa_reduce", st);
+    qsa_reduce_kernel<<<dim3((unsigned)z.nblk_cap, kKT / 16, (unsigned)z.Hk), 256, 0, st>>>(
+        a.part_dk, a.part_dv, a.item_count, p.seqitem, p.blk_seq, p.blkbase, a.cu, p.totals, (int)z.chunk,
+        (int)z.items_cap, a.scale, a.dk, a.dk_st, a.dk_sh, a.dv, a.dv_st, a.dv_sh);
+  }
+}
+
+}  // namespace msa

@@ -67,9 +67,13 @@ extern "C" {
 #define MSA_OP_FWD 2
 #define MSA_OP_BWD 3
 #define MSA_OP_QKNORM_BWD 4
+#define MSA_OP_QSA_FWD 5
+#define MSA_OP_QSA_BWD 6
 
 /* Longest sequence this build accepts (1024 blocks of 128 tokens). */
 #define MSA_MAX_SEQLEN 131072
+/* Longest sequence of the narrow-block entry points (8192 blocks of 4 tokens). */
+#define MSA_QSA_MAX_SEQLEN 32768
 
 typedef struct msa_dims {
   int32_t total_tokens; /* T = cu_seqlens[num_seqs]; 0 makes every call a no-op          */
@@ -234,6 +238,44 @@ int msa_attn_bwd(const msa_dims* dims,
                  void* dk, int64_t dk_st, int64_t dk_sh,
                  void* dv, int64_t dv_st, int64_t dv_sh,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Narrow-block variant of the block-sparse attention ([PR] kernel-tuning
+ * commit message: the block-sparse kernel also runs qwen3.8-next's 4-token
+ * blocks, 12 query heads per KV head, head dim 256).  Same definition as
+ * msa_attn_fwd / msa_attn_bwd with these differences:
+ *   dims: head_dim = 256, block_size = 4, topk_blocks = K in 1..1024 (the
+ *         number of block ids listed per query), num_q_heads = 12 * num_kv_heads,
+ *         max_seqlen <= MSA_QSA_MAX_SEQLEN; query head g reads KV head g / 12;
+ *   blk_idx [T, Hk, K] int32 contiguous, sequence-local 4-token block ids in
+ *         any order; ids below 0 and past the query's own block are ignored,
+ *         a repeated id counts once; the own block is attended only if listed
+ *         (the pages do not say how these blocks are chosen);
+ *   q, o, do_, dq [T, Hq, 256] and k, v, dk, dv [T, Hk, 256] bf16 with their
+ *         own strides (dim contiguous); lse [T, Hq] fp32.
+ * Workspaces: msa_workspace_size(dims, MSA_OP_QSA_FWD / MSA_OP_QSA_BWD, ...).
+ * Errors, ownership, determinism and stream semantics as for msa_attn_*.
+ */
+int msa_qsa_attn_fwd(const msa_dims* dims,
+                     const void* q, int64_t q_st, int64_t q_sh,
+                     const void* k, int64_t k_st, int64_t k_sh,
+                     const void* v, int64_t v_st, int64_t v_sh,
+                     const int32_t* blk_idx, const int32_t* cu_seqlens, float softmax_scale,
+                     void* o, int64_t o_st, int64_t o_sh, float* lse,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+int msa_qsa_attn_bwd(const msa_dims* dims,
+                     const void* q, int64_t q_st, int64_t q_sh,
+                     const void* k, int64_t k_st, int64_t k_sh,
+                     const void* v, int64_t v_st, int64_t v_sh,
+                     const void* o, int64_t o_st, int64_t o_sh,
+                     const float* lse,
+                     const void* do_, int64_t do_st, int64_t do_sh,
+                     const int32_t* blk_idx, const int32_t* cu_seqlens, float softmax_scale,
+                     void* dq, int64_t dq_st, int64_t dq_sh,
+                     void* dk, int64_t dk_st, int64_t dk_sh,
+                     void* dv, int64_t dv_st, int64_t dv_sh,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable text for a status code. */
 const char* msa_status_string(int status);
