@@ -43,17 +43,17 @@ D = 128
 FLOP_PER_KEY = {"attn_fwd": 4 * D, "attn_bwd_dq": 6 * D, "attn_bwd_dkdv": 8 * D}
 
 
-def selected_keys(blk: np.ndarray, cu: np.ndarray) -> int:
-    """Sum over (token, kv head) of the causal keys in the listed blocks."""
+def selected_keys(blk: np.ndarray, cu: np.ndarray, block: int = 128) -> int:
+    """Sum over (token, kv head) of the causal keys in the listed blocks (ids distinct per row)."""
     T = blk.shape[0]
     pos = np.empty(T, np.int64)
     for s in range(len(cu) - 1):
         pos[cu[s]:cu[s + 1]] = np.arange(cu[s + 1] - cu[s])
-    b = pos // 128
+    b = pos // block
     valid = (blk >= 0) & (blk <= b[:, None, None])
     full = (blk < b[:, None, None]) & valid
     own = (blk == b[:, None, None])
-    n = full.sum(axis=2) * 128 + own.sum(axis=2) * (pos % 128 + 1)[:, None]
+    n = full.sum(axis=2) * block + own.sum(axis=2) * (pos % block + 1)[:, None]
     return int(n.sum())
 
 
@@ -140,12 +140,76 @@ def cpu_baseline(p, stride: int):
             "host_cpus": os.cpu_count()}
 
 
+def qsa_leg(msa, seed: int, steps: int, warmup: int) -> dict:
+    """Narrow-block variant (msa_qsa_attn_*) on the qsa16k pack: 12 q / 1 kv heads, D 256,
+    4-token blocks, 512 seeded block ids per query (synth.random_block_lists)."""
+    p = synth.make_pack("qsa16k", seed)
+    dev = torch.device("cuda:0")
+    g = lambda t: t.to(dev)
+    cu_np = p.cu_seqlens.numpy()
+    blk_np = synth.random_block_lists(cu_np, p.num_kv_heads, 4, p.topk_blocks, seed)
+    cu, q, k, v, do = g(p.cu_seqlens), g(p.q), g(p.k), g(p.v), g(p.do)
+    blk = g(torch.from_numpy(blk_np))
+    T, Hq, Hk, Dn = p.total, p.num_q_heads, p.num_kv_heads, p.head_dim
+    dims = msa.make_dims(T, len(p.lengths), p.max_seqlen, Hq, Hk, head_dim=Dn, block_size=4,
+                         topk_blocks=p.topk_blocks)
+    ws = {op: torch.empty(max(msa.msa_workspace_size(dims, op), 1), dtype=torch.uint8, device=dev)
+          for op in (msa.MSA_OP_QSA_FWD, msa.MSA_OP_QSA_BWD)}
+    o, lse = torch.empty_like(q), torch.empty(T, Hq, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        msa.msa_qsa_attn_fwd(q, k, v, blk, cu, p.max_seqlen, out=o, lse=lse, workspace=ws[msa.MSA_OP_QSA_FWD])
+        if ev is not None:
+            ev[1].record()
+        msa.msa_qsa_attn_bwd(q, k, v, o, lse, do, blk, cu, p.max_seqlen, dq=dq, dk=dk, dv=dv,
+                             workspace=ws[msa.MSA_OP_QSA_BWD])
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    msa.msa_timing_collect()
+    msa.msa_timing_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kt = msa.msa_timing_collect()
+    msa.msa_timing_enable(False)
+    per_qhead = selected_keys(blk_np, cu_np, 4) * (Hq // Hk)
+    fb_flop = 14 * Dn * per_qhead
+    fb_ms = fwd_ms + bwd_ms
+    tflops = fb_flop / (fb_ms * 1e-3) / 1e12
+    return {
+        "workload": f"qsa16k: {T}-token THD pack, seed {seed}, lengths {p.lengths}, {Hq} q / {Hk} kv heads, "
+                    f"D {Dn}, 4-token blocks, {p.topk_blocks} listed per query (seeded)",
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "fwd_bwd_ms": round(fb_ms, 4),
+        "fwd_bwd_counted_gflop": round(fb_flop / 1e9, 1),
+        "fwd_bwd_tflops": round(tflops, 2),
+        "fwd_bwd_mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "kernels_avg_ms": {name: round(ms / n, 4) for name, (n, ms) in kt.items()},
+        "context_gb300_ms": {"fwd_bwd": 16.4, "note": "pages' GB300 figure for qwen3.8-next on unpublished 16k packs"},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="pack16k", choices=sorted(synth.CONFIGS))
+    ap.add_argument("--config", default="pack16k", choices=sorted(c for c in synth.CONFIGS if c != "qsa16k"))
+    ap.add_argument("--no-qsa", action="store_true", help="skip the narrow-block (qsa16k) leg")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-stride", type=int, default=3, help="oracle fwd+bwd sample: every n-th token")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -339,6 +403,8 @@ def main():
         "roofline": roofline,
         "context_gb300_ms": {"fwd_bwd": 6.7, "select": 0.62, "note": "pages' GB300 figures on unpublished 16k packs"},
     }
+    if not args.no_qsa:
+        line["qsa16k"] = qsa_leg(msa, args.seed, args.steps, args.warmup)
     if args.calibrate_copy > 0:
         # a plain streaming kernel of known traffic (read n, write n bytes); a
         # tensor copy would go to the DMA engines and leave no kernel to count
