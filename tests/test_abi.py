@@ -156,3 +156,61 @@ def test_select_and_bwd_argument_errors_launch_nothing():
     assert bwd(dv_sh=0) == msa.MSA_ERR_INVALID_ARG
     assert bwd(lse=None) == msa.MSA_ERR_INVALID_ARG
     assert bwd(n=msa.msa_workspace_size(d, msa.MSA_OP_BWD) - 256) == msa.MSA_ERR_WORKSPACE
+
+
+def qsa_dims(**kw):
+    base = dict(total_tokens=16384, num_seqs=3, max_seqlen=7122, num_q_heads=12, num_kv_heads=1, head_dim=256,
+                block_size=4, topk_blocks=512)
+    base.update(kw)
+    return msa.make_dims(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), msa.MSA_OK),
+    (dict(head_dim=128), msa.MSA_ERR_UNSUPPORTED),
+    (dict(block_size=128), msa.MSA_ERR_UNSUPPORTED),
+    (dict(topk_blocks=1025), msa.MSA_ERR_UNSUPPORTED),
+    (dict(topk_blocks=0), msa.MSA_ERR_INVALID_ARG),
+    (dict(num_q_heads=16), msa.MSA_ERR_UNSUPPORTED),
+    (dict(max_seqlen=40000, total_tokens=50000), msa.MSA_ERR_UNSUPPORTED),
+    (dict(num_seqs=0), msa.MSA_ERR_INVALID_ARG),
+])
+def test_qsa_workspace_dims(kw, status):
+    """The narrow-block entry points validate their own dims (D 256, block 4, 12 q / kv, K <= 1024)."""
+    n = ctypes.c_size_t(0)
+    d = qsa_dims(**kw)
+    for op in (msa.MSA_OP_QSA_FWD, msa.MSA_OP_QSA_BWD):
+        assert msa.load().msa_workspace_size(ctypes.byref(d), op, ctypes.byref(n)) == status
+        if status == msa.MSA_OK:
+            assert n.value > 0 and n.value % 256 == 0
+    # the wide dims are not narrow dims and vice versa
+    assert msa.load().msa_workspace_size(ctypes.byref(dims()), msa.MSA_OP_QSA_FWD, ctypes.byref(n)) == \
+        msa.MSA_ERR_UNSUPPORTED
+    assert msa.load().msa_workspace_size(ctypes.byref(qsa_dims()), msa.MSA_OP_FWD, ctypes.byref(n)) == \
+        msa.MSA_ERR_UNSUPPORTED
+
+
+@no_gpu
+def test_qsa_argument_errors_launch_nothing():
+    lib = msa.load()
+    d = qsa_dims()
+
+    def fwd(q=FAKE, o_sh=256, blk=FAKE, scale=0.0625, ws=FAKE, n=1 << 40, dd=d):
+        return lib.msa_qsa_attn_fwd(ctypes.byref(dd), q, 3072, 256, FAKE, 256, 256, FAKE, 256, 256, blk, FAKE, scale,
+                                    FAKE, 3072, o_sh, FAKE, ws, n, None)
+    assert fwd(q=None) == msa.MSA_ERR_INVALID_ARG
+    assert fwd(o_sh=0) == msa.MSA_ERR_INVALID_ARG
+    assert fwd(blk=None) == msa.MSA_ERR_INVALID_ARG
+    assert fwd(scale=-1.0) == msa.MSA_ERR_INVALID_ARG
+    assert fwd(ws=None) == msa.MSA_ERR_WORKSPACE
+    assert fwd(n=msa.msa_workspace_size(d, msa.MSA_OP_QSA_FWD) - 256) == msa.MSA_ERR_WORKSPACE
+    assert fwd(dd=dims()) == msa.MSA_ERR_UNSUPPORTED
+    assert fwd(dd=qsa_dims(total_tokens=0, num_seqs=0, max_seqlen=0), q=None, ws=None) == msa.MSA_OK
+
+    def bwd(dv_sh=256, lse=FAKE, n=1 << 40):
+        return lib.msa_qsa_attn_bwd(ctypes.byref(d), FAKE, 3072, 256, FAKE, 256, 256, FAKE, 256, 256, FAKE, 3072,
+                                    256, lse, FAKE, 3072, 256, FAKE, FAKE, 0.0625, FAKE, 3072, 256, FAKE, 256, 256,
+                                    FAKE, 256, dv_sh, FAKE, n, None)
+    assert bwd(dv_sh=0) == msa.MSA_ERR_INVALID_ARG
+    assert bwd(lse=None) == msa.MSA_ERR_INVALID_ARG
+    assert bwd(n=msa.msa_workspace_size(d, msa.MSA_OP_QSA_BWD) - 256) == msa.MSA_ERR_WORKSPACE
