@@ -32,6 +32,7 @@ MSA_ERR_UNSUPPORTED = -2
 MSA_ERR_WORKSPACE = -3
 MSA_ERR_HIP = -4
 MSA_SELECT_FORCE_INIT = 1
+MSA_ATTN_DENSE = 1
 MSA_OP_QKNORM_BWD = 4
 MSA_OP_SELECT = 1
 MSA_OP_FWD = 2
@@ -41,6 +42,7 @@ MSA_OP_QSA_BWD = 6
 
 # Every symbol include/msa.h declares.
 EXPORTED = ("msa_workspace_size", "msa_index_select", "msa_index_select_ex", "msa_attn_fwd", "msa_attn_bwd",
+            "msa_attn_fwd_ex", "msa_attn_bwd_ex",
             "msa_qk_norm_rope_fwd", "msa_qk_norm_rope_bwd", "msa_qsa_attn_fwd", "msa_qsa_attn_bwd",
             "msa_status_string", "msa_check_cu_seqlens", "msa_timing_enable", "msa_timing_collect",
             "msa_version")
@@ -98,6 +100,14 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                  _P, _P, _I64, _I64, _P, _P, _F,
                                  _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _SZ, _P]
     lib.msa_attn_bwd.restype = _I32
+    lib.msa_attn_fwd_ex.argtypes = [ctypes.POINTER(MsaDims), _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64,
+                                    _P, _P, _F, ctypes.c_uint32, _P, _I64, _I64, _P, _P, _SZ, _P]
+    lib.msa_attn_fwd_ex.restype = _I32
+    lib.msa_attn_bwd_ex.argtypes = [ctypes.POINTER(MsaDims),
+                                    _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64,
+                                    _P, _P, _I64, _I64, _P, _P, _F, ctypes.c_uint32,
+                                    _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _SZ, _P]
+    lib.msa_attn_bwd_ex.restype = _I32
     lib.msa_qsa_attn_fwd.argtypes = lib.msa_attn_fwd.argtypes
     lib.msa_qsa_attn_fwd.restype = _I32
     lib.msa_qsa_attn_bwd.argtypes = lib.msa_attn_bwd.argtypes
@@ -204,11 +214,12 @@ def msa_index_select(idx_q: torch.Tensor, idx_k: torch.Tensor, w_q: torch.Tensor
     return out
 
 
-def msa_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, blk_idx: torch.Tensor,
+def msa_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, blk_idx: Optional[torch.Tensor],
                  cu_seqlens: torch.Tensor, max_seqlen: int, softmax_scale: Optional[float] = None, *,
                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Block-sparse GQA attention forward: returns O [T, Hq, 128] bf16 and LSE [T, Hq] fp32."""
+                 workspace: Optional[torch.Tensor] = None, dense: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Block-sparse GQA attention forward: returns O [T, Hq, 128] bf16 and LSE [T, Hq] fp32.
+    ``dense`` attends to every causal key instead (msa_attn_fwd_ex, MSA_ATTN_DENSE; blk_idx unused)."""
     lib = load()
     T, Hq, D = q.shape
     Hk = k.shape[1]
@@ -221,19 +232,26 @@ def msa_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, blk_idx: tor
     so = _bf16_view(out, "out")
     dims = _dims_for(cu_seqlens, max_seqlen, Hq, Hk, T)
     ws, nbytes = _workspace(dims, MSA_OP_FWD, q.device, workspace)
-    st = lib.msa_attn_fwd(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0], sv[1],
-                          _ptr(blk_idx), _ptr(cu_seqlens), scale, _ptr(out), so[0], so[1], _ptr(lse),
-                          _ptr(ws), nbytes, _stream(q))
-    _check(st, "msa_attn_fwd")
+    if dense:
+        st = lib.msa_attn_fwd_ex(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0],
+                                 sv[1], None, _ptr(cu_seqlens), scale, MSA_ATTN_DENSE, _ptr(out), so[0], so[1],
+                                 _ptr(lse), _ptr(ws), nbytes, _stream(q))
+        _check(st, "msa_attn_fwd_ex")
+    else:
+        st = lib.msa_attn_fwd(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0],
+                              sv[1], _ptr(blk_idx), _ptr(cu_seqlens), scale, _ptr(out), so[0], so[1], _ptr(lse),
+                              _ptr(ws), nbytes, _stream(q))
+        _check(st, "msa_attn_fwd")
     return out, lse
 
 
 def msa_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
-                 do: torch.Tensor, blk_idx: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+                 do: torch.Tensor, blk_idx: Optional[torch.Tensor], cu_seqlens: torch.Tensor, max_seqlen: int,
                  softmax_scale: Optional[float] = None, *, dq: Optional[torch.Tensor] = None,
                  dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Backward of msa_attn_fwd: returns dQ, dK, dV (bf16, shaped like q, k, v)."""
+                 workspace: Optional[torch.Tensor] = None,
+                 dense: bool = False) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Backward of msa_attn_fwd: returns dQ, dK, dV (bf16, shaped like q, k, v); ``dense`` as in the forward."""
     lib = load()
     T, Hq, D = q.shape
     Hk = k.shape[1]
@@ -249,11 +267,18 @@ def msa_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Ten
     dims = _dims_for(cu_seqlens, max_seqlen, Hq, Hk, T)
     ws, nbytes = _workspace(dims, MSA_OP_BWD, q.device, workspace)
     (sq, sk, sv, so, sdo, sdq, sdk, sdv) = views
-    st = lib.msa_attn_bwd(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0], sv[1],
-                          _ptr(o), so[0], so[1], _ptr(lse), _ptr(do), sdo[0], sdo[1], _ptr(blk_idx),
-                          _ptr(cu_seqlens), scale, _ptr(dq), sdq[0], sdq[1], _ptr(dk), sdk[0], sdk[1],
-                          _ptr(dv), sdv[0], sdv[1], _ptr(ws), nbytes, _stream(q))
-    _check(st, "msa_attn_bwd")
+    if dense:
+        st = lib.msa_attn_bwd_ex(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0],
+                                 sv[1], _ptr(o), so[0], so[1], _ptr(lse), _ptr(do), sdo[0], sdo[1], None,
+                                 _ptr(cu_seqlens), scale, MSA_ATTN_DENSE, _ptr(dq), sdq[0], sdq[1], _ptr(dk), sdk[0],
+                                 sdk[1], _ptr(dv), sdv[0], sdv[1], _ptr(ws), nbytes, _stream(q))
+        _check(st, "msa_attn_bwd_ex")
+    else:
+        st = lib.msa_attn_bwd(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0],
+                              sv[1], _ptr(o), so[0], so[1], _ptr(lse), _ptr(do), sdo[0], sdo[1], _ptr(blk_idx),
+                              _ptr(cu_seqlens), scale, _ptr(dq), sdq[0], sdq[1], _ptr(dk), sdk[0], sdk[1],
+                              _ptr(dv), sdv[0], sdv[1], _ptr(ws), nbytes, _stream(q))
+        _check(st, "msa_attn_bwd")
     return dq, dk, dv
 
 

@@ -43,6 +43,8 @@ constexpr int kDqWaves = kTileTok / kTokPerWave;
 constexpr int kUnionWords = 34;
 constexpr int kMaxUnion = kTileTok * kTopk;
 
+// kDense: every causal key of the token's sequence (the dense layers), blk_idx unused.
+template <bool kDense>
 __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
     const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
@@ -57,8 +59,10 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
   __shared__ u32x4 kbuf[2][32][64];
   __shared__ u32x4 vbuf[2][32][64];
   __shared__ uint32_t bitmap[kUnionWords];
-  __shared__ int ulist[kMaxUnion];
-  __shared__ int ukey0[kMaxUnion];  // first token of each union block
+  // a dense tile's union is up to one sequence's 1024 blocks plus one per later sequence
+  constexpr int kUnionCap = kDense ? kUnionWords * 32 : kMaxUnion;
+  __shared__ int ulist[kUnionCap];
+  __shared__ int ukey0[kUnionCap];  // first token of each union block
   __shared__ int nunion;
 
   // workgroup b runs KV head b % Hk of the tile in launch slot b / Hk
@@ -80,15 +84,24 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     s_t = find_seq(cu, S, t);
     pos_t = t - cu[s_t];
     b_t = pos_t / kBlock;
-    const int c = blk_idx[((int64_t)t * Hk + h) * kTopk + li];
-    if (c >= 0 && c <= b_t) my_gb = blkbase[s_t] + c;
+    if constexpr (!kDense) {
+      const int c = blk_idx[((int64_t)t * Hk + h) * kTopk + li];
+      if (c >= 0 && c <= b_t) my_gb = blkbase[s_t] + c;
+    }
   }
   const int gb_lo = blkbase[find_seq(cu, S, t0)];
 
   if (threadIdx.x < kUnionWords) bitmap[threadIdx.x] = 0u;
   __syncthreads();
-  if (g < kTokPerWave && my_gb >= 0 && my_gb - gb_lo < kUnionWords * 32)
+  if constexpr (kDense) {
+    if (g < kTokPerWave && tvalid)
+      for (int c = li; c <= b_t; c += 16) {
+        const int rel = blkbase[s_t] + c - gb_lo;
+        atomicOr(&bitmap[rel >> 5], 1u << (rel & 31));
+      }
+  } else if (g < kTokPerWave && my_gb >= 0 && my_gb - gb_lo < kUnionWords * 32) {
     atomicOr(&bitmap[(my_gb - gb_lo) >> 5], 1u << ((my_gb - gb_lo) & 31));
+  }
   __syncthreads();
   if (wave == 0) {
     uint32_t bits = lane < kUnionWords ? bitmap[lane] : 0u;
@@ -192,10 +205,11 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     const int buf = u & 1;
     if (u + 1 < nsteps) stage(u + 1, buf ^ 1);
     const int gb = ulist[u];
-    const uint64_t hits = __ballot(my_gb == gb);
+    const uint64_t hits = kDense ? 0ull : __ballot(my_gb == gb);
 #pragma unroll
     for (int j = 0; j < kTokPerWave; ++j) {
-      if (((hits >> (16 * j)) & 0xFFFFull) == 0) continue;
+      if (kDense ? (gb < tok_base[j] || gb - tok_base[j] > tok_b[j]) : (((hits >> (16 * j)) & 0xFFFFull) == 0))
+        continue;
       const int c = gb - tok_base[j];
       const bool diag = (c == tok_b[j]);
       const int key0 = kBlock * c;
@@ -342,7 +356,8 @@ void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStr
   const int T = (int)z.T, Hk = (int)z.Hk, S = (int)z.S;
   {
     KernelTimer timer("attn_bwd_dq", st);
-    attn_bwd_dq_kernel<<<(unsigned)(z.ntiles * Hk), 64 * kDqWaves, 0, st>>>(
+    auto kern = a.dense ? attn_bwd_dq_kernel<true> : attn_bwd_dq_kernel<false>;
+    kern<<<(unsigned)(z.ntiles * Hk), 64 * kDqWaves, 0, st>>>(
         a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.o, a.o_st, a.o_sh, a.dO, a.do_st,
         a.do_sh, a.lse, a.blk_idx, a.cu, p.blkbase, p.blk_seq, p.tile_order, S, T, Hk, a.scale * kLog2e, a.scale,
         a.dq, a.dq_st,

@@ -65,6 +65,8 @@ __device__ __forceinline__ void stage_token(int t, int h, int Hk, int lane, uint
     dma4s(delta + row - 16, 4 * lane, stats_lds);
 }
 
+// kDense: every token of the chunk at or after the block's first key selects it (blk_idx unused).
+template <bool kDense>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
     const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
@@ -113,7 +115,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int p0 = p_begin; p0 < p_end; p0 += 256) {
     const int p = p0 + threadIdx.x;
     bool hit = false;
-    if (p < p_end) {
+    if (kDense) {
+      hit = p < p_end;
+    } else if (p < p_end) {
       const int4* ids = reinterpret_cast<const int4*>(blk_idx + ((int64_t)(seq0 + p) * Hk + h) * kTopk);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -365,6 +369,28 @@ __global__ __launch_bounds__(256) void dkdv_load_count_kernel(
       if (hist[i] != 0) atomicAdd(&gl[lo + i], hist[i]);
 }
 
+// Dense layers: item (s, j, c) is selected by every query of chunk j at or
+// after block c's first key.
+__global__ __launch_bounds__(256) void dkdv_dense_load_kernel(const int32_t* __restrict__ cu,
+                                                              const int32_t* __restrict__ seqitem,
+                                                              const int32_t* __restrict__ totals, int S, int chunk,
+                                                              int items_cap, int32_t* __restrict__ load) {
+  const int item = blockIdx.x * 256 + threadIdx.x;
+  const int h = blockIdx.y;
+  if (item >= totals[1]) return;
+  const int s = upper_index(seqitem, S, item);
+  const int L = cu[s + 1] - cu[s];
+  int r = item - seqitem[s];
+  int j = 0;
+  for (;;) {
+    const int cnt = (min((j + 1) * chunk, L) - 1) / kBlock + 1;
+    if (r < cnt) break;
+    r -= cnt;
+    ++j;
+  }
+  load[(int64_t)h * items_cap + item] = max(0, min((j + 1) * chunk, L) - max(j * chunk, kBlock * r));
+}
+
 // per KV head: counting sort of the items by decreasing load
 constexpr int kLoadBins = kDkdvChunkMax + 1;
 __global__ __launch_bounds__(1024) void dkdv_order_kernel(const int32_t* __restrict__ load,
@@ -415,13 +441,17 @@ __global__ __launch_bounds__(1024) void dkdv_order_kernel(const int32_t* __restr
 void launch_attn_bwd_dkdv(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStream_t st) {
   {
     KernelTimer timer("dkdv_order", st);
-    if (z.T > 0)
+    if (a.dense)
+      dkdv_dense_load_kernel<<<dim3((unsigned)((z.items_cap + 255) / 256), (unsigned)z.Hk), 256, 0, st>>>(
+          a.cu, p.seqitem, p.totals, (int)z.S, (int)z.chunk, (int)z.items_cap, a.item_load);
+    else if (z.T > 0)
       dkdv_load_count_kernel<<<dim3((unsigned)((z.T + 255) / 256), (unsigned)z.Hk), 256, 0, st>>>(
           a.blk_idx, a.cu, p.seqitem, (int)z.S, (int)z.T, (int)z.Hk, (int)z.chunk, (int)z.items_cap, a.item_load);
     dkdv_order_kernel<<<(unsigned)z.Hk, 1024, 0, st>>>(a.item_load, p.totals, (int)z.items_cap, a.item_order);
   }
   KernelTimer timer("attn_bwd_dkdv", st);
-  attn_bwd_dkdv_kernel<<<dim3((unsigned)z.items_cap, (unsigned)z.Hk), 256, 0, st>>>(
+  auto kern = a.dense ? attn_bwd_dkdv_kernel<true> : attn_bwd_dkdv_kernel<false>;
+  kern<<<dim3((unsigned)z.items_cap, (unsigned)z.Hk), 256, 0, st>>>(
       a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.dO, a.do_st, a.do_sh, a.nlse,
       a.delta, a.blk_idx, a.cu, p.blkbase, p.blk_seq, p.seqitem, p.totals, (int)z.S, (int)z.Hk, (int)z.chunk,
       (int)z.items_cap, a.item_order, a.scale * kLog2e, a.scale, a.item_count, a.part_dk, a.part_dv, a.dk, a.dk_st, a.dk_sh, a.dv,

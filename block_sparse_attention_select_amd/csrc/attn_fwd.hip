@@ -87,6 +87,8 @@ constexpr float kRescaleSlack = 8.f;  // log2 units
 constexpr int kUnionWords = 34;  // a tile's blocks span fewer than 34 * 32 global ids
 constexpr int kMaxUnion = kTileTok * kTopk;
 
+// kDense: every causal key of the token's sequence (the dense layers), blk_idx unused.
+template <bool kDense>
 __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
     const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
@@ -97,8 +99,10 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
   __shared__ u32x4 kbuf[2][32][64];
   __shared__ u32x4 vbuf[2][32][64];
   __shared__ uint32_t bitmap[kUnionWords];
-  __shared__ int ulist[kMaxUnion];
-  __shared__ int ukey0[kMaxUnion];  // first token of each union block
+  // a dense tile's union is up to one sequence's 1024 blocks plus one per later sequence
+  constexpr int kUnionCap = kDense ? kUnionWords * 32 : kMaxUnion;
+  __shared__ int ulist[kUnionCap];
+  __shared__ int ukey0[kUnionCap];  // first token of each union block
   __shared__ int nunion;
 
   // workgroup b runs KV head b % Hk of the tile in launch slot b / Hk
@@ -118,16 +122,25 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
     s_t = find_seq(cu, S, t);
     pos_t = t - cu[s_t];
     b_t = pos_t / kBlock;
-    const int c = blk_idx[((int64_t)t * Hk + h) * kTopk + li];
-    if (c >= 0 && c <= b_t) my_gb = blkbase[s_t] + c;
+    if constexpr (!kDense) {
+      const int c = blk_idx[((int64_t)t * Hk + h) * kTopk + li];
+      if (c >= 0 && c <= b_t) my_gb = blkbase[s_t] + c;
+    }
   }
   const int gb_lo = blkbase[find_seq(cu, S, t0)];
 
   // 1. union of the tile's blocks
   if (threadIdx.x < kUnionWords) bitmap[threadIdx.x] = 0u;
   __syncthreads();
-  if (g < kTokPerWave && my_gb >= 0 && my_gb - gb_lo < kUnionWords * 32)
+  if constexpr (kDense) {
+    if (g < kTokPerWave && tvalid)
+      for (int c = li; c <= b_t; c += 16) {
+        const int rel = blkbase[s_t] + c - gb_lo;
+        atomicOr(&bitmap[rel >> 5], 1u << (rel & 31));
+      }
+  } else if (g < kTokPerWave && my_gb >= 0 && my_gb - gb_lo < kUnionWords * 32) {
     atomicOr(&bitmap[(my_gb - gb_lo) >> 5], 1u << ((my_gb - gb_lo) & 31));
+  }
   __syncthreads();
   if (wave == 0) {
     uint32_t bits = lane < kUnionWords ? bitmap[lane] : 0u;
@@ -210,10 +223,11 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
     const int buf = u & 1;
     if (u + 1 < nu) stage(u + 1, buf ^ 1);
     const int gb = ulist[u];
-    const uint64_t hits = __ballot(my_gb == gb);
+    const uint64_t hits = kDense ? 0ull : __ballot(my_gb == gb);
 #pragma unroll
     for (int j = 0; j < kTokPerWave; ++j) {
-      if (((hits >> (16 * j)) & 0xFFFFull) == 0) continue;
+      if (kDense ? (gb < tok_base[j] || gb - tok_base[j] > tok_b[j]) : (((hits >> (16 * j)) & 0xFFFFull) == 0))
+        continue;
       const int c = gb - tok_base[j];
       const bool diag = (c == tok_b[j]);
       // Two halves of 64 keys, each a full online-softmax update.  Base 2 on
@@ -337,9 +351,10 @@ void launch_block_transpose(const Sizes& z, const u16* x, int64_t st_t, int64_t 
 void launch_attn_fwd(const Sizes& z, const u16* q, int64_t q_st, int64_t q_sh,
                      const u16* k, int64_t k_st, int64_t k_sh, const u16* vt,
                      const int32_t* blk_idx, const int32_t* cu, const PlanBufs& p, float scale,
-                     u16* o, int64_t o_st, int64_t o_sh, float* lse, hipStream_t st) {
+                     u16* o, int64_t o_st, int64_t o_sh, float* lse, bool dense, hipStream_t st) {
   KernelTimer timer("attn_fwd", st);
-  attn_fwd_kernel<<<(unsigned)(z.ntiles * z.Hk), 64 * kFwdWaves, 0, st>>>(
+  auto kern = dense ? attn_fwd_kernel<true> : attn_fwd_kernel<false>;
+  kern<<<(unsigned)(z.ntiles * z.Hk), 64 * kFwdWaves, 0, st>>>(
       q, q_st, q_sh, k, k_st, k_sh, vt, blk_idx, cu, p.blkbase, p.blk_seq, p.tile_order, (int)z.S, (int)z.T,
       (int)z.Hk, scale * kLog2e, o, o_st, o_sh, lse);
 }

@@ -328,13 +328,24 @@ int msa_attn_fwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh
                  int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh, const int32_t* blk_idx,
                  const int32_t* cu_seqlens, float softmax_scale, void* o, int64_t o_st, int64_t o_sh, float* lse,
                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return msa_attn_fwd_ex(dims, q, q_st, q_sh, k, k_st, k_sh, v, v_st, v_sh, blk_idx, cu_seqlens, softmax_scale, 0u,
+                         o, o_st, o_sh, lse, workspace, workspace_bytes, stream);
+}
+
+int msa_attn_fwd_ex(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh, const void* k, int64_t k_st,
+                    int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh, const int32_t* blk_idx,
+                    const int32_t* cu_seqlens, float softmax_scale, uint32_t flags, void* o, int64_t o_st,
+                    int64_t o_sh, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = check_dims(dims);
   if (st != MSA_OK) return st;
+  if (flags & ~MSA_ATTN_DENSE) return MSA_ERR_INVALID_ARG;
+  const bool dense = (flags & MSA_ATTN_DENSE) != 0;
   if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return MSA_ERR_INVALID_ARG;
   if (dims->total_tokens == 0) return MSA_OK;
   if (!in_view(q, q_st, q_sh) || !in_view(k, k_st, k_sh) || !in_view(v, v_st, v_sh) || !out_view(o, o_st, o_sh))
     return MSA_ERR_INVALID_ARG;
-  if (!blk_idx || !aligned(blk_idx, 16) || !cu_seqlens || !aligned(cu_seqlens, 4) || !lse || !aligned(lse, 16))
+  if ((!dense && (!blk_idx || !aligned(blk_idx, 16))) || !cu_seqlens || !aligned(cu_seqlens, 4) || !lse ||
+      !aligned(lse, 16))
     return MSA_ERR_INVALID_ARG;
   const Sizes z = sizes_of(dims);
   st = check_ws(workspace, workspace_bytes, ws_bytes_for(z, MSA_OP_FWD));
@@ -343,8 +354,8 @@ int msa_attn_fwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh
   FwdWs w = carve_fwd(c, z);
   msa::launch_plan(cu_seqlens, z, w.plan, stream);
   msa::launch_block_transpose(z, (const u16*)v, v_st, v_sh, cu_seqlens, w.plan, w.vt, stream);
-  msa::launch_attn_fwd(z, (const u16*)q, q_st, q_sh, (const u16*)k, k_st, k_sh, w.vt, blk_idx, cu_seqlens, w.plan,
-                       softmax_scale, (u16*)o, o_st, o_sh, lse, stream);
+  msa::launch_attn_fwd(z, (const u16*)q, q_st, q_sh, (const u16*)k, k_st, k_sh, w.vt, dense ? nullptr : blk_idx,
+                       cu_seqlens, w.plan, softmax_scale, (u16*)o, o_st, o_sh, lse, dense, stream);
   return launch_status();
 }
 
@@ -354,15 +365,29 @@ int msa_attn_bwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh
                  const int32_t* cu_seqlens, float softmax_scale, void* dq, int64_t dq_st, int64_t dq_sh, void* dk,
                  int64_t dk_st, int64_t dk_sh, void* dv, int64_t dv_st, int64_t dv_sh, void* workspace,
                  size_t workspace_bytes, hipStream_t stream) {
+  return msa_attn_bwd_ex(dims, q, q_st, q_sh, k, k_st, k_sh, v, v_st, v_sh, o, o_st, o_sh, lse, do_, do_st, do_sh,
+                         blk_idx, cu_seqlens, softmax_scale, 0u, dq, dq_st, dq_sh, dk, dk_st, dk_sh, dv, dv_st, dv_sh,
+                         workspace, workspace_bytes, stream);
+}
+
+int msa_attn_bwd_ex(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh, const void* k, int64_t k_st,
+                    int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh, const void* o, int64_t o_st,
+                    int64_t o_sh, const float* lse, const void* do_, int64_t do_st, int64_t do_sh,
+                    const int32_t* blk_idx, const int32_t* cu_seqlens, float softmax_scale, uint32_t flags, void* dq,
+                    int64_t dq_st, int64_t dq_sh, void* dk, int64_t dk_st, int64_t dk_sh, void* dv, int64_t dv_st,
+                    int64_t dv_sh, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = check_dims(dims);
   if (st != MSA_OK) return st;
+  if (flags & ~MSA_ATTN_DENSE) return MSA_ERR_INVALID_ARG;
+  const bool dense = (flags & MSA_ATTN_DENSE) != 0;
   if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return MSA_ERR_INVALID_ARG;
   if (dims->total_tokens == 0) return MSA_OK;
   if (!in_view(q, q_st, q_sh) || !in_view(k, k_st, k_sh) || !in_view(v, v_st, v_sh) || !in_view(o, o_st, o_sh) ||
       !in_view(do_, do_st, do_sh) || !out_view(dq, dq_st, dq_sh) || !out_view(dk, dk_st, dk_sh) ||
       !out_view(dv, dv_st, dv_sh))
     return MSA_ERR_INVALID_ARG;
-  if (!blk_idx || !aligned(blk_idx, 16) || !cu_seqlens || !aligned(cu_seqlens, 4) || !lse || !aligned(lse, 16))
+  if ((!dense && (!blk_idx || !aligned(blk_idx, 16))) || !cu_seqlens || !aligned(cu_seqlens, 4) || !lse ||
+      !aligned(lse, 16))
     return MSA_ERR_INVALID_ARG;
   const Sizes z = sizes_of(dims);
   st = check_ws(workspace, workspace_bytes, ws_bytes_for(z, MSA_OP_BWD));
@@ -376,9 +401,10 @@ int msa_attn_bwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh
   a.o = (const u16*)o; a.o_st = o_st; a.o_sh = o_sh;
   a.lse = lse;
   a.dO = (const u16*)do_; a.do_st = do_st; a.do_sh = do_sh;
-  a.blk_idx = blk_idx;
+  a.blk_idx = dense ? nullptr : blk_idx;
   a.cu = cu_seqlens;
   a.scale = softmax_scale;
+  a.dense = dense;
   a.dq = (u16*)dq; a.dq_st = dq_st; a.dq_sh = dq_sh;
   a.dk = (u16*)dk; a.dk_st = dk_st; a.dk_sh = dk_sh;
   a.dv = (u16*)dv; a.dv_st = dv_st; a.dv_sh = dv_sh;

@@ -187,7 +187,7 @@ void launch_block_transpose(const Sizes& z, const u16* x, int64_t st_t, int64_t 
 void launch_attn_fwd(const Sizes& z, const u16* q, int64_t q_st, int64_t q_sh,
                      const u16* k, int64_t k_st, int64_t k_sh, const u16* vt,
                      const int32_t* blk_idx, const int32_t* cu, const PlanBufs& p, float scale,
-                     u16* o, int64_t o_st, int64_t o_sh, float* lse, hipStream_t st);
+                     u16* o, int64_t o_st, int64_t o_sh, float* lse, bool dense, hipStream_t st);
 
 // Attention-side q/k norm + RoPE.  Forward: q, k in, qo, ko out.  Backward:
 // q, k (the forward's inputs) and dqh, dkh (gradients of its outputs) in,
@@ -221,6 +221,7 @@ struct BwdArgs {
   const int32_t* blk_idx;
   const int32_t* cu;
   float scale;
+  bool dense;       // every causal key (blk_idx unused)
   u16* dq; int64_t dq_st, dq_sh;
   u16* dk; int64_t dk_st, dk_sh;
   u16* dv; int64_t dv_st, dv_sh;

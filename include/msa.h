@@ -63,6 +63,9 @@ extern "C" {
 /* Selection flags of msa_index_select_ex. */
 #define MSA_SELECT_FORCE_INIT 1u /* keep block 0 in every selection (the "init" rule) */
 
+/* Attention flags of msa_attn_fwd_ex / msa_attn_bwd_ex. */
+#define MSA_ATTN_DENSE 1u /* every causal key of the sequence; blk_idx is not read (may be NULL) */
+
 #define MSA_OP_SELECT 1
 #define MSA_OP_FWD 2
 #define MSA_OP_BWD 3
@@ -276,6 +279,37 @@ int msa_qsa_attn_bwd(const msa_dims* dims,
                      void* dk, int64_t dk_st, int64_t dk_sh,
                      void* dv, int64_t dv_st, int64_t dv_sh,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * msa_attn_fwd / msa_attn_bwd with attention flags.  flags = 0 is the plain
+ * call.  MSA_ATTN_DENSE computes the same attention over every causal key of
+ * the query's sequence instead of its listed blocks: the plain dense causal
+ * attention of MiniMax-M3's first three layers ([PR] PR body: block-sparse
+ * attention on the sparse layers, plain dense attention on the first three).
+ * blk_idx is then ignored and may be NULL.
+ * Unknown flag bits return MSA_ERR_INVALID_ARG.  Same workspaces
+ * (MSA_OP_FWD / MSA_OP_BWD) and conventions as the plain calls.
+ */
+int msa_attn_fwd_ex(const msa_dims* dims,
+                    const void* q, int64_t q_st, int64_t q_sh,
+                    const void* k, int64_t k_st, int64_t k_sh,
+                    const void* v, int64_t v_st, int64_t v_sh,
+                    const int32_t* blk_idx, const int32_t* cu_seqlens, float softmax_scale, uint32_t flags,
+                    void* o, int64_t o_st, int64_t o_sh, float* lse,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+int msa_attn_bwd_ex(const msa_dims* dims,
+                    const void* q, int64_t q_st, int64_t q_sh,
+                    const void* k, int64_t k_st, int64_t k_sh,
+                    const void* v, int64_t v_st, int64_t v_sh,
+                    const void* o, int64_t o_st, int64_t o_sh,
+                    const float* lse,
+                    const void* do_, int64_t do_st, int64_t do_sh,
+                    const int32_t* blk_idx, const int32_t* cu_seqlens, float softmax_scale, uint32_t flags,
+                    void* dq, int64_t dq_st, int64_t dq_sh,
+                    void* dk, int64_t dk_st, int64_t dk_sh,
+                    void* dv, int64_t dv_st, int64_t dv_sh,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable text for a status code. */
 const char* msa_status_string(int status);

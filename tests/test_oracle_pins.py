@@ -298,6 +298,34 @@ def test_sparse_equals_masked_dense_attention():
     np.testing.assert_allclose(dV, dv_t, atol=1e-10)
 
 
+# ---------------------------------------------------------------- dense layers beyond 16 blocks
+def test_all_blocks_listed_equals_dense_causal_beyond_2048():
+    """The dense first layers: with every causal block listed (24 > 16 of them) the oracle's attention
+    is torch's causal flash attention (fp64), forward and backward."""
+    p, q, k, v, do, cu = _pack_np([3000, 700], 2, 1, 31)
+    seq, pos = O.sequence_layout(cu)
+    nb = (max(p.lengths) + 127) // 128
+    blk = np.full((int(cu[-1]), 1, nb), -1, np.int32)
+    for t in range(int(cu[-1])):
+        blk[t, 0, :pos[t] // 128 + 1] = np.arange(pos[t] // 128 + 1)
+    scale = 1 / math.sqrt(128)
+    Ofw, LSE = O.attention_forward(q, k, v, blk, cu, scale)
+    dQ, dK, dV = O.attention_backward(q, k, v, do, blk, cu, scale, rows=np.arange(0, int(cu[-1]), 1))
+    for s in range(2):
+        a, b = int(cu[s]), int(cu[s + 1])
+        Q = torch.tensor(q[a:b], dtype=torch.float64).permute(1, 0, 2)[None]
+        K = torch.tensor(k[a:b], dtype=torch.float64).permute(1, 0, 2).repeat_interleave(2, 0)[None]
+        V = torch.tensor(v[a:b], dtype=torch.float64).permute(1, 0, 2).repeat_interleave(2, 0)[None]
+        out, lse = torch.ops.aten._scaled_dot_product_flash_attention_for_cpu(Q, K, V, 0.0, True, scale=scale)
+        np.testing.assert_allclose(Ofw[a:b], out[0].permute(1, 0, 2).numpy(), atol=1e-12)
+        np.testing.assert_allclose(LSE[a:b], lse[0].permute(1, 0).numpy(), atol=1e-12)
+        mask = np.tril(np.ones((b - a, b - a), dtype=bool))
+        o_t, dq_t, dk_t, dv_t = _torch_dense(q[a:b], k[a:b], v[a:b], do[a:b], mask, scale)
+        np.testing.assert_allclose(dQ[a:b], dq_t, atol=1e-10)
+        np.testing.assert_allclose(dK[a:b], dk_t, atol=1e-10)
+        np.testing.assert_allclose(dV[a:b], dv_t, atol=1e-10)
+
+
 # ---------------------------------------------------------------- narrow-block variant (4-token blocks)
 def _narrow_pack(lengths, topk, seed):
     p = synth.make_custom_pack(lengths, num_q_heads=12, num_kv_heads=1, seed=seed, head_dim=256,
