@@ -37,8 +37,11 @@ __device__ __forceinline__ int chunk_items(int L, int chunk, int j) {
   return (min((j + 1) * chunk, L) - 1) / kUnit + 1;
 }
 
+constexpr int kCuCache = 4097;      // cu_seqlens entries held in LDS for the tile keys
+constexpr int kKeysPerThread = 8;    // tile keys kept in registers between the two passes
+
 // Order key of tile i: block of its first token within that token's sequence.
-__device__ __forceinline__ int tile_key(const int32_t* __restrict__ cu, int S, int i) {
+__device__ __forceinline__ int tile_key(const int32_t* cu, int S, int i) {
   const int t0 = i * kAttnTile;
   const int s = find_seq(cu, S, t0);
   return min((t0 - cu[s]) / kBlock, kOrderBins - 1);
@@ -54,6 +57,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   __shared__ int sb[kPlanThreads];
   __shared__ int si[kPlanThreads];
   __shared__ int hist[kOrderBins];
+  __shared__ int scu[kCuCache];
   const int tid = threadIdx.x;
   int carry_b = 0, carry_i = 0;
   if (tid == 0) {
@@ -96,10 +100,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   }
 
   // tile launch order: counting sort on the position key, largest key first
+  // (ntiles = 0: the caller needs no tile order)
+  if (ntiles == 0) return;
   static_assert(kOrderBins == kPlanThreads, "one scan slot per key");
+  const bool cached = S + 1 <= kCuCache;
+  if (cached)
+    for (int i = tid; i <= S; i += kPlanThreads) scu[i] = cu[i];
+  const int32_t* cus = cached ? (const int32_t*)scu : cu;
   hist[tid] = 0;
   __syncthreads();
-  for (int i = tid; i < ntiles; i += kPlanThreads) atomicAdd(&hist[tile_key(cu, S, i)], 1);
+  int keys[kKeysPerThread];
+#pragma unroll
+  for (int e = 0; e < kKeysPerThread; ++e) {
+    const int i = tid + e * kPlanThreads;
+    keys[e] = i < ntiles ? tile_key(cus, S, i) : 0;
+    if (i < ntiles) atomicAdd(&hist[keys[e]], 1);
+  }
+  for (int i = tid + kKeysPerThread * kPlanThreads; i < ntiles; i += kPlanThreads)
+    atomicAdd(&hist[tile_key(cus, S, i)], 1);
   __syncthreads();
   const int key = kOrderBins - 1 - tid;  // slot tid scans the keys from the top down
   const int cnt = hist[key];
@@ -113,19 +131,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   }
   hist[key] = sb[tid] - cnt;  // first launch slot of the key
   __syncthreads();
-  for (int i = tid; i < ntiles; i += kPlanThreads) tile_order[atomicAdd(&hist[tile_key(cu, S, i)], 1)] = i;
+#pragma unroll
+  for (int e = 0; e < kKeysPerThread; ++e) {
+    const int i = tid + e * kPlanThreads;
+    if (i < ntiles) tile_order[atomicAdd(&hist[keys[e]], 1)] = i;
+  }
+  for (int i = tid + kKeysPerThread * kPlanThreads; i < ntiles; i += kPlanThreads)
+    tile_order[atomicAdd(&hist[tile_key(cus, S, i)], 1)] = i;
 }
 
 }  // namespace
 
-void launch_plan(const int32_t* cu, const Sizes& z, const PlanBufs& p, hipStream_t st, int unit) {
+void launch_plan(const int32_t* cu, const Sizes& z, const PlanBufs& p, hipStream_t st, int unit, bool tiles) {
   KernelTimer timer("plan", st);
+  const int nt = tiles ? (int)z.ntiles : 0;
   if (unit == kQsaKeyTile)
-    plan_kernel<kQsaKeyTile><<<1, kPlanThreads, 0, st>>>(cu, (int)z.S, (int)z.chunk, (int)z.ntiles, p.blkbase,
-                                                        p.blk_seq, p.seqitem, p.totals, p.tile_order);
+    plan_kernel<kQsaKeyTile><<<1, kPlanThreads, 0, st>>>(cu, (int)z.S, (int)z.chunk, nt, p.blkbase, p.blk_seq,
+                                                        p.seqitem, p.totals, p.tile_order);
   else
-    plan_kernel<kBlock><<<1, kPlanThreads, 0, st>>>(cu, (int)z.S, (int)z.chunk, (int)z.ntiles, p.blkbase,
-                                                   p.blk_seq, p.seqitem, p.totals, p.tile_order);
+    plan_kernel<kBlock><<<1, kPlanThreads, 0, st>>>(cu, (int)z.S, (int)z.chunk, nt, p.blkbase, p.blk_seq,
+                                                   p.seqitem, p.totals, p.tile_order);
 }
 
 }  // namespace msa
