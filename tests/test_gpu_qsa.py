@@ -149,3 +149,45 @@ def test_qsa_deterministic(gpu_lib):
     b = run(gpu_lib, p, blk)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_qsa_empty_sequences_inside_a_pack(gpu_lib):
+    """Zero-length sequences between ragged ones (repeated cu_seqlens entries)."""
+    p, blk = pack([0, 300, 0, 5, 0, 130], 1, 40, 59)
+    check_full(p, blk, run(gpu_lib, p, blk), "qsa empty sequences")
+
+
+def test_qsa_empty_pack_is_a_noop(gpu_lib):
+    cu = torch.zeros(1, dtype=torch.int32, device="cuda")
+    z = torch.empty(0, 12, 256, dtype=torch.bfloat16, device="cuda")
+    zk = torch.empty(0, 1, 256, dtype=torch.bfloat16, device="cuda")
+    blk = torch.empty(0, 1, 8, dtype=torch.int32, device="cuda")
+    o, lse = gpu_lib.msa_qsa_attn_fwd(z, zk, zk, blk, cu, 1)
+    dq, dk, dv = gpu_lib.msa_qsa_attn_bwd(z, zk, zk, o, lse, z, blk, cu, 1)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and dq.numel() == 0
+
+
+def test_qsa_longest_sequence_most_blocks(gpu_lib):
+    """One 32768-token sequence (the narrow entry points' limit) with 1024 listed blocks per
+    query (the K limit): sampled rows of O, LSE and dQ, and dK/dV of the last key tile."""
+    p = synth.make_custom_pack([32768], num_q_heads=12, num_kv_heads=1, seed=60, head_dim=256, block_size=4,
+                               topk_blocks=1024)
+    cu = p.cu_seqlens.numpy()
+    blk = synth.random_block_lists(cu, 1, 4, 1024, 60)
+    o, lse, dq, dk, dv = run(gpu_lib, p, blk)
+    rows = np.array([0, 63, 64, 4095, 4096, 16383, 32703, 32704, 32767] +
+                    list(np.random.default_rng(61).integers(0, 32768, 8)))
+    q, k, v, do = f32(p.q), f32(p.k), f32(p.v), f32(p.do)
+    Ow, Lw = O.attention_forward(q, k, v, blk, cu, SCALE, block=4, rows=rows)
+    dQw, _, _ = O.attention_backward(q, k, v, do, blk, cu, SCALE, block=4, rows=rows)
+    eo = float(np.abs(f32(o)[rows] - Ow).max())
+    el = float(np.abs(lse.cpu().numpy()[rows] - Lw).max())
+    rq = rel(f32(dq)[rows], dQw)
+    last = np.arange(32704, 32768)
+    sel = np.nonzero(np.isin(blk[:, 0, :], np.arange(8176, 8192)).any(axis=1))[0]
+    _, dKw, dVw = O.attention_backward(q, k, v, do, blk, cu, SCALE, block=4, rows=sel)
+    rk, rv = rel(f32(dk)[last], dKw[last]), rel(f32(dv)[last], dVw[last])
+    say(f"[qsa 32768 K=1024] O maxabs={eo:.3e} LSE maxabs={el:.3e} dQ rel={rq:.3e} last tile ({len(sel)} "
+        f"selectors) dK rel={rk:.3e} dV rel={rv:.3e}")
+    assert eo <= O_TOL and el <= LSE_TOL and rq <= G_TOL and rk <= G_TOL and rv <= G_TOL
