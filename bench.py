@@ -13,6 +13,7 @@ timed on a bounded sample of the same pack.
 from __future__ import annotations
 
 import argparse
+import re
 import csv
 import glob
 import hashlib
@@ -79,6 +80,19 @@ def traffic_file(config: str) -> str:
     return os.path.join(PROFILES, f"traffic_{config}.json")
 
 
+def kernel_key(raw: str) -> str:
+    """Library kernel name of a profiler record: `attn_fwd_kernel<false>(...)` -> `attn_fwd_kernel`,
+    the dense template instance -> `attn_fwd_dense_kernel`; other kernels keep their name."""
+    n = raw.replace("(anonymous namespace)::", "").split("(")[0].replace("msa::", "").strip()
+    if n.startswith("void "):
+        n = n[len("void "):]
+    dense = n.endswith("<true>")
+    n = re.sub(r"<[^<>]*>$", "", n)
+    if dense and n.endswith("_kernel"):
+        n = n[:-len("_kernel")] + "_dense_kernel"
+    return n
+
+
 def summarize_pmc(dirs, config: str, copy_mib: int) -> dict:
     """Per-kernel HBM bytes per dispatch from rocprofv3 --pmc CSVs (FETCH_SIZE and
     WRITE_SIZE, in KiB), each scaled by what the same counter reads for the plain
@@ -89,7 +103,7 @@ def summarize_pmc(dirs, config: str, copy_mib: int) -> dict:
             for r in csv.DictReader(open(f)):
                 if r["Counter_Name"] not in ("FETCH_SIZE", "WRITE_SIZE"):
                     continue
-                name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("msa::", "")
+                name = kernel_key(r["Kernel_Name"])
                 e = acc.setdefault(name, {}).setdefault(r["Counter_Name"], {})
                 e[r["Dispatch_Id"]] = e.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
     avg = {k: {c: sum(v.values()) / len(v) for c, v in d.items()} for k, d in acc.items()}
