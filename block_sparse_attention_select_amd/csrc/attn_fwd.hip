@@ -154,13 +154,17 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
     int pos = incl - cnt;
     while (bits) {
       const int bit = __ffs(bits) - 1;
-      const int gbu = gb_lo + 32 * lane + bit;
-      const int sb = blk_seq[gbu];
-      ulist[pos] = gbu;
-      ukey0[pos++] = cu[sb] + kBlock * (gbu - blkbase[sb]);
+      ulist[pos++] = gb_lo + 32 * lane + bit;
       bits &= bits - 1u;
     }
     if (lane == 63) nunion = incl;
+  }
+  __syncthreads();
+  // first token of every union block, one entry per thread (independent loads)
+  for (int i = threadIdx.x; i < nunion; i += blockDim.x) {
+    const int gbu = ulist[i];
+    const int sb = blk_seq[gbu];
+    ukey0[i] = cu[sb] + kBlock * (gbu - blkbase[sb]);
   }
   __syncthreads();
   const int nu = nunion;

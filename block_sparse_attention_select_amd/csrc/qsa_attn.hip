@@ -161,13 +161,17 @@ __device__ __forceinline__ void build_union(TileUnion& tu, const uint32_t* __res
     int pos = incl - cnt;
     while (x) {
       const int bit = __ffs(x) - 1;
-      const int gk = gk_lo + 32 * lane + bit;
-      const int sb = kt_seq[gk];
-      tu.ulist[pos] = gk;
-      tu.ukey0[pos++] = cu[sb] + kKT * (gk - ktbase[sb]);
+      tu.ulist[pos++] = gk_lo + 32 * lane + bit;
       x &= x - 1u;
     }
     if (lane == 63) tu.nunion = incl;
+  }
+  __syncthreads();
+  // first token of every union key tile, one entry per thread (independent loads)
+  for (int i = threadIdx.x; i < tu.nunion; i += blockDim.x) {
+    const int gk = tu.ulist[i];
+    const int sb = kt_seq[gk];
+    tu.ukey0[i] = cu[sb] + kKT * (gk - ktbase[sb]);
   }
   __syncthreads();
 }
