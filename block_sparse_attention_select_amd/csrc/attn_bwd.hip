@@ -91,45 +91,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
   }
   const int gb_lo = blkbase[find_seq(cu, S, t0)];
 
-  if (threadIdx.x < kUnionWords) bitmap[threadIdx.x] = 0u;
-  __syncthreads();
-  if constexpr (kDense) {
-    if (g < kTokPerWave && tvalid)
-      for (int c = li; c <= b_t; c += 16) {
-        const int rel = blkbase[s_t] + c - gb_lo;
-        atomicOr(&bitmap[rel >> 5], 1u << (rel & 31));
-      }
-  } else if (g < kTokPerWave && my_gb >= 0 && my_gb - gb_lo < kUnionWords * 32) {
-    atomicOr(&bitmap[(my_gb - gb_lo) >> 5], 1u << ((my_gb - gb_lo) & 31));
-  }
-  __syncthreads();
-  if (wave == 0) {
-    uint32_t bits = lane < kUnionWords ? bitmap[lane] : 0u;
-    const int cnt = __popc(bits);
-    int incl = cnt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
-    int pos = incl - cnt;
-    while (bits) {
-      const int bit = __ffs(bits) - 1;
-      ulist[pos++] = gb_lo + 32 * lane + bit;
-      bits &= bits - 1u;
-    }
-    if (lane == 63) nunion = incl;
-  }
-  __syncthreads();
-  // first token of every union block, one entry per thread (independent loads)
-  for (int i = threadIdx.x; i < nunion; i += blockDim.x) {
-    const int gbu = ulist[i];
-    const int sb = blk_seq[gbu];
-    ukey0[i] = cu[sb] + kBlock * (gbu - blkbase[sb]);
-  }
-  __syncthreads();
-  const int nsteps = nunion;
-
+  // the token's q, dO, Delta and LSE, before the union build so the loads overlap it
   int tok_t[kTokPerWave], tok_pos[kTokPerWave], tok_b[kTokPerWave], tok_base[kTokPerWave];
   bool tok_ok[kTokPerWave];
   bf16x8 qb[kTokPerWave][4], db[kTokPerWave][4];
@@ -174,6 +136,46 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) dqacc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+
+
+  if (threadIdx.x < kUnionWords) bitmap[threadIdx.x] = 0u;
+  __syncthreads();
+  if constexpr (kDense) {
+    if (g < kTokPerWave && tvalid)
+      for (int c = li; c <= b_t; c += 16) {
+        const int rel = blkbase[s_t] + c - gb_lo;
+        atomicOr(&bitmap[rel >> 5], 1u << (rel & 31));
+      }
+  } else if (g < kTokPerWave && my_gb >= 0 && my_gb - gb_lo < kUnionWords * 32) {
+    atomicOr(&bitmap[(my_gb - gb_lo) >> 5], 1u << ((my_gb - gb_lo) & 31));
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t bits = lane < kUnionWords ? bitmap[lane] : 0u;
+    const int cnt = __popc(bits);
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    int pos = incl - cnt;
+    while (bits) {
+      const int bit = __ffs(bits) - 1;
+      ulist[pos++] = gb_lo + 32 * lane + bit;
+      bits &= bits - 1u;
+    }
+    if (lane == 63) nunion = incl;
+  }
+  __syncthreads();
+  // first token of every union block, one entry per thread (independent loads)
+  for (int i = threadIdx.x; i < nunion; i += blockDim.x) {
+    const int gbu = ulist[i];
+    const int sb = blk_seq[gbu];
+    ukey0[i] = cu[sb] + kBlock * (gbu - blkbase[sb]);
+  }
+  __syncthreads();
+  const int nsteps = nunion;
 
   // step u: union block u.  Wavefronts 0-7 copy the four K runs of key tile w
   // (run 4w + ds: keys score_key(w, .), dims 32 ds ..), wavefronts 8-15 the

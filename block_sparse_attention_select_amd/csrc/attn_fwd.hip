@@ -129,6 +129,20 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
   }
   const int gb_lo = blkbase[find_seq(cu, S, t0)];
 
+  // the token's q as B operands, loaded before the union build so the loads
+  // overlap it
+  int tok_t[kTokPerWave];
+  bool tok_ok[kTokPerWave];
+  bf16x8 qb[kTokPerWave][4];
+#pragma unroll
+  for (int j = 0; j < kTokPerWave; ++j) {
+    tok_t[j] = t0 + kTokPerWave * wave + j;
+    tok_ok[j] = tok_t[j] < T;
+    const u16* qrow = q + (int64_t)min(tok_t[j], T - 1) * q_st + (int64_t)(h * kGroup + li) * q_sh;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) qb[j][ds] = tok_ok[j] ? load_bf16x8(qrow + 32 * ds + 8 * g) : zero_bf16x8();
+  }
+
   // 1. union of the tile's blocks
   if (threadIdx.x < kUnionWords) bitmap[threadIdx.x] = 0u;
   __syncthreads();
@@ -170,21 +184,14 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
   const int nu = nunion;
 
   // per-token state (j = 0, 1 for tokens 2w, 2w+1)
-  int tok_t[kTokPerWave], tok_pos[kTokPerWave], tok_b[kTokPerWave], tok_base[kTokPerWave];
-  bool tok_ok[kTokPerWave];
-  bf16x8 qb[kTokPerWave][4];
+  int tok_pos[kTokPerWave], tok_b[kTokPerWave], tok_base[kTokPerWave];
   f32x4 oacc[kTokPerWave][8];
   float m_run[kTokPerWave], l_run[kTokPerWave];
 #pragma unroll
   for (int j = 0; j < kTokPerWave; ++j) {
-    tok_t[j] = t0 + kTokPerWave * wave + j;
-    tok_ok[j] = tok_t[j] < T;
     tok_pos[j] = __builtin_amdgcn_readlane(pos_t, 16 * j);
     tok_b[j] = __builtin_amdgcn_readlane(b_t, 16 * j);
     tok_base[j] = tok_ok[j] ? blkbase[__builtin_amdgcn_readlane(s_t, 16 * j)] : 0;
-    const u16* qrow = q + (int64_t)min(tok_t[j], T - 1) * q_st + (int64_t)(h * kGroup + li) * q_sh;
-#pragma unroll
-    for (int ds = 0; ds < 4; ++ds) qb[j][ds] = tok_ok[j] ? load_bf16x8(qrow + 32 * ds + 8 * g) : zero_bf16x8();
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[j] = -INFINITY;

@@ -212,10 +212,8 @@ __global__ __launch_bounds__(64 * kTok) void qsa_fwd_kernel(
   const int ktb_t = tok_ok ? ktbase[s_t] : 0;
   const int own_c = pos_t / kKT;
 
-  build_union(tu, bits, cu, ktbase, kt_seq, S, Hk, h, t0, wave, lane, tok_ok, t, pos_t, ktb_t);
-  const int nu = tu.nunion;
-
-  // q of this token as B operands (heads past 12 zero), O^T accumulators
+  // q of this token as B operands (heads past 12 zero), loaded before the
+  // union build so the loads overlap it; O^T accumulators
   bf16x8 qb[8];
   {
     const bool hv = tok_ok && li < kG;
@@ -223,6 +221,8 @@ __global__ __launch_bounds__(64 * kTok) void qsa_fwd_kernel(
 #pragma unroll
     for (int ds = 0; ds < 8; ++ds) qb[ds] = hv ? load_bf16x8(qrow + 32 * ds) : zero_bf16x8();
   }
+  build_union(tu, bits, cu, ktbase, kt_seq, S, Hk, h, t0, wave, lane, tok_ok, t, pos_t, ktb_t);
+  const int nu = tu.nunion;
   f32x4 oacc[16];
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -390,10 +390,8 @@ __global__ __launch_bounds__(64 * kTok) void qsa_dq_kernel(
   const int ktb_t = tok_ok ? ktbase[s_t] : 0;
   const int own_c = pos_t / kKT;
 
-  build_union(tu, bits, cu, ktbase, kt_seq, S, Hk, h, t0, wave, lane, tok_ok, t, pos_t, ktb_t);
-  const int nu = tu.nunion;
-
   // q and dO as B operands; Delta = rowsum(dO * O) and the LSE of this lane's head
+  // (before the union build so the loads overlap it)
   const bool hv = tok_ok && li < kG;
   const int hq = h * kG + min(li, kG - 1);
   const int trow = tok_ok ? t : 0;
@@ -421,6 +419,8 @@ __global__ __launch_bounds__(64 * kTok) void qsa_dq_kernel(
     }
   }
   const bool live = lse2 > -INFINITY;
+  build_union(tu, bits, cu, ktbase, kt_seq, S, Hk, h, t0, wave, lane, tok_ok, t, pos_t, ktb_t);
+  const int nu = tu.nunion;
   f32x4 dqacc[16];
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt) dqacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
