@@ -8,18 +8,18 @@
 // block, with P = exp(scale q.k - LSE) and dS = P (dO.v - Delta).
 //
 // One workgroup per (work item, KV head); a work item is one chunk of query
-// positions of a sequence paired with one block those queries may select (the
-// plan orders items by chunk, so concurrent workgroups share their queries in
-// L2).
+// positions of a sequence paired with one block those queries may select;
+// items are launched heaviest first (dkdv_order_kernel).
 //   1. The chunk's queries that selected the block are listed in token order
 //      (wavefront ballots, so the list and every later sum are deterministic).
 //   2. Each of the 4 wavefronts keeps 32 keys of K and V as MFMA B operands
 //      and the 32 x 128 fp32 dK and dV sums in registers for the whole item.
-//   3. Selecting tokens stream through LDS eight at a time (two per
-//      wavefront), double buffered with global_load_lds copies issued while
-//      the previous eight are used.  Per token the stage holds q and dO laid
-//      out so each MFMA A operand is one contiguous 1 KB read, plus the
-//      token's 16 LSE and Delta values.
+//   3. Selecting tokens stream through LDS two at a time through a ring of
+//      four slots: global_load_lds copies of the next three pairs are in
+//      flight while one pair is used (the gathered rows come from HBM, whose
+//      latency one pair of work does not cover).  Per token the stage holds q
+//      and dO laid out so each MFMA A operand is one contiguous 1 KB read, plus
+//      the token's 16 LSE and Delta values.
 //   4. Two tokens (32 query rows) per MFMA step: S = q K^T and dP = dO V^T
 //      (A from LDS, B from registers), then dV += P^T dO and dK += dS^T q
 //      with P and dS taken straight from the score registers.  The B operands
@@ -35,34 +35,38 @@ namespace msa {
 
 namespace {
 
-constexpr int kBatch = 4;  // tokens per staging round, kBatch / 4 loaded by each wavefront
+constexpr int kBatch = 2;  // tokens per staging round
+constexpr int kNBuf = 4;   // staging ring: rounds bi+1 .. bi+3 in flight while bi is used
 
 // Stage layout of one token (u32x4 units): [0,256) q and [256,512) dO as
 // [ds][slot], operand lane li + 16g of run ds (row li, dims 32ds + 8g .. +7)
 // at slot swz_slot(li + 16g); stats: 16 -LSE*log2(e) then 16 Delta values.
-// One wavefront copies a token: 8 runs of 1 KB and one 128-byte run.
-// Addresses are a wavefront-uniform base (the token's row, scalar registers)
-// plus a per-lane byte offset (head, dims 8g..).
-__device__ __forceinline__ void stage_token(int t, int h, int Hk, int lane, uint32_t slot_lds, uint32_t stats_lds,
-                                            const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
-                                            const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
-                                            const float* __restrict__ nlse, const float* __restrict__ delta) {
+// Two wavefronts copy a token: part 0 the 4 q runs of 1 KB and the 128-byte
+// stats run, part 1 the 4 dO runs.  Addresses are a wavefront-uniform base
+// (the token's row, scalar registers) plus a per-lane byte offset (head, dims
+// 8g..).
+__device__ __forceinline__ void stage_part(int t, int part, int h, int Hk, int lane, uint32_t slot_lds, uint32_t stats_lds,
+                                           const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
+                                           const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
+                                           const float* __restrict__ nlse, const float* __restrict__ delta) {
   t = __builtin_amdgcn_readfirstlane(t);
-  const int hr = swz_slot(lane) & 15;  // head of this lane's slot (runs stored swizzled)
-  const uint32_t q_off = (uint32_t)(2 * (hr * q_sh + 8 * (lane >> 4)));
-  const uint32_t do_off = (uint32_t)(2 * (hr * do_sh + 8 * (lane >> 4)));
-  const u16* qr = q + (int64_t)t * q_st + (int64_t)(h * kGroup) * q_sh;
-  const u16* dr = dO + (int64_t)t * do_st + (int64_t)(h * kGroup) * do_sh;
+  const int hr = swz_slot(lane) & 15;
+  if (part == 0) {
+    const uint32_t q_off = (uint32_t)(2 * (hr * q_sh + 8 * (lane >> 4)));
+    const u16* qr = q + (int64_t)t * q_st + (int64_t)(h * kGroup) * q_sh;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    dma16s(qr + 32 * i, q_off, slot_lds + i * 1024);
-    dma16s(dr + 32 * i, do_off, slot_lds + 4096 + i * 1024);
+    for (int i = 0; i < 4; ++i) dma16s(qr + 32 * i, q_off, slot_lds + i * 1024);
+    const int64_t row = (int64_t)t * (Hk * kGroup) + h * kGroup;
+    if (lane < 16)
+      dma4s(nlse + row, 4 * lane, stats_lds);
+    else if (lane < 32)
+      dma4s(delta + row - 16, 4 * lane, stats_lds);
+  } else {
+    const uint32_t do_off = (uint32_t)(2 * (hr * do_sh + 8 * (lane >> 4)));
+    const u16* dr = dO + (int64_t)t * do_st + (int64_t)(h * kGroup) * do_sh;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16s(dr + 32 * i, do_off, slot_lds + 4096 + i * 1024);
   }
-  const int64_t row = (int64_t)t * (Hk * kGroup) + h * kGroup;
-  if (lane < 16)
-    dma4s(nlse + row, 4 * lane, stats_lds);
-  else if (lane < 32)
-    dma4s(delta + row - 16, 4 * lane, stats_lds);
 }
 
 // kDense: every token of the chunk at or after the block's first key selects it (blk_idx unused).
@@ -79,8 +83,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int S, int Hk, int chunk, int items_cap, const int32_t* __restrict__ item_order, float scale_log2, float scale,
     int32_t* __restrict__ item_count, float* __restrict__ part_dk, float* __restrict__ part_dv,
     u16* __restrict__ dk_out, int64_t dk_st, int64_t dk_sh, u16* __restrict__ dv_out, int64_t dv_st, int64_t dv_sh) {
-  __shared__ u32x4 stage[2][kBatch][512];
-  __shared__ __align__(16) float stats[2][kBatch][32];
+  __shared__ u32x4 stage[kNBuf][kBatch][512];
+  __shared__ __align__(16) float stats[kNBuf][kBatch][32];
   __shared__ int sel[kDkdvChunkMax];
   __shared__ int wcount[4];
 
@@ -171,21 +175,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     const int nbatch = (nsel + kBatch - 1) / kBatch;
     // slots past the end repeat the last token (finite operands, masked to zero)
+    // wavefront w copies half of token w % 2 of a round: q and stats (w < 2) or dO
     auto stage_round = [&](int bi, int buf) {
-#pragma unroll
-      for (int e = 0; e < kBatch / 4; ++e) {
-        const int slot = (kBatch / 4) * wave + e;
-        stage_token(sel[min(bi * kBatch + slot, nsel - 1)], h, Hk, fresh_lane(), lds_offset(&stage[buf][slot][0]),
-                    lds_offset(&stats[buf][slot][0]), q, q_st, q_sh, dO, do_st, do_sh, nlse, delta);
-      }
+      const int slot = wave & 1;
+      stage_part(sel[min(bi * kBatch + slot, nsel - 1)], wave >> 1, h, Hk, fresh_lane(),
+                 lds_offset(&stage[buf][slot][0]), lds_offset(&stats[buf][slot][0]), q, q_st, q_sh, dO, do_st,
+                 do_sh, nlse, delta);
     };
-    stage_round(0, 0);
+    for (int r = 0; r < kNBuf - 1 && r < nbatch; ++r) stage_round(r, r);
     wait_copies();
     wait_all_loads();
     __syncthreads();
     for (int bi = 0; bi < nbatch; ++bi) {
-      const int cur = bi & 1;
-      if (bi + 1 < nbatch) stage_round(bi + 1, cur ^ 1);
+      const int cur = bi % kNBuf;
+      const bool ahead = bi + kNBuf - 1 < nbatch;
+      if (ahead) stage_round(bi + kNBuf - 1, (bi + kNBuf - 1) % kNBuf);
 #pragma unroll 1
       for (int pp = 0; pp < kBatch / 2; ++pp) {
         const int n0 = bi * kBatch + 2 * pp;
@@ -271,7 +275,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           }
         }
       }
-      wait_copies();
+      // round bi+1 must have landed: with rounds bi+2, bi+3 still in flight a
+      // wavefront may keep 2 rounds of its copies (6 or 4 instructions each)
+      if (ahead) {
+        if (wave < 2)
+          asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      } else {
+        wait_copies();
+      }
       lds_barrier();
     }
   }
