@@ -38,6 +38,40 @@ namespace {
 // dQ^T = K^T dS^T are read transposed from the same K copy.
 // ---------------------------------------------------------------------------
 constexpr int kTileTok = kAttnTile;
+
+// Per-(global block, KV head) copies of K and V in the dQ pass's staging order,
+// so every staged 1 KB run is one contiguous copy: run kt*4 + ds, slot l
+// holding x[key score_key(kt, swz_slot(l) % 16)][dims 32ds + 8(l / 16) .. +7]
+// (the swizzled stage the transposed K^T reads expect; keys past the sequence
+// end are zero).  blockIdx.z selects K (0) or V (1).
+__global__ __launch_bounds__(256) void bwd_block_prep_kernel(const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
+                                                             const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
+                                                             const int32_t* __restrict__ cu,
+                                                             const int32_t* __restrict__ blkbase,
+                                                             const int32_t* __restrict__ blk_seq,
+                                                             const int32_t* __restrict__ totals, int Hk,
+                                                             u16* __restrict__ kop, u16* __restrict__ vop) {
+  const int gb = blockIdx.x;
+  const int h = blockIdx.y;
+  if (gb >= totals[0]) return;
+  const bool is_v = blockIdx.z != 0;
+  const u16* x = is_v ? v : k;
+  const int64_t st_t = is_v ? v_st : k_st, st_h = is_v ? v_sh : k_sh;
+  const int s = blk_seq[gb];
+  const int c = gb - blkbase[s];
+  const int seq0 = cu[s];
+  const int L = cu[s + 1] - seq0;
+  u16* dst = (is_v ? vop : kop) + ((int64_t)gb * Hk + h) * (kHeadDim * kBlock);
+  for (int i = threadIdx.x; i < 32 * 64; i += 256) {
+    const int run = i >> 6, ln = i & 63;
+    const int kp = kBlock * c + score_key(run >> 2, swz_slot(ln) & 15);
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (kp < L)
+      val = *reinterpret_cast<const u32x4*>(x + (int64_t)(seq0 + kp) * st_t + (int64_t)h * st_h + 32 * (run & 3) +
+                                            8 * (ln >> 4));
+    *reinterpret_cast<u32x4*>(dst + (int64_t)i * 8) = val;
+  }
+}
 constexpr int kTokPerWave = 1;
 constexpr int kDqWaves = kTileTok / kTokPerWave;
 constexpr int kUnionWords = 34;
@@ -47,8 +81,7 @@ constexpr int kMaxUnion = kTileTok * kTopk;
 template <bool kDense>
 __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
-    const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
-    const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
+    const u16* __restrict__ kop, const u16* __restrict__ vop,
     const u16* __restrict__ o, int64_t o_st, int64_t o_sh,
     const u16* __restrict__ dO, int64_t do_st, int64_t do_sh, const float* __restrict__ lse,
     const int32_t* __restrict__ blk_idx, const int32_t* __restrict__ cu, const int32_t* __restrict__ blkbase,
@@ -62,7 +95,6 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
   // a dense tile's union is up to one sequence's 1024 blocks plus one per later sequence
   constexpr int kUnionCap = kDense ? kUnionWords * 32 : kMaxUnion;
   __shared__ int ulist[kUnionCap];
-  __shared__ int ukey0[kUnionCap];  // first token of each union block
   __shared__ int nunion;
 
   // workgroup b runs KV head b % Hk of the tile in launch slot b / Hk
@@ -168,13 +200,6 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     if (lane == 63) nunion = incl;
   }
   __syncthreads();
-  // first token of every union block, one entry per thread (independent loads)
-  for (int i = threadIdx.x; i < nunion; i += blockDim.x) {
-    const int gbu = ulist[i];
-    const int sb = blk_seq[gbu];
-    ukey0[i] = cu[sb] + kBlock * (gbu - blkbase[sb]);
-  }
-  __syncthreads();
   const int nsteps = nunion;
 
   // step u: union block u.  Wavefronts 0-7 copy the four K runs of key tile w
@@ -182,25 +207,14 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
   // same runs of V; each copy is a scalar base plus a lane offset.
   static_assert(kDqWaves == 16, "four K or V runs per wavefront");
   auto stage = [&](int u, int buf) {
-    const int kstart = __builtin_amdgcn_readfirstlane(ukey0[u]);
+    const int gb = __builtin_amdgcn_readfirstlane(ulist[u]);
     const int ln = fresh_lane();
     const int tile = wave & 7;
     const bool is_k = wave < 8;
-    const u16* x = is_k ? k : v;
-    const int64_t x_st = is_k ? k_st : v_st, x_sh = is_k ? k_sh : v_sh;
     u32x4* dst = is_k ? &kbuf[buf][4 * tile][0] : &vbuf[buf][4 * tile][0];
-    const int kl = score_key(tile, swz_slot(ln) & 15);  // runs stored swizzled
-    if (kstart + kBlock <= T) {
-      const u16* base = x + (int64_t)kstart * x_st + (int64_t)h * x_sh;
-      const uint32_t off = (uint32_t)(2 * (kl * x_st + 8 * (ln >> 4)));
+    const u16* base = (is_k ? kop : vop) + (((int64_t)gb * Hk + h) * 32 + 4 * tile) * 512;
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) dma16s(base + 32 * ds, off, lds_offset(dst + 64 * ds));
-    } else {  // the pack's last block: keys past the end repeat the last token
-      const int key = min(kstart + kl, T - 1);
-#pragma unroll
-      for (int ds = 0; ds < 4; ++ds)
-        dma16(x + (int64_t)key * x_st + (int64_t)h * x_sh + 32 * ds + 8 * (ln >> 4), lds_offset(dst + 64 * ds));
-    }
+    for (int ds = 0; ds < 4; ++ds) dma16s(base + 512 * ds, 16 * ln, lds_offset(dst + 64 * ds));
   };
   if (nsteps > 0) stage(0, 0);
   wait_copies();
@@ -361,10 +375,15 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
 void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStream_t st) {
   const int T = (int)z.T, Hk = (int)z.Hk, S = (int)z.S;
   {
+    KernelTimer timer("bwd_block_prep", st);
+    bwd_block_prep_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)Hk, 2), 256, 0, st>>>(
+        a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.cu, p.blkbase, p.blk_seq, p.totals, Hk, a.kop, a.vop);
+  }
+  {
     KernelTimer timer("attn_bwd_dq", st);
     auto kern = a.dense ? attn_bwd_dq_kernel<true> : attn_bwd_dq_kernel<false>;
     kern<<<(unsigned)(z.ntiles * Hk), 64 * kDqWaves, 0, st>>>(
-        a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.o, a.o_st, a.o_sh, a.dO, a.do_st,
+        a.q, a.q_st, a.q_sh, a.kop, a.vop, a.o, a.o_st, a.o_sh, a.dO, a.do_st,
         a.do_sh, a.lse, a.blk_idx, a.cu, p.blkbase, p.blk_seq, p.tile_order, S, T, Hk, a.scale * kLog2e, a.scale,
         a.dq, a.dq_st,
         a.dq_sh, a.delta, a.nlse, a.item_load, (int)(z.Hk * z.items_cap));

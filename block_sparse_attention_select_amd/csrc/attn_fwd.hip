@@ -25,16 +25,20 @@ namespace msa {
 
 namespace {
 
-// Per-block transposed copy in MFMA operand order: for global block gb and
-// KV head h, 32 runs of 64 lanes x 8 bf16, run dt*4 + ks, lane li + 16g holding
-// x[key = 32ks + 8g + 0..7][dim = 16dt + li] (keys past the sequence end are
-// zero).  This is the A operand of O^T = V^T P^T (and of dQ^T = K^T dS^T).
-__global__ __launch_bounds__(256) void block_transpose_kernel(const u16* __restrict__ x, int64_t st_t, int64_t st_h,
-                                                              const int32_t* __restrict__ cu,
-                                                              const int32_t* __restrict__ blkbase,
-                                                              const int32_t* __restrict__ blk_seq,
-                                                              const int32_t* __restrict__ totals, int Hk,
-                                                              u16* __restrict__ xt) {
+// Per-(global block, KV head) copies of K and V in the forward's staging
+// order, so that every staged 1 KB run is one contiguous copy (a run of raw K
+// rows would be sixteen 64-byte pieces).  Keys past the sequence end are zero.
+//   kop: run kt*4 + ds, lane li + 16g holding K[key score_key(kt, li)][dims
+//        32ds + 8g .. +7] -- the A operand of S^T = K Q^T;
+//   vt:  run dt*4 + ks, lane li + 16g holding V[keys 32ks + 8g + 0..7][dim
+//        16dt + li] -- the A operand of O^T = V^T P^T.
+__global__ __launch_bounds__(256) void block_prep_kernel(const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
+                                                         const u16* __restrict__ x, int64_t st_t, int64_t st_h,
+                                                         const int32_t* __restrict__ cu,
+                                                         const int32_t* __restrict__ blkbase,
+                                                         const int32_t* __restrict__ blk_seq,
+                                                         const int32_t* __restrict__ totals, int Hk,
+                                                         u16* __restrict__ kop, u16* __restrict__ xt) {
   __shared__ u16 tile[kBlock][kHeadDim + 8];
   const int gb = blockIdx.x;
   const int h = blockIdx.y;
@@ -50,6 +54,16 @@ __global__ __launch_bounds__(256) void block_transpose_kernel(const u16* __restr
     u32x4 v = {0u, 0u, 0u, 0u};
     if (kp < L) v = *reinterpret_cast<const u32x4*>(x + (int64_t)(seq0 + kp) * st_t + (int64_t)h * st_h + ch * 8);
     *reinterpret_cast<u32x4*>(&tile[key][ch * 8]) = v;
+  }
+  u16* kdst = kop + ((int64_t)gb * Hk + h) * (kHeadDim * kBlock);
+  for (int i = threadIdx.x; i < 32 * 64; i += 256) {
+    const int run = i >> 6, ln = i & 63;
+    const int kp = kBlock * c + score_key(run >> 2, ln & 15);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (kp < L)
+      v = *reinterpret_cast<const u32x4*>(k + (int64_t)(seq0 + kp) * k_st + (int64_t)h * k_sh + 32 * (run & 3) +
+                                          8 * (ln >> 4));
+    *reinterpret_cast<u32x4*>(kdst + (int64_t)i * 8) = v;
   }
   __syncthreads();
   u16* dst = xt + ((int64_t)gb * Hk + h) * (kHeadDim * kBlock);
@@ -91,8 +105,7 @@ constexpr int kMaxUnion = kTileTok * kTopk;
 template <bool kDense>
 __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
-    const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
-    const u16* __restrict__ vt, const int32_t* __restrict__ blk_idx,
+    const u16* __restrict__ kop, const u16* __restrict__ vt, const int32_t* __restrict__ blk_idx,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ blkbase, const int32_t* __restrict__ blk_seq,
     const int32_t* __restrict__ tile_order, int S, int T, int Hk, float scale_log2, u16* __restrict__ o,
     int64_t o_st, int64_t o_sh, float* __restrict__ lse) {
@@ -102,7 +115,6 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
   // a dense tile's union is up to one sequence's 1024 blocks plus one per later sequence
   constexpr int kUnionCap = kDense ? kUnionWords * 32 : kMaxUnion;
   __shared__ int ulist[kUnionCap];
-  __shared__ int ukey0[kUnionCap];  // first token of each union block
   __shared__ int nunion;
 
   // workgroup b runs KV head b % Hk of the tile in launch slot b / Hk
@@ -174,13 +186,6 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
     if (lane == 63) nunion = incl;
   }
   __syncthreads();
-  // first token of every union block, one entry per thread (independent loads)
-  for (int i = threadIdx.x; i < nunion; i += blockDim.x) {
-    const int gbu = ulist[i];
-    const int sb = blk_seq[gbu];
-    ukey0[i] = cu[sb] + kBlock * (gbu - blkbase[sb]);
-  }
-  __syncthreads();
   const int nu = nunion;
 
   // per-token state (j = 0, 1 for tokens 2w, 2w+1)
@@ -206,19 +211,9 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
     const int gb = __builtin_amdgcn_readfirstlane(ulist[u]);
     const int ln = fresh_lane();
     if (wave < 8) {
-      const int kstart = __builtin_amdgcn_readfirstlane(ukey0[u]);
-      if (kstart + kBlock <= T) {
-        const u16* base = k + (int64_t)kstart * k_st + (int64_t)h * k_sh;
-        const uint32_t off = (uint32_t)(2 * (score_key(wave, ln & 15) * k_st + 8 * (ln >> 4)));
+      const u16* base = kop + (((int64_t)gb * Hk + h) * 32 + 4 * wave) * 512;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) dma16s(base + 32 * ii, off, lds_offset(&kbuf[buf][4 * wave + ii][0]));
-      } else {  // the pack's last block: keys past the end repeat the last token
-        const int key = min(kstart + score_key(wave, ln & 15), T - 1);
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          dma16(k + (int64_t)key * k_st + (int64_t)h * k_sh + 32 * ii + 8 * (ln >> 4),
-                lds_offset(&kbuf[buf][4 * wave + ii][0]));
-      }
+      for (int ii = 0; ii < 4; ++ii) dma16s(base + 512 * ii, 16 * ln, lds_offset(&kbuf[buf][4 * wave + ii][0]));
     } else {
       const u16* base = vt + (((int64_t)gb * Hk + h) * 32 + 4 * (wave - 8)) * 512;
 #pragma unroll
@@ -350,23 +345,20 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
 
 }  // namespace
 
-void launch_block_transpose(const Sizes& z, const u16* x, int64_t st_t, int64_t st_h,
-                            const int32_t* cu, const PlanBufs& p, u16* xt, hipStream_t st) {
-  {
-    KernelTimer timer("block_transpose", st);
-    block_transpose_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk), 256, 0, st>>>(
-        x, st_t, st_h, cu, p.blkbase, p.blk_seq, p.totals, (int)z.Hk, xt);
-  }
+void launch_block_prep(const Sizes& z, const u16* k, int64_t k_st, int64_t k_sh, const u16* v, int64_t v_st,
+                       int64_t v_sh, const int32_t* cu, const PlanBufs& p, u16* kop, u16* vt, hipStream_t st) {
+  KernelTimer timer("block_prep", st);
+  block_prep_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk), 256, 0, st>>>(
+      k, k_st, k_sh, v, v_st, v_sh, cu, p.blkbase, p.blk_seq, p.totals, (int)z.Hk, kop, vt);
 }
 
 void launch_attn_fwd(const Sizes& z, const u16* q, int64_t q_st, int64_t q_sh,
-                     const u16* k, int64_t k_st, int64_t k_sh, const u16* vt,
-                     const int32_t* blk_idx, const int32_t* cu, const PlanBufs& p, float scale,
+                     const u16* kop, const u16* vt, const int32_t* blk_idx, const int32_t* cu, const PlanBufs& p, float scale,
                      u16* o, int64_t o_st, int64_t o_sh, float* lse, bool dense, hipStream_t st) {
   KernelTimer timer("attn_fwd", st);
   auto kern = dense ? attn_fwd_kernel<true> : attn_fwd_kernel<false>;
   kern<<<(unsigned)(z.ntiles * z.Hk), 64 * kFwdWaves, 0, st>>>(
-      q, q_st, q_sh, k, k_st, k_sh, vt, blk_idx, cu, p.blkbase, p.blk_seq, p.tile_order, (int)z.S, (int)z.T,
+      q, q_st, q_sh, kop, vt, blk_idx, cu, p.blkbase, p.blk_seq, p.tile_order, (int)z.S, (int)z.T,
       (int)z.Hk, scale * kLog2e, o, o_st, o_sh, lse);
 }
 

@@ -151,17 +151,21 @@ SelectWs carve_select(Carver& c, const Sizes& z) {
 
 struct FwdWs {
   PlanBufs plan;
+  u16* kop;
   u16* vt;
 };
 FwdWs carve_fwd(Carver& c, const Sizes& z) {
   FwdWs w;
   w.plan = carve_plan(c, z);
+  w.kop = c.take<u16>(z.nblk_cap * z.Hk * msa::kHeadDim * msa::kBlock);
   w.vt = c.take<u16>(z.nblk_cap * z.Hk * msa::kHeadDim * msa::kBlock);
   return w;
 }
 
 struct BwdWs {
   PlanBufs plan;
+  u16* kop;
+  u16* vop;
   float* delta;
   float* nlse;
   int32_t* item_count;
@@ -173,6 +177,8 @@ struct BwdWs {
 BwdWs carve_bwd(Carver& c, const Sizes& z) {
   BwdWs w;
   w.plan = carve_plan(c, z);
+  w.kop = c.take<u16>(z.nblk_cap * z.Hk * msa::kHeadDim * msa::kBlock);
+  w.vop = c.take<u16>(z.nblk_cap * z.Hk * msa::kHeadDim * msa::kBlock);
   w.delta = c.take<float>(z.T * z.Hq);
   w.nlse = c.take<float>(z.T * z.Hq);
   w.item_count = c.take<int32_t>(z.Hk * z.items_cap);
@@ -353,8 +359,9 @@ int msa_attn_fwd_ex(const msa_dims* dims, const void* q, int64_t q_st, int64_t q
   Carver c(workspace);
   FwdWs w = carve_fwd(c, z);
   msa::launch_plan(cu_seqlens, z, w.plan, stream);
-  msa::launch_block_transpose(z, (const u16*)v, v_st, v_sh, cu_seqlens, w.plan, w.vt, stream);
-  msa::launch_attn_fwd(z, (const u16*)q, q_st, q_sh, (const u16*)k, k_st, k_sh, w.vt, dense ? nullptr : blk_idx,
+  msa::launch_block_prep(z, (const u16*)k, k_st, k_sh, (const u16*)v, v_st, v_sh, cu_seqlens, w.plan, w.kop, w.vt,
+                         stream);
+  msa::launch_attn_fwd(z, (const u16*)q, q_st, q_sh, w.kop, w.vt, dense ? nullptr : blk_idx,
                        cu_seqlens, w.plan, softmax_scale, (u16*)o, o_st, o_sh, lse, dense, stream);
   return launch_status();
 }
@@ -408,6 +415,8 @@ int msa_attn_bwd_ex(const msa_dims* dims, const void* q, int64_t q_st, int64_t q
   a.dq = (u16*)dq; a.dq_st = dq_st; a.dq_sh = dq_sh;
   a.dk = (u16*)dk; a.dk_st = dk_st; a.dk_sh = dk_sh;
   a.dv = (u16*)dv; a.dv_st = dv_st; a.dv_sh = dv_sh;
+  a.kop = w.kop;
+  a.vop = w.vop;
   a.delta = w.delta;
   a.nlse = w.nlse;
   a.item_count = w.item_count;

@@ -182,11 +182,12 @@ void launch_select(const Sizes& z, const u16* idx_q, int64_t sq_t, int64_t sq_h,
                    float eps, float rope_base, const int32_t* cu, const PlanBufs& p,
                    bool force_init, u16* qfeat, u16* kfeat, float* scores, int32_t* blk_idx, hipStream_t st);
 
-void launch_block_transpose(const Sizes& z, const u16* x, int64_t st_t, int64_t st_h,
-                            const int32_t* cu, const PlanBufs& p, u16* xt, hipStream_t st);
+// Forward operand copies of K and V per (global block, KV head) (attn_fwd.hip).
+void launch_block_prep(const Sizes& z, const u16* k, int64_t k_st, int64_t k_sh, const u16* v, int64_t v_st,
+                       int64_t v_sh, const int32_t* cu, const PlanBufs& p, u16* kop, u16* vt, hipStream_t st);
 
 void launch_attn_fwd(const Sizes& z, const u16* q, int64_t q_st, int64_t q_sh,
-                     const u16* k, int64_t k_st, int64_t k_sh, const u16* vt,
+                     const u16* kop, const u16* vt,
                      const int32_t* blk_idx, const int32_t* cu, const PlanBufs& p, float scale,
                      u16* o, int64_t o_st, int64_t o_sh, float* lse, bool dense, hipStream_t st);
 
@@ -227,6 +228,8 @@ struct BwdArgs {
   u16* dk; int64_t dk_st, dk_sh;
   u16* dv; int64_t dv_st, dv_sh;
   // workspace
+  u16* kop;         // [nblk][Hk][32 runs][64 slots][8] K in the dQ pass's staging order
+  u16* vop;         // the same for V
   float* delta;     // [T][Hq]
   float* nlse;      // [T][Hq] -LSE * log2(e), -inf for rows without keys
   int32_t* item_count;  // [Hk][items_cap]
