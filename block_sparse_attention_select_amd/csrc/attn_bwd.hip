@@ -43,7 +43,7 @@ constexpr int kTileTok = kAttnTile;
 // so every staged 1 KB run is one contiguous copy: run kt*4 + ds, slot l
 // holding x[key score_key(kt, swz_slot(l) % 16)][dims 32ds + 8(l / 16) .. +7]
 // (the swizzled stage the transposed K^T reads expect; keys past the sequence
-// end are zero).  blockIdx.z selects K (0) or V (1).
+// end are zero).  blockIdx.z: K (0-3) or V (4-7), a quarter of the runs each.
 __global__ __launch_bounds__(256) void bwd_block_prep_kernel(const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
                                                              const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
                                                              const int32_t* __restrict__ cu,
@@ -54,7 +54,8 @@ __global__ __launch_bounds__(256) void bwd_block_prep_kernel(const u16* __restri
   const int gb = blockIdx.x;
   const int h = blockIdx.y;
   if (gb >= totals[0]) return;
-  const bool is_v = blockIdx.z != 0;
+  const bool is_v = blockIdx.z >= 4;
+  const int part = blockIdx.z & 3;  // runs 8 part .. 8 part + 7
   const u16* x = is_v ? v : k;
   const int64_t st_t = is_v ? v_st : k_st, st_h = is_v ? v_sh : k_sh;
   const int s = blk_seq[gb];
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(256) void bwd_block_prep_kernel(const u16* __restri
   const int seq0 = cu[s];
   const int L = cu[s + 1] - seq0;
   u16* dst = (is_v ? vop : kop) + ((int64_t)gb * Hk + h) * (kHeadDim * kBlock);
-  for (int i = threadIdx.x; i < 32 * 64; i += 256) {
+  for (int i = 512 * part + threadIdx.x; i < 512 * part + 512; i += 256) {
     const int run = i >> 6, ln = i & 63;
     const int kp = kBlock * c + score_key(run >> 2, swz_slot(ln) & 15);
     u32x4 val = {0u, 0u, 0u, 0u};
@@ -376,7 +377,7 @@ void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStr
   const int T = (int)z.T, Hk = (int)z.Hk, S = (int)z.S;
   {
     KernelTimer timer("bwd_block_prep", st);
-    bwd_block_prep_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)Hk, 2), 256, 0, st>>>(
+    bwd_block_prep_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)Hk, 8), 256, 0, st>>>(
         a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.cu, p.blkbase, p.blk_seq, p.totals, Hk, a.kop, a.vop);
   }
   {

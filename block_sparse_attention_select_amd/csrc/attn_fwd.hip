@@ -39,24 +39,28 @@ __global__ __launch_bounds__(256) void block_prep_kernel(const u16* __restrict__
                                                          const int32_t* __restrict__ blk_seq,
                                                          const int32_t* __restrict__ totals, int Hk,
                                                          u16* __restrict__ kop, u16* __restrict__ xt) {
-  __shared__ u16 tile[kBlock][kHeadDim + 8];
+  // workgroup part p (of 4): K runs 8p .. 8p+7 (key tiles 2p, 2p+1) and the
+  // V^T runs of dims 32p .. 32p+31 (runs 8p .. 8p+7)
+  __shared__ u16 tile[kBlock][32 + 8];
   const int gb = blockIdx.x;
   const int h = blockIdx.y;
+  const int part = blockIdx.z;
   if (gb >= totals[0]) return;
   const int s = blk_seq[gb];
   const int c = gb - blkbase[s];
   const int seq0 = cu[s];
   const int L = cu[s + 1] - seq0;
-  for (int i = threadIdx.x; i < kBlock * 16; i += 256) {
-    const int key = i >> 4;
-    const int ch = i & 15;
+  for (int i = threadIdx.x; i < kBlock * 4; i += 256) {
+    const int key = i >> 2;
+    const int ch = i & 3;
     const int kp = kBlock * c + key;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (kp < L) v = *reinterpret_cast<const u32x4*>(x + (int64_t)(seq0 + kp) * st_t + (int64_t)h * st_h + ch * 8);
+    if (kp < L)
+      v = *reinterpret_cast<const u32x4*>(x + (int64_t)(seq0 + kp) * st_t + (int64_t)h * st_h + 32 * part + ch * 8);
     *reinterpret_cast<u32x4*>(&tile[key][ch * 8]) = v;
   }
   u16* kdst = kop + ((int64_t)gb * Hk + h) * (kHeadDim * kBlock);
-  for (int i = threadIdx.x; i < 32 * 64; i += 256) {
+  for (int i = 512 * part + threadIdx.x; i < 512 * part + 512; i += 256) {
     const int run = i >> 6, ln = i & 63;
     const int kp = kBlock * c + score_key(run >> 2, ln & 15);
     u32x4 v = {0u, 0u, 0u, 0u};
@@ -67,10 +71,10 @@ __global__ __launch_bounds__(256) void block_prep_kernel(const u16* __restrict__
   }
   __syncthreads();
   u16* dst = xt + ((int64_t)gb * Hk + h) * (kHeadDim * kBlock);
-  for (int i = threadIdx.x; i < 32 * 64; i += 256) {
+  for (int i = 512 * part + threadIdx.x; i < 512 * part + 512; i += 256) {
     const int run = i >> 6;
     const int lane = i & 63;
-    const int d = 16 * (run >> 2) + (lane & 15);
+    const int d = 16 * (run >> 2) + (lane & 15) - 32 * part;
     const int k0 = 32 * (run & 3) + 8 * (lane >> 4);
     uint32_t w[4];
 #pragma unroll
@@ -348,7 +352,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
 void launch_block_prep(const Sizes& z, const u16* k, int64_t k_st, int64_t k_sh, const u16* v, int64_t v_st,
                        int64_t v_sh, const int32_t* cu, const PlanBufs& p, u16* kop, u16* vt, hipStream_t st) {
   KernelTimer timer("block_prep", st);
-  block_prep_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk), 256, 0, st>>>(
+  block_prep_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk, 4), 256, 0, st>>>(
       k, k_st, k_sh, v, v_st, v_sh, cu, p.blkbase, p.blk_seq, p.totals, (int)z.Hk, kop, vt);
 }
 
