@@ -193,18 +193,22 @@ struct QsaFwdWs {
   PlanBufs plan;
   uint32_t* bits;
   u16* vt;
+  u16* kop;
 };
 QsaFwdWs carve_qsa_fwd(Carver& c, const Sizes& z) {
   QsaFwdWs w;
   w.plan = carve_plan(c, z);
   w.bits = c.take<uint32_t>(z.T * z.Hk * msa::kQsaWords);
   w.vt = c.take<u16>(z.nblk_cap * z.Hk * msa::kQsaKeyTile * msa::kQsaHeadDim);
+  w.kop = c.take<u16>(z.nblk_cap * z.Hk * msa::kQsaKeyTile * msa::kQsaHeadDim);
   return w;
 }
 
 struct QsaBwdWs {
   PlanBufs plan;
   uint32_t* bits;
+  u16* kop;
+  u16* vop;
   float* delta;
   float* nlse;
   int32_t* item_count;
@@ -215,6 +219,8 @@ QsaBwdWs carve_qsa_bwd(Carver& c, const Sizes& z) {
   QsaBwdWs w;
   w.plan = carve_plan(c, z);
   w.bits = c.take<uint32_t>(z.T * z.Hk * msa::kQsaWords);
+  w.kop = c.take<u16>(z.nblk_cap * z.Hk * msa::kQsaKeyTile * msa::kQsaHeadDim);
+  w.vop = c.take<u16>(z.nblk_cap * z.Hk * msa::kQsaKeyTile * msa::kQsaHeadDim);
   w.delta = c.take<float>(z.T * z.Hk * 16);
   w.nlse = c.take<float>(z.T * z.Hk * 16);
   w.item_count = c.take<int32_t>(z.Hk * z.items_cap);
@@ -458,6 +464,7 @@ int msa_qsa_attn_fwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t 
   a.out_lse = lse;
   a.bits = w.bits;
   a.vt = w.vt;
+  a.kop = w.kop;
   msa::launch_plan(cu_seqlens, z, w.plan, stream, msa::kQsaKeyTile);
   msa::launch_qsa_fwd(z, a, w.plan, stream);
   return launch_status();
@@ -499,6 +506,8 @@ int msa_qsa_attn_bwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t 
   a.dk = (u16*)dk; a.dk_st = dk_st; a.dk_sh = dk_sh;
   a.dv = (u16*)dv; a.dv_st = dv_st; a.dv_sh = dv_sh;
   a.bits = w.bits;
+  a.kop = w.kop;
+  a.vop = w.vop;
   a.delta = w.delta;
   a.nlse = w.nlse;
   a.item_count = w.item_count;

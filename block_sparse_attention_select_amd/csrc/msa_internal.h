@@ -278,6 +278,8 @@ struct QsaArgs {
   // workspace
   uint32_t* bits;     // [T][Hk][kQsaWords] selected-block bitmaps
   u16* vt;            // [key tiles][Hk][32 runs][64 lanes][8] V^T in MFMA operand order (forward)
+  u16* kop;           // the same shape: K in the forward's (or, backward, the dQ pass's swizzled) stage order
+  u16* vop;           // V in the dQ pass's swizzled stage order (backward)
   float* delta;       // [T][Hk][16] (heads past 12 zero)
   float* nlse;        // [T][Hk][16] -LSE * log2(e) (-inf for heads past 12 and empty rows)
   int32_t* item_count;  // [Hk][items_cap]

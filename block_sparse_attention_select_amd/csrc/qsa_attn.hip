@@ -118,6 +118,44 @@ __global__ __launch_bounds__(256) void qsa_vt_kernel(const u16* __restrict__ v, 
 }
 
 // ---------------------------------------------------------------------------
+// Copies of K (and V) per (key tile, KV head) in the stage order of the
+// forward (K, plain) or the dQ pass (K and V, swizzled), so every staged 1 KB
+// run is one contiguous copy: run kt*8 + ds, slot l holding x[key
+// score_key(kt, r)][dims 32 ds + 8 (l / 16) .. +7] with r = l % 16 (plain) or
+// swz_slot(l) % 16 (swizzled); zero past the sequence end.  blockIdx.z: tensor
+// z / 4 of {K, V}, a quarter of the runs each.
+// ---------------------------------------------------------------------------
+template <bool kSwizzled>
+__global__ __launch_bounds__(256) void qsa_prep_kernel(const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
+                                                       const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
+                                                       const int32_t* __restrict__ cu,
+                                                       const int32_t* __restrict__ ktbase,
+                                                       const int32_t* __restrict__ kt_seq,
+                                                       const int32_t* __restrict__ totals, int Hk,
+                                                       u16* __restrict__ kop, u16* __restrict__ vop) {
+  const int gk = blockIdx.x, h = blockIdx.y;
+  if (gk >= totals[0]) return;
+  const bool is_v = blockIdx.z >= 4;
+  const int part = blockIdx.z & 3;
+  const u16* x = is_v ? v : k;
+  const int64_t st_t = is_v ? v_st : k_st, st_h = is_v ? v_sh : k_sh;
+  const int s = kt_seq[gk];
+  const int c = gk - ktbase[s];
+  const int seq0 = cu[s], L = cu[s + 1] - seq0;
+  u16* dst = (is_v ? vop : kop) + ((int64_t)gk * Hk + h) * (32 * 64 * 8);
+  for (int i = 512 * part + threadIdx.x; i < 512 * part + 512; i += 256) {
+    const int run = i >> 6, ln = i & 63;
+    const int r = kSwizzled ? (swz_slot(ln) & 15) : (ln & 15);
+    const int kp = kKT * c + score_key(run >> 3, r);
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (kp < L)
+      val = *reinterpret_cast<const u32x4*>(x + (int64_t)(seq0 + kp) * st_t + (int64_t)h * st_h + 32 * (run & 7) +
+                                            8 * (ln >> 4));
+    *reinterpret_cast<u32x4*>(dst + (int64_t)i * 8) = val;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Shared prologue of the token-major passes: the tile's 8 tokens' bitmap rows
 // into LDS and the ascending union of the global key tiles they touch.
 // ---------------------------------------------------------------------------
@@ -125,7 +163,6 @@ struct TileUnion {
   uint32_t bmap[kTok][kWords];
   uint32_t ubits[kUnionWords];
   int ulist[kUnionMax];
-  int ukey0[kUnionMax];  // first token of each union key tile
   int nunion;
 };
 
@@ -167,20 +204,13 @@ __device__ __forceinline__ void build_union(TileUnion& tu, const uint32_t* __res
     if (lane == 63) tu.nunion = incl;
   }
   __syncthreads();
-  // first token of every union key tile, one entry per thread (independent loads)
-  for (int i = threadIdx.x; i < tu.nunion; i += blockDim.x) {
-    const int gk = tu.ulist[i];
-    const int sb = kt_seq[gk];
-    tu.ukey0[i] = cu[sb] + kKT * (gk - ktbase[sb]);
-  }
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
 // Forward.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64 * kTok) void qsa_fwd_kernel(
-    const u16* __restrict__ q, int64_t q_st, int64_t q_sh, const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
+    const u16* __restrict__ q, int64_t q_st, int64_t q_sh, const u16* __restrict__ kop,
     const u16* __restrict__ vt, const uint32_t* __restrict__ bits, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ ktbase, const int32_t* __restrict__ kt_seq, const int32_t* __restrict__ tile_order,
     int S, int T, int Hk, float scale_log2, u16* __restrict__ o, int64_t o_st, int64_t o_sh,
@@ -232,21 +262,10 @@ __global__ __launch_bounds__(64 * kTok) void qsa_fwd_kernel(
   // w / 2, dims 128 (w % 2) + 32 ii ..) and V^T runs 4w .. 4w+3
   auto stage = [&](int u, int buf) {
     const int gk = __builtin_amdgcn_readfirstlane(tu.ulist[u]);
-    const int kstart = __builtin_amdgcn_readfirstlane(tu.ukey0[u]);
     const int ln = fresh_lane();
-    const int key = score_key(wave >> 1, ln & 15);
-    const int d0 = 128 * (wave & 1) + 8 * (ln >> 4);
-    if (kstart + kKT <= T) {
-      const u16* base = k + (int64_t)kstart * k_st + (int64_t)h * k_sh + 128 * (wave & 1);
-      const uint32_t off = (uint32_t)(2 * (key * k_st + 8 * (ln >> 4)));
+    const u16* kbase = kop + (((int64_t)gk * Hk + h) * 32 + 4 * wave) * 512;
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) dma16s(base + 32 * ii, off, lds_offset(&kbuf[buf][4 * wave + ii][0]));
-    } else {  // the pack's last key tile: keys past the end repeat the last token
-      const int kk = min(kstart + key, T - 1);
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        dma16(k + (int64_t)kk * k_st + (int64_t)h * k_sh + d0 + 32 * ii, lds_offset(&kbuf[buf][4 * wave + ii][0]));
-    }
+    for (int ii = 0; ii < 4; ++ii) dma16s(kbase + 512 * ii, 16 * ln, lds_offset(&kbuf[buf][4 * wave + ii][0]));
     const u16* vbase = vt + (((int64_t)gk * Hk + h) * 32 + 4 * wave) * 512;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) dma16s(vbase + 512 * ii, 16 * ln, lds_offset(&vbuf[buf][4 * wave + ii][0]));
@@ -358,8 +377,8 @@ __global__ __launch_bounds__(64 * kTok) void qsa_fwd_kernel(
 // dQ (and Delta, -LSE log2 e for the dK/dV pass).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64 * kTok) void qsa_dq_kernel(
-    const u16* __restrict__ q, int64_t q_st, int64_t q_sh, const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
-    const u16* __restrict__ v, int64_t v_st, int64_t v_sh, const u16* __restrict__ o, int64_t o_st, int64_t o_sh,
+    const u16* __restrict__ q, int64_t q_st, int64_t q_sh, const u16* __restrict__ kop,
+    const u16* __restrict__ vop, const u16* __restrict__ o, int64_t o_st, int64_t o_sh,
     const u16* __restrict__ dO, int64_t do_st, int64_t do_sh, const float* __restrict__ lse,
     const uint32_t* __restrict__ bits, const int32_t* __restrict__ cu, const int32_t* __restrict__ ktbase,
     const int32_t* __restrict__ kt_seq, const int32_t* __restrict__ tile_order, int S, int T, int Hk,
@@ -428,27 +447,13 @@ __global__ __launch_bounds__(64 * kTok) void qsa_dq_kernel(
   // staging of union step u: wavefront w copies K runs 4w .. 4w+3 and the same
   // V runs (key tile w / 2, dims 128 (w % 2) + 32 ii ..)
   auto stage = [&](int u, int buf) {
-    const int kstart = __builtin_amdgcn_readfirstlane(tu.ukey0[u]);
+    const int gk = __builtin_amdgcn_readfirstlane(tu.ulist[u]);
     const int ln = fresh_lane();
-    const int key = score_key(wave >> 1, swz_slot(ln) & 15);  // runs stored swizzled
-    const int d0 = 128 * (wave & 1) + 8 * (ln >> 4);
-    if (kstart + kKT <= T) {
-      const u16* kb = k + (int64_t)kstart * k_st + (int64_t)h * k_sh + 128 * (wave & 1);
-      const u16* vb = v + (int64_t)kstart * v_st + (int64_t)h * v_sh + 128 * (wave & 1);
-      const uint32_t koff = (uint32_t)(2 * (key * k_st + 8 * (ln >> 4)));
-      const uint32_t voff = (uint32_t)(2 * (key * v_st + 8 * (ln >> 4)));
+    const int64_t run0 = (((int64_t)gk * Hk + h) * 32 + 4 * wave) * 512;
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        dma16s(kb + 32 * ii, koff, lds_offset(&kbuf[buf][4 * wave + ii][0]));
-        dma16s(vb + 32 * ii, voff, lds_offset(&vbuf[buf][4 * wave + ii][0]));
-      }
-    } else {
-      const int kk = min(kstart + key, T - 1);
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        dma16(k + (int64_t)kk * k_st + (int64_t)h * k_sh + d0 + 32 * ii, lds_offset(&kbuf[buf][4 * wave + ii][0]));
-        dma16(v + (int64_t)kk * v_st + (int64_t)h * v_sh + d0 + 32 * ii, lds_offset(&vbuf[buf][4 * wave + ii][0]));
-      }
+    for (int ii = 0; ii < 4; ++ii) {
+      dma16s(kop + run0 + 512 * ii, 16 * ln, lds_offset(&kbuf[buf][4 * wave + ii][0]));
+      dma16s(vop + run0 + 512 * ii, 16 * ln, lds_offset(&vbuf[buf][4 * wave + ii][0]));
     }
   };
   if (nu > 0) stage(0, 0);
@@ -831,19 +836,26 @@ void launch_qsa_fwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStre
     KernelTimer timer("qsa_vt", st);
     qsa_vt_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk), 256, 0, st>>>(
         a.v, a.v_st, a.v_sh, a.cu, p.blkbase, p.blk_seq, p.totals, (int)z.Hk, a.vt);
+    qsa_prep_kernel<false><<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk, 4), 256, 0, st>>>(
+        a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.cu, p.blkbase, p.blk_seq, p.totals, (int)z.Hk, a.kop, nullptr);
   }
   KernelTimer timer("qsa_fwd", st);
   qsa_fwd_kernel<<<(unsigned)(2 * z.ntiles * z.Hk), 64 * kTok, 0, st>>>(
-      a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.vt, a.bits, a.cu, p.blkbase, p.blk_seq, p.tile_order, (int)z.S,
+      a.q, a.q_st, a.q_sh, a.kop, a.vt, a.bits, a.cu, p.blkbase, p.blk_seq, p.tile_order, (int)z.S,
       (int)z.T, (int)z.Hk, a.scale * kLog2e, a.out_o, a.oo_st, a.oo_sh, a.out_lse);
 }
 
 void launch_qsa_bwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStream_t st) {
   launch_bitmaps(z, a, st);
   {
+    KernelTimer timer("qsa_prep", st);
+    qsa_prep_kernel<true><<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk, 8), 256, 0, st>>>(
+        a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.cu, p.blkbase, p.blk_seq, p.totals, (int)z.Hk, a.kop, a.vop);
+  }
+  {
     KernelTimer timer("qsa_dq", st);
     qsa_dq_kernel<<<(unsigned)(2 * z.ntiles * z.Hk), 64 * kTok, 0, st>>>(
-        a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.o, a.o_st, a.o_sh, a.dO, a.do_st, a.do_sh,
+        a.q, a.q_st, a.q_sh, a.kop, a.vop, a.o, a.o_st, a.o_sh, a.dO, a.do_st, a.do_sh,
         a.lse, a.bits, a.cu, p.blkbase, p.blk_seq, p.tile_order, (int)z.S, (int)z.T, (int)z.Hk, a.scale * kLog2e,
         a.scale, a.dq, a.dq_st, a.dq_sh, a.delta, a.nlse);
   }
