@@ -50,9 +50,16 @@ __global__ __launch_bounds__(256) void bwd_block_prep_kernel(const u16* __restri
                                                              const int32_t* __restrict__ blkbase,
                                                              const int32_t* __restrict__ blk_seq,
                                                              const int32_t* __restrict__ totals, int Hk,
-                                                             u16* __restrict__ kop, u16* __restrict__ vop) {
+                                                             u16* __restrict__ kop, u16* __restrict__ vop,
+                                                             int32_t* __restrict__ clear, int nclear) {
   const int gb = blockIdx.x;
   const int h = blockIdx.y;
+  // zero the dK/dV item-load counters the dQ pass accumulates
+  {
+    const int wg = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    const int nwg = gridDim.x * gridDim.y * gridDim.z;
+    for (int i = wg * 256 + threadIdx.x; i < nclear; i += nwg * 256) clear[i] = 0;
+  }
   if (gb >= totals[0]) return;
   const bool is_v = blockIdx.z >= 4;
   const int part = blockIdx.z & 3;  // runs 8 part .. 8 part + 7
@@ -89,7 +96,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     const int32_t* __restrict__ blk_seq, const int32_t* __restrict__ tile_order, int S, int T, int Hk,
     float scale_log2, float scale,
     u16* __restrict__ dq, int64_t dq_st, int64_t dq_sh, float* __restrict__ delta, float* __restrict__ nlse,
-    int32_t* __restrict__ clear, int nclear) {
+    const int32_t* __restrict__ seqitem, int chunk, int items_cap, int32_t* __restrict__ item_load) {
   __shared__ u32x4 kbuf[2][32][64];
   __shared__ u32x4 vbuf[2][32][64];
   __shared__ uint32_t bitmap[kUnionWords];
@@ -101,8 +108,6 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
   // workgroup b runs KV head b % Hk of the tile in launch slot b / Hk
   const int h = blockIdx.x % Hk;
   const int t0 = tile_order[blockIdx.x / Hk] * kTileTok;
-  // zero the dK/dV item-load counters for the pass that follows
-  for (int i = blockIdx.x * 64 * kDqWaves + threadIdx.x; i < nclear; i += gridDim.x * 64 * kDqWaves) clear[i] = 0;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
@@ -123,6 +128,16 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     }
   }
   const int gb_lo = blkbase[find_seq(cu, S, t0)];
+  // launch order of the dK/dV pass: count this token's selection of its block
+  // toward work item (sequence, query chunk, block); the counters were zeroed
+  // by the preceding prep kernel
+  if constexpr (!kDense) {
+    if (g < kTokPerWave && my_gb >= 0) {
+      const int j = pos_t / chunk;
+      const int item = seqitem[s_t] + (chunk / kBlock) * (j * (j + 1) / 2) + (my_gb - blkbase[s_t]);
+      atomicAdd(&item_load[(int64_t)h * items_cap + item], 1);
+    }
+  }
 
   // the token's q, dO, Delta and LSE, before the union build so the loads overlap it
   int tok_t[kTokPerWave], tok_pos[kTokPerWave], tok_b[kTokPerWave], tok_base[kTokPerWave];
@@ -378,7 +393,8 @@ void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStr
   {
     KernelTimer timer("bwd_block_prep", st);
     bwd_block_prep_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)Hk, 8), 256, 0, st>>>(
-        a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.cu, p.blkbase, p.blk_seq, p.totals, Hk, a.kop, a.vop);
+        a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.cu, p.blkbase, p.blk_seq, p.totals, Hk, a.kop, a.vop,
+        a.item_load, (int)(z.Hk * z.items_cap));
   }
   {
     KernelTimer timer("attn_bwd_dq", st);
@@ -387,7 +403,7 @@ void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStr
         a.q, a.q_st, a.q_sh, a.kop, a.vop, a.o, a.o_st, a.o_sh, a.dO, a.do_st,
         a.do_sh, a.lse, a.blk_idx, a.cu, p.blkbase, p.blk_seq, p.tile_order, S, T, Hk, a.scale * kLog2e, a.scale,
         a.dq, a.dq_st,
-        a.dq_sh, a.delta, a.nlse, a.item_load, (int)(z.Hk * z.items_cap));
+        a.dq_sh, a.delta, a.nlse, p.seqitem, (int)z.chunk, (int)z.items_cap, a.item_load);
   }
   launch_attn_bwd_dkdv(z, a, p, st);
   {

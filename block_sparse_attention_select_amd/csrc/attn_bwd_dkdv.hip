@@ -326,62 +326,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // are selected by most of its queries, far blocks by few), and in index order
 // the heavy ones of the last sequence would run last.  The items are instead
 // launched by decreasing number of selecting queries (longest job first), which
-// only changes when each item runs, not what it computes.  The counters are
-// zeroed by the dQ pass that precedes this one.
+// only changes when each item runs, not what it computes.  For sparse layers
+// the counters are zeroed by the backward prep kernel and filled by the dQ
+// pass (one count per selecting query, head and block); the item of query
+// chunk j of sequence s and its block c has index seqitem[s] +
+// (chunk / kBlock) * j * (j + 1) / 2 + c.
 // ---------------------------------------------------------------------------
-// One workgroup per (256 consecutive tokens, KV head), a thread per token.
-// The items those tokens can touch form one contiguous index range (items are
-// ordered by sequence, chunk, block), so the counts are gathered in an LDS
-// histogram over that range and added to the global counts once per item.
-constexpr int kLoadSpan = 4096;
-__device__ __forceinline__ int item_base(const int32_t* seqitem, int s, int j, int chunk) {
-  return seqitem[s] + (chunk / kBlock) * (j * (j + 1) / 2);
-}
-__global__ __launch_bounds__(256) void dkdv_load_count_kernel(
-    const int32_t* __restrict__ blk_idx, const int32_t* __restrict__ cu, const int32_t* __restrict__ seqitem,
-    int S, int T, int Hk, int chunk, int items_cap, int32_t* __restrict__ load) {
-  __shared__ int hist[kLoadSpan];
-  const int h = blockIdx.y;
-  const int t0 = blockIdx.x * 256;
-  const int tB = min(t0 + 255, T - 1);
-  const int sA = find_seq(cu, S, t0), sB = find_seq(cu, S, tB);
-  const int jA = (t0 - cu[sA]) / chunk, jB = (tB - cu[sB]) / chunk;
-  const int LB = cu[sB + 1] - cu[sB];
-  const int lo = item_base(seqitem, sA, jA, chunk);
-  const int hi = item_base(seqitem, sB, jB, chunk) + (min((jB + 1) * chunk, LB) - 1) / kBlock + 1;
-  const bool in_lds = hi - lo <= kLoadSpan;
-  int32_t* gl = load + (int64_t)h * items_cap;
-  if (in_lds)
-    for (int i = threadIdx.x; i < hi - lo; i += 256) hist[i] = 0;
-  __syncthreads();
-  const int t = t0 + threadIdx.x;
-  if (t < T) {
-    const int s = find_seq(cu, S, t);
-    const int p = t - cu[s];
-    const int j = p / chunk;
-    const int base = item_base(seqitem, s, j, chunk);
-    const int4* ids = reinterpret_cast<const int4*>(blk_idx + ((int64_t)t * Hk + h) * kTopk);
-#pragma unroll
-    for (int q4 = 0; q4 < kTopk / 4; ++q4) {
-      const int4 x = ids[q4];
-      const int cs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = cs[e];
-        if (c < 0 || c > p / kBlock) continue;
-        if (in_lds)
-          atomicAdd(&hist[base + c - lo], 1);
-        else
-          atomicAdd(&gl[base + c], 1);
-      }
-    }
-  }
-  __syncthreads();
-  if (in_lds)
-    for (int i = threadIdx.x; i < hi - lo; i += 256)
-      if (hist[i] != 0) atomicAdd(&gl[lo + i], hist[i]);
-}
-
 // Dense layers: item (s, j, c) is selected by every query of chunk j at or
 // after block c's first key.
 __global__ __launch_bounds__(256) void dkdv_dense_load_kernel(const int32_t* __restrict__ cu,
@@ -454,12 +404,10 @@ __global__ __launch_bounds__(1024) void dkdv_order_kernel(const int32_t* __restr
 void launch_attn_bwd_dkdv(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStream_t st) {
   {
     KernelTimer timer("dkdv_order", st);
+    // sparse: the dQ pass counted the selections per item; dense: a closed form
     if (a.dense)
       dkdv_dense_load_kernel<<<dim3((unsigned)((z.items_cap + 255) / 256), (unsigned)z.Hk), 256, 0, st>>>(
           a.cu, p.seqitem, p.totals, (int)z.S, (int)z.chunk, (int)z.items_cap, a.item_load);
-    else if (z.T > 0)
-      dkdv_load_count_kernel<<<dim3((unsigned)((z.T + 255) / 256), (unsigned)z.Hk), 256, 0, st>>>(
-          a.blk_idx, a.cu, p.seqitem, (int)z.S, (int)z.T, (int)z.Hk, (int)z.chunk, (int)z.items_cap, a.item_load);
     dkdv_order_kernel<<<(unsigned)z.Hk, 1024, 0, st>>>(a.item_load, p.totals, (int)z.items_cap, a.item_order);
   }
   KernelTimer timer("attn_bwd_dkdv", st);
