@@ -329,7 +329,6 @@ int msa_index_select_ex(const msa_dims* dims, const void* idx_q, int64_t sq_t, i
   if (st != MSA_OK) return st;
   Carver c(workspace);
   SelectWs w = carve_select(c, z);
-  msa::launch_plan(cu_seqlens, z, w.plan, stream, msa::kBlock, /*tiles=*/false);
   msa::launch_select(z, (const u16*)idx_q, sq_t, sq_h, (const u16*)idx_k, sk_t, sk_h, (const u16*)w_q,
                      (const u16*)w_k, eps, rope_base, cu_seqlens, w.plan, (flags & MSA_SELECT_FORCE_INIT) != 0,
                      w.qfeat, w.kfeat, w.scores, blk_idx, stream);

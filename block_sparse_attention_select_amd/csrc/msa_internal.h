@@ -2,6 +2,7 @@
 // kernels, the workspace layout and the host-side launchers.  gfx950 only.
 #pragma once
 
+#include <cmath>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -89,6 +90,27 @@ __device__ __forceinline__ uint2 pack_bf16x4(f32x4 v) {
 }
 
 // Largest s in [0, S) with cu[s] <= t (the sequence holding token t).
+// RoPE inverse frequencies base^(-2i/64) of the 32 rotated pairs, computed
+// once on the host in fp64 and passed by value to the kernels that rotate
+struct RopeFreqs {
+  double f[32];
+};
+inline RopeFreqs rope_freqs(float rope_base) {
+  RopeFreqs r;
+  for (int i = 0; i < 32; ++i) r.f[i] = std::pow((double)rope_base, -(double)(2 * i) / 64.0);
+  return r;
+}
+
+// frequency of pair `lane` (lanes >= 32 get pair 0's, unused): a select
+// chain over scalar registers, so the by-value table is never indexed
+// per lane (which would put it in scratch memory)
+__device__ __forceinline__ double rope_freq_of(const RopeFreqs& fr, int lane) {
+  double f = fr.f[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) f = lane == i ? fr.f[i] : f;
+  return f;
+}
+
 __device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int S, int t) {
   int lo = 0, hi = S;
   while (hi - lo > 1) {

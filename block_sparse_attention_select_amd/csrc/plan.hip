@@ -23,7 +23,7 @@
 // long tiles first (longest-processing-time order) keeps the last wave of
 // workgroups short.  Tiles of equal key may come in any order; the order only
 // decides which workgroup runs when, never what any of them computes.
-#include "msa_internal.h"
+#include "plan_blocks.h"
 
 namespace msa {
 
@@ -31,11 +31,6 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 constexpr int kOrderBins = 1024;  // position keys: one per 128-token block (131072 tokens)
-
-template <int kUnit>
-__device__ __forceinline__ int chunk_items(int L, int chunk, int j) {
-  return (min((j + 1) * chunk, L) - 1) / kUnit + 1;
-}
 
 constexpr int kCuCache = 4097;      // cu_seqlens entries held in LDS for the tile keys
 constexpr int kKeysPerThread = 8;    // tile keys kept in registers between the two passes
@@ -59,45 +54,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   __shared__ int hist[kOrderBins];
   __shared__ int scu[kCuCache];
   const int tid = threadIdx.x;
-  int carry_b = 0, carry_i = 0;
-  if (tid == 0) {
-    blkbase[0] = 0;
-    seqitem[0] = 0;
-  }
-  for (int base = 0; base < S; base += kPlanThreads) {
-    const int s = base + tid;
-    int L = 0, nb = 0, ni = 0;
-    if (s < S) {
-      L = cu[s + 1] - cu[s];
-      nb = (L + kUnit - 1) / kUnit;
-      const int nch = (L + chunk - 1) / chunk;
-      for (int j = 0; j < nch; ++j) ni += chunk_items<kUnit>(L, chunk, j);
-    }
-    sb[tid] = nb;
-    si[tid] = ni;
-    __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive Hillis-Steele scan
-      int a = tid >= off ? sb[tid - off] : 0;
-      int b = tid >= off ? si[tid - off] : 0;
-      __syncthreads();
-      sb[tid] += a;
-      si[tid] += b;
-      __syncthreads();
-    }
-    if (s < S) {
-      const int b0 = carry_b + sb[tid] - nb;
-      blkbase[s + 1] = b0 + nb;
-      seqitem[s + 1] = carry_i + si[tid];
-      for (int c = 0; c < nb; ++c) blk_seq[b0 + c] = s;
-    }
-    carry_b += sb[kPlanThreads - 1];
-    carry_i += si[kPlanThreads - 1];
-    __syncthreads();
-  }
-  if (tid == 0) {
-    totals[0] = carry_b;
-    totals[1] = carry_i;
-  }
+  plan_blocks<kPlanThreads, kUnit>(cu, S, chunk, blkbase, blk_seq, seqitem, totals, sb, si);
 
   // tile launch order: counting sort on the position key, largest key first
   // (ntiles = 0: the caller needs no tile order)

@@ -33,13 +33,12 @@ namespace {
 constexpr int kQkWaves = 4;
 
 // cos / sin of this lane's RoPE pair at position pos (lanes >= 32: identity)
-__device__ __forceinline__ void rope_angles(int lane, int pos, float rope_base, float& c, float& s) {
+__device__ __forceinline__ void rope_angles(int lane, int pos, const RopeFreqs& fr, float& c, float& s) {
   c = 1.f;
   s = 0.f;
   if (lane < 32) {
-    const double inv_freq = pow((double)rope_base, -(double)(2 * lane) / 64.0);
     double sn, cs;
-    sincos((double)pos * inv_freq, &sn, &cs);
+    sincos((double)pos * rope_freq_of(fr, lane), &sn, &cs);
     c = (float)cs;
     s = (float)sn;
   }
@@ -47,7 +46,7 @@ __device__ __forceinline__ void rope_angles(int lane, int pos, float rope_base, 
 
 __global__ __launch_bounds__(64 * kQkWaves) void qk_norm_rope_fwd_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh, const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
-    const u16* __restrict__ w_q, const u16* __restrict__ w_k, float eps, float rope_base,
+    const u16* __restrict__ w_q, const u16* __restrict__ w_k, float eps, RopeFreqs fr,
     const int32_t* __restrict__ cu, int S, int T, int Hq, int Hk, u16* __restrict__ qo, int64_t qo_st,
     int64_t qo_sh, u16* __restrict__ ko, int64_t ko_st, int64_t ko_sh) {
 #pragma clang fp contract(off)
@@ -56,7 +55,7 @@ __global__ __launch_bounds__(64 * kQkWaves) void qk_norm_rope_fwd_kernel(
   if (t >= T) return;
   const int s = find_seq(cu, S, t);
   float c, sn;
-  rope_angles(lane, t - cu[s], rope_base, c, sn);
+  rope_angles(lane, t - cu[s], fr, c, sn);
   const int d0 = lane < 32 ? lane : 32 + lane;
   const int d1 = d0 + 32;
   for (int hh = 0; hh < Hq + Hk; ++hh) {
@@ -89,7 +88,7 @@ __global__ __launch_bounds__(64 * kQkWaves) void qk_norm_rope_fwd_kernel(
 // (q: dims 0..127, k: 128..255).
 __global__ __launch_bounds__(64 * kQkWaves) void qk_norm_rope_bwd_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh, const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
-    const u16* __restrict__ w_q, const u16* __restrict__ w_k, float eps, float rope_base,
+    const u16* __restrict__ w_q, const u16* __restrict__ w_k, float eps, RopeFreqs fr,
     const int32_t* __restrict__ cu, int S, int T, int Hq, int Hk,
     const u16* __restrict__ dqh, int64_t dqh_st, int64_t dqh_sh, const u16* __restrict__ dkh, int64_t dkh_st,
     int64_t dkh_sh, u16* __restrict__ dq, int64_t dq_st, int64_t dq_sh, u16* __restrict__ dk, int64_t dk_st,
@@ -105,7 +104,7 @@ __global__ __launch_bounds__(64 * kQkWaves) void qk_norm_rope_bwd_kernel(
   for (int t = blockIdx.x * kQkWaves + wave; t < T; t += gridDim.x * kQkWaves) {
     const int s = find_seq(cu, S, t);
     float c, sn;
-    rope_angles(lane, t - cu[s], rope_base, c, sn);
+    rope_angles(lane, t - cu[s], fr, c, sn);
     for (int hh = 0; hh < Hq + Hk; ++hh) {
       const bool isq = hh < Hq;
       const int h = isq ? hh : hh - Hq;
@@ -193,7 +192,7 @@ int qk_norm_bwd_rows(int64_t T) {
 void launch_qk_norm_fwd(const Sizes& z, const QkNormArgs& a, hipStream_t st) {
   KernelTimer timer("qk_norm_rope_fwd", st);
   qk_norm_rope_fwd_kernel<<<(unsigned)((z.T + kQkWaves - 1) / kQkWaves), 64 * kQkWaves, 0, st>>>(
-      a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.w_q, a.w_k, a.eps, a.rope_base, a.cu, (int)z.S, (int)z.T,
+      a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.w_q, a.w_k, a.eps, rope_freqs(a.rope_base), a.cu, (int)z.S, (int)z.T,
       (int)z.Hq, (int)z.Hk, a.qo, a.qo_st, a.qo_sh, a.ko, a.ko_st, a.ko_sh);
 }
 
@@ -202,7 +201,7 @@ void launch_qk_norm_bwd(const Sizes& z, const QkNormArgs& a, float* partial, hip
   if (rows > 0) {
     KernelTimer timer("qk_norm_rope_bwd", st);
     qk_norm_rope_bwd_kernel<<<(unsigned)rows, 64 * kQkWaves, 0, st>>>(
-        a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.w_q, a.w_k, a.eps, a.rope_base, a.cu, (int)z.S, (int)z.T,
+        a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.w_q, a.w_k, a.eps, rope_freqs(a.rope_base), a.cu, (int)z.S, (int)z.T,
         (int)z.Hq, (int)z.Hk, a.dqh, a.dqh_st, a.dqh_sh, a.dkh, a.dkh_st, a.dkh_sh, a.qo, a.qo_st, a.qo_sh, a.ko,
         a.ko_st, a.ko_sh, partial);
   }

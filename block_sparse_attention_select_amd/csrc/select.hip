@@ -10,69 +10,99 @@
 //   3. selection: blocks 0..b when b < 16, else the own block b plus the 15
 //      best of 0..b-1 (lower id first on equal scores), written ascending.
 //
-// Kernels: select_prologue (features), select_scores (MFMA + per-row block
-// maximum), select_topk (wavefront arg-max rounds).
+// Kernels: select_prologue (features, and the pack's block numbering),
+// select_scores (MFMA + per-row block maximum), select_topk (ranking).
 #include "attn_stage.h"
+#include "plan_blocks.h"
 
 namespace msa {
 
 namespace {
 
 // ---------------------------------------------------------------------------
-// 1. Features.  One wavefront per token: the RoPE angles of its position are
-// computed once (fp64, rounded to fp32) and applied to the q and k features of
-// every head.  Lane l < 32 holds the RoPE pair (l, l + 32); lane l >= 32 holds
-// dims 32 + l and 64 + l.  The arithmetic order (square, sum, scale by 1/128,
-// add eps, sqrt, divide, multiply by x, multiply by (1 + w); rotation as two
-// products and one sum) is kept free of fused multiply-adds so every step
-// rounds once in fp32.
+// 1. Features.  One wavefront per kProTok consecutive tokens.  Lane l < 32
+// holds the RoPE pair (l, l + 32) of a token, lane l >= 32 dims 32 + l and
+// 64 + l.  The RoPE angles (fp64 from the host's fp64 inverse frequencies,
+// rounded to fp32) are formed for two tokens at a time, lane l for pair l % 32
+// of token l / 32, and token 1's are then swapped into lanes 0..31.  Every
+// head's inputs are loaded before the position lookup and the angles.  The
+// arithmetic order (square, sum, scale by 1/128, add eps, sqrt, divide,
+// multiply by x, multiply by (1 + w); rotation as two products and one sum) is
+// kept free of fused multiply-adds so every step rounds once in fp32.
+// The launch has one more workgroup, which numbers the pack's blocks for the
+// scoring kernel (plan_blocks).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void select_prologue_kernel(
+constexpr int kProTok = 4;
+constexpr int kProWaves = 4;
+
+__global__ __launch_bounds__(64 * kProWaves) void select_prologue_kernel(
     const u16* __restrict__ idx_q, int64_t sq_t, int64_t sq_h,
     const u16* __restrict__ idx_k, int64_t sk_t, int64_t sk_h,
-    const u16* __restrict__ w_q, const u16* __restrict__ w_k, float eps, float rope_base,
-    const int32_t* __restrict__ cu, int S, int T, int Hk,
+    const u16* __restrict__ w_q, const u16* __restrict__ w_k, float eps, RopeFreqs fr,
+    const int32_t* __restrict__ cu, int S, int T, int Hk, int chunk, PlanBufs plan,
     u16* __restrict__ qfeat, u16* __restrict__ kfeat) {
 #pragma clang fp contract(off)
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blockIdx.x == gridDim.x - 1) {
+    __shared__ int sb[64 * kProWaves], si[64 * kProWaves];
+    plan_blocks<64 * kProWaves, kBlock>(cu, S, chunk, plan.blkbase, plan.blk_seq, plan.seqitem, plan.totals, sb, si);
+    return;
+  }
+  const int t0 = (blockIdx.x * kProWaves + (threadIdx.x >> 6)) * kProTok;
   const int lane = threadIdx.x & 63;
-  if (t >= T) return;
-  const int s = find_seq(cu, S, t);
-  const int pos = t - cu[s];
+  if (t0 >= T) return;
   const int d0 = lane < 32 ? lane : 32 + lane;
   const int d1 = d0 + 32;
-  float c = 1.f, sf = 0.f;
-  if (lane < 32) {
-    const double inv_freq = pow((double)rope_base, -(double)(2 * lane) / 64.0);
-    const double theta = (double)pos * inv_freq;
-    double sn, cs;
-    sincos(theta, &sn, &cs);
-    c = (float)cs;
-    sf = (float)sn;
-  }
+  const float wq0 = 1.0f + bf2f(w_q[d0]), wq1 = 1.0f + bf2f(w_q[d1]);
+  const float wk0 = 1.0f + bf2f(w_k[d0]), wk1 = 1.0f + bf2f(w_k[d1]);
+  float c[kProTok], sf[kProTok];
   for (int h = 0; h < Hk; ++h) {
+    float x[kProTok][2][2];
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
-      const u16* x = which ? idx_k + (int64_t)t * sk_t + (int64_t)h * sk_h
-                           : idx_q + (int64_t)t * sq_t + (int64_t)h * sq_h;
-      const u16* w = which ? w_k : w_q;
-      u16* out = (which ? kfeat : qfeat) + ((int64_t)t * Hk + h) * kHeadDim;
-      const float x0 = bf2f(x[d0]);
-      const float x1 = bf2f(x[d1]);
-      float ss = x0 * x0 + x1 * x1;
-      for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
-      const float ms = ss * (1.0f / 128.0f);
-      const float r = 1.0f / sqrtf(ms + eps);
-      float y0 = (x0 * r) * (1.0f + bf2f(w[d0]));
-      float y1 = (x1 * r) * (1.0f + bf2f(w[d1]));
-      if (lane < 32) {
-        const float o0 = (y0 * c) - (y1 * sf);
-        const float o1 = (y1 * c) + (y0 * sf);
-        y0 = o0;
-        y1 = o1;
+    for (int tt = 0; tt < kProTok; ++tt) {
+      const int t = min(t0 + tt, T - 1);
+      const u16* xq = idx_q + (int64_t)t * sq_t + (int64_t)h * sq_h;
+      const u16* xk = idx_k + (int64_t)t * sk_t + (int64_t)h * sk_h;
+      x[tt][0][0] = bf2f(xq[d0]);
+      x[tt][0][1] = bf2f(xq[d1]);
+      x[tt][1][0] = bf2f(xk[d0]);
+      x[tt][1][1] = bf2f(xk[d1]);
+    }
+    if (h == 0) {
+#pragma unroll
+      for (int rr = 0; rr < kProTok / 2; ++rr) {
+        const int t = min(t0 + 2 * rr + (lane >> 5), T - 1);
+        const int s = find_seq(cu, S, t);
+        double sn, cs;
+        sincos((double)(t - cu[s]) * rope_freq_of(fr, lane & 31), &sn, &cs);
+        c[2 * rr] = (float)cs;
+        sf[2 * rr] = (float)sn;
+        c[2 * rr + 1] = __shfl_xor(c[2 * rr], 32);
+        sf[2 * rr + 1] = __shfl_xor(sf[2 * rr], 32);
       }
-      out[d0] = f2bf(y0);
-      out[d1] = f2bf(y1);
+    }
+#pragma unroll
+    for (int tt = 0; tt < kProTok; ++tt) {
+      if (t0 + tt >= T) break;
+#pragma unroll
+      for (int which = 0; which < 2; ++which) {
+        u16* out = (which ? kfeat : qfeat) + ((int64_t)(t0 + tt) * Hk + h) * kHeadDim;
+        const float x0 = x[tt][which][0];
+        const float x1 = x[tt][which][1];
+        float ss = x0 * x0 + x1 * x1;
+        for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+        const float ms = ss * (1.0f / 128.0f);
+        const float r = 1.0f / sqrtf(ms + eps);
+        float y0 = (x0 * r) * (which ? wk0 : wq0);
+        float y1 = (x1 * r) * (which ? wk1 : wq1);
+        if (lane < 32) {
+          const float o0 = (y0 * c[tt]) - (y1 * sf[tt]);
+          const float o1 = (y1 * c[tt]) + (y0 * sf[tt]);
+          y0 = o0;
+          y1 = o1;
+        }
+        out[d0] = f2bf(y0);
+        out[d1] = f2bf(y1);
+      }
     }
   }
 }
@@ -142,42 +172,71 @@ __global__ __launch_bounds__(256) void select_scores_kernel(
     if (c + 1 < c1) stage(c + 1, buf ^ 1);
     const bool diag = c == qb;
     float m0 = -INFINITY, m1 = -INFINITY;
+    // two halves of four key tiles; the 16 K operands of the second half are
+    // read while the first half's 32 MFMAs run, and consecutive MFMAs belong
+    // to different accumulators
+    bf16x8 ka[2][16];
 #pragma unroll
-    for (int kt = 0; kt < 8; ++kt) {
-      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 16; ++i) ka[0][i] = __builtin_bit_cast(bf16x8, kst[buf][(i & 3) * 4 + (i >> 2)][lane]);
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) {
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, kst[buf][4 * kt + ds][lane]);
-        a0 = mfma16x16x32(ka, qf[0][ds], a0);
-        a1 = mfma16x16x32(ka, qf[1][ds], a1);
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x4 a0[4], a1[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) a0[kk] = a1[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (hf == 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          ka[1][i] = __builtin_bit_cast(bf16x8, kst[buf][(4 + (i & 3)) * 4 + (i >> 2)][lane]);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        a0[i & 3] = mfma16x16x32(ka[hf][i], qf[0][i >> 2], a0[i & 3]);
+        a1[i & 3] = mfma16x16x32(ka[hf][i], qf[1][i >> 2], a1[i & 3]);
+      }
+      if (hf == 0) {  // first half's reads, then one second-half read per two MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
       }
       if (diag) {  // key 16kt + 4g + r against query 32w + 16rt + li of the same block
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = 16 * kt + 4 * g + r;
-          if (key > 32 * wave + li) a0[r] = -INFINITY;
-          if (key > 32 * wave + 16 + li) a1[r] = -INFINITY;
-        }
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = 16 * (4 * hf + kk) + 4 * g + r;
+            if (key > 32 * wave + li) a0[kk][r] = -INFINITY;
+            if (key > 32 * wave + 16 + li) a1[kk][r] = -INFINITY;
+          }
       }
-      m0 = fmaxf(m0, fmaxf(fmaxf(a0[0], a0[1]), fmaxf(a0[2], a0[3])));
-      m1 = fmaxf(m1, fmaxf(fmaxf(a1[0], a1[1]), fmaxf(a1[2], a1[3])));
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        m0 = fmaxf(m0, fmaxf(fmaxf(a0[kk][0], a0[kk][1]), fmaxf(a0[kk][2], a0[kk][3])));
+        m1 = fmaxf(m1, fmaxf(fmaxf(a1[kk][0], a1[kk][1]), fmaxf(a1[kk][2], a1[kk][3])));
+      }
     }
     m0 = max_over_groups(m0);
     m1 = max_over_groups(m1);
+    // the wait counts stores too: the scores are stored after it, so the
+    // next block's wait finds them long completed instead of waiting out
+    // their write latency
+    wait_copies();
+    lds_barrier();
     if (g == 0) {
       const int qp = kBlock * qb + 32 * wave + li;
       if (qp < L) scores[((int64_t)(seq0 + qp) * Hk + h) * nbmax + c] = m0;
       if (qp + 16 < L) scores[((int64_t)(seq0 + qp + 16) * Hk + h) * nbmax + c] = m1;
     }
-    wait_copies();
-    lds_barrier();
   }
 }
 
 // ---------------------------------------------------------------------------
-// 3. Top-k.  One wavefront per (token, head).  The candidates are blocks
-// 0 .. b-1 (b = own block), or 1 .. b-1 when block 0 is forced in (then 14
-// are chosen instead of 15); order: score descending, id ascending.
+// 3. Top-k.  A wavefront ranks one (token, head) row at a time.  The
+// candidates are blocks 0 .. b-1 (b = own block), or 1 .. b-1 when block 0 is
+// forced in (then 14 are chosen instead of 15); order: score descending, id
+// ascending.
 //   * b <= 64: lane c holds candidate c; its rank is the number of candidates
 //     ordered before it, counted against each candidate in turn (broadcast
 //     from its lane).  The 15 of rank < 15 are written in id order (ballot
@@ -190,25 +249,16 @@ __device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
   return av > bv || (av == bv && ai < bi);
 }
 
-__global__ __launch_bounds__(256) void select_topk_kernel(const float* __restrict__ scores,
-                                                          const int32_t* __restrict__ cu, int S, int T,
-                                                          int Hk, int nbmax, int force_init,
-                                                          int32_t* __restrict__ blk_idx) {
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (wave >= T * Hk) return;
-  const int t = wave / Hk;
-  const int s = find_seq(cu, S, t);
-  const int pos = t - cu[s];
-  const int b = __builtin_amdgcn_readfirstlane(pos / kBlock);
-  int32_t* out = blk_idx + (int64_t)wave * kTopk;
+// row: the (token, head) row's scores; b: the token's own block; pre: this
+// lane's score of candidate `lane` when b <= 64 (loaded by the caller)
+__device__ __forceinline__ void topk_row(const float* __restrict__ row, int b, float pre, int lane, int nbmax,
+                                         int force_init, int32_t* __restrict__ out) {
   if (b < kTopk) {
     if (lane < kTopk) out[lane] = lane <= b ? lane : -1;
     return;
   }
   const int first = force_init ? 1 : 0;   // first candidate block
   const int npick = kTopk - 1 - first;     // blocks chosen by score
-  const float* row = scores + (int64_t)wave * nbmax;
   auto load = [&](int c) {
     float x = -INFINITY;
     if (c < b && c < nbmax) {
@@ -218,11 +268,20 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restric
     return x;
   };
   if (b <= 64) {
-    const float v = load(lane);
+    // one 64-bit key per candidate, larger = ordered first: the score's bits
+    // made order-preserving as an unsigned integer (NaN as -inf, -0 as +0),
+    // then the complemented id (lower id first among equal scores)
+    uint32_t u = __builtin_bit_cast(uint32_t, pre != pre ? -INFINITY : pre);
+    u = u == 0x80000000u ? 0u : u;
+    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t klo = ~(uint32_t)lane;
+    const uint64_t key = ((uint64_t)ord << 32) | klo;
     int rank = 0;
+#pragma unroll 4
     for (int j = first; j < b; ++j) {
-      const float vj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
-      rank += better(vj, j, v, lane) ? 1 : 0;
+      const uint64_t kj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ord, j) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)klo, j);
+      rank += kj > key ? 1 : 0;
     }
     const bool chosen = lane >= first && lane < b && rank < npick;
     const uint64_t m = __ballot(chosen);
@@ -274,6 +333,35 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restric
   if (lane < kTopk) out[rank] = mine;
 }
 
+// One wavefront per kTopRows consecutive (token, head) rows; the scores of
+// all its rows are loaded before any row is ranked.
+constexpr int kTopRows = 1;
+
+__global__ __launch_bounds__(256) void select_topk_kernel(const float* __restrict__ scores,
+                                                          const int32_t* __restrict__ cu, int S, int T,
+                                                          int Hk, int nbmax, int force_init,
+                                                          int32_t* __restrict__ blk_idx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r0 = (int64_t)(blockIdx.x * 4 + (threadIdx.x >> 6)) * kTopRows;
+  const int64_t nrows = (int64_t)T * Hk;
+  if (r0 >= nrows) return;
+  int b[kTopRows];
+  float pre[kTopRows];
+#pragma unroll
+  for (int e = 0; e < kTopRows; ++e) {
+    const int64_t row = min(r0 + e, nrows - 1);
+    const int t = (int)(row / Hk);
+    const int s = find_seq(cu, S, t);
+    b[e] = __builtin_amdgcn_readfirstlane((t - cu[s]) / kBlock);
+    pre[e] = -INFINITY;
+    if (b[e] >= kTopk && b[e] <= 64 && lane < b[e] && lane < nbmax) pre[e] = scores[row * nbmax + lane];
+  }
+#pragma unroll
+  for (int e = 0; e < kTopRows; ++e)
+    if (r0 + e < nrows)
+      topk_row(scores + (r0 + e) * nbmax, b[e], pre[e], lane, nbmax, force_init, blk_idx + (r0 + e) * kTopk);
+}
+
 }  // namespace
 
 void launch_select(const Sizes& z, const u16* idx_q, int64_t sq_t, int64_t sq_h,
@@ -283,8 +371,10 @@ void launch_select(const Sizes& z, const u16* idx_q, int64_t sq_t, int64_t sq_h,
   const int T = (int)z.T, Hk = (int)z.Hk, S = (int)z.S;
   {
     KernelTimer timer("select_prologue", st);
-    select_prologue_kernel<<<dim3((unsigned)((z.T + 3) / 4)), 256, 0, st>>>(
-        idx_q, sq_t, sq_h, idx_k, sk_t, sk_h, w_q, w_k, eps, rope_base, cu, S, T, Hk, qfeat, kfeat);
+    const int64_t waves = (z.T + kProTok - 1) / kProTok;
+    select_prologue_kernel<<<dim3((unsigned)((waves + kProWaves - 1) / kProWaves + 1)), 64 * kProWaves, 0, st>>>(
+        idx_q, sq_t, sq_h, idx_k, sk_t, sk_h, w_q, w_k, eps, rope_freqs(rope_base), cu, S, T, Hk, (int)z.chunk, p,
+        qfeat, kfeat);
   }
   const unsigned kchunks = (unsigned)((z.nbmax + kKeyChunk - 1) / kKeyChunk);
   {
@@ -292,7 +382,7 @@ void launch_select(const Sizes& z, const u16* idx_q, int64_t sq_t, int64_t sq_h,
     select_scores_kernel<<<dim3((unsigned)z.nblk_cap, kchunks, (unsigned)Hk), 256, 0, st>>>(
         qfeat, kfeat, cu, p.blkbase, p.blk_seq, p.totals, Hk, (int)z.nbmax, scores);
   }
-  const int64_t waves_top = z.T * z.Hk;
+  const int64_t waves_top = (z.T * z.Hk + kTopRows - 1) / kTopRows;
   {
     KernelTimer timer("select_topk", st);
     select_topk_kernel<<<dim3((unsigned)((waves_top + 3) / 4)), 256, 0, st>>>(scores, cu, S, T, Hk, (int)z.nbmax,
