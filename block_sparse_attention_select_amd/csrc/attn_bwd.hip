@@ -360,29 +360,56 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
   const int jmin = (kBlock * c) / chunk;
   if (jmin == nch - 1) return;  // a block with one work item was written by the dK/dV kernel itself
   const int item0 = seqitem[s];
-  const int e0 = slice * 16 * kHeadDim;
-  for (int e = e0 + threadIdx.x * 4; e < e0 + 16 * kHeadDim; e += 256 * 4) {
-    const int key = e / kHeadDim;
-    const int d = e - key * kHeadDim;
-    const int kp = kBlock * c + key;
-    if (kp >= L) continue;
-    f32x4 adk = {0.f, 0.f, 0.f, 0.f};
-    f32x4 adv = {0.f, 0.f, 0.f, 0.f};
-    int base = 0;  // items of the chunks before j
-    for (int j = 0; j < nch; ++j) {
-      const int cnt = (min((j + 1) * chunk, L) - 1) / kBlock + 1;
-      const int it = item0 + base + c;
-      base += cnt;
-      if (j < jmin || it >= items_cap) continue;
-      if (item_count[(int64_t)h * items_cap + it] == 0) continue;
-      const int64_t off = ((int64_t)h * items_cap + it) * (kBlock * kHeadDim) + e;
-      const f32x4 pa = *reinterpret_cast<const f32x4*>(part_dk + off);
-      const f32x4 pb = *reinterpret_cast<const f32x4*>(part_dv + off);
-      adk += pa;
-      adv += pb;
+  const int m = chunk / kBlock;  // blocks per full chunk: chunk j's items start at item0 + m j (j + 1) / 2
+  // this thread's two 4-element groups of the 16 keys x 128 dims
+  int eg[2], kp[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    eg[u] = slice * 16 * kHeadDim + threadIdx.x * 4 + u * 1024;
+    kp[u] = kBlock * c + eg[u] / kHeadDim;
+  }
+  f32x4 adk[2], adv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) adk[u] = adv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // four chunks at a time: their slices are loaded before any is added, then
+  // added in chunk order (chunks whose item no query selected wrote nothing)
+  for (int j0 = jmin; j0 < nch; j0 += 4) {
+    int cnt[4];
+    int64_t off[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int j = min(j0 + w, nch - 1);
+      const int it = item0 + m * (j * (j + 1) / 2) + c;
+      const bool ok = j0 + w < nch && it < items_cap;
+      const int itc = ok ? it : 0;
+      cnt[w] = ok ? item_count[(int64_t)h * items_cap + itc] : 0;
+      off[w] = ((int64_t)h * items_cap + itc) * (kBlock * kHeadDim);
     }
-    *reinterpret_cast<uint2*>(dk + (int64_t)(seq0 + kp) * dk_st + (int64_t)h * dk_sh + d) = pack_bf16x4(adk * scale);
-    *reinterpret_cast<uint2*>(dv + (int64_t)(seq0 + kp) * dv_st + (int64_t)h * dv_sh + d) = pack_bf16x4(adv);
+    f32x4 pk[4][2], pv[4][2];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        pk[w][u] = *reinterpret_cast<const f32x4*>(part_dk + off[w] + eg[u]);
+        pv[w][u] = *reinterpret_cast<const f32x4*>(part_dv + off[w] + eg[u]);
+      }
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (cnt[w] != 0) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          adk[u] += pk[w][u];
+          adv[u] += pv[w][u];
+        }
+      }
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (kp[u] >= L) continue;
+    const int d = eg[u] % kHeadDim;
+    *reinterpret_cast<uint2*>(dk + (int64_t)(seq0 + kp[u]) * dk_st + (int64_t)h * dk_sh + d) =
+        pack_bf16x4(adk[u] * scale);
+    *reinterpret_cast<uint2*>(dv + (int64_t)(seq0 + kp[u]) * dv_st + (int64_t)h * dv_sh + d) = pack_bf16x4(adv[u]);
   }
 }
 
