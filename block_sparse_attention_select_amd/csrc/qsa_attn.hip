@@ -798,27 +798,57 @@ __global__ __launch_bounds__(256) void qsa_reduce_kernel(
   const int jmin = (kKT * c) / chunk;
   if (jmin == nch - 1) return;  // a key tile with one work item was written by the dK/dV kernel
   const int item0 = seqitem[s];
-  const int e0 = slice * 16 * kD;
-  for (int e = e0 + threadIdx.x * 4; e < e0 + 16 * kD; e += 256 * 4) {
-    const int key = e / kD;
-    const int d = e - key * kD;
-    const int kp = kKT * c + key;
-    if (kp >= L) continue;
-    f32x4 adk = {0.f, 0.f, 0.f, 0.f};
-    f32x4 adv = {0.f, 0.f, 0.f, 0.f};
-    int base = 0;
-    for (int j = 0; j < nch; ++j) {
-      const int cnt = (min((j + 1) * chunk, L) - 1) / kKT + 1;
-      const int it = item0 + base + c;
-      base += cnt;
-      if (j < jmin || it >= items_cap) continue;
-      if (item_count[(int64_t)h * items_cap + it] == 0) continue;
-      const int64_t off = ((int64_t)h * items_cap + it) * (kKT * kD) + e;
-      adk += *reinterpret_cast<const f32x4*>(part_dk + off);
-      adv += *reinterpret_cast<const f32x4*>(part_dv + off);
+  const int m = chunk / kKT;  // key tiles per full chunk: chunk j's items start at item0 + m j (j + 1) / 2
+  // this thread's four 4-element groups of the 16 keys x 256 dims
+  constexpr int kGroups = 16 * kD / 1024;
+  int eg[kGroups], kp[kGroups];
+#pragma unroll
+  for (int u = 0; u < kGroups; ++u) {
+    eg[u] = slice * 16 * kD + threadIdx.x * 4 + u * 1024;
+    kp[u] = kKT * c + eg[u] / kD;
+  }
+  f32x4 adk[kGroups], adv[kGroups];
+#pragma unroll
+  for (int u = 0; u < kGroups; ++u) adk[u] = adv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // two chunks at a time: their slices are loaded before either is added, then
+  // added in chunk order (chunks whose item no query listed wrote nothing)
+  for (int j0 = jmin; j0 < nch; j0 += 2) {
+    int cnt[2];
+    int64_t off[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const int j = min(j0 + w, nch - 1);
+      const int it = item0 + m * (j * (j + 1) / 2) + c;
+      const bool ok = j0 + w < nch && it < items_cap;
+      const int itc = ok ? it : 0;
+      cnt[w] = ok ? item_count[(int64_t)h * items_cap + itc] : 0;
+      off[w] = ((int64_t)h * items_cap + itc) * (kKT * kD);
     }
-    *reinterpret_cast<uint2*>(dk + (int64_t)(seq0 + kp) * dk_st + (int64_t)h * dk_sh + d) = pack_bf16x4(adk * scale);
-    *reinterpret_cast<uint2*>(dv + (int64_t)(seq0 + kp) * dv_st + (int64_t)h * dv_sh + d) = pack_bf16x4(adv);
+    f32x4 pk[2][kGroups], pv[2][kGroups];
+#pragma unroll
+    for (int w = 0; w < 2; ++w)
+#pragma unroll
+      for (int u = 0; u < kGroups; ++u) {
+        pk[w][u] = *reinterpret_cast<const f32x4*>(part_dk + off[w] + eg[u]);
+        pv[w][u] = *reinterpret_cast<const f32x4*>(part_dv + off[w] + eg[u]);
+      }
+#pragma unroll
+    for (int w = 0; w < 2; ++w)
+      if (cnt[w] != 0) {
+#pragma unroll
+        for (int u = 0; u < kGroups; ++u) {
+          adk[u] += pk[w][u];
+          adv[u] += pv[w][u];
+        }
+      }
+  }
+#pragma unroll
+  for (int u = 0; u < kGroups; ++u) {
+    if (kp[u] >= L) continue;
+    const int d = eg[u] % kD;
+    *reinterpret_cast<uint2*>(dk + (int64_t)(seq0 + kp[u]) * dk_st + (int64_t)h * dk_sh + d) =
+        pack_bf16x4(adk[u] * scale);
+    *reinterpret_cast<uint2*>(dv + (int64_t)(seq0 + kp[u]) * dv_st + (int64_t)h * dv_sh + d) = pack_bf16x4(adv[u]);
   }
 }
 
