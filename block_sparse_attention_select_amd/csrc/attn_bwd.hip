@@ -22,6 +22,7 @@
 //                       writes bf16 dK/dV with their own strides; blocks with a
 //                       single chunk were finished by the dK/dV kernel.
 #include "attn_stage.h"
+#include "plan_blocks.h"
 
 namespace msa {
 
@@ -46,12 +47,11 @@ constexpr int kTileTok = kAttnTile;
 // end are zero).  blockIdx.z: K (0-3) or V (4-7), a quarter of the runs each.
 __global__ __launch_bounds__(256) void bwd_block_prep_kernel(const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
                                                              const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
-                                                             const int32_t* __restrict__ cu,
-                                                             const int32_t* __restrict__ blkbase,
-                                                             const int32_t* __restrict__ blk_seq,
-                                                             const int32_t* __restrict__ totals, int Hk,
+                                                             const int32_t* __restrict__ cu, int S, int chunk,
+                                                             int ntiles, PlanBufs plan, int Hk,
                                                              u16* __restrict__ kop, u16* __restrict__ vop,
                                                              int32_t* __restrict__ clear, int nclear) {
+  __shared__ int loc[2];
   const int gb = blockIdx.x;
   const int h = blockIdx.y;
   // zero the dK/dV item-load counters the dQ pass accumulates
@@ -60,13 +60,25 @@ __global__ __launch_bounds__(256) void bwd_block_prep_kernel(const u16* __restri
     const int nwg = gridDim.x * gridDim.y * gridDim.z;
     for (int i = wg * 256 + threadIdx.x; i < nclear; i += nwg * 256) clear[i] = 0;
   }
-  if (gb >= totals[0]) return;
+  // the last workgroup of the grid writes the plan (block numbering, dK/dV
+  // work items, tile launch order) for the kernels that follow; the copy
+  // workgroups locate their block from cu_seqlens directly
+  if (gb == (int)gridDim.x - 1) {
+    if (h == 0 && blockIdx.z == 0) {
+      __shared__ int sb[256], si[256], hist[kOrderBins], scu[kCuCache];
+      plan_blocks<256, kBlock>(cu, S, chunk, plan.blkbase, plan.blk_seq, plan.seqitem, plan.totals, sb, si);
+      plan_tile_order<256, 16>(cu, S, ntiles, plan.tile_order, sb, hist, scu);
+    }
+    return;
+  }
+  locate_block<kBlock>(cu, S, gb, loc);
+  const int s = loc[0];
+  if (s < 0) return;
+  const int c = loc[1];
   const bool is_v = blockIdx.z >= 4;
   const int part = blockIdx.z & 3;  // runs 8 part .. 8 part + 7
   const u16* x = is_v ? v : k;
   const int64_t st_t = is_v ? v_st : k_st, st_h = is_v ? v_sh : k_sh;
-  const int s = blk_seq[gb];
-  const int c = gb - blkbase[s];
   const int seq0 = cu[s];
   const int L = cu[s + 1] - seq0;
   u16* dst = (is_v ? vop : kop) + ((int64_t)gb * Hk + h) * (kHeadDim * kBlock);
@@ -419,9 +431,9 @@ void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStr
   const int T = (int)z.T, Hk = (int)z.Hk, S = (int)z.S;
   {
     KernelTimer timer("bwd_block_prep", st);
-    bwd_block_prep_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)Hk, 8), 256, 0, st>>>(
-        a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.cu, p.blkbase, p.blk_seq, p.totals, Hk, a.kop, a.vop,
-        a.item_load, (int)(z.Hk * z.items_cap));
+    bwd_block_prep_kernel<<<dim3((unsigned)(z.nblk_cap + 1), (unsigned)Hk, 8), 256, 0, st>>>(
+        a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.cu, (int)z.S, (int)z.chunk, (int)z.ntiles, p, Hk, a.kop,
+        a.vop, a.item_load, (int)(z.Hk * z.items_cap));
   }
   {
     KernelTimer timer("attn_bwd_dq", st);

@@ -20,6 +20,7 @@
 // eight P values a lane owns are eight consecutive keys -- the same eight
 // consecutive keys the V^T operand reads.
 #include "attn_stage.h"
+#include "plan_blocks.h"
 
 namespace msa {
 
@@ -34,20 +35,31 @@ namespace {
 //        16dt + li] -- the A operand of O^T = V^T P^T.
 __global__ __launch_bounds__(256) void block_prep_kernel(const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
                                                          const u16* __restrict__ x, int64_t st_t, int64_t st_h,
-                                                         const int32_t* __restrict__ cu,
-                                                         const int32_t* __restrict__ blkbase,
-                                                         const int32_t* __restrict__ blk_seq,
-                                                         const int32_t* __restrict__ totals, int Hk,
+                                                         const int32_t* __restrict__ cu, int S, int chunk,
+                                                         int ntiles, PlanBufs plan, int Hk,
                                                          u16* __restrict__ kop, u16* __restrict__ xt) {
   // workgroup part p (of 4): K runs 8p .. 8p+7 (key tiles 2p, 2p+1) and the
-  // V^T runs of dims 32p .. 32p+31 (runs 8p .. 8p+7)
+  // V^T runs of dims 32p .. 32p+31 (runs 8p .. 8p+7).  The last workgroup of
+  // the grid instead writes the plan (block numbering, tile launch order) for
+  // the forward kernel, so the pass needs no plan launch of its own; the copy
+  // workgroups locate their block from cu_seqlens directly.
   __shared__ u16 tile[kBlock][32 + 8];
+  __shared__ int loc[2];
   const int gb = blockIdx.x;
   const int h = blockIdx.y;
   const int part = blockIdx.z;
-  if (gb >= totals[0]) return;
-  const int s = blk_seq[gb];
-  const int c = gb - blkbase[s];
+  if (gb == (int)gridDim.x - 1) {
+    if (h == 0 && part == 0) {
+      __shared__ int sb[256], si[256], hist[kOrderBins], scu[kCuCache];
+      plan_blocks<256, kBlock>(cu, S, chunk, plan.blkbase, plan.blk_seq, plan.seqitem, plan.totals, sb, si);
+      plan_tile_order<256, 16>(cu, S, ntiles, plan.tile_order, sb, hist, scu);
+    }
+    return;
+  }
+  locate_block<kBlock>(cu, S, gb, loc);
+  const int s = loc[0];
+  if (s < 0) return;
+  const int c = loc[1];
   const int seq0 = cu[s];
   const int L = cu[s + 1] - seq0;
   for (int i = threadIdx.x; i < kBlock * 4; i += 256) {
@@ -352,8 +364,8 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
 void launch_block_prep(const Sizes& z, const u16* k, int64_t k_st, int64_t k_sh, const u16* v, int64_t v_st,
                        int64_t v_sh, const int32_t* cu, const PlanBufs& p, u16* kop, u16* vt, hipStream_t st) {
   KernelTimer timer("block_prep", st);
-  block_prep_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk, 4), 256, 0, st>>>(
-      k, k_st, k_sh, v, v_st, v_sh, cu, p.blkbase, p.blk_seq, p.totals, (int)z.Hk, kop, vt);
+  block_prep_kernel<<<dim3((unsigned)(z.nblk_cap + 1), (unsigned)z.Hk, 4), 256, 0, st>>>(
+      k, k_st, k_sh, v, v_st, v_sh, cu, (int)z.S, (int)z.chunk, (int)z.ntiles, p, (int)z.Hk, kop, vt);
 }
 
 void launch_attn_fwd(const Sizes& z, const u16* q, int64_t q_st, int64_t q_sh,

@@ -363,7 +363,6 @@ int msa_attn_fwd_ex(const msa_dims* dims, const void* q, int64_t q_st, int64_t q
   if (st != MSA_OK) return st;
   Carver c(workspace);
   FwdWs w = carve_fwd(c, z);
-  msa::launch_plan(cu_seqlens, z, w.plan, stream);
   msa::launch_block_prep(z, (const u16*)k, k_st, k_sh, (const u16*)v, v_st, v_sh, cu_seqlens, w.plan, w.kop, w.vt,
                          stream);
   msa::launch_attn_fwd(z, (const u16*)q, q_st, q_sh, w.kop, w.vt, dense ? nullptr : blk_idx,
@@ -429,7 +428,6 @@ int msa_attn_bwd_ex(const msa_dims* dims, const void* q, int64_t q_st, int64_t q
   a.item_order = w.item_order;
   a.part_dk = w.part_dk;
   a.part_dv = w.part_dv;
-  msa::launch_plan(cu_seqlens, z, w.plan, stream);
   msa::launch_attn_bwd(z, a, w.plan, stream);
   return launch_status();
 }

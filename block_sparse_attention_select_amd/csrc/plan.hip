@@ -30,17 +30,6 @@ namespace msa {
 namespace {
 
 constexpr int kPlanThreads = 1024;
-constexpr int kOrderBins = 1024;  // position keys: one per 128-token block (131072 tokens)
-
-constexpr int kCuCache = 4097;      // cu_seqlens entries held in LDS for the tile keys
-constexpr int kKeysPerThread = 8;    // tile keys kept in registers between the two passes
-
-// Order key of tile i: block of its first token within that token's sequence.
-__device__ __forceinline__ int tile_key(const int32_t* cu, int S, int i) {
-  const int t0 = i * kAttnTile;
-  const int s = find_seq(cu, S, t0);
-  return min((t0 - cu[s]) / kBlock, kOrderBins - 1);
-}
 
 template <int kUnit>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ cu, int S, int chunk,
@@ -53,48 +42,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   __shared__ int si[kPlanThreads];
   __shared__ int hist[kOrderBins];
   __shared__ int scu[kCuCache];
-  const int tid = threadIdx.x;
   plan_blocks<kPlanThreads, kUnit>(cu, S, chunk, blkbase, blk_seq, seqitem, totals, sb, si);
-
-  // tile launch order: counting sort on the position key, largest key first
-  // (ntiles = 0: the caller needs no tile order)
-  if (ntiles == 0) return;
-  static_assert(kOrderBins == kPlanThreads, "one scan slot per key");
-  const bool cached = S + 1 <= kCuCache;
-  if (cached)
-    for (int i = tid; i <= S; i += kPlanThreads) scu[i] = cu[i];
-  const int32_t* cus = cached ? (const int32_t*)scu : cu;
-  hist[tid] = 0;
-  __syncthreads();
-  int keys[kKeysPerThread];
-#pragma unroll
-  for (int e = 0; e < kKeysPerThread; ++e) {
-    const int i = tid + e * kPlanThreads;
-    keys[e] = i < ntiles ? tile_key(cus, S, i) : 0;
-    if (i < ntiles) atomicAdd(&hist[keys[e]], 1);
-  }
-  for (int i = tid + kKeysPerThread * kPlanThreads; i < ntiles; i += kPlanThreads)
-    atomicAdd(&hist[tile_key(cus, S, i)], 1);
-  __syncthreads();
-  const int key = kOrderBins - 1 - tid;  // slot tid scans the keys from the top down
-  const int cnt = hist[key];
-  sb[tid] = cnt;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    int a = tid >= off ? sb[tid - off] : 0;
-    __syncthreads();
-    sb[tid] += a;
-    __syncthreads();
-  }
-  hist[key] = sb[tid] - cnt;  // first launch slot of the key
-  __syncthreads();
-#pragma unroll
-  for (int e = 0; e < kKeysPerThread; ++e) {
-    const int i = tid + e * kPlanThreads;
-    if (i < ntiles) tile_order[atomicAdd(&hist[keys[e]], 1)] = i;
-  }
-  for (int i = tid + kKeysPerThread * kPlanThreads; i < ntiles; i += kPlanThreads)
-    tile_order[atomicAdd(&hist[tile_key(cus, S, i)], 1)] = i;
+  // ntiles = 0: the caller needs no tile order
+  if (ntiles > 0) plan_tile_order<kPlanThreads, 8>(cu, S, ntiles, tile_order, sb, hist, scu);
 }
 
 }  // namespace

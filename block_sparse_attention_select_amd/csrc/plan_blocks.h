@@ -65,4 +65,102 @@ __device__ __forceinline__ void plan_blocks(const int32_t* __restrict__ cu, int 
   }
 }
 
+constexpr int kOrderBins = 1024;  // tile order keys: one per 128-token block (131072 tokens)
+constexpr int kCuCache = 4097;    // cu_seqlens entries held in LDS for the tile keys
+
+// Order key of token tile i: block of its first token within that token's sequence.
+__device__ __forceinline__ int tile_key(const int32_t* cu, int S, int i) {
+  const int t0 = i * kAttnTile;
+  const int s = find_seq(cu, S, t0);
+  return min((t0 - cu[s]) / kBlock, kOrderBins - 1);
+}
+
+// Token tiles in launch order: a counting sort on tile_key, largest key first
+// (a later query chooses among more blocks, so its tile's union, and work,
+// is larger; the order within a key is free).  Run by all kThreads threads of
+// one workgroup; sb: kThreads ints, hist: kOrderBins ints, scu: kCuCache ints
+// of LDS.  kKeys tile keys per thread stay in registers between the passes.
+template <int kThreads, int kKeys>
+__device__ __forceinline__ void plan_tile_order(const int32_t* __restrict__ cu, int S, int ntiles,
+                                                int32_t* __restrict__ tile_order, int* sb, int* hist, int* scu) {
+  static_assert(kOrderBins % kThreads == 0, "whole bins per thread");
+  constexpr int kBins = kOrderBins / kThreads;
+  const int tid = threadIdx.x;
+  const bool cached = S + 1 <= kCuCache;
+  if (cached)
+    for (int i = tid; i <= S; i += kThreads) scu[i] = cu[i];
+  const int32_t* cus = cached ? (const int32_t*)scu : cu;
+  for (int b = tid; b < kOrderBins; b += kThreads) hist[b] = 0;
+  __syncthreads();
+  int keys[kKeys];
+#pragma unroll
+  for (int e = 0; e < kKeys; ++e) {
+    const int i = tid + e * kThreads;
+    keys[e] = i < ntiles ? tile_key(cus, S, i) : 0;
+    if (i < ntiles) atomicAdd(&hist[keys[e]], 1);
+  }
+  for (int i = tid + kKeys * kThreads; i < ntiles; i += kThreads) atomicAdd(&hist[tile_key(cus, S, i)], 1);
+  __syncthreads();
+  // thread tid owns scan slots kBins tid .. kBins tid + kBins - 1, slot j
+  // holding key kOrderBins - 1 - j (largest key first)
+  int cnt[kBins], sum = 0;
+#pragma unroll
+  for (int u = 0; u < kBins; ++u) {
+    cnt[u] = hist[kOrderBins - 1 - (kBins * tid + u)];
+    sum += cnt[u];
+  }
+  sb[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {  // inclusive Hillis-Steele scan
+    const int a = tid >= off ? sb[tid - off] : 0;
+    __syncthreads();
+    sb[tid] += a;
+    __syncthreads();
+  }
+  int run = sb[tid] - sum;  // first launch slot of this thread's first key
+#pragma unroll
+  for (int u = 0; u < kBins; ++u) {
+    hist[kOrderBins - 1 - (kBins * tid + u)] = run;
+    run += cnt[u];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kKeys; ++e) {
+    const int i = tid + e * kThreads;
+    if (i < ntiles) tile_order[atomicAdd(&hist[keys[e]], 1)] = i;
+  }
+  for (int i = tid + kKeys * kThreads; i < ntiles; i += kThreads)
+    tile_order[atomicAdd(&hist[tile_key(cus, S, i)], 1)] = i;
+}
+
+// Sequence and block index of global block gb (kUnit-token blocks), without
+// the plan's tables: wavefront 0 scans the sequences' block counts, 64 at a
+// time, and leaves {s, c} in loc (s = -1 when gb is past the pack's last
+// block).  Ends with a workgroup barrier.
+template <int kUnit>
+__device__ __forceinline__ void locate_block(const int32_t* __restrict__ cu, int S, int gb, int* loc) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int carry = 0;
+    for (int base = 0; base < S && carry <= gb; base += 64) {
+      const int s = base + lane;
+      const int nb = s < S ? (cu[s + 1] - cu[s] + kUnit - 1) / kUnit : 0;
+      int incl = nb;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      const int first = carry + incl - nb;
+      if (gb >= first && gb < first + nb) {
+        loc[0] = s;
+        loc[1] = gb - first;
+      }
+      carry += __shfl(incl, 63);
+    }
+    if (lane == 0 && carry <= gb) loc[0] = -1;
+  }
+  __syncthreads();
+}
+
 }  // namespace msa
