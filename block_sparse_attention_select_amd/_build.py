@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmsa.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["plan.hip", "select.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dkdv.hip", "qk_norm.hip", "qsa_attn.hip",
+SOURCES = ["select.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dkdv.hip", "qk_norm.hip", "qsa_attn.hip",
            "msa_api.cpp",
            "timing.cpp"]
 

@@ -462,7 +462,6 @@ int msa_qsa_attn_fwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t 
   a.bits = w.bits;
   a.vt = w.vt;
   a.kop = w.kop;
-  msa::launch_plan(cu_seqlens, z, w.plan, stream, msa::kQsaKeyTile);
   msa::launch_qsa_fwd(z, a, w.plan, stream);
   return launch_status();
 }
@@ -510,7 +509,6 @@ int msa_qsa_attn_bwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t 
   a.item_count = w.item_count;
   a.part_dk = w.part_dk;
   a.part_dv = w.part_dv;
-  msa::launch_plan(cu_seqlens, z, w.plan, stream, msa::kQsaKeyTile);
   msa::launch_qsa_bwd(z, a, w.plan, stream);
   return launch_status();
 }

@@ -194,10 +194,6 @@ class KernelTimer {
 // ----------------------------------------------------------------------------
 // Launchers (host functions, each defined next to its kernels).
 // ----------------------------------------------------------------------------
-// Plan of a pack (see plan.hip).  `unit` is the key-block width the plan
-// numbers: kBlock for the wide variant, kQsaKeyTile for the narrow one.
-void launch_plan(const int32_t* cu, const Sizes& z, const PlanBufs& p, hipStream_t st, int unit = 128,
-                 bool tiles = true);
 
 void launch_select(const Sizes& z, const u16* idx_q, int64_t sq_t, int64_t sq_h,
                    const u16* idx_k, int64_t sk_t, int64_t sk_h, const u16* w_q, const u16* w_k,

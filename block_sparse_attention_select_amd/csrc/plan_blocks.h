@@ -1,11 +1,32 @@
-// Block numbering and dK/dV work items of a THD pack, as a device function
-// shared by the plan kernel and the selection's feature kernel (which runs it
-// in one extra workgroup, so the selection needs no launch of its own for it).
+// Device-side plan of a THD pack: global block numbering, the dK/dV work
+// items and the launch order of token tiles, computed from cu_seqlens on the
+// GPU so that no offset ever travels back to the host (the pages' tile map is
+// likewise built with no host sync: radixark/miles PR #4581, PR body).  It is
+// written by one extra workgroup of the first kernel of each pass (the
+// selection's feature kernel, the forward and backward prep kernels, the
+// narrow variant's bitmap kernel); the kernels after it read it.
 //
-// Sequence s owns global blocks blkbase[s] .. blkbase[s+1]-1 (kUnit tokens
-// each); blk_seq maps a global block back to its sequence; seqitem[s] is the
-// first dK/dV work item of sequence s (items: every (query chunk, block the
-// chunk's queries may select) pair); totals = {blocks, items}.
+// Blocks are numbered pack-wide: sequence s owns global blocks
+// blkbase[s] .. blkbase[s+1]-1, block c of s being blkbase[s] + c; blk_seq
+// maps a global block back to its sequence.  The block width is a template
+// parameter: 128-token blocks for the wide variant, 64-key tiles for the
+// narrow one (whose 4-token blocks are grouped sixteen to a tile); "block"
+// below means that unit.
+//
+// dK/dV work items are ordered by (sequence, query chunk, block): chunk j of a
+// length-L sequence holds query positions [j*chunk, min((j+1)*chunk, L)) and
+// forms one item with every block c that one of those queries may select,
+// c = 0 .. (min((j+1)*chunk, L) - 1) / unit.  Consecutive items therefore read
+// the same queries.  seqitem[s] is the first item of sequence s; totals =
+// {blocks, items}.
+//
+// Token tiles (kAttnTile consecutive tokens of the pack) are put in launch
+// order by decreasing position of their first token within its sequence: a
+// later query has more causal blocks to choose from, so its tile's union of
+// selected blocks, and with it the tile's work, is larger.  Launching the
+// long tiles first (longest-processing-time order) keeps the last wave of
+// workgroups short.  Tiles of equal key may come in any order; the order only
+// decides which workgroup runs when, never what any of them computes.
 #pragma once
 #include "msa_internal.h"
 

@@ -32,6 +32,7 @@
 // Query heads are padded from 12 to the MFMA's 16 with zero q (forward, dQ) or
 // with statistics that zero P (dK/dV); padded outputs are never stored.
 #include "attn_stage.h"
+#include "plan_blocks.h"
 
 namespace msa {
 
@@ -55,10 +56,22 @@ __device__ __forceinline__ uint32_t tile_mask(const uint32_t* row, int c) {
 // Selection bitmaps: one wavefront per (token, KV head); bit b of the row is
 // set when block b is listed and b <= the token's own block.
 // ---------------------------------------------------------------------------
+// The last workgroup of the grid writes the plan (64-key tile numbering, dK/dV
+// work items, token tile launch order) for the kernels that follow, so the
+// narrow passes need no plan launch of their own.
 __global__ __launch_bounds__(256) void qsa_bitmap_kernel(const int32_t* __restrict__ blk_idx, int topk,
                                                          const int32_t* __restrict__ cu, int S, int T, int Hk,
+                                                         int chunk, int ntiles, PlanBufs plan,
                                                          uint32_t* __restrict__ bits) {
   __shared__ uint32_t row[4][kWords];
+  if (blockIdx.x == gridDim.x - 1) {
+    if (blockIdx.y == 0) {
+      __shared__ int sb[256], si[256], hist[kOrderBins], scu[kCuCache];
+      plan_blocks<256, kKT>(cu, S, chunk, plan.blkbase, plan.blk_seq, plan.seqitem, plan.totals, sb, si);
+      plan_tile_order<256, 16>(cu, S, ntiles, plan.tile_order, sb, hist, scu);
+    }
+    return;
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   const int h = blockIdx.y;
@@ -852,16 +865,16 @@ __global__ __launch_bounds__(256) void qsa_reduce_kernel(
   }
 }
 
-void launch_bitmaps(const Sizes& z, const QsaArgs& a, hipStream_t st) {
+void launch_bitmaps(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStream_t st) {
   KernelTimer timer("qsa_bitmap", st);
-  qsa_bitmap_kernel<<<dim3((unsigned)((z.T + 3) / 4), (unsigned)z.Hk), 256, 0, st>>>(
-      a.blk_idx, a.topk, a.cu, (int)z.S, (int)z.T, (int)z.Hk, a.bits);
+  qsa_bitmap_kernel<<<dim3((unsigned)((z.T + 3) / 4 + 1), (unsigned)z.Hk), 256, 0, st>>>(
+      a.blk_idx, a.topk, a.cu, (int)z.S, (int)z.T, (int)z.Hk, (int)z.chunk, (int)z.ntiles, p, a.bits);
 }
 
 }  // namespace
 
 void launch_qsa_fwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStream_t st) {
-  launch_bitmaps(z, a, st);
+  launch_bitmaps(z, a, p, st);
   {
     KernelTimer timer("qsa_vt", st);
     qsa_vt_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk), 256, 0, st>>>(
@@ -876,7 +889,7 @@ void launch_qsa_fwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStre
 }
 
 void launch_qsa_bwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStream_t st) {
-  launch_bitmaps(z, a, st);
+  launch_bitmaps(z, a, p, st);
   {
     KernelTimer timer("qsa_prep", st);
     qsa_prep_kernel<true><<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk, 8), 256, 0, st>>>(
