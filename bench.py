@@ -81,15 +81,18 @@ def traffic_file(config: str) -> str:
 
 
 def kernel_key(raw: str) -> str:
-    """Library kernel name of a profiler record: `attn_fwd_kernel<false>(...)` -> `attn_fwd_kernel`,
-    the dense template instance -> `attn_fwd_dense_kernel`; other kernels keep their name."""
+    """Library kernel name of a profiler record: `attn_fwd_kernel<false, false>(...)` -> `attn_fwd_kernel`;
+    a first template flag set (the dense instances) adds `_dense`, a second one (the fused q/k norm
+    instances) `_qknorm`; other kernels keep their name."""
     n = raw.replace("(anonymous namespace)::", "").split("(")[0].replace("msa::", "").strip()
     if n.startswith("void "):
         n = n[len("void "):]
-    dense = n.endswith("<true>")
+    m = re.search(r"<([^<>]*)>$", n)
+    flags = [a.strip() for a in m.group(1).split(",")] if m else []
     n = re.sub(r"<[^<>]*>$", "", n)
-    if dense and n.endswith("_kernel"):
-        n = n[:-len("_kernel")] + "_dense_kernel"
+    suffix = ("_dense" if flags[:1] == ["true"] else "") + ("_qknorm" if flags[1:2] == ["true"] else "")
+    if suffix and n.endswith("_kernel"):
+        n = n[:-len("_kernel")] + suffix + "_kernel"
     return n
 
 

@@ -39,10 +39,11 @@ MSA_OP_FWD = 2
 MSA_OP_BWD = 3
 MSA_OP_QSA_FWD = 5
 MSA_OP_QSA_BWD = 6
+MSA_OP_BWD_QKNORM = 7
 
 # Every symbol include/msa.h declares.
 EXPORTED = ("msa_workspace_size", "msa_index_select", "msa_index_select_ex", "msa_attn_fwd", "msa_attn_bwd",
-            "msa_attn_fwd_ex", "msa_attn_bwd_ex",
+            "msa_attn_fwd_ex", "msa_attn_bwd_ex", "msa_attn_fwd_qknorm", "msa_attn_bwd_qknorm",
             "msa_qk_norm_rope_fwd", "msa_qk_norm_rope_bwd", "msa_qsa_attn_fwd", "msa_qsa_attn_bwd",
             "msa_status_string", "msa_check_cu_seqlens", "msa_timing_enable", "msa_timing_collect",
             "msa_version")
@@ -108,6 +109,15 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                     _P, _P, _I64, _I64, _P, _P, _F, ctypes.c_uint32,
                                     _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _SZ, _P]
     lib.msa_attn_bwd_ex.restype = _I32
+    lib.msa_attn_fwd_qknorm.argtypes = [ctypes.POINTER(MsaDims), _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64,
+                                        _P, _P, _F, _F, _I32, _P, _P, _F, ctypes.c_uint32, _P, _I64, _I64, _P, _P,
+                                        _SZ, _P]
+    lib.msa_attn_fwd_qknorm.restype = _I32
+    lib.msa_attn_bwd_qknorm.argtypes = [ctypes.POINTER(MsaDims),
+                                        _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _P, _F, _F, _I32,
+                                        _P, _I64, _I64, _P, _P, _I64, _I64, _P, _P, _F, ctypes.c_uint32,
+                                        _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _P, _P, _SZ, _P]
+    lib.msa_attn_bwd_qknorm.restype = _I32
     lib.msa_qsa_attn_fwd.argtypes = lib.msa_attn_fwd.argtypes
     lib.msa_qsa_attn_fwd.restype = _I32
     lib.msa_qsa_attn_bwd.argtypes = lib.msa_attn_bwd.argtypes
@@ -280,6 +290,64 @@ def msa_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Ten
                               _ptr(dv), sdv[0], sdv[1], _ptr(ws), nbytes, _stream(q))
         _check(st, "msa_attn_bwd")
     return dq, dk, dv
+
+
+def msa_attn_fwd_qknorm(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
+                        blk_idx: Optional[torch.Tensor], cu_seqlens: torch.Tensor, max_seqlen: int,
+                        softmax_scale: Optional[float] = None, *, eps: float = 1e-6, rope_base: float = 1e7,
+                        rope_dims: int = 64, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None,
+                        dense: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """msa_attn_fwd on raw q, k with the attention-side norm + partial RoPE applied inside the kernels."""
+    lib = load()
+    T, Hq, D = q.shape
+    Hk = k.shape[1]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    sq, sk, sv = _bf16_view(q, "q"), _bf16_view(k, "k"), _bf16_view(v, "v")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty(T, Hq, dtype=torch.float32, device=q.device)
+    so = _bf16_view(out, "out")
+    dims = _dims_for(cu_seqlens, max_seqlen, Hq, Hk, T)
+    ws, nbytes = _workspace(dims, MSA_OP_FWD, q.device, workspace)
+    st = lib.msa_attn_fwd_qknorm(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0],
+                                 sv[1], _ptr(w_q.contiguous()), _ptr(w_k.contiguous()), float(eps), float(rope_base),
+                                 int(rope_dims), None if dense else _ptr(blk_idx), _ptr(cu_seqlens), scale,
+                                 MSA_ATTN_DENSE if dense else 0, _ptr(out), so[0], so[1], _ptr(lse), _ptr(ws), nbytes,
+                                 _stream(q))
+    _check(st, "msa_attn_fwd_qknorm")
+    return out, lse
+
+
+def msa_attn_bwd_qknorm(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor,
+                        o: torch.Tensor, lse: torch.Tensor, do: torch.Tensor, blk_idx: Optional[torch.Tensor],
+                        cu_seqlens: torch.Tensor, max_seqlen: int, softmax_scale: Optional[float] = None, *,
+                        eps: float = 1e-6, rope_base: float = 1e7, rope_dims: int = 64,
+                        workspace: Optional[torch.Tensor] = None, dense: bool = False):
+    """Backward of msa_attn_fwd_qknorm: dQ, dK (for the raw q, k), dV (bf16) and dw_q, dw_k (fp32 [128])."""
+    lib = load()
+    T, Hq, D = q.shape
+    Hk = k.shape[1]
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format)
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format)
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    dw_q = torch.empty(128, dtype=torch.float32, device=q.device)
+    dw_k = torch.empty(128, dtype=torch.float32, device=q.device)
+    views = [_bf16_view(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do"),
+                                           (dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    (sq, sk, sv, so, sdo, sdq, sdk, sdv) = views
+    dims = _dims_for(cu_seqlens, max_seqlen, Hq, Hk, T)
+    ws, nbytes = _workspace(dims, MSA_OP_BWD_QKNORM, q.device, workspace)
+    st = lib.msa_attn_bwd_qknorm(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0],
+                                 sv[1], _ptr(w_q.contiguous()), _ptr(w_k.contiguous()), float(eps), float(rope_base),
+                                 int(rope_dims), _ptr(o), so[0], so[1], _ptr(lse), _ptr(do), sdo[0], sdo[1],
+                                 None if dense else _ptr(blk_idx), _ptr(cu_seqlens), scale,
+                                 MSA_ATTN_DENSE if dense else 0, _ptr(dq), sdq[0], sdq[1], _ptr(dk), sdk[0], sdk[1],
+                                 _ptr(dv), sdv[0], sdv[1], _ptr(dw_q), _ptr(dw_k), _ptr(ws), nbytes, _stream(q))
+    _check(st, "msa_attn_bwd_qknorm")
+    return dq, dk, dv, dw_q, dw_k
 
 
 def _qsa_dims(cu_seqlens: torch.Tensor, max_seqlen: int, Hq: int, Hk: int, T: int, topk: int) -> MsaDims:

@@ -21,6 +21,7 @@
 // consecutive keys the V^T operand reads.
 #include "attn_stage.h"
 #include "plan_blocks.h"
+#include "qk_rope.h"
 
 namespace msa {
 
@@ -33,10 +34,13 @@ namespace {
 //        32ds + 8g .. +7] -- the A operand of S^T = K Q^T;
 //   vt:  run dt*4 + ks, lane li + 16g holding V[keys 32ks + 8g + 0..7][dim
 //        16dt + li] -- the A operand of O^T = V^T P^T.
+// kNorm: K is raw; its rows get the attention-side norm and RoPE (qk_rope.h)
+// on the way into the staging copy.
+template <bool kNorm>
 __global__ __launch_bounds__(256) void block_prep_kernel(const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
                                                          const u16* __restrict__ x, int64_t st_t, int64_t st_h,
                                                          const int32_t* __restrict__ cu, int S, int chunk,
-                                                         int ntiles, PlanBufs plan, int Hk,
+                                                         int ntiles, PlanBufs plan, int Hk, QkNormParams nrm,
                                                          u16* __restrict__ kop, u16* __restrict__ xt) {
   // workgroup part p (of 4): K runs 8p .. 8p+7 (key tiles 2p, 2p+1) and the
   // V^T runs of dims 32p .. 32p+31 (runs 8p .. 8p+7).  The last workgroup of
@@ -72,14 +76,50 @@ __global__ __launch_bounds__(256) void block_prep_kernel(const u16* __restrict__
     *reinterpret_cast<u32x4*>(&tile[key][ch * 8]) = v;
   }
   u16* kdst = kop + ((int64_t)gb * Hk + h) * (kHeadDim * kBlock);
-  for (int i = 512 * part + threadIdx.x; i < 512 * part + 512; i += 256) {
-    const int run = i >> 6, ln = i & 63;
-    const int kp = kBlock * c + score_key(run >> 2, ln & 15);
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (kp < L)
-      v = *reinterpret_cast<const u32x4*>(k + (int64_t)(seq0 + kp) * k_st + (int64_t)h * k_sh + 32 * (run & 3) +
-                                          8 * (ln >> 4));
-    *reinterpret_cast<u32x4*>(kdst + (int64_t)i * 8) = v;
+  if constexpr (kNorm) {
+    // the part's 32 keys (tiles 2p, 2p+1): each row normalized and rotated by
+    // 8 lanes (norm_rope_row8), kept in LDS, then copied in run order
+    __shared__ u16 krows[32][kHeadDim + 8];
+    {
+      const int row = threadIdx.x >> 3, j = threadIdx.x & 7;
+      const int kp = kBlock * c + score_key(2 * part + (row >> 4), row & 15);
+      float xv[16], w1[16], cs[4], sn[4];
+      const u16* src = k + (int64_t)(seq0 + min(kp, L - 1)) * k_st + (int64_t)h * k_sh + 4 * j;
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const uint2 wv = *reinterpret_cast<const uint2*>(src + 32 * qd);
+        xv[4 * qd] = __uint_as_float(wv.x << 16);
+        xv[4 * qd + 1] = __uint_as_float(wv.x & 0xFFFF0000u);
+        xv[4 * qd + 2] = __uint_as_float(wv.y << 16);
+        xv[4 * qd + 3] = __uint_as_float(wv.y & 0xFFFF0000u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w1[4 * qd + e] = 1.0f + bf2f(nrm.w_k[32 * qd + 4 * j + e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rope_angle(nrm.fr, 4 * j + e, min(kp, L - 1), cs[e], sn[e]);
+      norm_rope_row8(xv, w1, cs, sn, nrm.eps);
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) krows[row][32 * qd + 4 * j + e] = kp < L ? f2bf(xv[4 * qd + e]) : (u16)0;
+    }
+    __syncthreads();
+    for (int i = 512 * part + threadIdx.x; i < 512 * part + 512; i += 256) {
+      const int run = i >> 6, ln = i & 63;
+      const int row = ((run >> 2) - 2 * part) * 16 + (ln & 15);
+      *reinterpret_cast<u32x4*>(kdst + (int64_t)i * 8) =
+          *reinterpret_cast<const u32x4*>(&krows[row][32 * (run & 3) + 8 * (ln >> 4)]);
+    }
+  } else {
+    for (int i = 512 * part + threadIdx.x; i < 512 * part + 512; i += 256) {
+      const int run = i >> 6, ln = i & 63;
+      const int kp = kBlock * c + score_key(run >> 2, ln & 15);
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (kp < L)
+        v = *reinterpret_cast<const u32x4*>(k + (int64_t)(seq0 + kp) * k_st + (int64_t)h * k_sh + 32 * (run & 3) +
+                                            8 * (ln >> 4));
+      *reinterpret_cast<u32x4*>(kdst + (int64_t)i * 8) = v;
+    }
   }
   __syncthreads();
   u16* dst = xt + ((int64_t)gb * Hk + h) * (kHeadDim * kBlock);
@@ -118,13 +158,15 @@ constexpr int kUnionWords = 34;  // a tile's blocks span fewer than 34 * 32 glob
 constexpr int kMaxUnion = kTileTok * kTopk;
 
 // kDense: every causal key of the token's sequence (the dense layers), blk_idx unused.
-template <bool kDense>
+// kNorm: q is raw; the token's heads get the attention-side norm and RoPE
+// (qk_rope.h) in registers before the walk.
+template <bool kDense, bool kNorm>
 __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
     const u16* __restrict__ kop, const u16* __restrict__ vt, const int32_t* __restrict__ blk_idx,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ blkbase, const int32_t* __restrict__ blk_seq,
-    const int32_t* __restrict__ tile_order, int S, int T, int Hk, float scale_log2, u16* __restrict__ o,
-    int64_t o_st, int64_t o_sh, float* __restrict__ lse) {
+    const int32_t* __restrict__ tile_order, int S, int T, int Hk, float scale_log2, QkNormParams nrm,
+    u16* __restrict__ o, int64_t o_st, int64_t o_sh, float* __restrict__ lse) {
   __shared__ u32x4 kbuf[2][32][64];
   __shared__ u32x4 vbuf[2][32][64];
   __shared__ uint32_t bitmap[kUnionWords];
@@ -132,6 +174,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
   constexpr int kUnionCap = kDense ? kUnionWords * 32 : kMaxUnion;
   __shared__ int ulist[kUnionCap];
   __shared__ int nunion;
+  __shared__ float qang[kNorm ? kFwdWaves : 1][64];
 
   // workgroup b runs KV head b % Hk of the tile in launch slot b / Hk
   const int h = blockIdx.x % Hk;
@@ -140,6 +183,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int li = lane & 15;
+  static_assert(!kNorm || kTokPerWave == 1, "the norm assumes one token per wavefront");
 
   // this lane's (token, slot): token kTokPerWave * wave + g % kTokPerWave, slot li
   const int tj = kTokPerWave * wave + g % kTokPerWave;
@@ -203,6 +247,8 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
   }
   __syncthreads();
   const int nu = nunion;
+
+  if constexpr (kNorm) norm_rope_q(qb[0], nrm.w_q, nrm.eps, nrm.fr, pos_t, lane, qang[wave]);
 
   // per-token state (j = 0, 1 for tokens 2w, 2w+1)
   int tok_pos[kTokPerWave], tok_b[kTokPerWave], tok_base[kTokPerWave];
@@ -362,20 +408,27 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
 }  // namespace
 
 void launch_block_prep(const Sizes& z, const u16* k, int64_t k_st, int64_t k_sh, const u16* v, int64_t v_st,
-                       int64_t v_sh, const int32_t* cu, const PlanBufs& p, u16* kop, u16* vt, hipStream_t st) {
+                       int64_t v_sh, const int32_t* cu, const PlanBufs& p, const QkNormParams* nrm, u16* kop,
+                       u16* vt, hipStream_t st) {
   KernelTimer timer("block_prep", st);
-  block_prep_kernel<<<dim3((unsigned)(z.nblk_cap + 1), (unsigned)z.Hk, 4), 256, 0, st>>>(
-      k, k_st, k_sh, v, v_st, v_sh, cu, (int)z.S, (int)z.chunk, (int)z.ntiles, p, (int)z.Hk, kop, vt);
+  const QkNormParams none{};
+  auto kern = nrm ? block_prep_kernel<true> : block_prep_kernel<false>;
+  kern<<<dim3((unsigned)(z.nblk_cap + 1), (unsigned)z.Hk, 4), 256, 0, st>>>(
+      k, k_st, k_sh, v, v_st, v_sh, cu, (int)z.S, (int)z.chunk, (int)z.ntiles, p, (int)z.Hk, nrm ? *nrm : none, kop,
+      vt);
 }
 
 void launch_attn_fwd(const Sizes& z, const u16* q, int64_t q_st, int64_t q_sh,
-                     const u16* kop, const u16* vt, const int32_t* blk_idx, const int32_t* cu, const PlanBufs& p, float scale,
-                     u16* o, int64_t o_st, int64_t o_sh, float* lse, bool dense, hipStream_t st) {
+                     const u16* kop, const u16* vt, const int32_t* blk_idx, const int32_t* cu, const PlanBufs& p,
+                     float scale, u16* o, int64_t o_st, int64_t o_sh, float* lse, bool dense, const QkNormParams* nrm,
+                     hipStream_t st) {
   KernelTimer timer("attn_fwd", st);
-  auto kern = dense ? attn_fwd_kernel<true> : attn_fwd_kernel<false>;
+  const QkNormParams none{};
+  auto kern = dense ? (nrm ? attn_fwd_kernel<true, true> : attn_fwd_kernel<true, false>)
+                    : (nrm ? attn_fwd_kernel<false, true> : attn_fwd_kernel<false, false>);
   kern<<<(unsigned)(z.ntiles * z.Hk), 64 * kFwdWaves, 0, st>>>(
       q, q_st, q_sh, kop, vt, blk_idx, cu, p.blkbase, p.blk_seq, p.tile_order, (int)z.S, (int)z.T,
-      (int)z.Hk, scale * kLog2e, o, o_st, o_sh, lse);
+      (int)z.Hk, scale * kLog2e, nrm ? *nrm : none, o, o_st, o_sh, lse);
 }
 
 }  // namespace msa

@@ -189,6 +189,59 @@ BwdWs carve_bwd(Carver& c, const Sizes& z) {
   return w;
 }
 
+// Backward with the attention-side norm: the plain backward's workspace, the
+// normalized q and k, their gradients, and the norm backward's partial rows.
+struct BwdQkWs {
+  BwdWs bwd;
+  u16* qhat;
+  u16* khat;
+  u16* dqhat;
+  u16* dkhat;
+  float* partial;
+};
+BwdQkWs carve_bwd_qknorm(Carver& c, const Sizes& z) {
+  BwdQkWs w;
+  w.bwd = carve_bwd(c, z);
+  w.qhat = c.take<u16>(z.T * z.Hq * msa::kHeadDim);
+  w.khat = c.take<u16>(z.T * z.Hk * msa::kHeadDim);
+  w.dqhat = c.take<u16>(z.T * z.Hq * msa::kHeadDim);
+  w.dkhat = c.take<u16>(z.T * z.Hk * msa::kHeadDim);
+  w.partial = c.take<float>((int64_t)(msa::kQkBwdMaxRows + msa::kQkBwdMaxRows / 16 + 1) * 256);
+  return w;
+}
+
+// The backward kernels of the wide variant on the given (normalized) q and k.
+void launch_bwd_on(const Sizes& z, const BwdWs& w, const u16* q, int64_t q_st, int64_t q_sh, const u16* k,
+                   int64_t k_st, int64_t k_sh, const u16* v, int64_t v_st, int64_t v_sh, const u16* o, int64_t o_st,
+                   int64_t o_sh, const float* lse, const u16* dO, int64_t do_st, int64_t do_sh, const int32_t* blk_idx,
+                   const int32_t* cu, float scale, bool dense, u16* dq, int64_t dq_st, int64_t dq_sh, u16* dk,
+                   int64_t dk_st, int64_t dk_sh, u16* dv, int64_t dv_st, int64_t dv_sh, hipStream_t stream) {
+  msa::BwdArgs a;
+  a.q = q; a.q_st = q_st; a.q_sh = q_sh;
+  a.k = k; a.k_st = k_st; a.k_sh = k_sh;
+  a.v = v; a.v_st = v_st; a.v_sh = v_sh;
+  a.o = o; a.o_st = o_st; a.o_sh = o_sh;
+  a.lse = lse;
+  a.dO = dO; a.do_st = do_st; a.do_sh = do_sh;
+  a.blk_idx = blk_idx;
+  a.cu = cu;
+  a.scale = scale;
+  a.dense = dense;
+  a.dq = dq; a.dq_st = dq_st; a.dq_sh = dq_sh;
+  a.dk = dk; a.dk_st = dk_st; a.dk_sh = dk_sh;
+  a.dv = dv; a.dv_st = dv_st; a.dv_sh = dv_sh;
+  a.kop = w.kop;
+  a.vop = w.vop;
+  a.delta = w.delta;
+  a.nlse = w.nlse;
+  a.item_count = w.item_count;
+  a.item_load = w.item_load;
+  a.item_order = w.item_order;
+  a.part_dk = w.part_dk;
+  a.part_dv = w.part_dv;
+  msa::launch_attn_bwd(z, a, w.plan, stream);
+}
+
 struct QsaFwdWs {
   PlanBufs plan;
   uint32_t* bits;
@@ -238,6 +291,7 @@ size_t ws_bytes_for(const Sizes& z, int op) {
     case MSA_OP_QKNORM_BWD: c.take<float>((int64_t)(msa::kQkBwdMaxRows + msa::kQkBwdMaxRows / 16 + 1) * 256); break;
     case MSA_OP_QSA_FWD: carve_qsa_fwd(c, z); break;
     case MSA_OP_QSA_BWD: carve_qsa_bwd(c, z); break;
+    case MSA_OP_BWD_QKNORM: carve_bwd_qknorm(c, z); break;
     default: return 0;
   }
   return c.off;
@@ -297,7 +351,8 @@ int msa_workspace_size(const msa_dims* dims, int op, size_t* bytes) {
   }
   int st = check_dims(dims);
   if (st != MSA_OK) return st;
-  if (op != MSA_OP_SELECT && op != MSA_OP_FWD && op != MSA_OP_BWD && op != MSA_OP_QKNORM_BWD)
+  if (op != MSA_OP_SELECT && op != MSA_OP_FWD && op != MSA_OP_BWD && op != MSA_OP_QKNORM_BWD &&
+      op != MSA_OP_BWD_QKNORM)
     return MSA_ERR_INVALID_ARG;
   *bytes = dims->total_tokens == 0 ? 0 : ws_bytes_for(sizes_of(dims), op);
   return MSA_OK;
@@ -363,10 +418,10 @@ int msa_attn_fwd_ex(const msa_dims* dims, const void* q, int64_t q_st, int64_t q
   if (st != MSA_OK) return st;
   Carver c(workspace);
   FwdWs w = carve_fwd(c, z);
-  msa::launch_block_prep(z, (const u16*)k, k_st, k_sh, (const u16*)v, v_st, v_sh, cu_seqlens, w.plan, w.kop, w.vt,
-                         stream);
+  msa::launch_block_prep(z, (const u16*)k, k_st, k_sh, (const u16*)v, v_st, v_sh, cu_seqlens, w.plan, nullptr,
+                         w.kop, w.vt, stream);
   msa::launch_attn_fwd(z, (const u16*)q, q_st, q_sh, w.kop, w.vt, dense ? nullptr : blk_idx,
-                       cu_seqlens, w.plan, softmax_scale, (u16*)o, o_st, o_sh, lse, dense, stream);
+                       cu_seqlens, w.plan, softmax_scale, (u16*)o, o_st, o_sh, lse, dense, nullptr, stream);
   return launch_status();
 }
 
@@ -405,30 +460,101 @@ int msa_attn_bwd_ex(const msa_dims* dims, const void* q, int64_t q_st, int64_t q
   if (st != MSA_OK) return st;
   Carver c(workspace);
   BwdWs w = carve_bwd(c, z);
-  msa::BwdArgs a;
+  launch_bwd_on(z, w, (const u16*)q, q_st, q_sh, (const u16*)k, k_st, k_sh, (const u16*)v, v_st, v_sh,
+                (const u16*)o, o_st, o_sh, lse, (const u16*)do_, do_st, do_sh, dense ? nullptr : blk_idx,
+                cu_seqlens, softmax_scale, dense, (u16*)dq, dq_st, dq_sh, (u16*)dk, dk_st, dk_sh, (u16*)dv, dv_st,
+                dv_sh, stream);
+  return launch_status();
+}
+
+int msa_attn_fwd_qknorm(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh, const void* k,
+                        int64_t k_st, int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh, const void* w_q,
+                        const void* w_k, float eps, float rope_base, int32_t rope_dims, const int32_t* blk_idx,
+                        const int32_t* cu_seqlens, float softmax_scale, uint32_t flags, void* o, int64_t o_st,
+                        int64_t o_sh, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MSA_OK) return st;
+  if (flags & ~MSA_ATTN_DENSE) return MSA_ERR_INVALID_ARG;
+  const bool dense = (flags & MSA_ATTN_DENSE) != 0;
+  if (rope_dims != 64) return MSA_ERR_UNSUPPORTED;
+  if (!(eps >= 0.f) || !(rope_base > 1.f) || rope_base != rope_base) return MSA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return MSA_ERR_INVALID_ARG;
+  if (dims->total_tokens == 0) return MSA_OK;
+  if (!in_view(q, q_st, q_sh) || !in_view(k, k_st, k_sh) || !in_view(v, v_st, v_sh) || !out_view(o, o_st, o_sh))
+    return MSA_ERR_INVALID_ARG;
+  if (!w_q || !w_k || !aligned(w_q, 2) || !aligned(w_k, 2)) return MSA_ERR_INVALID_ARG;
+  if ((!dense && (!blk_idx || !aligned(blk_idx, 16))) || !cu_seqlens || !aligned(cu_seqlens, 4) || !lse ||
+      !aligned(lse, 16))
+    return MSA_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(dims);
+  st = check_ws(workspace, workspace_bytes, ws_bytes_for(z, MSA_OP_FWD));
+  if (st != MSA_OK) return st;
+  Carver c(workspace);
+  FwdWs w = carve_fwd(c, z);
+  const msa::QkNormParams nrm{(const u16*)w_q, (const u16*)w_k, eps, msa::rope_freqs(rope_base)};
+  msa::launch_block_prep(z, (const u16*)k, k_st, k_sh, (const u16*)v, v_st, v_sh, cu_seqlens, w.plan, &nrm, w.kop,
+                         w.vt, stream);
+  msa::launch_attn_fwd(z, (const u16*)q, q_st, q_sh, w.kop, w.vt, dense ? nullptr : blk_idx, cu_seqlens, w.plan,
+                       softmax_scale, (u16*)o, o_st, o_sh, lse, dense, &nrm, stream);
+  return launch_status();
+}
+
+int msa_attn_bwd_qknorm(const msa_dims* dims, const void* q, int64_t q_st, int64_t q_sh, const void* k,
+                        int64_t k_st, int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh, const void* w_q,
+                        const void* w_k, float eps, float rope_base, int32_t rope_dims, const void* o, int64_t o_st,
+                        int64_t o_sh, const float* lse, const void* do_, int64_t do_st, int64_t do_sh,
+                        const int32_t* blk_idx, const int32_t* cu_seqlens, float softmax_scale, uint32_t flags,
+                        void* dq, int64_t dq_st, int64_t dq_sh, void* dk, int64_t dk_st, int64_t dk_sh, void* dv,
+                        int64_t dv_st, int64_t dv_sh, float* dw_q, float* dw_k, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st != MSA_OK) return st;
+  if (flags & ~MSA_ATTN_DENSE) return MSA_ERR_INVALID_ARG;
+  const bool dense = (flags & MSA_ATTN_DENSE) != 0;
+  if (rope_dims != 64) return MSA_ERR_UNSUPPORTED;
+  if (!(eps >= 0.f) || !(rope_base > 1.f) || rope_base != rope_base) return MSA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return MSA_ERR_INVALID_ARG;
+  if (!dw_q || !dw_k || !aligned(dw_q, 4) || !aligned(dw_k, 4)) return MSA_ERR_INVALID_ARG;
+  if (dims->total_tokens == 0) {  // no rows: the weight gradients are zero
+    msa::QkNormArgs a{};
+    a.dw_q = dw_q;
+    a.dw_k = dw_k;
+    msa::launch_qk_norm_bwd(sizes_of(dims), a, nullptr, stream);
+    return launch_status();
+  }
+  if (!in_view(q, q_st, q_sh) || !in_view(k, k_st, k_sh) || !in_view(v, v_st, v_sh) || !in_view(o, o_st, o_sh) ||
+      !in_view(do_, do_st, do_sh) || !out_view(dq, dq_st, dq_sh) || !out_view(dk, dk_st, dk_sh) ||
+      !out_view(dv, dv_st, dv_sh))
+    return MSA_ERR_INVALID_ARG;
+  if (!w_q || !w_k || !aligned(w_q, 2) || !aligned(w_k, 2)) return MSA_ERR_INVALID_ARG;
+  if ((!dense && (!blk_idx || !aligned(blk_idx, 16))) || !cu_seqlens || !aligned(cu_seqlens, 4) || !lse ||
+      !aligned(lse, 16))
+    return MSA_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(dims);
+  st = check_ws(workspace, workspace_bytes, ws_bytes_for(z, MSA_OP_BWD_QKNORM));
+  if (st != MSA_OK) return st;
+  Carver c(workspace);
+  BwdQkWs w = carve_bwd_qknorm(c, z);
+  const int64_t D = msa::kHeadDim;
+  // normalized q and k, the plain backward on them, then the norm's backward
+  msa::QkNormArgs a{};
   a.q = (const u16*)q; a.q_st = q_st; a.q_sh = q_sh;
   a.k = (const u16*)k; a.k_st = k_st; a.k_sh = k_sh;
-  a.v = (const u16*)v; a.v_st = v_st; a.v_sh = v_sh;
-  a.o = (const u16*)o; a.o_st = o_st; a.o_sh = o_sh;
-  a.lse = lse;
-  a.dO = (const u16*)do_; a.do_st = do_st; a.do_sh = do_sh;
-  a.blk_idx = dense ? nullptr : blk_idx;
+  a.w_q = (const u16*)w_q; a.w_k = (const u16*)w_k;
+  a.eps = eps; a.rope_base = rope_base;
   a.cu = cu_seqlens;
-  a.scale = softmax_scale;
-  a.dense = dense;
-  a.dq = (u16*)dq; a.dq_st = dq_st; a.dq_sh = dq_sh;
-  a.dk = (u16*)dk; a.dk_st = dk_st; a.dk_sh = dk_sh;
-  a.dv = (u16*)dv; a.dv_st = dv_st; a.dv_sh = dv_sh;
-  a.kop = w.kop;
-  a.vop = w.vop;
-  a.delta = w.delta;
-  a.nlse = w.nlse;
-  a.item_count = w.item_count;
-  a.item_load = w.item_load;
-  a.item_order = w.item_order;
-  a.part_dk = w.part_dk;
-  a.part_dv = w.part_dv;
-  msa::launch_attn_bwd(z, a, w.plan, stream);
+  a.qo = w.qhat; a.qo_st = z.Hq * D; a.qo_sh = D;
+  a.ko = w.khat; a.ko_st = z.Hk * D; a.ko_sh = D;
+  msa::launch_qk_norm_fwd(z, a, stream);
+  launch_bwd_on(z, w.bwd, w.qhat, z.Hq * D, D, w.khat, z.Hk * D, D, (const u16*)v, v_st, v_sh, (const u16*)o, o_st,
+                o_sh, lse, (const u16*)do_, do_st, do_sh, dense ? nullptr : blk_idx, cu_seqlens, softmax_scale, dense,
+                w.dqhat, z.Hq * D, D, w.dkhat, z.Hk * D, D, (u16*)dv, dv_st, dv_sh, stream);
+  a.dqh = w.dqhat; a.dqh_st = z.Hq * D; a.dqh_sh = D;
+  a.dkh = w.dkhat; a.dkh_st = z.Hk * D; a.dkh_sh = D;
+  a.qo = (u16*)dq; a.qo_st = dq_st; a.qo_sh = dq_sh;
+  a.ko = (u16*)dk; a.ko_st = dk_st; a.ko_sh = dk_sh;
+  a.dw_q = dw_q; a.dw_k = dw_k;
+  msa::launch_qk_norm_bwd(z, a, w.partial, stream);
   return launch_status();
 }
 

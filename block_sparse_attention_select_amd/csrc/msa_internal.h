@@ -101,6 +101,16 @@ inline RopeFreqs rope_freqs(float rope_base) {
   return r;
 }
 
+// Parameters of the attention-side norm fused into the attention kernels:
+// the [128] bf16 gemma weights of q and k (used as 1 + w), eps and the host's
+// inverse RoPE frequencies.
+struct QkNormParams {
+  const u16* w_q;
+  const u16* w_k;
+  float eps;
+  RopeFreqs fr;
+};
+
 // frequency of pair `lane` (lanes >= 32 get pair 0's, unused): a select
 // chain over scalar registers, so the by-value table is never indexed
 // per lane (which would put it in scratch memory)
@@ -201,13 +211,17 @@ void launch_select(const Sizes& z, const u16* idx_q, int64_t sq_t, int64_t sq_h,
                    bool force_init, u16* qfeat, u16* kfeat, float* scores, int32_t* blk_idx, hipStream_t st);
 
 // Forward operand copies of K and V per (global block, KV head) (attn_fwd.hip).
+// nrm: the attention-side norm fused into the prep (K) and forward (q)
+// kernels, or nullptr for already normalized q and k.
 void launch_block_prep(const Sizes& z, const u16* k, int64_t k_st, int64_t k_sh, const u16* v, int64_t v_st,
-                       int64_t v_sh, const int32_t* cu, const PlanBufs& p, u16* kop, u16* vt, hipStream_t st);
+                       int64_t v_sh, const int32_t* cu, const PlanBufs& p, const QkNormParams* nrm, u16* kop,
+                       u16* vt, hipStream_t st);
 
 void launch_attn_fwd(const Sizes& z, const u16* q, int64_t q_st, int64_t q_sh,
                      const u16* kop, const u16* vt,
                      const int32_t* blk_idx, const int32_t* cu, const PlanBufs& p, float scale,
-                     u16* o, int64_t o_st, int64_t o_sh, float* lse, bool dense, hipStream_t st);
+                     u16* o, int64_t o_st, int64_t o_sh, float* lse, bool dense, const QkNormParams* nrm,
+                     hipStream_t st);
 
 // Attention-side q/k norm + RoPE.  Forward: q, k in, qo, ko out.  Backward:
 // q, k (the forward's inputs) and dqh, dkh (gradients of its outputs) in,

@@ -72,6 +72,7 @@ extern "C" {
 #define MSA_OP_QKNORM_BWD 4
 #define MSA_OP_QSA_FWD 5
 #define MSA_OP_QSA_BWD 6
+#define MSA_OP_BWD_QKNORM 7
 
 /* Longest sequence this build accepts (1024 blocks of 128 tokens). */
 #define MSA_MAX_SEQLEN 131072
@@ -190,6 +191,54 @@ int msa_qk_norm_rope_bwd(const msa_dims* dims,
                          void* dk, int64_t dk_st, int64_t dk_sh,
                          float* dw_q, float* dw_k,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Attention with the attention-side q/k norm and partial RoPE fused in
+ * (miles docs "MiniMax-M3.1-Flash", section 1: per-head gemma q/k norm and RoPE
+ * on the first 64 dims ahead of the attention; Megatron-Bridge "MiniMax-M3",
+ * Architecture Notes).  q and k are the raw projections [T, H, 128]; every
+ * head row gets x * r * (1 + w) with r = 1 / sqrt(mean(x^2) + eps) and
+ * rotate-half RoPE at its sequence-local position, rounded once to bf16 (the
+ * arithmetic of msa_qk_norm_rope_fwd; only the order of the 128-term sum of
+ * squares may differ, so q and k may differ from that kernel's by one bf16
+ * unit in rare elements), and the block-sparse attention of msa_attn_fwd_ex
+ * runs on the result.  w_q, w_k: [128] bf16 weights, 2-byte aligned; eps >= 0,
+ * rope_base > 1, rope_dims must be 64; flags, outputs, strides and errors as
+ * msa_attn_fwd_ex.
+ *
+ * msa_attn_fwd_qknorm: the forward kernels apply the norm themselves (K in the
+ *   staging copy, q in the forward kernel's registers); the normalized q and k
+ *   are never written.  Workspace: msa_workspace_size(dims, MSA_OP_FWD, ...).
+ * msa_attn_bwd_qknorm: gradients with respect to the raw q and k (dq, dk with
+ *   their own strides), dv, and the weight gradients dw_q, dw_k (fp32 [128],
+ *   4-byte aligned, overwritten; sums over every (token, head) in a fixed
+ *   order).  It normalizes q and k into the workspace, runs the backward of
+ *   msa_attn_bwd_ex on them and then the backward of msa_qk_norm_rope_fwd.
+ *   Workspace: msa_workspace_size(dims, MSA_OP_BWD_QKNORM, ...).  With no
+ *   tokens only dw_q, dw_k are written (zeros).
+ */
+int msa_attn_fwd_qknorm(const msa_dims* dims,
+                        const void* q, int64_t q_st, int64_t q_sh,
+                        const void* k, int64_t k_st, int64_t k_sh,
+                        const void* v, int64_t v_st, int64_t v_sh,
+                        const void* w_q, const void* w_k, float eps, float rope_base, int32_t rope_dims,
+                        const int32_t* blk_idx, const int32_t* cu_seqlens, float softmax_scale, uint32_t flags,
+                        void* o, int64_t o_st, int64_t o_sh, float* lse,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+int msa_attn_bwd_qknorm(const msa_dims* dims,
+                        const void* q, int64_t q_st, int64_t q_sh,
+                        const void* k, int64_t k_st, int64_t k_sh,
+                        const void* v, int64_t v_st, int64_t v_sh,
+                        const void* w_q, const void* w_k, float eps, float rope_base, int32_t rope_dims,
+                        const void* o, int64_t o_st, int64_t o_sh, const float* lse,
+                        const void* dO, int64_t do_st, int64_t do_sh,
+                        const int32_t* blk_idx, const int32_t* cu_seqlens, float softmax_scale, uint32_t flags,
+                        void* dq, int64_t dq_st, int64_t dq_sh,
+                        void* dk, int64_t dk_st, int64_t dk_sh,
+                        void* dv, int64_t dv_st, int64_t dv_sh,
+                        float* dw_q, float* dw_k,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Block-sparse GQA attention forward ([M31] section 1: each query attends to
