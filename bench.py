@@ -328,8 +328,21 @@ def main():
     ws_qk = torch.empty(max(msa.msa_workspace_size(dims, msa.MSA_OP_QKNORM_BWD), 1), dtype=torch.uint8, device=dev)
     qk_fwd = lambda: msa.msa_qk_norm_rope_fwd(q, k, wq_a, wk_a, cu, p.max_seqlen, q_out=qh, k_out=kh)
     qk_bwd = lambda: msa.msa_qk_norm_rope_bwd(q, k, wq_a, wk_a, cu, p.max_seqlen, dq, dk, workspace=ws_qk)
+    # the attention with that norm fused in (msa_attn_fwd_qknorm / _bwd_qknorm) on the raw q, k, against the
+    # separate passes (norm forward + attention forward; attention backward + norm backward)
+    ws_fq = torch.empty(max(msa.msa_workspace_size(dims, msa.MSA_OP_BWD_QKNORM), 1), dtype=torch.uint8, device=dev)
+    fo, flse = torch.empty_like(q), torch.empty_like(lse)
+    fused_fwd = lambda: msa.msa_attn_fwd_qknorm(q, k, v, wq_a, wk_a, blk, cu, p.max_seqlen, out=fo, lse=flse,
+                                                workspace=ws[msa.MSA_OP_FWD])
+    fused_bwd = lambda: msa.msa_attn_bwd_qknorm(q, k, v, wq_a, wk_a, fo, flse, do, blk, cu, p.max_seqlen,
+                                                workspace=ws_fq)
+
+    def sep_fwd():
+        qk_fwd()
+        msa.msa_attn_fwd(qh, kh, v, blk, cu, p.max_seqlen, out=fo, lse=flse, workspace=ws[msa.MSA_OP_FWD])
     qk_ms = {}
-    for name, fn in (("fwd", qk_fwd), ("bwd", qk_bwd)):
+    for name, fn in (("fwd", qk_fwd), ("bwd", qk_bwd), ("fused_fwd", fused_fwd), ("fused_bwd", fused_bwd),
+                     ("sep_fwd", sep_fwd)):
         for _ in range(2):
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -408,6 +421,9 @@ def main():
         "qk_norm_rope_fwd_ms": round(qk_ms["fwd"], 4),
         "qk_norm_rope_bwd_ms": round(qk_ms["bwd"], 4),
         "qk_norm_rope_fwd_hbm_frac": round(qk_bytes["fwd"] / (qk_ms["fwd"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "attn_qknorm_fused_fwd_ms": round(qk_ms["fused_fwd"], 4),
+        "attn_qknorm_separate_fwd_ms": round(qk_ms["sep_fwd"], 4),
+        "attn_qknorm_fused_bwd_ms": round(qk_ms["fused_bwd"], 4),
         "qk_norm_rope_bwd_hbm_frac": round(qk_bytes["bwd"] / (qk_ms["bwd"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
