@@ -23,6 +23,7 @@
 //                       single chunk were finished by the dK/dV kernel.
 #include "attn_stage.h"
 #include "plan_blocks.h"
+#include "qk_rope.h"
 
 namespace msa {
 
@@ -45,10 +46,15 @@ constexpr int kTileTok = kAttnTile;
 // holding x[key score_key(kt, swz_slot(l) % 16)][dims 32ds + 8(l / 16) .. +7]
 // (the swizzled stage the transposed K^T reads expect; keys past the sequence
 // end are zero).  blockIdx.z: K (0-3) or V (4-7), a quarter of the runs each.
+// kNorm: K is raw; its rows get the attention-side norm and RoPE (qk_rope.h)
+// on the way into the copy, and the normalized rows are also written to khat
+// ([T][Hk][128]) for the dK/dV pass.
+template <bool kNorm>
 __global__ __launch_bounds__(256) void bwd_block_prep_kernel(const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
                                                              const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
                                                              const int32_t* __restrict__ cu, int S, int chunk,
-                                                             int ntiles, PlanBufs plan, int Hk,
+                                                             int ntiles, PlanBufs plan, int Hk, QkNormParams nrm,
+                                                             u16* __restrict__ khat,
                                                              u16* __restrict__ kop, u16* __restrict__ vop,
                                                              int32_t* __restrict__ clear, int nclear) {
   __shared__ int loc[2];
@@ -82,6 +88,56 @@ __global__ __launch_bounds__(256) void bwd_block_prep_kernel(const u16* __restri
   const int seq0 = cu[s];
   const int L = cu[s + 1] - seq0;
   u16* dst = (is_v ? vop : kop) + ((int64_t)gb * Hk + h) * (kHeadDim * kBlock);
+  if constexpr (kNorm) {
+    if (!is_v) {
+      // the part's 32 keys (tiles 2p, 2p+1): each row normalized and rotated
+      // by 8 lanes, kept in LDS, then copied in run order
+      __shared__ u16 krows[32][kHeadDim + 8];
+      {
+        const int row = threadIdx.x >> 3, j = threadIdx.x & 7;
+        const int kp = kBlock * c + score_key(2 * part + (row >> 4), row & 15);
+        const int kc = min(kp, L - 1);
+        float xv[16], w1[16], cs[4], sn[4];
+        const u16* src = k + (int64_t)(seq0 + kc) * k_st + (int64_t)h * k_sh + 4 * j;
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const uint2 wv = *reinterpret_cast<const uint2*>(src + 32 * qd);
+          xv[4 * qd] = __uint_as_float(wv.x << 16);
+          xv[4 * qd + 1] = __uint_as_float(wv.x & 0xFFFF0000u);
+          xv[4 * qd + 2] = __uint_as_float(wv.y << 16);
+          xv[4 * qd + 3] = __uint_as_float(wv.y & 0xFFFF0000u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w1[4 * qd + e] = 1.0f + bf2f(nrm.w_k[32 * qd + 4 * j + e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rope_angle(nrm.fr, 4 * j + e, kc, cs[e], sn[e]);
+        norm_rope_row8(xv, w1, cs, sn, nrm.eps);
+        u16* hrow = khat + ((int64_t)(seq0 + kc) * Hk + h) * kHeadDim + 4 * j;
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          uint32_t pk[2];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const u16 b = kp < L ? f2bf(xv[4 * qd + e]) : (u16)0;
+            krows[row][32 * qd + 4 * j + e] = b;
+            if (e & 1)
+              pk[e >> 1] |= (uint32_t)b << 16;
+            else
+              pk[e >> 1] = b;
+          }
+          if (kp < L) *reinterpret_cast<uint2*>(hrow + 32 * qd) = uint2{pk[0], pk[1]};
+        }
+      }
+      __syncthreads();
+      for (int i = 512 * part + threadIdx.x; i < 512 * part + 512; i += 256) {
+        const int run = i >> 6, ln = i & 63;
+        const int row = ((run >> 2) - 2 * part) * 16 + (swz_slot(ln) & 15);
+        *reinterpret_cast<u32x4*>(dst + (int64_t)i * 8) =
+            *reinterpret_cast<const u32x4*>(&krows[row][32 * (run & 3) + 8 * (ln >> 4)]);
+      }
+      return;
+    }
+  }
   for (int i = 512 * part + threadIdx.x; i < 512 * part + 512; i += 256) {
     const int run = i >> 6, ln = i & 63;
     const int kp = kBlock * c + score_key(run >> 2, swz_slot(ln) & 15);
@@ -98,7 +154,15 @@ constexpr int kUnionWords = 34;
 constexpr int kMaxUnion = kTileTok * kTopk;
 
 // kDense: every causal key of the token's sequence (the dense layers), blk_idx unused.
-template <bool kDense>
+// kNorm: q is raw.  The token's heads get the attention-side norm and RoPE
+// (qk_rope.h) after loading, the normalized rows go to qhat ([T][Hq][128]) for
+// the dK/dV pass, and the epilogue takes dq back through the norm:
+//     dy = RoPE^T(dq_hat),  g = dy (1 + w),
+//     dq = r g - x r^3 (g . x) / 128,   dw_q += sum over heads of dy x r
+// with the dw_q sums of the workgroup's 16 tokens and 16 heads added in a fixed
+// order into row (tile * Hk + head) of dwq_rows ([rows][256], columns
+// 128..255 zero).
+template <bool kDense, bool kNorm>
 __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
     const u16* __restrict__ kop, const u16* __restrict__ vop,
@@ -108,8 +172,11 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     const int32_t* __restrict__ blk_seq, const int32_t* __restrict__ tile_order, int S, int T, int Hk,
     float scale_log2, float scale,
     u16* __restrict__ dq, int64_t dq_st, int64_t dq_sh, float* __restrict__ delta, float* __restrict__ nlse,
-    const int32_t* __restrict__ seqitem, int chunk, int items_cap, int32_t* __restrict__ item_load) {
+    const int32_t* __restrict__ seqitem, int chunk, int items_cap, int32_t* __restrict__ item_load,
+    QkNormParams nrm, u16* __restrict__ qhat, float* __restrict__ dwq_rows) {
   __shared__ u32x4 kbuf[2][32][64];
+  __shared__ float qang[kNorm ? kDqWaves : 1][64];
+  static_assert(!kNorm || kTokPerWave == 1, "the norm assumes one token per wavefront");
   __shared__ u32x4 vbuf[2][32][64];
   __shared__ uint32_t bitmap[kUnionWords];
   // a dense tile's union is up to one sequence's 1024 blocks plus one per later sequence
@@ -119,7 +186,8 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
 
   // workgroup b runs KV head b % Hk of the tile in launch slot b / Hk
   const int h = blockIdx.x % Hk;
-  const int t0 = tile_order[blockIdx.x / Hk] * kTileTok;
+  const int tile_id = tile_order[blockIdx.x / Hk];
+  const int t0 = tile_id * kTileTok;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
@@ -245,6 +313,14 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     for (int ds = 0; ds < 4; ++ds) dma16s(base + 512 * ds, 16 * ln, lds_offset(dst + 64 * ds));
   };
   if (nsteps > 0) stage(0, 0);
+  if constexpr (kNorm) {
+    norm_rope_q(qb[0], nrm.w_q, nrm.eps, nrm.fr, pos_t, lane, qang[wave]);
+    if (tok_ok[0]) {
+      u16* hrow = qhat + ((int64_t)tok_t[0] * Hq + h * kGroup + li) * kHeadDim + 8 * g;
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) *reinterpret_cast<u32x4*>(hrow + 32 * ds) = __builtin_bit_cast(u32x4, qb[0][ds]);
+    }
+  }
   wait_copies();
   wait_all_loads();
   __syncthreads();
@@ -343,12 +419,92 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     lds_barrier();
   }
 
+  if constexpr (kNorm) {
+    // the lane holds dims 16 dt + 4 g + r of head li; pairs (i, i + 32) of the
+    // rotation sit in dt and dt + 2 of the same lane
+#pragma clang fp contract(off)
+    float x[8][4], dy[8][4];
+    float ss = 0.f;
+    {
+      const int tc = min(tok_t[0], T - 1);
+      const u16* qrow = q + (int64_t)tc * q_st + (int64_t)(h * kGroup + li) * q_sh;
 #pragma unroll
-  for (int j = 0; j < kTokPerWave; ++j) {
-    if (!tok_ok[j]) continue;
-    u16* out = dq + (int64_t)tok_t[j] * dq_st + (int64_t)(h * kGroup + li) * dq_sh;
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint2 wv = *reinterpret_cast<const uint2*>(qrow + 16 * dt + 4 * g);
+        x[dt][0] = __uint_as_float(wv.x << 16);
+        x[dt][1] = __uint_as_float(wv.x & 0xFFFF0000u);
+        x[dt][2] = __uint_as_float(wv.y << 16);
+        x[dt][3] = __uint_as_float(wv.y & 0xFFFF0000u);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<uint2*>(out + 16 * dt + 4 * g) = pack_bf16x4(dqacc[j][dt] * scale);
+        for (int r = 0; r < 4; ++r) ss += x[dt][r] * x[dt][r];
+      }
+    }
+    ss = sum_over_groups(ss);
+    const float rr = 1.0f / sqrtf(ss * (1.0f / 128.0f) + nrm.eps);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dy[dt][r] = dqacc[0][dt][r] * scale;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * dt + 4 * g + r;
+        const float c = qang[wave][i], sn = qang[wave][32 + i];
+        const float a = dy[dt][r], b = dy[dt + 2][r];
+        dy[dt][r] = (c * a) + (sn * b);
+        dy[dt + 2][r] = (c * b) - (sn * a);
+      }
+    float gr[8][4];
+    float dot = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        gr[dt][r] = dy[dt][r] * (1.0f + bf2f(nrm.w_q[16 * dt + 4 * g + r]));
+        dot += gr[dt][r] * x[dt][r];
+      }
+    dot = sum_over_groups(dot);
+    const float k3 = rr * rr * rr * dot * (1.0f / 128.0f);
+    if (tok_ok[0]) {
+      u16* out = dq + (int64_t)tok_t[0] * dq_st + (int64_t)(h * kGroup + li) * dq_sh;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        f32x4 dx;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dx[r] = (rr * gr[dt][r]) - (x[dt][r] * k3);
+        *reinterpret_cast<uint2*>(out + 16 * dt + 4 * g) = pack_bf16x4(dx);
+      }
+    }
+    // dw_q: the token's 16 heads (lanes li of the group) added by a butterfly,
+    // then the 16 tokens (wavefronts) in order; the K stage is free by now
+    float* red = reinterpret_cast<float*>(&kbuf[0][0][0]);  // [kDqWaves][128]
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float a = tok_ok[0] ? (dy[dt][r] * x[dt][r]) * rr : 0.f;
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) a += __shfl_xor(a, m);
+        if (li == 0) red[wave * kHeadDim + 16 * dt + 4 * g + r] = a;
+      }
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      float acc = 0.f;
+      if (threadIdx.x < kHeadDim)
+#pragma unroll
+        for (int w = 0; w < kDqWaves; ++w) acc += red[w * kHeadDim + threadIdx.x];
+      dwq_rows[((int64_t)tile_id * Hk + h) * 256 + threadIdx.x] = acc;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kTokPerWave; ++j) {
+      if (!tok_ok[j]) continue;
+      u16* out = dq + (int64_t)tok_t[j] * dq_st + (int64_t)(h * kGroup + li) * dq_sh;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<uint2*>(out + 16 * dt + 4 * g) = pack_bf16x4(dqacc[j][dt] * scale);
+    }
   }
 }
 
@@ -429,20 +585,24 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
 
 void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStream_t st) {
   const int T = (int)z.T, Hk = (int)z.Hk, S = (int)z.S;
+  const QkNormParams none{};
   {
     KernelTimer timer("bwd_block_prep", st);
-    bwd_block_prep_kernel<<<dim3((unsigned)(z.nblk_cap + 1), (unsigned)Hk, 8), 256, 0, st>>>(
-        a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.cu, (int)z.S, (int)z.chunk, (int)z.ntiles, p, Hk, a.kop,
-        a.vop, a.item_load, (int)(z.Hk * z.items_cap));
+    auto kern = a.nrm ? bwd_block_prep_kernel<true> : bwd_block_prep_kernel<false>;
+    kern<<<dim3((unsigned)(z.nblk_cap + 1), (unsigned)Hk, 8), 256, 0, st>>>(
+        a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.cu, (int)z.S, (int)z.chunk, (int)z.ntiles, p, Hk,
+        a.nrm ? *a.nrm : none, a.khat, a.kop, a.vop, a.item_load, (int)(z.Hk * z.items_cap));
   }
   {
     KernelTimer timer("attn_bwd_dq", st);
-    auto kern = a.dense ? attn_bwd_dq_kernel<true> : attn_bwd_dq_kernel<false>;
+    auto kern = a.nrm ? (a.dense ? attn_bwd_dq_kernel<true, true> : attn_bwd_dq_kernel<false, true>)
+                      : (a.dense ? attn_bwd_dq_kernel<true, false> : attn_bwd_dq_kernel<false, false>);
     kern<<<(unsigned)(z.ntiles * Hk), 64 * kDqWaves, 0, st>>>(
         a.q, a.q_st, a.q_sh, a.kop, a.vop, a.o, a.o_st, a.o_sh, a.dO, a.do_st,
         a.do_sh, a.lse, a.blk_idx, a.cu, p.blkbase, p.blk_seq, p.tile_order, S, T, Hk, a.scale * kLog2e, a.scale,
         a.dq, a.dq_st,
-        a.dq_sh, a.delta, a.nlse, p.seqitem, (int)z.chunk, (int)z.items_cap, a.item_load);
+        a.dq_sh, a.delta, a.nlse, p.seqitem, (int)z.chunk, (int)z.items_cap, a.item_load, a.nrm ? *a.nrm : none,
+        a.qhat, a.dwq_rows);
   }
   launch_attn_bwd_dkdv(z, a, p, st);
   {

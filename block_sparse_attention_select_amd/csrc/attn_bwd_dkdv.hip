@@ -412,8 +412,15 @@ void launch_attn_bwd_dkdv(const Sizes& z, const BwdArgs& a, const PlanBufs& p, h
   }
   KernelTimer timer("attn_bwd_dkdv", st);
   auto kern = a.dense ? attn_bwd_dkdv_kernel<true> : attn_bwd_dkdv_kernel<false>;
+  // with the attention-side norm fused in, the pass reads the normalized rows
+  // the prep and dQ kernels wrote
+  const int64_t D = kHeadDim;
+  const u16* q = a.nrm ? a.qhat : a.q;
+  const int64_t q_st = a.nrm ? z.Hq * D : a.q_st, q_sh = a.nrm ? D : a.q_sh;
+  const u16* k = a.nrm ? a.khat : a.k;
+  const int64_t k_st = a.nrm ? z.Hk * D : a.k_st, k_sh = a.nrm ? D : a.k_sh;
   kern<<<dim3((unsigned)z.items_cap, (unsigned)z.Hk), 256, 0, st>>>(
-      a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.dO, a.do_st, a.do_sh, a.nlse,
+      q, q_st, q_sh, k, k_st, k_sh, a.v, a.v_st, a.v_sh, a.dO, a.do_st, a.do_sh, a.nlse,
       a.delta, a.blk_idx, a.cu, p.blkbase, p.blk_seq, p.seqitem, p.totals, (int)z.S, (int)z.Hk, (int)z.chunk,
       (int)z.items_cap, a.item_order, a.scale * kLog2e, a.scale, a.item_count, a.part_dk, a.part_dv, a.dk, a.dk_st, a.dk_sh, a.dv,
       a.dv_st, a.dv_sh);

@@ -193,20 +193,21 @@ BwdWs carve_bwd(Carver& c, const Sizes& z) {
 // normalized q and k, their gradients, and the norm backward's partial rows.
 struct BwdQkWs {
   BwdWs bwd;
-  u16* qhat;
-  u16* khat;
-  u16* dqhat;
-  u16* dkhat;
-  float* partial;
+  u16* qhat;        // [T][Hq][128] normalized q (written by the dQ kernel)
+  u16* khat;        // [T][Hk][128] normalized k (written by the prep kernel)
+  u16* dkhat;       // [T][Hk][128] gradient of the normalized k
+  float* partial;   // weight-gradient rows: the k pass's, then one per (tile, KV head)
+  float* mid;       // first-stage sums of those rows
 };
+int64_t qknorm_partial_rows(const Sizes& z) { return msa::kQkBwdMaxRows + z.ntiles * z.Hk; }
 BwdQkWs carve_bwd_qknorm(Carver& c, const Sizes& z) {
   BwdQkWs w;
   w.bwd = carve_bwd(c, z);
   w.qhat = c.take<u16>(z.T * z.Hq * msa::kHeadDim);
   w.khat = c.take<u16>(z.T * z.Hk * msa::kHeadDim);
-  w.dqhat = c.take<u16>(z.T * z.Hq * msa::kHeadDim);
   w.dkhat = c.take<u16>(z.T * z.Hk * msa::kHeadDim);
-  w.partial = c.take<float>((int64_t)(msa::kQkBwdMaxRows + msa::kQkBwdMaxRows / 16 + 1) * 256);
+  w.partial = c.take<float>(qknorm_partial_rows(z) * 256);
+  w.mid = c.take<float>((qknorm_partial_rows(z) / 16 + 1) * 256);
   return w;
 }
 
@@ -215,7 +216,9 @@ void launch_bwd_on(const Sizes& z, const BwdWs& w, const u16* q, int64_t q_st, i
                    int64_t k_st, int64_t k_sh, const u16* v, int64_t v_st, int64_t v_sh, const u16* o, int64_t o_st,
                    int64_t o_sh, const float* lse, const u16* dO, int64_t do_st, int64_t do_sh, const int32_t* blk_idx,
                    const int32_t* cu, float scale, bool dense, u16* dq, int64_t dq_st, int64_t dq_sh, u16* dk,
-                   int64_t dk_st, int64_t dk_sh, u16* dv, int64_t dv_st, int64_t dv_sh, hipStream_t stream) {
+                   int64_t dk_st, int64_t dk_sh, u16* dv, int64_t dv_st, int64_t dv_sh, hipStream_t stream,
+                   const msa::QkNormParams* nrm = nullptr, u16* qhat = nullptr, u16* khat = nullptr,
+                   float* dwq_rows = nullptr) {
   msa::BwdArgs a;
   a.q = q; a.q_st = q_st; a.q_sh = q_sh;
   a.k = k; a.k_st = k_st; a.k_sh = k_sh;
@@ -239,6 +242,10 @@ void launch_bwd_on(const Sizes& z, const BwdWs& w, const u16* q, int64_t q_st, i
   a.item_order = w.item_order;
   a.part_dk = w.part_dk;
   a.part_dv = w.part_dv;
+  a.nrm = nrm;
+  a.qhat = qhat;
+  a.khat = khat;
+  a.dwq_rows = dwq_rows;
   msa::launch_attn_bwd(z, a, w.plan, stream);
 }
 
@@ -536,25 +543,24 @@ int msa_attn_bwd_qknorm(const msa_dims* dims, const void* q, int64_t q_st, int64
   Carver c(workspace);
   BwdQkWs w = carve_bwd_qknorm(c, z);
   const int64_t D = msa::kHeadDim;
-  // normalized q and k, the plain backward on them, then the norm's backward
+  // the backward with the norm fused into its prep and dQ kernels (dq comes
+  // out for the raw q, dk for the normalized k), then the norm's backward over
+  // the k rows and the weight-gradient sums
+  const msa::QkNormParams nrm{(const u16*)w_q, (const u16*)w_k, eps, msa::rope_freqs(rope_base)};
+  const int rows_k = msa::qk_norm_bwd_rows(z.T);
+  launch_bwd_on(z, w.bwd, (const u16*)q, q_st, q_sh, (const u16*)k, k_st, k_sh, (const u16*)v, v_st, v_sh,
+                (const u16*)o, o_st, o_sh, lse, (const u16*)do_, do_st, do_sh, dense ? nullptr : blk_idx, cu_seqlens,
+                softmax_scale, dense, (u16*)dq, dq_st, dq_sh, w.dkhat, z.Hk * D, D, (u16*)dv, dv_st, dv_sh, stream,
+                &nrm, w.qhat, w.khat, w.partial + (int64_t)rows_k * 256);
   msa::QkNormArgs a{};
-  a.q = (const u16*)q; a.q_st = q_st; a.q_sh = q_sh;
   a.k = (const u16*)k; a.k_st = k_st; a.k_sh = k_sh;
   a.w_q = (const u16*)w_q; a.w_k = (const u16*)w_k;
   a.eps = eps; a.rope_base = rope_base;
   a.cu = cu_seqlens;
-  a.qo = w.qhat; a.qo_st = z.Hq * D; a.qo_sh = D;
-  a.ko = w.khat; a.ko_st = z.Hk * D; a.ko_sh = D;
-  msa::launch_qk_norm_fwd(z, a, stream);
-  launch_bwd_on(z, w.bwd, w.qhat, z.Hq * D, D, w.khat, z.Hk * D, D, (const u16*)v, v_st, v_sh, (const u16*)o, o_st,
-                o_sh, lse, (const u16*)do_, do_st, do_sh, dense ? nullptr : blk_idx, cu_seqlens, softmax_scale, dense,
-                w.dqhat, z.Hq * D, D, w.dkhat, z.Hk * D, D, (u16*)dv, dv_st, dv_sh, stream);
-  a.dqh = w.dqhat; a.dqh_st = z.Hq * D; a.dqh_sh = D;
   a.dkh = w.dkhat; a.dkh_st = z.Hk * D; a.dkh_sh = D;
-  a.qo = (u16*)dq; a.qo_st = dq_st; a.qo_sh = dq_sh;
   a.ko = (u16*)dk; a.ko_st = dk_st; a.ko_sh = dk_sh;
   a.dw_q = dw_q; a.dw_k = dw_k;
-  msa::launch_qk_norm_bwd(z, a, w.partial, stream);
+  msa::launch_qk_norm_bwd_k(z, a, w.partial, (int)(z.ntiles * z.Hk), w.mid, stream);
   return launch_status();
 }
 

@@ -244,6 +244,12 @@ constexpr int kQkBwdMaxRows = 1024;  // workgroups of the backward (weight-gradi
 int qk_norm_bwd_rows(int64_t T);
 void launch_qk_norm_fwd(const Sizes& z, const QkNormArgs& a, hipStream_t st);
 void launch_qk_norm_bwd(const Sizes& z, const QkNormArgs& a, float* partial, hipStream_t st);
+// The backward over the k rows alone (q's part done elsewhere): dkh in, dx to
+// ko, partial rows [0, qk_norm_bwd_rows(T)) with a zero q half; then the
+// weight-gradient sums over those rows and the extra_rows rows after them,
+// through mid (one row per 16 rows summed).
+void launch_qk_norm_bwd_k(const Sizes& z, const QkNormArgs& a, float* partial, int extra_rows, float* mid,
+                          hipStream_t st);
 
 struct BwdArgs {
   const u16* q; int64_t q_st, q_sh;
@@ -269,6 +275,15 @@ struct BwdArgs {
   int32_t* item_order;  // [Hk][items_cap] items by decreasing load
   float* part_dk;   // [Hk][items_cap][128][128]
   float* part_dv;
+  // attention-side norm fused in (nrm != nullptr): q and k are raw; the prep
+  // and dQ kernels normalize them (writing the normalized rows to khat and
+  // qhat for the dK/dV pass), dq comes out for the raw q, and the dQ kernel
+  // leaves one weight-gradient row per (tile, head, token slot) in dwq_rows
+  // ([rows][256]: dw_q sums in columns 0..127, zeros in 128..255)
+  const QkNormParams* nrm = nullptr;
+  u16* qhat = nullptr;
+  u16* khat = nullptr;
+  float* dwq_rows = nullptr;
 };
 
 void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStream_t st);

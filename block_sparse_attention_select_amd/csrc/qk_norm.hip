@@ -300,4 +300,23 @@ void launch_qk_norm_bwd(const Sizes& z, const QkNormArgs& a, float* partial, hip
   }
 }
 
+void launch_qk_norm_bwd_k(const Sizes& z, const QkNormArgs& a, float* partial, int extra_rows, float* mid,
+                          hipStream_t st) {
+  const int rows_k = qk_norm_bwd_rows(z.T);
+  if (rows_k > 0) {
+    KernelTimer timer("qk_norm_rope_bwd", st);
+    // no q rows: the kernel's q half of each partial row stays zero
+    qk_norm_rope_bwd_kernel<<<(unsigned)rows_k, 64 * kQkWaves, 0, st>>>(
+        nullptr, 0, 0, a.k, a.k_st, a.k_sh, a.w_q, a.w_k, a.eps, rope_freqs(a.rope_base), a.cu, (int)z.S, (int)z.T, 0,
+        (int)z.Hk, nullptr, 0, 0, a.dkh, a.dkh_st, a.dkh_sh, nullptr, 0, 0, a.ko, a.ko_st, a.ko_sh, partial);
+  }
+  {
+    KernelTimer timer("qk_norm_dw_reduce", st);
+    const int rows = rows_k + extra_rows;
+    const int mid_rows = (rows + kReduceRows - 1) / kReduceRows;
+    if (mid_rows > 0) qk_norm_dw_stage1_kernel<<<(unsigned)mid_rows, 256, 0, st>>>(partial, rows, mid);
+    qk_norm_dw_stage2_kernel<<<1, 256, 0, st>>>(mid, mid_rows, a.dw_q, a.dw_k);
+  }
+}
+
 }  // namespace msa

@@ -212,9 +212,11 @@ int msa_qk_norm_rope_bwd(const msa_dims* dims,
  * msa_attn_bwd_qknorm: gradients with respect to the raw q and k (dq, dk with
  *   their own strides), dv, and the weight gradients dw_q, dw_k (fp32 [128],
  *   4-byte aligned, overwritten; sums over every (token, head) in a fixed
- *   order).  It normalizes q and k into the workspace, runs the backward of
- *   msa_attn_bwd_ex on them and then the backward of msa_qk_norm_rope_fwd.
- *   Workspace: msa_workspace_size(dims, MSA_OP_BWD_QKNORM, ...).  With no
+ *   order).  The norm is fused in: the backward's K prep kernel normalizes
+ *   k, its dQ kernel normalizes q after loading and takes dq back through the
+ *   norm in its epilogue (with that tile's dw_q sums); the normalized rows are
+ *   kept in the workspace for the dK/dV pass, whose dk then goes through the
+ *   norm's backward over the k rows.  Workspace: msa_workspace_size(dims, MSA_OP_BWD_QKNORM, ...).  With no
  *   tokens only dw_q, dw_k are written (zeros).
  */
 int msa_attn_fwd_qknorm(const msa_dims* dims,
