@@ -176,6 +176,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     QkNormParams nrm, u16* __restrict__ qhat, float* __restrict__ dwq_rows) {
   __shared__ u32x4 kbuf[2][32][64];
   __shared__ float qang[kNorm ? kDqWaves : 1][64];
+  __shared__ float wq1[kNorm ? kHeadDim : 1];
   static_assert(!kNorm || kTokPerWave == 1, "the norm assumes one token per wavefront");
   __shared__ u32x4 vbuf[2][32][64];
   __shared__ uint32_t bitmap[kUnionWords];
@@ -241,20 +242,27 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
       qb[j][ds] = tok_ok[j] ? load_bf16x8(qrow + 32 * ds + 8 * g) : zero_bf16x8();
       db[j][ds] = tok_ok[j] ? load_bf16x8(drow + 32 * ds + 8 * g) : zero_bf16x8();
     }
+    const u16* orow = o + (int64_t)tc * o_st + (int64_t)(h * kGroup + li) * o_sh;
+    bf16x8 ov[4];
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) ov[ds] = tok_ok[j] ? load_bf16x8(orow + 32 * ds + 8 * g) : zero_bf16x8();
+    // the norm's angles and 1 + w_q, formed while the token's loads are in
+    // flight; the union build's barriers publish them
+    if constexpr (kNorm) {
+      rope_angles_lds(nrm.fr, pos_t, lane, qang[wave]);
+      if (threadIdx.x < kHeadDim) wq1[threadIdx.x] = 1.0f + bf2f(nrm.w_q[threadIdx.x]);
+    }
     const int64_t row = (int64_t)tc * Hq + h * kGroup + li;
     const float l2 = lse[row];
     live[j] = tok_ok[j] && l2 > -INFINITY;
     lse2[j] = live[j] ? l2 * kLog2e : 0.f;
     // Delta = rowsum(dO * O) of head li: this lane's 32 dims (those of its dO
     // operand), then the four row groups
-    const u16* orow = o + (int64_t)tc * o_st + (int64_t)(h * kGroup + li) * o_sh;
     float dsum = 0.f;
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds) {
-      const bf16x8 ov = tok_ok[j] ? load_bf16x8(orow + 32 * ds + 8 * g) : zero_bf16x8();
+    for (int ds = 0; ds < 4; ++ds)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dsum += (float)db[j][ds][e] * (float)ov[e];
-    }
+      for (int e = 0; e < 8; ++e) dsum += (float)db[j][ds][e] * (float)ov[ds][e];
     dl[j] = sum_over_groups(dsum);
     // Delta and -LSE in base 2 (-inf for a row without keys) for the dK/dV pass
     if (tok_ok[j] && g == 0) {
@@ -314,7 +322,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
   };
   if (nsteps > 0) stage(0, 0);
   if constexpr (kNorm) {
-    norm_rope_q(qb[0], nrm.w_q, nrm.eps, nrm.fr, pos_t, lane, qang[wave]);
+    norm_rope_q_with(qb[0], [&](int d) { return wq1[d]; }, nrm.eps, lane, qang[wave]);
     if (tok_ok[0]) {
       u16* hrow = qhat + ((int64_t)tok_t[0] * Hq + h * kGroup + li) * kHeadDim + 8 * g;
 #pragma unroll
@@ -461,7 +469,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        gr[dt][r] = dy[dt][r] * (1.0f + bf2f(nrm.w_q[16 * dt + 4 * g + r]));
+        gr[dt][r] = dy[dt][r] * wq1[16 * dt + 4 * g + r];
         dot += gr[dt][r] * x[dt][r];
       }
     dot = sum_over_groups(dot);
@@ -476,17 +484,22 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
         *reinterpret_cast<uint2*>(out + 16 * dt + 4 * g) = pack_bf16x4(dx);
       }
     }
-    // dw_q: the token's 16 heads (lanes li of the group) added by a butterfly,
-    // then the 16 tokens (wavefronts) in order; the K stage is free by now
+    // dw_q: the token's 16 heads (the 16 lanes li of a row) added by a
+    // shift-and-add scan within the row (DPP row_shr 1, 2, 4, 8 with zero
+    // fill: lane li ends with the sum over heads 0..li, lane 15 with the
+    // row's total), then the 16 tokens (wavefronts) in order; the K stage is
+    // free by now
     float* red = reinterpret_cast<float*>(&kbuf[0][0][0]);  // [kDqWaves][128]
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float a = tok_ok[0] ? (dy[dt][r] * x[dt][r]) * rr : 0.f;
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) a += __shfl_xor(a, m);
-        if (li == 0) red[wave * kHeadDim + 16 * dt + 4 * g + r] = a;
+        a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x111, 0xF, 0xF, true));
+        a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x112, 0xF, 0xF, true));
+        a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x114, 0xF, 0xF, true));
+        a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x118, 0xF, 0xF, true));
+        if (li == 15) red[wave * kHeadDim + 16 * dt + 4 * g + r] = a;
       }
     __syncthreads();
     if (threadIdx.x < 256) {

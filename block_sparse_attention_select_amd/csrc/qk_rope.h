@@ -47,24 +47,26 @@ __device__ __forceinline__ void rope_angle(const RopeFreqs& fr, int i, int pos, 
   s = (float)sd;
 }
 
-// The 16 heads of one token held as MFMA B operands (lane li + 16 g holds
-// dims 32 ds + 8 g + e of head li in qb[ds][e]): normalized per head (the sum
-// of squares over the lane's 32 dims, then over the four lane groups) and
-// rotated in place; pairs (i, i + 32) of dims i = 8 g + e sit in qb[0], qb[1]
-// of the same lane.  The token's angles are formed once per wavefront (lanes
-// 0..31, one pair each) and passed through ang (64 floats of LDS).
-__device__ __forceinline__ void norm_rope_q(bf16x8 (&qb)[4], const u16* __restrict__ w, float eps,
-                                            const RopeFreqs& fr, int pos, int lane, float* ang) {
-#pragma clang fp contract(off)
+// The token's RoPE angles for a wavefront: lanes 0..31 write cos / sin of
+// pair `lane` to ang[lane], ang[32 + lane] (64 floats of LDS).
+__device__ __forceinline__ void rope_angles_lds(const RopeFreqs& fr, int pos, int lane, float* ang) {
   if (lane < 32) {
     float c, s;
     rope_angle(fr, lane, pos, c, s);
     ang[lane] = c;
     ang[32 + lane] = s;
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The 16 heads of one token held as MFMA B operands (lane li + 16 g holds
+// dims 32 ds + 8 g + e of head li in qb[ds][e]): normalized per head (the sum
+// of squares over the lane's 32 dims, then over the four lane groups) and
+// rotated in place; pairs (i, i + 32) of dims i = 8 g + e sit in qb[0], qb[1]
+// of the same lane.  w1(d) gives 1 + w of dim d; ang holds the token's angles
+// (rope_angles_lds), visible to the wavefront.
+template <class W1>
+__device__ __forceinline__ void norm_rope_q_with(bf16x8 (&qb)[4], W1 w1, float eps, int lane, const float* ang) {
+#pragma clang fp contract(off)
   const int g = lane >> 4;
   float x[4][8];
   float ss = 0.f;
@@ -81,7 +83,7 @@ __device__ __forceinline__ void norm_rope_q(bf16x8 (&qb)[4], const u16* __restri
 #pragma unroll
   for (int ds = 0; ds < 4; ++ds)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[ds][e] = (x[ds][e] * r) * (1.0f + bf2f(w[32 * ds + 8 * g + e]));
+    for (int e = 0; e < 8; ++e) y[ds][e] = (x[ds][e] * r) * w1(32 * ds + 8 * g + e);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float c = ang[8 * g + e], s = ang[32 + 8 * g + e];
@@ -94,6 +96,17 @@ __device__ __forceinline__ void norm_rope_q(bf16x8 (&qb)[4], const u16* __restri
   for (int ds = 0; ds < 4; ++ds)
 #pragma unroll
     for (int e = 0; e < 8; ++e) qb[ds][e] = (__bf16)y[ds][e];
+}
+
+// norm_rope_q_with on the weights in global memory, the angles formed here
+// (once per wavefront, through ang: 64 floats of LDS).
+__device__ __forceinline__ void norm_rope_q(bf16x8 (&qb)[4], const u16* __restrict__ w, float eps,
+                                            const RopeFreqs& fr, int pos, int lane, float* ang) {
+  rope_angles_lds(fr, pos, lane, ang);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  norm_rope_q_with(qb, [&](int d) { return 1.0f + bf2f(w[d]); }, eps, lane, ang);
 }
 
 }  // namespace msa
