@@ -175,6 +175,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
   __shared__ int ulist[kUnionCap];
   __shared__ int nunion;
   __shared__ float qang[kNorm ? kFwdWaves : 1][64];
+  __shared__ float wq1[kNorm ? kHeadDim : 1];
 
   // workgroup b runs KV head b % Hk of the tile in launch slot b / Hk
   const int h = blockIdx.x % Hk;
@@ -214,6 +215,12 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) qb[j][ds] = tok_ok[j] ? load_bf16x8(qrow + 32 * ds + 8 * g) : zero_bf16x8();
   }
+  // the norm's angles and 1 + w_q, formed while the loads are in flight; the
+  // union build's barriers publish them
+  if constexpr (kNorm) {
+    rope_angles_lds(nrm.fr, pos_t, lane, qang[wave]);
+    if (threadIdx.x < kHeadDim) wq1[threadIdx.x] = 1.0f + bf2f(nrm.w_q[threadIdx.x]);
+  }
 
   // 1. union of the tile's blocks
   if (threadIdx.x < kUnionWords) bitmap[threadIdx.x] = 0u;
@@ -248,7 +255,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
   __syncthreads();
   const int nu = nunion;
 
-  if constexpr (kNorm) norm_rope_q(qb[0], nrm.w_q, nrm.eps, nrm.fr, pos_t, lane, qang[wave]);
+  if constexpr (kNorm) norm_rope_q_with(qb[0], [&](int d) { return wq1[d]; }, nrm.eps, lane, qang[wave]);
 
   // per-token state (j = 0, 1 for tokens 2w, 2w+1)
   int tok_pos[kTokPerWave], tok_b[kTokPerWave], tok_base[kTokPerWave];

@@ -98,15 +98,4 @@ __device__ __forceinline__ void norm_rope_q_with(bf16x8 (&qb)[4], W1 w1, float e
     for (int e = 0; e < 8; ++e) qb[ds][e] = (__bf16)y[ds][e];
 }
 
-// norm_rope_q_with on the weights in global memory, the angles formed here
-// (once per wavefront, through ang: 64 floats of LDS).
-__device__ __forceinline__ void norm_rope_q(bf16x8 (&qb)[4], const u16* __restrict__ w, float eps,
-                                            const RopeFreqs& fr, int pos, int lane, float* ang) {
-  rope_angles_lds(fr, pos, lane, ang);
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  norm_rope_q_with(qb, [&](int d) { return 1.0f + bf2f(w[d]); }, eps, lane, ang);
-}
-
 }  // namespace msa
