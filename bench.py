@@ -80,17 +80,24 @@ def traffic_file(config: str) -> str:
     return os.path.join(PROFILES, f"traffic_{config}.json")
 
 
+# template flags of the library's kernel instances, in order; kernels not listed take (dense, qknorm)
+KERNEL_FLAGS = {"block_prep_kernel": ("qknorm",), "bwd_block_prep_kernel": ("qknorm",),
+                "qsa_prep_kernel": ("swizzled",), "attn_bwd_dkdv_kernel": ("dense",)}
+
+
 def kernel_key(raw: str) -> str:
-    """Library kernel name of a profiler record: `attn_fwd_kernel<false, false>(...)` -> `attn_fwd_kernel`;
-    a first template flag set (the dense instances) adds `_dense`, a second one (the fused q/k norm
-    instances) `_qknorm`; other kernels keep their name."""
+    """Library kernel name of a profiler record: `attn_fwd_kernel<false, true>(...)` -> `attn_fwd_qknorm_kernel`:
+    each template flag that is set adds its name (KERNEL_FLAGS: `_dense` for the dense instances, `_qknorm`
+    for the fused q/k norm ones, `_swizzled` for the narrow variant's dQ-stage copy); other kernels keep their
+    name."""
     n = raw.replace("(anonymous namespace)::", "").split("(")[0].replace("msa::", "").strip()
     if n.startswith("void "):
         n = n[len("void "):]
     m = re.search(r"<([^<>]*)>$", n)
     flags = [a.strip() for a in m.group(1).split(",")] if m else []
     n = re.sub(r"<[^<>]*>$", "", n)
-    suffix = ("_dense" if flags[:1] == ["true"] else "") + ("_qknorm" if flags[1:2] == ["true"] else "")
+    names = KERNEL_FLAGS.get(n, ("dense", "qknorm"))
+    suffix = "".join("_" + nm for nm, f in zip(names, flags) if f == "true")
     if suffix and n.endswith("_kernel"):
         n = n[:-len("_kernel")] + suffix + "_kernel"
     return n
