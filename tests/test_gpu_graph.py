@@ -59,3 +59,54 @@ def test_graph_replays_match_eager(gpu_lib, lengths, hk):
         print(f"[graph {lengths} hk={hk}] replay {rep} bitwise equal", flush=True)
         step()  # eager work on the same buffers between replays
         torch.cuda.synchronize()
+
+
+def test_graph_replays_match_eager_fused_norm(gpu_lib):
+    """The fused-norm forward and backward (msa_attn_fwd_qknorm / msa_attn_bwd_qknorm) captured together;
+    the backward's outputs are allocated inside the capture, from the graph's pool, and kept alive."""
+    msa = gpu_lib
+    p = synth.make_custom_pack([1300, 420, 9], num_q_heads=32, num_kv_heads=2, seed=72)
+    dev = torch.device("cuda:0")
+    g = lambda t: t.to(dev)
+    cu = g(p.cu_seqlens)
+    q, k, v, do = g(p.q), g(p.k), g(p.v), g(p.do)
+    gen = torch.Generator().manual_seed(73)
+    wq = g((0.1 * torch.randn(128, generator=gen)).bfloat16())
+    wk = g((0.1 * torch.randn(128, generator=gen)).bfloat16())
+    iq, ik, iwq, iwk = g(p.idx_q), g(p.idx_k), g(p.w_q), g(p.w_k)
+    T, Hq, Hk = p.total, p.num_q_heads, p.num_kv_heads
+    dims = msa.make_dims(T, len(p.lengths), p.max_seqlen, Hq, Hk)
+    ws = {op: torch.empty(max(msa.msa_workspace_size(dims, op), 1), dtype=torch.uint8, device=dev)
+          for op in (msa.MSA_OP_FWD, msa.MSA_OP_BWD_QKNORM)}
+    blk = msa.msa_index_select(iq, ik, iwq, iwk, cu, p.max_seqlen)
+    o, lse = torch.empty_like(q), torch.empty(T, Hq, dtype=torch.float32, device=dev)
+
+    def step():
+        msa.msa_attn_fwd_qknorm(q, k, v, wq, wk, blk, cu, p.max_seqlen, out=o, lse=lse, workspace=ws[msa.MSA_OP_FWD])
+        return msa.msa_attn_bwd_qknorm(q, k, v, wq, wk, o, lse, do, blk, cu, p.max_seqlen,
+                                       workspace=ws[msa.MSA_OP_BWD_QKNORM])
+
+    ref = [t.clone() for t in (o, lse, *step())]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        grads = step()
+    torch.cuda.synchronize()
+    outs = (o, lse, *grads)
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want, name in zip(outs, ref, ("O", "LSE", "dQ", "dK", "dV", "dw_q", "dw_k")):
+            assert torch.equal(got, want), f"replay {rep}: {name}"
+        print(f"[graph fused norm] replay {rep} bitwise equal", flush=True)
+        step()  # eager work on the same inputs between replays
+        torch.cuda.synchronize()
