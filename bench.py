@@ -36,12 +36,19 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 D = 128
 
-# Algorithmic work per unit, for the roofline of each kernel:
+# Algorithmic (counted) work per unit, for the roofline of each kernel.  The
+# counted fwd+bwd work is 14*D FLOP per (query head, selected causal key): the
+# forward's S and PV, and the backward's S recompute, dP, dV, dK and dQ.  The
+# backward runs in two passes that both need S and dP; the dK/dV pass is
+# charged S, dP, dV and dK, the dQ pass only dQ, so the per-kernel figures sum
+# to the counted total:
 #   select_scores: 2*D FLOP per causal (query, key) pair per index head;
 #   attn_fwd:      4*D FLOP per (query head, selected causal key)   [S, PV];
-#   attn_bwd_dq:   6*D FLOP per (query head, selected causal key)   [S, dP, dQ];
+#   attn_bwd_dq:   2*D FLOP per (query head, selected causal key)   [dQ];
 #   attn_bwd_dkdv: 8*D FLOP per (query head, selected causal key)   [S, dP, dV, dK].
-FLOP_PER_KEY = {"attn_fwd": 4 * D, "attn_bwd_dq": 6 * D, "attn_bwd_dkdv": 8 * D}
+FLOP_PER_KEY = {"attn_fwd": 4 * D, "attn_bwd_dq": 2 * D, "attn_bwd_dkdv": 8 * D}
+# What the kernels execute (the dQ pass recomputes S and dP): 18*D in all.
+EXEC_FLOP_PER_KEY = {"attn_fwd": 4 * D, "attn_bwd_dq": 6 * D, "attn_bwd_dkdv": 8 * D}
 
 
 def selected_keys(blk: np.ndarray, cu: np.ndarray, block: int = 128) -> int:
@@ -137,6 +144,63 @@ def summarize_pmc(dirs, config: str, copy_mib: int) -> dict:
     return out
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def measured_peaks(dev) -> dict:
+    """What this GPU reaches on two plain library kernels: a large bf16 GEMM
+    (torch.matmul, hipBLASLt) and a streaming pass over 1 GiB (torch.neg: read
+    n and write n bytes).  Reported beside the spec peaks, not instead of them."""
+    n = 8192
+    a = torch.randn(n, n, device=dev).bfloat16()
+    b = torch.randn(n, n, device=dev).bfloat16()
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    src = torch.zeros(2 ** 28, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    e0.record()
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return {"bf16_gemm_tflops": round(gemm_tflops, 1), "bf16_gemm": f"torch.matmul {n}x{n}x{n}",
+            "copy_gbs": round(copy_gbs, 1), "copy": "torch.neg over 1 GiB int32 (read + write)"}
+
+
+def select_parity(p, blk_np) -> dict:
+    """The GPU selection against the oracle's on every row: rows whose 16th/17th
+    oracle scores are within 1e-3 relative are near ties; mismatches are counted
+    inside and outside them."""
+    import oracle as O
+    f = lambda t: t.float().numpy()
+    res = O.index_select(f(p.idx_q), f(p.idx_k), f(p.w_q), f(p.w_k), p.cu_seqlens.numpy())
+    diff = (blk_np != res.blk_idx).any(axis=2)
+    tie = res.near_tie(1e-3)
+    return {"rows": int(diff.size), "near_tie_rows": int(tie.sum()),
+            "mismatch_in_near_ties": int((diff & tie).sum()), "mismatch_outside": int((diff & ~tie).sum())}, res
+
+
 def cpu_baseline(p, stride: int):
     """The oracle as it stands, on this host: select on the whole pack, fwd+bwd on
     every `stride`-th token, scaled to the full pack."""
@@ -161,7 +225,7 @@ def cpu_baseline(p, stride: int):
     return {"value": round(est_ms, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
             "sample": f"select on all {p.total} tokens ({t_sel:.1f} s); fwd+bwd on every {stride}th token "
                       f"({len(rows)} rows, {t_att:.1f} s) scaled x{p.total / len(rows):.0f}",
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def qsa_leg(msa, seed: int, steps: int, warmup: int) -> dict:
@@ -236,7 +300,8 @@ def main():
     ap.add_argument("--no-qsa", action="store_true", help="skip the narrow-block (qsa16k) leg")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-stride", type=int, default=3, help="oracle fwd+bwd sample: every n-th token")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle (timing and selection parity)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured GEMM and copy peaks")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after timing, copy MIB MiB device-to-device (a PMC calibration kernel)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
@@ -386,8 +451,10 @@ def main():
 
     dom = max(kt.items(), key=lambda kv: kv[1][1])[0]
     dom_ms = kt[dom][1] / kt[dom][0]
+    dom_exec = None
     if dom in FLOP_PER_KEY:
         dom_flop = FLOP_PER_KEY[dom] * per_qhead
+        dom_exec = EXEC_FLOP_PER_KEY[dom] * per_qhead
     elif dom == "select_scores":
         dom_flop = sel_flop
     else:
@@ -405,6 +472,16 @@ def main():
                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                     "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                     "avg_launch_ms": round(dom_ms, 4), "algorithmic_flop_per_launch": int(dom_flop)}
+        if dom_exec is not None:
+            roofline["executed_flop_per_launch"] = int(dom_exec)
+            roofline["executed_tflops"] = round(dom_exec / (dom_ms * 1e-3) / 1e12, 2)
+    per_kernel = {}
+    for name, fpk in FLOP_PER_KEY.items():
+        if name in kt:
+            ms = kt[name][1] / kt[name][0]
+            per_kernel[name] = {"ms": round(ms, 4),
+                                "counted_tflops": round(fpk * per_qhead / (ms * 1e-3) / 1e12, 1),
+                                "executed_tflops": round(EXEC_FLOP_PER_KEY[name] * per_qhead / (ms * 1e-3) / 1e12, 1)}
 
     line = {
         "metric": METRIC,
@@ -446,6 +523,8 @@ def main():
         "select_binding_frac": round(max(sel_bytes / (PEAK_HBM_GBS * 1e9), sel_flop / (PEAK_BF16_TFLOPS * 1e12))
                                      / (sel_ms * 1e-3), 4),
         "kernels_avg_ms": kernels,
+        "kernel_rates": per_kernel,
+        "fwd_bwd_executed_tflops": round(18 * D * per_qhead / (fb_ms * 1e-3) / 1e12, 2),
         "roofline": roofline,
         "context_gb300_ms": {"fwd_bwd": 6.7, "select": 0.62, "note": "pages' GB300 figures on unpublished 16k packs"},
     }
@@ -460,9 +539,15 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    if not args.no_peaks:
+        pk = measured_peaks(dev)
+        pk["fwd_bwd_frac_of_gemm"] = round(fb_tflops / pk["bf16_gemm_tflops"], 4)
+        line["measured_peaks"] = pk
     if not args.no_cpu_baseline:
+        line["select_parity"], _ = select_parity(p, blk_np)
         line["cpu_baseline"] = cpu_baseline(p, args.cpu_stride)
     else:
+        line["select_parity"] = None
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
 

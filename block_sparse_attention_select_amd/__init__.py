@@ -172,10 +172,58 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _bf16_view(t: torch.Tensor, name: str) -> Tuple[int, int]:
+def _bf16_view(t: torch.Tensor, name: str, shape: Optional[Tuple[int, int, int]] = None,
+               device: Optional[torch.device] = None) -> Tuple[int, int]:
     if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1 or not t.is_cuda:
         raise ValueError(f"{name}: expected a CUDA bf16 [T, H, D] tensor with a contiguous last dim")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
     return t.stride(0), t.stride(1)
+
+
+# The kernels read the tensors below as plain arrays (no strides), so the
+# binding rejects anything else before a launch; a wrong dtype or layout there
+# would be read as garbage or, for cu_seqlens, as out-of-range offsets.
+
+def _cu_seqlens(cu: torch.Tensor, device: torch.device) -> torch.Tensor:
+    if not isinstance(cu, torch.Tensor) or cu.dtype != torch.int32 or cu.dim() != 1 or cu.numel() < 1:
+        raise ValueError("cu_seqlens: expected a 1-D int32 tensor of S+1 offsets")
+    if not cu.is_cuda or cu.device != device or not cu.is_contiguous():
+        raise ValueError(f"cu_seqlens: expected a contiguous int32 tensor on {device}")
+    return cu
+
+
+def _weight(w: torch.Tensor, name: str, device: torch.device) -> torch.Tensor:
+    """A [128] bf16 norm weight; returns it contiguous (the caller keeps the
+    result alive until the launch is enqueued)."""
+    if not isinstance(w, torch.Tensor) or w.dtype != torch.bfloat16 or w.numel() != 128 or w.dim() != 1:
+        raise ValueError(f"{name}: expected a bf16 [128] tensor")
+    if not w.is_cuda or w.device != device:
+        raise ValueError(f"{name}: expected a tensor on {device}")
+    return w.contiguous()
+
+
+def _int32_rows(b: torch.Tensor, name: str, T: int, H: int, device: torch.device,
+                k: Optional[int] = None) -> torch.Tensor:
+    if not isinstance(b, torch.Tensor) or b.dtype != torch.int32 or b.dim() != 3:
+        raise ValueError(f"{name}: expected an int32 [T, H, K] tensor")
+    if b.shape[0] != T or b.shape[1] != H or (k is not None and b.shape[2] != k):
+        want = (T, H, k if k is not None else "K")
+        raise ValueError(f"{name}: expected shape {want}, got {tuple(b.shape)}")
+    if not b.is_cuda or b.device != device or not b.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor on {device}")
+    return b
+
+
+def _lse_rows(t: torch.Tensor, name: str, T: int, Hq: int, device: torch.device) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or tuple(t.shape) != (T, Hq):
+        raise ValueError(f"{name}: expected an fp32 [{T}, {Hq}] tensor")
+    if not t.is_cuda or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor on {device}")
+    return t
+
 
 
 def _workspace(dims: MsaDims, op: int, device, workspace: Optional[torch.Tensor]) -> Tuple[Optional[torch.Tensor], int]:
@@ -201,25 +249,32 @@ def msa_index_select(idx_q: torch.Tensor, idx_k: torch.Tensor, w_q: torch.Tensor
     """Block ids [T, Hk, 16] (int32, ascending, -1 padded) chosen by the frozen indexer.
     ``force_init`` keeps block 0 in every selection (msa_index_select_ex, MSA_SELECT_FORCE_INIT)."""
     lib = load()
-    T, Hk, _ = idx_q.shape
+    T, Hk, D = idx_q.shape
+    dev = idx_q.device
     sq = _bf16_view(idx_q, "idx_q")
-    sk = _bf16_view(idx_k, "idx_k")
+    if idx_k.dim() != 3 or idx_k.shape[0] != T or idx_k.shape[1] not in (1, Hk) or idx_k.shape[2] != D:
+        raise ValueError(f"idx_k: expected shape ({T}, {Hk} or 1, {D}), got {tuple(idx_k.shape)}")
+    sk = _bf16_view(idx_k, "idx_k", device=dev)
     if idx_k.shape[1] == 1 and Hk > 1:
         sk = (sk[0], 0)
+    cu_seqlens = _cu_seqlens(cu_seqlens, dev)
+    wq = _weight(w_q, "w_q", dev)
+    wk = _weight(w_k, "w_k", dev)
     dims = _dims_for(cu_seqlens, max_seqlen, 16 * Hk, Hk, T)
     if out is None:
-        out = torch.empty(T, Hk, 16, dtype=torch.int32, device=idx_q.device)
-    ws, nbytes = _workspace(dims, MSA_OP_SELECT, idx_q.device, workspace)
+        out = torch.empty(T, Hk, 16, dtype=torch.int32, device=dev)
+    out = _int32_rows(out, "out", T, Hk, dev, 16)
+    ws, nbytes = _workspace(dims, MSA_OP_SELECT, dev, workspace)
     if force_init:
         st = lib.msa_index_select_ex(ctypes.byref(dims), _ptr(idx_q), sq[0], sq[1], _ptr(idx_k), sk[0], sk[1],
-                                     _ptr(w_q.contiguous()), _ptr(w_k.contiguous()), float(eps), float(rope_base),
-                                     int(rope_dims), MSA_SELECT_FORCE_INIT, _ptr(cu_seqlens), _ptr(out), _ptr(ws),
-                                     nbytes, _stream(idx_q))
+                                     _ptr(wq), _ptr(wk), float(eps), float(rope_base), int(rope_dims),
+                                     MSA_SELECT_FORCE_INIT, _ptr(cu_seqlens), _ptr(out), _ptr(ws), nbytes,
+                                     _stream(idx_q))
         _check(st, "msa_index_select_ex")
     else:
         st = lib.msa_index_select(ctypes.byref(dims), _ptr(idx_q), sq[0], sq[1], _ptr(idx_k), sk[0], sk[1],
-                                  _ptr(w_q.contiguous()), _ptr(w_k.contiguous()), float(eps), float(rope_base),
-                                  int(rope_dims), _ptr(cu_seqlens), _ptr(out), _ptr(ws), nbytes, _stream(idx_q))
+                                  _ptr(wq), _ptr(wk), float(eps), float(rope_base), int(rope_dims),
+                                  _ptr(cu_seqlens), _ptr(out), _ptr(ws), nbytes, _stream(idx_q))
         _check(st, "msa_index_select")
     return out
 
@@ -233,15 +288,21 @@ def msa_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, blk_idx: Opt
     lib = load()
     T, Hq, D = q.shape
     Hk = k.shape[1]
+    dev = q.device
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
-    sq, sk, sv = _bf16_view(q, "q"), _bf16_view(k, "k"), _bf16_view(v, "v")
+    sq = _bf16_view(q, "q")
+    sk, sv = _bf16_view(k, "k", (T, Hk, D), dev), _bf16_view(v, "v", (T, Hk, D), dev)
+    cu_seqlens = _cu_seqlens(cu_seqlens, dev)
+    if not dense:
+        blk_idx = _int32_rows(blk_idx, "blk_idx", T, Hk, dev, 16)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
-        lse = torch.empty(T, Hq, dtype=torch.float32, device=q.device)
-    so = _bf16_view(out, "out")
+        lse = torch.empty(T, Hq, dtype=torch.float32, device=dev)
+    so = _bf16_view(out, "out", (T, Hq, D), dev)
+    lse = _lse_rows(lse, "lse", T, Hq, dev)
     dims = _dims_for(cu_seqlens, max_seqlen, Hq, Hk, T)
-    ws, nbytes = _workspace(dims, MSA_OP_FWD, q.device, workspace)
+    ws, nbytes = _workspace(dims, MSA_OP_FWD, dev, workspace)
     if dense:
         st = lib.msa_attn_fwd_ex(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0],
                                  sv[1], None, _ptr(cu_seqlens), scale, MSA_ATTN_DENSE, _ptr(out), so[0], so[1],
@@ -265,6 +326,7 @@ def msa_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Ten
     lib = load()
     T, Hq, D = q.shape
     Hk = k.shape[1]
+    dev = q.device
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     if dq is None:
         dq = torch.empty_like(q, memory_format=torch.contiguous_format)
@@ -272,10 +334,16 @@ def msa_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Ten
         dk = torch.empty_like(k, memory_format=torch.contiguous_format)
     if dv is None:
         dv = torch.empty_like(v, memory_format=torch.contiguous_format)
-    views = [_bf16_view(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do"),
-                                           (dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    qs, ks = (T, Hq, D), (T, Hk, D)
+    views = [_bf16_view(t, n, sh, dev) for t, n, sh in ((q, "q", qs), (k, "k", ks), (v, "v", ks), (o, "o", qs),
+                                                         (do, "do", qs), (dq, "dq", qs), (dk, "dk", ks),
+                                                         (dv, "dv", ks))]
+    cu_seqlens = _cu_seqlens(cu_seqlens, dev)
+    lse = _lse_rows(lse, "lse", T, Hq, dev)
+    if not dense:
+        blk_idx = _int32_rows(blk_idx, "blk_idx", T, Hk, dev, 16)
     dims = _dims_for(cu_seqlens, max_seqlen, Hq, Hk, T)
-    ws, nbytes = _workspace(dims, MSA_OP_BWD, q.device, workspace)
+    ws, nbytes = _workspace(dims, MSA_OP_BWD, dev, workspace)
     (sq, sk, sv, so, sdo, sdq, sdk, sdv) = views
     if dense:
         st = lib.msa_attn_bwd_ex(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0],
@@ -302,17 +370,25 @@ def msa_attn_fwd_qknorm(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: 
     lib = load()
     T, Hq, D = q.shape
     Hk = k.shape[1]
+    dev = q.device
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
-    sq, sk, sv = _bf16_view(q, "q"), _bf16_view(k, "k"), _bf16_view(v, "v")
+    sq = _bf16_view(q, "q")
+    sk, sv = _bf16_view(k, "k", (T, Hk, D), dev), _bf16_view(v, "v", (T, Hk, D), dev)
+    cu_seqlens = _cu_seqlens(cu_seqlens, dev)
+    wq = _weight(w_q, "w_q", dev)
+    wk = _weight(w_k, "w_k", dev)
+    if not dense:
+        blk_idx = _int32_rows(blk_idx, "blk_idx", T, Hk, dev, 16)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
-        lse = torch.empty(T, Hq, dtype=torch.float32, device=q.device)
-    so = _bf16_view(out, "out")
+        lse = torch.empty(T, Hq, dtype=torch.float32, device=dev)
+    so = _bf16_view(out, "out", (T, Hq, D), dev)
+    lse = _lse_rows(lse, "lse", T, Hq, dev)
     dims = _dims_for(cu_seqlens, max_seqlen, Hq, Hk, T)
-    ws, nbytes = _workspace(dims, MSA_OP_FWD, q.device, workspace)
+    ws, nbytes = _workspace(dims, MSA_OP_FWD, dev, workspace)
     st = lib.msa_attn_fwd_qknorm(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0],
-                                 sv[1], _ptr(w_q.contiguous()), _ptr(w_k.contiguous()), float(eps), float(rope_base),
+                                 sv[1], _ptr(wq), _ptr(wk), float(eps), float(rope_base),
                                  int(rope_dims), None if dense else _ptr(blk_idx), _ptr(cu_seqlens), scale,
                                  MSA_ATTN_DENSE if dense else 0, _ptr(out), so[0], so[1], _ptr(lse), _ptr(ws), nbytes,
                                  _stream(q))
@@ -329,19 +405,28 @@ def msa_attn_bwd_qknorm(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w_q: 
     lib = load()
     T, Hq, D = q.shape
     Hk = k.shape[1]
+    dev = q.device
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     dq = torch.empty_like(q, memory_format=torch.contiguous_format)
     dk = torch.empty_like(k, memory_format=torch.contiguous_format)
     dv = torch.empty_like(v, memory_format=torch.contiguous_format)
-    dw_q = torch.empty(128, dtype=torch.float32, device=q.device)
-    dw_k = torch.empty(128, dtype=torch.float32, device=q.device)
-    views = [_bf16_view(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do"),
-                                           (dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    dw_q = torch.empty(128, dtype=torch.float32, device=dev)
+    dw_k = torch.empty(128, dtype=torch.float32, device=dev)
+    qs, ks = (T, Hq, D), (T, Hk, D)
+    views = [_bf16_view(t, n, sh, dev) for t, n, sh in ((q, "q", qs), (k, "k", ks), (v, "v", ks), (o, "o", qs),
+                                                         (do, "do", qs), (dq, "dq", qs), (dk, "dk", ks),
+                                                         (dv, "dv", ks))]
     (sq, sk, sv, so, sdo, sdq, sdk, sdv) = views
+    cu_seqlens = _cu_seqlens(cu_seqlens, dev)
+    lse = _lse_rows(lse, "lse", T, Hq, dev)
+    wq = _weight(w_q, "w_q", dev)
+    wk = _weight(w_k, "w_k", dev)
+    if not dense:
+        blk_idx = _int32_rows(blk_idx, "blk_idx", T, Hk, dev, 16)
     dims = _dims_for(cu_seqlens, max_seqlen, Hq, Hk, T)
-    ws, nbytes = _workspace(dims, MSA_OP_BWD_QKNORM, q.device, workspace)
+    ws, nbytes = _workspace(dims, MSA_OP_BWD_QKNORM, dev, workspace)
     st = lib.msa_attn_bwd_qknorm(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0],
-                                 sv[1], _ptr(w_q.contiguous()), _ptr(w_k.contiguous()), float(eps), float(rope_base),
+                                 sv[1], _ptr(wq), _ptr(wk), float(eps), float(rope_base),
                                  int(rope_dims), _ptr(o), so[0], so[1], _ptr(lse), _ptr(do), sdo[0], sdo[1],
                                  None if dense else _ptr(blk_idx), _ptr(cu_seqlens), scale,
                                  MSA_ATTN_DENSE if dense else 0, _ptr(dq), sdq[0], sdq[1], _ptr(dk), sdk[0], sdk[1],
@@ -369,8 +454,11 @@ def msa_qsa_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, blk_idx:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
         lse = torch.empty(T, Hq, dtype=torch.float32, device=q.device)
-    so = _bf16_view(out, "out")
-    blk_idx = blk_idx.contiguous()
+    so = _bf16_view(out, "out", (T, Hq, D), q.device)
+    sk, sv = _bf16_view(k, "k", (T, Hk, D), q.device), _bf16_view(v, "v", (T, Hk, D), q.device)
+    cu_seqlens = _cu_seqlens(cu_seqlens, q.device)
+    lse = _lse_rows(lse, "lse", T, Hq, q.device)
+    blk_idx = _int32_rows(blk_idx, "blk_idx", T, Hk, q.device)
     dims = _qsa_dims(cu_seqlens, max_seqlen, Hq, Hk, T, blk_idx.shape[2])
     ws, nbytes = _workspace(dims, MSA_OP_QSA_FWD, q.device, workspace)
     st = lib.msa_qsa_attn_fwd(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0],
@@ -396,9 +484,14 @@ def msa_qsa_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch
         dk = torch.empty_like(k, memory_format=torch.contiguous_format)
     if dv is None:
         dv = torch.empty_like(v, memory_format=torch.contiguous_format)
-    views = [_bf16_view(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do"),
-                                           (dq, "dq"), (dk, "dk"), (dv, "dv"))]
-    blk_idx = blk_idx.contiguous()
+    dev = q.device
+    qs, ks = (T, Hq, D), (T, Hk, D)
+    views = [_bf16_view(t, n, sh, dev) for t, n, sh in ((q, "q", qs), (k, "k", ks), (v, "v", ks), (o, "o", qs),
+                                                         (do, "do", qs), (dq, "dq", qs), (dk, "dk", ks),
+                                                         (dv, "dv", ks))]
+    cu_seqlens = _cu_seqlens(cu_seqlens, dev)
+    lse = _lse_rows(lse, "lse", T, Hq, dev)
+    blk_idx = _int32_rows(blk_idx, "blk_idx", T, Hk, dev)
     dims = _qsa_dims(cu_seqlens, max_seqlen, Hq, Hk, T, blk_idx.shape[2])
     ws, nbytes = _workspace(dims, MSA_OP_QSA_BWD, q.device, workspace)
     (sq, sk, sv, so, sdo, sdq, sdk, sdv) = views
@@ -422,10 +515,17 @@ def msa_qk_norm_rope_fwd(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_
         q_out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if k_out is None:
         k_out = torch.empty(k.shape, dtype=k.dtype, device=k.device)
-    sq, sk, sqo, sko = (_bf16_view(t, n) for t, n in ((q, "q"), (k, "k"), (q_out, "q_out"), (k_out, "k_out")))
+    dev = q.device
+    D = q.shape[2]
+    sq, sk, sqo, sko = (_bf16_view(t, n, sh, dev) for t, n, sh in
+                        ((q, "q", (T, Hq, D)), (k, "k", (T, Hk, D)), (q_out, "q_out", (T, Hq, D)),
+                         (k_out, "k_out", (T, Hk, D))))
+    cu_seqlens = _cu_seqlens(cu_seqlens, dev)
+    wq = _weight(w_q, "w_q", dev)
+    wk = _weight(w_k, "w_k", dev)
     dims = _dims_for(cu_seqlens, max_seqlen, Hq, Hk, T)
     st = lib.msa_qk_norm_rope_fwd(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1],
-                                  _ptr(w_q.contiguous()), _ptr(w_k.contiguous()), float(eps), float(rope_base),
+                                  _ptr(wq), _ptr(wk), float(eps), float(rope_base),
                                   int(rope_dims), _ptr(cu_seqlens), _ptr(q_out), sqo[0], sqo[1], _ptr(k_out),
                                   sko[0], sko[1], _stream(q))
     _check(st, "msa_qk_norm_rope_fwd")
@@ -444,13 +544,19 @@ def msa_qk_norm_rope_bwd(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_
     dk = torch.empty(k.shape, dtype=k.dtype, device=k.device)
     dw_q = torch.empty(128, dtype=torch.float32, device=q.device)
     dw_k = torch.empty(128, dtype=torch.float32, device=q.device)
-    views = [_bf16_view(t, n) for t, n in ((q, "q"), (k, "k"), (dq_hat, "dq_hat"), (dk_hat, "dk_hat"),
-                                           (dq, "dq"), (dk, "dk"))]
+    dev = q.device
+    D = q.shape[2]
+    qs, ks = (T, Hq, D), (T, Hk, D)
+    views = [_bf16_view(t, n, sh, dev) for t, n, sh in ((q, "q", qs), (k, "k", ks), (dq_hat, "dq_hat", qs),
+                                                         (dk_hat, "dk_hat", ks), (dq, "dq", qs), (dk, "dk", ks))]
     sq, sk, sdqh, sdkh, sdq, sdk = views
+    cu_seqlens = _cu_seqlens(cu_seqlens, dev)
+    wq = _weight(w_q, "w_q", dev)
+    wk = _weight(w_k, "w_k", dev)
     dims = _dims_for(cu_seqlens, max_seqlen, Hq, Hk, T)
-    ws, nbytes = _workspace(dims, MSA_OP_QKNORM_BWD, q.device, workspace)
+    ws, nbytes = _workspace(dims, MSA_OP_QKNORM_BWD, dev, workspace)
     st = lib.msa_qk_norm_rope_bwd(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1],
-                                  _ptr(w_q.contiguous()), _ptr(w_k.contiguous()), float(eps), float(rope_base),
+                                  _ptr(wq), _ptr(wk), float(eps), float(rope_base),
                                   int(rope_dims), _ptr(cu_seqlens), _ptr(dq_hat), sdqh[0], sdqh[1], _ptr(dk_hat),
                                   sdkh[0], sdkh[1], _ptr(dq), sdq[0], sdq[1], _ptr(dk), sdk[0], sdk[1], _ptr(dw_q),
                                   _ptr(dw_k), _ptr(ws), nbytes, _stream(q))
@@ -461,6 +567,7 @@ def msa_qk_norm_rope_bwd(q: torch.Tensor, k: torch.Tensor, w_q: torch.Tensor, w_
 def msa_check_cu_seqlens(cu_seqlens: torch.Tensor, total_tokens: int, max_seqlen: int,
                          num_q_heads: int = 16, num_kv_heads: int = 1) -> int:
     """Debug check of the cu_seqlens contract (synchronizes the stream); returns the status."""
+    cu_seqlens = _cu_seqlens(cu_seqlens, cu_seqlens.device)
     dims = make_dims(total_tokens, cu_seqlens.numel() - 1, max_seqlen, num_q_heads, num_kv_heads)
     return int(load().msa_check_cu_seqlens(ctypes.byref(dims), _ptr(cu_seqlens), _stream(cu_seqlens)))
 

@@ -216,7 +216,9 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
     if (g < kTokPerWave && my_gb >= 0) {
       const int j = pos_t / chunk;
       const int item = seqitem[s_t] + (chunk / kBlock) * (j * (j + 1) / 2) + (my_gb - blkbase[s_t]);
-      atomicAdd(&item_load[(int64_t)h * items_cap + item], 1);
+      // items_cap is sized from max_seqlen: a sequence longer than that (a
+      // broken caller contract) must not count past the array
+      if (item < items_cap) atomicAdd(&item_load[(int64_t)h * items_cap + item], 1);
     }
   }
 

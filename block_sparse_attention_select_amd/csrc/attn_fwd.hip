@@ -12,8 +12,8 @@
 // S^T[key][head] = K Q^T (A = K rows, B = the token's q held in registers),
 // which leaves each lane with one head row: the online softmax needs only two
 // cross-lane steps per block.  O^T = V^T P^T then takes P straight from the
-// score registers (B operand) and V^T from a per-block transposed copy made
-// by block_transpose_kernel, so every MFMA operand is one 16-byte load.
+// score registers (B operand) and V^T from the per-block transposed copy that
+// block_prep_kernel writes, so every MFMA operand is one 16-byte load.
 //
 // Key order inside a 32-key step: score tile 2s holds keys 32s + 8g + {0..3}
 // and tile 2s+1 keys 32s + 8g + {4..7} in lane group g = lane / 16, so the

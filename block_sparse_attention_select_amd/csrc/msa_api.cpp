@@ -1,6 +1,7 @@
 // C ABI of the MSA library: argument validation, workspace carving and the
 // launch sequence of each operation on the caller's stream.  No host sync
-// (except the explicit debug check), no allocation, no state.
+// (except the explicit debug check) and no allocation; the only state is the
+// optional kernel-timing event pool (timing.cpp), off unless enabled.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>

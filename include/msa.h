@@ -33,8 +33,10 @@
  * query heads per KV head (one TP4 shard of MiniMax-M3 is 16 q / 1 kv).
  *
  * Ownership and execution: the caller allocates every input, output and the
- * workspace (size from msa_workspace_size).  The library allocates nothing,
- * keeps no pointer after a call returns and holds no state between calls.
+ * workspace (size from msa_workspace_size).  The library allocates nothing
+ * and keeps no pointer after a call returns.  Its only state between calls
+ * is the optional kernel-timing pool of msa_timing_enable (off by default;
+ * see below).
  * Work is enqueued on `stream` and runs asynchronously; outputs are
  * overwritten, never accumulated.  Identical inputs give bitwise identical
  * outputs.  Calls sharing one workspace must be ordered on one stream.

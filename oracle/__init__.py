@@ -18,6 +18,7 @@ from .msa_oracle import (  # noqa: F401
     rope_rotate_half,
     round_to_bf16,
     select_row,
+    selection_valid_within_ties,
     selectors_of_block,
     sequence_layout,
 )

@@ -235,11 +235,42 @@ def select_row(scores: np.ndarray, own: int, topk: int, force_init: bool = False
     return sorted(keep + forced), float(gap)
 
 
+def selection_valid_within_ties(scores: np.ndarray, own: int, ids: Sequence[int], topk: int,
+                                rel: float = 1e-3, force_init: bool = False) -> bool:
+    """Whether ``ids`` is a correct selection for a query in block ``own``
+    once near ties may go either way.
+
+    The rule ([M31] section 1) fixes the forced blocks (the own block, plus
+    block 0 under ``force_init``) and that every other chosen block scores at
+    least as high as every causal block left out.  Two correct selections may
+    differ only where the two scores are within ``rel`` of each other
+    (relative to the larger magnitude): the near-tie exemption of the parity
+    bar.  ``ids`` is a row of a block list: ascending, distinct, -1 padded.
+    """
+    ids = [int(c) for c in ids]
+    got = [c for c in ids if c >= 0]
+    if got != sorted(set(got)) or any(c > own for c in got) or ids[len(got):] != [-1] * (len(ids) - len(got)):
+        return False
+    if own + 1 <= topk:
+        return got == list(range(own + 1))
+    forced = {0, own} if force_init else {own}
+    if len(got) != topk or not forced <= set(got):
+        return False
+    chosen = [c for c in got if c not in forced]
+    left = [c for c in range(own) if c not in forced and c not in set(got)]
+    lo = F64(min(scores[c] for c in chosen))
+    hi = F64(max(scores[c] for c in left))
+    if lo >= hi:
+        return True
+    return abs(lo - hi) / max(abs(lo), abs(hi)) < rel
+
+
 @dataclass
 class SelectResult:
     blk_idx: np.ndarray        # int32 [T, Hk, topk], ascending, -1 padded
     gap: np.ndarray            # fp64 [T, Hk]: relative 16th/17th gap (inf when nothing is decided)
     rows: np.ndarray           # token ids covered (all tokens unless sampled)
+    scores: Optional[np.ndarray] = None   # fp32 [rows, Hk, blocks] block scores (-inf past own), if kept
 
     def near_tie(self, rel: float = 1e-3) -> np.ndarray:
         return self.gap < rel
@@ -249,14 +280,15 @@ def index_select(idx_q: np.ndarray, idx_k: np.ndarray, w_q: np.ndarray, w_k: np.
                  cu_seqlens: Sequence[int], block: int = 128, topk: int = 16,
                  eps: float = 1e-6, rope_base: float = 1e7, rope_dims: int = 64,
                  rows: Optional[np.ndarray] = None, round_bf16: bool = True,
-                 force_init: bool = False) -> SelectResult:
+                 force_init: bool = False, keep_scores: bool = False) -> SelectResult:
     """Frozen lightning-indexer block selection ([M31] section 1, [PR]).
 
     ``idx_q``: [T, Hk, D]; ``idx_k``: [T, Hk, D] or [T, 1, D] (one key head
     shared by every index head).  Index head h selects the blocks for KV head
     h.  ``rows`` restricts the output to a subset of tokens (sampled checks);
     the returned arrays then follow ``rows``.  ``force_init`` keeps block 0 in
-    every selection (see ``select_row``).
+    every selection (see ``select_row``).  ``keep_scores`` also returns every
+    row's block scores (for checking a selection that differs at a near tie).
     """
     idx_q = np.asarray(idx_q, dtype=F32)
     idx_k = np.asarray(idx_k, dtype=F32)
@@ -267,6 +299,9 @@ def index_select(idx_q: np.ndarray, idx_k: np.ndarray, w_q: np.ndarray, w_k: np.
     blk = np.full((len(all_rows), Hk, topk), -1, dtype=np.int32)
     gap = np.full((len(all_rows), Hk), np.inf, dtype=F64)
     row_slot = {int(t): n for n, t in enumerate(all_rows)}
+    if keep_scores:
+        max_len = int(max(cu[1:] - cu[:-1])) if len(cu) > 1 else 0
+        scores = np.full((len(all_rows), Hk, max(1, (max_len + block - 1) // block)), -np.inf, dtype=F32)
     for s in range(len(cu) - 1):
         a, b = int(cu[s]), int(cu[s + 1])
         mine = all_rows[(all_rows >= a) & (all_rows < b)]
@@ -289,7 +324,9 @@ def index_select(idx_q: np.ndarray, idx_k: np.ndarray, w_q: np.ndarray, w_k: np.
                 slot = row_slot[int(t)]
                 blk[slot, h, :len(ids)] = ids
                 gap[slot, h] = g
-    return SelectResult(blk_idx=blk, gap=gap, rows=all_rows)
+                if keep_scores:
+                    scores[slot, h, :sc.shape[1]] = sc[n]
+    return SelectResult(blk_idx=blk, gap=gap, rows=all_rows, scores=scores if keep_scores else None)
 
 
 # ---------------------------------------------------------------------------

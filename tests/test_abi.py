@@ -214,3 +214,61 @@ def test_qsa_argument_errors_launch_nothing():
     assert bwd(dv_sh=0) == msa.MSA_ERR_INVALID_ARG
     assert bwd(lse=None) == msa.MSA_ERR_INVALID_ARG
     assert bwd(n=msa.msa_workspace_size(d, msa.MSA_OP_QSA_BWD) - 256) == msa.MSA_ERR_WORKSPACE
+
+
+# ---------------------------------------------------------------- binding argument checks
+# The binding validates every tensor the kernels read as a plain array before
+# it calls into the library.  Dtype, shape and layout are checked before the
+# device, so these rejections show on a CPU too.
+CPU = torch.device("cpu")
+
+
+def test_binding_rejects_bad_cu_seqlens():
+    for bad in (torch.zeros(4, dtype=torch.int64), torch.zeros(2, 2, dtype=torch.int32),
+                torch.zeros(0, dtype=torch.int32), torch.zeros(4, dtype=torch.float32), [0, 5]):
+        with pytest.raises(ValueError, match="cu_seqlens"):
+            msa._cu_seqlens(bad, CPU)
+    with pytest.raises(ValueError, match="cu_seqlens"):              # host memory: never handed to a kernel
+        msa._cu_seqlens(torch.zeros(4, dtype=torch.int32), torch.device("cuda", 0))
+
+
+def test_binding_rejects_bad_norm_weights():
+    for bad in (torch.zeros(128, dtype=torch.float32), torch.zeros(64, dtype=torch.bfloat16),
+                torch.zeros(2, 128, dtype=torch.bfloat16)):
+        with pytest.raises(ValueError, match="w_q"):
+            msa._weight(bad, "w_q", CPU)
+
+
+def test_binding_weight_copy_is_kept_for_the_call():
+    """A strided weight comes back as a contiguous copy the caller holds (not a
+    temporary whose memory could be reused by the next copy before the launch)."""
+    w = torch.arange(256, dtype=torch.float32).bfloat16()[::2]
+    with pytest.raises(ValueError):
+        msa._weight(w, "w_q", torch.device("cuda", 0))                # device check comes after the layout
+    src = open(os.path.join(ROOT, "block_sparse_attention_select_amd", "__init__.py")).read()
+    assert "_ptr(w_q.contiguous())" not in src and "_ptr(w_k.contiguous())" not in src
+
+
+def test_binding_rejects_bad_block_lists_and_lse():
+    with pytest.raises(ValueError, match="blk_idx"):
+        msa._int32_rows(torch.zeros(10, 1, 16, dtype=torch.int64), "blk_idx", 10, 1, CPU, 16)
+    with pytest.raises(ValueError, match="blk_idx"):
+        msa._int32_rows(torch.zeros(10, 2, 16, dtype=torch.int32), "blk_idx", 10, 1, CPU, 16)
+    with pytest.raises(ValueError, match="blk_idx"):
+        msa._int32_rows(torch.zeros(10, 1, 8, dtype=torch.int32), "blk_idx", 10, 1, CPU, 16)
+    with pytest.raises(ValueError, match="blk_idx"):
+        msa._int32_rows(torch.zeros(10, 16, 1, dtype=torch.int32).transpose(1, 2), "blk_idx", 10, 1, CPU, 16)
+    with pytest.raises(ValueError, match="lse"):
+        msa._lse_rows(torch.zeros(10, 16, dtype=torch.float64), "lse", 10, 16, CPU)
+    with pytest.raises(ValueError, match="lse"):
+        msa._lse_rows(torch.zeros(10, 8, dtype=torch.float32), "lse", 10, 16, CPU)
+    with pytest.raises(ValueError, match="lse"):
+        msa._lse_rows(torch.zeros(16, 10, dtype=torch.float32).t(), "lse", 10, 16, CPU)
+
+
+def test_binding_rejects_mismatched_shapes():
+    k = torch.zeros(10, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        msa._bf16_view(k, "k", (10, 1, 128))
+    with pytest.raises(ValueError):
+        msa._bf16_view(torch.zeros(10, 1, 128, dtype=torch.float16), "k")

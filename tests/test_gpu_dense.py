@@ -9,12 +9,10 @@ import torch
 
 import oracle as O
 import synth
+from parity import check_grad, check_out
 
 pytestmark = pytest.mark.gpu
 
-O_TOL = 2e-2
-G_TOL = 1e-2
-LSE_TOL = 1e-3
 SCALE = 1 / math.sqrt(128)
 
 
@@ -24,16 +22,6 @@ def f32(t):
 
 def dev(t):
     return t.to("cuda")
-
-
-def say(*a):
-    print(*a, flush=True)
-
-
-def rel(a, b):
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
-    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
 
 
 def all_blocks(cu, hk, width=None):
@@ -64,13 +52,11 @@ def test_dense_parity(gpu_lib, lengths, hk, seed):
     blk = all_blocks(cu, hk)
     Ow, Lw = O.attention_forward(f32(p.q), f32(p.k), f32(p.v), blk, cu, SCALE)
     dQw, dKw, dVw = O.attention_backward(f32(p.q), f32(p.k), f32(p.v), f32(p.do), blk, cu, SCALE)
-    eo = float(np.abs(f32(o) - Ow).max())
-    el = float(np.abs(lse.cpu().numpy() - Lw).max())
-    rq, rk, rv = rel(f32(dq), dQw), rel(f32(dk), dKw), rel(f32(dv), dVw)
-    say(f"[dense {lengths} hk={hk}] O maxabs={eo:.3e} LSE maxabs={el:.3e} dQ rel={rq:.3e} dK rel={rk:.3e} "
-        f"dV rel={rv:.3e}")
-    assert eo <= O_TOL and el <= LSE_TOL
-    assert rq <= G_TOL and rk <= G_TOL and rv <= G_TOL
+    label = f"dense {lengths} hk={hk}"
+    check_out(label, f32(o), Ow, lse.cpu().numpy(), Lw)
+    check_grad(label, "dQ", f32(dq), dQw)
+    check_grad(label, "dK", f32(dk), dKw)
+    check_grad(label, "dV", f32(dv), dVw)
 
 
 def test_dense_equals_sparse_with_every_block_listed(gpu_lib):
@@ -95,12 +81,9 @@ def test_dense_long_sequence_sampled(gpu_lib):
     q, k, v, do = f32(p.q), f32(p.k), f32(p.v), f32(p.do)
     Ow, Lw = O.attention_forward(q, k, v, blk, cu, SCALE, rows=rows)
     dQw, _, _ = O.attention_backward(q, k, v, do, blk, cu, SCALE, rows=rows)
-    eo = float(np.abs(f32(o)[rows] - Ow).max())
-    el = float(np.abs(lse.cpu().numpy()[rows] - Lw).max())
-    rq = rel(f32(dq)[rows], dQw)
+    check_out("dense single8k", f32(o)[rows], Ow, lse.cpu().numpy()[rows], Lw)
+    check_grad("dense single8k", "dQ (sampled rows)", f32(dq)[rows], dQw)
     last = np.arange(8064, 8192)
     _, dKw, dVw = O.attention_backward(q, k, v, do, blk, cu, SCALE, rows=last)
-    rk, rv = rel(f32(dk)[last], dKw[last]), rel(f32(dv)[last], dVw[last])
-    say(f"[dense single8k] O maxabs={eo:.3e} LSE maxabs={el:.3e} dQ rel={rq:.3e} last-block dK rel={rk:.3e} "
-        f"dV rel={rv:.3e}")
-    assert eo <= O_TOL and el <= LSE_TOL and rq <= G_TOL and rk <= G_TOL and rv <= G_TOL
+    check_grad("dense single8k", "dK (last block)", f32(dk)[last], dKw[last])
+    check_grad("dense single8k", "dV (last block)", f32(dv)[last], dVw[last])

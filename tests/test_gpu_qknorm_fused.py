@@ -12,6 +12,7 @@ import torch
 
 import oracle as O
 import synth
+from parity import check_grad, rel
 
 pytestmark = pytest.mark.gpu
 
@@ -22,12 +23,6 @@ def f32(t):
 
 def dev(t):
     return t.to("cuda")
-
-
-def rel(a, b):
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
-    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
 
 
 def inputs(lengths, hk, seed):
@@ -81,8 +76,12 @@ def test_fused_norm_attention_matches_oracle_chain(gpu_lib, lengths, hk, seed, d
     print(f"[fused qknorm {lengths} hk={hk} dense={dense}] O maxabs {eo:.2e} LSE maxabs {el:.2e} dq {r[0]:.2e} "
           f"dk {r[1]:.2e} dv {r[2]:.2e} dw_q {r[3]:.2e} dw_k {r[4]:.2e}", flush=True)
     assert eo <= 2e-2 and el <= 1e-3
-    assert max(r[:3]) <= 1e-2
-    assert r[3] <= 2e-2 and r[4] <= 2e-2
+    label = f"fused qknorm {lengths} hk={hk} dense={dense}"
+    check_grad(label, "dq", f32(dq), dxq)
+    check_grad(label, "dk", f32(dk), dxk)
+    check_grad(label, "dv", f32(dv), dVw)
+    check_grad(label, "dw_q", dwq.cpu().numpy()[None], dwq_w[None])
+    check_grad(label, "dw_k", dwk.cpu().numpy()[None], dwk_w[None])
 
 
 def test_fused_forward_matches_separate_passes(gpu_lib):

@@ -2,8 +2,9 @@
 heads per KV head) through the C ABI (msa_qsa_attn_fwd / msa_qsa_attn_bwd)
 against the CPU oracle (the same attention functions with block=4).
 
-Tolerances as for the wide variant: O max-abs <= 2e-2, LSE max-abs <= 1e-3,
-dQ, dK, dV relative Frobenius error <= 1e-2 per tensor.
+Tolerances as for the wide variant (tests/parity.py): O max-abs <= 2e-2, LSE
+max-abs <= 1e-3, dQ, dK, dV relative Frobenius error <= 1e-2 per tensor plus a
+per-row and a max-abs bound.
 """
 import math
 
@@ -13,12 +14,10 @@ import torch
 
 import oracle as O
 import synth
+from parity import check_grad, check_out, say
 
 pytestmark = pytest.mark.gpu
 
-O_TOL = 2e-2
-G_TOL = 1e-2
-LSE_TOL = 1e-3
 SCALE = 1 / math.sqrt(256)
 
 
@@ -28,16 +27,6 @@ def f32(t):
 
 def dev(t):
     return t.to("cuda")
-
-
-def say(*a):
-    print(*a, flush=True)
-
-
-def rel(a, b):
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
-    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
 
 
 def pack(lengths, hk, topk, seed):
@@ -62,12 +51,10 @@ def check_full(p, blk_np, out, label):
     cu = p.cu_seqlens.numpy()
     Ow, Lw = O.attention_forward(f32(p.q), f32(p.k), f32(p.v), blk_np, cu, SCALE, block=4)
     dQw, dKw, dVw = O.attention_backward(f32(p.q), f32(p.k), f32(p.v), f32(p.do), blk_np, cu, SCALE, block=4)
-    eo = float(np.abs(f32(o) - Ow).max())
-    el = float(np.abs(lse.cpu().numpy() - Lw).max())
-    rq, rk, rv = rel(f32(dq), dQw), rel(f32(dk), dKw), rel(f32(dv), dVw)
-    say(f"[{label}] O maxabs={eo:.3e} LSE maxabs={el:.3e} dQ rel={rq:.3e} dK rel={rk:.3e} dV rel={rv:.3e}")
-    assert eo <= O_TOL and el <= LSE_TOL
-    assert rq <= G_TOL and rk <= G_TOL and rv <= G_TOL
+    check_out(label, f32(o), Ow, lse.cpu().numpy(), Lw)
+    check_grad(label, "dQ", f32(dq), dQw)
+    check_grad(label, "dK", f32(dk), dKw)
+    check_grad(label, "dV", f32(dv), dVw)
 
 
 def test_qsa_dense_equality(gpu_lib):
@@ -126,11 +113,9 @@ def test_qsa_fullsize_sampled(gpu_lib):
     q, k, v, do = f32(p.q), f32(p.k), f32(p.v), f32(p.do)
     Ow, Lw = O.attention_forward(q, k, v, blk, cu, SCALE, block=4, rows=rows)
     dQw, _, _ = O.attention_backward(q, k, v, do, blk, cu, SCALE, block=4, rows=rows)
-    eo = float(np.abs(f32(o)[rows] - Ow).max())
-    el = float(np.abs(lse.cpu().numpy()[rows] - Lw).max())
-    rq = rel(f32(dq)[rows], dQw)
-    say(f"[qsa16k rows={len(rows)}] O maxabs={eo:.3e} LSE maxabs={el:.3e} dQ rel={rq:.3e}")
-    assert eo <= O_TOL and el <= LSE_TOL and rq <= G_TOL
+    label = f"qsa16k rows={len(rows)}"
+    check_out(label, f32(o)[rows], Ow, lse.cpu().numpy()[rows], Lw)
+    check_grad(label, "dQ", f32(dq)[rows], dQw)
     # dK / dV of key tile c of sequence s come from every query that listed one of its blocks
     for s, c in [(0, 37), (2, 0)]:
         a, b = int(cu[s]), int(cu[s + 1])
@@ -138,9 +123,9 @@ def test_qsa_fullsize_sampled(gpu_lib):
         tile_blocks = np.arange(16 * c, 16 * c + 16)
         sel = a + np.nonzero(np.isin(blk[a:b, 0, :], tile_blocks).any(axis=1))[0]
         _, dKw, dVw = O.attention_backward(q, k, v, do, blk, cu, SCALE, block=4, rows=sel)
-        rk, rv = rel(f32(dk)[lo:hi], dKw[lo:hi]), rel(f32(dv)[lo:hi], dVw[lo:hi])
-        say(f"[qsa16k key tile s={s} c={c} selectors={len(sel)}] dK rel={rk:.3e} dV rel={rv:.3e}")
-        assert rk <= G_TOL and rv <= G_TOL
+        label = f"qsa16k key tile s={s} c={c} selectors={len(sel)}"
+        check_grad(label, "dK", f32(dk)[lo:hi], dKw[lo:hi])
+        check_grad(label, "dV", f32(dv)[lo:hi], dVw[lo:hi])
 
 
 def test_qsa_deterministic(gpu_lib):
@@ -181,13 +166,10 @@ def test_qsa_longest_sequence_most_blocks(gpu_lib):
     q, k, v, do = f32(p.q), f32(p.k), f32(p.v), f32(p.do)
     Ow, Lw = O.attention_forward(q, k, v, blk, cu, SCALE, block=4, rows=rows)
     dQw, _, _ = O.attention_backward(q, k, v, do, blk, cu, SCALE, block=4, rows=rows)
-    eo = float(np.abs(f32(o)[rows] - Ow).max())
-    el = float(np.abs(lse.cpu().numpy()[rows] - Lw).max())
-    rq = rel(f32(dq)[rows], dQw)
+    check_out("qsa 32768 K=1024", f32(o)[rows], Ow, lse.cpu().numpy()[rows], Lw)
+    check_grad("qsa 32768 K=1024", "dQ (sampled rows)", f32(dq)[rows], dQw)
     last = np.arange(32704, 32768)
     sel = np.nonzero(np.isin(blk[:, 0, :], np.arange(8176, 8192)).any(axis=1))[0]
     _, dKw, dVw = O.attention_backward(q, k, v, do, blk, cu, SCALE, block=4, rows=sel)
-    rk, rv = rel(f32(dk)[last], dKw[last]), rel(f32(dv)[last], dVw[last])
-    say(f"[qsa 32768 K=1024] O maxabs={eo:.3e} LSE maxabs={el:.3e} dQ rel={rq:.3e} last tile ({len(sel)} "
-        f"selectors) dK rel={rk:.3e} dV rel={rv:.3e}")
-    assert eo <= O_TOL and el <= LSE_TOL and rq <= G_TOL and rk <= G_TOL and rv <= G_TOL
+    check_grad(f"qsa 32768 K=1024 last tile ({len(sel)} selectors)", "dK", f32(dk)[last], dKw[last])
+    check_grad(f"qsa 32768 K=1024 last tile ({len(sel)} selectors)", "dV", f32(dv)[last], dVw[last])

@@ -127,6 +127,113 @@ def test_planted_selection_golden():
     assert res.gap[P["expected"][3][0], 0] > 1e-2
 
 
+# Hand-built score row for the gap pins: blocks 0..19 precede the own block 20.
+# The twenty scores, best first, are GAP_VALUES; block b holds rank GAP_RANK[b]
+# (1 = best).  Consecutive values are spaced unevenly (2, 3, 4, ... apart), so a
+# gap taken between the wrong pair of ranks gives a different number.
+GAP_VALUES = [50, 48, 45, 41, 36, 30, 23, 15, 6, -4, -15, -27, -40, -54, -69, -85, -102, -120, -139, -159]
+GAP_RANK = [1, 7, 16, 4, 12, 20, 2, 15, 9, 18, 5, 13, 3, 19, 10, 6, 17, 8, 14, 11]
+
+
+def gap_row(rank_of, shift=0.0, own_score=-75.0):
+    row = np.full(24, 1000.0, dtype=np.float32)      # blocks past the own block: never candidates
+    for b, r in enumerate(rank_of):
+        row[b] = GAP_VALUES[r - 1] + shift
+    row[20] = own_score                                # the own block is forced, its score unused
+    return row
+
+
+def test_select_row_gap_hand_built():
+    """The near-tie gap is |a - b| / max(|a|, |b|) between the last score-chosen
+    block and the best block left out: with the own block forced, the 15th and
+    16th best of blocks 0..19 (ranks 15 and 16: -69 and -85)."""
+    ids, gap = O.select_row(gap_row(GAP_RANK), 20, 16)
+    assert ids == sorted([b for b, r in enumerate(GAP_RANK) if r <= 15] + [20])
+    assert gap == pytest.approx(16 / 85, rel=1e-12)
+    # mixed signs: shifted by +71 the pair is (2, -14): |2 + 14| / 14, not (14 - 2) / 14
+    _, gap = O.select_row(gap_row(GAP_RANK, shift=71.0, own_score=2.5), 20, 16)
+    assert gap == pytest.approx(16 / 14, rel=1e-12)
+    # the own block's score does not enter the ranking even when it sits between the pair
+    for own_score in (-70.0, -80.0, 1e6, -1e6):
+        assert O.select_row(gap_row(GAP_RANK, own_score=own_score), 20, 16)[1] == pytest.approx(16 / 85, rel=1e-12)
+    # fewer than 16 earlier blocks: nothing is decided by score
+    assert O.select_row(gap_row(GAP_RANK), 15, 16)[1] == math.inf
+
+
+def test_select_row_gap_force_init_slot_count():
+    """With the initial block forced, 14 slots go by score among blocks 1..19.
+    Block 0 made the weakest: the gap falls between ranks 14 and 15 (-54, -69),
+    not 15 and 16 as without the rule.  Block 0 made the best: it leaves the
+    candidates, so ranks 2..15 are chosen and the gap is ranks 15/16 again."""
+    rank = list(GAP_RANK)
+    rank[0], rank[5] = rank[5], rank[0]                # block 0 now rank 20, block 5 rank 1
+    ids, gap = O.select_row(gap_row(rank), 20, 16, force_init=True)
+    assert ids == sorted([0, 20] + [b for b, r in enumerate(rank) if b > 0 and r <= 14])
+    assert gap == pytest.approx(15 / 69, rel=1e-12)
+    assert O.select_row(gap_row(rank), 20, 16)[1] == pytest.approx(16 / 85, rel=1e-12)
+    ids, gap = O.select_row(gap_row(GAP_RANK), 20, 16, force_init=True)
+    assert gap == pytest.approx(16 / 85, rel=1e-12)
+    assert ids == sorted([b for b, r in enumerate(GAP_RANK) if r <= 15] + [20])
+
+
+def test_planted_gap_closed_form():
+    """The gap through the whole oracle on the planted pack.  With every logit
+    position independent (content only in dims 64.., where RoPE is the
+    identity), a key x*e64 + e65 against the query e64 scores, up to the bf16
+    rounding of the features and eps, 128 * x / sqrt(x^2 + 1).  At block 16 of
+    sequence 0 the 15th and 16th best peaks are x = -0.75 and x = -0.875, so
+    the gap is about 0.0888; the neighbouring pairs would give 0.117 and 0.069.
+    The planted exact tie (blocks 3 and 9 of sequence 2) has gap 0."""
+    P = load_planted()
+    res = O.index_select(f32(P["idx_q"]), f32(P["idx_k"]), f32(P["w_q"]), f32(P["w_k"]),
+                         P["cu_seqlens"], block=P["block"], topk=P["topk"])
+    s = lambda x: x / math.sqrt(x * x + 1)
+    want = abs(s(-0.75) - s(-0.875)) / abs(s(-0.875))
+    t16 = [t for t, _, why in P["expected"] if "block 16: own block kept" in why][0]
+    assert res.gap[t16, 0] == pytest.approx(want, rel=2e-2)
+    t_tie = [t for t, _, why in P["expected"] if "tie (identical peak keys)" in why][0]
+    assert res.gap[t_tie, 0] == 0.0
+    assert res.near_tie()[t_tie, 0] and not res.near_tie()[t16, 0]
+    early = [t for t, ids, _ in P["expected"] if len([c for c in ids if c >= 0]) < 16]
+    assert all(np.isinf(res.gap[t, 0]) and not res.near_tie()[t, 0] for t in early)
+
+
+def test_selection_valid_within_ties_hand_built():
+    """The checker used for rows where two correct selections may differ.  On
+    the hand-built row: the oracle's own answer is valid; swapping the last
+    chosen block (rank 15) for the first left out (rank 16) is valid only when
+    the two scores are within 1e-3 relative; dropping the own block, a wrong
+    count, a non-causal id or an unsorted row is never valid."""
+    row = gap_row(GAP_RANK)
+    ids, _ = O.select_row(row, 20, 16)
+    pad = lambda xs: list(xs) + [-1] * (16 - len(xs))
+    assert O.selection_valid_within_ties(row, 20, ids, 16)
+    r15, r16 = GAP_RANK.index(15), GAP_RANK.index(16)
+    swapped = sorted([c for c in ids if c != r15] + [r16])
+    assert not O.selection_valid_within_ties(row, 20, swapped, 16)            # gap 16/85: far from a tie
+    near = row.copy()
+    near[r16] = np.float32(-69.05)                                              # gap 0.05/69 < 1e-3
+    assert O.selection_valid_within_ties(near, 20, swapped, 16)
+    near[r16] = np.float32(-69.1)                                               # gap 0.1/69 > 1e-3
+    assert not O.selection_valid_within_ties(near, 20, swapped, 16)
+    assert not O.selection_valid_within_ties(row, 20, sorted([c for c in ids if c != 20] + [r16]), 16)
+    assert not O.selection_valid_within_ties(row, 20, pad(ids[:15]), 16)
+    assert not O.selection_valid_within_ties(row, 20, sorted(ids[:15] + [21]), 16)
+    assert not O.selection_valid_within_ties(row, 20, ids[::-1], 16)
+    # below 16 causal blocks the answer is unique: blocks 0..b
+    assert O.selection_valid_within_ties(row, 3, pad([0, 1, 2, 3]), 16)
+    assert not O.selection_valid_within_ties(row, 3, pad([0, 1, 3]), 16)
+    # under the initial-block rule block 0 must be present
+    fi, _ = O.select_row(row, 20, 16, force_init=True)
+    assert O.selection_valid_within_ties(row, 20, fi, 16, force_init=True)
+    rank = list(GAP_RANK)
+    rank[0], rank[5] = rank[5], rank[0]                # block 0 the weakest: plain selection drops it
+    row0 = gap_row(rank)
+    plain, _ = O.select_row(row0, 20, 16)
+    assert 0 not in plain and O.selection_valid_within_ties(row0, 20, plain, 16)
+    assert not O.selection_valid_within_ties(row0, 20, plain, 16, force_init=True)
+
+
 def test_planted_selection_force_init_golden():
     """The forced initial block, on hand-derived planted cases."""
     P = load_planted()
