@@ -15,6 +15,15 @@ Bars:
   errors of the same order, so a correct kernel sits near 3e-3 per row.  A row
   that is wrong (dropped key, wrong block, stale value) is off by O(1) of its
   own norm and fails.
+  dQ rows get a larger absolute floor (ROW_ABS_DQ).  A dQ row is
+  scale * sum_j dS_j k_j over the query's keys, and the softmax makes
+  sum_j dS_j = 0 exactly, so for a query with few keys (the first tokens of a
+  sequence) the exact row is a small difference of large terms.  The kernel
+  rounds each dS_j to bf16 (2^-9 relative) and takes Delta from the bf16 O; those
+  errors do not cancel, which leaves an absolute error of about
+  2^-9 * scale * sum_j |dS_j| |k_j| however small the exact row is: up to
+  0.033 of the rms row norm on the tested packs.  dK and dV rows sum over many
+  (query, head) pairs with no such constraint (worst 0.0016 of the rms).
 """
 import numpy as np
 
@@ -25,6 +34,7 @@ LSE_TOL = 1e-3
 G_TOL = 1e-2
 ROW_REL = 2e-2
 ROW_ABS = 1e-2
+ROW_ABS_DQ = 1e-1
 MAX_REL = 2e-2
 TIE = 1e-3
 
@@ -39,26 +49,37 @@ def rel(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
 
 
-def grad_stats(got, want):
-    """(Frobenius rel, worst row ratio to its bound, max-abs / max|want|)."""
+def grad_stats(got, want, row_abs=ROW_ABS):
+    """(Frobenius rel, worst row ratio to its bound, max-abs / max|want|, text on the worst rows)."""
     g = np.asarray(got, np.float64)
     w = np.asarray(want, np.float64)
     d = g.shape[-1]
     g2, w2 = g.reshape(-1, d), w.reshape(-1, d)
+    if not w2.size:
+        return 0.0, 0.0, 0.0, ""
     wn = np.linalg.norm(w2, axis=1)
     en = np.linalg.norm(g2 - w2, axis=1)
-    rms = float(np.sqrt(np.mean(wn * wn))) if wn.size else 0.0
-    bound = ROW_REL * wn + ROW_ABS * rms
-    worst = float(np.max(en / np.maximum(bound, 1e-30))) if wn.size else 0.0
-    mx = float(np.abs(w2).max()) if wn.size else 0.0
-    mrel = float(np.abs(g2 - w2).max() / max(mx, 1e-30)) if wn.size else 0.0
-    return rel(g, w), worst, mrel
+    rms = float(np.sqrt(np.mean(wn * wn)))
+    bound = ROW_REL * wn + row_abs * rms
+    ratio = en / np.maximum(bound, 1e-30)
+    worst = float(ratio.max())
+    top = np.argsort(-ratio)[:3]
+    lead = w.shape[:-1]
+    info = "; ".join(f"row {np.unravel_index(i, lead)}: |err| {en[i]:.2e} |ref| {wn[i]:.2e}" for i in top)
+    info += f"; rms row norm {rms:.2e}"
+    mx = float(np.abs(w2).max())
+    mrel = float(np.abs(g2 - w2).max() / max(mx, 1e-30))
+    return rel(g, w), worst, mrel, info
 
 
 def check_grad(label, name, got, want, tol=G_TOL):
-    """Frobenius, per-row and max-abs bars for one gradient tensor."""
-    fro, worst, mrel = grad_stats(got, want)
+    """Frobenius, per-row and max-abs bars for one gradient tensor.  A tensor
+    named dQ / dq (a query gradient) takes the dQ row floor."""
+    row_abs = ROW_ABS_DQ if name.lower().startswith("dq") else ROW_ABS
+    fro, worst, mrel, info = grad_stats(got, want, row_abs)
     say(f"[{label}] {name}: rel {fro:.3e}, worst row {worst:.3f} of its bound, max-abs {mrel:.3e} of max")
+    if worst > 0.5:
+        say(f"[{label}] {name} worst rows: {info}")
     assert fro <= tol, (label, name, fro)
     assert worst <= 1.0, (label, name, worst)
     assert mrel <= MAX_REL, (label, name, mrel)
