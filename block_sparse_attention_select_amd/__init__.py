@@ -10,6 +10,7 @@ Entry points carry the C names:
 * ``msa_index_select`` -- frozen lightning-indexer block selection;
 * ``msa_attn_fwd``     -- block-sparse GQA attention forward (O, LSE);
 * ``msa_attn_bwd``     -- its backward (dQ, dK, dV);
+* ``msa_attn_fwd_noalloc`` -- the forward with the library's static scratch (no workspace);
 * ``msa_workspace_size``, ``msa_status_string``, ``msa_check_cu_seqlens``.
 
 ``MSAAttention`` wraps forward and backward as a ``torch.autograd.Function``.
@@ -46,7 +47,8 @@ EXPORTED = ("msa_workspace_size", "msa_index_select", "msa_index_select_ex", "ms
             "msa_attn_fwd_ex", "msa_attn_bwd_ex", "msa_attn_fwd_qknorm", "msa_attn_bwd_qknorm",
             "msa_qk_norm_rope_fwd", "msa_qk_norm_rope_bwd", "msa_qsa_attn_fwd", "msa_qsa_attn_bwd",
             "msa_status_string", "msa_check_cu_seqlens", "msa_timing_enable", "msa_timing_collect",
-            "msa_version")
+            "msa_version", "msa_attn_fwd_noalloc")
+MSA_NOALLOC_SCRATCH_BYTES = 72 << 20
 
 
 class MsaDims(ctypes.Structure):
@@ -96,6 +98,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.msa_attn_fwd.argtypes = [ctypes.POINTER(MsaDims), _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64,
                                  _P, _P, _F, _P, _I64, _I64, _P, _P, _SZ, _P]
     lib.msa_attn_fwd.restype = _I32
+    lib.msa_attn_fwd_noalloc.argtypes = [ctypes.POINTER(MsaDims), _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64,
+                                         _P, _P, _F, _P, _I64, _I64, _P, _P]
+    lib.msa_attn_fwd_noalloc.restype = _I32
     lib.msa_attn_bwd.argtypes = [ctypes.POINTER(MsaDims),
                                  _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64,
                                  _P, _P, _I64, _I64, _P, _P, _F,
@@ -313,6 +318,36 @@ def msa_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, blk_idx: Opt
                               sv[1], _ptr(blk_idx), _ptr(cu_seqlens), scale, _ptr(out), so[0], so[1], _ptr(lse),
                               _ptr(ws), nbytes, _stream(q))
         _check(st, "msa_attn_fwd")
+    return out, lse
+
+
+def msa_attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, blk_idx: torch.Tensor,
+                         cu_seqlens: torch.Tensor, max_seqlen: int, softmax_scale: Optional[float] = None, *,
+                         out: Optional[torch.Tensor] = None,
+                         lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """msa_attn_fwd with the library's static device scratch instead of a workspace: the library
+    allocates nothing (pass ``out`` and ``lse`` to allocate nothing here either).  Calls that overlap
+    on one GPU race on that scratch."""
+    lib = load()
+    T, Hq, D = q.shape
+    Hk = k.shape[1]
+    dev = q.device
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    sq = _bf16_view(q, "q")
+    sk, sv = _bf16_view(k, "k", (T, Hk, D), dev), _bf16_view(v, "v", (T, Hk, D), dev)
+    cu_seqlens = _cu_seqlens(cu_seqlens, dev)
+    blk_idx = _int32_rows(blk_idx, "blk_idx", T, Hk, dev, 16)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty(T, Hq, dtype=torch.float32, device=dev)
+    so = _bf16_view(out, "out", (T, Hq, D), dev)
+    lse = _lse_rows(lse, "lse", T, Hq, dev)
+    dims = _dims_for(cu_seqlens, max_seqlen, Hq, Hk, T)
+    st = lib.msa_attn_fwd_noalloc(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0],
+                                  sv[1], _ptr(blk_idx), _ptr(cu_seqlens), scale, _ptr(out), so[0], so[1], _ptr(lse),
+                                  _stream(q))
+    _check(st, "msa_attn_fwd_noalloc")
     return out, lse
 
 

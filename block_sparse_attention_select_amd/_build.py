@@ -14,7 +14,7 @@ LIB = os.path.join(PKG, "libmsa.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["select.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dkdv.hip", "qk_norm.hip", "qsa_attn.hip",
-           "msa_api.cpp",
+           "noalloc.hip", "msa_api.cpp",
            "timing.cpp"]
 
 # -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU forms.

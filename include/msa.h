@@ -364,6 +364,28 @@ int msa_attn_bwd_ex(const msa_dims* dims,
                     void* dv, int64_t dv_st, int64_t dv_sh,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, result and conventions as msa_attn_fwd, minus
+ * the workspace: the forward's workspace lives in a static device array of
+ * MSA_NOALLOC_SCRATCH_BYTES that each GPU holds until the process ends.  When
+ * msa_workspace_size(dims, MSA_OP_FWD) exceeds that size the call returns
+ * MSA_ERR_WORKSPACE before anything is launched (the array holds the forward's
+ * workspace of up to about 1150 (128-token block, KV head) pairs: the 32768-
+ * token, 4-KV-head layer fits).  The call allocates nothing; the first call on
+ * a device looks the array's address up once.  All calls on one GPU share its
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * and must be serialized by the caller.
+ */
+#define MSA_NOALLOC_SCRATCH_BYTES (72u << 20)
+int msa_attn_fwd_noalloc(const msa_dims* dims,
+                         const void* q, int64_t q_st, int64_t q_sh,
+                         const void* k, int64_t k_st, int64_t k_sh,
+                         const void* v, int64_t v_st, int64_t v_sh,
+                         const int32_t* blk_idx, const int32_t* cu_seqlens, float softmax_scale,
+                         void* o, int64_t o_st, int64_t o_sh, float* lse, hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char* msa_status_string(int status);
 

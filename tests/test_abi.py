@@ -272,3 +272,17 @@ def test_binding_rejects_mismatched_shapes():
         msa._bf16_view(k, "k", (10, 1, 128))
     with pytest.raises(ValueError):
         msa._bf16_view(torch.zeros(10, 1, 128, dtype=torch.float16), "k")
+
+
+def test_noalloc_forward_rejects_oversize_before_anything():
+    """The allocation-free forward checks the workspace it would need against its
+    static scratch first: a pack beyond it returns MSA_ERR_WORKSPACE with no
+    pointer read, no HIP call and no launch (null pointers here)."""
+    d = msa.make_dims(131072, 1, 131072, 32, 2)
+    assert msa.msa_workspace_size(d, msa.MSA_OP_FWD) > msa.MSA_NOALLOC_SCRATCH_BYTES
+    st = msa.load().msa_attn_fwd_noalloc(d, None, 0, 0, None, 0, 0, None, 0, 0, None, None, 0.1, None, 0, 0,
+                                         None, None)
+    assert st == msa.MSA_ERR_WORKSPACE
+    assert msa.msa_workspace_size(dims(), msa.MSA_OP_FWD) <= msa.MSA_NOALLOC_SCRATCH_BYTES
+    big = msa.make_dims(32768, 1, 32768, 64, 4)                  # the unsharded 32k layer fits
+    assert msa.msa_workspace_size(big, msa.MSA_OP_FWD) <= msa.MSA_NOALLOC_SCRATCH_BYTES
