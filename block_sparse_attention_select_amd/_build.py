@@ -59,5 +59,41 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-code sanitizers for the CPU checks of the ABI: address and undefined
+# behaviour instrumentation of the host side of every source (each
+# -fsanitize= applies to the host pass only; device code is built as usual).
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+ASAN_DIR = os.path.join(PKG, "_build_asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libmsa_asan.so")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """libmsa_asan.so: the library with sanitized host code (for tests/abi_host_check.cpp)."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+
+    def one(src: str) -> str:
+        obj = os.path.join(ASAN_DIR, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc(), *FLAGS, *SANITIZE, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if verbose or r.returncode != 0:
+            print(" ".join(cmd))
+            print(r.stdout + r.stderr)
+        if r.returncode != 0:
+            raise RuntimeError(f"compiling {src} (sanitized) failed")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(one, SOURCES))
+    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", *SANITIZE, "-o", ASAN_LIB, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if verbose or r.returncode != 0:
+        print(" ".join(cmd))
+        print(r.stdout + r.stderr)
+    if r.returncode != 0:
+        raise RuntimeError("linking libmsa_asan.so failed")
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
