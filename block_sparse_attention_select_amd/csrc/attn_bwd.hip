@@ -10,11 +10,24 @@
 // the key-block sums running over every (query, head) of the group that
 // selected the block.
 //
+// Two pipelines.  Sparse layers (unless the workspace would exceed
+// kDsBufMaxBytes of dS): bwd_block_prep (K copies, plan) -> bwd_delta_kernel
+// (Delta, -LSE log2(e), dK/dV item loads) -> dK/dV, which also writes every
+// (selecting query, block)'s dS in bf16 -> dkdv_reduce -> attn_bwd_dq_ds_kernel
+// (dQ = scale dS K from the stored dS, one product per selected block instead
+// of three).  Dense layers and the fused attention-side norm: bwd_block_prep
+// (K and V copies) -> attn_bwd_dq_kernel (recomputes S and dP) -> dK/dV ->
+// dkdv_reduce.
+//
 // Kernels:
 //   attn_bwd_dq_kernel  token-major dQ, tiles of 16 tokens walking the union
 //                       of their blocks with K, V and K^T staged in LDS; it
 //                       also forms Delta = rowsum(dO * O) and -LSE * log2(e)
 //                       for the dK/dV pass;
+//   bwd_delta_kernel    Delta and -LSE * log2(e) per (token, query head), and
+//                       the dK/dV item loads, ahead of the dK/dV pass;
+//   attn_bwd_dq_ds_kernel token-major dQ from the dS the dK/dV pass stored:
+//                       the same tiles and union walk with only K^T staged;
 //   attn_bwd_dkdv_kernel (attn_bwd_dkdv.hip) key-block-major dK/dV per chunk
 //                       of selecting queries;
 //   dkdv_reduce_kernel  sums the per-chunk slices of a block in chunk order
@@ -524,6 +537,283 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Delta = rowsum(dO * O) and -LSE * log2(e) (-inf for a row without keys) per
+// (token, query head) for the dK/dV pass, and each (token, listed block)
+// counted toward its dK/dV work item's load (the counters were zeroed by the
+// prep kernel).  Workgroup per (16 consecutive tokens, KV head), wavefront w
+// taking token w: lane (head li, group g) sums dims 32 ds + 8 g .. +7 of its
+// head, the same lanes and order as the dQ kernel's prologue.  The counts of
+// the tokens in the first token's (sequence, query chunk) are gathered in an
+// LDS histogram over its blocks and added with one global atomic per block;
+// other tokens (a tile crossing a chunk or sequence) add theirs directly.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void bwd_delta_kernel(
+    const u16* __restrict__ o, int64_t o_st, int64_t o_sh, const u16* __restrict__ dO, int64_t do_st,
+    int64_t do_sh, const float* __restrict__ lse, const int32_t* __restrict__ blk_idx,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ seqitem, int S, int T, int Hk, int chunk,
+    int items_cap, float* __restrict__ delta, float* __restrict__ nlse, int32_t* __restrict__ item_load) {
+  constexpr int kHistBins = kMaxBlocks;
+  __shared__ int hist[kHistBins];
+  const int h = blockIdx.y;
+  const int t0 = blockIdx.x * 16;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int li = lane & 15;
+  const int t = t0 + wave;
+  for (int i = threadIdx.x; i < kHistBins; i += 1024) hist[i] = 0;
+  const int s0 = find_seq(cu, S, t0);
+  const int j0 = (t0 - cu[s0]) / chunk;
+  const int base0 = seqitem[s0] + (chunk / kBlock) * (j0 * (j0 + 1) / 2);
+  __syncthreads();
+  if (t < T) {
+    const u16* orow = o + (int64_t)t * o_st + (int64_t)(h * kGroup + li) * o_sh;
+    const u16* drow = dO + (int64_t)t * do_st + (int64_t)(h * kGroup + li) * do_sh;
+    bf16x8 db[4], ov[4];
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      db[ds] = load_bf16x8(drow + 32 * ds + 8 * g);
+      ov[ds] = load_bf16x8(orow + 32 * ds + 8 * g);
+    }
+    const int64_t row = (int64_t)t * (Hk * kGroup) + h * kGroup + li;
+    const float l2 = lse[row];
+    const int s = find_seq(cu, S, t);
+    const int pos = t - cu[s];
+    const int c = blk_idx[((int64_t)t * Hk + h) * kTopk + li];
+    float dsum = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum += (float)db[ds][e] * (float)ov[ds][e];
+    const float dl = sum_over_groups(dsum);
+    if (g == 0) {
+      delta[row] = dl;
+      nlse[row] = l2 > -INFINITY ? -l2 * kLog2e : -INFINITY;
+      if (c >= 0 && c <= pos / kBlock) {
+        const int j = pos / chunk;
+        if (s == s0 && j == j0) {
+          atomicAdd(&hist[c], 1);
+        } else {
+          const int item = seqitem[s] + (chunk / kBlock) * (j * (j + 1) / 2) + c;
+          // items_cap is sized from max_seqlen: a sequence longer than that
+          // (a broken caller contract) must not count past the array
+          if (item < items_cap) atomicAdd(&item_load[(int64_t)h * items_cap + item], 1);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kHistBins; i += 1024) {
+    const int n = hist[i];
+    if (n > 0 && base0 + i < items_cap) atomicAdd(&item_load[(int64_t)h * items_cap + base0 + i], n);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ from the stored dS.  The dK/dV pass left, for every (token, KV head,
+// listed block), the block's dS^T in the B-operand order of dQ^T = K^T dS^T:
+// quarter qq (keys 32 qq .. +31), lane (head li, group g) holding keys
+// 32 qq + 8 g .. +7 (16 bytes; ds_buf[((t Hk + h) 16 + slot) 4 + qq][lane],
+// slot = the block's first position in the token's list).  The tiling and
+// union walk are the dQ kernel's with only K staged (its K^T operands read
+// transposed), three K buffers deep: block u + 2 is copied while block u is
+// used, and each wavefront's dS loads run two of its own blocks ahead, so the
+// wait that ends a step (for block u + 1's copies) leaves the newest loads in
+// flight (loads and copies complete in issue order).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_ds_kernel(
+    const u16* __restrict__ kop, const u16* __restrict__ ds_buf, const int32_t* __restrict__ blk_idx,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ blkbase, const int32_t* __restrict__ tile_order,
+    int S, int T, int Hk, float scale, u16* __restrict__ dq, int64_t dq_st, int64_t dq_sh) {
+  __shared__ u32x4 kbuf[3][32][64];
+  __shared__ uint32_t bitmap[kUnionWords];
+  __shared__ int ulist[kMaxUnion];
+  __shared__ int nunion;
+
+  const int h = blockIdx.x % Hk;
+  const int tile_id = tile_order[blockIdx.x / Hk];
+  const int t0 = tile_id * kTileTok;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int li = lane & 15;
+
+  const int t = t0 + wave;
+  const bool tvalid = t < T;
+  int s_t = 0, pos_t = 0, b_t = -1, my_gb = -1;
+  if (tvalid && g == 0) {
+    s_t = find_seq(cu, S, t);
+    pos_t = t - cu[s_t];
+    b_t = pos_t / kBlock;
+    const int c = blk_idx[((int64_t)t * Hk + h) * kTopk + li];
+    if (c >= 0 && c <= b_t) my_gb = blkbase[s_t] + c;
+  }
+  const int gb_lo = blkbase[find_seq(cu, S, t0)];
+  const int tok_pos = __builtin_amdgcn_readlane(pos_t, 0);
+  const int tok_b = __builtin_amdgcn_readlane(b_t, 0);
+  const int tok_base = tvalid ? blkbase[__builtin_amdgcn_readlane(s_t, 0)] : 0;
+
+  // the token's blocks in the order the walk meets them (ascending global id),
+  // each at the first list position holding it: lane li (group 0) gets the
+  // rank of its entry, or -1 for a hole or a repeat
+  int rank = -1;
+  {
+    bool first = my_gb >= 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < li && __builtin_amdgcn_readlane(my_gb, j) == my_gb) first = false;
+    const int fg = first ? my_gb : 0x7fffffff;
+    int r = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r += __builtin_amdgcn_readlane(fg, j) < fg ? 1 : 0;
+    if (first && g == 0) rank = r;
+  }
+  // the token's 16 x 4 KB of dS through a buffer resource: a load at an offset
+  // past its 64 KB (no block of that rank, or no token) returns zeros without
+  // reading memory, so every hit issues the same loads
+  const __amdgpu_buffer_rsrc_t dsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(ds_buf + (((int64_t)(tvalid ? t : 0) * Hk + h) * kTopk) * 4 * 512), (short)0,
+      tvalid ? kTopk * 4096 : 0, 0x00020000);
+  // loads the dS of the k-th block the walk will meet (zeros when there is none)
+  auto load_ds = [&](int k, bf16x8* dst) {
+    const uint64_t m = __ballot(rank == k);
+    const int off = (m != 0ull ? __builtin_ctzll(m) * 4096 : kTopk * 4096) + 16 * fresh_lane();
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+      dst[qq] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(dsrc, off + 1024 * qq, 0, 0));
+  };
+
+  // union of the tile's blocks
+  if (threadIdx.x < kUnionWords) bitmap[threadIdx.x] = 0u;
+  __syncthreads();
+  if (g == 0 && my_gb >= 0 && my_gb - gb_lo < kUnionWords * 32)
+    atomicOr(&bitmap[(my_gb - gb_lo) >> 5], 1u << ((my_gb - gb_lo) & 31));
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t bits = lane < kUnionWords ? bitmap[lane] : 0u;
+    const int cnt = __popc(bits);
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    int pos = incl - cnt;
+    while (bits) {
+      const int bit = __ffs(bits) - 1;
+      ulist[pos++] = gb_lo + 32 * lane + bit;
+      bits &= bits - 1u;
+    }
+    if (lane == 63) nunion = incl;
+  }
+  __syncthreads();
+  const int nsteps = nunion;
+
+  // wavefronts 0-7 copy the four K runs of key tile w
+  const bool stager = wave < 8;
+  auto stage = [&](int u, int buf) {
+    if (!stager) return;
+    const int gb = __builtin_amdgcn_readfirstlane(ulist[u]);
+    const int ln = fresh_lane();
+    const u16* base = kop + (((int64_t)gb * Hk + h) * 32 + 4 * wave) * 512;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) dma16s(base + 512 * ds, 16 * ln, lds_offset(&kbuf[buf][4 * wave + ds][0]));
+  };
+  // three dS buffers in turn: block k's in buffer k % 3
+  bf16x8 ds0[4], ds1[4], ds2[4];
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) ds0[qq] = ds1[qq] = ds2[qq] = zero_bf16x8();
+  load_ds(0, ds0);
+  load_ds(1, ds1);
+  f32x4 dqacc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) dqacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (nsteps > 0) stage(0, 0);
+  if (nsteps > 1) stage(1, 1);
+  wait_copies();
+  wait_all_loads();
+  __syncthreads();
+
+  int k = 0;              // blocks of the token met so far
+  bool hit_prev = false;  // dS loads issued in the previous step
+  int buf = 0;            // u % 3
+  int u = 0;
+  auto is_hit = [&]() { return __ballot(my_gb == ulist[u]) != 0ull; };
+  // block u + 2's copies into the buffer block u - 1 used; whether this
+  // wavefront issued any
+  auto stage_ahead = [&]() {
+    if (u + 2 < nsteps) stage(u + 2, buf == 0 ? 2 : buf - 1);
+    return stager && u + 2 < nsteps;
+  };
+  // block u + 1's copies (issued in the previous step, or before the loop)
+  // have landed; issued after them and allowed in flight: the previous
+  // step's dS loads, this step's copies and this step's dS loads
+  auto end_step = [&](bool staging, bool hit) {
+    const int after = (hit_prev ? 4 : 0) + (staging ? 4 : 0) + (hit ? 4 : 0);
+    if (after == 12)
+      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if (after == 8)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (after == 4)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+      wait_copies();
+    lds_barrier();
+    hit_prev = hit;
+    buf = buf == 2 ? 0 : buf + 1;
+    ++u;
+  };
+  // steps up to the token's next block; false when the walk ends first
+  auto skip_to_hit = [&]() {
+    while (u < nsteps) {
+      if (is_hit()) return true;
+      end_step(stage_ahead(), false);
+    }
+    return false;
+  };
+  // the step of block k: its dS (loaded two blocks ago, in cur) times K^T;
+  // block k + 2's dS loads into nxt (the buffer block k - 1 used)
+  auto hit_step = [&](bf16x8 (&cur)[4], bf16x8 (&nxt)[4]) {
+    // take cur before the next copy is issued, so that waiting for it never
+    // waits for that copy
+    asm volatile("" ::"v"(cur[0]), "v"(cur[1]), "v"(cur[2]), "v"(cur[3]));
+    const bool staging = stage_ahead();
+    load_ds(k + 2, nxt);
+    const int c = ulist[u] - tok_base;
+    const bool diag = (c == tok_b);
+    const int key0 = kBlock * c;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      if (diag && key0 + 32 * qq > tok_pos) break;
+      const uint32_t kq = lds_offset(&kbuf[buf][8 * qq][0]) + tr_lane_offset(fresh_lane());
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint32_t off = kq + (dt >> 1) * 1024 + (dt & 1) * 512;
+        const uint2 lo = read_tr16(off), hi = read_tr16(off + 4096);
+        const bf16x8 ta = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        dqacc[dt] = mfma16x16x32(ta, cur[qq], dqacc[dt]);
+      }
+    }
+    ++k;
+    end_step(staging, true);
+  };
+  // three phases, one per buffer role, so every buffer has one load site
+  for (;;) {
+    if (!skip_to_hit()) break;
+    hit_step(ds0, ds2);
+    if (!skip_to_hit()) break;
+    hit_step(ds1, ds0);
+    if (!skip_to_hit()) break;
+    hit_step(ds2, ds1);
+  }
+  if (tvalid) {
+    u16* out = dq + (int64_t)t * dq_st + (int64_t)(h * kGroup + li) * dq_sh;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<uint2*>(out + 16 * dt + 4 * g) = pack_bf16x4(dqacc[dt] * scale);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Ordered reduction of the per-chunk slices of one (block, KV head).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
@@ -601,6 +891,34 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
 void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStream_t st) {
   const int T = (int)z.T, Hk = (int)z.Hk, S = (int)z.S;
   const QkNormParams none{};
+  if (a.ds) {
+    // sparse, no fused norm: dK/dV first (storing dS), then dQ from the stored dS
+    {
+      KernelTimer timer("bwd_block_prep", st);
+      bwd_block_prep_kernel<false><<<dim3((unsigned)(z.nblk_cap + 1), (unsigned)Hk, 4), 256, 0, st>>>(
+          a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.cu, S, (int)z.chunk, (int)z.ntiles, p, Hk, none, nullptr,
+          a.kop, nullptr, a.item_load, (int)(z.Hk * z.items_cap));
+    }
+    {
+      KernelTimer timer("bwd_delta", st);
+      bwd_delta_kernel<<<dim3((unsigned)((z.T + 15) / 16), (unsigned)Hk), 1024, 0, st>>>(
+          a.o, a.o_st, a.o_sh, a.dO, a.do_st, a.do_sh, a.lse, a.blk_idx, a.cu, p.seqitem, S, T, Hk, (int)z.chunk,
+          (int)z.items_cap, a.delta, a.nlse, a.item_load);
+    }
+    launch_attn_bwd_dkdv(z, a, p, st);
+    {
+      KernelTimer timer("dkdv_reduce", st);
+      dkdv_reduce_kernel<<<dim3((unsigned)z.nblk_cap, kBlock / 16, (unsigned)Hk), 256, 0, st>>>(
+          a.part_dk, a.part_dv, a.item_count, p.seqitem, p.blk_seq, p.blkbase, a.cu, p.totals, Hk, (int)z.chunk,
+          (int)z.items_cap, a.scale, a.dk, a.dk_st, a.dk_sh, a.dv, a.dv_st, a.dv_sh);
+    }
+    {
+      KernelTimer timer("attn_bwd_dq", st);
+      attn_bwd_dq_ds_kernel<<<(unsigned)(z.ntiles * Hk), 64 * kDqWaves, 0, st>>>(
+          a.kop, a.ds, a.blk_idx, a.cu, p.blkbase, p.tile_order, S, T, Hk, a.scale, a.dq, a.dq_st, a.dq_sh);
+    }
+    return;
+  }
   {
     KernelTimer timer("bwd_block_prep", st);
     auto kern = a.nrm ? bwd_block_prep_kernel<true> : bwd_block_prep_kernel<false>;

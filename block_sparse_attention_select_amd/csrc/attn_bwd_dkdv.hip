@@ -29,6 +29,10 @@
 //   5. A block whose selecting queries all lie in one chunk writes bf16 dK/dV
 //      itself; other blocks write fp32 slices that dkdv_reduce_kernel sums in
 //      chunk order.
+//   kWriteDs: every selecting (token, block)'s bf16 dS also goes to HBM, in
+//      the order the token-major dQ pass takes it as an MFMA operand, so that
+//      pass needs one product per block (dQ = scale dS K) instead of
+//      recomputing S and dP.
 #include "attn_stage.h"
 
 namespace msa {
@@ -70,7 +74,11 @@ __device__ __forceinline__ void stage_part(int t, int part, int h, int Hk, int l
 }
 
 // kDense: every token of the chunk at or after the block's first key selects it (blk_idx unused).
-template <bool kDense>
+// kWriteDs (sparse only): ds_out[((t Hk + h) 16 + slot) 4 + w][lane][8] gets the
+// token's bf16 dS for keys 32 w .. 32 w + 31 of the block, lane (head li,
+// group g) holding keys 32 w + 8 g .. +7 of head li, where slot is the
+// block's first position in the token's list of selected blocks.
+template <bool kDense, bool kWriteDs>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
     const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
@@ -82,11 +90,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int32_t* __restrict__ seqitem, const int32_t* __restrict__ totals,
     int S, int Hk, int chunk, int items_cap, const int32_t* __restrict__ item_order, float scale_log2, float scale,
     int32_t* __restrict__ item_count, float* __restrict__ part_dk, float* __restrict__ part_dv,
-    u16* __restrict__ dk_out, int64_t dk_st, int64_t dk_sh, u16* __restrict__ dv_out, int64_t dv_st, int64_t dv_sh) {
+    u16* __restrict__ dk_out, int64_t dk_st, int64_t dk_sh, u16* __restrict__ dv_out, int64_t dv_st, int64_t dv_sh,
+    u16* __restrict__ ds_out) {
+  static_assert(!(kDense && kWriteDs), "dS is stored for sparse layers only");
   __shared__ u32x4 stage[kNBuf][kBatch][512];
   __shared__ __align__(16) float stats[kNBuf][kBatch][32];
+  // selecting tokens as (token << 4) | list slot of the block
   __shared__ int sel[kDkdvChunkMax];
   __shared__ int wcount[4];
+  // per wavefront: one token's dS of its 32 keys, [key][head group] x 4 heads,
+  // transposed on the way out
+  __shared__ __align__(16) uint2 dsx[kWriteDs ? 4 : 1][kWriteDs ? 128 : 1];
 
   const int h = blockIdx.y;
   if ((int)blockIdx.x >= totals[1]) return;
@@ -119,15 +133,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int p0 = p_begin; p0 < p_end; p0 += 256) {
     const int p = p0 + threadIdx.x;
     bool hit = false;
+    int slot = 0;  // first list position holding block c
     if (kDense) {
       hit = p < p_end;
     } else if (p < p_end) {
       const int4* ids = reinterpret_cast<const int4*>(blk_idx + ((int64_t)(seq0 + p) * Hk + h) * kTopk);
+      slot = kTopk;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
+      for (int jj = 3; jj >= 0; --jj) {
         const int4 x = ids[jj];
-        hit |= (x.x == c) | (x.y == c) | (x.z == c) | (x.w == c);
+        slot = x.w == c ? 4 * jj + 3 : slot;
+        slot = x.z == c ? 4 * jj + 2 : slot;
+        slot = x.y == c ? 4 * jj + 1 : slot;
+        slot = x.x == c ? 4 * jj : slot;
       }
+      hit = slot < kTopk;
     }
     const uint64_t m = __ballot(hit);
     const int before = __popcll(m & ((1ull << lane) - 1ull));
@@ -140,7 +160,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       off += w < wave ? wcount[w] : 0;
       tot += wcount[w];
     }
-    if (hit) sel[off + before] = seq0 + p;
+    if (hit) sel[off + before] = ((seq0 + p) << 4) | slot;
     nsel += tot;
     __syncthreads();
   }
@@ -178,7 +198,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // wavefront w copies half of token w % 2 of a round: q and stats (w < 2) or dO
     auto stage_round = [&](int bi, int buf) {
       const int slot = wave & 1;
-      stage_part(sel[min(bi * kBatch + slot, nsel - 1)], wave >> 1, h, Hk, fresh_lane(),
+      stage_part(sel[min(bi * kBatch + slot, nsel - 1)] >> 4, wave >> 1, h, Hk, fresh_lane(),
                  lds_offset(&stage[buf][slot][0]), lds_offset(&stats[buf][slot][0]), q, q_st, q_sh, dO, do_st,
                  do_sh, nlse, delta);
     };
@@ -196,7 +216,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (n0 < nsel) {
           // a missing second token is treated as a query at position -1 of
           // this block: every key is after it, so it contributes nothing
-          const int pos[2] = {sel[n0] - seq0, n0 + 1 < nsel ? sel[n0 + 1] - seq0 : -1};
+          const int tsel[2] = {sel[n0], n0 + 1 < nsel ? sel[n0 + 1] : -1};
+          const int pos[2] = {(tsel[0] >> 4) - seq0, tsel[1] >= 0 ? (tsel[1] >> 4) - seq0 : -1};
           const u32x4* b[2] = {stage[cur][2 * pp], stage[cur][2 * pp + 1]};
           const float* st[2] = {stats[cur][2 * pp], stats[cur][2 * pp + 1]};
 
@@ -248,6 +269,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               pw[kk][2 * tk + 1] = pack_bf16x2(e[kk][2], e[kk][3]);
               sw[kk][2 * tk] = pack_bf16x2(d[0], d[1]);
               sw[kk][2 * tk + 1] = pack_bf16x2(d[2], d[3]);
+            }
+            if constexpr (kWriteDs) {
+              // lane (key li, group g) holds heads 4g..4g+3 of keys li and
+              // 16 + li: written as [key][group], read back transposed so that
+              // lane (head s, group gg) gets keys 8gg .. 8gg+7 (source lane
+              // 4e + s/4 of the transposed read points at key 8gg + e, heads
+              // 4(s%4) ..)
+              if (tsel[tk] >= 0) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) dsx[wave][(16 * kk + li) * 4 + g] = uint2{sw[kk][2 * tk], sw[kk][2 * tk + 1]};
+                const int sl = ln & 15, gg = ln >> 4;
+                const uint32_t rd = lds_offset(&dsx[wave][0]) + (uint32_t)(((8 * gg + (sl >> 2)) * 4 + (sl & 3)) * 8);
+                const uint2 lo = read_tr16(rd), hi = read_tr16(rd + 128);
+                const int64_t row = ((int64_t)(tsel[tk] >> 4) * Hk + h) * kTopk + (tsel[tk] & 15);
+                *reinterpret_cast<u32x4*>(ds_out + (row * 4 + wave) * 512 + 8 * ln) = u32x4{lo.x, lo.y, hi.x, hi.y};
+              }
             }
           }
           bf16x8 pA[2], sA[2];
@@ -328,7 +365,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // launched by decreasing number of selecting queries (longest job first), which
 // only changes when each item runs, not what it computes.  For sparse layers
 // the counters are zeroed by the backward prep kernel and filled by the dQ
-// pass (one count per selecting query, head and block); the item of query
+// pass or the Delta kernel ahead of this one (one count per selecting query,
+// head and block); the item of query
 // chunk j of sequence s and its block c has index seqitem[s] +
 // (chunk / kBlock) * j * (j + 1) / 2 + c.
 // ---------------------------------------------------------------------------
@@ -404,14 +442,15 @@ __global__ __launch_bounds__(1024) void dkdv_order_kernel(const int32_t* __restr
 void launch_attn_bwd_dkdv(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStream_t st) {
   {
     KernelTimer timer("dkdv_order", st);
-    // sparse: the dQ pass counted the selections per item; dense: a closed form
+    // sparse: the selections per item were counted by an earlier pass; dense: a closed form
     if (a.dense)
       dkdv_dense_load_kernel<<<dim3((unsigned)((z.items_cap + 255) / 256), (unsigned)z.Hk), 256, 0, st>>>(
           a.cu, p.seqitem, p.totals, (int)z.S, (int)z.chunk, (int)z.items_cap, a.item_load);
     dkdv_order_kernel<<<(unsigned)z.Hk, 1024, 0, st>>>(a.item_load, p.totals, (int)z.items_cap, a.item_order);
   }
   KernelTimer timer("attn_bwd_dkdv", st);
-  auto kern = a.dense ? attn_bwd_dkdv_kernel<true> : attn_bwd_dkdv_kernel<false>;
+  auto kern = a.dense ? attn_bwd_dkdv_kernel<true, false>
+                      : (a.ds ? attn_bwd_dkdv_kernel<false, true> : attn_bwd_dkdv_kernel<false, false>);
   // with the attention-side norm fused in, the pass reads the normalized rows
   // the prep and dQ kernels wrote
   const int64_t D = kHeadDim;
@@ -423,7 +462,7 @@ void launch_attn_bwd_dkdv(const Sizes& z, const BwdArgs& a, const PlanBufs& p, h
       q, q_st, q_sh, k, k_st, k_sh, a.v, a.v_st, a.v_sh, a.dO, a.do_st, a.do_sh, a.nlse,
       a.delta, a.blk_idx, a.cu, p.blkbase, p.blk_seq, p.seqitem, p.totals, (int)z.S, (int)z.Hk, (int)z.chunk,
       (int)z.items_cap, a.item_order, a.scale * kLog2e, a.scale, a.item_count, a.part_dk, a.part_dv, a.dk, a.dk_st, a.dk_sh, a.dv,
-      a.dv_st, a.dv_sh);
+      a.dv_st, a.dv_sh, a.ds);
 }
 
 }  // namespace msa

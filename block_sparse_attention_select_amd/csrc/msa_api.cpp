@@ -174,8 +174,13 @@ struct BwdWs {
   int32_t* item_order;
   float* part_dk;
   float* part_dv;
+  u16* ds;  // stored dS, or null (the backward then recomputes S and dP for dQ)
 };
-BwdWs carve_bwd(Carver& c, const Sizes& z) {
+// Whether the stored-dS buffer of a pack stays within its cap.
+bool ds_fits(const Sizes& z) { return z.T * z.Hk * msa::kDsBytesPerRow <= msa::kDsBufMaxBytes; }
+// with_ds: a sparse backward without the fused norm, which stores dS when it
+// fits (the buffer is carved last, so the other layouts are its prefix)
+BwdWs carve_bwd(Carver& c, const Sizes& z, bool with_ds) {
   BwdWs w;
   w.plan = carve_plan(c, z);
   w.kop = c.take<u16>(z.nblk_cap * z.Hk * msa::kHeadDim * msa::kBlock);
@@ -187,6 +192,7 @@ BwdWs carve_bwd(Carver& c, const Sizes& z) {
   w.item_order = c.take<int32_t>(z.Hk * z.items_cap);
   w.part_dk = c.take<float>(z.Hk * z.items_cap * msa::kBlock * msa::kHeadDim);
   w.part_dv = c.take<float>(z.Hk * z.items_cap * msa::kBlock * msa::kHeadDim);
+  w.ds = with_ds && ds_fits(z) ? c.take<u16>(z.T * z.Hk * (msa::kDsBytesPerRow / 2)) : nullptr;
   return w;
 }
 
@@ -203,7 +209,7 @@ struct BwdQkWs {
 int64_t qknorm_partial_rows(const Sizes& z) { return msa::kQkBwdMaxRows + z.ntiles * z.Hk; }
 BwdQkWs carve_bwd_qknorm(Carver& c, const Sizes& z) {
   BwdQkWs w;
-  w.bwd = carve_bwd(c, z);
+  w.bwd = carve_bwd(c, z, false);
   w.qhat = c.take<u16>(z.T * z.Hq * msa::kHeadDim);
   w.khat = c.take<u16>(z.T * z.Hk * msa::kHeadDim);
   w.dkhat = c.take<u16>(z.T * z.Hk * msa::kHeadDim);
@@ -243,6 +249,7 @@ void launch_bwd_on(const Sizes& z, const BwdWs& w, const u16* q, int64_t q_st, i
   a.item_order = w.item_order;
   a.part_dk = w.part_dk;
   a.part_dv = w.part_dv;
+  a.ds = w.ds;
   a.nrm = nrm;
   a.qhat = qhat;
   a.khat = khat;
@@ -295,7 +302,7 @@ size_t ws_bytes_for(const Sizes& z, int op) {
   switch (op) {
     case MSA_OP_SELECT: carve_select(c, z); break;
     case MSA_OP_FWD: carve_fwd(c, z); break;
-    case MSA_OP_BWD: carve_bwd(c, z); break;
+    case MSA_OP_BWD: carve_bwd(c, z, true); break;
     case MSA_OP_QKNORM_BWD: c.take<float>((int64_t)(msa::kQkBwdMaxRows + msa::kQkBwdMaxRows / 16 + 1) * 256); break;
     case MSA_OP_QSA_FWD: carve_qsa_fwd(c, z); break;
     case MSA_OP_QSA_BWD: carve_qsa_bwd(c, z); break;
@@ -464,10 +471,17 @@ int msa_attn_bwd_ex(const msa_dims* dims, const void* q, int64_t q_st, int64_t q
       !aligned(lse, 16))
     return MSA_ERR_INVALID_ARG;
   const Sizes z = sizes_of(dims);
-  st = check_ws(workspace, workspace_bytes, ws_bytes_for(z, MSA_OP_BWD));
+  // a dense backward does not use the stored-dS tail of the workspace
+  size_t need = ws_bytes_for(z, MSA_OP_BWD);
+  if (dense) {
+    Carver cc(nullptr);
+    carve_bwd(cc, z, false);
+    need = cc.off;
+  }
+  st = check_ws(workspace, workspace_bytes, need);
   if (st != MSA_OK) return st;
   Carver c(workspace);
-  BwdWs w = carve_bwd(c, z);
+  BwdWs w = carve_bwd(c, z, !dense);
   launch_bwd_on(z, w, (const u16*)q, q_st, q_sh, (const u16*)k, k_st, k_sh, (const u16*)v, v_st, v_sh,
                 (const u16*)o, o_st, o_sh, lse, (const u16*)do_, do_st, do_sh, dense ? nullptr : blk_idx,
                 cu_seqlens, softmax_scale, dense, (u16*)dq, dq_st, dq_sh, (u16*)dk, dk_st, dk_sh, (u16*)dv, dv_st,

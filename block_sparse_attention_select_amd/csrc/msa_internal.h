@@ -275,6 +275,10 @@ struct BwdArgs {
   int32_t* item_order;  // [Hk][items_cap] items by decreasing load
   float* part_dk;   // [Hk][items_cap][128][128]
   float* part_dv;
+  // sparse layers without the fused norm, when it fits kDsBufMaxBytes: the
+  // dK/dV pass stores every (token, KV head, listed block)'s bf16 dS here
+  // ([T][Hk][16][4 quarters][64 lanes][8]) and dQ is formed from it
+  u16* ds = nullptr;
   // attention-side norm fused in (nrm != nullptr): q and k are raw; the prep
   // and dQ kernels normalize them (writing the normalized rows to khat and
   // qhat for the dK/dV pass), dq comes out for the raw q, and the dQ kernel
@@ -291,6 +295,11 @@ void launch_attn_bwd_dkdv(const Sizes& z, const BwdArgs& a, const PlanBufs& p, h
 
 // Largest number of query positions in one dK/dV work item.
 constexpr int kDkdvChunkMax = 2048;
+
+// Largest stored-dS buffer (16 blocks x 4 KB per token and KV head); longer
+// packs take the backward that recomputes S and dP in the dQ pass.
+constexpr int64_t kDsBufMaxBytes = int64_t(4) << 30;
+constexpr int64_t kDsBytesPerRow = int64_t(kTopk) * kBlock * kGroup * 2;
 
 // ----------------------------------------------------------------------------
 // Narrow-block variant: 4-token blocks, head dim 256, 12 query heads per KV
