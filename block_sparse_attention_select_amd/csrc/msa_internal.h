@@ -298,7 +298,7 @@ constexpr int kDkdvChunkMax = 2048;
 
 // Largest stored-dS buffer (16 blocks x 4 KB per token and KV head); longer
 // packs take the backward that recomputes S and dP in the dQ pass.
-constexpr int64_t kDsBufMaxBytes = int64_t(4) << 30;
+constexpr int64_t kDsBufMaxBytes = int64_t(16) << 30;
 constexpr int64_t kDsBytesPerRow = int64_t(kTopk) * kBlock * kGroup * 2;
 
 // ----------------------------------------------------------------------------

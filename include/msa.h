@@ -281,6 +281,13 @@ int msa_attn_fwd(const msa_dims* dims,
  *   q, k, v, o, do_ as in the forward (each with its own strides), lse [T,Hq]
  *   fp32 from the forward; outputs dq [T,Hq,128], dk, dv [T,Hk,128] bf16
  *   with their own strides (dv need not share dk's layout).
+ *
+ * Workspace: msa_workspace_size(dims, MSA_OP_BWD).  When T * Hk <= 262144
+ * it ends with 64 KB per (token, KV head) where the dK/dV pass stores each
+ * selection's bf16 dS, from which dQ is then formed (16 GiB at that limit);
+ * larger packs recompute S and dP in the dQ pass instead.  A dense call
+ * (msa_attn_bwd_ex with MSA_ATTN_DENSE) does not use that tail and accepts a
+ * workspace without it.
  */
 int msa_attn_bwd(const msa_dims* dims,
                  const void* q, int64_t q_st, int64_t q_sh,
