@@ -611,21 +611,26 @@ __global__ __launch_bounds__(1024) void bwd_delta_kernel(
 
 // ---------------------------------------------------------------------------
 // dQ from the stored dS.  The dK/dV pass left, for every (token, KV head,
-// listed block), the block's dS^T in the B-operand order of dQ^T = K^T dS^T:
-// quarter qq (keys 32 qq .. +31), lane (head li, group g) holding keys
-// 32 qq + 8 g .. +7 (16 bytes; ds_buf[((t Hk + h) 16 + slot) 4 + qq][lane],
-// slot = the block's first position in the token's list).  The tiling and
-// union walk are the dQ kernel's with only K staged (its K^T operands read
-// transposed), three K buffers deep: block u + 2 is copied while block u is
-// used, and each wavefront's dS loads run two of its own blocks ahead, so the
-// wait that ends a step (for block u + 1's copies) leaves the newest loads in
-// flight (loads and copies complete in issue order).
+// listed block), the block's bf16 dS as its score registers held it: quarter
+// qq (keys 32 qq .. +31) as two runs of 64 lanes x 8 bytes, lane (key li,
+// group g) of run x holding heads 4g .. 4g+3 of key 32 qq + 16 x + li
+// (ds_buf[((t Hk + h) 16 + slot) 4 + qq][x][lane], slot = the block's first
+// position in the token's list).  dQ^T = K^T dS^T wants dS^T as the B operand,
+// lane (head s, group gg) holding keys 32 qq + 8 gg .. +7 of head s: each
+// quarter is written to a 1 KB LDS slot of the wavefront and read back with
+// ds_read_b64_tr_b16.  The tiling and union walk are the dQ kernel's with only
+// K staged (its K^T operands read transposed), three K buffers deep: block
+// u + 2 is copied while block u is used, and each wavefront's dS loads run two
+// of its own blocks ahead, so the wait that ends a step (for block u + 1's
+// copies) leaves the newest loads in flight (loads and copies complete in
+// issue order).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_ds_kernel(
     const u16* __restrict__ kop, const u16* __restrict__ ds_buf, const int32_t* __restrict__ blk_idx,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ blkbase, const int32_t* __restrict__ tile_order,
     int S, int T, int Hk, float scale, u16* __restrict__ dq, int64_t dq_st, int64_t dq_sh) {
   __shared__ u32x4 kbuf[3][32][64];
+  __shared__ u32x4 dsx[kDqWaves][2][64];
   __shared__ uint32_t bitmap[kUnionWords];
   __shared__ int ulist[kMaxUnion];
   __shared__ int nunion;
@@ -637,6 +642,24 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_ds_kernel(
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int li = lane & 15;
+
+  // The dS transpose.  Lane l loads bytes 16 l .. of the quarter (the 8-byte
+  // pieces of lanes 2l, 2l+1 of run l / 32) and writes them to 16-byte slot
+  // sigma(l) = l ^ 2 (l / 16 % 2) of the wavefront's 1 KB.  ds_read_b64_tr_b16
+  // hands output lane i of a 16-lane group element e of source lane 4e + i/4,
+  // whose 4 bf16 must then be heads 4(i/4) .. of one key: source lane j of
+  // group gg points at key 8 gg + j/4 (+4 for the second read), heads
+  // 4(j%4) .., i.e. at the piece of lane L = key % 16 + 16 (j%4) of run
+  // key / 16, held by loading lane 32 (key / 16) + L / 2 at byte 8 (L % 2).
+  // With sigma, the 32 reads of each half wavefront touch every bank once and
+  // each 16-lane write touches 16 distinct slots.
+  const uint32_t ds_wr = (uint32_t)(16 * (lane ^ (2 * (g & 1))));
+  auto ds_rd = [&](int key) {
+    const int L = (key & 15) + 16 * (li & 3);
+    const int lp = 32 * (key >> 4) + (L >> 1);
+    return (uint32_t)(16 * (lp ^ (2 * ((lp >> 4) & 1))) + 8 * (L & 1));
+  };
+  const uint32_t ds_rd0 = ds_rd(8 * g + (li >> 2)), ds_rd1 = ds_rd(8 * g + 4 + (li >> 2));
 
   const int t = t0 + wave;
   const bool tvalid = t < T;
@@ -785,13 +808,20 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_ds_kernel(
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       if (diag && key0 + 32 * qq > tok_pos) break;
+      bf16x8 bop;
+      {
+        const uint32_t slot = lds_offset(&dsx[wave][qq & 1][0]);
+        dsx[wave][qq & 1][ds_wr / 16] = __builtin_bit_cast(u32x4, cur[qq]);
+        const uint2 lo = read_tr16(slot + ds_rd0), hi = read_tr16(slot + ds_rd1);
+        bop = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+      }
       const uint32_t kq = lds_offset(&kbuf[buf][8 * qq][0]) + tr_lane_offset(fresh_lane());
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const uint32_t off = kq + (dt >> 1) * 1024 + (dt & 1) * 512;
         const uint2 lo = read_tr16(off), hi = read_tr16(off + 4096);
         const bf16x8 ta = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-        dqacc[dt] = mfma16x16x32(ta, cur[qq], dqacc[dt]);
+        dqacc[dt] = mfma16x16x32(ta, bop, dqacc[dt]);
       }
     }
     ++k;

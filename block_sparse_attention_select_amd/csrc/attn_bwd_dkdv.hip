@@ -29,10 +29,10 @@
 //   5. A block whose selecting queries all lie in one chunk writes bf16 dK/dV
 //      itself; other blocks write fp32 slices that dkdv_reduce_kernel sums in
 //      chunk order.
-//   kWriteDs: every selecting (token, block)'s bf16 dS also goes to HBM, in
-//      the order the token-major dQ pass takes it as an MFMA operand, so that
-//      pass needs one product per block (dQ = scale dS K) instead of
-//      recomputing S and dP.
+//   kWriteDs: every selecting (token, block)'s bf16 dS also goes to HBM as the
+//      score registers hold it (two 8-byte stores per lane and token), so the
+//      token-major dQ pass needs one product per block (dQ = scale dS K)
+//      instead of recomputing S and dP.
 #include "attn_stage.h"
 
 namespace msa {
@@ -74,10 +74,10 @@ __device__ __forceinline__ void stage_part(int t, int part, int h, int Hk, int l
 }
 
 // kDense: every token of the chunk at or after the block's first key selects it (blk_idx unused).
-// kWriteDs (sparse only): ds_out[((t Hk + h) 16 + slot) 4 + w][lane][8] gets the
-// token's bf16 dS for keys 32 w .. 32 w + 31 of the block, lane (head li,
-// group g) holding keys 32 w + 8 g .. +7 of head li, where slot is the
-// block's first position in the token's list of selected blocks.
+// kWriteDs (sparse only): ds_out[((t Hk + h) 16 + slot) 4 + w][half][lane][4]
+// gets the token's bf16 dS for keys 32 w .. 32 w + 31 of the block, lane (key
+// li, group g) holding heads 4g .. 4g+3 of key 32 w + 16 half + li, where slot
+// is the block's first position in the token's list of selected blocks.
 template <bool kDense, bool kWriteDs>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
@@ -98,9 +98,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // selecting tokens as (token << 4) | list slot of the block
   __shared__ int sel[kDkdvChunkMax];
   __shared__ int wcount[4];
-  // per wavefront: one token's dS of its 32 keys, [key][head group] x 4 heads,
-  // transposed on the way out
-  __shared__ __align__(16) uint2 dsx[kWriteDs ? 4 : 1][kWriteDs ? 128 : 1];
 
   const int h = blockIdx.y;
   if ((int)blockIdx.x >= totals[1]) return;
@@ -271,20 +268,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               sw[kk][2 * tk + 1] = pack_bf16x2(d[2], d[3]);
             }
             if constexpr (kWriteDs) {
-              // lane (key li, group g) holds heads 4g..4g+3 of keys li and
-              // 16 + li: written as [key][group], read back transposed so that
-              // lane (head s, group gg) gets keys 8gg .. 8gg+7 (source lane
-              // 4e + s/4 of the transposed read points at key 8gg + e, heads
-              // 4(s%4) ..)
               if (tsel[tk] >= 0) {
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) dsx[wave][(16 * kk + li) * 4 + g] = uint2{sw[kk][2 * tk], sw[kk][2 * tk + 1]};
-                const int sl = ln & 15, gg = ln >> 4;
-                const uint32_t rd = lds_offset(&dsx[wave][0]) + (uint32_t)(((8 * gg + (sl >> 2)) * 4 + (sl & 3)) * 8);
-                const uint2 lo = read_tr16(rd), hi = read_tr16(rd + 128);
+                // two 512-byte runs of register pairs: one 16-byte store per
+                // lane would need the halves copied into four consecutive
+                // registers, which this loop does not have to spare
                 const int64_t row = ((int64_t)(tsel[tk] >> 4) * Hk + h) * kTopk + (tsel[tk] & 15);
-                *reinterpret_cast<u32x4*>(ds_out + (row * 4 + wave) * 512 + 8 * ln) = u32x4{lo.x, lo.y, hi.x, hi.y};
+                u16* dst = ds_out + (row * 4 + wave) * 512 + 4 * ln;
+                *reinterpret_cast<uint2*>(dst) = uint2{sw[0][2 * tk], sw[0][2 * tk + 1]};
+                *reinterpret_cast<uint2*>(dst + 256) = uint2{sw[1][2 * tk], sw[1][2 * tk + 1]};
               }
+              // keep the stores here: moved later, the dS registers would stay
+              // live across the next token's products
+              __builtin_amdgcn_sched_barrier(0);
             }
           }
           bf16x8 pA[2], sA[2];
