@@ -47,8 +47,11 @@ D = 128
 #   attn_bwd_dq:   2*D FLOP per (query head, selected causal key)   [dQ];
 #   attn_bwd_dkdv: 8*D FLOP per (query head, selected causal key)   [S, dP, dV, dK].
 FLOP_PER_KEY = {"attn_fwd": 4 * D, "attn_bwd_dq": 2 * D, "attn_bwd_dkdv": 8 * D}
-# What the kernels execute (the dQ pass recomputes S and dP): 18*D in all.
-EXEC_FLOP_PER_KEY = {"attn_fwd": 4 * D, "attn_bwd_dq": 6 * D, "attn_bwd_dkdv": 8 * D}
+# What the kernels execute.  With the stored dS (the default whenever its buffer
+# fits) the dQ pass is one product, 14*D in all; when the dQ pass recomputes S
+# and dP (MSA_ATTN_RECOMPUTE, or packs too large for the stored dS), 18*D.
+EXEC_FLOP_PER_KEY = {"attn_fwd": 4 * D, "attn_bwd_dq": 2 * D, "attn_bwd_dkdv": 8 * D}
+EXEC_FLOP_PER_KEY_RECOMPUTE = {"attn_fwd": 4 * D, "attn_bwd_dq": 6 * D, "attn_bwd_dkdv": 8 * D}
 
 
 def selected_keys(blk: np.ndarray, cu: np.ndarray, block: int = 128) -> int:
@@ -412,9 +415,13 @@ def main():
     def sep_fwd():
         qk_fwd()
         msa.msa_attn_fwd(qh, kh, v, blk, cu, p.max_seqlen, out=fo, lse=flse, workspace=ws[msa.MSA_OP_FWD])
+    # the low-memory backward (MSA_ATTN_RECOMPUTE: dQ recomputes S and dP, no stored dS) on the step's inputs
+    rdq, rdk, rdv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    rc_bwd = lambda: msa.msa_attn_bwd(q, k, v, o, lse, do, blk, cu, p.max_seqlen, dq=rdq, dk=rdk, dv=rdv,
+                                      workspace=ws[msa.MSA_OP_BWD], recompute=True)
     qk_ms = {}
     for name, fn in (("fwd", qk_fwd), ("bwd", qk_bwd), ("fused_fwd", fused_fwd), ("fused_bwd", fused_bwd),
-                     ("sep_fwd", sep_fwd)):
+                     ("sep_fwd", sep_fwd), ("recompute_bwd", rc_bwd)):
         for _ in range(2):
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -449,12 +456,15 @@ def main():
     fb_ms = fwd_ms + bwd_ms
     fb_tflops = fb_flop / (fb_ms * 1e-3) / 1e12
 
+    # the backward stores dS (and its dQ pass executes one product) when its workspace carries the dS tail
+    stored_ds = msa.msa_workspace_size(dims, msa.MSA_OP_BWD) > msa.msa_workspace_size(dims, msa.MSA_OP_BWD_RECOMPUTE)
+    exec_fpk = EXEC_FLOP_PER_KEY if stored_ds else EXEC_FLOP_PER_KEY_RECOMPUTE
     dom = max(kt.items(), key=lambda kv: kv[1][1])[0]
     dom_ms = kt[dom][1] / kt[dom][0]
     dom_exec = None
     if dom in FLOP_PER_KEY:
         dom_flop = FLOP_PER_KEY[dom] * per_qhead
-        dom_exec = EXEC_FLOP_PER_KEY[dom] * per_qhead
+        dom_exec = exec_fpk[dom] * per_qhead
     elif dom == "select_scores":
         dom_flop = sel_flop
     else:
@@ -481,7 +491,7 @@ def main():
             ms = kt[name][1] / kt[name][0]
             per_kernel[name] = {"ms": round(ms, 4),
                                 "counted_tflops": round(fpk * per_qhead / (ms * 1e-3) / 1e12, 1),
-                                "executed_tflops": round(EXEC_FLOP_PER_KEY[name] * per_qhead / (ms * 1e-3) / 1e12, 1)}
+                                "executed_tflops": round(exec_fpk[name] * per_qhead / (ms * 1e-3) / 1e12, 1)}
 
     line = {
         "metric": METRIC,
@@ -511,6 +521,9 @@ def main():
         "qk_norm_rope_bwd_hbm_frac": round(qk_bytes["bwd"] / (qk_ms["bwd"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
+        "bwd_recompute_ms": round(qk_ms["recompute_bwd"], 4),
+        "bwd_workspace_mb": round(msa.msa_workspace_size(dims, msa.MSA_OP_BWD) / 2**20, 1),
+        "bwd_recompute_workspace_mb": round(msa.msa_workspace_size(dims, msa.MSA_OP_BWD_RECOMPUTE) / 2**20, 1),
         "fwd_bwd_ms": round(fb_ms, 4),
         "fwd_bwd_counted_gflop": round(fb_flop / 1e9, 1),
         "fwd_bwd_tflops": round(fb_tflops, 2),
@@ -524,7 +537,8 @@ def main():
                                      / (sel_ms * 1e-3), 4),
         "kernels_avg_ms": kernels,
         "kernel_rates": per_kernel,
-        "fwd_bwd_executed_tflops": round(18 * D * per_qhead / (fb_ms * 1e-3) / 1e12, 2),
+        "fwd_bwd_executed_tflops": round(sum(exec_fpk.values()) * per_qhead / (fb_ms * 1e-3) / 1e12, 2),
+        "bwd_stored_ds": bool(stored_ds),
         "roofline": roofline,
         "context_gb300_ms": {"fwd_bwd": 6.7, "select": 0.62, "note": "pages' GB300 figures on unpublished 16k packs"},
     }

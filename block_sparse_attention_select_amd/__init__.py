@@ -34,6 +34,7 @@ MSA_ERR_WORKSPACE = -3
 MSA_ERR_HIP = -4
 MSA_SELECT_FORCE_INIT = 1
 MSA_ATTN_DENSE = 1
+MSA_ATTN_RECOMPUTE = 2
 MSA_OP_QKNORM_BWD = 4
 MSA_OP_SELECT = 1
 MSA_OP_FWD = 2
@@ -41,6 +42,7 @@ MSA_OP_BWD = 3
 MSA_OP_QSA_FWD = 5
 MSA_OP_QSA_BWD = 6
 MSA_OP_BWD_QKNORM = 7
+MSA_OP_BWD_RECOMPUTE = 8
 
 # Every symbol include/msa.h declares.
 EXPORTED = ("msa_workspace_size", "msa_index_select", "msa_index_select_ex", "msa_attn_fwd", "msa_attn_bwd",
@@ -356,8 +358,10 @@ def msa_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Ten
                  softmax_scale: Optional[float] = None, *, dq: Optional[torch.Tensor] = None,
                  dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
                  workspace: Optional[torch.Tensor] = None,
-                 dense: bool = False) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Backward of msa_attn_fwd: returns dQ, dK, dV (bf16, shaped like q, k, v); ``dense`` as in the forward."""
+                 dense: bool = False, recompute: bool = False) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Backward of msa_attn_fwd: returns dQ, dK, dV (bf16, shaped like q, k, v); ``dense`` as in the forward.
+    ``recompute`` (MSA_ATTN_RECOMPUTE): the dQ pass recomputes S and dP instead of reading the dS stored by the
+    dK/dV pass; slower, with a workspace smaller by 64 KB per (token, KV head)."""
     lib = load()
     T, Hq, D = q.shape
     Hk = k.shape[1]
@@ -378,13 +382,15 @@ def msa_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Ten
     if not dense:
         blk_idx = _int32_rows(blk_idx, "blk_idx", T, Hk, dev, 16)
     dims = _dims_for(cu_seqlens, max_seqlen, Hq, Hk, T)
-    ws, nbytes = _workspace(dims, MSA_OP_BWD, dev, workspace)
+    flags = (MSA_ATTN_DENSE if dense else 0) | (MSA_ATTN_RECOMPUTE if recompute else 0)
+    ws, nbytes = _workspace(dims, MSA_OP_BWD_RECOMPUTE if flags else MSA_OP_BWD, dev, workspace)
     (sq, sk, sv, so, sdo, sdq, sdk, sdv) = views
-    if dense:
+    if flags:
         st = lib.msa_attn_bwd_ex(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0],
-                                 sv[1], _ptr(o), so[0], so[1], _ptr(lse), _ptr(do), sdo[0], sdo[1], None,
-                                 _ptr(cu_seqlens), scale, MSA_ATTN_DENSE, _ptr(dq), sdq[0], sdq[1], _ptr(dk), sdk[0],
-                                 sdk[1], _ptr(dv), sdv[0], sdv[1], _ptr(ws), nbytes, _stream(q))
+                                 sv[1], _ptr(o), so[0], so[1], _ptr(lse), _ptr(do), sdo[0], sdo[1],
+                                 None if dense else _ptr(blk_idx), _ptr(cu_seqlens), scale, flags, _ptr(dq), sdq[0],
+                                 sdq[1], _ptr(dk), sdk[0], sdk[1], _ptr(dv), sdv[0], sdv[1], _ptr(ws), nbytes,
+                                 _stream(q))
         _check(st, "msa_attn_bwd_ex")
     else:
         st = lib.msa_attn_bwd(ctypes.byref(dims), _ptr(q), sq[0], sq[1], _ptr(k), sk[0], sk[1], _ptr(v), sv[0],

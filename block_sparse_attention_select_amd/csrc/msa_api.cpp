@@ -303,6 +303,7 @@ size_t ws_bytes_for(const Sizes& z, int op) {
     case MSA_OP_SELECT: carve_select(c, z); break;
     case MSA_OP_FWD: carve_fwd(c, z); break;
     case MSA_OP_BWD: carve_bwd(c, z, true); break;
+    case MSA_OP_BWD_RECOMPUTE: carve_bwd(c, z, false); break;
     case MSA_OP_QKNORM_BWD: c.take<float>((int64_t)(msa::kQkBwdMaxRows + msa::kQkBwdMaxRows / 16 + 1) * 256); break;
     case MSA_OP_QSA_FWD: carve_qsa_fwd(c, z); break;
     case MSA_OP_QSA_BWD: carve_qsa_bwd(c, z); break;
@@ -367,7 +368,7 @@ int msa_workspace_size(const msa_dims* dims, int op, size_t* bytes) {
   int st = check_dims(dims);
   if (st != MSA_OK) return st;
   if (op != MSA_OP_SELECT && op != MSA_OP_FWD && op != MSA_OP_BWD && op != MSA_OP_QKNORM_BWD &&
-      op != MSA_OP_BWD_QKNORM)
+      op != MSA_OP_BWD_QKNORM && op != MSA_OP_BWD_RECOMPUTE)
     return MSA_ERR_INVALID_ARG;
   *bytes = dims->total_tokens == 0 ? 0 : ws_bytes_for(sizes_of(dims), op);
   return MSA_OK;
@@ -459,8 +460,10 @@ int msa_attn_bwd_ex(const msa_dims* dims, const void* q, int64_t q_st, int64_t q
                     int64_t dv_sh, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = check_dims(dims);
   if (st != MSA_OK) return st;
-  if (flags & ~MSA_ATTN_DENSE) return MSA_ERR_INVALID_ARG;
+  if (flags & ~(MSA_ATTN_DENSE | MSA_ATTN_RECOMPUTE)) return MSA_ERR_INVALID_ARG;
   const bool dense = (flags & MSA_ATTN_DENSE) != 0;
+  // the stored-dS pipeline, unless dense or asked to recompute
+  const bool store_ds = !dense && !(flags & MSA_ATTN_RECOMPUTE);
   if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return MSA_ERR_INVALID_ARG;
   if (dims->total_tokens == 0) return MSA_OK;
   if (!in_view(q, q_st, q_sh) || !in_view(k, k_st, k_sh) || !in_view(v, v_st, v_sh) || !in_view(o, o_st, o_sh) ||
@@ -471,17 +474,10 @@ int msa_attn_bwd_ex(const msa_dims* dims, const void* q, int64_t q_st, int64_t q
       !aligned(lse, 16))
     return MSA_ERR_INVALID_ARG;
   const Sizes z = sizes_of(dims);
-  // a dense backward does not use the stored-dS tail of the workspace
-  size_t need = ws_bytes_for(z, MSA_OP_BWD);
-  if (dense) {
-    Carver cc(nullptr);
-    carve_bwd(cc, z, false);
-    need = cc.off;
-  }
-  st = check_ws(workspace, workspace_bytes, need);
+  st = check_ws(workspace, workspace_bytes, ws_bytes_for(z, store_ds ? MSA_OP_BWD : MSA_OP_BWD_RECOMPUTE));
   if (st != MSA_OK) return st;
   Carver c(workspace);
-  BwdWs w = carve_bwd(c, z, !dense);
+  BwdWs w = carve_bwd(c, z, store_ds);
   launch_bwd_on(z, w, (const u16*)q, q_st, q_sh, (const u16*)k, k_st, k_sh, (const u16*)v, v_st, v_sh,
                 (const u16*)o, o_st, o_sh, lse, (const u16*)do_, do_st, do_sh, dense ? nullptr : blk_idx,
                 cu_seqlens, softmax_scale, dense, (u16*)dq, dq_st, dq_sh, (u16*)dk, dk_st, dk_sh, (u16*)dv, dv_st,

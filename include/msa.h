@@ -67,6 +67,11 @@ extern "C" {
 
 /* Attention flags of msa_attn_fwd_ex / msa_attn_bwd_ex. */
 #define MSA_ATTN_DENSE 1u /* every causal key of the sequence; blk_idx is not read (may be NULL) */
+/* msa_attn_bwd_ex only: the dQ pass recomputes S and dP instead of reading the
+ * dS the dK/dV pass stores, so the workspace needs no dS tail
+ * (msa_workspace_size(..., MSA_OP_BWD_RECOMPUTE)); same results within
+ * rounding, slower, 64 KB less workspace per (token, KV head). */
+#define MSA_ATTN_RECOMPUTE 2u
 
 #define MSA_OP_SELECT 1
 #define MSA_OP_FWD 2
@@ -75,6 +80,7 @@ extern "C" {
 #define MSA_OP_QSA_FWD 5
 #define MSA_OP_QSA_BWD 6
 #define MSA_OP_BWD_QKNORM 7
+#define MSA_OP_BWD_RECOMPUTE 8 /* msa_attn_bwd_ex with MSA_ATTN_RECOMPUTE (or MSA_ATTN_DENSE) */
 
 /* Longest sequence this build accepts (1024 blocks of 128 tokens). */
 #define MSA_MAX_SEQLEN 131072
@@ -285,9 +291,9 @@ int msa_attn_fwd(const msa_dims* dims,
  * Workspace: msa_workspace_size(dims, MSA_OP_BWD).  When T * Hk <= 262144
  * it ends with 64 KB per (token, KV head) where the dK/dV pass stores each
  * selection's bf16 dS, from which dQ is then formed (16 GiB at that limit);
- * larger packs recompute S and dP in the dQ pass instead.  A dense call
- * (msa_attn_bwd_ex with MSA_ATTN_DENSE) does not use that tail and accepts a
- * workspace without it.
+ * larger packs recompute S and dP in the dQ pass instead.  A dense call, or
+ * one with MSA_ATTN_RECOMPUTE (msa_attn_bwd_ex), does not use that tail and
+ * accepts a workspace without it (MSA_OP_BWD_RECOMPUTE).
  */
 int msa_attn_bwd(const msa_dims* dims,
                  const void* q, int64_t q_st, int64_t q_sh,
@@ -346,9 +352,11 @@ int msa_qsa_attn_bwd(const msa_dims* dims,
  * the query's sequence instead of its listed blocks: the plain dense causal
  * attention of MiniMax-M3's first three layers ([PR] PR body: block-sparse
  * attention on the sparse layers, plain dense attention on the first three).
- * blk_idx is then ignored and may be NULL.
+ * blk_idx is then ignored and may be NULL.  MSA_ATTN_RECOMPUTE (backward
+ * only) trades speed for workspace, as described at its definition.
  * Unknown flag bits return MSA_ERR_INVALID_ARG.  Same workspaces
- * (MSA_OP_FWD / MSA_OP_BWD) and conventions as the plain calls.
+ * (MSA_OP_FWD / MSA_OP_BWD, or MSA_OP_BWD_RECOMPUTE) and conventions as the
+ * plain calls.
  */
 int msa_attn_fwd_ex(const msa_dims* dims,
                     const void* q, int64_t q_st, int64_t q_sh,

@@ -42,7 +42,7 @@ int main() {
   size_t n = 0;
 
   // workspace sizes and dims validation
-  for (int op = MSA_OP_SELECT; op <= MSA_OP_BWD_QKNORM; ++op) {
+  for (int op = MSA_OP_SELECT; op <= MSA_OP_BWD_RECOMPUTE; ++op) {
     if (op == MSA_OP_QSA_FWD || op == MSA_OP_QSA_BWD) continue;
     EXPECT(msa_workspace_size(&d, op, &n), MSA_OK);
     if (n == 0 || n % 256) {
@@ -128,6 +128,22 @@ int main() {
   EXPECT(bwd(0, Lp, BIG), MSA_ERR_INVALID_ARG);
   EXPECT(bwd(128, nullptr, BIG), MSA_ERR_INVALID_ARG);
   EXPECT(bwd(128, Lp, need_bwd - 256), MSA_ERR_WORKSPACE);
+
+  // the recompute flag: a smaller workspace (no stored-dS tail); unknown bits rejected
+  size_t need_rc = 0;
+  EXPECT(msa_workspace_size(&d, MSA_OP_BWD_RECOMPUTE, &need_rc), MSA_OK);
+  if (!(need_rc > 0 && need_rc + (size_t)16384 * 65536 == need_bwd)) {
+    fprintf(stderr, "recompute workspace %zu, stored-dS workspace %zu\n", need_rc, need_bwd);
+    ++failures;
+  }
+  auto bwdx = [&](uint32_t flags, size_t nb) {
+    return msa_attn_bwd_ex(&d, F, 2048, 128, F, 128, 128, F, 128, 128, F, 2048, 128, Lp, F, 2048, 128, B, B, 0.088f,
+                           flags, F, 2048, 128, F, 128, 128, F, 128, 128, F, nb, nullptr);
+  };
+  EXPECT(bwdx(4u, BIG), MSA_ERR_INVALID_ARG);
+  EXPECT(bwdx(MSA_ATTN_RECOMPUTE, need_rc - 256), MSA_ERR_WORKSPACE);
+  EXPECT(bwdx(MSA_ATTN_DENSE, need_rc - 256), MSA_ERR_WORKSPACE);
+  EXPECT(bwdx(0u, need_rc), MSA_ERR_WORKSPACE);
 
   // attention-side q/k norm
   EXPECT(msa_qk_norm_rope_fwd(&d, F, 2048, 128, F, 128, 128, F, F, 1e-6f, 1e7f, 32, B, F, 2048, 128, F, 128, 128,

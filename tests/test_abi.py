@@ -58,9 +58,21 @@ def test_workspace_sizes_are_positive_and_monotone():
         assert 0 < small[op] < big[op]
         assert big[op] % 256 == 0
     assert msa.msa_workspace_size(dims(total_tokens=0, num_seqs=0, max_seqlen=0), msa.MSA_OP_BWD) == 0
-    # the unsharded 32k layer stays within a few GiB of scratch
-    assert msa.msa_workspace_size(dims(total_tokens=32768, num_seqs=1, max_seqlen=32768, num_q_heads=64,
-                                       num_kv_heads=4), msa.MSA_OP_BWD) < 3 << 30
+    # without the stored dS the unsharded 32k layer stays within a few GiB of scratch
+    layer = dims(total_tokens=32768, num_seqs=1, max_seqlen=32768, num_q_heads=64, num_kv_heads=4)
+    assert msa.msa_workspace_size(layer, msa.MSA_OP_BWD_RECOMPUTE) < 3 << 30
+
+
+@pytest.mark.parametrize("T,S,L,hk", [(16384, 3, 7122, 1), (32768, 1, 32768, 4), (65536, 2, 65536, 4),
+                                      (131072, 1, 131072, 2), (131072, 1, 131072, 4)])
+def test_backward_workspace_stored_ds_tail(T, S, L, hk):
+    """The backward workspace ends with 64 KB of stored dS per (token, KV head) while that tail stays within
+    16 GiB (T * Hk <= 262144); beyond it the backward recomputes and needs no tail."""
+    d = dims(total_tokens=T, num_seqs=S, max_seqlen=L, num_q_heads=16 * hk, num_kv_heads=hk)
+    full = msa.msa_workspace_size(d, msa.MSA_OP_BWD)
+    lean = msa.msa_workspace_size(d, msa.MSA_OP_BWD_RECOMPUTE)
+    tail = T * hk * 65536 if T * hk <= 262144 else 0
+    assert full == lean + tail
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -40,12 +40,12 @@ def select_both(msa, p, rows=None):
     return res, blk.cpu().numpy()
 
 
-def run_attn(msa, p, blk_np):
+def run_attn(msa, p, blk_np, recompute=False):
     cu = dev(p.cu_seqlens)
     q, k, v, do = dev(p.q), dev(p.k), dev(p.v), dev(p.do)
     blk = dev(torch.from_numpy(np.ascontiguousarray(blk_np)))
     o, lse = msa.msa_attn_fwd(q, k, v, blk, cu, p.max_seqlen)
-    dq, dk, dv = msa.msa_attn_bwd(q, k, v, o, lse, do, blk, cu, p.max_seqlen)
+    dq, dk, dv = msa.msa_attn_bwd(q, k, v, o, lse, do, blk, cu, p.max_seqlen, recompute=recompute)
     torch.cuda.synchronize()
     return o, lse, dq, dk, dv
 
@@ -105,6 +105,23 @@ def test_attention_parity_sparse(gpu_lib, lengths, hk, seed):
     p = synth.make_custom_pack(lengths, num_q_heads=16 * hk, num_kv_heads=hk, seed=seed)
     res = O.index_select(f32(p.idx_q), f32(p.idx_k), f32(p.w_q), f32(p.w_k), p.cu_seqlens.numpy())
     check_attn_full(p, res.blk_idx, run_attn(gpu_lib, p, res.blk_idx), f"attn {lengths} hk={hk}")
+
+
+@pytest.mark.parametrize("lengths,hk,seed", [([2400, 600], 1, 5), ([2300, 1100], 2, 8),
+                                             ([1, 127, 129, 2049, 300], 1, 12)])
+def test_recompute_backward(gpu_lib, lengths, hk, seed):
+    """MSA_ATTN_RECOMPUTE (the dQ pass recomputes S and dP; no stored dS): oracle parity, and bitwise the
+    stored-dS backward's gradients -- both passes form the same fp32 S, dP and Delta, round dS to bf16 the
+    same way and add the dQ products in the same order, and the dK/dV pass is the same kernel."""
+    p = synth.make_custom_pack(lengths, num_q_heads=16 * hk, num_kv_heads=hk, seed=seed)
+    res = O.index_select(f32(p.idx_q), f32(p.idx_k), f32(p.w_q), f32(p.w_k), p.cu_seqlens.numpy())
+    label = f"recompute {lengths} hk={hk}"
+    a = run_attn(gpu_lib, p, res.blk_idx, recompute=True)
+    check_attn_full(p, res.blk_idx, a, label)
+    b = run_attn(gpu_lib, p, res.blk_idx)
+    for x, y, n in zip(a[2:], b[2:], ("dQ", "dK", "dV")):
+        assert torch.equal(x, y), (label, n)
+    say(f"[{label}] dQ, dK, dV bitwise equal to the stored-dS backward")
 
 
 def test_edge_lengths(gpu_lib):
