@@ -61,8 +61,10 @@ int check_qsa_dims(const msa_dims* d) {
 }
 
 // Grid and workspace bounds of a pack whose blocks (dK/dV work items, key
-// numbering) are `unit` tokens wide, with `dhead` dims per head.
-void size_blocks(Sizes& z, int64_t unit, int64_t dhead) {
+// numbering) are `unit` tokens wide, with `dhead` dims per head.  The dK/dV
+// query chunk starts at `chunk0` tokens and doubles while the chunk slices
+// would exceed kPartialBudget.
+void size_blocks(Sizes& z, int64_t unit, int64_t dhead, int64_t chunk0) {
   // sum_s ceil(L_s / unit) <= (T + (unit - 1) S) / unit, and <= T
   int64_t cap = (z.T + (unit - 1) * z.S) / unit;
   if (cap > z.T) cap = z.T;
@@ -73,7 +75,7 @@ void size_blocks(Sizes& z, int64_t unit, int64_t dhead) {
   // 0 .. (min((j+1)*chunk, L) - 1) / unit.  With n = ceil(L / chunk) chunks and
   // m = chunk / unit, a sequence has at most min(n * ceil(L / unit),
   // m * n * (n + 1) / 2) items; both sum over a pack to the bounds below.
-  int64_t chunk = 512;
+  int64_t chunk = chunk0;
   for (;;) {
     const int64_t m = chunk / unit;
     const int64_t b1 = z.T * z.max_seqlen / (unit * chunk) + z.T / chunk + z.T / unit + 2 * z.S + 1;
@@ -97,7 +99,7 @@ Sizes sizes_of_qsa(const msa_dims* d) {
   z.Hk = d->num_kv_heads;
   z.max_seqlen = d->max_seqlen;
   z.nbmax = (z.max_seqlen + msa::kQsaKeyTile - 1) / msa::kQsaKeyTile;
-  size_blocks(z, msa::kQsaKeyTile, msa::kQsaHeadDim);
+  size_blocks(z, msa::kQsaKeyTile, msa::kQsaHeadDim, 512);
   return z;
 }
 
@@ -109,7 +111,16 @@ Sizes sizes_of(const msa_dims* d) {
   z.Hk = d->num_kv_heads;
   z.max_seqlen = d->max_seqlen;
   z.nbmax = (z.max_seqlen + msa::kBlock - 1) / msa::kBlock;
-  size_blocks(z, msa::kBlock, msa::kHeadDim);
+  // The dK/dV pass launches its items longest first over two workgroups per
+  // CU (512 slots), and an item's work grows with its chunk: the item of a
+  // chunk's own block is selected by every query of the chunk.  Chunks stay
+  // at 512 tokens until a slot's share of the T * Hk * 16 selections exceeds
+  // that (T * Hk / 32 > chunk), then grow with it up to 2048: fewer, longer
+  // items, so fewer chunk slices for the reduce to sum, while no single item
+  // outlasts a slot's share (16k pack 512, 32k pack 1024, 32k x 4 heads 2048).
+  int64_t chunk0 = 512;
+  while (chunk0 < msa::kDkdvChunkMax && 2 * chunk0 <= z.T * z.Hk / 32) chunk0 *= 2;
+  size_blocks(z, msa::kBlock, msa::kHeadDim, chunk0);
   return z;
 }
 
