@@ -92,7 +92,15 @@ def traffic_file(config: str) -> str:
 
 # template flags of the library's kernel instances, in order; kernels not listed take (dense, qknorm)
 KERNEL_FLAGS = {"block_prep_kernel": ("qknorm",), "bwd_block_prep_kernel": ("qknorm",),
-                "qsa_prep_kernel": ("swizzled",), "attn_bwd_dkdv_kernel": ("dense",)}
+                "qsa_prep_kernel": ("swizzled",)}
+# instances named outright: the backward's stored-dS kernels carry the names of the library's timers (what
+# the bench step runs); the sparse recompute instances (MSA_ATTN_RECOMPUTE, or packs too large for the
+# stored dS) get a _recompute suffix
+KERNEL_NAMES = {"attn_bwd_dkdv_kernel<false, true>": "attn_bwd_dkdv_kernel",
+                "attn_bwd_dkdv_kernel<false, false>": "attn_bwd_dkdv_recompute_kernel",
+                "attn_bwd_dkdv_kernel<true, false>": "attn_bwd_dkdv_dense_kernel",
+                "attn_bwd_dq_ds_kernel": "attn_bwd_dq_kernel",
+                "attn_bwd_dq_kernel<false, false>": "attn_bwd_dq_recompute_kernel"}
 
 
 def kernel_key(raw: str) -> str:
@@ -103,6 +111,8 @@ def kernel_key(raw: str) -> str:
     n = raw.replace("(anonymous namespace)::", "").split("(")[0].replace("msa::", "").strip()
     if n.startswith("void "):
         n = n[len("void "):]
+    if n in KERNEL_NAMES:
+        return KERNEL_NAMES[n]
     m = re.search(r"<([^<>]*)>$", n)
     flags = [a.strip() for a in m.group(1).split(",")] if m else []
     n = re.sub(r"<[^<>]*>$", "", n)
