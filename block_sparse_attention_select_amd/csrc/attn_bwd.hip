@@ -697,13 +697,16 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_ds_kernel(
   const __amdgpu_buffer_rsrc_t dsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(ds_buf + (((int64_t)(tvalid ? t : 0) * Hk + h) * kTopk) * 4 * 512), (short)0,
       tvalid ? kTopk * 4096 : 0, 0x00020000);
-  // loads the dS of the k-th block the walk will meet (zeros when there is none)
+  // loads the dS of the k-th block the walk will meet (zeros when there is
+  // none); non-temporal: each dS is read once
+  constexpr int kNonTemporal = 2;  // the cache-policy bit of a streaming access
   auto load_ds = [&](int k, bf16x8* dst) {
     const uint64_t m = __ballot(rank == k);
     const int off = (m != 0ull ? __builtin_ctzll(m) * 4096 : kTopk * 4096) + 16 * fresh_lane();
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
-      dst[qq] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(dsrc, off + 1024 * qq, 0, 0));
+      dst[qq] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(dsrc, off + 1024 * qq, 0, kNonTemporal));
   };
 
   // union of the tile's blocks

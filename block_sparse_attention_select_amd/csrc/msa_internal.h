@@ -48,6 +48,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // Native 16-byte vector: unlike HIP's uint4 (a union-based struct) it stays in
 // registers when copied around.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(u16 h) { return __uint_as_float(((uint32_t)h) << 16); }
