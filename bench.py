@@ -241,6 +241,58 @@ def cpu_baseline(p, stride: int):
             "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
+def seed_leg(msa, config: str, seed: int, steps: int, warmup: int) -> dict:
+    """The bench step (select -> forward on its ids -> backward) on another seed's pack of the same config:
+    wall time per step, the select / forward / backward split from events between the calls, and the counted
+    fwd+bwd rate."""
+    p = synth.make_pack(config, seed)
+    dev = torch.device("cuda:0")
+    g = lambda t: t.to(dev)
+    cu = g(p.cu_seqlens)
+    q, k, v, do = g(p.q), g(p.k), g(p.v), g(p.do)
+    iq, ik, wq, wk = g(p.idx_q), g(p.idx_k), g(p.w_q), g(p.w_k)
+    T, Hq, Hk = p.total, p.num_q_heads, p.num_kv_heads
+    dims = msa.make_dims(T, len(p.lengths), p.max_seqlen, Hq, Hk)
+    ws = {op: torch.empty(max(msa.msa_workspace_size(dims, op), 1), dtype=torch.uint8, device=dev)
+          for op in (msa.MSA_OP_SELECT, msa.MSA_OP_FWD, msa.MSA_OP_BWD)}
+    blk = torch.empty(T, Hk, 16, dtype=torch.int32, device=dev)
+    o, lse = torch.empty_like(q), torch.empty(T, Hq, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        msa.msa_index_select(iq, ik, wq, wk, cu, p.max_seqlen, out=blk, workspace=ws[msa.MSA_OP_SELECT])
+        if ev is not None:
+            ev[1].record()
+        msa.msa_attn_fwd(q, k, v, blk, cu, p.max_seqlen, out=o, lse=lse, workspace=ws[msa.MSA_OP_FWD])
+        if ev is not None:
+            ev[2].record()
+        msa.msa_attn_bwd(q, k, v, o, lse, do, blk, cu, p.max_seqlen, dq=dq, dk=dk, dv=dv,
+                         workspace=ws[msa.MSA_OP_BWD])
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    split = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i in range(3)]
+    per_qhead = selected_keys(blk.cpu().numpy(), p.cu_seqlens.numpy()) * (Hq // Hk)
+    fb_ms = split[1] + split[2]
+    return {"seed": seed, "lengths": p.lengths, "step_ms": round(wall_ms, 4), "select_ms": round(split[0], 4),
+            "fwd_ms": round(split[1], 4), "bwd_ms": round(split[2], 4), "fwd_bwd_ms": round(fb_ms, 4),
+            "fwd_bwd_mfma_frac": round(14 * D * per_qhead / (fb_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def qsa_leg(msa, seed: int, steps: int, warmup: int) -> dict:
     """Narrow-block variant (msa_qsa_attn_*) on the qsa16k pack: 12 q / 1 kv heads, D 256,
     4-token blocks, 512 seeded block ids per query (synth.random_block_lists)."""
@@ -311,6 +363,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)  # the clocks settle over the first tens of steps
     ap.add_argument("--config", default="pack16k", choices=sorted(c for c in synth.CONFIGS if c != "qsa16k"))
     ap.add_argument("--no-qsa", action="store_true", help="skip the narrow-block (qsa16k) leg")
+    ap.add_argument("--no-seeds", action="store_true", help="skip the step timing on the other two seeds' packs")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-stride", type=int, default=3, help="oracle fwd+bwd sample: every n-th token")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle (timing and selection parity)")
@@ -552,6 +605,18 @@ def main():
         "roofline": roofline,
         "context_gb300_ms": {"fwd_bwd": 6.7, "select": 0.62, "note": "pages' GB300 figures on unpublished 16k packs"},
     }
+    if not args.no_seeds:
+        # the same config's packs for two more seeds (other lengths and data): the step time per seed and the
+        # mean over the three
+        legs = [{"seed": args.seed, "lengths": p.lengths, "step_ms": round(wall_ms, 4), "select_ms": round(sel_ms, 4),
+                 "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4), "fwd_bwd_ms": round(fb_ms, 4),
+                 "fwd_bwd_mfma_frac": round(fb_tflops / PEAK_BF16_TFLOPS, 4)}]
+        for sd in (args.seed + 1, args.seed + 2):
+            legs.append(seed_leg(msa, args.config, sd, max(10, args.steps // 2), min(args.warmup, 20)))
+        line["seeds"] = {"per_seed": legs,
+                         "mean_step_ms": round(float(np.mean([x["step_ms"] for x in legs])), 4),
+                         "mean_fwd_bwd_ms": round(float(np.mean([x["fwd_bwd_ms"] for x in legs])), 4),
+                         "mean_fwd_bwd_mfma_frac": round(float(np.mean([x["fwd_bwd_mfma_frac"] for x in legs])), 4)}
     if not args.no_qsa:
         line["qsa16k"] = qsa_leg(msa, args.seed, args.steps, args.warmup)
     if args.calibrate_copy > 0:
