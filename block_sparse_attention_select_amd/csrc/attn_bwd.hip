@@ -10,14 +10,15 @@
 // the key-block sums running over every (query, head) of the group that
 // selected the block.
 //
-// Two pipelines.  Sparse layers (unless the workspace would exceed
-// kDsBufMaxBytes of dS): bwd_block_prep (K copies, plan) -> bwd_delta_kernel
+// Two pipelines.  Sparse layers (unless the caller asks for the recomputing
+// form or the dS would exceed kDsBufMaxBytes): bwd_block_prep (K copies,
+// plan) -> bwd_delta_kernel
 // (Delta, -LSE log2(e), dK/dV item loads) -> dK/dV, which also writes every
 // (selecting query, block)'s dS in bf16 -> dkdv_reduce -> attn_bwd_dq_ds_kernel
 // (dQ = scale dS K from the stored dS, one product per selected block instead
-// of three).  Dense layers and the fused attention-side norm: bwd_block_prep
-// (K and V copies) -> attn_bwd_dq_kernel (recomputes S and dP) -> dK/dV ->
-// dkdv_reduce.
+// of three).  Dense layers, the fused attention-side norm and the recomputing
+// form: bwd_block_prep (K and V copies) -> attn_bwd_dq_kernel (recomputes S
+// and dP) -> dK/dV -> dkdv_reduce.
 //
 // Kernels:
 //   attn_bwd_dq_kernel  token-major dQ, tiles of 16 tokens walking the union

@@ -276,8 +276,9 @@ struct BwdArgs {
   int32_t* item_order;  // [Hk][items_cap] items by decreasing load
   float* part_dk;   // [Hk][items_cap][128][128]
   float* part_dv;
-  // sparse layers without the fused norm, when it fits kDsBufMaxBytes: the
-  // dK/dV pass stores every (token, KV head, listed block)'s bf16 dS here
+  // sparse layers without the fused norm, when it fits kDsBufMaxBytes and the
+  // caller did not ask for the recomputing form: the dK/dV pass stores every
+  // (token, KV head, listed block)'s bf16 dS here
   // ([T][Hk][16][4 quarters][64 lanes][8]) and dQ is formed from it
   u16* ds = nullptr;
   // attention-side norm fused in (nrm != nullptr): q and k are raw; the prep
