@@ -319,11 +319,14 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
         if (diag && kBlock * c + 64 * hf > tok_pos[j]) break;
         // S^T for the half's four key tiles: the four accumulation chains are
         // interleaved (consecutive MFMAs independent) and the K operand reads
-        // run eight ahead of the MFMAs that consume them
+        // run eight ahead of the MFMAs that consume them.  The MFMA blocks run
+        // at raised wave priority, so on a SIMD whose other wavefronts are in
+        // their softmax the matrix unit is fed first (16k pack: 3 % faster)
         f32x4 st[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
         {
+          __builtin_amdgcn_s_setprio(1);
           bf16x8 ka[16];
 #pragma unroll
           for (int i = 0; i < 16; ++i)
@@ -338,6 +341,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
           }
           __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
         float mx = -INFINITY;
         if (diag) {
 #pragma unroll
@@ -378,6 +382,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
         // O^T += V^T P^T: eight independent accumulators per sweep, V operand
         // reads eight ahead
         {
+          __builtin_amdgcn_s_setprio(1);
           bf16x8 va[16];
 #pragma unroll
           for (int i = 0; i < 16; ++i)
@@ -392,6 +397,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
           }
           __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
       }
     }
     wait_copies();

@@ -302,6 +302,9 @@ __global__ __launch_bounds__(64 * kTok) void qsa_fwd_kernel(
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
       {
+        // the MFMA blocks run at raised wave priority, so on a SIMD whose other
+        // wavefronts are in their softmax the matrix unit is fed first
+        __builtin_amdgcn_s_setprio(1);
         bf16x8 ka[32];
 #pragma unroll
         for (int i = 0; i < 32; ++i) ka[i] = __builtin_bit_cast(bf16x8, kbuf[buf][(i & 3) * 8 + (i >> 2)][lane]);
@@ -314,6 +317,7 @@ __global__ __launch_bounds__(64 * kTok) void qsa_fwd_kernel(
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_s_setprio(0);
       }
       // mask: accumulator row r of tile kt in lane group g is tile key
       // score_key(kt, 4g + r) = 32 (kt/2) + 8g + 4 (kt%2) + r, all four in
@@ -356,6 +360,7 @@ __global__ __launch_bounds__(64 * kTok) void qsa_fwd_kernel(
       const bf16x8 pf1 = pack_bf16x8(st[2], st[3]);
       // O^T += V^T P^T over the tile's two 32-key halves
       {
+        __builtin_amdgcn_s_setprio(1);
         bf16x8 va[32];
 #pragma unroll
         for (int i = 0; i < 32; ++i) va[i] = __builtin_bit_cast(bf16x8, vbuf[buf][(i & 15) * 2 + (i >> 4)][lane]);
@@ -368,6 +373,7 @@ __global__ __launch_bounds__(64 * kTok) void qsa_fwd_kernel(
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_s_setprio(0);
       }
     }
     wait_copies();
