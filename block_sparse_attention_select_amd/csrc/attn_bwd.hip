@@ -28,7 +28,8 @@
 //   bwd_delta_kernel    Delta and -LSE * log2(e) per (token, query head), and
 //                       the dK/dV item loads, ahead of the dK/dV pass;
 //   attn_bwd_dq_ds_kernel token-major dQ from the dS the dK/dV pass stored:
-//                       the same tiles and union walk with only K^T staged;
+//                       the same tiles and union walk with only K^T staged
+//                       (bwd_block_prep writes it in operand order);
 //   attn_bwd_dkdv_kernel (attn_bwd_dkdv.hip) key-block-major dK/dV per chunk
 //                       of selecting queries;
 //   dkdv_reduce_kernel  sums the per-chunk slices of a block in chunk order
@@ -63,7 +64,12 @@ constexpr int kTileTok = kAttnTile;
 // kNorm: K is raw; its rows get the attention-side norm and RoPE (qk_rope.h)
 // on the way into the copy, and the normalized rows are also written to khat
 // ([T][Hk][128]) for the dK/dV pass.
-template <bool kNorm>
+// kKt (the stored-dS backward, K only): kop instead gets K^T in the operand
+// order of dQ^T = K^T dS^T, run dt * 4 + q (dims 16 dt .., keys 32 q ..) with
+// lane (dim 16 dt + l % 16, group l / 16) holding keys 32 q + 8 (l / 16) .. +7,
+// transposed through an LDS tile of the part's 32 dims (workgroup part p:
+// runs 8p .. 8p+7), so each dQ operand is one plain 16-byte LDS read.
+template <bool kNorm, bool kKt = false>
 __global__ __launch_bounds__(256) void bwd_block_prep_kernel(const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
                                                              const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
                                                              const int32_t* __restrict__ cu, int S, int chunk,
@@ -102,6 +108,29 @@ __global__ __launch_bounds__(256) void bwd_block_prep_kernel(const u16* __restri
   const int seq0 = cu[s];
   const int L = cu[s + 1] - seq0;
   u16* dst = (is_v ? vop : kop) + ((int64_t)gb * Hk + h) * (kHeadDim * kBlock);
+  if constexpr (kKt) {
+    static_assert(!kNorm, "the transposed copy serves the plain stored-dS backward");
+    __shared__ u16 tile[kBlock][32 + 8];
+    for (int i = threadIdx.x; i < kBlock * 4; i += 256) {
+      const int key = i >> 2, ch = i & 3;
+      const int kp = kBlock * c + key;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (kp < L)
+        val = *reinterpret_cast<const u32x4*>(k + (int64_t)(seq0 + kp) * k_st + (int64_t)h * k_sh + 32 * part + 8 * ch);
+      *reinterpret_cast<u32x4*>(&tile[key][8 * ch]) = val;
+    }
+    __syncthreads();
+    for (int i = 512 * part + threadIdx.x; i < 512 * part + 512; i += 256) {
+      const int run = i >> 6, ln = i & 63;
+      const int d = 16 * (run >> 2) + (ln & 15) - 32 * part;
+      const int k0 = 32 * (run & 3) + 8 * (ln >> 4);
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (uint32_t)tile[k0 + 2 * e][d] | ((uint32_t)tile[k0 + 2 * e + 1][d] << 16);
+      *reinterpret_cast<u32x4*>(dst + (int64_t)i * 8) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    return;
+  }
   if constexpr (kNorm) {
     if (!is_v) {
       // the part's 32 keys (tiles 2p, 2p+1): each row normalized and rotated
@@ -620,8 +649,9 @@ __global__ __launch_bounds__(1024) void bwd_delta_kernel(
 // lane (head s, group gg) holding keys 32 qq + 8 gg .. +7 of head s: each
 // quarter is written to a 1 KB LDS slot of the wavefront and read back with
 // ds_read_b64_tr_b16.  The tiling and union walk are the dQ kernel's with only
-// K staged (its K^T operands read transposed), three K buffers deep: block
-// u + 2 is copied while block u is used, and each wavefront's dS loads run two
+// K^T staged, from the prep kernel's copy in operand order (each A operand one
+// 16-byte read), three buffers deep: block u + 2 is copied while block u is
+// used, and each wavefront's dS loads run two
 // of its own blocks ahead, so the wait that ends a step (for block u + 1's
 // copies) leaves the newest loads in flight (loads and copies complete in
 // issue order).
@@ -736,7 +766,8 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_ds_kernel(
   __syncthreads();
   const int nsteps = nunion;
 
-  // wavefronts 0-7 copy the four K runs of key tile w
+  // wavefronts 0-7 copy the K^T runs 4w .. 4w+3 (dims 16 w .., the block's
+  // four key quarters)
   const bool stager = wave < 8;
   auto stage = [&](int u, int buf) {
     if (!stager) return;
@@ -819,14 +850,9 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_ds_kernel(
         const uint2 lo = read_tr16(slot + ds_rd0), hi = read_tr16(slot + ds_rd1);
         bop = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
       }
-      const uint32_t kq = lds_offset(&kbuf[buf][8 * qq][0]) + tr_lane_offset(fresh_lane());
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const uint32_t off = kq + (dt >> 1) * 1024 + (dt & 1) * 512;
-        const uint2 lo = read_tr16(off), hi = read_tr16(off + 4096);
-        const bf16x8 ta = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-        dqacc[dt] = mfma16x16x32(ta, bop, dqacc[dt]);
-      }
+      for (int dt = 0; dt < 8; ++dt)
+        dqacc[dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, kbuf[buf][4 * dt + qq][lane]), bop, dqacc[dt]);
     }
     ++k;
     end_step(staging, true);
@@ -929,7 +955,7 @@ void launch_attn_bwd(const Sizes& z, const BwdArgs& a, const PlanBufs& p, hipStr
     // sparse, no fused norm: dK/dV first (storing dS), then dQ from the stored dS
     {
       KernelTimer timer("bwd_block_prep", st);
-      bwd_block_prep_kernel<false><<<dim3((unsigned)(z.nblk_cap + 1), (unsigned)Hk, 4), 256, 0, st>>>(
+      bwd_block_prep_kernel<false, true><<<dim3((unsigned)(z.nblk_cap + 1), (unsigned)Hk, 4), 256, 0, st>>>(
           a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.cu, S, (int)z.chunk, (int)z.ntiles, p, Hk, none, nullptr,
           a.kop, nullptr, a.item_load, (int)(z.Hk * z.items_cap));
     }
