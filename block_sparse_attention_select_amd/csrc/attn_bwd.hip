@@ -733,11 +733,16 @@ __global__ __launch_bounds__(64 * kDqWaves) void attn_bwd_dq_ds_kernel(
   constexpr int kNonTemporal = 2;  // the cache-policy bit of a streaming access
   auto load_ds = [&](int k, bf16x8* dst) {
     const uint64_t m = __ballot(rank == k);
-    const int off = (m != 0ull ? __builtin_ctzll(m) * 4096 : kTopk * 4096) + 16 * fresh_lane();
+    const int slot = m != 0ull ? __builtin_ctzll(m) : 0;
+    // on the token's own block the quarters after the query are skipped by
+    // the walk (and were not stored): they are not read either
+    const int c = __builtin_amdgcn_readlane(my_gb, slot) - tok_base;
+    const int qlast = m == 0ull ? -1 : (c == tok_b ? (tok_pos - kBlock * c) >> 5 : 3);
+    const int off = slot * 4096 + 16 * fresh_lane();
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq)
-      dst[qq] = __builtin_bit_cast(
-          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(dsrc, off + 1024 * qq, 0, kNonTemporal));
+      dst[qq] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                               dsrc, qq <= qlast ? off + 1024 * qq : kTopk * 4096, 0, kNonTemporal));
   };
 
   // union of the tile's blocks

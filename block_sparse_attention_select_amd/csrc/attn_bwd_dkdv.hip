@@ -268,7 +268,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               sw[kk][2 * tk + 1] = pack_bf16x2(d[2], d[3]);
             }
             if constexpr (kWriteDs) {
-              if (tsel[tk] >= 0) {
+              // a query before the wavefront's first key (on its own block)
+              // has only zero dS here, which the dQ pass never reads
+              if (tsel[tk] >= 0 && pos[tk] >= kbase) {
                 // two 512-byte runs of register pairs: one 16-byte store per
                 // lane would need the halves copied into four consecutive
                 // registers, which this loop does not have to spare.  The
