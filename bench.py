@@ -76,13 +76,35 @@ CSRC = os.path.join(ROOT, "block_sparse_attention_select_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+# a C++ comment or string literal (strings kept as written, comments dropped)
+_CPP_TOKEN = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
+
+
+def code_text(src: str) -> str:
+    """The source without its comments, whitespace runs outside string literals collapsed to one space."""
+    out, code, pos = [], [], 0
+    for m in _CPP_TOKEN.finditer(src):
+        code.append(src[pos:m.start()])
+        if m.group().startswith("/"):
+            code.append(" ")
+        else:
+            out.append(re.sub(r"\s+", " ", "".join(code)))
+            out.append(m.group())
+            code = []
+        pos = m.end()
+    code.append(src[pos:])
+    out.append(re.sub(r"\s+", " ", "".join(code)))
+    return "".join(out).strip()
+
+
 def kernel_source_hash() -> str:
-    """Hash of every HIP/C++ source of the library: counters taken on other sources are stale."""
+    """Hash of the code of every HIP/C++ source of the library (comments and layout ignored): counters
+    taken on other code are stale."""
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
-        with open(f, "rb") as fh:
+        with open(f, encoding="utf-8") as fh:
             h.update(os.path.basename(f).encode())
-            h.update(fh.read())
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

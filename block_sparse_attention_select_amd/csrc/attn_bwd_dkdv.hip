@@ -30,7 +30,8 @@
 //      itself; other blocks write fp32 slices that dkdv_reduce_kernel sums in
 //      chunk order.
 //   kWriteDs: every selecting (token, block)'s bf16 dS also goes to HBM as the
-//      score registers hold it (two 8-byte stores per lane and token), so the
+//      score registers hold it (two 8-byte stores per lane and token; on the
+//      token's own block not the 32-key quarters past it), so the
 //      token-major dQ pass needs one product per block (dQ = scale dS K)
 //      instead of recomputing S and dP.
 #include "attn_stage.h"
