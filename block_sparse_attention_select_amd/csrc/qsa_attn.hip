@@ -26,11 +26,12 @@
 //             and -LSE * log2(e) per head for the dK/dV pass;
 //   dK/dV     key-tile major: one workgroup per (sequence, query chunk, key
 //             tile), four wavefronts of 16 keys with K and V in registers,
-//             streaming the chunk's selecting tokens through LDS two at a time;
-//             chunk slices are summed in chunk order by qsa_reduce_kernel
-//             (fixed order, no atomics).
-// Query heads are padded from 12 to the MFMA's 16 with zero q (forward, dQ) or
-// with statistics that zero P (dK/dV); padded outputs are never stored.
+//             streaming the (selecting token, query head) rows of the chunk
+//             through LDS 32 at a time, so a step mixes tokens and carries no
+//             padding heads; chunk slices are summed in chunk order by
+//             qsa_reduce_kernel (fixed order, no atomics).
+// In the forward and dQ, query heads are padded from 12 to the MFMA's 16 with
+// zero q; padded outputs are never stored.
 #include "attn_stage.h"
 #include "plan_blocks.h"
 
@@ -575,32 +576,40 @@ __global__ __launch_bounds__(64 * kTok) void qsa_dq_kernel(
 // ---------------------------------------------------------------------------
 // dK/dV.
 // ---------------------------------------------------------------------------
-constexpr int kPair = 2;  // tokens per staging round (one MFMA step)
+constexpr int kPair = 2;  // 16-row tiles per staging round (one MFMA step of 32 rows)
 
-// Stage layout of one token (u32x4 units): [0, 512) q and [512, 1024) dO as
-// [ds][slot], operand lane li + 16g of run ds (head li, dims 32 ds + 8g ..) at
-// slot swz_slot(li + 16g); heads past 12 repeat head 11 (finite operands whose
-// P the statistics zero).  Stats: 16 -LSE log2 e, then 16 Delta.
-__device__ __forceinline__ void stage_token(int t, int h, int Hk, int lane, uint32_t slot_lds, uint32_t stats_lds,
-                                            const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
-                                            const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
-                                            const float* __restrict__ nlse, const float* __restrict__ delta) {
-  t = __builtin_amdgcn_readfirstlane(t);
-  const int hr = min(swz_slot(lane) & 15, kG - 1);
-  const uint32_t q_off = (uint32_t)(2 * (hr * q_sh + 8 * (lane >> 4)));
-  const uint32_t do_off = (uint32_t)(2 * (hr * do_sh + 8 * (lane >> 4)));
-  const u16* qr = q + (int64_t)t * q_st + (int64_t)(h * kG) * q_sh;
-  const u16* dr = dO + (int64_t)t * do_st + (int64_t)(h * kG) * do_sh;
+// The selecting tokens' query heads are taken as one list of rows, row r being
+// head r % 12 of selecting token r / 12, so that a 32-row MFMA step carries
+// no padding heads (a step of two tokens would carry 8 of 32).  Stage layout
+// of one 16-row tile (u32x4 units): [0, 512) q and [512, 1024) dO as
+// [ds][slot], operand lane li + 16g of run ds (row li of the tile, dims
+// 32 ds + 8g ..) at slot swz_slot(li + 16g); rows past the list's end repeat
+// its last row (finite operands, masked).  Stats: the tile's 16 -LSE log2 e,
+// then its 16 Delta.  Every lane reads its own row, so the copies take
+// per-lane addresses.
+__device__ __forceinline__ void stage_rows(int row0, int nrows, const int* sel, int tok0, int h, int Hk, int lane,
+                                           uint32_t slot_lds, uint32_t stats_lds,
+                                           const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
+                                           const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
+                                           const float* __restrict__ nlse, const float* __restrict__ delta) {
+  const int r = min(row0 + (swz_slot(lane) & 15), nrows - 1);
+  const int n = r / kG;
+  const int t = tok0 + (sel[n] & 0xFFFF);
+  const int head = h * kG + (r - kG * n);
+  const u16* qr = q + (int64_t)t * q_st + (int64_t)head * q_sh + 8 * (lane >> 4);
+  const u16* dr = dO + (int64_t)t * do_st + (int64_t)head * do_sh + 8 * (lane >> 4);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    dma16s(qr + 32 * i, q_off, slot_lds + i * 1024);
-    dma16s(dr + 32 * i, do_off, slot_lds + 8192 + i * 1024);
+    dma16(qr + 32 * i, slot_lds + i * 1024);
+    dma16(dr + 32 * i, slot_lds + 8192 + i * 1024);
   }
-  const int64_t row = ((int64_t)t * Hk + h) * 16;
-  if (lane < 16)
-    dma4s(nlse + row, 4 * lane, stats_lds);
-  else if (lane < 32)
-    dma4s(delta + row - 16, 4 * lane, stats_lds);
+  // lanes 0-15: -LSE of rows row0 + lane; lanes 16-31: Delta of rows row0 + lane - 16
+  if (lane < 32) {
+    const int rs = min(row0 + (lane & 15), nrows - 1);
+    const int ns = rs / kG;
+    const int ts = tok0 + (sel[ns] & 0xFFFF);
+    dma4((lane < 16 ? nlse : delta) + ((int64_t)ts * Hk + h) * 16 + (rs - kG * ns), stats_lds);
+  }
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void qsa_dkdv_kernel(
@@ -687,16 +696,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // 3. stream the selecting tokens through LDS, two per MFMA step; wavefronts
-  // 0 and 1 copy the two tokens of a round
+  // 3. stream the selecting tokens' rows through LDS, 32 per MFMA step;
+  // wavefronts 0 and 1 copy the two 16-row tiles of a round
   if (nsel > 0) {
-    const int nround = (nsel + kPair - 1) / kPair;
+    const int nrows = kG * nsel;
+    const int nround = (nrows + 32 - 1) / 32;
     auto stage_round = [&](int bi, int buf) {
-      if (wave < kPair) {
-        const int n = min(bi * kPair + wave, nsel - 1);  // past the end: repeat the last token (masked)
-        stage_token(seq0 + p_begin + (sel[n] & 0xFFFF), h, Hk, fresh_lane(), lds_offset(&stage[buf][wave][0]),
-                    lds_offset(&stats[buf][wave][0]), q, q_st, q_sh, dO, do_st, do_sh, nlse, delta);
-      }
+      if (wave < kPair)
+        stage_rows(32 * bi + 16 * wave, nrows, sel, seq0 + p_begin, h, Hk, fresh_lane(),
+                   lds_offset(&stage[buf][wave][0]), lds_offset(&stats[buf][wave][0]), q, q_st, q_sh, dO, do_st,
+                   do_sh, nlse, delta);
     };
     stage_round(0, 0);
     wait_copies();
@@ -706,20 +715,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int bi = 0; bi < nround; ++bi) {
       const int cur = bi & 1;
       if (bi + 1 < nround) stage_round(bi + 1, cur ^ 1);
-      const int n0 = bi * kPair;
-      // a missing second token is masked out entirely
+      // per tile tk, this lane's accumulator rows 4g .. 4g+3 (rows
+      // 32 bi + 16 tk + 4g ..) belong to one token (12 is a multiple of 4);
+      // rows past the list's end are masked out entirely
       int pos[2];
       uint32_t msk[2];
 #pragma unroll
       for (int tk = 0; tk < 2; ++tk) {
-        const bool ok = n0 + tk < nsel;
-        const int e = sel[min(n0 + tk, nsel - 1)];
+        const int row = 32 * bi + 16 * tk + 4 * g;
+        const int e = sel[min(row / kG, nsel - 1)];
         pos[tk] = p_begin + (e & 0xFFFF);
-        msk[tk] = ok ? ((uint32_t)e >> 16) : 0u;
+        msk[tk] = row < nrows ? ((uint32_t)e >> 16) : 0u;
       }
-      // S = q K^T and dP = dO V^T per token, turned into bf16 P and dS: lane
-      // (key li, group g) keeps heads 4g .. 4g+3 of each token, two per dword,
-      // as the A operand of dV and dK (dwords 0-1 token 0, dwords 2-3 token 1)
+      // S = q K^T and dP = dO V^T per 16-row tile, turned into bf16 P and dS:
+      // lane (key li, group g) keeps rows 4g .. 4g+3 of each tile, two per
+      // dword, as the A operand of dV and dK (dwords 0-1 tile 0, 2-3 tile 1)
       u32x4 pw, sw;
       const int ln = fresh_lane();
       const int sl = swz_slot(ln);
