@@ -20,20 +20,44 @@ namespace msa {
 namespace {
 
 // ---------------------------------------------------------------------------
-// 1. Features.  One wavefront per kProTok consecutive tokens.  Lane l < 32
-// holds the RoPE pair (l, l + 32) of a token, lane l >= 32 dims 32 + l and
-// 64 + l.  The RoPE angles (fp64 from the host's fp64 inverse frequencies,
-// rounded to fp32) are formed for two tokens at a time, lane l for pair l % 32
-// of token l / 32, and token 1's are then swapped into lanes 0..31.  Every
-// head's inputs are loaded before the position lookup and the angles.  The
-// arithmetic order (square, sum, scale by 1/128, add eps, sqrt, divide,
-// multiply by x, multiply by (1 + w); rotation as two products and one sum) is
-// kept free of fused multiply-adds so every step rounds once in fp32.
+// 1. Features.  One wavefront per two tokens.  First the RoPE angles of both
+// tokens, one per lane (lane l: token l / 32, pair l % 32; fp64 from the host's
+// fp64 inverse frequencies, rounded to fp32), into LDS.  Then, per head, one
+// pass over four rows {token 0, token 1} x {q, k}: lane group g = lane / 16
+// holds row g (token g / 2, q for even g, k for odd g) and lane j = lane % 16
+// its dims 8j .. 8j+7, one 16-byte load.  The sum of squares has a fixed
+// order: eight partial sums over the dims of each residue mod 8, each adding
+// its 16 squares in dim order (carried lane to lane by DPP), then the
+// partials as ((0+1)+(2+3))+((4+5)+(6+7)); the rotation partner of dims
+// 8j .. 8j+7 (j < 8) sits in lane j ^ 4.  Each operation is a separately rounded fp32 operation: no fused
+// multiply-adds (norm: square, sum, scale by 1/128, add eps, sqrt, divide,
+// multiply by x, multiply by (1 + w); rotation: two products and one sum).
+// The sequence of a token comes from a ballot over cu_seqlens held one entry
+// per lane (packs of up to 63 sequences; a binary search beyond).
 // The launch has one more workgroup, which numbers the pack's blocks for the
 // scoring kernel (plan_blocks).
 // ---------------------------------------------------------------------------
-constexpr int kProTok = 4;
 constexpr int kProWaves = 4;
+
+// Sequence of token t: lane l holds cu[l] (or INT_MAX past S) when S < 64.
+__device__ __forceinline__ int seq_of(const int32_t* __restrict__ cu, int S, int cu_lane, int t) {
+  if (S < 64) return __popcll(__ballot(cu_lane <= t)) - 1;
+  return find_seq(cu, S, t);
+}
+
+// Lane i - 1's value within each 16-lane row; 0 in the row's first lane.
+__device__ __forceinline__ float dpp_shr1(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xF, 0xF, false));
+}
+// The value of the last lane of each 16-lane row, in every lane of the row.
+__device__ __forceinline__ float row_lane15(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x10 | (0x0F << 5)));
+}
+// ds_swizzle in bit-mask mode: lane ^ m within each 32-lane half
+template <int kMask>
+__device__ __forceinline__ float swz_xor(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F | (kMask << 10)));
+}
 
 __global__ __launch_bounds__(64 * kProWaves) void select_prologue_kernel(
     const u16* __restrict__ idx_q, int64_t sq_t, int64_t sq_h,
@@ -42,67 +66,106 @@ __global__ __launch_bounds__(64 * kProWaves) void select_prologue_kernel(
     const int32_t* __restrict__ cu, int S, int T, int Hk, int chunk, PlanBufs plan,
     u16* __restrict__ qfeat, u16* __restrict__ kfeat) {
 #pragma clang fp contract(off)
+  __shared__ __align__(16) float ang[kProWaves][2][2][32];  // [wave][token][cos, sin][pair]
   if (blockIdx.x == gridDim.x - 1) {
     __shared__ int sb[64 * kProWaves], si[64 * kProWaves];
     plan_blocks<64 * kProWaves, kBlock>(cu, S, chunk, plan.blkbase, plan.blk_seq, plan.seqitem, plan.totals, sb, si);
     return;
   }
-  const int t0 = (blockIdx.x * kProWaves + (threadIdx.x >> 6)) * kProTok;
+  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  if (t0 >= T) return;
-  const int d0 = lane < 32 ? lane : 32 + lane;
-  const int d1 = d0 + 32;
-  const float wq0 = 1.0f + bf2f(w_q[d0]), wq1 = 1.0f + bf2f(w_q[d1]);
-  const float wk0 = 1.0f + bf2f(w_k[d0]), wk1 = 1.0f + bf2f(w_k[d1]);
-  float c[kProTok], sf[kProTok];
+  const int t0 = (blockIdx.x * kProWaves + wave) * 2;  // may be past T: such a wavefront stores nothing
+  const int g = lane >> 4, j = lane & 15;
+  const int tt = g >> 1, which = g & 1;
+  const int t = t0 + tt;
+  const bool ok = t < T;
+  const int tc = min(t, T - 1);
+
+  // this lane's row: the first head's 16 bytes are loaded before the lookups
+  const u16* xb = which ? idx_k + (int64_t)tc * sk_t : idx_q + (int64_t)tc * sq_t;
+  const int64_t x_sh = which ? sk_h : sq_h;
+  u32x4 raw = *reinterpret_cast<const u32x4*>(xb + 8 * j);
+  const int cu_lane = (S < 64 && lane <= S) ? cu[lane] : 0x7fffffff;
+  const u16* wp = (which ? w_k : w_q) + 8 * j;
+  float w1[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w1[e] = 1.0f + bf2f(wp[e]);
+
+  // RoPE angles of the two tokens (lane: token lane / 32, pair lane % 32)
+  {
+    const int ta = min(t0 + (lane >> 5), T - 1);
+    const int sa = seq_of(cu, S, cu_lane, min(t0, T - 1));
+    const int sb = seq_of(cu, S, cu_lane, min(t0 + 1, T - 1));
+    const int cs0 = S < 64 ? __builtin_amdgcn_readlane(cu_lane, sa) : cu[sa];
+    const int cs1 = S < 64 ? __builtin_amdgcn_readlane(cu_lane, sb) : cu[sb];
+    const int pos = ta - (lane < 32 ? cs0 : cs1);
+    double sn, cs;
+    sincos((double)pos * rope_freq_of(fr, lane & 31), &sn, &cs);
+    ang[wave][lane >> 5][0][lane & 31] = (float)cs;
+    ang[wave][lane >> 5][1][lane & 31] = (float)sn;
+  }
+  __syncthreads();
+  float c[8], sf[8];
+  {
+    const int f0 = 8 * (j & 3);
+    const f32x4 c0 = *reinterpret_cast<const f32x4*>(&ang[wave][tt][0][f0]);
+    const f32x4 c1 = *reinterpret_cast<const f32x4*>(&ang[wave][tt][0][f0 + 4]);
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(&ang[wave][tt][1][f0]);
+    const f32x4 s1 = *reinterpret_cast<const f32x4*>(&ang[wave][tt][1][f0 + 4]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c[e] = c0[e];
+      c[e + 4] = c1[e];
+      sf[e] = s0[e];
+      sf[e + 4] = s1[e];
+    }
+  }
+
   for (int h = 0; h < Hk; ++h) {
-    float x[kProTok][2][2];
+    if (h > 0) raw = *reinterpret_cast<const u32x4*>(xb + (int64_t)h * x_sh + 8 * j);
+    float x[8];
 #pragma unroll
-    for (int tt = 0; tt < kProTok; ++tt) {
-      const int t = min(t0 + tt, T - 1);
-      const u16* xq = idx_q + (int64_t)t * sq_t + (int64_t)h * sq_h;
-      const u16* xk = idx_k + (int64_t)t * sk_t + (int64_t)h * sk_h;
-      x[tt][0][0] = bf2f(xq[d0]);
-      x[tt][0][1] = bf2f(xq[d1]);
-      x[tt][1][0] = bf2f(xk[d0]);
-      x[tt][1][1] = bf2f(xk[d1]);
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(raw[e] << 16);
+      x[2 * e + 1] = __uint_as_float(raw[e] & 0xFFFF0000u);
     }
-    if (h == 0) {
+    // sum of squares in a fixed order: partial e (e = 0..7) adds the squares
+    // of dims e, e + 8, ..., e + 120 one after another, carried along the
+    // row's lanes (lane m adds dim 8m + e, after lane m - 1); lane 15 then
+    // combines the eight partials as ((0+1)+(2+3))+((4+5)+(6+7)), and the
+    // row's lanes take its sum
+    float part[8];
 #pragma unroll
-      for (int rr = 0; rr < kProTok / 2; ++rr) {
-        const int t = min(t0 + 2 * rr + (lane >> 5), T - 1);
-        const int s = find_seq(cu, S, t);
-        double sn, cs;
-        sincos((double)(t - cu[s]) * rope_freq_of(fr, lane & 31), &sn, &cs);
-        c[2 * rr] = (float)cs;
-        sf[2 * rr] = (float)sn;
-        c[2 * rr + 1] = __shfl_xor(c[2 * rr], 32);
-        sf[2 * rr + 1] = __shfl_xor(sf[2 * rr], 32);
-      }
+    for (int e = 0; e < 8; ++e) part[e] = x[e] * x[e];
+    const float sq0[8] = {part[0], part[1], part[2], part[3], part[4], part[5], part[6], part[7]};
+#pragma unroll 1
+    for (int m = 1; m < 16; ++m) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[e] = dpp_shr1(part[e]) + sq0[e];
     }
+    float ss = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+    ss = row_lane15(ss);
+    const float ms = ss * (1.0f / 128.0f);
+    const float r = 1.0f / sqrtf(ms + eps);
+    float y[8];
 #pragma unroll
-    for (int tt = 0; tt < kProTok; ++tt) {
-      if (t0 + tt >= T) break;
+    for (int e = 0; e < 8; ++e) y[e] = (x[e] * r) * w1[e];
+    uint32_t o[4];
 #pragma unroll
-      for (int which = 0; which < 2; ++which) {
-        u16* out = (which ? kfeat : qfeat) + ((int64_t)(t0 + tt) * Hk + h) * kHeadDim;
-        const float x0 = x[tt][which][0];
-        const float x1 = x[tt][which][1];
-        float ss = x0 * x0 + x1 * x1;
-        for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
-        const float ms = ss * (1.0f / 128.0f);
-        const float r = 1.0f / sqrtf(ms + eps);
-        float y0 = (x0 * r) * (which ? wk0 : wq0);
-        float y1 = (x1 * r) * (which ? wk1 : wq1);
-        if (lane < 32) {
-          const float o0 = (y0 * c[tt]) - (y1 * sf[tt]);
-          const float o1 = (y1 * c[tt]) + (y0 * sf[tt]);
-          y0 = o0;
-          y1 = o1;
-        }
-        out[d0] = f2bf(y0);
-        out[d1] = f2bf(y1);
+    for (int e = 0; e < 8; e += 2) {
+      float v[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float yp = swz_xor<4>(y[e + u]);  // the rotation partner (dims 8(j^4) + e + u)
+        const float lo = (y[e + u] * c[e + u]) - (yp * sf[e + u]);
+        const float hi = (y[e + u] * c[e + u]) + (yp * sf[e + u]);
+        v[u] = j < 4 ? lo : (j < 8 ? hi : y[e + u]);
       }
+      o[e / 2] = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+    }
+    if (ok) {
+      u16* out = (which ? kfeat : qfeat) + ((int64_t)t * Hk + h) * kHeadDim + 8 * j;
+      *reinterpret_cast<u32x4*>(out) = u32x4{o[0], o[1], o[2], o[3]};
     }
   }
 }
@@ -347,12 +410,14 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restric
   if (r0 >= nrows) return;
   int b[kTopRows];
   float pre[kTopRows];
+  const int cu_lane = (S < 64 && lane <= S) ? cu[lane] : 0x7fffffff;
 #pragma unroll
   for (int e = 0; e < kTopRows; ++e) {
     const int64_t row = min(r0 + e, nrows - 1);
     const int t = (int)(row / Hk);
-    const int s = find_seq(cu, S, t);
-    b[e] = __builtin_amdgcn_readfirstlane((t - cu[s]) / kBlock);
+    const int s = seq_of(cu, S, cu_lane, t);
+    const int cs = S < 64 ? __builtin_amdgcn_readlane(cu_lane, s) : cu[s];
+    b[e] = __builtin_amdgcn_readfirstlane((t - cs) / kBlock);
     pre[e] = -INFINITY;
     if (b[e] >= kTopk && b[e] <= 64 && lane < b[e] && lane < nbmax) pre[e] = scores[row * nbmax + lane];
   }
@@ -371,7 +436,7 @@ void launch_select(const Sizes& z, const u16* idx_q, int64_t sq_t, int64_t sq_h,
   const int T = (int)z.T, Hk = (int)z.Hk, S = (int)z.S;
   {
     KernelTimer timer("select_prologue", st);
-    const int64_t waves = (z.T + kProTok - 1) / kProTok;
+    const int64_t waves = (z.T + 1) / 2;
     select_prologue_kernel<<<dim3((unsigned)((waves + kProWaves - 1) / kProWaves + 1)), 64 * kProWaves, 0, st>>>(
         idx_q, sq_t, sq_h, idx_k, sk_t, sk_h, w_q, w_k, eps, rope_freqs(rope_base), cu, S, T, Hk, (int)z.chunk, p,
         qfeat, kfeat);

@@ -71,3 +71,44 @@ def test_force_init_attention(gpu_lib):
     check_grad("force_init attn", "dQ", f32(dq), dQw)
     check_grad("force_init attn", "dK", f32(dk), dKw)
     check_grad("force_init attn", "dV", f32(dv), dVw)
+
+
+def _select_workspace_features(msa, p, ws):
+    """The q and k indexer features msa_index_select left in its workspace:
+    the plan tables (blkbase [S+1], blk_seq [block bound], seqitem [S+1],
+    totals [4], tile order [ceil(T/16)] int32), then q and k features
+    [T, Hk, 128] bf16, each region starting on a 256-byte boundary."""
+    T, Hk, _ = p.idx_q.shape
+    S = p.cu_seqlens.numel() - 1
+    up = lambda x: (x + 255) // 256 * 256
+    off = 0
+    for n in (S + 1, min((T + 127 * S) // 128, T), S + 1, 4, (T + 15) // 16):
+        off = up(off + 4 * n)
+    raw = ws.cpu().numpy()
+    nbytes = T * Hk * 128 * 2
+    qf = raw[off:off + nbytes].view(np.uint16).reshape(T, Hk, 128)
+    kf = raw[up(off + nbytes):up(off + nbytes) + nbytes].view(np.uint16).reshape(T, Hk, 128)
+    return qf, kf
+
+
+@pytest.mark.parametrize("lengths,hk,seed", [([2600, 700, 2300], 1, 55), ([3000, 1100], 4, 56)])
+def test_select_features_bitwise(gpu_lib, lengths, hk, seed):
+    """The selection's q / k features (norm, RoPE, one bf16 rounding) equal the
+    oracle's bit for bit: the norm's sum of squares runs in the oracle's fp32
+    order, so the two only meet fp32 rounding differences in the scores."""
+    msa = gpu_lib
+    p = synth.make_custom_pack(lengths, num_q_heads=16 * hk, num_kv_heads=hk, seed=seed)
+    T = p.idx_q.shape[0]
+    need = msa.msa_workspace_size(msa.make_dims(T, len(lengths), p.max_seqlen, 16 * hk, hk), msa.MSA_OP_SELECT)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    msa.msa_index_select(dev(p.idx_q), dev(p.idx_k), dev(p.w_q), dev(p.w_k), dev(p.cu_seqlens), p.max_seqlen,
+                         workspace=ws)
+    torch.cuda.synchronize()
+    gq, gk = _select_workspace_features(msa, p, ws)
+    _, pos = O.sequence_layout(p.cu_seqlens.numpy())
+    bits = lambda a: (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    for h in range(hk):
+        wq = O.indexer_features(f32(p.idx_q)[:, h], f32(p.w_q), pos, 1e-6, 1e7, 64)
+        wk = O.indexer_features(f32(p.idx_k)[:, h], f32(p.w_k), pos, 1e-6, 1e7, 64)
+        assert np.array_equal(gq[:, h], bits(wq)), int((gq[:, h] != bits(wq)).sum())
+        assert np.array_equal(gk[:, h], bits(wk)), int((gk[:, h] != bits(wk)).sum())
