@@ -51,6 +51,25 @@ def test_rmsnorm_closed_forms():
     np.testing.assert_allclose(O.gemma_rmsnorm(x, w, eps), O.gemma_rmsnorm(x, w0, eps) * (1 + w), rtol=1e-6)
 
 
+def test_indexer_features_norm_before_rope_closed_form():
+    """The indexer's features are the norm first, then the rotation.  With x
+    = e_0, 1 + w = 2 on dim 0 and 1 on dim 32, and angle theta on pair 0: norm
+    first gives dim 32 = 2 r sin(theta) (r = 1 / sqrt(1/128 + eps)); rotating
+    first would give r sin(theta) there, since the weight of dim 32 then
+    scales the rotated component."""
+    eps = 1e-6
+    x = np.zeros((1, 128), np.float32)
+    x[0, 0] = 1.0
+    w = np.zeros(128, np.float32)
+    w[0] = 1.0
+    p = 3
+    y = O.indexer_features(x, w, np.array([p]), eps, 1e7, 64, round_bf16=False).astype(np.float64)[0]
+    r = 1.0 / math.sqrt(1.0 / 128.0 + eps)
+    np.testing.assert_allclose(y[0], 2 * r * math.cos(p), rtol=1e-6)
+    np.testing.assert_allclose(y[32], 2 * r * math.sin(p), rtol=1e-6)
+    assert np.count_nonzero(y) == 2
+
+
 # ---------------------------------------------------------------- RoPE
 def test_rope_identity_at_position_zero_and_passthrough():
     y = RNG.standard_normal((5, 128)).astype(np.float32)
