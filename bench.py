@@ -570,6 +570,15 @@ def main():
         if dom_exec is not None:
             roofline["executed_flop_per_launch"] = int(dom_exec)
             roofline["executed_tflops"] = round(dom_exec / (dom_ms * 1e-3) / 1e12, 2)
+        if dom == "attn_bwd_dkdv":
+            # what the pass must move once: q and dO of every (token, q head), K and V, the per-row
+            # -LSE log2(e) and Delta ([T][Hk][16] fp32) and the block lists in; dK and dV (bf16) out,
+            # and with the stored dS its bf16 dS, 2 B per (query head, selected causal key)
+            alg = (2 * T * Hq * D * 2 + 2 * T * Hk * D * 2 + 3 * T * Hk * 16 * 4 + 2 * T * Hk * D * 2
+                   + (2 * per_qhead if stored_ds else 0))
+            roofline["algorithmic_bytes_per_launch"] = int(alg)
+            if traffic is not None:
+                roofline["traffic_over_algorithmic"] = round(traffic / alg, 2)
     per_kernel = {}
     for name, fpk in FLOP_PER_KEY.items():
         if name in kt:
