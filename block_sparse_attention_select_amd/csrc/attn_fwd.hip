@@ -27,6 +27,16 @@ namespace msa {
 
 namespace {
 
+// Forward tiles: kTPW tokens per wavefront (see the forward kernel below).
+template <int kTPW>
+struct FwdTile {
+  static constexpr int kWaves = kTPW == 1 ? 16 : 8;
+  static constexpr int kTok = kWaves * kTPW;        // tokens per tile
+  static constexpr int kRuns = 64 / kWaves;         // K and V^T runs staged per wavefront
+  static constexpr int kAhead = kTPW == 1 ? 8 : 4;  // operand reads ahead of the MFMAs (register budget)
+  static constexpr int kMaxUnion = kTok * kTopk;
+};
+
 // Per-(global block, KV head) copies of K and V in the forward's staging
 // order, so that every staged 1 KB run is one contiguous copy (a run of raw K
 // rows would be sixteen 64-byte pieces).  Keys past the sequence end are zero.
@@ -40,8 +50,9 @@ template <bool kNorm>
 __global__ __launch_bounds__(256) void block_prep_kernel(const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
                                                          const u16* __restrict__ x, int64_t st_t, int64_t st_h,
                                                          const int32_t* __restrict__ cu, int S, int chunk,
-                                                         int ntiles, PlanBufs plan, int Hk, QkNormParams nrm,
-                                                         u16* __restrict__ kop, u16* __restrict__ xt) {
+                                                         int ntiles, int tile_tok, PlanBufs plan, int Hk,
+                                                         QkNormParams nrm, u16* __restrict__ kop,
+                                                         u16* __restrict__ xt) {
   // workgroup part p (of 4): K runs 8p .. 8p+7 (key tiles 2p, 2p+1) and the
   // V^T runs of dims 32p .. 32p+31 (runs 8p .. 8p+7).  The last workgroup of
   // the grid instead writes the plan (block numbering, tile launch order) for
@@ -56,7 +67,11 @@ __global__ __launch_bounds__(256) void block_prep_kernel(const u16* __restrict__
     if (h == 0 && part == 0) {
       __shared__ int sb[256], si[256], hist[kOrderBins], scu[kCuCache];
       plan_blocks<256, kBlock>(cu, S, chunk, plan.blkbase, plan.blk_seq, plan.seqitem, plan.totals, sb, si);
-      plan_tile_order<256, 16>(cu, S, ntiles, plan.tile_order, sb, hist, scu);
+      // the order of the forward's tiles: tile_tok tokens each (ntiles of them)
+      if (tile_tok == FwdTile<4>::kTok)
+        plan_tile_order<256, 16, FwdTile<4>::kTok>(cu, S, ntiles, plan.tile_order, sb, hist, scu);
+      else
+        plan_tile_order<256, 16, FwdTile<1>::kTok>(cu, S, ntiles, plan.tile_order, sb, hist, scu);
     }
     return;
   }
@@ -136,42 +151,47 @@ __global__ __launch_bounds__(256) void block_prep_kernel(const u16* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Forward.  One workgroup of 16 wavefronts per (tile of 16 consecutive tokens,
-// KV head); wavefront w owns token w of the tile (its q as MFMA B operands, its
-// O accumulators and softmax state, all in registers).  One token per
-// wavefront keeps a wavefront within 128 registers, so four of them share a
-// SIMD and hide each other's MFMA -> softmax -> MFMA dependency chains.
+// Forward.  One workgroup per (tile of consecutive tokens, KV head); each
+// wavefront owns kTPW tokens of the tile (their q as MFMA B operands, their O
+// accumulators and softmax state, all in registers).
+//   * kTPW = 1: 16 wavefronts, 16-token tiles.  One token per wavefront keeps
+//     a wavefront within 128 registers, so four of them share a SIMD and hide
+//     each other's MFMA -> softmax -> MFMA dependency chains.
+//   * kTPW = 4: 8 wavefronts of 4 tokens (two per SIMD, 256 registers),
+//     32-token tiles.  For long sequences a 16-token tile's union is close to
+//     every causal block while each staged block serves few of its tokens
+//     (2.5 on the unsharded 32k layer), so the walk is paced by per-step costs;
+//     the wider tile walks about 40 % fewer blocks per token there.
 //   1. The union of the tile's selected blocks is built in LDS (a bitmap over
 //      the tile's global block range, compacted in ascending order).
 //   2. The workgroup walks that union.  Each block's K (A operand of
 //      S^T = K Q^T) and V^T (A operand of O^T = V^T P^T) are copied into one of
 //      two LDS buffers while the previous block is being used; every wavefront
-//      then updates its token if that token selected the block.  K and V are
-//      read from HBM/L2 once per tile instead of once per token.
+//      then updates its tokens that selected the block.  K and V are read from
+//      HBM/L2 once per tile instead of once per token.
+// Each token meets its blocks in ascending order with either tile, so the
+// results do not depend on the tile.
 // ---------------------------------------------------------------------------
-constexpr int kTileTok = kAttnTile;
-constexpr int kTokPerWave = 1;
-constexpr int kFwdWaves = kTileTok / kTokPerWave;
-constexpr int kRunsPerWave = 64 / kFwdWaves;  // K and V^T runs staged per wavefront
 constexpr float kRescaleSlack = 8.f;  // log2 units
 constexpr int kUnionWords = 34;  // a tile's blocks span fewer than 34 * 32 global ids
-constexpr int kMaxUnion = kTileTok * kTopk;
 
-// kDense: every causal key of the token's sequence (the dense layers), blk_idx unused.
-// kNorm: q is raw; the token's heads get the attention-side norm and RoPE
-// (qk_rope.h) in registers before the walk.
-template <bool kDense, bool kNorm>
-__global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
+
+template <bool kDense, bool kNorm, int kTPW>
+__global__ __launch_bounds__(64 * FwdTile<kTPW>::kWaves) void attn_fwd_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh,
     const u16* __restrict__ kop, const u16* __restrict__ vt, const int32_t* __restrict__ blk_idx,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ blkbase, const int32_t* __restrict__ blk_seq,
     const int32_t* __restrict__ tile_order, int S, int T, int Hk, float scale_log2, QkNormParams nrm,
     u16* __restrict__ o, int64_t o_st, int64_t o_sh, float* __restrict__ lse) {
+  using Tile = FwdTile<kTPW>;
+  constexpr int kTokPerWave = kTPW;
+  constexpr int kFwdWaves = Tile::kWaves;
+  constexpr int kTileTok = Tile::kTok;
   __shared__ u32x4 kbuf[2][32][64];
   __shared__ u32x4 vbuf[2][32][64];
   __shared__ uint32_t bitmap[kUnionWords];
   // a dense tile's union is up to one sequence's 1024 blocks plus one per later sequence
-  constexpr int kUnionCap = kDense ? kUnionWords * 32 : kMaxUnion;
+  constexpr int kUnionCap = kDense ? kUnionWords * 32 : Tile::kMaxUnion;
   __shared__ int ulist[kUnionCap];
   __shared__ int nunion;
   __shared__ float qang[kNorm ? kFwdWaves : 1][64];
@@ -185,6 +205,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
   const int g = lane >> 4;
   const int li = lane & 15;
   static_assert(!kNorm || kTokPerWave == 1, "the norm assumes one token per wavefront");
+  static_assert(kTPW == 1 || kTPW == 4, "16- or 32-token tiles");
 
   // this lane's (token, slot): token kTokPerWave * wave + g % kTokPerWave, slot li
   const int tj = kTokPerWave * wave + g % kTokPerWave;
@@ -272,21 +293,23 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
     l_run[j] = 0.f;
   }
 
-  // 2. walk the union, staging block u+1 while block u is used.  Waves 0-7
-  // copy K runs 4w .. 4w+3 (keys score_key(w, .), dims 32 ii ..), waves 8-15
-  // V^T runs 4(w-8) .. +3; each copy is a scalar base plus a lane offset.
-  static_assert(kFwdWaves == 16 && kRunsPerWave == 4, "staging assumes 16 wavefronts");
+  // 2. walk the union, staging block u+1 while block u is used.  The first
+  // half of the wavefronts copies the K runs (kRuns each: keys score_key(w, .),
+  // dims 32 ii ..), the second half the V^T runs; each copy is a scalar base
+  // plus a lane offset.
   auto stage = [&](int u, int buf) {
     const int gb = __builtin_amdgcn_readfirstlane(ulist[u]);
     const int ln = fresh_lane();
-    if (wave < 8) {
-      const u16* base = kop + (((int64_t)gb * Hk + h) * 32 + 4 * wave) * 512;
+    constexpr int kHalf = kFwdWaves / 2, kR = Tile::kRuns;
+    if (wave < kHalf) {
+      const u16* base = kop + (((int64_t)gb * Hk + h) * 32 + kR * wave) * 512;
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) dma16s(base + 512 * ii, 16 * ln, lds_offset(&kbuf[buf][4 * wave + ii][0]));
+      for (int ii = 0; ii < kR; ++ii) dma16s(base + 512 * ii, 16 * ln, lds_offset(&kbuf[buf][kR * wave + ii][0]));
     } else {
-      const u16* base = vt + (((int64_t)gb * Hk + h) * 32 + 4 * (wave - 8)) * 512;
+      const u16* base = vt + (((int64_t)gb * Hk + h) * 32 + kR * (wave - kHalf)) * 512;
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) dma16s(base + 512 * ii, 16 * ln, lds_offset(&vbuf[buf][4 * (wave - 8) + ii][0]));
+      for (int ii = 0; ii < kR; ++ii)
+        dma16s(base + 512 * ii, 16 * ln, lds_offset(&vbuf[buf][kR * (wave - kHalf) + ii][0]));
     }
   };
   if (nu > 0) stage(0, 0);
@@ -319,7 +342,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
         if (diag && kBlock * c + 64 * hf > tok_pos[j]) break;
         // S^T for the half's four key tiles: the four accumulation chains are
         // interleaved (consecutive MFMAs independent) and the K operand reads
-        // run eight ahead of the MFMAs that consume them.  The MFMA blocks run
+        // run kAhead ahead of the MFMAs that consume them.  The MFMA blocks run
         // at raised wave priority, so on a SIMD whose other wavefronts are in
         // their softmax the matrix unit is fed first (16k pack: 3 % faster)
         f32x4 st[4];
@@ -333,13 +356,13 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
             ka[i] = __builtin_bit_cast(bf16x8, kbuf[buf][(4 * hf + (i & 3)) * 4 + (i >> 2)][lane]);
 #pragma unroll
           for (int i = 0; i < 16; ++i) st[i & 3] = mfma16x16x32(ka[i], qb[j][i >> 2], st[i & 3]);
-          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, Tile::kAhead, 0);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
+          for (int i = 0; i < 16 - Tile::kAhead; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, Tile::kAhead, 0);
         }
         __builtin_amdgcn_s_setprio(0);
         float mx = -INFINITY;
@@ -380,7 +403,7 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
         const bf16x8 pf0 = pack_bf16x8(st[0], st[1]);
         const bf16x8 pf1 = pack_bf16x8(st[2], st[3]);
         // O^T += V^T P^T: eight independent accumulators per sweep, V operand
-        // reads eight ahead
+        // reads kAhead ahead
         {
           __builtin_amdgcn_s_setprio(1);
           bf16x8 va[16];
@@ -389,13 +412,13 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
             va[i] = __builtin_bit_cast(bf16x8, vbuf[buf][(i & 7) * 4 + 2 * hf + (i >> 3)][lane]);
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[j][i & 7] = mfma16x16x32(va[i], i < 8 ? pf0 : pf1, oacc[j][i & 7]);
-          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, Tile::kAhead, 0);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
+          for (int i = 0; i < 16 - Tile::kAhead; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, Tile::kAhead, 0);
         }
         __builtin_amdgcn_s_setprio(0);
       }
@@ -420,15 +443,20 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(
 
 }  // namespace
 
+int fwd_tokens_per_wave(const Sizes& z, bool dense, bool nrm) {
+  return (!dense && !nrm && z.max_seqlen >= kWideFwdSeqlen) ? 4 : 1;
+}
+
 void launch_block_prep(const Sizes& z, const u16* k, int64_t k_st, int64_t k_sh, const u16* v, int64_t v_st,
-                       int64_t v_sh, const int32_t* cu, const PlanBufs& p, const QkNormParams* nrm, u16* kop,
-                       u16* vt, hipStream_t st) {
+                       int64_t v_sh, const int32_t* cu, const PlanBufs& p, const QkNormParams* nrm, bool dense,
+                       u16* kop, u16* vt, hipStream_t st) {
   KernelTimer timer("block_prep", st);
   const QkNormParams none{};
   auto kern = nrm ? block_prep_kernel<true> : block_prep_kernel<false>;
+  const int tile = fwd_tokens_per_wave(z, dense, nrm != nullptr) == 4 ? FwdTile<4>::kTok : FwdTile<1>::kTok;
   kern<<<dim3((unsigned)(z.nblk_cap + 1), (unsigned)z.Hk, 4), 256, 0, st>>>(
-      k, k_st, k_sh, v, v_st, v_sh, cu, (int)z.S, (int)z.chunk, (int)z.ntiles, p, (int)z.Hk, nrm ? *nrm : none, kop,
-      vt);
+      k, k_st, k_sh, v, v_st, v_sh, cu, (int)z.S, (int)z.chunk, (int)((z.T + tile - 1) / tile), tile, p, (int)z.Hk,
+      nrm ? *nrm : none, kop, vt);
 }
 
 void launch_attn_fwd(const Sizes& z, const u16* q, int64_t q_st, int64_t q_sh,
@@ -437,9 +465,13 @@ void launch_attn_fwd(const Sizes& z, const u16* q, int64_t q_st, int64_t q_sh,
                      hipStream_t st) {
   KernelTimer timer("attn_fwd", st);
   const QkNormParams none{};
-  auto kern = dense ? (nrm ? attn_fwd_kernel<true, true> : attn_fwd_kernel<true, false>)
-                    : (nrm ? attn_fwd_kernel<false, true> : attn_fwd_kernel<false, false>);
-  kern<<<(unsigned)(z.ntiles * z.Hk), 64 * kFwdWaves, 0, st>>>(
+  const bool wide = fwd_tokens_per_wave(z, dense, nrm != nullptr) == 4;
+  auto kern = wide ? attn_fwd_kernel<false, false, 4>
+                   : (dense ? (nrm ? attn_fwd_kernel<true, true, 1> : attn_fwd_kernel<true, false, 1>)
+                            : (nrm ? attn_fwd_kernel<false, true, 1> : attn_fwd_kernel<false, false, 1>));
+  const int tile = wide ? FwdTile<4>::kTok : FwdTile<1>::kTok;
+  const int waves = wide ? FwdTile<4>::kWaves : FwdTile<1>::kWaves;
+  kern<<<(unsigned)(((z.T + tile - 1) / tile) * z.Hk), 64 * waves, 0, st>>>(
       q, q_st, q_sh, kop, vt, blk_idx, cu, p.blkbase, p.blk_seq, p.tile_order, (int)z.S, (int)z.T,
       (int)z.Hk, scale * kLog2e, nrm ? *nrm : none, o, o_st, o_sh, lse);
 }

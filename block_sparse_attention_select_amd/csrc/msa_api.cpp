@@ -449,7 +449,7 @@ int msa_attn_fwd_ex(const msa_dims* dims, const void* q, int64_t q_st, int64_t q
   Carver c(workspace);
   FwdWs w = carve_fwd(c, z);
   msa::launch_block_prep(z, (const u16*)k, k_st, k_sh, (const u16*)v, v_st, v_sh, cu_seqlens, w.plan, nullptr,
-                         w.kop, w.vt, stream);
+                         dense, w.kop, w.vt, stream);
   msa::launch_attn_fwd(z, (const u16*)q, q_st, q_sh, w.kop, w.vt, dense ? nullptr : blk_idx,
                        cu_seqlens, w.plan, softmax_scale, (u16*)o, o_st, o_sh, lse, dense, nullptr, stream);
   return launch_status();
@@ -524,8 +524,8 @@ int msa_attn_fwd_qknorm(const msa_dims* dims, const void* q, int64_t q_st, int64
   Carver c(workspace);
   FwdWs w = carve_fwd(c, z);
   const msa::QkNormParams nrm{(const u16*)w_q, (const u16*)w_k, eps, msa::rope_freqs(rope_base)};
-  msa::launch_block_prep(z, (const u16*)k, k_st, k_sh, (const u16*)v, v_st, v_sh, cu_seqlens, w.plan, &nrm, w.kop,
-                         w.vt, stream);
+  msa::launch_block_prep(z, (const u16*)k, k_st, k_sh, (const u16*)v, v_st, v_sh, cu_seqlens, w.plan, &nrm, dense,
+                         w.kop, w.vt, stream);
   msa::launch_attn_fwd(z, (const u16*)q, q_st, q_sh, w.kop, w.vt, dense ? nullptr : blk_idx, cu_seqlens, w.plan,
                        softmax_scale, (u16*)o, o_st, o_sh, lse, dense, &nrm, stream);
   return launch_status();

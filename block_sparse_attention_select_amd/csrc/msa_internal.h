@@ -215,8 +215,14 @@ void launch_select(const Sizes& z, const u16* idx_q, int64_t sq_t, int64_t sq_h,
 // nrm: the attention-side norm fused into the prep (K) and forward (q)
 // kernels, or nullptr for already normalized q and k.
 void launch_block_prep(const Sizes& z, const u16* k, int64_t k_st, int64_t k_sh, const u16* v, int64_t v_st,
-                       int64_t v_sh, const int32_t* cu, const PlanBufs& p, const QkNormParams* nrm, u16* kop,
-                       u16* vt, hipStream_t st);
+                       int64_t v_sh, const int32_t* cu, const PlanBufs& p, const QkNormParams* nrm, bool dense,
+                       u16* kop, u16* vt, hipStream_t st);
+
+// The forward's tile: 32 tokens (4 per wavefront) for sparse layers without
+// the fused norm whose longest sequence is at least kWideFwdSeqlen tokens,
+// else 16 (1 per wavefront).  launch_block_prep orders the tiles for it.
+constexpr int64_t kWideFwdSeqlen = 12288;
+int fwd_tokens_per_wave(const Sizes& z, bool dense, bool nrm);
 
 void launch_attn_fwd(const Sizes& z, const u16* q, int64_t q_st, int64_t q_sh,
                      const u16* kop, const u16* vt,

@@ -20,7 +20,8 @@
 // the same queries.  seqitem[s] is the first item of sequence s; totals =
 // {blocks, items}.
 //
-// Token tiles (kAttnTile consecutive tokens of the pack) are put in launch
+// Token tiles (kAttnTile consecutive tokens of the pack, or the forward's
+// wider tiles) are put in launch
 // order by decreasing position of their first token within its sequence: a
 // later query has more causal blocks to choose from, so its tile's union of
 // selected blocks, and with it the tile's work, is larger.  Launching the
@@ -89,19 +90,20 @@ __device__ __forceinline__ void plan_blocks(const int32_t* __restrict__ cu, int 
 constexpr int kOrderBins = 1024;  // tile order keys: one per 128-token block (131072 tokens)
 constexpr int kCuCache = 4097;    // cu_seqlens entries held in LDS for the tile keys
 
-// Order key of token tile i: block of its first token within that token's sequence.
+// Order key of token tile i (kTile tokens a tile): block of its first token within that token's sequence.
+template <int kTile>
 __device__ __forceinline__ int tile_key(const int32_t* cu, int S, int i) {
-  const int t0 = i * kAttnTile;
+  const int t0 = i * kTile;
   const int s = find_seq(cu, S, t0);
   return min((t0 - cu[s]) / kBlock, kOrderBins - 1);
 }
 
-// Token tiles in launch order: a counting sort on tile_key, largest key first
+// Token tiles (kTile tokens each) in launch order: a counting sort on tile_key, largest key first
 // (a later query chooses among more blocks, so its tile's union, and work,
 // is larger; the order within a key is free).  Run by all kThreads threads of
 // one workgroup; sb: kThreads ints, hist: kOrderBins ints, scu: kCuCache ints
 // of LDS.  kKeys tile keys per thread stay in registers between the passes.
-template <int kThreads, int kKeys>
+template <int kThreads, int kKeys, int kTile = kAttnTile>
 __device__ __forceinline__ void plan_tile_order(const int32_t* __restrict__ cu, int S, int ntiles,
                                                 int32_t* __restrict__ tile_order, int* sb, int* hist, int* scu) {
   static_assert(kOrderBins % kThreads == 0, "whole bins per thread");
@@ -117,10 +119,10 @@ __device__ __forceinline__ void plan_tile_order(const int32_t* __restrict__ cu, 
 #pragma unroll
   for (int e = 0; e < kKeys; ++e) {
     const int i = tid + e * kThreads;
-    keys[e] = i < ntiles ? tile_key(cus, S, i) : 0;
+    keys[e] = i < ntiles ? tile_key<kTile>(cus, S, i) : 0;
     if (i < ntiles) atomicAdd(&hist[keys[e]], 1);
   }
-  for (int i = tid + kKeys * kThreads; i < ntiles; i += kThreads) atomicAdd(&hist[tile_key(cus, S, i)], 1);
+  for (int i = tid + kKeys * kThreads; i < ntiles; i += kThreads) atomicAdd(&hist[tile_key<kTile>(cus, S, i)], 1);
   __syncthreads();
   // thread tid owns scan slots kBins tid .. kBins tid + kBins - 1, slot j
   // holding key kOrderBins - 1 - j (largest key first)
@@ -151,7 +153,7 @@ __device__ __forceinline__ void plan_tile_order(const int32_t* __restrict__ cu, 
     if (i < ntiles) tile_order[atomicAdd(&hist[keys[e]], 1)] = i;
   }
   for (int i = tid + kKeys * kThreads; i < ntiles; i += kThreads)
-    tile_order[atomicAdd(&hist[tile_key(cus, S, i)], 1)] = i;
+    tile_order[atomicAdd(&hist[tile_key<kTile>(cus, S, i)], 1)] = i;
 }
 
 // Sequence and block index of global block gb (kUnit-token blocks), without
