@@ -15,9 +15,10 @@
 //   2. Each of the 4 wavefronts keeps 32 keys of K and V as MFMA B operands
 //      and the 32 x 128 fp32 dK and dV sums in registers for the whole item.
 //   3. Selecting tokens stream through LDS two at a time through a ring of
-//      four slots: global_load_lds copies of the next three pairs are in
+//      four slots: global_load_lds copies of the next two pairs are in
 //      flight while one pair is used (the gathered rows come from HBM, whose
-//      latency one pair of work does not cover).  Per token the stage holds q
+//      latency one pair of work does not cover), with a barrier after every
+//      second pair.  Per token the stage holds q
 //      and dO laid out so each MFMA A operand is one contiguous 1 KB read, plus
 //      the token's 16 LSE and Delta values.
 //   4. Two tokens (32 query rows) per MFMA step: S = q K^T and dP = dO V^T
@@ -41,7 +42,7 @@ namespace msa {
 namespace {
 
 constexpr int kBatch = 2;  // tokens per staging round
-constexpr int kNBuf = 4;   // staging ring: rounds bi+1 .. bi+3 in flight while bi is used
+constexpr int kNBuf = 4;   // staging ring: rounds bi+1, bi+2 in flight while bi is used
 
 // Stage layout of one token (u32x4 units): [0,256) q and [256,512) dO as
 // [ds][slot], operand lane li + 16g of run ds (row li, dims 32ds + 8g .. +7)
@@ -200,14 +201,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                  lds_offset(&stage[buf][slot][0]), lds_offset(&stats[buf][slot][0]), q, q_st, q_sh, dO, do_st,
                  do_sh, nlse, delta);
     };
-    for (int r = 0; r < kNBuf - 1 && r < nbatch; ++r) stage_round(r, r);
+    // round bi + 2 is copied while round bi is used, into the slot of round
+    // bi - 2; a barrier follows only every second round (16k pack 444 ->
+    // 435 us): there every wavefront has waited for all its copies, rounds
+    // bi + 1 and bi + 2 included, and the slot a round refills was released by
+    // the barrier after round bi - 2 or bi - 1, whichever is odd
+    for (int r = 0; r < kNBuf - 2 && r < nbatch; ++r) stage_round(r, r);
     wait_copies();
     wait_all_loads();
     __syncthreads();
     for (int bi = 0; bi < nbatch; ++bi) {
       const int cur = bi % kNBuf;
-      const bool ahead = bi + kNBuf - 1 < nbatch;
-      if (ahead) stage_round(bi + kNBuf - 1, (bi + kNBuf - 1) % kNBuf);
+      const bool ahead = bi + kNBuf - 2 < nbatch;
+      if (ahead) stage_round(bi + kNBuf - 2, (bi + kNBuf - 2) % kNBuf);
 #pragma unroll 1
       for (int pp = 0; pp < kBatch / 2; ++pp) {
         const int n0 = bi * kBatch + 2 * pp;
@@ -315,17 +321,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           }
         }
       }
-      // round bi+1 must have landed: with rounds bi+2, bi+3 still in flight a
-      // wavefront may keep 2 rounds of its copies (6 or 4 instructions each)
-      if (ahead) {
-        if (wave < 2)
-          asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      } else {
+      if ((bi & 1) || bi + 1 == nbatch) {
         wait_copies();
+        lds_barrier();
       }
-      lds_barrier();
     }
   }
 
