@@ -299,101 +299,85 @@ __global__ __launch_bounds__(256) void select_scores_kernel(
 // 3. Top-k.  A wavefront ranks one (token, head) row at a time.  The
 // candidates are blocks 0 .. b-1 (b = own block), or 1 .. b-1 when block 0 is
 // forced in (then 14 are chosen instead of 15); order: score descending, id
-// ascending.
-//   * b <= 64: lane c holds candidate c; its rank is the number of candidates
-//     ordered before it, counted against each candidate in turn (broadcast
-//     from its lane).  The 15 of rank < 15 are written in id order (ballot
-//     prefix), then the own block.
-//   * b > 64: 15 rounds of a wavefront-wide arg-max over the candidates, each
-//     lane scanning its up to 16 (only as far as b reaches), then the 16 ids
-//     are ranked to ascending order.
+// ascending, a NaN score after every number.  Lane l holds candidates
+// l + 64 j as 32-bit keys that order like the scores (the float's bits made
+// order-preserving as an unsigned integer, -0 as +0, NaN just below -inf; 0
+// for a non-candidate).  The 15th largest key is found bit by bit, from the
+// top: a bit is kept when at least 15 candidates' keys reach the value so far
+// with that bit set (ballot counts, no cross-lane data movement).  Chosen are
+// the keys above it, then, lowest ids first, as many of the keys equal to it
+// as are still missing; they are written in id order (ballot prefix counts),
+// then the own block.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
+__device__ __forceinline__ uint32_t order_key(float x) {
+  if (x != x) return 0x007FFFFEu;  // NaN: below -inf (0x007FFFFF)
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  u = u == 0x80000000u ? 0u : u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // row: the (token, head) row's scores; b: the token's own block; pre: this
-// lane's score of candidate `lane` when b <= 64 (loaded by the caller)
+// lane's score of candidate `lane` (loaded by the caller when b >= kTopk)
 __device__ __forceinline__ void topk_row(const float* __restrict__ row, int b, float pre, int lane, int nbmax,
                                          int force_init, int32_t* __restrict__ out) {
   if (b < kTopk) {
     if (lane < kTopk) out[lane] = lane <= b ? lane : -1;
     return;
   }
-  const int first = force_init ? 1 : 0;   // first candidate block
-  const int npick = kTopk - 1 - first;     // blocks chosen by score
-  auto load = [&](int c) {
-    float x = -INFINITY;
-    if (c < b && c < nbmax) {
-      x = row[c];
-      if (x != x) x = -INFINITY;  // NaN ranks last
-    }
-    return x;
-  };
-  if (b <= 64) {
-    // one 64-bit key per candidate, larger = ordered first: the score's bits
-    // made order-preserving as an unsigned integer (NaN as -inf, -0 as +0),
-    // then the complemented id (lower id first among equal scores)
-    uint32_t u = __builtin_bit_cast(uint32_t, pre != pre ? -INFINITY : pre);
-    u = u == 0x80000000u ? 0u : u;
-    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    const uint32_t klo = ~(uint32_t)lane;
-    const uint64_t key = ((uint64_t)ord << 32) | klo;
-    int rank = 0;
-#pragma unroll 4
-    for (int j = first; j < b; ++j) {
-      const uint64_t kj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ord, j) << 32) |
-                          (uint32_t)__builtin_amdgcn_readlane((int)klo, j);
-      rank += kj > key ? 1 : 0;
-    }
-    const bool chosen = lane >= first && lane < b && rank < npick;
-    const uint64_t m = __ballot(chosen);
-    if (chosen) out[first + __popcll(m & ((1ull << lane) - 1ull))] = lane;
-    if (lane == 0) {
-      if (first) out[0] = 0;
-      out[kTopk - 1] = b;
-    }
-    return;
-  }
+  const int first = force_init ? 1 : 0;  // first candidate block
+  const int npick = kTopk - 1 - first;    // blocks chosen by score
+  const int nplanes = (b + 63) / 64;
   constexpr int kPer = kMaxBlocks / 64;
-  float v[kPer];
+  uint32_t key[kPer];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) v[j] = 64 * j < b ? load(lane + 64 * j) : -INFINITY;
-  unsigned taken = (first && lane == 0) ? 1u : 0u;  // a forced block 0 is not a candidate
-  int mine = -1;
-  for (int k = 0; k < npick; ++k) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+  for (int j = 0; j < kPer; ++j) {
+    key[j] = 0u;
+    if (j < nplanes) {
+      const int c = lane + 64 * j;
+      if (c >= first && c < b) key[j] = order_key(j == 0 ? pre : (c < nbmax ? row[c] : -INFINITY));
+    }
+  }
+  // every candidate's key is >= 0x007FFFFE and there are >= npick of them
+  uint32_t thr = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    int cnt = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      if (64 * j >= b) break;
-      const int c = lane + 64 * j;
-      if (c < b && !((taken >> j) & 1u) && better(v[j], c, bv, bi)) {
-        bv = v[j];
-        bi = c;
-      }
+      if (j >= nplanes) break;
+      cnt += __popcll(__ballot(key[j] >= cand));
     }
+    if (cnt >= npick) thr = cand;
+  }
+  int above = 0;
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(bv, m);
-      const int oi = __shfl_xor(bi, m);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
+  for (int j = 0; j < kPer; ++j) {
+    if (j >= nplanes) break;
+    above += __popcll(__ballot(key[j] > thr));
+  }
+  int rem = npick - above;  // keys equal to thr still to take, lowest ids first
+  int base = first;
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (j >= nplanes) break;
+    const uint64_t eq = __ballot(key[j] == thr);
+    uint64_t take = eq;
+    const int k = __popcll(eq);
+    if (rem < k) {
+      uint64_t rest = eq;
+      for (int i = 0; i < rem; ++i) rest &= rest - 1ull;
+      take = eq ^ rest;
     }
-    if (lane == (bi & 63)) taken |= 1u << (bi >> 6);
-    if (lane == k) mine = bi;
+    rem = rem < k ? 0 : rem - k;
+    const uint64_t ch = __ballot(key[j] > thr) | take;
+    if ((ch >> lane) & 1ull) out[base + __popcll(ch & below)] = lane + 64 * j;
+    base += __popcll(ch);
   }
-  if (first && lane == npick) mine = 0;
-  if (lane == kTopk - 1) mine = b;
-  int rank = 0;
-#pragma unroll
-  for (int j = 0; j < kTopk; ++j) {
-    const int o = __shfl(mine, j);
-    rank += o < mine ? 1 : 0;
+  if (lane == 0) {
+    if (first) out[0] = 0;
+    out[kTopk - 1] = b;
   }
-  if (lane < kTopk) out[rank] = mine;
 }
 
 // One wavefront per kTopRows consecutive (token, head) rows; the scores of
@@ -419,7 +403,7 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restric
     const int cs = S < 64 ? __builtin_amdgcn_readlane(cu_lane, s) : cu[s];
     b[e] = __builtin_amdgcn_readfirstlane((t - cs) / kBlock);
     pre[e] = -INFINITY;
-    if (b[e] >= kTopk && b[e] <= 64 && lane < b[e] && lane < nbmax) pre[e] = scores[row * nbmax + lane];
+    if (b[e] >= kTopk && lane < b[e] && lane < nbmax) pre[e] = scores[row * nbmax + lane];
   }
 #pragma unroll
   for (int e = 0; e < kTopRows; ++e)
