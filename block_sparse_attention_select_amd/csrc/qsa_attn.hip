@@ -43,7 +43,9 @@ constexpr int kD = kQsaHeadDim;   // 256
 constexpr int kG = kQsaGroup;     // 12
 constexpr int kKT = kQsaKeyTile;  // 64
 constexpr int kWords = kQsaWords; // 256
-constexpr int kTok = 8;           // tokens (wavefronts) per forward / dQ workgroup
+constexpr int kTok = 8;           // tokens (wavefronts) per dQ workgroup
+constexpr int kQTok = kAttnTile;  // tokens per forward workgroup (16)
+constexpr int kRowWaves = kQTok * kG / 16;  // forward wavefronts: the tile's 192 (token, head) rows, 16 each
 constexpr int kUnionWords = 32;   // a tile's key tiles span fewer than 1024 global ids
 constexpr int kUnionMax = kUnionWords * 32;
 constexpr float kRescaleSlack = 8.f;  // log2 units
@@ -220,69 +222,136 @@ __device__ __forceinline__ void build_union(TileUnion& tu, const uint32_t* __res
   __syncthreads();
 }
 
+// The same prologue for a tile of kN tokens walked by kWaves wavefronts that
+// do not each own a token: wavefront w reads the bitmap rows of tokens w,
+// w + kWaves, ..., and each token's sequence position (-1 past the end of the
+// pack) and its sequence's first global key tile are kept beside the rows.
+template <int kN>
+struct TileUnionRows {
+  uint32_t bmap[kN][kWords];
+  uint32_t ubits[kUnionWords];
+  int ulist[kUnionMax];
+  int tpos[kN];
+  int tktb[kN];
+  int nunion;
+};
+
+template <int kN, int kWaves>
+__device__ __forceinline__ void build_union_rows(TileUnionRows<kN>& tu, const uint32_t* __restrict__ bits,
+                                                 const int32_t* __restrict__ cu, const int32_t* __restrict__ ktbase,
+                                                 int S, int T, int Hk, int h, int t0, int wave, int lane) {
+  const int gk_lo = ktbase[find_seq(cu, S, t0)];
+  if (threadIdx.x < kUnionWords) tu.ubits[threadIdx.x] = 0u;
+  __syncthreads();
+  for (int j = wave; j < kN; j += kWaves) {
+    const int t = t0 + j;
+    const bool ok = t < T;
+    int pos = -1, ktb = 0;
+    if (ok) {
+      const int s = find_seq(cu, S, t);
+      pos = t - cu[s];
+      ktb = ktbase[s];
+    }
+    if (lane == 0) {
+      tu.tpos[j] = pos;
+      tu.tktb[j] = ktb;
+    }
+    const uint32_t* brow = bits + ((int64_t)(ok ? t : 0) * Hk + h) * kWords;
+    const int nw = ok ? (pos / kQsaBlock) / 32 + 1 : 0;
+    for (int w = lane; w < kWords; w += 64) {
+      const uint32_t x = w < nw ? brow[w] : 0u;
+      tu.bmap[j][w] = x;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        if ((x >> (16 * hh)) & 0xFFFFu) {
+          const int rel = ktb + 2 * w + hh - gk_lo;
+          atomicOr(&tu.ubits[rel >> 5], 1u << (rel & 31));
+        }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t x = lane < kUnionWords ? tu.ubits[lane] : 0u;
+    const int cnt = __popc(x);
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    int pos = incl - cnt;
+    while (x) {
+      const int bit = __ffs(x) - 1;
+      tu.ulist[pos++] = gk_lo + 32 * lane + bit;
+      x &= x - 1u;
+    }
+    if (lane == 63) tu.nunion = incl;
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // Forward.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64 * kTok) void qsa_fwd_kernel(
+__global__ __launch_bounds__(64 * kRowWaves) void qsa_fwd_kernel(
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh, const u16* __restrict__ kop,
     const u16* __restrict__ vt, const uint32_t* __restrict__ bits, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ ktbase, const int32_t* __restrict__ kt_seq, const int32_t* __restrict__ tile_order,
-    int S, int T, int Hk, float scale_log2, u16* __restrict__ o, int64_t o_st, int64_t o_sh,
-    float* __restrict__ lse) {
+    const int32_t* __restrict__ ktbase, const int32_t* __restrict__ tile_order, int S, int T, int Hk,
+    float scale_log2, u16* __restrict__ o, int64_t o_st, int64_t o_sh, float* __restrict__ lse) {
   // K runs kt * 8 + ds: keys score_key(kt, .) of the tile, dims 32 ds ..;
   // V^T runs 2 dt + kc as laid out by qsa_vt_kernel
   __shared__ u32x4 kbuf[2][32][64];
   __shared__ u32x4 vbuf[2][32][64];
-  __shared__ TileUnion tu;
+  __shared__ TileUnionRows<kQTok> tu;
 
-  // workgroup b: KV head b % Hk, second or first half of the 16-token tile in
-  // launch slot b / (2 Hk)
+  // workgroup b: KV head b % Hk, 16-token tile in launch slot b / Hk
   const int h = blockIdx.x % Hk;
-  const int t0 = tile_order[blockIdx.x / (2 * Hk)] * kAttnTile + kTok * ((blockIdx.x / Hk) & 1);
+  const int t0 = tile_order[blockIdx.x / Hk] * kAttnTile;
   if (t0 >= T) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int li = lane & 15;
-  const int t = t0 + wave;
+  // this lane's MFMA column: row 16 wave + li of the tile, head hd of token tk
+  const int row = 16 * wave + li;
+  const int tk = row / kG;
+  const int hd = row - kG * tk;
+  const int t = t0 + tk;
   const bool tok_ok = t < T;
-  int s_t = 0, pos_t = 0;
-  if (tok_ok) {
-    s_t = find_seq(cu, S, t);
-    pos_t = t - cu[s_t];
-  }
-  s_t = __builtin_amdgcn_readfirstlane(s_t);
-  pos_t = __builtin_amdgcn_readfirstlane(pos_t);
-  const int ktb_t = tok_ok ? ktbase[s_t] : 0;
-  const int own_c = pos_t / kKT;
 
-  // q of this token as B operands (heads past 12 zero), loaded before the
-  // union build so the loads overlap it; O^T accumulators
+  // q of this row as B operands, loaded before the union build so the loads
+  // overlap it; O^T accumulators
   bf16x8 qb[8];
   {
-    const bool hv = tok_ok && li < kG;
-    const u16* qrow = q + (int64_t)(tok_ok ? t : 0) * q_st + (int64_t)(h * kG + min(li, kG - 1)) * q_sh + 8 * g;
+    const u16* qrow = q + (int64_t)(tok_ok ? t : 0) * q_st + (int64_t)(h * kG + hd) * q_sh + 8 * g;
 #pragma unroll
-    for (int ds = 0; ds < 8; ++ds) qb[ds] = hv ? load_bf16x8(qrow + 32 * ds) : zero_bf16x8();
+    for (int ds = 0; ds < 8; ++ds) qb[ds] = tok_ok ? load_bf16x8(qrow + 32 * ds) : zero_bf16x8();
   }
-  build_union(tu, bits, cu, ktbase, kt_seq, S, Hk, h, t0, wave, lane, tok_ok, t, pos_t, ktb_t);
+  build_union_rows<kQTok, kRowWaves>(tu, bits, cu, ktbase, S, T, Hk, h, t0, wave, lane);
   const int nu = tu.nunion;
+  const int pos_t = tu.tpos[tk];
+  const int ktb_t = tu.tktb[tk];
+  const int own_c = tok_ok ? pos_t / kKT : -1;
   f32x4 oacc[16];
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // staging of union step u: wavefront w copies K runs 4w .. 4w+3 (key tile
-  // w / 2, dims 128 (w % 2) + 32 ii ..) and V^T runs 4w .. 4w+3
+  // staging of union step u: the tile's 32 K runs and 32 V^T runs, run
+  // wave + 12 ii copied by wavefront `wave`
   auto stage = [&](int u, int buf) {
     const int gk = __builtin_amdgcn_readfirstlane(tu.ulist[u]);
     const int ln = fresh_lane();
-    const u16* kbase = kop + (((int64_t)gk * Hk + h) * 32 + 4 * wave) * 512;
+    const u16* kbase = kop + ((int64_t)gk * Hk + h) * 32 * 512;
+    const u16* vbase = vt + ((int64_t)gk * Hk + h) * 32 * 512;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) dma16s(kbase + 512 * ii, 16 * ln, lds_offset(&kbuf[buf][4 * wave + ii][0]));
-    const u16* vbase = vt + (((int64_t)gk * Hk + h) * 32 + 4 * wave) * 512;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) dma16s(vbase + 512 * ii, 16 * ln, lds_offset(&vbuf[buf][4 * wave + ii][0]));
+    for (int ii = 0; ii < (64 + kRowWaves - 1) / kRowWaves; ++ii) {
+      const int r = wave + kRowWaves * ii;
+      if (r < 32)
+        dma16s(kbase + 512 * r, 16 * ln, lds_offset(&kbuf[buf][r][0]));
+      else if (r < 64)
+        dma16s(vbase + 512 * (r - 32), 16 * ln, lds_offset(&vbuf[buf][r - 32][0]));
+    }
   };
   if (nu > 0) stage(0, 0);
   wait_copies();
@@ -292,9 +361,11 @@ __global__ __launch_bounds__(64 * kTok) void qsa_fwd_kernel(
   for (int u = 0; u < nu; ++u) {
     const int buf = u & 1;
     if (u + 1 < nu) stage(u + 1, buf ^ 1);
-    const int c = tu.ulist[u] - ktb_t;  // key tile of this token's sequence (when in range)
-    const uint32_t m16 = (tok_ok && c >= 0 && c <= own_c) ? tile_mask(tu.bmap[wave], c) : 0u;
-    if (m16 != 0u) {
+    // key tile of this row's sequence (when in range) and the blocks the row's
+    // token lists in it; the wavefront works the tile when any of its rows does
+    const int c = tu.ulist[u] - ktb_t;
+    const uint32_t m16 = (c >= 0 && c <= own_c) ? tile_mask(tu.bmap[tk], c) : 0u;
+    if (__ballot(m16 != 0u)) {
       const bool own = (c == own_c);
       const int plim = pos_t - kKT * c;  // causal: tile keys at index <= plim
       // S^T for the tile's four 16-key tiles: four chains interleaved, K
@@ -336,18 +407,21 @@ __global__ __launch_bounds__(64 * kTok) void qsa_fwd_kernel(
         }
       }
       // online softmax in base 2 (scale folded into the exponent's FMA); the
-      // running max moves only when it grows by more than kRescaleSlack
+      // running max moves only when it grows by more than kRescaleSlack.  A
+      // row whose token lists nothing in this tile adds P = 0 (its max stays
+      // -inf until its token lists a key, hence the 0 in the exponent then)
       mx = max_over_groups(mx);
       const float m_cand = mx * scale_log2;
       const bool grow = m_cand > m_run + kRescaleSlack;
       const float m_use = grow ? m_cand : m_run;
       const float alpha = grow ? fast_exp2(m_run - m_cand) : 1.f;
+      const float m_sub = m_use > -INFINITY ? m_use : 0.f;
       float rs = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(fmaf(st[kt][r], scale_log2, -m_use));
+          const float p = fast_exp2(fmaf(st[kt][r], scale_log2, -m_sub));
           st[kt][r] = p;
           rs += p;
         }
@@ -383,13 +457,13 @@ __global__ __launch_bounds__(64 * kTok) void qsa_fwd_kernel(
 
   // l_run holds this lane's share of the row sum (its keys 8g.. of every 32)
   l_run = sum_over_groups(l_run);
-  if (tok_ok && li < kG) {
+  if (tok_ok) {
     const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-    u16* orow = o + (int64_t)t * o_st + (int64_t)(h * kG + li) * o_sh;
+    u16* orow = o + (int64_t)t * o_st + (int64_t)(h * kG + hd) * o_sh;
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = pack_bf16x4(oacc[dt] * inv);
     if (g == 0)
-      lse[(int64_t)t * (Hk * kG) + h * kG + li] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+      lse[(int64_t)t * (Hk * kG) + h * kG + hd] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
   }
 }
 
@@ -899,9 +973,9 @@ void launch_qsa_fwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStre
         a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.cu, p.blkbase, p.blk_seq, p.totals, (int)z.Hk, a.kop, nullptr);
   }
   KernelTimer timer("qsa_fwd", st);
-  qsa_fwd_kernel<<<(unsigned)(2 * z.ntiles * z.Hk), 64 * kTok, 0, st>>>(
-      a.q, a.q_st, a.q_sh, a.kop, a.vt, a.bits, a.cu, p.blkbase, p.blk_seq, p.tile_order, (int)z.S,
-      (int)z.T, (int)z.Hk, a.scale * kLog2e, a.out_o, a.oo_st, a.oo_sh, a.out_lse);
+  qsa_fwd_kernel<<<(unsigned)(z.ntiles * z.Hk), 64 * kRowWaves, 0, st>>>(
+      a.q, a.q_st, a.q_sh, a.kop, a.vt, a.bits, a.cu, p.blkbase, p.tile_order, (int)z.S, (int)z.T, (int)z.Hk,
+      a.scale * kLog2e, a.out_o, a.oo_st, a.oo_sh, a.out_lse);
 }
 
 void launch_qsa_bwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStream_t st) {
