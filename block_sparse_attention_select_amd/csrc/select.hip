@@ -172,31 +172,42 @@ __global__ __launch_bounds__(64 * kProWaves) void select_prologue_kernel(
 
 // ---------------------------------------------------------------------------
 // 2. Block scores.  One workgroup (4 wavefronts) per (query block, chunk of
-// kKeyChunk key blocks, head).  Wavefront w owns query rows 32w..32w+31 of the
+// key blocks, head).  Wavefront w owns query rows 32w..32w+31 of the
 // query block; their bf16 features stay in registers as MFMA B operands of
 // S^T = K Q^T, so a lane's accumulators are keys of one query and the block
 // maximum is a per-lane maximum plus one exchange across the four row groups.
 // Key blocks are copied into LDS in A-operand order with global_load_lds, the
 // next one while the current one is used; each K operand read feeds the
-// MFMAs of both 16-query tiles of the wavefront.
+// MFMAs of both 16-query tiles of the wavefront.  The chunk's maxima collect
+// in LDS and leave as one contiguous run per query row.  Chunks are 8 key
+// blocks, or 32 from 16k-token sequences on, where the fp32 score matrix
+// outgrows the L2s: a row's 32 maxima then fill whole 128-byte lines (with
+// 4-byte stores from eight separately scheduled workgroups per line, the
+// unsharded 32k layer wrote the 134 MB matrix as 709 MB).
 // ---------------------------------------------------------------------------
 constexpr int kKeyChunk = 8;
+constexpr int kMaxKeyChunk = 32;
+constexpr int64_t kLongKeyChunkSeqlen = 16384;
 
 __global__ __launch_bounds__(256) void select_scores_kernel(
     const u16* __restrict__ qfeat, const u16* __restrict__ kfeat, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ blkbase, const int32_t* __restrict__ blk_seq,
-    const int32_t* __restrict__ totals, int Hk, int nbmax, float* __restrict__ scores) {
+    const int32_t* __restrict__ totals, int Hk, int nbmax, int key_chunk, float* __restrict__ scores) {
   // run kt * 4 + ds, lane li + 16 g: key 16 kt + li, dims 32 ds + 8 g .. +7
   __shared__ u32x4 kst[2][32][64];
+  // the workgroup's block maxima, [query][key block of the chunk], written out
+  // as contiguous row segments once the chunk is done (64 + 16 KB of LDS: two
+  // workgroups per CU)
+  __shared__ float smax[kBlock * kMaxKeyChunk];
   const int gb = blockIdx.x;
   const int kc = blockIdx.y;
   const int h = blockIdx.z;
   if (gb >= totals[0]) return;
   const int s = blk_seq[gb];
   const int qb = gb - blkbase[s];
-  const int c0 = kc * kKeyChunk;
+  const int c0 = kc * key_chunk;
   if (c0 > qb) return;
-  const int c1 = min(min(c0 + kKeyChunk, qb + 1), nbmax);  // nbmax bound holds when lengths <= max_seqlen
+  const int c1 = min(min(c0 + key_chunk, qb + 1), nbmax);  // nbmax bound holds when lengths <= max_seqlen
   const int seq0 = cu[s];
   const int L = cu[s + 1] - seq0;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -282,16 +293,19 @@ __global__ __launch_bounds__(256) void select_scores_kernel(
     }
     m0 = max_over_groups(m0);
     m1 = max_over_groups(m1);
-    // the wait counts stores too: the scores are stored after it, so the
-    // next block's wait finds them long completed instead of waiting out
-    // their write latency
+    if (g == 0) {
+      smax[(32 * wave + li) * key_chunk + c - c0] = m0;
+      smax[(32 * wave + 16 + li) * key_chunk + c - c0] = m1;
+    }
     wait_copies();
     lds_barrier();
-    if (g == 0) {
-      const int qp = kBlock * qb + 32 * wave + li;
-      if (qp < L) scores[((int64_t)(seq0 + qp) * Hk + h) * nbmax + c] = m0;
-      if (qp + 16 < L) scores[((int64_t)(seq0 + qp + 16) * Hk + h) * nbmax + c] = m1;
-    }
+  }
+  // rows of the query block past the sequence end are not stored
+  const int n = c1 - c0;
+  const int rows = min(kBlock, L - kBlock * qb);
+  for (int i = threadIdx.x; i < rows * n; i += 256) {
+    const int r = i / n, j = i - r * n;
+    scores[((int64_t)(seq0 + kBlock * qb + r) * Hk + h) * nbmax + c0 + j] = smax[r * key_chunk + j];
   }
 }
 
@@ -304,16 +318,80 @@ __global__ __launch_bounds__(256) void select_scores_kernel(
 // order-preserving as an unsigned integer, -0 as +0, NaN just below -inf; 0
 // for a non-candidate).  The 15th largest key is found bit by bit, from the
 // top: a bit is kept when at least 15 candidates' keys reach the value so far
-// with that bit set (ballot counts, no cross-lane data movement).  Chosen are
-// the keys above it, then, lowest ids first, as many of the keys equal to it
-// as are still missing; they are written in id order (ballot prefix counts),
-// then the own block.
+// with that bit set (ballot counts, no cross-lane data movement), and the
+// search ends early once exactly 15 do.  Chosen are the keys above it, then,
+// lowest ids first, as many of the keys equal to it as are still missing;
+// they are written in id order (ballot prefix counts), then the own block.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t order_key(float x) {
   if (x != x) return 0x007FFFFEu;  // NaN: below -inf (0x007FFFFF)
   uint32_t u = __builtin_bit_cast(uint32_t, x);
   u = u == 0x80000000u ? 0u : u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// The threshold search and the writes for a row with at most 64 kP
+// candidates (its keys in registers, kP planes of 64).  The search stops as
+// soon as exactly npick keys reach the value built so far: those are the
+// chosen ones.  Otherwise it ends on the npick-th largest key itself, and ties
+// with it are taken lowest ids first.
+template <int kP>
+__device__ __forceinline__ void topk_planes(const float* __restrict__ row, int b, float pre, int lane, int nbmax,
+                                            int first, int npick, int32_t* __restrict__ out) {
+  uint32_t key[kP];
+#pragma unroll
+  for (int j = 0; j < kP; ++j) {
+    const int c = lane + 64 * j;
+    key[j] = 0u;
+    if (c >= first && c < b) key[j] = order_key(j == 0 ? pre : (c < nbmax ? row[c] : -INFINITY));
+  }
+  // every candidate's key is >= 0x007FFFFE and there are more than npick of them
+  uint32_t thr = 0u;
+  bool exact = false;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kP; ++j) cnt += __popcll(__ballot(key[j] >= cand));
+    if (cnt >= npick) {
+      thr = cand;
+      if (cnt == npick) {
+        exact = true;
+        break;
+      }
+    }
+  }
+  int rem = 0;  // keys equal to thr still to take, lowest ids first
+  if (!exact) {
+    int above = 0;
+#pragma unroll
+    for (int j = 0; j < kP; ++j) above += __popcll(__ballot(key[j] > thr));
+    rem = npick - above;
+  }
+  int base = first;
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int j = 0; j < kP; ++j) {
+    uint64_t ch = __ballot(exact ? key[j] >= thr : key[j] > thr);
+    if (rem > 0) {
+      const uint64_t eq = __ballot(key[j] == thr);
+      const int k = __popcll(eq);
+      uint64_t take = eq;
+      if (rem < k) {
+        uint64_t rest = eq;
+        for (int i = 0; i < rem; ++i) rest &= rest - 1ull;
+        take = eq ^ rest;
+      }
+      rem = rem < k ? 0 : rem - k;
+      ch |= take;
+    }
+    if ((ch >> lane) & 1ull) out[base + __popcll(ch & below)] = lane + 64 * j;
+    base += __popcll(ch);
+  }
+  if (lane == 0) {
+    if (first) out[0] = 0;
+    out[kTopk - 1] = b;
+  }
 }
 
 // row: the (token, head) row's scores; b: the token's own block; pre: this
@@ -326,58 +404,17 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, int b, f
   }
   const int first = force_init ? 1 : 0;  // first candidate block
   const int npick = kTopk - 1 - first;    // blocks chosen by score
-  const int nplanes = (b + 63) / 64;
-  constexpr int kPer = kMaxBlocks / 64;
-  uint32_t key[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    key[j] = 0u;
-    if (j < nplanes) {
-      const int c = lane + 64 * j;
-      if (c >= first && c < b) key[j] = order_key(j == 0 ? pre : (c < nbmax ? row[c] : -INFINITY));
-    }
-  }
-  // every candidate's key is >= 0x007FFFFE and there are >= npick of them
-  uint32_t thr = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = thr | (1u << bit);
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      if (j >= nplanes) break;
-      cnt += __popcll(__ballot(key[j] >= cand));
-    }
-    if (cnt >= npick) thr = cand;
-  }
-  int above = 0;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    if (j >= nplanes) break;
-    above += __popcll(__ballot(key[j] > thr));
-  }
-  int rem = npick - above;  // keys equal to thr still to take, lowest ids first
-  int base = first;
-  const uint64_t below = (1ull << lane) - 1ull;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    if (j >= nplanes) break;
-    const uint64_t eq = __ballot(key[j] == thr);
-    uint64_t take = eq;
-    const int k = __popcll(eq);
-    if (rem < k) {
-      uint64_t rest = eq;
-      for (int i = 0; i < rem; ++i) rest &= rest - 1ull;
-      take = eq ^ rest;
-    }
-    rem = rem < k ? 0 : rem - k;
-    const uint64_t ch = __ballot(key[j] > thr) | take;
-    if ((ch >> lane) & 1ull) out[base + __popcll(ch & below)] = lane + 64 * j;
-    base += __popcll(ch);
-  }
-  if (lane == 0) {
-    if (first) out[0] = 0;
-    out[kTopk - 1] = b;
-  }
+  static_assert(kMaxBlocks <= 64 * 16, "top-k planes");
+  if (b <= 64)
+    topk_planes<1>(row, b, pre, lane, nbmax, first, npick, out);
+  else if (b <= 128)
+    topk_planes<2>(row, b, pre, lane, nbmax, first, npick, out);
+  else if (b <= 256)
+    topk_planes<4>(row, b, pre, lane, nbmax, first, npick, out);
+  else if (b <= 512)
+    topk_planes<8>(row, b, pre, lane, nbmax, first, npick, out);
+  else
+    topk_planes<16>(row, b, pre, lane, nbmax, first, npick, out);
 }
 
 // One wavefront per kTopRows consecutive (token, head) rows; the scores of
@@ -425,11 +462,12 @@ void launch_select(const Sizes& z, const u16* idx_q, int64_t sq_t, int64_t sq_h,
         idx_q, sq_t, sq_h, idx_k, sk_t, sk_h, w_q, w_k, eps, rope_freqs(rope_base), cu, S, T, Hk, (int)z.chunk, p,
         qfeat, kfeat);
   }
-  const unsigned kchunks = (unsigned)((z.nbmax + kKeyChunk - 1) / kKeyChunk);
+  const int key_chunk = z.max_seqlen >= kLongKeyChunkSeqlen ? kMaxKeyChunk : kKeyChunk;
+  const unsigned kchunks = (unsigned)((z.nbmax + key_chunk - 1) / key_chunk);
   {
     KernelTimer timer("select_scores", st);
     select_scores_kernel<<<dim3((unsigned)z.nblk_cap, kchunks, (unsigned)Hk), 256, 0, st>>>(
-        qfeat, kfeat, cu, p.blkbase, p.blk_seq, p.totals, Hk, (int)z.nbmax, scores);
+        qfeat, kfeat, cu, p.blkbase, p.blk_seq, p.totals, Hk, (int)z.nbmax, key_chunk, scores);
   }
   const int64_t waves_top = (z.T * z.Hk + kTopRows - 1) / kTopRows;
   {
