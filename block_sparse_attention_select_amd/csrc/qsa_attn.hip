@@ -884,6 +884,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // Ordered sum of the chunk slices of one (key tile, 16 keys, KV head).
+constexpr int kRedBatch = 4;  // chunk slices in flight per reduce step
+
 __global__ __launch_bounds__(256) void qsa_reduce_kernel(
     const float* __restrict__ part_dk, const float* __restrict__ part_dv, const int32_t* __restrict__ item_count,
     const int32_t* __restrict__ seqitem, const int32_t* __restrict__ kt_seq, const int32_t* __restrict__ ktbase,
@@ -913,13 +915,13 @@ __global__ __launch_bounds__(256) void qsa_reduce_kernel(
   f32x4 adk[kGroups], adv[kGroups];
 #pragma unroll
   for (int u = 0; u < kGroups; ++u) adk[u] = adv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // two chunks at a time: their slices are loaded before either is added, then
-  // added in chunk order (chunks whose item no query listed wrote nothing)
-  for (int j0 = jmin; j0 < nch; j0 += 2) {
-    int cnt[2];
-    int64_t off[2];
+  // kRedBatch chunks at a time: their slices are loaded before any is added,
+  // then added in chunk order (chunks whose item no query listed wrote nothing)
+  for (int j0 = jmin; j0 < nch; j0 += kRedBatch) {
+    int cnt[kRedBatch];
+    int64_t off[kRedBatch];
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
+    for (int w = 0; w < kRedBatch; ++w) {
       const int j = min(j0 + w, nch - 1);
       const int it = item0 + m * (j * (j + 1) / 2) + c;
       const bool ok = j0 + w < nch && it < items_cap;
@@ -927,16 +929,16 @@ __global__ __launch_bounds__(256) void qsa_reduce_kernel(
       cnt[w] = ok ? item_count[(int64_t)h * items_cap + itc] : 0;
       off[w] = ((int64_t)h * items_cap + itc) * (kKT * kD);
     }
-    f32x4 pk[2][kGroups], pv[2][kGroups];
+    f32x4 pk[kRedBatch][kGroups], pv[kRedBatch][kGroups];
 #pragma unroll
-    for (int w = 0; w < 2; ++w)
+    for (int w = 0; w < kRedBatch; ++w)
 #pragma unroll
       for (int u = 0; u < kGroups; ++u) {
         pk[w][u] = *reinterpret_cast<const f32x4*>(part_dk + off[w] + eg[u]);
         pv[w][u] = *reinterpret_cast<const f32x4*>(part_dv + off[w] + eg[u]);
       }
 #pragma unroll
-    for (int w = 0; w < 2; ++w)
+    for (int w = 0; w < kRedBatch; ++w)
       if (cnt[w] != 0) {
 #pragma unroll
         for (int u = 0; u < kGroups; ++u) {
