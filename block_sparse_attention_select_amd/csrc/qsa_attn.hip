@@ -59,15 +59,16 @@ __device__ __forceinline__ uint32_t tile_mask(const uint32_t* row, int c) {
 // Selection bitmaps: one wavefront per (token, KV head); bit b of the row is
 // set when block b is listed and b <= the token's own block.
 // ---------------------------------------------------------------------------
-// The last workgroup of the grid writes the plan (64-key tile numbering, dK/dV
-// work items, token tile launch order) for the kernels that follow, so the
-// narrow passes need no plan launch of their own.
+// Workgroup (0, 0) writes the plan (64-key tile numbering, dK/dV work items,
+// token tile launch order) for the kernels that follow, so the narrow passes
+// need no plan launch of their own; dispatched first, it runs beside the
+// bitmap workgroups instead of after them.
 __global__ __launch_bounds__(256) void qsa_bitmap_kernel(const int32_t* __restrict__ blk_idx, int topk,
                                                          const int32_t* __restrict__ cu, int S, int T, int Hk,
                                                          int chunk, int ntiles, PlanBufs plan,
                                                          uint32_t* __restrict__ bits) {
   __shared__ uint32_t row[4][kWords];
-  if (blockIdx.x == gridDim.x - 1) {
+  if (blockIdx.x == 0) {
     if (blockIdx.y == 0) {
       __shared__ int sb[256], si[256], hist[kOrderBins], scu[kCuCache];
       plan_blocks<256, kKT>(cu, S, chunk, plan.blkbase, plan.blk_seq, plan.seqitem, plan.totals, sb, si);
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(256) void qsa_bitmap_kernel(const int32_t* __restri
     return;
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
+  const int t = (blockIdx.x - 1) * 4 + wave;
   const int h = blockIdx.y;
   for (int i = lane; i < kWords; i += 64) row[wave][i] = 0u;
   __syncthreads();

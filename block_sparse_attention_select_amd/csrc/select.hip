@@ -67,14 +67,16 @@ __global__ __launch_bounds__(64 * kProWaves) void select_prologue_kernel(
     u16* __restrict__ qfeat, u16* __restrict__ kfeat) {
 #pragma clang fp contract(off)
   __shared__ __align__(16) float ang[kProWaves][2][2][32];  // [wave][token][cos, sin][pair]
-  if (blockIdx.x == gridDim.x - 1) {
+  // workgroup 0 writes the plan, dispatched first so that it runs beside the
+  // feature workgroups instead of after them
+  if (blockIdx.x == 0) {
     __shared__ int sb[64 * kProWaves], si[64 * kProWaves];
     plan_blocks<64 * kProWaves, kBlock>(cu, S, chunk, plan.blkbase, plan.blk_seq, plan.seqitem, plan.totals, sb, si);
     return;
   }
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int t0 = (blockIdx.x * kProWaves + wave) * 2;  // may be past T: such a wavefront stores nothing
+  const int t0 = ((blockIdx.x - 1) * kProWaves + wave) * 2;  // may be past T: such a wavefront stores nothing
   const int g = lane >> 4, j = lane & 15;
   const int tt = g >> 1, which = g & 1;
   const int t = t0 + tt;
