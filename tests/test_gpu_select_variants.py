@@ -38,6 +38,11 @@ def test_force_init_planted_golden(gpu_lib):
     plain = gpu_lib.msa_index_select(*args).cpu().numpy()
     for t, ids, why in P["expected"]:
         assert list(plain[t, 0]) == ids, (t, why)
+    # every row: exact ties decided by the lower-id rule, as the oracle decides them
+    res = O.index_select(f32(P["idx_q"]), f32(P["idx_k"]), f32(P["w_q"]), f32(P["w_k"]), P["cu_seqlens"],
+                         force_init=True)
+    bad = np.nonzero((forced != res.blk_idx).any(axis=(1, 2)))[0]
+    assert bad.size == 0, f"{bad.size} rows differ from the oracle, first {bad[:8]}"
 
 
 @pytest.mark.parametrize("lengths,hk,seed", [([2600, 700, 2300], 1, 51), ([3000, 1100], 2, 52), ([9000], 1, 53)])
