@@ -64,7 +64,7 @@ int check_qsa_dims(const msa_dims* d) {
 // numbering) are `unit` tokens wide, with `dhead` dims per head.  The dK/dV
 // query chunk starts at `chunk0` tokens and doubles while the chunk slices
 // would exceed kPartialBudget.
-void size_blocks(Sizes& z, int64_t unit, int64_t dhead, int64_t chunk0) {
+void size_blocks(Sizes& z, int64_t unit, int64_t dhead, int64_t chunk0, int64_t chunk_max = msa::kDkdvChunkMax) {
   // sum_s ceil(L_s / unit) <= (T + (unit - 1) S) / unit, and <= T
   int64_t cap = (z.T + (unit - 1) * z.S) / unit;
   if (cap > z.T) cap = z.T;
@@ -82,7 +82,7 @@ void size_blocks(Sizes& z, int64_t unit, int64_t dhead, int64_t chunk0) {
     const int64_t b2 = z.T * z.max_seqlen / (2 * unit * chunk) + 3 * z.T / (2 * unit) + z.S * m + 1;
     const int64_t items = b1 < b2 ? b1 : b2;
     const int64_t bytes = items * z.Hk * unit * dhead * 4 * 2;
-    if (bytes <= kPartialBudget || chunk >= msa::kDkdvChunkMax) {
+    if (bytes <= kPartialBudget || chunk >= chunk_max) {
       z.chunk = chunk;
       z.items_cap = items;
       break;
@@ -99,10 +99,11 @@ Sizes sizes_of_qsa(const msa_dims* d) {
   z.Hk = d->num_kv_heads;
   z.max_seqlen = d->max_seqlen;
   z.nbmax = (z.max_seqlen + msa::kQsaKeyTile - 1) / msa::kQsaKeyTile;
+  z.topk = d->topk_blocks;
   // dK/dV query chunks of 256 tokens: on the 16k narrow pack (512 listed
   // blocks per query) 512-token chunks took the dK/dV pass 1.79 ms against
   // 1.59 ms, while the reduce grew from 52 to 103 us; 128 gained nothing more
-  size_blocks(z, msa::kQsaKeyTile, msa::kQsaHeadDim, 256);
+  size_blocks(z, msa::kQsaKeyTile, msa::kQsaHeadDim, 256, msa::kQsaChunkMax);
   return z;
 }
 
@@ -289,8 +290,9 @@ QsaFwdWs carve_qsa_fwd(Carver& c, const Sizes& z) {
 struct QsaBwdWs {
   PlanBufs plan;
   uint32_t* bits;
+  uint16_t* lpre;
   u16* kop;
-  u16* vop;
+  u16* ds;
   float* delta;
   float* nlse;
   int32_t* item_count;
@@ -301,8 +303,11 @@ QsaBwdWs carve_qsa_bwd(Carver& c, const Sizes& z) {
   QsaBwdWs w;
   w.plan = carve_plan(c, z);
   w.bits = c.take<uint32_t>(z.T * z.Hk * msa::kQsaWords);
+  w.lpre = c.take<uint16_t>(z.T * z.Hk * msa::kQsaWords);
   w.kop = c.take<u16>(z.nblk_cap * z.Hk * msa::kQsaKeyTile * msa::kQsaHeadDim);
-  w.vop = c.take<u16>(z.nblk_cap * z.Hk * msa::kQsaKeyTile * msa::kQsaHeadDim);
+  // one 4-key dS record per listed block of each (token, KV head, query head);
+  // the dQ pass copies 16 bytes from a record, so 16 bytes of tail padding
+  w.ds = c.take<u16>(z.T * z.Hk * z.topk * msa::kQsaGroup * msa::kQsaBlock + 8);
   w.delta = c.take<float>(z.T * z.Hk * 16);
   w.nlse = c.take<float>(z.T * z.Hk * 16);
   w.item_count = c.take<int32_t>(z.Hk * z.items_cap);
@@ -659,8 +664,9 @@ int msa_qsa_attn_bwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t 
   a.dk = (u16*)dk; a.dk_st = dk_st; a.dk_sh = dk_sh;
   a.dv = (u16*)dv; a.dv_st = dv_st; a.dv_sh = dv_sh;
   a.bits = w.bits;
+  a.lpre = w.lpre;
   a.kop = w.kop;
-  a.vop = w.vop;
+  a.ds = w.ds;
   a.delta = w.delta;
   a.nlse = w.nlse;
   a.item_count = w.item_count;

@@ -28,6 +28,7 @@ struct Sizes {
   int64_t chunk;      // query positions per dK/dV work item (a multiple of 128)
   int64_t items_cap;  // bound on the number of dK/dV work items per KV head
   int64_t ntiles;     // ceil(T / kAttnTile)
+  int64_t topk = 0;   // block ids per (token, KV head) (narrow variant)
 };
 
 struct PlanBufs {
@@ -321,6 +322,7 @@ constexpr int kQsaGroup = 12;
 constexpr int kQsaKeyTile = 64;
 constexpr int kQsaMaxSeqlen = 32768;
 constexpr int kQsaMaxTopk = 1024;
+constexpr int kQsaChunkMax = 1024;  // query positions per narrow dK/dV work item, at most
 constexpr int kQsaWords = kQsaMaxSeqlen / kQsaBlock / 32;  // bitmap words per (token, KV head)
 
 struct QsaArgs {
@@ -341,11 +343,12 @@ struct QsaArgs {
   u16* dv; int64_t dv_st, dv_sh;
   // workspace
   uint32_t* bits;     // [T][Hk][kQsaWords] selected-block bitmaps
+  uint16_t* lpre;     // [T][Hk][kQsaWords] listed blocks before each bitmap word (backward)
   u16* vt;            // [key tiles][Hk][32 runs][64 lanes][8] V^T in MFMA operand order (forward)
   u16* kop;           // the same shape: K in the forward's (or, backward, the dQ pass's swizzled) stage order
-  u16* vop;           // V in the dQ pass's swizzled stage order (backward)
-  float* delta;       // [T][Hk][16] (heads past 12 zero)
-  float* nlse;        // [T][Hk][16] -LSE * log2(e) (-inf for heads past 12 and empty rows)
+  u16* ds;            // [T][Hk][12][topk][4] bf16 dS per listed block, in the token's block order (backward)
+  float* delta;       // [T][Hk][16] (heads past 12 unused)
+  float* nlse;        // [T][Hk][16] -LSE * log2(e) (-inf for empty rows; heads past 12 unused)
   int32_t* item_count;  // [Hk][items_cap]
   float* part_dk;     // [Hk][items_cap][64][256]
   float* part_dv;

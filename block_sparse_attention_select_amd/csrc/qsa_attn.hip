@@ -17,21 +17,24 @@
 // walk key tiles and mask, per query, the blocks it did not list.  Selections
 // arrive as a per-(token, KV head) bitmap over the sequence's blocks
 // (qsa_bitmap_kernel), 16 bits per key tile.
-//   forward   one 8-wavefront workgroup per (8 consecutive tokens, KV head),
-//             wavefront w owning token w (q as MFMA B operands, O^T in
-//             registers); the workgroup walks the union of its tokens' key
-//             tiles with K and V^T staged in LDS, double buffered;
-//   dQ        the same walk with K and V staged; K^T operands are read
-//             transposed from the K stage; it also forms Delta = rowsum(dO*O)
-//             and -LSE * log2(e) per head for the dK/dV pass;
+//   forward   one 12-wavefront workgroup per (16 consecutive tokens, KV head):
+//             the tile's 192 (token, head) rows packed 16 per wavefront as the
+//             MFMA columns (q as B operands, O^T in registers), so no padding
+//             heads are computed; the workgroup walks the union of its tokens'
+//             key tiles with K and V^T staged in LDS, double buffered;
+//   Delta     Delta = rowsum(dO*O) and -LSE * log2(e) per (token, head);
 //   dK/dV     key-tile major: one workgroup per (sequence, query chunk, key
 //             tile), four wavefronts of 16 keys with K and V in registers,
 //             streaming the (selecting token, query head) rows of the chunk
 //             through LDS 32 at a time, so a step mixes tokens and carries no
 //             padding heads; chunk slices are summed in chunk order by
-//             qsa_reduce_kernel (fixed order, no atomics).
-// In the forward and dQ, query heads are padded from 12 to the MFMA's 16 with
-// zero q; padded outputs are never stored.
+//             qsa_reduce_kernel (fixed order, no atomics).  It also stores the
+//             bf16 dS of every listed block as a 4-key record per (token, KV
+//             head, query head), indexed by the block's rank in the token's
+//             ascending list;
+//   dQ        the forward's tiling and row packing over the stored dS: only K
+//             is staged (K^T read transposed), and dQ^T = K^T dS^T is one
+//             product per listed block instead of three.
 #include "attn_stage.h"
 #include "plan_blocks.h"
 
@@ -43,9 +46,9 @@ constexpr int kD = kQsaHeadDim;   // 256
 constexpr int kG = kQsaGroup;     // 12
 constexpr int kKT = kQsaKeyTile;  // 64
 constexpr int kWords = kQsaWords; // 256
-constexpr int kTok = 8;           // tokens (wavefronts) per dQ workgroup
-constexpr int kQTok = kAttnTile;  // tokens per forward workgroup (16)
-constexpr int kRowWaves = kQTok * kG / 16;  // forward wavefronts: the tile's 192 (token, head) rows, 16 each
+constexpr int kQTok = kAttnTile;  // tokens per forward / dQ workgroup (16)
+constexpr int kRowWaves = kQTok * kG / 16;  // their wavefronts: the tile's 192 (token, head) rows, 16 each
+constexpr int kDqTrAhead = 3;  // dQ: transposed K^T operands read ahead of their MFMAs
 constexpr int kUnionWords = 32;   // a tile's key tiles span fewer than 1024 global ids
 constexpr int kUnionMax = kUnionWords * 32;
 constexpr float kRescaleSlack = 8.f;  // log2 units
@@ -63,10 +66,13 @@ __device__ __forceinline__ uint32_t tile_mask(const uint32_t* row, int c) {
 // token tile launch order) for the kernels that follow, so the narrow passes
 // need no plan launch of their own; dispatched first, it runs beside the
 // bitmap workgroups instead of after them.
+// lpre (optional, the backward's): per word of the row, the number of listed
+// blocks in the words before it, so that a listed block's rank in the token's
+// ascending list (the index of its dS record) is one lookup and one popcount.
 __global__ __launch_bounds__(256) void qsa_bitmap_kernel(const int32_t* __restrict__ blk_idx, int topk,
                                                          const int32_t* __restrict__ cu, int S, int T, int Hk,
                                                          int chunk, int ntiles, PlanBufs plan,
-                                                         uint32_t* __restrict__ bits) {
+                                                         uint32_t* __restrict__ bits, uint16_t* __restrict__ lpre) {
   __shared__ uint32_t row[4][kWords];
   if (blockIdx.x == 0) {
     if (blockIdx.y == 0) {
@@ -94,6 +100,59 @@ __global__ __launch_bounds__(256) void qsa_bitmap_kernel(const int32_t* __restri
   if (t < T) {
     const u32x4 x = {row[wave][4 * lane], row[wave][4 * lane + 1], row[wave][4 * lane + 2], row[wave][4 * lane + 3]};
     *reinterpret_cast<u32x4*>(bits + ((int64_t)t * Hk + h) * kWords + 4 * lane) = x;
+    if (lpre != nullptr) {
+      const int c0 = __popc(x[0]), c1 = __popc(x[1]), c2 = __popc(x[2]), c3 = __popc(x[3]);
+      const int cnt = c0 + c1 + c2 + c3;
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      const int e0 = incl - cnt;
+      const uint2 pr = {(uint32_t)e0 | ((uint32_t)(e0 + c0) << 16),
+                        (uint32_t)(e0 + c0 + c1) | ((uint32_t)(e0 + c0 + c1 + c2) << 16)};
+      *reinterpret_cast<uint2*>(lpre + ((int64_t)t * Hk + h) * kWords + 4 * lane) = pr;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Delta = rowsum(dO * O) and -LSE * log2(e) per (token, query head), ahead of
+// the dK/dV pass: one wavefront per (token, KV head), 16 lanes per query head
+// (16 dims a lane), four heads at a time.  Layout [T][Hk][16], heads past 12
+// unused.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void qsa_delta_kernel(const u16* __restrict__ o, int64_t o_st, int64_t o_sh,
+                                                        const u16* __restrict__ dO, int64_t do_st, int64_t do_sh,
+                                                        const float* __restrict__ lse, int T, int Hk,
+                                                        float* __restrict__ delta, float* __restrict__ nlse) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  const int h = blockIdx.y;
+  if (t >= T) return;
+  const int hg = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int pass = 0; pass < kG / 4; ++pass) {
+    const int hh = 4 * pass + hg;
+    const int hq = h * kG + hh;
+    const u16* orow = o + (int64_t)t * o_st + (int64_t)hq * o_sh + 16 * l16;
+    const u16* drow = dO + (int64_t)t * do_st + (int64_t)hq * do_sh + 16 * l16;
+    const bf16x8 o0 = load_bf16x8(orow), o1 = load_bf16x8(orow + 8);
+    const bf16x8 d0 = load_bf16x8(drow), d1 = load_bf16x8(drow + 8);
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part = fmaf((float)d0[e], (float)o0[e], part);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part = fmaf((float)d1[e], (float)o1[e], part);
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) part += __shfl_xor(part, m);
+    if (l16 == 0) {
+      const int64_t slot = ((int64_t)t * Hk + h) * 16 + hh;
+      delta[slot] = part;
+      const float l2 = lse[(int64_t)t * (Hk * kG) + hq] * kLog2e;
+      nlse[slot] = l2 > -INFINITY ? -l2 : -INFINITY;
+    }
   }
 }
 
@@ -136,7 +195,7 @@ __global__ __launch_bounds__(256) void qsa_vt_kernel(const u16* __restrict__ v, 
 
 // ---------------------------------------------------------------------------
 // Copies of K (and V) per (key tile, KV head) in the stage order of the
-// forward (K, plain) or the dQ pass (K and V, swizzled), so every staged 1 KB
+// forward (K, plain) or the dQ pass (K, swizzled), so every staged 1 KB
 // run is one contiguous copy: run kt*8 + ds, slot l holding x[key
 // score_key(kt, r)][dims 32 ds + 8 (l / 16) .. +7] with r = l % 16 (plain) or
 // swz_slot(l) % 16 (swizzled); zero past the sequence end.  blockIdx.z: tensor
@@ -173,60 +232,13 @@ __global__ __launch_bounds__(256) void qsa_prep_kernel(const u16* __restrict__ k
 }
 
 // ---------------------------------------------------------------------------
-// Shared prologue of the token-major passes: the tile's 8 tokens' bitmap rows
-// into LDS and the ascending union of the global key tiles they touch.
+// Shared prologue of the token-major passes: the tile's kN tokens' bitmap rows
+// into LDS and the ascending union of the global key tiles they touch, walked
+// by kWaves wavefronts that do not each own a token: wavefront w reads the
+// bitmap rows of tokens w, w + kWaves, ..., and each token's sequence position
+// (-1 past the end of the pack) and its sequence's first global key tile are
+// kept beside the rows.
 // ---------------------------------------------------------------------------
-struct TileUnion {
-  uint32_t bmap[kTok][kWords];
-  uint32_t ubits[kUnionWords];
-  int ulist[kUnionMax];
-  int nunion;
-};
-
-__device__ __forceinline__ void build_union(TileUnion& tu, const uint32_t* __restrict__ bits,
-                                            const int32_t* __restrict__ cu, const int32_t* __restrict__ ktbase,
-                                            const int32_t* __restrict__ kt_seq, int S, int Hk, int h, int t0,
-                                            int wave, int lane, bool tok_ok, int t, int pos_t, int ktb_t) {
-  const int gk_lo = ktbase[find_seq(cu, S, t0)];
-  if (threadIdx.x < kUnionWords) tu.ubits[threadIdx.x] = 0u;
-  __syncthreads();
-  const uint32_t* brow = bits + ((int64_t)(tok_ok ? t : 0) * Hk + h) * kWords;
-  const int nw = tok_ok ? (pos_t / kQsaBlock) / 32 + 1 : 0;
-  for (int w = lane; w < kWords; w += 64) {
-    const uint32_t x = w < nw ? brow[w] : 0u;
-    tu.bmap[wave][w] = x;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-      if ((x >> (16 * hh)) & 0xFFFFu) {
-        const int rel = ktb_t + 2 * w + hh - gk_lo;
-        atomicOr(&tu.ubits[rel >> 5], 1u << (rel & 31));
-      }
-  }
-  __syncthreads();
-  if (wave == 0) {
-    uint32_t x = lane < kUnionWords ? tu.ubits[lane] : 0u;
-    const int cnt = __popc(x);
-    int incl = cnt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
-    int pos = incl - cnt;
-    while (x) {
-      const int bit = __ffs(x) - 1;
-      tu.ulist[pos++] = gk_lo + 32 * lane + bit;
-      x &= x - 1u;
-    }
-    if (lane == 63) tu.nunion = incl;
-  }
-  __syncthreads();
-}
-
-// The same prologue for a tile of kN tokens walked by kWaves wavefronts that
-// do not each own a token: wavefront w reads the bitmap rows of tokens w,
-// w + kWaves, ..., and each token's sequence position (-1 past the end of the
-// pack) and its sequence's first global key tile are kept beside the rows.
 template <int kN>
 struct TileUnionRows {
   uint32_t bmap[kN][kWords];
@@ -469,180 +481,142 @@ __global__ __launch_bounds__(64 * kRowWaves) void qsa_fwd_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dQ (and Delta, -LSE log2 e for the dK/dV pass).
+// dQ from the dS the dK/dV pass stored.  The forward's tiling: 12 wavefronts
+// per (16-token tile, KV head), lane column = row 16 wave + li of the tile
+// (head hd of token tk), so no padding heads are computed; only the 168
+// registers of three wavefronts per SIMD are needed (dQ^T accumulators 64).
+// The union of the tile's key tiles is walked with K staged (swizzled, from
+// the prep kernel's copy) and K^T read transposed; per 32-key half a lane's
+// dS^T operand is keys 8g .. 8g+7 of its row, i.e. two listed blocks' records
+// (zero for unlisted blocks).  A record's index is the block's rank in its
+// token's ascending list: the lane counts its token's listed blocks tile by
+// tile.  The records of step u + 1 are loaded during step u, after its
+// copies, and stay in flight across the step's wait (loads and copies
+// complete in issue order).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64 * kTok) void qsa_dq_kernel(
-    const u16* __restrict__ q, int64_t q_st, int64_t q_sh, const u16* __restrict__ kop,
-    const u16* __restrict__ vop, const u16* __restrict__ o, int64_t o_st, int64_t o_sh,
-    const u16* __restrict__ dO, int64_t do_st, int64_t do_sh, const float* __restrict__ lse,
-    const uint32_t* __restrict__ bits, const int32_t* __restrict__ cu, const int32_t* __restrict__ ktbase,
-    const int32_t* __restrict__ kt_seq, const int32_t* __restrict__ tile_order, int S, int T, int Hk,
-    float scale_log2, float scale, u16* __restrict__ dq, int64_t dq_st, int64_t dq_sh, float* __restrict__ delta,
-    float* __restrict__ nlse) {
-  // K and V runs kt * 8 + ds (keys score_key(kt, .), dims 32 ds ..), stored
+__global__ __launch_bounds__(64 * kRowWaves) void qsa_dq_ds_kernel(
+    const u16* __restrict__ kop, const u16* ds, const uint32_t* __restrict__ bits, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ ktbase, const int32_t* __restrict__ tile_order, int S, int T, int Hk, int topk,
+    float scale, u16* __restrict__ dq, int64_t dq_st, int64_t dq_sh) {
+  // K runs kt * 8 + ds (keys score_key(kt, .), dims 32 ds ..), stored
   // swizzled (swz_slot) for the transposed K^T reads
   __shared__ u32x4 kbuf[2][32][64];
-  __shared__ u32x4 vbuf[2][32][64];
-  __shared__ TileUnion tu;
+  // per wavefront and 32-key half, each lane's 16 bytes of dS records (the
+  // half's two blocks from the rank of the first listed one)
+  __shared__ u32x4 dsl[2][kRowWaves][2][64];
+  __shared__ TileUnionRows<kQTok> tu;
 
   const int h = blockIdx.x % Hk;
-  const int t0 = tile_order[blockIdx.x / (2 * Hk)] * kAttnTile + kTok * ((blockIdx.x / Hk) & 1);
+  const int t0 = tile_order[blockIdx.x / Hk] * kAttnTile;
   if (t0 >= T) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int li = lane & 15;
-  const int t = t0 + wave;
+  const int row = 16 * wave + li;
+  const int tk = row / kG;
+  const int hd = row - kG * tk;
+  const int t = t0 + tk;
   const bool tok_ok = t < T;
-  int s_t = 0, pos_t = 0;
-  if (tok_ok) {
-    s_t = find_seq(cu, S, t);
-    pos_t = t - cu[s_t];
-  }
-  s_t = __builtin_amdgcn_readfirstlane(s_t);
-  pos_t = __builtin_amdgcn_readfirstlane(pos_t);
-  const int ktb_t = tok_ok ? ktbase[s_t] : 0;
-  const int own_c = pos_t / kKT;
 
-  // q and dO as B operands; Delta = rowsum(dO * O) and the LSE of this lane's head
-  // (before the union build so the loads overlap it)
-  const bool hv = tok_ok && li < kG;
-  const int hq = h * kG + min(li, kG - 1);
-  const int trow = tok_ok ? t : 0;
-  bf16x8 qb[8], db[8];
-  float dl, lse2;
-  {
-    const u16* qrow = q + (int64_t)trow * q_st + (int64_t)hq * q_sh + 8 * g;
-    const u16* drow = dO + (int64_t)trow * do_st + (int64_t)hq * do_sh + 8 * g;
-    const u16* orow = o + (int64_t)trow * o_st + (int64_t)hq * o_sh + 8 * g;
-    float part = 0.f;
-#pragma unroll
-    for (int ds = 0; ds < 8; ++ds) {
-      qb[ds] = hv ? load_bf16x8(qrow + 32 * ds) : zero_bf16x8();
-      db[ds] = hv ? load_bf16x8(drow + 32 * ds) : zero_bf16x8();
-      const bf16x8 ob = hv ? load_bf16x8(orow + 32 * ds) : zero_bf16x8();
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part = fmaf((float)db[ds][e], (float)ob[e], part);
-    }
-    dl = sum_over_groups(part);
-    const float l = hv ? lse[(int64_t)t * (Hk * kG) + hq] : -INFINITY;
-    lse2 = l * kLog2e;  // -inf for empty rows and padded heads: P = 0 there
-    if (tok_ok && g == 0) {
-      delta[((int64_t)t * Hk + h) * 16 + li] = hv ? dl : 0.f;
-      nlse[((int64_t)t * Hk + h) * 16 + li] = lse2 > -INFINITY ? -lse2 : -INFINITY;
-    }
-  }
-  const bool live = lse2 > -INFINITY;
-  build_union(tu, bits, cu, ktbase, kt_seq, S, Hk, h, t0, wave, lane, tok_ok, t, pos_t, ktb_t);
+  build_union_rows<kQTok, kRowWaves>(tu, bits, cu, ktbase, S, T, Hk, h, t0, wave, lane);
   const int nu = tu.nunion;
+  const int pos_t = tu.tpos[tk];
+  const int ktb_t = tu.tktb[tk];
+  const int own_c = tok_ok ? pos_t / kKT : -1;
+  // this row's records: [rank][4 keys] of its (token, KV head, query head)
+  const u16* drow = ds + (((int64_t)(tok_ok ? t : 0) * Hk + h) * kG + hd) * topk * 4;
   f32x4 dqacc[16];
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt) dqacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // staging of union step u: wavefront w copies K runs 4w .. 4w+3 and the same
-  // V runs (key tile w / 2, dims 128 (w % 2) + 32 ii ..)
-  auto stage = [&](int u, int buf) {
+  // the row's listed blocks in step u's key tile
+  auto tile_bits = [&](int u) -> uint32_t {
+    const int c = tu.ulist[u] - ktb_t;
+    return (c >= 0 && c <= own_c) ? tile_mask(tu.bmap[tk], c) : 0u;
+  };
+  // staging of union step u: the tile's 32 K runs (run wave + 12 ii copied by
+  // wavefront `wave`), then each lane's 16 bytes of records per half, from
+  // the rank of the half's first listed block of the lane's pair (every lane
+  // copies, so each wavefront issues the same number of copies; rank 0 of the
+  // row stands in where nothing is listed, the buffer's tail is padded)
+  auto stage = [&](int u, int buf, uint32_t m16, int rank) {
     const int gk = __builtin_amdgcn_readfirstlane(tu.ulist[u]);
     const int ln = fresh_lane();
-    const int64_t run0 = (((int64_t)gk * Hk + h) * 32 + 4 * wave) * 512;
+    const u16* kbase = kop + ((int64_t)gk * Hk + h) * 32 * 512;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      dma16s(kop + run0 + 512 * ii, 16 * ln, lds_offset(&kbuf[buf][4 * wave + ii][0]));
-      dma16s(vop + run0 + 512 * ii, 16 * ln, lds_offset(&vbuf[buf][4 * wave + ii][0]));
+    for (int ii = 0; ii < (32 + kRowWaves - 1) / kRowWaves; ++ii) {
+      const int r = wave + kRowWaves * ii;
+      if (r < 32) dma16s(kbase + 512 * r, 16 * ln, lds_offset(&kbuf[buf][r][0]));
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const int b0 = 8 * kc + 2 * g;
+      const int base = rank + __popc(m16 & ((1u << b0) - 1u));
+      dma16(drow + (int64_t)base * 4, lds_offset(&dsl[buf][wave][kc][0]));
     }
   };
-  if (nu > 0) stage(0, 0);
+  int rank = 0;  // listed blocks of the row's token in the tiles before the current one
+  uint32_t m_cur = 0u;
+  if (nu > 0) {
+    m_cur = tile_bits(0);
+    stage(0, 0, m_cur, 0);
+  }
   wait_copies();
   wait_all_loads();
   __syncthreads();
 
   for (int u = 0; u < nu; ++u) {
     const int buf = u & 1;
-    if (u + 1 < nu) stage(u + 1, buf ^ 1);
-    const int c = tu.ulist[u] - ktb_t;
-    const uint32_t m16 = (tok_ok && c >= 0 && c <= own_c) ? tile_mask(tu.bmap[wave], c) : 0u;
-    if (m16 != 0u) {
+    const int rank_next = rank + __popc(m_cur);
+    const uint32_t m_next = u + 1 < nu ? tile_bits(u + 1) : 0u;
+    if (u + 1 < nu) stage(u + 1, buf ^ 1, m_next, rank_next);
+    if (__ballot(m_cur != 0u)) {
+      const int c = tu.ulist[u] - ktb_t;
       const bool own = (c == own_c);
       const int plim = pos_t - kKT * c;
-      // two halves of 32 keys (key tiles 2kc, 2kc+1): S^T and dP^T, then
-      // dS^T as the B operand of dQ^T = K^T dS^T
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        if (own && 32 * kc > plim) break;
-        f32x4 sacc[2], pacc[2];
+        // a half no row has a causal key in holds only zero records
+        if (!__ballot(m_cur != 0u && !(own && 32 * kc > plim))) continue;
+        // dS^T operand: keys 8g .. 8g+7 of the row = blocks b0, b0 + 1 of the
+        // tile (zero where unlisted); the copy holds the records of ranks
+        // base and base + 1
+        const int b0 = 8 * kc + 2 * g;
+        const bool l0 = (m_cur >> b0) & 1u, l1 = (m_cur >> (b0 + 1)) & 1u;
+        const u32x4 rec = dsl[buf][wave][kc][lane];
+        const uint32_t hx = l0 ? rec[2] : rec[0], hy = l0 ? rec[3] : rec[1];
+        const bf16x8 dsb = __builtin_bit_cast(
+            bf16x8, u32x4{l0 ? rec[0] : 0u, l0 ? rec[1] : 0u, l1 ? hx : 0u, l1 ? hy : 0u});
+        // K^T operands read transposed from the K stage: keys 8g .. 8g+7 of
+        // the half (tiles 2kc, 2kc+1, rows 4g .. 4g+3) at dim 16 dt + li
+        const uint32_t kq = lds_offset(&kbuf[buf][16 * kc][0]) + tr_lane_offset(fresh_lane());
+        bf16x8 ta[16];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          sacc[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
-          pacc[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int dt = 0; dt < 16; ++dt) {
+          const uint32_t off = kq + (dt >> 1) * 1024 + (dt & 1) * 512;
+          const uint2 lo = read_tr16(off), hi = read_tr16(off + 8192);
+          ta[dt] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
         }
-        {
-          const int swz = swz_slot(lane);
-          bf16x8 op[32];  // i = ds * 4 + kk * 2 + (0: K, 1: V)
 #pragma unroll
-          for (int i = 0; i < 32; ++i) {
-            const int run = (2 * kc + ((i >> 1) & 1)) * 8 + (i >> 2);
-            op[i] = __builtin_bit_cast(bf16x8, (i & 1) ? vbuf[buf][run][swz] : kbuf[buf][run][swz]);
-          }
+        for (int dt = 0; dt < 16; ++dt) dqacc[dt] = mfma16x16x32(ta[dt], dsb, dqacc[dt]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kDqTrAhead, 0);
 #pragma unroll
-          for (int i = 0; i < 32; ++i) {
-            const int kk = (i >> 1) & 1, ds = i >> 2;
-            if (i & 1)
-              pacc[kk] = mfma16x16x32(op[i], db[ds], pacc[kk]);
-            else
-              sacc[kk] = mfma16x16x32(op[i], qb[ds], sacc[kk]);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-          for (int i = 0; i < 24; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        for (int i = 0; i < 16 - kDqTrAhead; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
-        // dS^T = P^T (dP^T - Delta) on listed causal keys; row r of tile
-        // 2kc + kk in lane group g is tile key 32 kc + 8g + 4kk + r, block
-        // 8 kc + 2g + kk
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const bool listed = live && ((m16 >> (8 * kc + 2 * g + kk)) & 1u);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int kl = 32 * kc + 8 * g + 4 * kk + r;
-            const bool on = listed && (!own || kl <= plim);
-            const float e = fast_exp2(fmaf(sacc[kk][r], scale_log2, -lse2));
-            sacc[kk][r] = on ? e * (pacc[kk][r] - dl) : 0.f;
-          }
-        }
-        const bf16x8 dsf = pack_bf16x8(sacc[0], sacc[1]);
-        {
-          // K^T operands read transposed from the K stage: keys 8g .. 8g+7 of
-          // the half (tiles 2kc, 2kc+1, rows 4g .. 4g+3) at dim 16 dt + li
-          const uint32_t kq = lds_offset(&kbuf[buf][16 * kc][0]) + tr_lane_offset(fresh_lane());
-          bf16x8 ta[16];
-#pragma unroll
-          for (int dt = 0; dt < 16; ++dt) {
-            const uint32_t off = kq + (dt >> 1) * 1024 + (dt & 1) * 512;
-            const uint2 lo = read_tr16(off), hi = read_tr16(off + 8192);
-            ta[dt] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-          }
-#pragma unroll
-          for (int dt = 0; dt < 16; ++dt) dqacc[dt] = mfma16x16x32(ta[dt], dsf, dqacc[dt]);
-          __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-#pragma unroll
-          for (int i = 0; i < 10; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kDqTrAhead, 0);
       }
     }
     wait_copies();
     lds_barrier();
+    rank = rank_next;
+    m_cur = m_next;
   }
 
-  if (tok_ok && li < kG) {
-    u16* out = dq + (int64_t)t * dq_st + (int64_t)(h * kG + li) * dq_sh;
+  if (tok_ok) {
+    u16* out = dq + (int64_t)t * dq_st + (int64_t)(h * kG + hd) * dq_sh;
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) *reinterpret_cast<uint2*>(out + 16 * dt + 4 * g) = pack_bf16x4(dqacc[dt] * scale);
   }
@@ -691,14 +665,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh, const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
     const u16* __restrict__ v, int64_t v_st, int64_t v_sh, const u16* __restrict__ dO, int64_t do_st,
     int64_t do_sh, const float* __restrict__ nlse, const float* __restrict__ delta,
-    const uint32_t* __restrict__ bits, const int32_t* __restrict__ cu, const int32_t* __restrict__ seqitem,
-    const int32_t* __restrict__ totals, int S, int Hk, int chunk, int items_cap, float scale_log2, float scale,
-    int32_t* __restrict__ item_count, float* __restrict__ part_dk, float* __restrict__ part_dv,
+    const uint32_t* __restrict__ bits, const uint16_t* __restrict__ lpre, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ seqitem, const int32_t* __restrict__ totals, int S, int Hk, int chunk,
+    int items_cap, int topk, float scale_log2, float scale, int32_t* __restrict__ item_count,
+    float* __restrict__ part_dk, float* __restrict__ part_dv, u16* __restrict__ ds_out,
     u16* __restrict__ dk_out, int64_t dk_st, int64_t dk_sh, u16* __restrict__ dv_out, int64_t dv_st,
     int64_t dv_sh) {
   __shared__ u32x4 stage[2][kPair][1024];
   __shared__ __align__(16) float stats[2][kPair][32];
-  __shared__ int sel[kDkdvChunkMax];  // (position - p_begin) | (block mask << 16)
+  __shared__ int sel[kQsaChunkMax];  // (position - p_begin) | (block mask << 16)
+  __shared__ uint16_t selrank[kQsaChunkMax];  // listed blocks of the token before key tile c
+  // the dS of a round, [wavefront (16 keys)][row][key], stored during the next
+  // round (double buffered: the next round's writes go to the other half)
+  __shared__ __align__(16) u16 dsx[2][4][32][16];
   __shared__ int wcount[4];
 
   const int h = blockIdx.y;
@@ -732,7 +711,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int p0 = p_begin; p0 < p_end; p0 += 256) {
     const int p = p0 + threadIdx.x;
     uint32_t m = 0u;
-    if (p < p_end) m = tile_mask(bits + ((int64_t)(seq0 + p) * Hk + h) * kWords, c);
+    int rb = 0;
+    if (p < p_end) {
+      const int64_t ro = ((int64_t)(seq0 + p) * Hk + h) * kWords + (c >> 1);
+      const uint32_t wd = bits[ro];
+      m = (wd >> (16 * (c & 1))) & 0xFFFFu;
+      if (m != 0u) rb = lpre[ro] + ((c & 1) ? __popc(wd & 0xFFFFu) : 0);
+    }
     const uint64_t bal = __ballot(m != 0u);
     const int before = __popcll(bal & ((1ull << lane) - 1ull));
     if (lane == 0) wcount[wave] = __popcll(bal);
@@ -744,7 +729,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       off += w < wave ? wcount[w] : 0;
       tot += wcount[w];
     }
-    if (m != 0u) sel[off + before] = (p - p_begin) | (int)(m << 16);
+    if (m != 0u) {
+      sel[off + before] = (p - p_begin) | (int)(m << 16);
+      selrank[off + before] = (uint16_t)rb;
+    }
     nsel += tot;
     __syncthreads();
   }
@@ -782,6 +770,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                    lds_offset(&stage[buf][wave][0]), lds_offset(&stats[buf][wave][0]), q, q_st, q_sh, dO, do_st,
                    do_sh, nlse, delta);
     };
+    // round b's dS from the stash into the dQ pass's compact records: per
+    // (token, KV head, query head) one 4-key record per listed block, in rank
+    // order.  Eight threads per row: store k writes the listed blocks among
+    // 8k .. 8k+7, whose records are consecutive, so a row's records of this
+    // key tile leave as two contiguous runs
+    auto flush = [&](int b) {
+      const int R = threadIdx.x >> 3, j = threadIdx.x & 7;
+      const int rrow = 32 * b + R;
+      if (rrow < nrows) {
+        const int n = rrow / kG;
+        const int e = sel[n];
+        const uint32_t m = (uint32_t)e >> 16;
+        const int tok = seq0 + p_begin + (e & 0xFFFF);
+        u16* dst = ds_out + (((int64_t)tok * Hk + h) * kG + (rrow - kG * n)) * topk * 4;
+#pragma unroll
+        for (int k8 = 0; k8 < 2; ++k8) {
+          const int bt = j + 8 * k8;
+          if ((m >> bt) & 1u) {
+            const int rank = selrank[n] + __popc(m & ((1u << bt) - 1u));
+            *reinterpret_cast<uint2*>(dst + (int64_t)rank * 4) =
+                *reinterpret_cast<const uint2*>(&dsx[b & 1][bt >> 2][R][4 * (bt & 3)]);
+          }
+        }
+      }
+      asm volatile("" ::: "memory");
+    };
     stage_round(0, 0);
     wait_copies();
     wait_all_loads();
@@ -790,6 +804,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int bi = 0; bi < nround; ++bi) {
       const int cur = bi & 1;
       if (bi + 1 < nround) stage_round(bi + 1, cur ^ 1);
+      if (bi > 0) flush(bi - 1);
       // per tile tk, this lane's accumulator rows 4g .. 4g+3 (rows
       // 32 bi + 16 tk + 4g ..) belong to one token (12 is a multiple of 4);
       // rows past the list's end are masked out entirely
@@ -835,6 +850,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         sw[2 * tk] = pack_bf16x2(d[0], d[1]);
         sw[2 * tk + 1] = pack_bf16x2(d[2], d[3]);
       }
+      // the round's dS into the LDS stash; after the round's barrier it holds
+      // all 64 keys of the round's rows
+#pragma unroll
+      for (int tk = 0; tk < 2; ++tk) {
+        u16* col = &dsx[bi & 1][wave][16 * tk + 4 * g][li];
+        col[0] = (u16)(sw[2 * tk] & 0xFFFFu);
+        col[16] = (u16)(sw[2 * tk] >> 16);
+        col[32] = (u16)(sw[2 * tk + 1] & 0xFFFFu);
+        col[48] = (u16)(sw[2 * tk + 1] >> 16);
+      }
+      asm volatile("" ::: "memory");
       const bf16x8 pA = __builtin_bit_cast(bf16x8, pw);
       const bf16x8 sA = __builtin_bit_cast(bf16x8, sw);
       const uint32_t tro = tr_lane_offset(ln);
@@ -854,6 +880,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       wait_copies();
       lds_barrier();
     }
+    flush(nround - 1);
   }
 
   // 4. results: lane holds key kbase + 4g + r, dim 16 dt + li
@@ -958,16 +985,16 @@ __global__ __launch_bounds__(256) void qsa_reduce_kernel(
   }
 }
 
-void launch_bitmaps(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStream_t st) {
+void launch_bitmaps(const Sizes& z, const QsaArgs& a, const PlanBufs& p, uint16_t* lpre, hipStream_t st) {
   KernelTimer timer("qsa_bitmap", st);
   qsa_bitmap_kernel<<<dim3((unsigned)((z.T + 3) / 4 + 1), (unsigned)z.Hk), 256, 0, st>>>(
-      a.blk_idx, a.topk, a.cu, (int)z.S, (int)z.T, (int)z.Hk, (int)z.chunk, (int)z.ntiles, p, a.bits);
+      a.blk_idx, a.topk, a.cu, (int)z.S, (int)z.T, (int)z.Hk, (int)z.chunk, (int)z.ntiles, p, a.bits, lpre);
 }
 
 }  // namespace
 
 void launch_qsa_fwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStream_t st) {
-  launch_bitmaps(z, a, p, st);
+  launch_bitmaps(z, a, p, nullptr, st);
   {
     KernelTimer timer("qsa_vt", st);
     qsa_vt_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk), 256, 0, st>>>(
@@ -982,31 +1009,37 @@ void launch_qsa_fwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStre
 }
 
 void launch_qsa_bwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStream_t st) {
-  launch_bitmaps(z, a, p, st);
+  launch_bitmaps(z, a, p, a.lpre, st);
   {
+    // K in the dQ pass's swizzled stage order (parts 0-3 of the prep grid)
     KernelTimer timer("qsa_prep", st);
-    qsa_prep_kernel<true><<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk, 8), 256, 0, st>>>(
-        a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.cu, p.blkbase, p.blk_seq, p.totals, (int)z.Hk, a.kop, a.vop);
+    qsa_prep_kernel<true><<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk, 4), 256, 0, st>>>(
+        a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.cu, p.blkbase, p.blk_seq, p.totals, (int)z.Hk, a.kop, nullptr);
   }
   {
-    KernelTimer timer("qsa_dq", st);
-    qsa_dq_kernel<<<(unsigned)(2 * z.ntiles * z.Hk), 64 * kTok, 0, st>>>(
-        a.q, a.q_st, a.q_sh, a.kop, a.vop, a.o, a.o_st, a.o_sh, a.dO, a.do_st, a.do_sh,
-        a.lse, a.bits, a.cu, p.blkbase, p.blk_seq, p.tile_order, (int)z.S, (int)z.T, (int)z.Hk, a.scale * kLog2e,
-        a.scale, a.dq, a.dq_st, a.dq_sh, a.delta, a.nlse);
+    KernelTimer timer("qsa_delta", st);
+    qsa_delta_kernel<<<dim3((unsigned)((z.T + 3) / 4), (unsigned)z.Hk), 256, 0, st>>>(
+        a.o, a.o_st, a.o_sh, a.dO, a.do_st, a.do_sh, a.lse, (int)z.T, (int)z.Hk, a.delta, a.nlse);
   }
   {
     KernelTimer timer("qsa_dkdv", st);
     qsa_dkdv_kernel<<<dim3((unsigned)z.items_cap, (unsigned)z.Hk), 256, 0, st>>>(
         a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.dO, a.do_st, a.do_sh, a.nlse, a.delta,
-        a.bits, a.cu, p.seqitem, p.totals, (int)z.S, (int)z.Hk, (int)z.chunk, (int)z.items_cap, a.scale * kLog2e,
-        a.scale, a.item_count, a.part_dk, a.part_dv, a.dk, a.dk_st, a.dk_sh, a.dv, a.dv_st, a.dv_sh);
+        a.bits, a.lpre, a.cu, p.seqitem, p.totals, (int)z.S, (int)z.Hk, (int)z.chunk, (int)z.items_cap, a.topk,
+        a.scale * kLog2e, a.scale, a.item_count, a.part_dk, a.part_dv, a.ds, a.dk, a.dk_st, a.dk_sh, a.dv,
+        a.dv_st, a.dv_sh);
   }
   {
     KernelTimer timer("qsa_reduce", st);
     qsa_reduce_kernel<<<dim3((unsigned)z.nblk_cap, kKT / 16, (unsigned)z.Hk), 256, 0, st>>>(
         a.part_dk, a.part_dv, a.item_count, p.seqitem, p.blk_seq, p.blkbase, a.cu, p.totals, (int)z.chunk,
         (int)z.items_cap, a.scale, a.dk, a.dk_st, a.dk_sh, a.dv, a.dv_st, a.dv_sh);
+  }
+  {
+    KernelTimer timer("qsa_dq", st);
+    qsa_dq_ds_kernel<<<(unsigned)(z.ntiles * z.Hk), 64 * kRowWaves, 0, st>>>(
+        a.kop, a.ds, a.bits, a.cu, p.blkbase, p.tile_order, (int)z.S, (int)z.T, (int)z.Hk, a.topk, a.scale, a.dq,
+        a.dq_st, a.dq_sh);
   }
 }
 
