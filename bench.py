@@ -122,7 +122,8 @@ KERNEL_NAMES = {"attn_bwd_dkdv_kernel<false, true>": "attn_bwd_dkdv_kernel",
                 "attn_bwd_dkdv_kernel<false, false>": "attn_bwd_dkdv_recompute_kernel",
                 "attn_bwd_dkdv_kernel<true, false>": "attn_bwd_dkdv_dense_kernel",
                 "attn_bwd_dq_ds_kernel": "attn_bwd_dq_kernel",
-                "attn_bwd_dq_kernel<false, false>": "attn_bwd_dq_recompute_kernel"}
+                "attn_bwd_dq_kernel<false, false>": "attn_bwd_dq_recompute_kernel",
+                "qsa_dq_ds_kernel": "qsa_dq_kernel"}
 
 
 def kernel_key(raw: str) -> str:
