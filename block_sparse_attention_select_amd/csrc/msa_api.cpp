@@ -99,7 +99,6 @@ Sizes sizes_of_qsa(const msa_dims* d) {
   z.Hk = d->num_kv_heads;
   z.max_seqlen = d->max_seqlen;
   z.nbmax = (z.max_seqlen + msa::kQsaKeyTile - 1) / msa::kQsaKeyTile;
-  z.topk = d->topk_blocks;
   // dK/dV query chunks of 256 tokens: on the 16k narrow pack (512 listed
   // blocks per query) 512-token chunks took the dK/dV pass 1.79 ms against
   // 1.59 ms, while the reduce grew from 52 to 103 us; 128 gained nothing more
@@ -290,7 +289,7 @@ QsaFwdWs carve_qsa_fwd(Carver& c, const Sizes& z) {
 struct QsaBwdWs {
   PlanBufs plan;
   uint32_t* bits;
-  uint16_t* lpre;
+  int64_t* dsbase;
   u16* kop;
   u16* ds;
   float* delta;
@@ -299,15 +298,31 @@ struct QsaBwdWs {
   float* part_dk;
   float* part_dv;
 };
+// Bound on the narrow backward's dS slots: a token at position p owns p / 64 + 1
+// (one per causal key tile), so a length-L sequence f(L) = sum over p < L.  f
+// is convex, so over lengths <= max_seqlen M summing to T the sum is largest
+// for T / M sequences of length M and one of T % M; nor does it exceed
+// T * ceil(M / 64).
+int64_t qsa_ds_slots(const Sizes& z) {
+  const int64_t M = z.max_seqlen, T = z.T;
+  if (T == 0 || M == 0) return 0;
+  auto f = [](int64_t L) {
+    const int64_t a = L / 64;
+    return (a + 1) * (32 * a + L % 64);
+  };
+  const int64_t by_len = (T / M) * f(M) + f(T % M);
+  const int64_t by_tok = T * ((M - 1) / 64 + 1);
+  return by_len < by_tok ? by_len : by_tok;
+}
+
 QsaBwdWs carve_qsa_bwd(Carver& c, const Sizes& z) {
   QsaBwdWs w;
   w.plan = carve_plan(c, z);
   w.bits = c.take<uint32_t>(z.T * z.Hk * msa::kQsaWords);
-  w.lpre = c.take<uint16_t>(z.T * z.Hk * msa::kQsaWords);
+  w.dsbase = c.take<int64_t>(z.S + 1);
   w.kop = c.take<u16>(z.nblk_cap * z.Hk * msa::kQsaKeyTile * msa::kQsaHeadDim);
-  // one 4-key dS record per listed block of each (token, KV head, query head);
-  // the dQ pass copies 16 bytes from a record, so 16 bytes of tail padding
-  w.ds = c.take<u16>(z.T * z.Hk * z.topk * msa::kQsaGroup * msa::kQsaBlock + 8);
+  // one 128-byte dS line per (token, causal key tile, KV head, query head)
+  w.ds = c.take<u16>(qsa_ds_slots(z) * z.Hk * msa::kQsaGroup * msa::kQsaKeyTile);
   w.delta = c.take<float>(z.T * z.Hk * 16);
   w.nlse = c.take<float>(z.T * z.Hk * 16);
   w.item_count = c.take<int32_t>(z.Hk * z.items_cap);
@@ -664,7 +679,7 @@ int msa_qsa_attn_bwd(const msa_dims* dims, const void* q, int64_t q_st, int64_t 
   a.dk = (u16*)dk; a.dk_st = dk_st; a.dk_sh = dk_sh;
   a.dv = (u16*)dv; a.dv_st = dv_st; a.dv_sh = dv_sh;
   a.bits = w.bits;
-  a.lpre = w.lpre;
+  a.dsbase = w.dsbase;
   a.kop = w.kop;
   a.ds = w.ds;
   a.delta = w.delta;

@@ -28,7 +28,6 @@ struct Sizes {
   int64_t chunk;      // query positions per dK/dV work item (a multiple of 128)
   int64_t items_cap;  // bound on the number of dK/dV work items per KV head
   int64_t ntiles;     // ceil(T / kAttnTile)
-  int64_t topk = 0;   // block ids per (token, KV head) (narrow variant)
 };
 
 struct PlanBufs {
@@ -343,10 +342,10 @@ struct QsaArgs {
   u16* dv; int64_t dv_st, dv_sh;
   // workspace
   uint32_t* bits;     // [T][Hk][kQsaWords] selected-block bitmaps
-  uint16_t* lpre;     // [T][Hk][kQsaWords] listed blocks before each bitmap word (backward)
+  int64_t* dsbase;    // [S+1] first dS slot of each sequence (backward)
   u16* vt;            // [key tiles][Hk][32 runs][64 lanes][8] V^T in MFMA operand order (forward)
   u16* kop;           // the same shape: K in the forward's (or, backward, the dQ pass's swizzled) stage order
-  u16* ds;            // [T][Hk][12][topk][4] bf16 dS per listed block, in the token's block order (backward)
+  u16* ds;            // [slot][Hk][12][64] bf16 dS per (token, causal key tile) slot (backward)
   float* delta;       // [T][Hk][16] (heads past 12 unused)
   float* nlse;        // [T][Hk][16] -LSE * log2(e) (-inf for empty rows; heads past 12 unused)
   int32_t* item_count;  // [Hk][items_cap]

@@ -29,9 +29,10 @@
 //             through LDS 32 at a time, so a step mixes tokens and carries no
 //             padding heads; chunk slices are summed in chunk order by
 //             qsa_reduce_kernel (fixed order, no atomics).  It also stores the
-//             bf16 dS of every listed block as a 4-key record per (token, KV
-//             head, query head), indexed by the block's rank in the token's
-//             ascending list;
+//             bf16 dS of each (token, causal key tile, KV head, query head) it
+//             covers as one whole 128-byte line (its 64 keys, zero where the
+//             token listed nothing), at a slot found in closed form from the
+//             token's position;
 //   dQ        the forward's tiling and row packing over the stored dS: only K
 //             is staged (K^T read transposed), and dQ^T = K^T dS^T is one
 //             product per listed block instead of three.
@@ -66,19 +67,51 @@ __device__ __forceinline__ uint32_t tile_mask(const uint32_t* row, int c) {
 // token tile launch order) for the kernels that follow, so the narrow passes
 // need no plan launch of their own; dispatched first, it runs beside the
 // bitmap workgroups instead of after them.
-// lpre (optional, the backward's): per word of the row, the number of listed
-// blocks in the words before it, so that a listed block's rank in the token's
-// ascending list (the index of its dS record) is one lookup and one popcount.
+// dS slots of the backward: a token at sequence position p owns one slot per
+// key tile c <= p / 64, the slots of a sequence's tokens in position order, so
+// the positions before p hold slots_before(p) of them.  dsbase (optional, the
+// backward's) receives each sequence's first slot ([S+1], prefix sums).
+__device__ __forceinline__ int64_t slots_before(int p) {
+  const int a = p >> 6;
+  return (int64_t)(a + 1) * (32 * a + (p & 63));
+}
+
 __global__ __launch_bounds__(256) void qsa_bitmap_kernel(const int32_t* __restrict__ blk_idx, int topk,
                                                          const int32_t* __restrict__ cu, int S, int T, int Hk,
                                                          int chunk, int ntiles, PlanBufs plan,
-                                                         uint32_t* __restrict__ bits, uint16_t* __restrict__ lpre) {
+                                                         uint32_t* __restrict__ bits, int64_t* __restrict__ dsbase) {
   __shared__ uint32_t row[4][kWords];
   if (blockIdx.x == 0) {
     if (blockIdx.y == 0) {
       __shared__ int sb[256], si[256], hist[kOrderBins], scu[kCuCache];
       plan_blocks<256, kKT>(cu, S, chunk, plan.blkbase, plan.blk_seq, plan.seqitem, plan.totals, sb, si);
       plan_tile_order<256, 16>(cu, S, ntiles, plan.tile_order, sb, hist, scu);
+      if (dsbase != nullptr) {
+        // thread i sums a contiguous run of sequences; the 256 partial sums
+        // are scanned, then each run is written out from its offset
+        __shared__ int64_t part[256];
+        const int per = (S + 255) / 256;
+        const int s0 = threadIdx.x * per, s1 = min(s0 + per, S);
+        int64_t sum = 0;
+        for (int q = s0; q < s1; ++q) sum += slots_before(cu[q + 1] - cu[q]);
+        part[threadIdx.x] = sum;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          int64_t acc = 0;
+          for (int i = 0; i < 256; ++i) {
+            const int64_t x = part[i];
+            part[i] = acc;
+            acc += x;
+          }
+        }
+        __syncthreads();
+        int64_t acc = part[threadIdx.x];
+        for (int q = s0; q < s1; ++q) {
+          dsbase[q] = acc;
+          acc += slots_before(cu[q + 1] - cu[q]);
+        }
+        if (threadIdx.x == 255) dsbase[S] = acc;
+      }
     }
     return;
   }
@@ -100,20 +133,6 @@ __global__ __launch_bounds__(256) void qsa_bitmap_kernel(const int32_t* __restri
   if (t < T) {
     const u32x4 x = {row[wave][4 * lane], row[wave][4 * lane + 1], row[wave][4 * lane + 2], row[wave][4 * lane + 3]};
     *reinterpret_cast<u32x4*>(bits + ((int64_t)t * Hk + h) * kWords + 4 * lane) = x;
-    if (lpre != nullptr) {
-      const int c0 = __popc(x[0]), c1 = __popc(x[1]), c2 = __popc(x[2]), c3 = __popc(x[3]);
-      const int cnt = c0 + c1 + c2 + c3;
-      int incl = cnt;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
-      const int e0 = incl - cnt;
-      const uint2 pr = {(uint32_t)e0 | ((uint32_t)(e0 + c0) << 16),
-                        (uint32_t)(e0 + c0 + c1) | ((uint32_t)(e0 + c0 + c1 + c2) << 16)};
-      *reinterpret_cast<uint2*>(lpre + ((int64_t)t * Hk + h) * kWords + 4 * lane) = pr;
-    }
   }
 }
 
@@ -246,13 +265,15 @@ struct TileUnionRows {
   int ulist[kUnionMax];
   int tpos[kN];
   int tktb[kN];
+  int64_t tslot[kN];  // the token's dS slot of key tile 0 (the backward's)
   int nunion;
 };
 
 template <int kN, int kWaves>
 __device__ __forceinline__ void build_union_rows(TileUnionRows<kN>& tu, const uint32_t* __restrict__ bits,
                                                  const int32_t* __restrict__ cu, const int32_t* __restrict__ ktbase,
-                                                 int S, int T, int Hk, int h, int t0, int wave, int lane) {
+                                                 const int64_t* __restrict__ dsbase, int S, int T, int Hk, int h,
+                                                 int t0, int wave, int lane) {
   const int gk_lo = ktbase[find_seq(cu, S, t0)];
   if (threadIdx.x < kUnionWords) tu.ubits[threadIdx.x] = 0u;
   __syncthreads();
@@ -260,14 +281,17 @@ __device__ __forceinline__ void build_union_rows(TileUnionRows<kN>& tu, const ui
     const int t = t0 + j;
     const bool ok = t < T;
     int pos = -1, ktb = 0;
+    int64_t slot = 0;
     if (ok) {
       const int s = find_seq(cu, S, t);
       pos = t - cu[s];
       ktb = ktbase[s];
+      if (dsbase != nullptr) slot = dsbase[s] + slots_before(pos);
     }
     if (lane == 0) {
       tu.tpos[j] = pos;
       tu.tktb[j] = ktb;
+      tu.tslot[j] = slot;
     }
     const uint32_t* brow = bits + ((int64_t)(ok ? t : 0) * Hk + h) * kWords;
     const int nw = ok ? (pos / kQsaBlock) / 32 + 1 : 0;
@@ -340,7 +364,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void qsa_fwd_kernel(
 #pragma unroll
     for (int ds = 0; ds < 8; ++ds) qb[ds] = tok_ok ? load_bf16x8(qrow + 32 * ds) : zero_bf16x8();
   }
-  build_union_rows<kQTok, kRowWaves>(tu, bits, cu, ktbase, S, T, Hk, h, t0, wave, lane);
+  build_union_rows<kQTok, kRowWaves>(tu, bits, cu, ktbase, nullptr, S, T, Hk, h, t0, wave, lane);
   const int nu = tu.nunion;
   const int pos_t = tu.tpos[tk];
   const int ktb_t = tu.tktb[tk];
@@ -495,14 +519,14 @@ __global__ __launch_bounds__(64 * kRowWaves) void qsa_fwd_kernel(
 // complete in issue order).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64 * kRowWaves) void qsa_dq_ds_kernel(
-    const u16* __restrict__ kop, const u16* ds, const uint32_t* __restrict__ bits, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ ktbase, const int32_t* __restrict__ tile_order, int S, int T, int Hk, int topk,
-    float scale, u16* __restrict__ dq, int64_t dq_st, int64_t dq_sh) {
+    const u16* __restrict__ kop, const u16* ds, const int64_t* __restrict__ dsbase,
+    const uint32_t* __restrict__ bits, const int32_t* __restrict__ cu, const int32_t* __restrict__ ktbase,
+    const int32_t* __restrict__ tile_order, int S, int T, int Hk, float scale, u16* __restrict__ dq, int64_t dq_st,
+    int64_t dq_sh) {
   // K runs kt * 8 + ds (keys score_key(kt, .), dims 32 ds ..), stored
   // swizzled (swz_slot) for the transposed K^T reads
   __shared__ u32x4 kbuf[2][32][64];
-  // per wavefront and 32-key half, each lane's 16 bytes of dS records (the
-  // half's two blocks from the rank of the first listed one)
+  // per wavefront and 32-key half, each lane's 8 keys of dS
   __shared__ u32x4 dsl[2][kRowWaves][2][64];
   __shared__ TileUnionRows<kQTok> tu;
 
@@ -519,13 +543,13 @@ __global__ __launch_bounds__(64 * kRowWaves) void qsa_dq_ds_kernel(
   const int t = t0 + tk;
   const bool tok_ok = t < T;
 
-  build_union_rows<kQTok, kRowWaves>(tu, bits, cu, ktbase, S, T, Hk, h, t0, wave, lane);
+  build_union_rows<kQTok, kRowWaves>(tu, bits, cu, ktbase, dsbase, S, T, Hk, h, t0, wave, lane);
   const int nu = tu.nunion;
   const int pos_t = tu.tpos[tk];
   const int ktb_t = tu.tktb[tk];
   const int own_c = tok_ok ? pos_t / kKT : -1;
-  // this row's records: [rank][4 keys] of its (token, KV head, query head)
-  const u16* drow = ds + (((int64_t)(tok_ok ? t : 0) * Hk + h) * kG + hd) * topk * 4;
+  // this row's dS line of its token's key tile c: slot tslot + c
+  const int64_t slot0 = tu.tslot[tk];
   f32x4 dqacc[16];
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt) dqacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -536,11 +560,10 @@ __global__ __launch_bounds__(64 * kRowWaves) void qsa_dq_ds_kernel(
     return (c >= 0 && c <= own_c) ? tile_mask(tu.bmap[tk], c) : 0u;
   };
   // staging of union step u: the tile's 32 K runs (run wave + 12 ii copied by
-  // wavefront `wave`), then each lane's 16 bytes of records per half, from
-  // the rank of the half's first listed block of the lane's pair (every lane
-  // copies, so each wavefront issues the same number of copies; rank 0 of the
-  // row stands in where nothing is listed, the buffer's tail is padded)
-  auto stage = [&](int u, int buf, uint32_t m16, int rank) {
+  // wavefront `wave`), then each lane's 16 bytes of its row's dS line per half
+  // (every lane copies, so each wavefront issues the same number of copies;
+  // the row's token's first slot stands in where its token lists nothing)
+  auto stage = [&](int u, int buf, uint32_t m16) {
     const int gk = __builtin_amdgcn_readfirstlane(tu.ulist[u]);
     const int ln = fresh_lane();
     const u16* kbase = kop + ((int64_t)gk * Hk + h) * 32 * 512;
@@ -549,18 +572,15 @@ __global__ __launch_bounds__(64 * kRowWaves) void qsa_dq_ds_kernel(
       const int r = wave + kRowWaves * ii;
       if (r < 32) dma16s(kbase + 512 * r, 16 * ln, lds_offset(&kbuf[buf][r][0]));
     }
+    const int c = m16 != 0u ? tu.ulist[u] - ktb_t : 0;
+    const u16* line = ds + (((slot0 + c) * Hk + h) * kG + hd) * kKT + 8 * g;
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const int b0 = 8 * kc + 2 * g;
-      const int base = rank + __popc(m16 & ((1u << b0) - 1u));
-      dma16(drow + (int64_t)base * 4, lds_offset(&dsl[buf][wave][kc][0]));
-    }
+    for (int kc = 0; kc < 2; ++kc) dma16(line + 32 * kc, lds_offset(&dsl[buf][wave][kc][0]));
   };
-  int rank = 0;  // listed blocks of the row's token in the tiles before the current one
   uint32_t m_cur = 0u;
   if (nu > 0) {
     m_cur = tile_bits(0);
-    stage(0, 0, m_cur, 0);
+    stage(0, 0, m_cur);
   }
   wait_copies();
   wait_all_loads();
@@ -568,9 +588,8 @@ __global__ __launch_bounds__(64 * kRowWaves) void qsa_dq_ds_kernel(
 
   for (int u = 0; u < nu; ++u) {
     const int buf = u & 1;
-    const int rank_next = rank + __popc(m_cur);
     const uint32_t m_next = u + 1 < nu ? tile_bits(u + 1) : 0u;
-    if (u + 1 < nu) stage(u + 1, buf ^ 1, m_next, rank_next);
+    if (u + 1 < nu) stage(u + 1, buf ^ 1, m_next);
     if (__ballot(m_cur != 0u)) {
       const int c = tu.ulist[u] - ktb_t;
       const bool own = (c == own_c);
@@ -579,15 +598,12 @@ __global__ __launch_bounds__(64 * kRowWaves) void qsa_dq_ds_kernel(
       for (int kc = 0; kc < 2; ++kc) {
         // a half no row has a causal key in holds only zero records
         if (!__ballot(m_cur != 0u && !(own && 32 * kc > plim))) continue;
-        // dS^T operand: keys 8g .. 8g+7 of the row = blocks b0, b0 + 1 of the
-        // tile (zero where unlisted); the copy holds the records of ranks
-        // base and base + 1
-        const int b0 = 8 * kc + 2 * g;
-        const bool l0 = (m_cur >> b0) & 1u, l1 = (m_cur >> (b0 + 1)) & 1u;
+        // dS^T operand: keys 32 kc + 8g .. +7 of the row (zero where its
+        // token lists nothing in the tile: that line was never written)
         const u32x4 rec = dsl[buf][wave][kc][lane];
-        const uint32_t hx = l0 ? rec[2] : rec[0], hy = l0 ? rec[3] : rec[1];
-        const bf16x8 dsb = __builtin_bit_cast(
-            bf16x8, u32x4{l0 ? rec[0] : 0u, l0 ? rec[1] : 0u, l1 ? hx : 0u, l1 ? hy : 0u});
+        const bool on = m_cur != 0u;
+        const bf16x8 dsb =
+            __builtin_bit_cast(bf16x8, u32x4{on ? rec[0] : 0u, on ? rec[1] : 0u, on ? rec[2] : 0u, on ? rec[3] : 0u});
         // K^T operands read transposed from the K stage: keys 8g .. 8g+7 of
         // the half (tiles 2kc, 2kc+1, rows 4g .. 4g+3) at dim 16 dt + li
         const uint32_t kq = lds_offset(&kbuf[buf][16 * kc][0]) + tr_lane_offset(fresh_lane());
@@ -611,7 +627,6 @@ __global__ __launch_bounds__(64 * kRowWaves) void qsa_dq_ds_kernel(
     }
     wait_copies();
     lds_barrier();
-    rank = rank_next;
     m_cur = m_next;
   }
 
@@ -665,16 +680,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const u16* __restrict__ q, int64_t q_st, int64_t q_sh, const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
     const u16* __restrict__ v, int64_t v_st, int64_t v_sh, const u16* __restrict__ dO, int64_t do_st,
     int64_t do_sh, const float* __restrict__ nlse, const float* __restrict__ delta,
-    const uint32_t* __restrict__ bits, const uint16_t* __restrict__ lpre, const int32_t* __restrict__ cu,
+    const uint32_t* __restrict__ bits, const int64_t* __restrict__ dsbase, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ seqitem, const int32_t* __restrict__ totals, int S, int Hk, int chunk,
-    int items_cap, int topk, float scale_log2, float scale, int32_t* __restrict__ item_count,
+    int items_cap, float scale_log2, float scale, int32_t* __restrict__ item_count,
     float* __restrict__ part_dk, float* __restrict__ part_dv, u16* __restrict__ ds_out,
     u16* __restrict__ dk_out, int64_t dk_st, int64_t dk_sh, u16* __restrict__ dv_out, int64_t dv_st,
     int64_t dv_sh) {
   __shared__ u32x4 stage[2][kPair][1024];
   __shared__ __align__(16) float stats[2][kPair][32];
   __shared__ int sel[kQsaChunkMax];  // (position - p_begin) | (block mask << 16)
-  __shared__ uint16_t selrank[kQsaChunkMax];  // listed blocks of the token before key tile c
   // the dS of a round, [wavefront (16 keys)][row][key], stored during the next
   // round (double buffered: the next round's writes go to the other half)
   __shared__ __align__(16) u16 dsx[2][4][32][16];
@@ -711,13 +725,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int p0 = p_begin; p0 < p_end; p0 += 256) {
     const int p = p0 + threadIdx.x;
     uint32_t m = 0u;
-    int rb = 0;
-    if (p < p_end) {
-      const int64_t ro = ((int64_t)(seq0 + p) * Hk + h) * kWords + (c >> 1);
-      const uint32_t wd = bits[ro];
-      m = (wd >> (16 * (c & 1))) & 0xFFFFu;
-      if (m != 0u) rb = lpre[ro] + ((c & 1) ? __popc(wd & 0xFFFFu) : 0);
-    }
+    if (p < p_end) m = tile_mask(bits + ((int64_t)(seq0 + p) * Hk + h) * kWords, c);
     const uint64_t bal = __ballot(m != 0u);
     const int before = __popcll(bal & ((1ull << lane) - 1ull));
     if (lane == 0) wcount[wave] = __popcll(bal);
@@ -729,10 +737,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       off += w < wave ? wcount[w] : 0;
       tot += wcount[w];
     }
-    if (m != 0u) {
-      sel[off + before] = (p - p_begin) | (int)(m << 16);
-      selrank[off + before] = (uint16_t)rb;
-    }
+    if (m != 0u) sel[off + before] = (p - p_begin) | (int)(m << 16);
     nsel += tot;
     __syncthreads();
   }
@@ -770,29 +775,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                    lds_offset(&stage[buf][wave][0]), lds_offset(&stats[buf][wave][0]), q, q_st, q_sh, dO, do_st,
                    do_sh, nlse, delta);
     };
-    // round b's dS from the stash into the dQ pass's compact records: per
-    // (token, KV head, query head) one 4-key record per listed block, in rank
-    // order.  Eight threads per row: store k writes the listed blocks among
-    // 8k .. 8k+7, whose records are consecutive, so a row's records of this
-    // key tile leave as two contiguous runs
+    // round b's dS from the stash into the dQ pass's slots: per (token, key
+    // tile c, KV head, query head) the 64 keys' bf16 dS (zero where unlisted
+    // or past the query), one 128-byte line written whole by eight threads
+    const int64_t seqslot = dsbase[s];
     auto flush = [&](int b) {
       const int R = threadIdx.x >> 3, j = threadIdx.x & 7;
       const int rrow = 32 * b + R;
       if (rrow < nrows) {
         const int n = rrow / kG;
-        const int e = sel[n];
-        const uint32_t m = (uint32_t)e >> 16;
-        const int tok = seq0 + p_begin + (e & 0xFFFF);
-        u16* dst = ds_out + (((int64_t)tok * Hk + h) * kG + (rrow - kG * n)) * topk * 4;
-#pragma unroll
-        for (int k8 = 0; k8 < 2; ++k8) {
-          const int bt = j + 8 * k8;
-          if ((m >> bt) & 1u) {
-            const int rank = selrank[n] + __popc(m & ((1u << bt) - 1u));
-            *reinterpret_cast<uint2*>(dst + (int64_t)rank * 4) =
-                *reinterpret_cast<const uint2*>(&dsx[b & 1][bt >> 2][R][4 * (bt & 3)]);
-          }
-        }
+        const int pos = p_begin + (sel[n] & 0xFFFF);
+        const int64_t slot = seqslot + slots_before(pos) + c;
+        *reinterpret_cast<u32x4*>(ds_out + ((slot * Hk + h) * kG + (rrow - kG * n)) * kKT + 8 * j) =
+            *reinterpret_cast<const u32x4*>(&dsx[b & 1][j >> 1][R][8 * (j & 1)]);
       }
       asm volatile("" ::: "memory");
     };
@@ -985,10 +980,10 @@ __global__ __launch_bounds__(256) void qsa_reduce_kernel(
   }
 }
 
-void launch_bitmaps(const Sizes& z, const QsaArgs& a, const PlanBufs& p, uint16_t* lpre, hipStream_t st) {
+void launch_bitmaps(const Sizes& z, const QsaArgs& a, const PlanBufs& p, int64_t* dsbase, hipStream_t st) {
   KernelTimer timer("qsa_bitmap", st);
   qsa_bitmap_kernel<<<dim3((unsigned)((z.T + 3) / 4 + 1), (unsigned)z.Hk), 256, 0, st>>>(
-      a.blk_idx, a.topk, a.cu, (int)z.S, (int)z.T, (int)z.Hk, (int)z.chunk, (int)z.ntiles, p, a.bits, lpre);
+      a.blk_idx, a.topk, a.cu, (int)z.S, (int)z.T, (int)z.Hk, (int)z.chunk, (int)z.ntiles, p, a.bits, dsbase);
 }
 
 }  // namespace
@@ -1009,7 +1004,7 @@ void launch_qsa_fwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStre
 }
 
 void launch_qsa_bwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStream_t st) {
-  launch_bitmaps(z, a, p, a.lpre, st);
+  launch_bitmaps(z, a, p, a.dsbase, st);
   {
     // K in the dQ pass's swizzled stage order (parts 0-3 of the prep grid)
     KernelTimer timer("qsa_prep", st);
@@ -1025,7 +1020,7 @@ void launch_qsa_bwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStre
     KernelTimer timer("qsa_dkdv", st);
     qsa_dkdv_kernel<<<dim3((unsigned)z.items_cap, (unsigned)z.Hk), 256, 0, st>>>(
         a.q, a.q_st, a.q_sh, a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.dO, a.do_st, a.do_sh, a.nlse, a.delta,
-        a.bits, a.lpre, a.cu, p.seqitem, p.totals, (int)z.S, (int)z.Hk, (int)z.chunk, (int)z.items_cap, a.topk,
+        a.bits, a.dsbase, a.cu, p.seqitem, p.totals, (int)z.S, (int)z.Hk, (int)z.chunk, (int)z.items_cap,
         a.scale * kLog2e, a.scale, a.item_count, a.part_dk, a.part_dv, a.ds, a.dk, a.dk_st, a.dk_sh, a.dv,
         a.dv_st, a.dv_sh);
   }
@@ -1038,8 +1033,8 @@ void launch_qsa_bwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStre
   {
     KernelTimer timer("qsa_dq", st);
     qsa_dq_ds_kernel<<<(unsigned)(z.ntiles * z.Hk), 64 * kRowWaves, 0, st>>>(
-        a.kop, a.ds, a.bits, a.cu, p.blkbase, p.tile_order, (int)z.S, (int)z.T, (int)z.Hk, a.topk, a.scale, a.dq,
-        a.dq_st, a.dq_sh);
+        a.kop, a.ds, a.dsbase, a.bits, a.cu, p.blkbase, p.tile_order, (int)z.S, (int)z.T, (int)z.Hk, a.scale,
+        a.dq, a.dq_st, a.dq_sh);
   }
 }
 
