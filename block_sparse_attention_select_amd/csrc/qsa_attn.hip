@@ -526,8 +526,9 @@ __global__ __launch_bounds__(64 * kRowWaves) void qsa_dq_ds_kernel(
   // K runs kt * 8 + ds (keys score_key(kt, .), dims 32 ds ..), stored
   // swizzled (swz_slot) for the transposed K^T reads
   __shared__ u32x4 kbuf[2][32][64];
-  // per wavefront and 32-key half, each lane's 8 keys of dS
-  __shared__ u32x4 dsl[2][kRowWaves][2][64];
+  // per wavefront and 32-key half, each lane's 8 keys of dS, three steps deep
+  // (copied two steps ahead; each wavefront reads only its own slots)
+  __shared__ u32x4 dsl[3][kRowWaves][2][64];
   __shared__ TileUnionRows<kQTok> tu;
 
   const int h = blockIdx.x % Hk;
@@ -559,11 +560,9 @@ __global__ __launch_bounds__(64 * kRowWaves) void qsa_dq_ds_kernel(
     const int c = tu.ulist[u] - ktb_t;
     return (c >= 0 && c <= own_c) ? tile_mask(tu.bmap[tk], c) : 0u;
   };
-  // staging of union step u: the tile's 32 K runs (run wave + 12 ii copied by
-  // wavefront `wave`), then each lane's 16 bytes of its row's dS line per half
-  // (every lane copies, so each wavefront issues the same number of copies;
-  // the row's token's first slot stands in where its token lists nothing)
-  auto stage = [&](int u, int buf, uint32_t m16) {
+  // staging of union step u's K: the tile's 32 K runs, run wave + 12 ii
+  // copied by wavefront `wave`
+  auto stage_k = [&](int u, int buf) {
     const int gk = __builtin_amdgcn_readfirstlane(tu.ulist[u]);
     const int ln = fresh_lane();
     const u16* kbase = kop + ((int64_t)gk * Hk + h) * 32 * 512;
@@ -572,24 +571,37 @@ __global__ __launch_bounds__(64 * kRowWaves) void qsa_dq_ds_kernel(
       const int r = wave + kRowWaves * ii;
       if (r < 32) dma16s(kbase + 512 * r, 16 * ln, lds_offset(&kbuf[buf][r][0]));
     }
+  };
+  // step u's dS: each lane's 16 bytes of its row's line per half, two copies
+  // per wavefront whatever the masks (the row's token's first slot stands in
+  // where its token lists nothing)
+  auto stage_ds = [&](int u, int dbuf, uint32_t m16) {
     const int c = m16 != 0u ? tu.ulist[u] - ktb_t : 0;
     const u16* line = ds + (((slot0 + c) * Hk + h) * kG + hd) * kKT + 8 * g;
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) dma16(line + 32 * kc, lds_offset(&dsl[buf][wave][kc][0]));
+    for (int kc = 0; kc < 2; ++kc) dma16(line + 32 * kc, lds_offset(&dsl[dbuf][wave][kc][0]));
   };
-  uint32_t m_cur = 0u;
+  uint32_t m_cur = 0u, m_n1 = 0u;
   if (nu > 0) {
     m_cur = tile_bits(0);
-    stage(0, 0, m_cur);
+    stage_k(0, 0);
+    stage_ds(0, 0, m_cur);
+  }
+  if (nu > 1) {
+    m_n1 = tile_bits(1);
+    stage_ds(1, 1, m_n1);
   }
   wait_copies();
   wait_all_loads();
   __syncthreads();
 
+  int dbuf = 0;
   for (int u = 0; u < nu; ++u) {
     const int buf = u & 1;
-    const uint32_t m_next = u + 1 < nu ? tile_bits(u + 1) : 0u;
-    if (u + 1 < nu) stage(u + 1, buf ^ 1, m_next);
+    const bool ahead2 = u + 2 < nu;
+    const uint32_t m_n2 = ahead2 ? tile_bits(u + 2) : 0u;
+    if (u + 1 < nu) stage_k(u + 1, buf ^ 1);
+    if (ahead2) stage_ds(u + 2, dbuf == 0 ? 2 : dbuf - 1, m_n2);
     if (__ballot(m_cur != 0u)) {
       const int c = tu.ulist[u] - ktb_t;
       const bool own = (c == own_c);
@@ -600,7 +612,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void qsa_dq_ds_kernel(
         if (!__ballot(m_cur != 0u && !(own && 32 * kc > plim))) continue;
         // dS^T operand: keys 32 kc + 8g .. +7 of the row (zero where its
         // token lists nothing in the tile: that line was never written)
-        const u32x4 rec = dsl[buf][wave][kc][lane];
+        const u32x4 rec = dsl[dbuf][wave][kc][lane];
         const bool on = m_cur != 0u;
         const bf16x8 dsb =
             __builtin_bit_cast(bf16x8, u32x4{on ? rec[0] : 0u, on ? rec[1] : 0u, on ? rec[2] : 0u, on ? rec[3] : 0u});
@@ -625,9 +637,16 @@ __global__ __launch_bounds__(64 * kRowWaves) void qsa_dq_ds_kernel(
         __builtin_amdgcn_sched_group_barrier(0x008, kDqTrAhead, 0);
       }
     }
-    wait_copies();
+    // step u + 1's K and dS have landed; step u + 2's dS (the wavefront's
+    // last two copies) may still be in flight: copies complete in issue order
+    if (ahead2)
+      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else
+      wait_copies();
     lds_barrier();
-    m_cur = m_next;
+    m_cur = m_n1;
+    m_n1 = m_n2;
+    dbuf = dbuf == 2 ? 0 : dbuf + 1;
   }
 
   if (tok_ok) {
