@@ -213,38 +213,33 @@ __global__ __launch_bounds__(256) void qsa_vt_kernel(const u16* __restrict__ v, 
 }
 
 // ---------------------------------------------------------------------------
-// Copies of K (and V) per (key tile, KV head) in the stage order of the
-// forward (K, plain) or the dQ pass (K, swizzled), so every staged 1 KB
-// run is one contiguous copy: run kt*8 + ds, slot l holding x[key
-// score_key(kt, r)][dims 32 ds + 8 (l / 16) .. +7] with r = l % 16 (plain) or
-// swz_slot(l) % 16 (swizzled); zero past the sequence end.  blockIdx.z: tensor
-// z / 4 of {K, V}, a quarter of the runs each.
+// Copies of K per (key tile, KV head) in the stage order of the forward
+// (plain) or the dQ pass (swizzled), so every staged 1 KB run is one
+// contiguous copy: run kt*8 + ds, slot l holding k[key score_key(kt, r)][dims
+// 32 ds + 8 (l / 16) .. +7] with r = l % 16 (plain) or swz_slot(l) % 16
+// (swizzled); zero past the sequence end.  blockIdx.z: a quarter of the runs.
 // ---------------------------------------------------------------------------
 template <bool kSwizzled>
 __global__ __launch_bounds__(256) void qsa_prep_kernel(const u16* __restrict__ k, int64_t k_st, int64_t k_sh,
-                                                       const u16* __restrict__ v, int64_t v_st, int64_t v_sh,
                                                        const int32_t* __restrict__ cu,
                                                        const int32_t* __restrict__ ktbase,
                                                        const int32_t* __restrict__ kt_seq,
                                                        const int32_t* __restrict__ totals, int Hk,
-                                                       u16* __restrict__ kop, u16* __restrict__ vop) {
+                                                       u16* __restrict__ kop) {
   const int gk = blockIdx.x, h = blockIdx.y;
   if (gk >= totals[0]) return;
-  const bool is_v = blockIdx.z >= 4;
-  const int part = blockIdx.z & 3;
-  const u16* x = is_v ? v : k;
-  const int64_t st_t = is_v ? v_st : k_st, st_h = is_v ? v_sh : k_sh;
+  const int part = blockIdx.z;
   const int s = kt_seq[gk];
   const int c = gk - ktbase[s];
   const int seq0 = cu[s], L = cu[s + 1] - seq0;
-  u16* dst = (is_v ? vop : kop) + ((int64_t)gk * Hk + h) * (32 * 64 * 8);
+  u16* dst = kop + ((int64_t)gk * Hk + h) * (32 * 64 * 8);
   for (int i = 512 * part + threadIdx.x; i < 512 * part + 512; i += 256) {
     const int run = i >> 6, ln = i & 63;
     const int r = kSwizzled ? (swz_slot(ln) & 15) : (ln & 15);
     const int kp = kKT * c + score_key(run >> 3, r);
     u32x4 val = {0u, 0u, 0u, 0u};
     if (kp < L)
-      val = *reinterpret_cast<const u32x4*>(x + (int64_t)(seq0 + kp) * st_t + (int64_t)h * st_h + 32 * (run & 7) +
+      val = *reinterpret_cast<const u32x4*>(k + (int64_t)(seq0 + kp) * k_st + (int64_t)h * k_sh + 32 * (run & 7) +
                                             8 * (ln >> 4));
     *reinterpret_cast<u32x4*>(dst + (int64_t)i * 8) = val;
   }
@@ -1014,7 +1009,7 @@ void launch_qsa_fwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStre
     qsa_vt_kernel<<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk), 256, 0, st>>>(
         a.v, a.v_st, a.v_sh, a.cu, p.blkbase, p.blk_seq, p.totals, (int)z.Hk, a.vt);
     qsa_prep_kernel<false><<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk, 4), 256, 0, st>>>(
-        a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.cu, p.blkbase, p.blk_seq, p.totals, (int)z.Hk, a.kop, nullptr);
+        a.k, a.k_st, a.k_sh, a.cu, p.blkbase, p.blk_seq, p.totals, (int)z.Hk, a.kop);
   }
   KernelTimer timer("qsa_fwd", st);
   qsa_fwd_kernel<<<(unsigned)(z.ntiles * z.Hk), 64 * kRowWaves, 0, st>>>(
@@ -1025,10 +1020,10 @@ void launch_qsa_fwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStre
 void launch_qsa_bwd(const Sizes& z, const QsaArgs& a, const PlanBufs& p, hipStream_t st) {
   launch_bitmaps(z, a, p, a.dsbase, st);
   {
-    // K in the dQ pass's swizzled stage order (parts 0-3 of the prep grid)
+    // K in the dQ pass's swizzled stage order
     KernelTimer timer("qsa_prep", st);
     qsa_prep_kernel<true><<<dim3((unsigned)z.nblk_cap, (unsigned)z.Hk, 4), 256, 0, st>>>(
-        a.k, a.k_st, a.k_sh, a.v, a.v_st, a.v_sh, a.cu, p.blkbase, p.blk_seq, p.totals, (int)z.Hk, a.kop, nullptr);
+        a.k, a.k_st, a.k_sh, a.cu, p.blkbase, p.blk_seq, p.totals, (int)z.Hk, a.kop);
   }
   {
     KernelTimer timer("qsa_delta", st);
