@@ -2,6 +2,8 @@
 header declares, sizes workspaces, and rejects bad arguments before it
 launches anything.  No GPU is needed (and none is touched)."""
 import ctypes
+
+import numpy as np
 import os
 import re
 import subprocess
@@ -200,6 +202,33 @@ def test_qsa_workspace_dims(kw, status):
         msa.MSA_ERR_UNSUPPORTED
     assert msa.load().msa_workspace_size(ctypes.byref(qsa_dims()), msa.MSA_OP_FWD, ctypes.byref(n)) == \
         msa.MSA_ERR_UNSUPPORTED
+
+
+def _dslines(lengths):
+    """dS lines of the narrow backward per (KV head, query head): one per (token, causal 64-key tile)."""
+    return sum(p // 64 + 1 for L in lengths for p in range(L))
+
+
+@pytest.mark.parametrize("T,M,S,hk", [(16384, 7122, 3, 1), (5000, 5000, 1, 2), (4097, 64, 65, 1), (3000, 1100, 3, 1),
+                                      (200, 7, 40, 1)])
+def test_qsa_backward_workspace_holds_every_dslines_mix(T, M, S, hk):
+    """The narrow backward workspace covers the dS lines of the worst pack its dims allow (sequences as long as
+    max_seqlen, the rest in one), by brute force over the lines."""
+    n_b = ctypes.c_size_t(0)
+    d = qsa_dims(total_tokens=T, num_seqs=S, max_seqlen=M, num_q_heads=12 * hk, num_kv_heads=hk)
+    assert msa.load().msa_workspace_size(ctypes.byref(d), msa.MSA_OP_QSA_BWD, ctypes.byref(n_b)) == msa.MSA_OK
+    worst = [M] * (T // M) + ([T % M] if T % M else [])
+    lines = _dslines(worst) * hk * 12
+    assert n_b.value >= lines * 128
+    # any other mix of lengths up to M summing to T needs no more lines
+    rng = np.random.default_rng(T)
+    for _ in range(20):
+        left, mix = T, []
+        while left > 0:
+            L = int(rng.integers(1, min(M, left) + 1))
+            mix.append(L)
+            left -= L
+        assert _dslines(mix) * hk * 12 <= lines
 
 
 @no_gpu
