@@ -502,16 +502,16 @@ __global__ __launch_bounds__(64 * kRowWaves) void qsa_fwd_kernel(
 // ---------------------------------------------------------------------------
 // dQ from the dS the dK/dV pass stored.  The forward's tiling: 12 wavefronts
 // per (16-token tile, KV head), lane column = row 16 wave + li of the tile
-// (head hd of token tk), so no padding heads are computed; only the 168
-// registers of three wavefronts per SIMD are needed (dQ^T accumulators 64).
-// The union of the tile's key tiles is walked with K staged (swizzled, from
-// the prep kernel's copy) and K^T read transposed; per 32-key half a lane's
-// dS^T operand is keys 8g .. 8g+7 of its row, i.e. two listed blocks' records
-// (zero for unlisted blocks).  A record's index is the block's rank in its
-// token's ascending list: the lane counts its token's listed blocks tile by
-// tile.  The records of step u + 1 are loaded during step u, after its
-// copies, and stay in flight across the step's wait (loads and copies
-// complete in issue order).
+// (head hd of token tk), so no padding heads are computed, within the 168
+// registers of three wavefronts per SIMD (dQ^T accumulators 64).  The union
+// of the tile's key tiles is walked with K staged (swizzled, from the prep
+// kernel's copy) and K^T read transposed; per 32-key half a lane's dS^T
+// operand is keys 32 kc + 8g .. +7 of its row's dS line for the tile (slot
+// tslot + c of the row's token), zero where the token lists nothing in the
+// tile.  The lines are copied into LDS two steps ahead through a three-deep
+// ring, K one step ahead; every wait in the walk is the step's own explicit
+// one, which leaves the wavefront's last two copies (step u + 2's dS) in
+// flight (copies complete in issue order).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64 * kRowWaves) void qsa_dq_ds_kernel(
     const u16* __restrict__ kop, const u16* ds, const int64_t* __restrict__ dsbase,
@@ -803,7 +803,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int pos = p_begin + (sel[n] & 0xFFFF);
         const int64_t slot = seqslot + slots_before(pos) + c;
         __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&dsx[b & 1][j >> 1][R][8 * (j & 1)]),
-                                    reinterpret_cast<u32x4*>(ds_out + ((slot * Hk + h) * kG + (rrow - kG * n)) * kKT + 8 * j));
+                                    reinterpret_cast<u32x4*>(ds_out +
+                                                             ((slot * Hk + h) * kG + (rrow - kG * n)) * kKT + 8 * j));
       }
       asm volatile("" ::: "memory");
     };
