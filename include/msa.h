@@ -323,6 +323,10 @@ int msa_attn_bwd(const msa_dims* dims,
  *   q, o, do_, dq [T, Hq, 256] and k, v, dk, dv [T, Hk, 256] bf16 with their
  *         own strides (dim contiguous); lse [T, Hq] fp32.
  * Workspaces: msa_workspace_size(dims, MSA_OP_QSA_FWD / MSA_OP_QSA_BWD, ...).
+ * The backward's holds dS for every (token, causal 64-key tile, KV head):
+ * 1.5 KB each, so it grows with the square of the sequence lengths (about
+ * 1.8 GB for 16384 tokens in sequences of up to 7122, 14 GB for one
+ * 32768-token sequence with one KV head).
  * Errors, ownership, determinism and stream semantics as for msa_attn_*.
  */
 int msa_qsa_attn_fwd(const msa_dims* dims,
